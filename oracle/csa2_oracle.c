@@ -1,0 +1,331 @@
+/*
+ * csa2_oracle.c -- TEST INFRASTRUCTURE.  The plain, slow CPU oracle of the
+ * CSA2 FP4-KV decode path.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product library never does,
+ * and it shares no code, header or table with the HIP path.
+ *
+ * Every function is written from the definition of what it computes, scalar,
+ * without blocking or reordering, so that it can be checked by eye.  Floating
+ * point is double unless stated; the quantiser compares exact products.
+ *
+ * Citations name the page and its section:
+ *   [P1] "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M Context, FP4 KV
+ *        Cache, and Cross-Layer Attention Reuse" (thecryptopost.io)
+ *   [P3] "DeepSeek-V4.1 Flash: Pushing the Limits of KV Cache Compression"
+ *        (tldrocket.com)
+ *   [P4] "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression"
+ *        (agihunt.info paper page 2609.19969), summary
+ *
+ * Readings taken where the pages are silent are marked READING and are the
+ * same ones the library documents in its header.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define D_LATENT 512   /* [P3]: a 512-dimensional latent shared by key and value */
+#define GROUP 16       /* [P1 "FP4 KV, ..."]: one E4M3 scale per 16 channels */
+#define N_GROUPS (D_LATENT / GROUP)
+#define CODE_BYTES (D_LATENT / 2)
+#define IDX_HEADS 8
+#define IDX_DIM 64
+#define MAIN_HEADS 16
+
+/* ---------------------------------------------------------------- formats */
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double orc_bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* E4M3 (OCP 8-bit float "E4M3FN"): sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 is subnormal; no infinities; the
+ * all-ones exponent with all-ones mantissa is NaN.  [P1 "FP4 KV, ..."]:
+ * the per-16-channel scale is E4M3. READING: the OCP FN variant. */
+double orc_e4m3_value(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* E2M1 (4-bit float): sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * exponent field 0 is subnormal (0 or 0.5).  [P1 "FP4 KV, ..."]. */
+double orc_e2m1_value(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v;
+  if (e == 0)
+    v = 0.5 * (double)m;
+  else
+    v = ldexp(1.0 + (double)m / 2.0, e - 1);
+  return s ? -v : v;
+}
+
+/* Round num/den to the nearest of the ascending values vals[0..n-1],
+ * ties to the even index, saturating past the last value.  Compares num
+ * with den * (midpoint of two neighbours); both operands of every
+ * comparison are exact doubles (short significands), so the result is the
+ * exact round-to-nearest-even of the rational num/den. */
+static int nearest_even_index(double num, double den, const double* vals, int n) {
+  for (int c = 0; c + 1 < n; ++c) {
+    double mid = den * (0.5 * (vals[c] + vals[c + 1]));
+    if (num < mid) return c;
+    if (num == mid) return (c % 2 == 0) ? c : c + 1;
+  }
+  return n - 1;
+}
+
+static double g_e4m3_pos[127]; /* codes 0x00..0x7E, ascending */
+static double g_e2m1_pos[8];   /* codes 0..7, ascending */
+
+/* Filled once when the library is loaded, before any thread can call in. */
+__attribute__((constructor)) static void tables_init(void) {
+  for (int c = 0; c < 127; ++c) g_e4m3_pos[c] = orc_e4m3_value((uint8_t)c);
+  for (int c = 0; c < 8; ++c) g_e2m1_pos[c] = orc_e2m1_value((uint8_t)c);
+}
+
+/* Scale code of one 16-channel group with absolute maximum `amax`:
+ * E4M3 round-to-nearest-even of amax / 6 (6 = the largest E2M1 magnitude,
+ * the NVFP4 convention that [P1 "FP4 KV, ..."] says is followed, without
+ * its second-level global scale).  Saturates at 448. */
+uint8_t orc_scale_code(double amax) {
+  return (uint8_t)nearest_even_index(amax, 6.0, g_e4m3_pos, 127);
+}
+
+/* E2M1 code of one value x under the group scale s: magnitude is
+ * round-to-nearest-even of |x| / s onto {0,0.5,1,1.5,2,3,4,6}, saturating at
+ * 6; the sign bit is the sign bit of x (READING: also for magnitude 0).
+ * A zero scale gives magnitude 0.  `neg` is the sign bit of x. */
+uint8_t orc_e2m1_code(double absx, int neg, double s) {
+  int m = 0;
+  if (s > 0.0) m = nearest_even_index(absx, s, g_e2m1_pos, 8);
+  return (uint8_t)((neg ? 8 : 0) | m);
+}
+
+/* Quantise one 512-channel bf16 latent row [P1 "FP4 KV, ..."]:
+ * 32 groups of 16 channels, one E4M3 scale byte per group, one E2M1 code per
+ * channel.  READING (byte layout, not on the pages): code byte j holds
+ * channel 2j in its low nibble and channel 2j+1 in its high nibble; scale
+ * byte g belongs to channels 16g..16g+15. */
+void orc_quant_row(const uint16_t* x, uint8_t* codes, uint8_t* scales) {
+  uint8_t c[D_LATENT];
+  for (int g = 0; g < N_GROUPS; ++g) {
+    double amax = 0.0;
+    for (int i = 0; i < GROUP; ++i) {
+      double a = fabs(orc_bf16_value(x[g * GROUP + i]));
+      if (a > amax) amax = a;
+    }
+    uint8_t sc = orc_scale_code(amax);
+    double s = orc_e4m3_value(sc);
+    scales[g] = sc;
+    for (int i = 0; i < GROUP; ++i) {
+      uint16_t b = x[g * GROUP + i];
+      c[g * GROUP + i] = orc_e2m1_code(fabs(orc_bf16_value(b)), (b >> 15) & 1, s);
+    }
+  }
+  for (int j = 0; j < CODE_BYTES; ++j) codes[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+}
+
+void orc_quant_rows(const uint16_t* x, int64_t n, uint8_t* codes, uint8_t* scales) {
+  for (int64_t r = 0; r < n; ++r)
+    orc_quant_row(x + r * D_LATENT, codes + r * CODE_BYTES, scales + r * N_GROUPS);
+}
+
+/* Dequantise one row: value = E2M1(code) * E4M3(scale) (exact). */
+void orc_dequant_row(const uint8_t* codes, const uint8_t* scales, double* out) {
+  for (int d = 0; d < D_LATENT; ++d) {
+    uint8_t byte = codes[d / 2];
+    uint8_t code = (d % 2 == 0) ? (byte & 15) : (byte >> 4);
+    out[d] = orc_e2m1_value(code) * orc_e4m3_value(scales[d / GROUP]);
+  }
+}
+
+/* ------------------------------------------------------------ indexer score */
+
+/* Indexer score of one key [P1 "Compressed Sparse Attention 2 (CSA2)"]: the
+ * pages name an indexer Q scored against indexer K but print no formula.
+ * READING: per indexer head h, r_h = max(0, q_h . k); score = sum_h w_h r_h.
+ * Without weights (w == NULL) every w_h = 1 and the score is the exact sum.
+ * With weights the sum is taken in binary32 in a fixed order:
+ * ((w0 r0 + w1 r1) + w2 r2) + w3 r3, the same for heads 4..7, then the two
+ * partial sums are added. */
+float orc_index_score_one(const uint16_t* q, const float* w, const uint16_t* k) {
+  double r[IDX_HEADS];
+  for (int h = 0; h < IDX_HEADS; ++h) {
+    double dot = 0.0;
+    for (int d = 0; d < IDX_DIM; ++d)
+      dot += orc_bf16_value(q[h * IDX_DIM + d]) * orc_bf16_value(k[d]);
+    r[h] = dot > 0.0 ? dot : 0.0;
+  }
+  if (!w) {
+    double s = 0.0;
+    for (int h = 0; h < IDX_HEADS; ++h) s += r[h];
+    return (float)s;
+  } else {
+    float lo = (float)w[0] * (float)r[0];
+    for (int h = 1; h < 4; ++h) lo = lo + (float)w[h] * (float)r[h];
+    float hi = (float)w[4] * (float)r[4];
+    for (int h = 5; h < 8; ++h) hi = hi + (float)w[h] * (float)r[h];
+    return lo + hi;
+  }
+}
+
+/* Scores of n keys given by row ids into a key array [*][64]. */
+void orc_index_score(const uint16_t* q, const float* w, const uint16_t* keys,
+                     const int64_t* ids, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_index_score_one(q, w, keys + ids[i] * IDX_DIM);
+}
+
+/* --------------------------------------------------------------- selection */
+
+typedef struct {
+  float score;
+  int64_t id;
+} cand_t;
+
+/* Larger score first; equal scores: lower id first (READING: ties go to the
+ * lower position; the pages give no tie rule). */
+static int cand_order(const void* pa, const void* pb) {
+  const cand_t* a = (const cand_t*)pa;
+  const cand_t* b = (const cand_t*)pb;
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+  return (a->id < b->id) ? -1 : (a->id > b->id) ? 1 : 0;
+}
+
+static int id_order(const void* pa, const void* pb) {
+  int64_t a = *(const int64_t*)pa, b = *(const int64_t*)pb;
+  return (a < b) ? -1 : (a > b) ? 1 : 0;
+}
+
+/* Top-k of n candidates [P1 "Compressed Sparse Attention 2 (CSA2)"]: keep the
+ * min(k, n) best by (score desc, id asc); write their ids ascending into
+ * out[0..k-1], padding with -1 (READING: output order and padding).
+ * Returns the number selected. */
+int64_t orc_select(const float* scores, const int64_t* ids, int64_t n, int64_t k, int64_t* out) {
+  cand_t* c = (cand_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(cand_t));
+  int64_t take = n < k ? n : k;
+  for (int64_t i = 0; i < n; ++i) {
+    c[i].score = scores[i];
+    c[i].id = ids[i];
+  }
+  qsort(c, (size_t)n, sizeof(cand_t), cand_order);
+  for (int64_t i = 0; i < take; ++i) out[i] = c[i].id;
+  qsort(out, (size_t)take, sizeof(int64_t), id_order);
+  for (int64_t i = take; i < k; ++i) out[i] = -1;
+  free(c);
+  return take;
+}
+
+/* Flat Full layer [P1 "Compressed Sparse Attention 2 (CSA2)"]: score all L
+ * positions with the layer's indexer Q and select a fresh Top-k. */
+int64_t orc_flat_select(const uint16_t* q, const float* w, const uint16_t* tok_keys, int64_t L,
+                        int64_t k, int64_t* out) {
+  int64_t* ids = (int64_t*)malloc((size_t)(L > 0 ? L : 1) * sizeof(int64_t));
+  float* sc = (float*)malloc((size_t)(L > 0 ? L : 1) * sizeof(float));
+  for (int64_t i = 0; i < L; ++i) ids[i] = i;
+  orc_index_score(q, w, tok_keys, ids, L, sc);
+  int64_t r = orc_select(sc, ids, L, k, out);
+  free(ids);
+  free(sc);
+  return r;
+}
+
+/* Pool of a hierarchical Full layer [P1 "Compressed Sparse Attention 2
+ * (CSA2)"]: the decoder's Full layer builds a candidate pool of up to
+ * n_pool_blocks blocks of `blk` positions.  Block b covers positions
+ * blk*b .. blk*b+blk-1 and is a candidate iff blk*b < L (READING: a partial
+ * last block is a candidate).  Blocks are ranked by their block key's score
+ * (READING: block keys are given inputs).  Writes the kept block ids
+ * ascending, -1 padded. */
+int64_t orc_pool_blocks(const uint16_t* q, const float* w, const uint16_t* blk_keys, int64_t L,
+                        int64_t blk, int64_t n_pool_blocks, int64_t* pool_out) {
+  int64_t nb = (L + blk - 1) / blk;
+  return orc_flat_select(q, w, blk_keys, nb, n_pool_blocks, pool_out);
+}
+
+/* Token-level selection inside a pool: the candidates are the positions
+ * blk*b + j (j < blk) of every pool block b >= 0 that lie below L; each is
+ * scored with the given indexer Q on the token indexer K.  Used by the
+ * hierarchical Full layer (its own Q) and by Reindex layers (their own Q,
+ * [P1 "Compressed Sparse Attention 2 (CSA2)"]: rescore with own indexer Q). */
+int64_t orc_pool_select(const uint16_t* q, const float* w, const uint16_t* tok_keys, int64_t L,
+                        const int64_t* pool, int64_t n_pool_blocks, int64_t blk, int64_t k,
+                        int64_t* out) {
+  int64_t cap = n_pool_blocks * blk, n = 0;
+  int64_t* ids = (int64_t*)malloc((size_t)(cap > 0 ? cap : 1) * sizeof(int64_t));
+  float* sc = (float*)malloc((size_t)(cap > 0 ? cap : 1) * sizeof(float));
+  for (int64_t p = 0; p < n_pool_blocks; ++p) {
+    if (pool[p] < 0) continue;
+    for (int64_t j = 0; j < blk; ++j) {
+      int64_t pos = pool[p] * blk + j;
+      if (pos < L) ids[n++] = pos;
+    }
+  }
+  orc_index_score(q, w, tok_keys, ids, n, sc);
+  int64_t r = orc_select(sc, ids, n, k, out);
+  free(ids);
+  free(sc);
+  return r;
+}
+
+/* ---------------------------------------------------------------- attention */
+
+/* Sparse + SWA attention of one query token in one layer.
+ * [P1 "Compressed Sparse Attention 2 (CSA2)"]: each layer attends with its
+ * own main Q over the selected main-KV positions; [P1 "Causal
+ * Encoder-Decoder: Half the Prefill"]: a 128-token sliding window runs in
+ * every layer; [P3]: keys and values share one 512-d latent.
+ * The attended set is the dequantised rows idx[i] >= 0 of the FP4 cache
+ * (codes [*][256], scales [*][32]) followed by the first swa_len bf16 SWA rows
+ * (READING: one softmax over the concatenation, no de-duplication).
+ * For each head h: z_j = sm_scale * (q_h . x_j), p = softmax(z),
+ * o_h = sum_j p_j x_j, rounded to binary32.  An empty set gives o_h = 0. */
+void orc_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                     const int64_t* idx, int64_t n_idx, const uint16_t* swa, int64_t swa_len,
+                     double sm_scale, float* out) {
+  int64_t n_sel = 0;
+  for (int64_t i = 0; i < n_idx; ++i) n_sel += idx[i] >= 0;
+  int64_t n = n_sel + (swa_len > 0 ? swa_len : 0);
+  double* x = (double*)malloc((size_t)(n > 0 ? n : 1) * D_LATENT * sizeof(double));
+  double* z = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+  int64_t r = 0;
+  for (int64_t i = 0; i < n_idx; ++i) {
+    if (idx[i] < 0) continue;
+    orc_dequant_row(codes + idx[i] * CODE_BYTES, scales + idx[i] * N_GROUPS, x + r * D_LATENT);
+    ++r;
+  }
+  for (int64_t j = 0; j < swa_len; ++j, ++r)
+    for (int d = 0; d < D_LATENT; ++d) x[r * D_LATENT + d] = orc_bf16_value(swa[j * D_LATENT + d]);
+
+  for (int h = 0; h < MAIN_HEADS; ++h) {
+    double zmax = -INFINITY, denom = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < D_LATENT; ++d) dot += orc_bf16_value(q[h * D_LATENT + d]) * x[j * D_LATENT + d];
+      z[j] = sm_scale * dot;
+      if (z[j] > zmax) zmax = z[j];
+    }
+    for (int64_t j = 0; j < n; ++j) {
+      z[j] = exp(z[j] - zmax);
+      denom += z[j];
+    }
+    for (int d = 0; d < D_LATENT; ++d) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < n; ++j) acc += z[j] * x[j * D_LATENT + d];
+      out[h * D_LATENT + d] = (n > 0) ? (float)(acc / denom) : 0.0f;
+    }
+  }
+  free(x);
+  free(z);
+}
