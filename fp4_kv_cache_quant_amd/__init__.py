@@ -1,0 +1,263 @@
+"""Python binding of libcsa2, the CSA2 FP4-KV decode path for MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libcsa2.so.
+PyTorch provides device memory and the current HIP stream.  The functions
+mirror the C entry points of include/csa2.h (same names without the
+``csa2_`` prefix); tensors must already be on the GPU with the documented
+shapes and dtypes (bf16 data may be passed as torch.bfloat16 or int16).
+There is no fallback: if the library is missing, importing raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk",
+    "sparse_attn", "sparse_attn_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
+    "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+LATENT, CODE_BYTES, SCALE_BYTES = 512, 256, 32
+HEADS, IDX_HEADS, IDX_DIM = 16, 8, 64
+FULL, REINDEX, REUSE = 0, 1, 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with `python -m fp4_kv_cache_quant_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class _FP4KV(ctypes.Structure):
+    _fields_ = [("codes", _P), ("scales", _P), ("cap", _I64), ("n_seq", _I32)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("mode", _I32), ("kv_id", _I32), ("hierarchical", _I32)]
+
+
+class _SchedDesc(ctypes.Structure):
+    _fields_ = [("n_seq", _I32), ("n_layers", _I32), ("layers", _P), ("key_cap", _I64),
+                ("blk_cap", _I64), ("topk", _I32), ("pool_blocks", _I32), ("blk", _I32),
+                ("swa_max", _I32), ("sm_scale", _F32)]
+
+
+class _StepIO(ctypes.Structure):
+    _fields_ = [("n_kv", _I32), ("kv", _P), ("lens", _P), ("new_row", _P), ("append_kv", _I32),
+                ("idx_k", _P), ("blk_k", _P), ("idx_q", _P), ("idx_w", _P), ("main_q", _P),
+                ("swa", _P), ("swa_len", _P), ("out", _P)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_last_error = _sig("csa2_last_error", ctypes.c_char_p)
+abi_version = _sig("csa2_abi_version", _I32)
+_quant_rows = _sig("csa2_quant_rows", _I32, _P, _I64, _P, _P, _P)
+_quant_append = _sig("csa2_quant_append", _I32, _P, _FP4KV, _P, _P, _P)
+_index_score = _sig("csa2_index_score", _I32, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _I64, _I32, _P)
+_topk = _sig("csa2_topk", _I32, _P, _I64, _P, _I32, _I32, _P, _I32, _I32, _P, _I32, _P)
+_attn_ws = _sig("csa2_sparse_attn_workspace_size", _SZ, _I32, _I32, _I32)
+_attn = _sig("csa2_sparse_attn", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
+             _I32, _F32, _P, _P, _SZ, _P)
+_sched_create = _sig("csa2_sched_create", _I32, ctypes.POINTER(_SchedDesc), ctypes.POINTER(_P))
+_sched_step = _sig("csa2_sched_decode_step", _I32, _P, ctypes.POINTER(_StepIO), _P)
+_sched_indices = _sig("csa2_sched_indices", _P, _P, _I32)
+_sched_pool = _sig("csa2_sched_pool", _P, _P)
+_sched_check = _sig("csa2_sched_check", _I32, _P, ctypes.POINTER(_I32))
+_sched_destroy = _sig("csa2_sched_destroy", None, _P)
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"csa2 error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise Csa2Error(rc, _last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+class FP4KV:
+    """An FP4 main-KV tensor: codes [n_seq][cap][256] u8 + scales [n_seq][cap][32] u8."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        assert codes.dtype == torch.uint8 and scales.dtype == torch.uint8
+        assert codes.dim() == 3 and codes.shape[2] == CODE_BYTES
+        assert scales.shape == (*codes.shape[:2], SCALE_BYTES)
+        self.codes, self.scales = codes, scales
+
+    @classmethod
+    def empty(cls, n_seq: int, cap: int, device="cuda"):
+        return cls(torch.zeros(n_seq, cap, CODE_BYTES, dtype=torch.uint8, device=device),
+                   torch.zeros(n_seq, cap, SCALE_BYTES, dtype=torch.uint8, device=device))
+
+    @property
+    def n_seq(self):
+        return self.codes.shape[0]
+
+    @property
+    def cap(self):
+        return self.codes.shape[1]
+
+    def c(self) -> _FP4KV:
+        return _FP4KV(_ptr(self.codes), _ptr(self.scales), self.cap, self.n_seq)
+
+
+def quant_rows(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """src [n][512] bf16 -> codes [n][256], scales [n][32] (views of a cache are fine if contiguous)."""
+    n = src.numel() // LATENT
+    assert codes.numel() >= n * CODE_BYTES and scales.numel() >= n * SCALE_BYTES
+    _check(_quant_rows(_ptr(src), n, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def quant_append(src: torch.Tensor, kv: FP4KV, lens: torch.Tensor, err_flag: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    assert src.numel() == kv.n_seq * LATENT and lens.dtype == torch.int32 and lens.numel() == kv.n_seq
+    _check(_quant_append(_ptr(src), kv.c(), _ptr(lens), _ptr(err_flag), _stream(stream)))
+
+
+def index_score(q: torch.Tensor, keys: torch.Tensor, lens: torch.Tensor, scores: torch.Tensor,
+                w: Optional[torch.Tensor] = None, len_div: int = 1, pool: Optional[torch.Tensor] = None,
+                blk: int = 8, stream=None) -> None:
+    """q [n_seq][8][64], keys [n_seq][key_cap][64], scores [n_seq][n_out] f32."""
+    n_seq, key_cap = keys.shape[0], keys.shape[1]
+    n_out = scores.shape[1]
+    n_pool = pool.shape[1] if pool is not None else 0
+    _check(_index_score(_ptr(q), _ptr(w), _ptr(keys), key_cap, _ptr(lens), len_div, _ptr(pool), n_pool,
+                        blk, _ptr(scores), n_out, n_seq, _stream(stream)))
+
+
+def topk(scores: torch.Tensor, k: int, out: torch.Tensor, lens: Optional[torch.Tensor] = None,
+         len_div: int = 1, pool: Optional[torch.Tensor] = None, blk: int = 8, stream=None) -> None:
+    """scores [n_seq][n] f32 -> out [n_seq][k] int32 ascending ids, -1 padded."""
+    n_seq, n = scores.shape
+    n_pool = pool.shape[1] if pool is not None else 0
+    _check(_topk(_ptr(scores), n, _ptr(lens), len_div, k, _ptr(pool), n_pool, blk, _ptr(out), n_seq,
+                 _stream(stream)))
+
+
+def sparse_attn_workspace_size(n_q: int, k_idx: int, swa_max: int) -> int:
+    return int(_attn_ws(n_q, k_idx, swa_max))
+
+
+def sparse_attn(q: torch.Tensor, kv: FP4KV, idx: torch.Tensor, swa: torch.Tensor, swa_len: torch.Tensor,
+                sm_scale: float, out: torch.Tensor, ws: Optional[torch.Tensor] = None, q_per_seq: int = 1,
+                swa_q_stride_rows: Optional[int] = None, swa_max: Optional[int] = None, stream=None) -> None:
+    """q [n_q][16][512] bf16; idx [n_q][k_idx] int32; swa rows [..][512] bf16; out [n_q][16][512] f32."""
+    n_q = q.shape[0]
+    k_idx = idx.shape[1] if idx is not None and idx.dim() == 2 else 0
+    if swa_max is None:
+        swa_max = swa.shape[1] if swa.dim() == 3 else 0
+    if swa_q_stride_rows is None:
+        swa_q_stride_rows = swa_max
+    need = sparse_attn_workspace_size(n_q, k_idx, swa_max)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    kvc = kv.c()
+    _check(_attn(_ptr(q), n_q, ctypes.byref(kvc), q_per_seq, _ptr(idx), k_idx, _ptr(swa), swa_q_stride_rows,
+                 _ptr(swa_len), swa_max, sm_scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class Layer:
+    def __init__(self, mode: int, kv_id: int = 0, hierarchical: bool = False):
+        self.mode, self.kv_id, self.hierarchical = mode, kv_id, hierarchical
+
+
+class Sched:
+    """The native layer-group scheduler (csa2_sched_*)."""
+
+    def __init__(self, layers: Sequence[Layer], n_seq: int, key_cap: int, blk_cap: int = 0, topk: int = 512,
+                 pool_blocks: int = 2048, blk: int = 8, swa_max: int = 128, sm_scale: float = 512 ** -0.5):
+        arr = (_Layer * len(layers))(*[_Layer(l.mode, l.kv_id, int(l.hierarchical)) for l in layers])
+        desc = _SchedDesc(n_seq, len(layers), ctypes.cast(arr, _P), key_cap, blk_cap, topk, pool_blocks, blk,
+                          swa_max, sm_scale)
+        h = _P()
+        _check(_sched_create(ctypes.byref(desc), ctypes.byref(h)))
+        self._h = h
+        self.layers, self.n_seq, self.topk, self.pool_blocks = list(layers), n_seq, topk, pool_blocks
+        self._keep = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def prepare(self, kv: Sequence[FP4KV], lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k=None,
+                new_row=None, append_kv: int = 0, idx_w=None) -> "_StepIO":
+        """Build (and keep alive) the step descriptor for a fixed set of tensors."""
+        nl = len(self.layers)
+        kvs = (_FP4KV * len(kv))(*[k.c() for k in kv])
+        P = _P * nl
+        iq = P(*[_ptr(t) if t is not None else None for t in idx_q])
+        iw = P(*[_ptr(t) for t in idx_w]) if idx_w is not None else None
+        mq, sw, ou = P(*[_ptr(t) for t in main_q]), P(*[_ptr(t) for t in swa]), P(*[_ptr(t) for t in out])
+        io = _StepIO(len(kv), ctypes.cast(kvs, _P), _ptr(lens), _ptr(new_row), append_kv, _ptr(idx_k),
+                     _ptr(blk_k), ctypes.cast(iq, _P), ctypes.cast(iw, _P) if iw is not None else None,
+                     ctypes.cast(mq, _P), ctypes.cast(sw, _P), _ptr(swa_len), ctypes.cast(ou, _P))
+        io._keep = (kvs, iq, iw, mq, sw, ou, kv, lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k,
+                    new_row, idx_w)
+        return io
+
+    def decode_step(self, io: "_StepIO", stream=None) -> None:
+        _check(_sched_step(self._h, ctypes.byref(io), _stream(stream)))
+
+    def indices(self, layer: int) -> torch.Tensor:
+        """Copy of the indices [n_seq][topk] a layer attended with in the last step."""
+        p = _sched_indices(self._h, layer)
+        return _device_copy_int32(p, self.n_seq * self.topk).view(self.n_seq, self.topk)
+
+    def pool(self) -> Optional[torch.Tensor]:
+        p = _sched_pool(self._h)
+        if not p:
+            return None
+        return _device_copy_int32(p, self.n_seq * self.pool_blocks).view(self.n_seq, self.pool_blocks)
+
+    def check(self) -> int:
+        f = _I32()
+        _check(_sched_check(self._h, ctypes.byref(f)))
+        return f.value
+
+
+_hip = None
+
+
+def _device_copy_int32(ptr: int, n: int) -> torch.Tensor:
+    """Copy n int32 from a library-owned device buffer into a new tensor (on the current stream)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpyAsync.argtypes = [_P, _P, _SZ, ctypes.c_int, _P]
+        _hip.hipMemcpyAsync.restype = ctypes.c_int
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    rc = _hip.hipMemcpyAsync(out.data_ptr(), ptr, 4 * n, 3, torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpyAsync failed ({rc})")
+    return out

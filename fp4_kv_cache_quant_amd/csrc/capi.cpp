@@ -1,0 +1,178 @@
+// C ABI of libcsa2: argument validation, error reporting, dispatch to the
+// kernel launchers.  Semantics of every entry point are documented in
+// include/csa2.h.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "common.hpp"
+
+namespace csa2 {
+
+csa2_status quant_rows_launch(const uint16_t*, int64_t, uint8_t*, uint8_t*, hipStream_t);
+csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, int32_t*, hipStream_t);
+csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
+                               int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
+                               hipStream_t);
+csa2_status topk_launch(const float*, int64_t, const int32_t*, int32_t, int32_t, const int32_t*, int32_t,
+                        int32_t, int32_t*, int32_t, hipStream_t);
+size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
+csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
+                        const uint16_t*, int64_t, const int32_t*, int32_t, float, float*, void*,
+                        hipStream_t);
+
+namespace {
+thread_local std::string g_error;
+}
+
+void set_error(const std::string& msg) { g_error = msg; }
+void clear_error() { g_error.clear(); }
+
+csa2_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return CSA2_OK;
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return CSA2_EHIP;
+}
+
+// Checks shared by the standalone calls and the scheduler.
+csa2_status check_kv(const csa2_fp4_kv& kv, const char* who) {
+  CSA2_REQUIRE(kv.codes && kv.scales, CSA2_EINVAL, std::string(who) + ": null FP4 cache pointer");
+  CSA2_REQUIRE(kv.cap > 0 && kv.n_seq >= 0, CSA2_ESHAPE, std::string(who) + ": bad FP4 cache shape");
+  CSA2_REQUIRE(kv.cap < (int64_t(1) << 31), CSA2_ESHAPE,
+               std::string(who) + ": cache capacity must be below 2^31 rows");
+  return CSA2_OK;
+}
+
+csa2_status check_index_score(const uint16_t* q, const uint16_t* keys, int64_t key_cap,
+                              const int32_t* lens, int32_t len_div, const int32_t* pool, int32_t n_pool,
+                              int32_t blk, const float* scores, int64_t n_out, int32_t n_seq) {
+  CSA2_REQUIRE(n_seq >= 0 && n_seq <= 65535, CSA2_ESHAPE, "csa2_index_score: n_seq must be in [0, 65535]");
+  if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(q && keys && lens && scores, CSA2_EINVAL, "csa2_index_score: null pointer");
+  CSA2_REQUIRE(key_cap > 0 && n_out >= 0, CSA2_ESHAPE, "csa2_index_score: bad key_cap / n_out");
+  if (pool) {
+    CSA2_REQUIRE(n_pool > 0 && blk > 0, CSA2_ESHAPE, "csa2_index_score: bad n_pool / blk");
+    CSA2_REQUIRE(n_out == (int64_t)n_pool * blk, CSA2_ESHAPE,
+                 "csa2_index_score: pool mode needs n_out == n_pool * blk");
+  } else {
+    CSA2_REQUIRE(len_div > 0, CSA2_EINVAL, "csa2_index_score: len_div must be positive");
+    CSA2_REQUIRE(n_out <= key_cap, CSA2_ESHAPE, "csa2_index_score: n_out exceeds key_cap");
+  }
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(q) & 15) == 0 && (reinterpret_cast<uintptr_t>(keys) & 15) == 0,
+               CSA2_EINVAL, "csa2_index_score: q and keys must be 16-byte aligned");
+  return CSA2_OK;
+}
+
+csa2_status check_topk(const float* scores, int64_t n, int32_t len_div, int32_t k, const int32_t* pool,
+                       int32_t n_pool, int32_t blk, const int32_t* out, int32_t n_seq) {
+  CSA2_REQUIRE(n_seq >= 0, CSA2_ESHAPE, "csa2_topk: negative n_seq");
+  if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(scores && out, CSA2_EINVAL, "csa2_topk: null pointer");
+  CSA2_REQUIRE(k >= 1 && k <= CSA2_TOPK_MAX, CSA2_ESHAPE, "csa2_topk: k must be in [1, 2048]");
+  CSA2_REQUIRE(n >= 0 && n <= CSA2_TOPK_NMAX, CSA2_ESHAPE, "csa2_topk: n must be in [0, 262144]");
+  CSA2_REQUIRE(len_div > 0, CSA2_EINVAL, "csa2_topk: len_div must be positive");
+  if (pool) {
+    CSA2_REQUIRE(n_pool > 0 && blk > 0 && n == (int64_t)n_pool * blk, CSA2_ESHAPE,
+                 "csa2_topk: pool mode needs n == n_pool * blk");
+  }
+  return CSA2_OK;
+}
+
+csa2_status check_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                       const int32_t* idx, int32_t k_idx, const uint16_t* swa, const int32_t* swa_len,
+                       int32_t swa_max, const float* out, const void* ws, size_t ws_bytes) {
+  CSA2_REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ESHAPE, "csa2_sparse_attn: n_q must be in [0, 65535]");
+  if (n_q == 0) return CSA2_OK;
+  CSA2_REQUIRE(q && kv && swa_len && out && ws, CSA2_EINVAL, "csa2_sparse_attn: null pointer");
+  CSA2_REQUIRE(k_idx >= 0 && swa_max >= 0 && k_idx + swa_max >= 1, CSA2_ESHAPE,
+               "csa2_sparse_attn: need k_idx + swa_max >= 1");
+  CSA2_REQUIRE(k_idx == 0 || idx, CSA2_EINVAL, "csa2_sparse_attn: null idx");
+  CSA2_REQUIRE(swa_max == 0 || swa, CSA2_EINVAL, "csa2_sparse_attn: null swa");
+  CSA2_REQUIRE(swa_max <= 4096 && (int64_t)k_idx + swa_max <= 128 * 64, CSA2_ESHAPE,
+               "csa2_sparse_attn: k_idx + swa_max must be <= 8192 and swa_max <= 4096");
+  CSA2_REQUIRE(q_per_seq >= 1, CSA2_EINVAL, "csa2_sparse_attn: q_per_seq must be >= 1");
+  csa2_status st = check_kv(*kv, "csa2_sparse_attn");
+  if (st != CSA2_OK) return st;
+  CSA2_REQUIRE((n_q + q_per_seq - 1) / q_per_seq <= kv->n_seq, CSA2_ESHAPE,
+               "csa2_sparse_attn: queries address more cache sequences than kv.n_seq");
+  CSA2_REQUIRE(ws_bytes >= attn_workspace_bytes(n_q, k_idx, swa_max), CSA2_ECAPACITY,
+               "csa2_sparse_attn: workspace too small");
+  const uintptr_t a = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv->codes) |
+                      reinterpret_cast<uintptr_t>(swa) | reinterpret_cast<uintptr_t>(out) |
+                      reinterpret_cast<uintptr_t>(ws);
+  CSA2_REQUIRE((a & 15) == 0 && (reinterpret_cast<uintptr_t>(kv->scales) & 7) == 0, CSA2_EINVAL,
+               "csa2_sparse_attn: q, codes, swa, out, ws need 16-byte and scales 8-byte alignment");
+  return CSA2_OK;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" {
+
+const char* csa2_last_error(void) { return g_error.c_str(); }
+
+int32_t csa2_abi_version(void) { return 1; }
+
+csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_rows >= 0, CSA2_ESHAPE, "csa2_quant_rows: negative n_rows");
+  if (n_rows == 0) return CSA2_OK;
+  CSA2_REQUIRE(src && codes && scales, CSA2_EINVAL, "csa2_quant_rows: null pointer");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(codes) & 3) == 0,
+               CSA2_EINVAL, "csa2_quant_rows: src needs 16-byte and codes 4-byte alignment");
+  return quant_rows_launch(src, n_rows, codes, scales, as_stream(stream));
+}
+
+csa2_status csa2_quant_append(const uint16_t* src, csa2_fp4_kv kv, int32_t* lens, int32_t* err_flag,
+                              void* stream) {
+  clear_error();
+  CSA2_REQUIRE(kv.n_seq >= 0 && kv.n_seq <= 65535, CSA2_ESHAPE, "csa2_quant_append: bad n_seq");
+  if (kv.n_seq == 0) return CSA2_OK;
+  csa2_status st = check_kv(kv, "csa2_quant_append");
+  if (st != CSA2_OK) return st;
+  CSA2_REQUIRE(src && lens, CSA2_EINVAL, "csa2_quant_append: null pointer");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(kv.codes) & 3) == 0,
+               CSA2_EINVAL, "csa2_quant_append: src needs 16-byte and codes 4-byte alignment");
+  return quant_append_launch(src, kv, lens, err_flag, as_stream(stream));
+}
+
+csa2_status csa2_index_score(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, int32_t len_div, const int32_t* pool, int32_t n_pool,
+                             int32_t blk, float* scores, int64_t n_out, int32_t n_seq, void* stream) {
+  clear_error();
+  csa2_status st = check_index_score(q, keys, key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, n_seq);
+  if (st != CSA2_OK || n_seq == 0) return st;
+  return index_score_launch(q, w, keys, key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, n_seq,
+                            as_stream(stream));
+}
+
+csa2_status csa2_topk(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
+                      const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, int32_t n_seq,
+                      void* stream) {
+  clear_error();
+  csa2_status st = check_topk(scores, n, len_div, k, pool, n_pool, blk, out, n_seq);
+  if (st != CSA2_OK || n_seq == 0) return st;
+  return topk_launch(scores, n, lens, len_div, k, pool, n_pool, blk, out, n_seq, as_stream(stream));
+}
+
+size_t csa2_sparse_attn_workspace_size(int32_t n_q, int32_t k_idx, int32_t swa_max) {
+  if (n_q <= 0 || k_idx < 0 || swa_max < 0 || k_idx + swa_max < 1) return 0;
+  return attn_workspace_bytes(n_q, k_idx, swa_max);
+}
+
+csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                             const int32_t* idx, int32_t k_idx, const uint16_t* swa,
+                             int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                             float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_len, swa_max, out, ws, ws_bytes);
+  if (st != CSA2_OK || n_q == 0) return st;
+  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+                     sm_scale, out, ws, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+"""Device-resident inputs of a decode workload (see synth/configs.py).
+
+Every tensor is generated on the GPU by the seeded generator (synth's fill
+kernel) and the FP4 caches are quantised on the GPU with csa2_quant_rows,
+so a 1M-position, 16-sequence, 5-tensor cache (24 GB) is built in seconds
+without host traffic.  The oracle side regenerates any row on the host from
+the same seeds.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+import synth
+from synth.configs import DecodeConfig
+
+from . import FP4KV, LATENT, Layer, Sched, quant_rows
+
+
+def _fill(shape, tid_kind, seed=0):
+    """A new bf16 tensor [n_seq][rows][dim] holding rows 0.. of each sequence."""
+    tid, kind = tid_kind
+    t = torch.empty(shape, dtype=torch.int16, device="cuda")
+    synth.fill_rows_device(t, seed, tid, kind)
+    return t
+
+
+def fill_kv_rows(kv: FP4KV, b: int, row0: int, n_rows: int, tid_kind, seed: int, chunk: int = 1 << 19,
+                 staging: Optional[torch.Tensor] = None):
+    """Generate bf16 source rows row0.. of sequence b and quantise them into kv."""
+    tid, kind = tid_kind
+    if staging is None:
+        staging = torch.empty(min(chunk, n_rows), LATENT, dtype=torch.int16, device="cuda")
+    done = 0
+    while done < n_rows:
+        m = min(staging.shape[0], n_rows - done)
+        st = staging[:m]
+        synth.fill_rows_device(st.view(1, m, LATENT), seed, tid, kind, b0=b, row0=row0 + done)
+        quant_rows(st, kv.codes[b, row0 + done:row0 + done + m], kv.scales[b, row0 + done:row0 + done + m])
+        done += m
+
+
+@dataclass
+class DecodeInputs:
+    cfg: DecodeConfig
+    steps: int
+    kv: List[FP4KV]
+    lens: torch.Tensor
+    idx_k: torch.Tensor
+    blk_k: Optional[torch.Tensor]
+    swa: List[torch.Tensor]
+    swa_len: torch.Tensor
+    out: List[torch.Tensor]
+    idx_q: List[List[Optional[torch.Tensor]]] = field(default_factory=list)   # [set][layer]
+    main_q: List[List[torch.Tensor]] = field(default_factory=list)            # [set][layer]
+    new_row: List[Optional[torch.Tensor]] = field(default_factory=list)       # [set]
+
+    @property
+    def cap(self):
+        return self.cfg.cap(self.steps)
+
+    def reset_lens(self):
+        self.lens.fill_(self.cfg.L0)
+
+
+def build_decode_inputs(cfg: DecodeConfig, steps: int) -> DecodeInputs:
+    """Allocate and fill every input of `steps` decode steps of cfg."""
+    n, seed = cfg.n_seq, cfg.seed
+    cap, nl = cfg.cap(steps), len(cfg.layers)
+    kv = []
+    staging = torch.empty(min(1 << 19, cap), LATENT, dtype=torch.int16, device="cuda")
+    for k in range(cfg.n_kv):
+        t = FP4KV.empty(n, cap)
+        rows = cfg.L0 if (cfg.append and k == cfg.append_kv) else cap
+        for b in range(n):
+            fill_kv_rows(t, b, 0, rows, cfg.kv_src(k), seed, staging=staging)
+        kv.append(t)
+    del staging
+    idx_k = _fill((n, cap, 64), cfg.idx_k(), seed=seed)
+    blk_k = _fill((n, cfg.blk_cap(steps), 64), cfg.blk_k(), seed=seed) if cfg.hierarchical else None
+    swa = [_fill((n, cfg.swa, LATENT), cfg.swa_rows(l), seed=seed) for l in range(nl)]
+    inp = DecodeInputs(cfg=cfg, steps=steps, kv=kv,
+                       lens=torch.full((n,), cfg.L0, dtype=torch.int32, device="cuda"),
+                       idx_k=idx_k, blk_k=blk_k, swa=swa,
+                       swa_len=torch.full((n,), cfg.swa, dtype=torch.int32, device="cuda"),
+                       out=[torch.empty(n, 16, LATENT, dtype=torch.float32, device="cuda") for _ in range(nl)])
+    for s in range(cfg.q_sets):
+        inp.idx_q.append([_fill((n, 8, 64), cfg.idx_q(l, s), seed=seed) if cfg.layers[l][0] != 2 else None
+                          for l in range(nl)])
+        inp.main_q.append([_fill((n, 16, LATENT), cfg.main_q(l, s), seed=seed) for l in range(nl)])
+        inp.new_row.append(_fill((n, 1, LATENT), cfg.new_row(s), seed=seed) if cfg.append else None)
+    torch.cuda.synchronize()
+    return inp
+
+
+def make_sched(inp: DecodeInputs) -> Sched:
+    cfg = inp.cfg
+    layers = [Layer(m, k, bool(h)) for m, k, h in cfg.layers]
+    return Sched(layers, n_seq=cfg.n_seq, key_cap=inp.cap,
+                 blk_cap=cfg.blk_cap(inp.steps) if cfg.hierarchical else 0, topk=cfg.topk,
+                 pool_blocks=cfg.pool_blocks, blk=cfg.blk, swa_max=cfg.swa)
+
+
+def step_ios(sched: Sched, inp: DecodeInputs):
+    """One prepared step descriptor per query set (step s uses ios[s % q_sets])."""
+    return [sched.prepare(kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, main_q=inp.main_q[s], swa=inp.swa,
+                          swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q[s], blk_k=inp.blk_k,
+                          new_row=inp.new_row[s], append_kv=inp.cfg.append_kv)
+            for s in range(inp.cfg.q_sets)]

@@ -1,0 +1,243 @@
+/*
+ * csa2.h -- C ABI of the CSA2 FP4-KV decode path for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The path (one decode step of a stack of CSA2 layers):
+ *   (a) append a 512-d latent row to the FP4 main KV cache (E2M1 values, one
+ *       E4M3 scale per 16 channels);
+ *   (b) score an indexer query against indexer keys;
+ *   (c) keep the Top-K positions, under the static Full / Reindex / Reuse
+ *       layer modes and the hierarchical pool of 2,048 blocks of 8;
+ *   (d) gather and dequantise the selected FP4 rows;
+ *   (e) attend over them together with the layer's bf16 128-row sliding
+ *       window, with online softmax.
+ *
+ * Citations name the page and its section:
+ *   [P1] "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M Context, FP4 KV
+ *        Cache, and Cross-Layer Attention Reuse" (thecryptopost.io)
+ *   [P3] "DeepSeek-V4.1 Flash: Pushing the Limits of KV Cache Compression"
+ *        (tldrocket.com)
+ *   [P4] "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression"
+ *        (agihunt.info paper page 2609.19969), summary
+ *
+ * Conventions for every call:
+ *   - Pointers to tensors are DEVICE pointers owned by the caller; the
+ *     library never frees them.  Arrays of pointers inside descriptors are
+ *     host memory.  Shapes are given in the comments, row-major, last index
+ *     contiguous.  bf16 values travel as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on that stream, never synchronises the
+ *     host, and allocates nothing, except csa2_sched_create/_destroy and
+ *     csa2_sched_check.  Calls are therefore capturable in a HIP graph.
+ *   - Return value: CSA2_OK (0) or a negative csa2_status.  On error nothing
+ *     was enqueued and csa2_last_error() returns a message (thread-local).
+ *     Argument errors are detected on the host; device-side conditions
+ *     (appending past capacity) are reported through a device flag.
+ *   - Numerics: quantised bytes, scores of integer-valued indexer inputs and
+ *     selected indices are exact and deterministic; attention is computed
+ *     with bf16 MFMA inputs and fp32 accumulation.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t csa2_status;
+#define CSA2_OK 0
+#define CSA2_EINVAL (-1)    /* null pointer or invalid argument value */
+#define CSA2_ESHAPE (-2)    /* a size outside what the call supports */
+#define CSA2_ECAPACITY (-3) /* a buffer is too small */
+#define CSA2_EMODE (-4)     /* invalid layer table */
+#define CSA2_EHIP (-5)      /* the HIP runtime reported an error */
+#define CSA2_ENOMEM (-6)    /* device allocation failed (create only) */
+
+#define CSA2_LATENT 512     /* [P3]: 512-d latent shared by key and value */
+#define CSA2_GROUP 16       /* [P1 "FP4 KV, ..."]: one scale per 16 channels */
+#define CSA2_CODE_BYTES 256 /* 512 E2M1 codes, two per byte */
+#define CSA2_SCALE_BYTES 32 /* 32 E4M3 scales */
+#define CSA2_HEADS 16       /* main query heads */
+#define CSA2_IDX_HEADS 8    /* indexer heads */
+#define CSA2_IDX_DIM 64     /* indexer head dimension */
+#define CSA2_SWA_MAX 128    /* [P1 "Causal Encoder-Decoder..."]: 128-token window */
+#define CSA2_TOPK_MAX 2048  /* largest k of one csa2_topk call */
+#define CSA2_TOPK_NMAX 262144 /* most candidates per sequence of one csa2_topk call */
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* csa2_last_error(void);
+/* Version of this ABI (bumped on any signature change). */
+int32_t csa2_abi_version(void);
+
+/* ------------------------------------------------------------ FP4 cache
+ * One FP4 main-KV tensor [P1 "FP4 KV, Bounded Replay, and Other
+ * Extensions"]: E2M1 elements with one E4M3 (OCP E4M3FN) scale per 16
+ * channels, no second-level scale.  Planar layout:
+ *   codes  [n_seq][cap][256] uint8: byte j holds channel 2j (low nibble)
+ *                                   and channel 2j+1 (high nibble);
+ *                                   nibble = sign<<3 | E2M1 magnitude code
+ *   scales [n_seq][cap][32]  uint8: E4M3 scale of channels 16g..16g+15
+ * 288 bytes per row.  Value of channel d = E2M1(code_d) * E4M3(scale_{d/16}). */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t cap;   /* rows per sequence */
+  int32_t n_seq; /* sequences */
+} csa2_fp4_kv;
+
+/* Quantise n_rows bf16 rows src [n_rows][512] into codes [n_rows][256] and
+ * scales [n_rows][32] (the caller offsets the pointers to the first
+ * destination row).  Per 16-channel group with absolute maximum a: scale =
+ * E4M3 round-to-nearest-even of a/6, saturating at 448 (the NVFP4 recipe the
+ * pages say is followed, [P1 "FP4 KV, ..."]); each channel's magnitude is
+ * the round-to-nearest-even of |x|/scale onto {0,.5,1,1.5,2,3,4,6},
+ * saturating at 6, with ties to the even code; the sign bit is copied from
+ * x (also for magnitude 0); a zero scale gives magnitude 0.  Exact for
+ * every finite bf16 input. */
+csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                            void* stream);
+
+/* Step (a): append one new latent row per sequence.  For each sequence b:
+ * row = lens[b]; if row < kv.cap, quantise src[b] (as csa2_quant_rows) into
+ * row `row` of sequence b and set lens[b] = row + 1; otherwise leave the
+ * cache and lens[b] unchanged and OR 1 into *err_flag (if err_flag is not
+ * NULL).  src [kv.n_seq][512] bf16; lens [kv.n_seq] int32 (device). */
+csa2_status csa2_quant_append(const uint16_t* src, csa2_fp4_kv kv, int32_t* lens, int32_t* err_flag,
+                              void* stream);
+
+/* Step (b): indexer scores [P1 "Compressed Sparse Attention 2 (CSA2)"]:
+ * a layer scores its indexer Q against indexer K (Full: all positions or a
+ * block pool; Reindex: rescoring with its own Q).  The pages print no
+ * formula; the score of key k is
+ *     score = sum_h w_h * max(0, q_h . k),   h < 8 indexer heads,
+ * (w == NULL means w_h = 1; with w the sum is taken in binary32 as
+ * ((w0r0 + w1r1) + w2r2) + w3r3, the same for heads 4..7, then lo + hi).
+ * Exact when q, k are integer-valued with |partial sums| < 2^24.
+ *   q      [n_seq][8][64] bf16; w [n_seq][8] f32 or NULL
+ *   keys   [n_seq][key_cap][64] bf16
+ *   lens   [n_seq] int32 (device): positions per sequence
+ *   scores [n_seq][n_out] f32 out; a slot that is not a candidate gets -inf.
+ * Flat mode (pool == NULL): slot i scores key row i; it is a candidate iff
+ *   i < ceil(lens[b] / len_div) (len_div = 1 for position keys, 8 for the
+ *   keys of blocks of 8 positions).  Requires n_out <= key_cap.
+ * Pool mode (pool != NULL): pool [n_seq][n_pool] int32 block ids (-1 =
+ *   empty); n_out must be n_pool * blk; slot p scores key row
+ *   pool[b][p/blk]*blk + p%blk, a candidate iff the block id is >= 0 and
+ *   the row is < lens[b] and < key_cap. */
+csa2_status csa2_index_score(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, int32_t len_div, const int32_t* pool, int32_t n_pool,
+                             int32_t blk, float* scores, int64_t n_out, int32_t n_seq, void* stream);
+
+/* Step (c): Top-k [P1 "Compressed Sparse Attention 2 (CSA2)"]: a fresh
+ * Top-512 (and the 2,048-block pool of the hierarchical indexer).  Among the
+ * candidate slots of scores [n_seq][n] -- slots i < ceil(lens[b]/len_div)
+ * if lens != NULL (else all n) whose score is neither -inf nor NaN --
+ * keep the min(k, #candidates) best by (score descending, slot ascending:
+ * ties go to the lower position), and write their ids in ascending order to
+ * out [n_seq][k], padding with -1.  The id of slot i is i, or with a pool
+ * pool[b][i/blk]*blk + i%blk (pool [n_seq][n_pool], n == n_pool*blk; pool
+ * ids ascending makes slot order = id order).  -0 and +0 are equal.
+ * Limits: 1 <= k <= CSA2_TOPK_MAX, n <= CSA2_TOPK_NMAX. */
+csa2_status csa2_topk(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
+                      const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, int32_t n_seq,
+                      void* stream);
+
+/* Steps (d)+(e): sparse + SWA attention of n_q queries.
+ * [P1 "Compressed Sparse Attention 2 (CSA2)"]: each layer attends with its
+ * own main Q over the selected main-KV rows; [P1 "Causal Encoder-Decoder:
+ * Half the Prefill"]: a 128-token sliding window runs in every layer; [P3]:
+ * key and value are the same 512-d latent.  For query b the attended set
+ * is the FP4 rows idx[b][i] (0 <= id < kv->cap; other entries are skipped)
+ * of cache sequence b / q_per_seq, dequantised (step d), followed by SWA
+ * rows swa[b*swa_q_stride_rows + j] for j < swa_len[b]; one softmax over the
+ * whole set per head:  o_h = sum_j softmax_j(sm_scale * q_h . x_j) x_j.
+ * An empty set gives o_h = 0.
+ *   q   [n_q][16][512] bf16;  idx [n_q][k_idx] int32
+ *   swa [*][512] bf16 rows;   swa_len [n_q] int32 (device), each <= swa_max
+ *   out [n_q][16][512] f32
+ *   ws  device workspace of csa2_sparse_attn_workspace_size(...) bytes,
+ *       256-byte aligned, contents need no initialisation.
+ * Limits: k_idx + swa_max >= 1, swa_max <= 4096. */
+size_t csa2_sparse_attn_workspace_size(int32_t n_q, int32_t k_idx, int32_t swa_max);
+csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                             const int32_t* idx, int32_t k_idx, const uint16_t* swa,
+                             int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                             float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ scheduler
+ * Static layer-mode table [P1 "Compressed Sparse Attention 2 (CSA2)"]:
+ *   Full    computes its own selection: a fresh Top-k over all positions,
+ *           or (hierarchical) Top-pool_blocks blocks by block key, then a
+ *           Top-k over the pool's positions;
+ *   Reindex rescores with its own indexer Q the keys of the last Full layer
+ *           (its pool when that layer is hierarchical, else all positions);
+ *   Reuse   reuses the latest Full/Reindex indices and skips the indexer.
+ * Every layer attends with its own main Q and SWA window over the main-KV
+ * tensor kv_id.  Layer 0 must be Full; Reindex needs an earlier Full; Reuse
+ * needs an earlier Full or Reindex (else CSA2_EMODE). */
+#define CSA2_FULL 0
+#define CSA2_REINDEX 1
+#define CSA2_REUSE 2
+
+typedef struct {
+  int32_t mode;         /* CSA2_FULL / CSA2_REINDEX / CSA2_REUSE */
+  int32_t kv_id;        /* main-KV tensor attended over (index into io.kv) */
+  int32_t hierarchical; /* Full only: 1 = select through the block pool */
+} csa2_layer;
+
+typedef struct {
+  int32_t n_seq;
+  int32_t n_layers;
+  const csa2_layer* layers; /* host [n_layers], copied at create */
+  int64_t key_cap;          /* rows per sequence of indexer K (>= every lens) */
+  int64_t blk_cap;          /* rows per sequence of block keys (hierarchical) */
+  int32_t topk;             /* positions kept (512) */
+  int32_t pool_blocks;      /* blocks kept by a hierarchical Full layer (2048) */
+  int32_t blk;              /* positions per block (8) */
+  int32_t swa_max;          /* rows per sequence of each SWA buffer (128) */
+  float sm_scale;           /* softmax scale (READING: 1/sqrt(512)) */
+} csa2_sched_desc;
+
+/* Per-step inputs/outputs.  Arrays marked "host" hold device pointers. */
+typedef struct {
+  int32_t n_kv;
+  const csa2_fp4_kv* kv;        /* host [n_kv]; each n_seq = desc.n_seq */
+  int32_t* lens;                /* [n_seq] positions, shared by all tensors */
+  const uint16_t* new_row;      /* [n_seq][512] bf16 row to append, or NULL */
+  int32_t append_kv;            /* tensor that receives the appended row */
+  const uint16_t* idx_k;        /* [n_seq][key_cap][64] bf16 indexer K */
+  const uint16_t* blk_k;        /* [n_seq][blk_cap][64] bf16 block keys, or NULL */
+  const uint16_t* const* idx_q; /* host [n_layers]: [n_seq][8][64] (Reuse: ignored) */
+  const float* const* idx_w;    /* host [n_layers] of [n_seq][8] f32 or NULL; NULL array = all 1 */
+  const uint16_t* const* main_q; /* host [n_layers]: [n_seq][16][512] bf16 */
+  const uint16_t* const* swa;   /* host [n_layers]: [n_seq][swa_max][512] bf16 */
+  const int32_t* swa_len;       /* [n_seq] valid SWA rows (<= swa_max) */
+  float* const* out;            /* host [n_layers]: [n_seq][16][512] f32 */
+} csa2_step_io;
+
+typedef struct csa2_sched csa2_sched;
+
+/* Validate the table and allocate the scheduler's device workspace. */
+csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out);
+/* One decode step on `stream`: the append (if io.new_row), then every layer
+ * in table order.  Asynchronous; capturable in a HIP graph. */
+csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* stream);
+/* Device pointer to the indices [n_seq][topk] int32 that layer `layer`
+ * attended over in the last step (Reuse layers share their source's
+ * buffer), or NULL if out of range. */
+const int32_t* csa2_sched_indices(const csa2_sched* s, int32_t layer);
+/* Device pointer to the pool [n_seq][pool_blocks] int32 built by the last
+ * hierarchical Full layer, or NULL if the table has none. */
+const int32_t* csa2_sched_pool(const csa2_sched* s);
+/* Blocking: read and clear the device error flags (bit 0: an append found a
+ * full cache).  Returns CSA2_OK and stores the flags in *flags. */
+csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags);
+void csa2_sched_destroy(csa2_sched* s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,68 @@
+"""TEST INFRASTRUCTURE: oracle results of a decode workload (synth/configs.py).
+
+Regenerates on the host, from the same seeds as the device builder, exactly
+the inputs one decode step of one sequence reads, and runs the oracle's
+layer walk on them.  Only tests, the smoke check and the benchmark's CPU
+baseline use it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+from synth.configs import REUSE, DecodeConfig
+
+from . import Layer, LayerInputs, SeqState, decode_layers, quant_rows
+
+SM_SCALE = 512 ** -0.5
+
+
+def _gen(cfg: DecodeConfig, tid_kind, b: int, rows, dim: int) -> np.ndarray:
+    tid, kind = tid_kind
+    return synth.gen_rows(cfg.seed, tid, kind, [b], np.asarray(rows, dtype=np.int64), dim)[0]
+
+
+def kv_source_rows(cfg: DecodeConfig, kv_id: int, b: int, ids: np.ndarray) -> np.ndarray:
+    """bf16 latent rows at positions ids (all >= 0) of tensor kv_id, sequence b:
+    the pre-filled source row, or for an appended position the row appended by
+    the step that wrote it."""
+    ids = np.asarray(ids, dtype=np.int64)
+    out = _gen(cfg, cfg.kv_src(kv_id), b, ids, 512)
+    if cfg.append and kv_id == cfg.append_kv:
+        for i, p in enumerate(ids):
+            if p >= cfg.L0:
+                out[i] = _gen(cfg, cfg.new_row(int(p - cfg.L0)), b, [0], 512)[0]
+    return out
+
+
+def seq_state(cfg: DecodeConfig, b: int, step: int) -> SeqState:
+    L = cfg.lens_at(step)
+    tok = _gen(cfg, cfg.idx_k(), b, np.arange(L), 64)
+    blk = _gen(cfg, cfg.blk_k(), b, np.arange(-(-L // cfg.blk)), 64) if cfg.hierarchical else None
+
+    def kv_rows(kv_id, ids):
+        ids = np.asarray(ids, dtype=np.int64)
+        src = np.zeros((len(ids), 512), np.uint16)
+        ok = ids >= 0
+        if ok.any():
+            src[ok] = kv_source_rows(cfg, kv_id, b, ids[ok])
+        return quant_rows(src)
+
+    return SeqState(L=L, tok_keys=tok, blk_keys=blk, kv_rows=kv_rows)
+
+
+def layer_inputs(cfg: DecodeConfig, b: int, step: int):
+    ins = []
+    for l, (mode, _, _) in enumerate(cfg.layers):
+        iq = None if mode == REUSE else _gen(cfg, cfg.idx_q(l, step), b, np.arange(8), 64)
+        mq = _gen(cfg, cfg.main_q(l, step), b, np.arange(16), 512)
+        sw = _gen(cfg, cfg.swa_rows(l), b, np.arange(cfg.swa), 512)
+        ins.append(LayerInputs(idx_q=iq, main_q=mq, swa=sw, swa_len=cfg.swa))
+    return ins
+
+
+def reference_step(cfg: DecodeConfig, step: int, b: int, attend=True):
+    """Oracle LayerResults of decode step `step` (0-based) for sequence b."""
+    layers = [Layer(m, k, bool(h)) for m, k, h in cfg.layers]
+    return decode_layers(layers, seq_state(cfg, b, step), layer_inputs(cfg, b, step), SM_SCALE,
+                         k=cfg.topk, n_pool=cfg.pool_blocks, attend=attend)

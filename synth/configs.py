@@ -1,0 +1,100 @@
+"""Workload descriptions of the CSA2 decode path: shapes, layer-mode tables
+and the synthetic tensor behind every input.  Pure data, shared by the device
+input builder and the oracle side; no step of the method lives here.
+
+Layer modes use the ABI's numbering: 0 = Full, 1 = Reindex, 2 = Reuse.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Tuple
+
+from . import (INT9, NORMAL, KIND_BLK_K, KIND_IDX_K, KIND_IDX_Q, KIND_KV_SRC, KIND_MAIN_Q,
+               KIND_NEW_ROW, KIND_SWA, tensor_id)
+
+FULL, REINDEX, REUSE = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    n_seq: int
+    L0: int                                   # positions before the first step
+    layers: Tuple[Tuple[int, int, int], ...]  # (mode, kv_id, hierarchical)
+    n_kv: int = 1
+    append: bool = False                      # one appended row per sequence per step
+    append_kv: int = 0
+    topk: int = 512
+    pool_blocks: int = 2048
+    blk: int = 8
+    swa: int = 128
+    q_sets: int = 4                           # step s uses query set s % q_sets
+    seed: int = 0
+
+    def cap(self, steps: int) -> int:
+        """Rows per sequence of every main-KV tensor and of indexer K."""
+        return self.L0 + (steps if self.append else 0)
+
+    def blk_cap(self, steps: int) -> int:
+        return -(-self.cap(steps) // self.blk)
+
+    @property
+    def hierarchical(self) -> bool:
+        return any(m == FULL and h for m, _, h in self.layers)
+
+    def lens_at(self, step: int) -> int:
+        """Positions seen by the layers of step `step` (after its append)."""
+        return self.L0 + (step + 1 if self.append else 0)
+
+    def with_(self, **kw) -> "DecodeConfig":
+        return replace(self, **kw)
+
+    # ---- synthetic tensors (tensor id, value kind)
+    def kv_src(self, kv_id: int):
+        return tensor_id(KIND_KV_SRC, kv_id), NORMAL
+
+    def new_row(self, step: int):
+        return tensor_id(KIND_NEW_ROW, self.append_kv, step % self.q_sets), NORMAL
+
+    def idx_k(self):
+        return tensor_id(KIND_IDX_K), INT9
+
+    def blk_k(self):
+        return tensor_id(KIND_BLK_K), INT9
+
+    def idx_q(self, layer: int, step: int):
+        return tensor_id(KIND_IDX_Q, layer, step % self.q_sets), INT9
+
+    def main_q(self, layer: int, step: int):
+        return tensor_id(KIND_MAIN_Q, layer, step % self.q_sets), NORMAL
+
+    def swa_rows(self, layer: int):
+        return tensor_id(KIND_SWA, layer, 0), NORMAL
+
+
+def _group(mode0: int, kv: int, hier: int, n_reuse: int):
+    return ((mode0, kv, hier),) + ((REUSE, kv, 0),) * n_reuse
+
+
+# One Full CSA2 layer over 4,096 cached positions, one decode query.
+SINGLE_LAYER_4K = DecodeConfig(name="single Full layer, 4K positions, batch 1", n_seq=1, L0=4096,
+                               layers=((FULL, 0, 0),), q_sets=1)
+
+# Decoder group at ratio 1: Full + 3 Reuse over 64K positions, batch 32, one append per step.
+GROUP_64K = DecodeConfig(name="decoder group Full+3 Reuse, 64K positions, batch 32", n_seq=32,
+                         L0=65536, layers=_group(FULL, 0, 0, 3), append=True)
+
+# Hierarchical Full + Reindex over 1M positions, batch 8.
+HIER_1M = DecodeConfig(name="hierarchical Full + Reindex, 1M positions, batch 8", n_seq=8,
+                       L0=1 << 20, layers=((FULL, 0, 1), (REINDEX, 0, 0)))
+
+# 20-layer decoder schedule at 1M, batch 16: group 1 = Full + 3 Reuse, groups
+# 2-5 = Reindex + 3 Reuse, one FP4 main-KV tensor per group, one append per
+# sequence per step into the Full group's tensor.
+DECODER_20L_1M = DecodeConfig(
+    name="20-layer decoder schedule, 1M positions, batch 16", n_seq=16, L0=1 << 20,
+    layers=_group(FULL, 0, 1, 3) + sum((_group(REINDEX, g, 0, 3) for g in range(1, 5)), ()),
+    n_kv=5, append=True)
+
+DECODE_CONFIGS = {"single_4k": SINGLE_LAYER_4K, "group_64k": GROUP_64K, "hier_1m": HIER_1M,
+                  "decoder20_1m": DECODER_20L_1M}

@@ -1,0 +1,106 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point declared in include/csa2.h, and rejects bad arguments on the host
+before anything is enqueued (no call here reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def csa2():
+    import fp4_kv_cache_quant_amd as m
+    return m
+
+
+def test_every_declared_symbol_is_exported(csa2):
+    names = _declared_symbols()
+    assert len(names) >= 14, names
+    lib = ctypes.CDLL(csa2.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version(csa2):
+    assert csa2.abi_version() == 1
+
+
+def _err(csa2):
+    return csa2._last_error().decode()
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def test_topk_rejects_bad_k_and_n(csa2):
+    assert csa2._topk(FAKE, 100, None, 1, 0, None, 0, 8, FAKE, 1, None) == -2
+    assert "k must be" in _err(csa2)
+    assert csa2._topk(FAKE, 100, None, 1, 4096, None, 0, 8, FAKE, 1, None) == -2
+    assert csa2._topk(FAKE, 300000, None, 1, 512, None, 0, 8, FAKE, 1, None) == -2
+    assert csa2._topk(FAKE, 100, None, 1, 512, FAKE, 10, 8, FAKE, 1, None) == -2  # n != n_pool*blk
+    assert csa2._topk(None, 100, None, 1, 512, None, 0, 8, FAKE, 1, None) == -1
+    assert csa2._topk(FAKE, 100, None, 0, 512, None, 0, 8, FAKE, 1, None) == -1  # len_div
+    assert csa2._topk(None, 100, None, 1, 512, None, 0, 8, None, 0, None) == 0   # n_seq = 0: no-op
+
+
+def test_index_score_rejects_bad_shapes(csa2):
+    assert csa2._index_score(FAKE, None, FAKE, 100, FAKE, 1, None, 0, 8, FAKE, 200, 1, None) == -2
+    assert "exceeds key_cap" in _err(csa2)
+    assert csa2._index_score(FAKE, None, FAKE, 100, FAKE, 1, FAKE, 10, 8, FAKE, 81, 1, None) == -2
+    assert csa2._index_score(FAKE + 2, None, FAKE, 100, FAKE, 1, None, 0, 8, FAKE, 50, 1, None) == -1
+    assert "aligned" in _err(csa2)
+    assert csa2._index_score(FAKE, None, None, 100, FAKE, 1, None, 0, 8, FAKE, 50, 1, None) == -1
+
+
+def test_attention_rejects_small_workspace_and_bad_sizes(csa2):
+    kv = csa2._FP4KV(FAKE, FAKE, 1000, 1)
+    need = csa2.sparse_attn_workspace_size(1, 512, 128)
+    assert need > 0
+    args = dict(q=FAKE, n_q=1, q_per_seq=1, idx=FAKE, k_idx=512, swa=FAKE, st=128, swa_len=FAKE, swa_max=128)
+
+    def call(ws_bytes, **kw):
+        a = {**args, **kw}
+        return csa2._attn(a["q"], a["n_q"], ctypes.byref(kv), a["q_per_seq"], a["idx"], a["k_idx"], a["swa"],
+                          a["st"], a["swa_len"], a["swa_max"], 0.04, FAKE, FAKE, ws_bytes, None)
+
+    assert call(need - 1) == -3 and "workspace" in _err(csa2)
+    assert call(need, swa_max=5000) == -2
+    assert call(need, k_idx=0, swa_max=0) == -2
+    assert call(need, n_q=2) == -2  # two queries, one cache sequence
+    assert call(need, q=FAKE + 8) == -1
+
+
+def test_quant_calls_reject_bad_arguments(csa2):
+    assert csa2._quant_rows(FAKE, -1, FAKE, FAKE, None) == -2
+    assert csa2._quant_rows(FAKE + 4, 3, FAKE, FAKE, None) == -1
+    assert csa2._quant_rows(None, 0, None, None, None) == 0
+    bad = csa2._FP4KV(FAKE, FAKE, 0, 1)
+    assert csa2._quant_append(FAKE, bad, FAKE, None, None) == -2
+
+
+def test_scheduler_rejects_invalid_tables(csa2):
+    L = csa2.Layer
+    with pytest.raises(csa2.Csa2Error) as e:
+        csa2.Sched([L(csa2.REUSE)], n_seq=1, key_cap=100)
+    assert e.value.code == -4
+    with pytest.raises(csa2.Csa2Error) as e:
+        csa2.Sched([L(csa2.REINDEX)], n_seq=1, key_cap=100)
+    assert e.value.code == -4
+    with pytest.raises(csa2.Csa2Error) as e:
+        csa2.Sched([L(csa2.FULL), L(7)], n_seq=1, key_cap=100)
+    assert e.value.code == -4
+    with pytest.raises(csa2.Csa2Error) as e:  # flat selection over too many positions
+        csa2.Sched([L(csa2.FULL)], n_seq=1, key_cap=1 << 20)
+    assert e.value.code == -2
+    with pytest.raises(csa2.Csa2Error) as e:  # hierarchical: blocks must cover key_cap
+        csa2.Sched([L(csa2.FULL, 0, True)], n_seq=1, key_cap=1 << 20, blk_cap=1000)
+    assert e.value.code == -2

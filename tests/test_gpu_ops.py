@@ -1,0 +1,280 @@
+"""GPU parity of each C-ABI operation against the CPU oracle.
+
+Quantised bytes, scores (integer-valued inputs), selected indices and pool
+blocks must match bit-exactly; attention must be within rel. L2 1e-3 and max
+abs 5e-3 per (query, head) in fp32.  Both sides read the same seeded inputs
+from ``synth``; neither side's output feeds the other.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (SEED, SM_SCALE, assert_attention_close, dev, host_u16, kv_source, print_case)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa2():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_kv_cache_quant_amd as m
+    return m
+
+
+def _bf16_of(x):
+    return synth._f32_to_bf16_rne(np.asarray(x, np.float32))
+
+
+# ---------------------------------------------------------------- step (a)
+def _exhaustive_quant_rows():
+    """Rows covering (1) every finite non-negative bf16 value as a group's
+    amax (all 126 nonzero scale codes and the zero scale arise), and (2) for
+    every nonzero scale code, every bf16 magnitude up to that group's amax,
+    in both signs."""
+    mags = np.arange(0, 0x7F80, dtype=np.uint16)
+    groups = []
+    # (1) one value per group, other 15 channels hold a fixed pattern below it
+    for a in mags:
+        g = np.zeros(16, np.uint16)
+        g[0] = a
+        g[1] = a | 0x8000
+        groups.append(g)
+    # (2) amax = 6 * v(sc) exactly, so the scale is v(sc); 15 test magnitudes per group
+    mvals = synth.bf16_to_f32(mags).astype(np.float64)
+    for sc in range(1, 127):
+        top = 6.0 * oracle.e4m3_value(sc)
+        cand = mags[mvals <= top][::3]  # every third magnitude below amax
+        amax_bits = _bf16_of(top)
+        for i in range(0, len(cand), 15):
+            g = np.zeros(16, np.uint16)
+            g[0] = amax_bits
+            chunk = cand[i:i + 15]
+            signs = np.where(np.arange(len(chunk)) % 2 == 1, 0x8000, 0).astype(np.uint16)
+            g[1:1 + len(chunk)] = chunk | signs
+            groups.append(g)
+    groups = np.stack(groups)
+    pad = (-len(groups)) % 32
+    groups = np.concatenate([groups, np.zeros((pad, 16), np.uint16)])
+    return groups.reshape(-1, 512)
+
+
+def test_quant_rows_exhaustive_bit_exact(csa2):
+    src = _exhaustive_quant_rows()
+    print_case(f"quant_rows exhaustive rows={len(src)}")
+    n = len(src)
+    codes = torch.zeros(n, 256, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(n, 32, dtype=torch.uint8, device="cuda")
+    csa2.quant_rows(dev(src), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant_rows(src)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quant_rows_normal_and_edge_rows(csa2):
+    src = kv_source(0, 1, 3000)[0]
+    edge = np.zeros((6, 512), np.uint16)
+    edge[1] = 0x8000                                  # -0 everywhere
+    edge[2] = 0x7F7F                                  # largest finite bf16
+    edge[3, ::2], edge[3, 1::2] = 0x0001, 0x8001      # smallest subnormals
+    edge[4] = _bf16_of(np.tile([6, 5, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25], 64))  # exact midpoints
+    edge[5] = _bf16_of(np.linspace(-448 * 6, 448 * 6, 512))
+    src = np.concatenate([src, edge])
+    print_case(f"quant_rows normal+edge rows={len(src)}")
+    codes = torch.zeros(len(src), 256, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(len(src), 32, dtype=torch.uint8, device="cuda")
+    csa2.quant_rows(dev(src), codes, scales)
+    rc, rs = oracle.quant_rows(src)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quant_append_writes_row_lens_and_capacity_flag(csa2):
+    n_seq, cap = 3, 5
+    print_case("quant_append cap=5")
+    kv = csa2.FP4KV.empty(n_seq, cap)
+    lens = torch.tensor([0, 4, 5], dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    src = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_NEW_ROW), synth.NORMAL, range(n_seq), [0], 512)[:, 0]
+    csa2.quant_append(dev(src), kv, lens, err)
+    assert lens.cpu().tolist() == [1, 5, 5] and err.item() == 1
+    rc, rs = oracle.quant_rows(src)
+    codes, scales = kv.codes.cpu().numpy(), kv.scales.cpu().numpy()
+    assert np.array_equal(codes[0, 0], rc[0]) and np.array_equal(scales[0, 0], rs[0])
+    assert np.array_equal(codes[1, 4], rc[1]) and np.array_equal(scales[1, 4], rs[1])
+    assert not codes[2].any() and not codes[0, 1:].any() and not codes[1, :4].any()
+
+
+# ---------------------------------------------------------------- step (b)
+def _int_keys(tid, n_seq, n_rows, seed=SEED):
+    return synth.gen_rows(seed, tid, synth.INT9, range(n_seq), np.arange(n_rows), 64)
+
+
+@pytest.mark.parametrize("weights", [None, "int", "float"])
+def test_index_score_flat_exact(csa2, weights):
+    n_seq, key_cap = 3, 5000
+    lens = np.array([4096, 1, 4999], np.int32)
+    keys = _int_keys(synth.tensor_id(synth.KIND_IDX_K), n_seq, key_cap)
+    q = _int_keys(synth.tensor_id(synth.KIND_IDX_Q), n_seq, 8)
+    w = None
+    if weights == "int":
+        w = np.array([[1, 2, 0, 3, 1, 1, 4, 2]] * n_seq, np.float32)
+    elif weights == "float":
+        w = np.random.default_rng(7).standard_normal((n_seq, 8)).astype(np.float32)
+    print_case(f"index_score flat weights={weights}")
+    scores = torch.empty(n_seq, key_cap, dtype=torch.float32, device="cuda")
+    csa2.index_score(dev(q), dev(keys), dev(lens), scores, w=None if w is None else dev(w))
+    got = scores.cpu().numpy()
+    for b in range(n_seq):
+        ref = oracle.index_score(q[b], keys[b], np.arange(lens[b]), w=None if w is None else w[b])
+        assert np.array_equal(got[b, :lens[b]], ref)
+        assert np.all(got[b, lens[b]:] == -np.inf)
+
+
+def test_index_score_blocks_len_div_and_pool_mode(csa2):
+    n_seq, key_cap, blk = 2, 4000, 8
+    lens = np.array([3999, 1234], np.int32)
+    keys = _int_keys(synth.tensor_id(synth.KIND_IDX_K), n_seq, key_cap)
+    bkeys = _int_keys(synth.tensor_id(synth.KIND_BLK_K), n_seq, 500)
+    q = _int_keys(synth.tensor_id(synth.KIND_IDX_Q), n_seq, 8)
+    print_case("index_score blocks + pool")
+    bs = torch.empty(n_seq, 500, dtype=torch.float32, device="cuda")
+    csa2.index_score(dev(q), dev(bkeys), dev(lens), bs, len_div=blk)
+    got = bs.cpu().numpy()
+    for b in range(n_seq):
+        nb = (lens[b] + 7) // 8
+        assert np.array_equal(got[b, :nb], oracle.index_score(q[b], bkeys[b], np.arange(nb)))
+        assert np.all(got[b, nb:] == -np.inf)
+    rng = np.random.default_rng(3)
+    pool = np.full((n_seq, 64), -1, np.int32)
+    pool[0, :60] = np.sort(rng.choice(500, 60, replace=False))
+    pool[1, :64] = np.sort(rng.choice(160, 64, replace=False))  # some blocks beyond lens[1]
+    ps = torch.empty(n_seq, 64 * blk, dtype=torch.float32, device="cuda")
+    csa2.index_score(dev(q), dev(keys), dev(lens), ps, pool=dev(pool), blk=blk)
+    got = ps.cpu().numpy()
+    for b in range(n_seq):
+        for p in range(64 * blk):
+            blkid = pool[b, p // blk]
+            pos = blkid * blk + p % blk
+            if blkid < 0 or pos >= lens[b]:
+                assert got[b, p] == -np.inf
+            else:
+                assert got[b, p] == oracle.index_score(q[b], keys[b], [pos])[0]
+
+
+# ---------------------------------------------------------------- step (c)
+@pytest.mark.parametrize("n,k,levels,L", [
+    (4096, 512, 9000, 4096), (4096, 512, 3, 4096), (65537, 512, 50, 65537), (131073, 2048, 400, 131073),
+    (131085, 2048, 10 ** 6, 131073), (300, 512, 4, 300), (5000, 512, 1, 5000), (5000, 512, 2, 1),
+    (20000, 512, 1, 19999), (262144, 2048, 7, 262144)])
+def test_topk_matches_oracle(csa2, n, k, levels, L):
+    n_seq = 2
+    rng = np.random.default_rng(n + k + levels)
+    sc = rng.integers(0, levels, size=(n_seq, n)).astype(np.float32)
+    sc[1, ::97] = -np.inf                      # some non-candidates
+    lens = np.array([L, max(1, L // 2)], np.int32)
+    print_case(f"topk n={n} k={k} levels={levels} L={L}")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    csa2.topk(dev(sc), k, out, lens=dev(lens))
+    got = out.cpu().numpy()
+    for b in range(n_seq):
+        nv = min(n, lens[b])
+        ids = np.arange(nv)
+        ok = np.isfinite(sc[b, :nv])
+        ref = oracle.select(sc[b, :nv][ok], ids[ok], k)
+        assert np.array_equal(got[b], ref), b
+
+
+def test_topk_signed_scores_and_zero_signs(csa2):
+    rng = np.random.default_rng(11)
+    sc = rng.standard_normal((1, 10000)).astype(np.float32)
+    sc[0, :3000:3] = 0.0
+    sc[0, 1:3000:3] = -0.0
+    sc[0, 5000:5100] = np.nan
+    print_case("topk signed + zero signs")
+    for k in (512, 2048, 7000 // 4):
+        out = torch.empty(1, k, dtype=torch.int32, device="cuda")
+        csa2.topk(dev(sc), k, out)
+        ok = ~np.isnan(sc[0])
+        ref = oracle.select(sc[0][ok] + 0.0, np.arange(10000)[ok], k)
+        assert np.array_equal(out.cpu().numpy()[0], ref)
+
+
+def test_topk_pool_mapping(csa2):
+    n_seq, n_pool, blk, k = 2, 2048, 8, 512
+    rng = np.random.default_rng(5)
+    pool = np.stack([np.sort(rng.choice(131073, n_pool, replace=False)) for _ in range(n_seq)]).astype(np.int32)
+    pool[1, 2000:] = -1
+    sc = rng.integers(0, 30, size=(n_seq, n_pool * blk)).astype(np.float32)
+    sc[1, 2000 * blk:] = -np.inf
+    print_case("topk pool mapping")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    csa2.topk(dev(sc), k, out, pool=dev(pool), blk=blk)
+    got = out.cpu().numpy()
+    for b in range(n_seq):
+        ids = (pool[b][:, None].astype(np.int64) * blk + np.arange(blk)).ravel()
+        ok = np.isfinite(sc[b]) & (np.repeat(pool[b], blk) >= 0)
+        assert np.array_equal(got[b], oracle.select(sc[b][ok], ids[ok], k))
+
+
+# ------------------------------------------------------------ steps (d)+(e)
+def _device_cache(csa2, src):
+    """Quantise bf16 sources [n_seq][cap][512] on the device."""
+    n_seq, cap, _ = src.shape
+    kv = csa2.FP4KV.empty(n_seq, cap)
+    csa2.quant_rows(dev(src.reshape(-1, 512)), kv.codes, kv.scales)
+    return kv
+
+
+@pytest.mark.parametrize("k_idx,swa_lens", [(512, [128, 5, 0]), (512, [0, 0, 1]), (100, [128, 128, 7]),
+                                            (0, [128, 3, 64]), (2000, [128, 0, 20])])
+def test_sparse_attn_matches_oracle(csa2, k_idx, swa_lens):
+    n_q, cap = 3, 2500
+    src = kv_source(0, n_q, cap)
+    kv = _device_cache(csa2, src)
+    rng = np.random.default_rng(k_idx + sum(swa_lens))
+    idx = np.stack([np.sort(rng.choice(cap, k_idx, replace=False)) for _ in range(n_q)]).astype(np.int32) \
+        if k_idx else np.zeros((n_q, 0), np.int32)
+    if k_idx:
+        idx[1, k_idx // 2:] = -1              # padded selection
+        idx[2, :3] = idx[2, 3]                # duplicates attend twice
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q), synth.NORMAL, range(n_q), np.arange(16), 512)
+    swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA), synth.NORMAL, range(n_q), np.arange(128), 512)
+    swa_len = np.array(swa_lens, np.int32)
+    print_case(f"sparse_attn k_idx={k_idx} swa={swa_lens}")
+    out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+    csa2.sparse_attn(dev(q), kv, dev(idx) if k_idx else None, dev(swa), dev(swa_len), SM_SCALE, out)
+    got = out.cpu().numpy()
+    for b in range(n_q):
+        codes, scales = oracle.quant_rows(src[b])
+        ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa[b], swa_len[b], SM_SCALE)
+        if k_idx == 0 and swa_len[b] == 0:
+            assert np.all(got[b] == 0)
+        else:
+            assert_attention_close(got[b], ref, f"query {b}")
+
+
+def test_sparse_attn_all_positions_is_dense(csa2):
+    cap = 400
+    src = kv_source(1, 1, cap)
+    kv = _device_cache(csa2, src)
+    idx = np.arange(512, dtype=np.int32)[None]
+    idx[0, cap:] = -1
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 1), synth.NORMAL, [0], np.arange(16), 512)
+    swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 1), synth.NORMAL, [0], np.arange(128), 512)
+    print_case("sparse_attn dense")
+    out = torch.empty(1, 16, 512, dtype=torch.float32, device="cuda")
+    csa2.sparse_attn(dev(q), kv, dev(idx), dev(swa), dev(np.array([128], np.int32)), SM_SCALE, out)
+    codes, scales = oracle.quant_rows(src[0])
+    x = np.stack([oracle.dequant_row(codes[i], scales[i]) for i in range(cap)]
+                 + [synth.bf16_to_f32(r).astype(np.float64) for r in swa[0]])
+    qf = synth.bf16_to_f32(q[0]).astype(np.float64)
+    z = SM_SCALE * qf @ x.T
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    ref = (p / p.sum(axis=1, keepdims=True)) @ x
+    assert_attention_close(out.cpu().numpy()[0], ref, "dense")
