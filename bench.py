@@ -1,0 +1,253 @@
+"""Benchmark of the CSA2 FP4-KV decode step on one MI355X.
+
+Workload: the 20-layer decoder schedule at 1M positions, batch 16 (group 1 =
+hierarchical Full + 3 Reuse, groups 2-5 = Reindex + 3 Reuse, five FP4 main-KV
+tensors, one FP4 append per sequence per step), seeded synthetic inputs
+resident in HBM.  A step is one pass of the whole path: append, indexer
+scoring, Top-512 with the 2,048 x 8 pool, gather + dequant, sparse + SWA
+attention for all 20 layers.
+
+Prints one JSON line: (seq.layer)-steps/s, ms per step, the step's
+algorithmic HBM bytes as GB/s and fraction of the 8 TB/s peak, the
+roofline of the dominant kernel (timed with HIP events), the CPU oracle on a
+bounded sample of the same workload, and a parity check of one step
+against that oracle sample.
+
+usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-graph]
+                       [--cpu-seqs 16] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "CSA2 decode (seq·layer)-steps/s at 1M ctx + achieved HBM GB/s as % of peak"
+PEAK_HBM_GBPS = 8000.0
+
+
+def algorithmic_bytes(cfg, L: int) -> dict:
+    """Bytes the method must move in one decode step (each distinct byte once).
+
+    Per sequence: the block keys of all ceil(L/8) blocks (128 B each), the
+    indexer keys of the pool's positions (128 B each; shared by the Full and
+    Reindex layers), the selected FP4 rows of each main-KV tensor (512 x 288
+    B), every layer's SWA window (128 x 1 KiB), main Q (16 KiB) and f32
+    output (32 KiB), each selecting layer's indexer Q (1 KiB) and indices
+    (2 KiB), and the append (1 KiB read, 288 B written)."""
+    n = cfg.n_seq
+    nl = len(cfg.layers)
+    sel_layers = sum(1 for m, _, _ in cfg.layers if m != 2)
+    groups = len({k for _, k, _ in cfg.layers})
+    nblk = -(-L // cfg.blk)
+    pool_pos = min(L, cfg.pool_blocks * cfg.blk) if cfg.hierarchical else L
+    parts = {
+        "block_keys": n * nblk * 128 if cfg.hierarchical else 0,
+        "indexer_keys": n * pool_pos * 128,
+        "fp4_rows": n * groups * cfg.topk * 288,
+        "swa": n * nl * cfg.swa * 1024,
+        "main_q": n * nl * 16 * 1024,
+        "out": n * nl * 16 * 512 * 4,
+        "indexer_q_and_indices": n * sel_layers * (1024 + cfg.topk * 4),
+        "append": n * (1024 + 288) if cfg.append else 0,
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def cpu_baseline(cfg, step: int, seqs, threads: int):
+    """Oracle (as it stands) on one full decode step of `seqs`: inputs are
+    regenerated first (not timed), then the oracle's layer walk is timed."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import workloads as ow
+    import oracle
+
+    prep = {}
+
+    def prepare(b):
+        prep[b] = (ow.seq_state(cfg, b, step), ow.layer_inputs(cfg, b, step))
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(prepare, seqs))
+    layers = [oracle.Layer(m, k, bool(h)) for m, k, h in cfg.layers]
+
+    def run(b):
+        st, ins = prep[b]
+        return b, oracle.decode_layers(layers, st, ins, ow.SM_SCALE, k=cfg.topk, n_pool=cfg.pool_blocks)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        res = dict(ex.map(run, seqs))
+    dt = time.perf_counter() - t0
+    return res, dt
+
+
+def compare_step(cfg, gpu, ref) -> dict:
+    """GPU step-0 results against the oracle sample: indices and pool
+    bit-exact, attention rel. L2 <= 1e-3 and max abs <= 5e-3 per (seq, head)."""
+    import numpy as np
+
+    idx_ok = pool_ok = True
+    worst_rel = worst_abs = 0.0
+    for b, layers in ref.items():
+        for l, r in enumerate(layers):
+            idx_ok &= bool(np.array_equal(gpu["idx"][l][b], r.idx))
+            if r.pool is not None and gpu["pool"] is not None and cfg.layers[l][0] == 0:
+                pool_ok &= bool(np.array_equal(gpu["pool"][b], r.pool))
+            o = gpu["out"][l][b].astype(np.float64)
+            e = o - r.out.astype(np.float64)
+            rel = np.linalg.norm(e, axis=1) / np.maximum(np.linalg.norm(r.out, axis=1), 1e-30)
+            worst_rel = max(worst_rel, float(rel.max()))
+            worst_abs = max(worst_abs, float(np.abs(e).max()))
+    ok = idx_ok and pool_ok and worst_rel <= 1e-3 and worst_abs <= 5e-3
+    return {"ok": ok, "indices_bit_exact": idx_ok, "pool_bit_exact": pool_ok,
+            "attn_max_rel_l2": worst_rel, "attn_max_abs": worst_abs, "seqs": len(ref)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-graph", action="store_true", help="launch each step eagerly")
+    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--config", default="decoder20_1m")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the multi-GPU split of this path is designed but "
+              "not built, so only --gpus 1 is supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp4_kv_cache_quant_amd as csa2
+    from fp4_kv_cache_quant_amd import workloads as wl
+    from synth.configs import DECODE_CONFIGS
+
+    cfg = DECODE_CONFIGS[args.config]
+    K, W = args.steps, args.warmup
+    total_steps = 1 + W + K          # step 0 (parity) + warmup + timed
+    torch.cuda.init()
+    t_build = time.perf_counter()
+    inp = wl.build_decode_inputs(cfg, total_steps)
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    build_s = time.perf_counter() - t_build
+    nl = len(cfg.layers)
+    stream = torch.cuda.current_stream()
+
+    # Step 0, eager: kept for the parity check against the oracle sample.
+    sched.decode_step(ios[0])
+    torch.cuda.synchronize()
+    gpu0 = {"idx": [sched.indices(l).cpu().numpy() for l in range(nl)],
+            "pool": sched.pool().cpu().numpy() if cfg.hierarchical else None,
+            "out": [o.cpu().numpy() for o in inp.out]}
+
+    # One captured graph per query set; step s replays graph s % q_sets.
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for s in range(cfg.q_sets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    sched.decode_step(ios[s])
+                graphs.append(g)
+        stream.wait_stream(side)
+
+    def run_step(s):
+        if graphs:
+            graphs[s % cfg.q_sets].replay()
+        else:
+            sched.decode_step(ios[s % cfg.q_sets])
+
+    for s in range(1, 1 + W):
+        run_step(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(1 + W, 1 + W + K):
+        run_step(s)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    if sched.check() != 0:
+        print("an append found a full cache during the timed steps", file=sys.stderr)
+        return 1
+    ms_per_step = gpu_ms / K
+    units_per_step = cfg.n_seq * nl
+    value = units_per_step / (ms_per_step * 1e-3)
+    L_mid = cfg.lens_at(1 + W + K // 2)
+    ab = algorithmic_bytes(cfg, L_mid)
+    hbm_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
+
+    # Dominant kernel: the block-key scan of the hierarchical Full layer, the
+    # same launch the step makes (csa2_index_score over all block keys),
+    # timed with HIP events on the stream it runs on.
+    dom = None
+    if cfg.hierarchical:
+        blk_cap = cfg.blk_cap(total_steps)
+        scores = torch.empty(cfg.n_seq, blk_cap, dtype=torch.float32, device="cuda")
+        q0 = inp.idx_q[0][0]
+        for _ in range(3):
+            csa2.index_score(q0, inp.blk_k, inp.lens, scores, len_div=cfg.blk)
+        reps = max(10, K)
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for _ in range(reps):
+            csa2.index_score(q0, inp.blk_k, inp.lens, scores, len_div=cfg.blk)
+        d1.record()
+        torch.cuda.synchronize()
+        dur_s = d0.elapsed_time(d1) * 1e-3 / reps
+        L_now = int(inp.lens[0].item())
+        nblk = -(-L_now // cfg.blk)
+        # keys read + scores written + indexer Q read, per launch
+        dom_bytes = cfg.n_seq * (nblk * 128 + nblk * 4 + 1024)
+        dom = {"kernel": "index_score_kernel<flat> (block keys)", "bytes_per_launch": dom_bytes,
+               "avg_us": dur_s * 1e6}
+        achieved = dom_bytes / dur_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+    else:
+        roofline = None
+
+    # CPU oracle on a bounded sample: step 0 of the first cpu_seqs sequences.
+    cpu = parity = None
+    if not args.no_cpu:
+        threads = max(1, min(args.cpu_seqs, len(os.sched_getaffinity(0)), 16))
+        seqs = list(range(min(args.cpu_seqs, cfg.n_seq)))
+        res, dt = cpu_baseline(cfg, 0, seqs, threads)
+        cpu = {"value": round(len(seqs) * nl / dt, 2), "unit": "(seq·layer)-steps/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"decode step 0 of {len(seqs)} of {cfg.n_seq} sequences, all {nl} layers "
+                         f"(hierarchical select, 4 Reindex rescorings, {nl} attentions), {dt:.1f} s"}
+        parity = compare_step(cfg, gpu0, res)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "(seq·layer)-steps/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; FP4 E2M1 + E4M3/16 main KV, integer indexer Q/K, N(0,1) bf16 latents)",
+        "config": {"workload": cfg.name, "n_seq": cfg.n_seq, "positions": cfg.L0, "layers": nl,
+                   "fp4_kv_tensors": cfg.n_kv, "topk": cfg.topk, "pool": f"{cfg.pool_blocks}x{cfg.blk}",
+                   "swa": cfg.swa, "graph": bool(graphs)},
+        "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": round(hbm_gbps, 1),
+                "frac_of_peak": round(hbm_gbps / PEAK_HBM_GBPS, 4), "parts": ab},
+        "roofline": roofline, "dominant_kernel": dom, "cpu_baseline": cpu, "parity_step0": parity,
+        "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+    sched.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk",
+    "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
     "sparse_attn", "sparse_attn_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
@@ -27,7 +27,7 @@ HEADS, IDX_HEADS, IDX_DIM = 16, 8, 64
 FULL, REINDEX, REUSE = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing; build it with `python -m fp4_kv_cache_quant_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing; build it with `python fp4_kv_cache_quant_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -65,7 +65,8 @@ abi_version = _sig("csa2_abi_version", _I32)
 _quant_rows = _sig("csa2_quant_rows", _I32, _P, _I64, _P, _P, _P)
 _quant_append = _sig("csa2_quant_append", _I32, _P, _FP4KV, _P, _P, _P)
 _index_score = _sig("csa2_index_score", _I32, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _I64, _I32, _P)
-_topk = _sig("csa2_topk", _I32, _P, _I64, _P, _I32, _I32, _P, _I32, _I32, _P, _I32, _P)
+_topk_ws = _sig("csa2_topk_workspace_size", _SZ, _I64, _I32)
+_topk = _sig("csa2_topk", _I32, _P, _I64, _P, _I32, _I32, _P, _I32, _I32, _P, _P, _SZ, _I32, _P)
 _attn_ws = _sig("csa2_sparse_attn_workspace_size", _SZ, _I32, _I32, _I32)
 _attn = _sig("csa2_sparse_attn", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
              _I32, _F32, _P, _P, _SZ, _P)
@@ -152,13 +153,21 @@ def index_score(q: torch.Tensor, keys: torch.Tensor, lens: torch.Tensor, scores:
                         blk, _ptr(scores), n_out, n_seq, _stream(stream)))
 
 
+def topk_workspace_size(n: int, n_seq: int) -> int:
+    return int(_topk_ws(n, n_seq))
+
+
 def topk(scores: torch.Tensor, k: int, out: torch.Tensor, lens: Optional[torch.Tensor] = None,
-         len_div: int = 1, pool: Optional[torch.Tensor] = None, blk: int = 8, stream=None) -> None:
-    """scores [n_seq][n] f32 -> out [n_seq][k] int32 ascending ids, -1 padded."""
+         len_div: int = 1, pool: Optional[torch.Tensor] = None, blk: int = 8,
+         ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """scores [n_seq][n] f32 -> out [n_seq][k] int32 ascending ids, -1 padded.
+    ws: a zero-filled workspace reused across calls (a fresh one if None)."""
     n_seq, n = scores.shape
     n_pool = pool.shape[1] if pool is not None else 0
-    _check(_topk(_ptr(scores), n, _ptr(lens), len_div, k, _ptr(pool), n_pool, blk, _ptr(out), n_seq,
-                 _stream(stream)))
+    if ws is None:
+        ws = torch.zeros(max(topk_workspace_size(n, n_seq), 1), dtype=torch.uint8, device=scores.device)
+    _check(_topk(_ptr(scores), n, _ptr(lens), len_div, k, _ptr(pool), n_pool, blk, _ptr(out), _ptr(ws),
+                 ws.numel(), n_seq, _stream(stream)))
 
 
 def sparse_attn_workspace_size(n_q: int, k_idx: int, swa_max: int) -> int:

@@ -2,7 +2,8 @@
 
 Every source is compiled on each call (objects in parallel), then linked
 in-tree next to this file, so the built library travels with the source
-tree.  Usage: ``python -m fp4_kv_cache_quant_amd.build``.
+tree.  Usage: ``python fp4_kv_cache_quant_amd/build.py`` (a plain script:
+importing the package needs the library it builds).
 """
 from __future__ import annotations
 

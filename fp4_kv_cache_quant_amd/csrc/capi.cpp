@@ -6,6 +6,7 @@
 #include <string>
 
 #include "common.hpp"
+#include "topk_ws.hpp"
 
 namespace csa2 {
 
@@ -13,9 +14,7 @@ csa2_status quant_rows_launch(const uint16_t*, int64_t, uint8_t*, uint8_t*, hipS
 csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, int32_t*, hipStream_t);
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
-                               hipStream_t);
-csa2_status topk_launch(const float*, int64_t, const int32_t*, int32_t, int32_t, const int32_t*, int32_t,
-                        int32_t, int32_t*, int32_t, hipStream_t);
+                               uint32_t*, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const uint16_t*, int64_t, const int32_t*, int32_t, float, float*, void*,
@@ -65,17 +64,20 @@ csa2_status check_index_score(const uint16_t* q, const uint16_t* keys, int64_t k
 }
 
 csa2_status check_topk(const float* scores, int64_t n, int32_t len_div, int32_t k, const int32_t* pool,
-                       int32_t n_pool, int32_t blk, const int32_t* out, int32_t n_seq) {
-  CSA2_REQUIRE(n_seq >= 0, CSA2_ESHAPE, "csa2_topk: negative n_seq");
+                       int32_t n_pool, int32_t blk, const int32_t* out, const void* ws, size_t ws_bytes,
+                       int32_t n_seq) {
+  CSA2_REQUIRE(n_seq >= 0 && n_seq <= 65535, CSA2_ESHAPE, "csa2_topk: n_seq must be in [0, 65535]");
   if (n_seq == 0) return CSA2_OK;
-  CSA2_REQUIRE(scores && out, CSA2_EINVAL, "csa2_topk: null pointer");
+  CSA2_REQUIRE(scores && out && ws, CSA2_EINVAL, "csa2_topk: null pointer");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, CSA2_EINVAL, "csa2_topk: ws must be 16-byte aligned");
   CSA2_REQUIRE(k >= 1 && k <= CSA2_TOPK_MAX, CSA2_ESHAPE, "csa2_topk: k must be in [1, 2048]");
   CSA2_REQUIRE(n >= 0 && n <= CSA2_TOPK_NMAX, CSA2_ESHAPE, "csa2_topk: n must be in [0, 262144]");
   CSA2_REQUIRE(len_div > 0, CSA2_EINVAL, "csa2_topk: len_div must be positive");
   if (pool) {
-    CSA2_REQUIRE(n_pool > 0 && blk > 0 && n == (int64_t)n_pool * blk, CSA2_ESHAPE,
-                 "csa2_topk: pool mode needs n == n_pool * blk");
+    CSA2_REQUIRE(n_pool > 0 && n_pool <= CSA2_TOPK_MAX && blk > 0 && n == (int64_t)n_pool * blk, CSA2_ESHAPE,
+                 "csa2_topk: pool mode needs n == n_pool * blk and n_pool <= 2048");
   }
+  CSA2_REQUIRE(ws_bytes >= topk_workspace_bytes(n, n_seq), CSA2_ECAPACITY, "csa2_topk: workspace too small");
   return CSA2_OK;
 }
 
@@ -147,16 +149,22 @@ csa2_status csa2_index_score(const uint16_t* q, const float* w, const uint16_t* 
   csa2_status st = check_index_score(q, keys, key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, n_seq);
   if (st != CSA2_OK || n_seq == 0) return st;
   return index_score_launch(q, w, keys, key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, n_seq,
-                            as_stream(stream));
+                            nullptr, as_stream(stream));
+}
+
+size_t csa2_topk_workspace_size(int64_t n, int32_t n_seq) {
+  if (n < 0 || n_seq <= 0 || n > CSA2_TOPK_NMAX) return 0;
+  return topk_workspace_bytes(n, n_seq);
 }
 
 csa2_status csa2_topk(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
-                      const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, int32_t n_seq,
-                      void* stream) {
+                      const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, void* ws,
+                      size_t ws_bytes, int32_t n_seq, void* stream) {
   clear_error();
-  csa2_status st = check_topk(scores, n, len_div, k, pool, n_pool, blk, out, n_seq);
+  csa2_status st = check_topk(scores, n, len_div, k, pool, n_pool, blk, out, ws, ws_bytes, n_seq);
   if (st != CSA2_OK || n_seq == 0) return st;
-  return topk_launch(scores, n, lens, len_div, k, pool, n_pool, blk, out, n_seq, as_stream(stream));
+  return topk_launch(scores, n, lens, len_div, k, pool, n_pool, blk, out, topk_ws_carve(ws, n, n_seq), false,
+                     n_seq, as_stream(stream));
 }
 
 size_t csa2_sparse_attn_workspace_size(int32_t n_q, int32_t k_idx, int32_t swa_max) {

@@ -69,6 +69,12 @@ __host__ __device__ __forceinline__ float e2m1_mag_value(uint32_t m) {
   return m >= 2u ? normal : 0.5f * (float)m;
 }
 
+// Byte permute (v_perm_b32): result byte i = byte sel_i of the 8-byte value
+// hi:lo (selector 0..3 = bytes of lo, 4..7 = bytes of hi, 12 = zero byte).
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
 // Scores that are not candidates.
 constexpr float kNegInf = -__builtin_huge_valf();
 

@@ -14,7 +14,10 @@
 //
 // The kernel is a pure HBM stream (128 bytes per key); each wavefront
 // issues all its key loads before its MFMAs to keep many bytes in flight.
+#include <algorithm>
+
 #include "common.hpp"
+#include "topk_ws.hpp"
 
 namespace csa2 {
 namespace {
@@ -32,16 +35,23 @@ __device__ __forceinline__ float relu_wsum4(const f32x4& acc, const float* wh) {
   return part;
 }
 
-template <bool kPool, bool kWeights>
+// kHist: also add the scores' top key digits into a per-sequence histogram
+// (ghist [n_seq][4096]) for the Top-k that follows.
+template <bool kPool, bool kWeights, bool kHist>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ keys,
     int64_t key_cap, const int32_t* __restrict__ lens, int32_t len_div,
     const int32_t* __restrict__ pool, int32_t n_pool, int32_t blk, float* __restrict__ scores,
-    int64_t n_out) {
+    int64_t n_out, uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t hist[kHist ? kTopkBins : 1];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t L = lens[b];
+  if (kHist) {
+    for (int i = threadIdx.x; i < kTopkBins; i += 256) hist[i] = 0;
+    __syncthreads();
+  }
   int64_t n_valid = n_out;
   if (!kPool) n_valid = min(n_out, (L + len_div - 1) / len_div);
 
@@ -63,52 +73,66 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     for (int r = 0; r < 4; ++r) wh[r] = w[(int64_t)b * 8 + 4 * g + r];
   }
 
-  const int64_t base = (int64_t)blockIdx.x * kKeysPerWG + (int64_t)wave * (kTilesPerWave * 16);
   const uint16_t* kb = keys + (int64_t)b * key_cap * 64;
-
-  u32x4 kv[kTilesPerWave][2];
-  bool valid[kTilesPerWave];
+  float* sb = scores + (int64_t)b * n_out;
+  // Grid-stride over chunks of kKeysPerWG keys (one histogram flush per workgroup).
+  for (int64_t chunk = blockIdx.x; chunk * kKeysPerWG < n_out; chunk += gridDim.x) {
+    const int64_t base = chunk * kKeysPerWG + (int64_t)wave * (kTilesPerWave * 16);
+    u32x4 kv[kTilesPerWave][2];
+    bool valid[kTilesPerWave];
 #pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int64_t slot = base + t * 16 + n;
-    int64_t row = slot;
-    bool ok = slot < n_valid;
-    if (kPool && ok) {
-      const int32_t blk_id = pool[(int64_t)b * n_pool + slot / blk];
-      row = (int64_t)blk_id * blk + slot % blk;
-      ok = blk_id >= 0 && row < L && row < key_cap;
-    }
-    valid[t] = ok;
-    if (ok) {
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kb + row * 64 + 16 * g);
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int64_t slot = base + t * 16 + n;
+      int64_t row = slot;
+      bool ok = slot < n_valid;
+      if (kPool && ok) {
+        const int32_t blk_id = pool[(int64_t)b * n_pool + slot / blk];  // slot < n_out = n_pool * blk
+        row = (int64_t)blk_id * blk + slot % blk;
+        ok = blk_id >= 0 && row < L && row < key_cap;
+      }
+      valid[t] = ok;
+      // Unconditional load of a clamped row (an invalid slot reads row 0 and
+      // is masked below), so the wavefront's loads are all in flight together.
+      const u32x4* kp = reinterpret_cast<const u32x4*>(kb + (ok ? row : 0) * 64 + 16 * g);
       kv[t][0] = __builtin_nontemporal_load(kp);
       kv[t][1] = __builtin_nontemporal_load(kp + 1);
-    } else {
-      kv[t][0] = u32x4{0, 0, 0, 0};
-      kv[t][1] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      if (!valid[t]) kv[t][0] = kv[t][1] = u32x4{0, 0, 0, 0};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16x16x32(qa[0], as_bf16x8(kv[t][0]), acc);
+      acc = mfma16x16x32(qa[1], as_bf16x8(kv[t][1]), acc);
+      // acc[r] = q_{4g+r} . key n.
+      const float part = relu_wsum4(acc, wh);
+      const float other = __shfl_xor(part, 16);
+      const int64_t slot = base + t * 16 + n;
+      if (g == 0 && slot < n_out) {
+        const float score = part + other;
+        sb[slot] = valid[t] ? score : kNegInf;
+        const uint32_t key = order_key(score);
+        if (kHist && valid[t] && key) atomicAdd(&hist[key >> 20], 1u);
+      }
     }
   }
-
-  float* sb = scores + (int64_t)b * n_out;
-#pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma16x16x32(qa[0], as_bf16x8(kv[t][0]), acc);
-    acc = mfma16x16x32(qa[1], as_bf16x8(kv[t][1]), acc);
-    // acc[r] = q_{4g+r} . key n.
-    const float part = relu_wsum4(acc, wh);
-    const float other = __shfl_xor(part, 16);
-    const int64_t slot = base + t * 16 + n;
-    if (g == 0 && slot < n_out) sb[slot] = valid[t] ? part + other : kNegInf;
+  if (kHist) {
+    __syncthreads();
+    uint32_t* gh = ghist + (int64_t)b * kTopkBins;
+    for (int i = threadIdx.x; i < kTopkBins; i += 256)
+      if (hist[i]) atomicAdd(&gh[i], hist[i]);
   }
 }
 
 template <bool kPool, bool kWeights>
 void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const float* w, const uint16_t* keys,
                 int64_t key_cap, const int32_t* lens, int32_t len_div, const int32_t* pool,
-                int32_t n_pool, int32_t blk, float* scores, int64_t n_out) {
-  hipLaunchKernelGGL((index_score_kernel<kPool, kWeights>), grid, dim3(256), 0, stream, q, w, keys,
-                     key_cap, lens, len_div, pool, n_pool, blk, scores, n_out);
+                int32_t n_pool, int32_t blk, float* scores, int64_t n_out, uint32_t* ghist) {
+  if (ghist)
+    hipLaunchKernelGGL((index_score_kernel<kPool, kWeights, true>), grid, dim3(256), 0, stream, q, w, keys,
+                       key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, ghist);
+  else
+    hipLaunchKernelGGL((index_score_kernel<kPool, kWeights, false>), grid, dim3(256), 0, stream, q, w, keys,
+                       key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, ghist);
 }
 
 }  // namespace
@@ -116,17 +140,21 @@ void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const float* w
 csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
                                const int32_t* lens, int32_t len_div, const int32_t* pool,
                                int32_t n_pool, int32_t blk, float* scores, int64_t n_out, int32_t n_seq,
-                               hipStream_t stream) {
+                               uint32_t* ghist, hipStream_t stream) {
   if (n_seq == 0 || n_out == 0) return CSA2_OK;
-  const int64_t wgs = (n_out + kKeysPerWG - 1) / kKeysPerWG;
-  CSA2_REQUIRE(wgs <= 0x7FFFFFFF && n_seq <= 65535, CSA2_ESHAPE, "csa2_index_score: grid too large");
-  const dim3 grid((uint32_t)wgs, (uint32_t)n_seq);
+  // About two workgroups per CU in total; each loops over chunks of 512
+  // keys, so a fused histogram is flushed by few workgroups (its hot bins
+  // see one global atomic per workgroup).
+  const int64_t chunks = (n_out + kKeysPerWG - 1) / kKeysPerWG;
+  const int64_t per_seq = std::max<int64_t>(1, std::min<int64_t>(chunks, (512 + n_seq - 1) / n_seq));
+  CSA2_REQUIRE(n_seq <= 65535, CSA2_ESHAPE, "csa2_index_score: grid too large");
+  const dim3 grid((uint32_t)per_seq, (uint32_t)n_seq);
   if (pool) {
-    if (w) launch_one<true, true>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out);
-    else launch_one<true, false>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out);
+    if (w) launch_one<true, true>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out, ghist);
+    else launch_one<true, false>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out, ghist);
   } else {
-    if (w) launch_one<false, true>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out);
-    else launch_one<false, false>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out);
+    if (w) launch_one<false, true>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out, ghist);
+    else launch_one<false, false>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out, ghist);
   }
   return launch_status("csa2_index_score");
 }

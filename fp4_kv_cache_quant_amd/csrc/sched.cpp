@@ -14,14 +14,13 @@
 #include <vector>
 
 #include "common.hpp"
+#include "topk_ws.hpp"
 
 namespace csa2 {
 csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, int32_t*, hipStream_t);
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
-                               hipStream_t);
-csa2_status topk_launch(const float*, int64_t, const int32_t*, int32_t, int32_t, const int32_t*, int32_t,
-                        int32_t, int32_t*, int32_t, hipStream_t);
+                               uint32_t*, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const uint16_t*, int64_t, const int32_t*, int32_t, float, float*, void*,
@@ -45,6 +44,9 @@ struct csa2_sched {
   int64_t scores_n = 0;
   void* attn_ws = nullptr;
   size_t attn_ws_bytes = 0;
+  void* topk_ws = nullptr;      // Top-k workspace (histogram, counters, bitmap, candidates)
+  size_t topk_ws_bytes = 0;
+  TopkWs tw{};
   int32_t* err = nullptr;
 };
 
@@ -56,6 +58,7 @@ void free_sched(csa2_sched* s) {
   hipFree(s->pool);
   hipFree(s->scores);
   hipFree(s->attn_ws);
+  hipFree(s->topk_ws);
   hipFree(s->err);
   delete s;
 }
@@ -156,16 +159,20 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
     s->scores_n = std::max<int64_t>(s->scores_n, d.key_cap);
   }
   s->attn_ws_bytes = attn_workspace_bytes(d.n_seq, d.topk, d.swa_max);
+  s->topk_ws_bytes = topk_workspace_bytes(s->scores_n, d.n_seq);
   const size_t n = (size_t)d.n_seq;
   if ((st = dev_alloc(&s->idx_bufs, (size_t)s->n_idx_bufs * n * d.topk * sizeof(int32_t))) != CSA2_OK ||
       (st = dev_alloc(&s->pool, s->any_hier ? n * d.pool_blocks * sizeof(int32_t) : 0)) != CSA2_OK ||
       (st = dev_alloc(&s->scores, n * (size_t)s->scores_n * sizeof(float))) != CSA2_OK ||
       (st = dev_alloc(&s->attn_ws, s->attn_ws_bytes)) != CSA2_OK ||
+      (st = dev_alloc(&s->topk_ws, s->topk_ws_bytes)) != CSA2_OK ||
       (st = dev_alloc(&s->err, sizeof(int32_t))) != CSA2_OK) {
     free_sched(s);
     return st;
   }
+  s->tw = topk_ws_carve(s->topk_ws, s->scores_n, d.n_seq);
   if (hipMemset(s->err, 0, sizeof(int32_t)) != hipSuccess ||
+      hipMemset(s->topk_ws, 0, s->topk_ws_bytes) != hipSuccess ||
       hipMemset(s->idx_bufs, 0xFF, (size_t)s->n_idx_bufs * n * d.topk * sizeof(int32_t)) != hipSuccess) {
     free_sched(s);
     set_error("csa2_sched_create: hipMemset failed");
@@ -215,12 +222,12 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
     csa2_status st = CSA2_OK;
     bool use_pool = false;
     if (L.mode == CSA2_FULL && L.hierarchical) {
-      // Blocks: flat scores of block keys, keep pool_blocks of them.
+      // Blocks: flat scores of block keys (with their histogram), keep pool_blocks of them.
       st = index_score_launch(io->idx_q[l], w, io->blk_k, d.blk_cap, io->lens, d.blk, nullptr, 0, 1,
-                              s->scores, d.blk_cap, d.n_seq, stream);
+                              s->scores, d.blk_cap, d.n_seq, s->tw.hist, stream);
       if (st == CSA2_OK)
-        st = topk_launch(s->scores, d.blk_cap, io->lens, d.blk, d.pool_blocks, nullptr, 0, 1, s->pool,
-                         d.n_seq, stream);
+        st = topk_launch(s->scores, d.blk_cap, io->lens, d.blk, d.pool_blocks, nullptr, 0, 1, s->pool, s->tw,
+                         true, d.n_seq, stream);
       use_pool = true;
     } else if (L.mode == CSA2_REINDEX) {
       use_pool = s->layers[s->full_of_layer[l]].hierarchical != 0;
@@ -229,15 +236,16 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       if (use_pool) {
         const int64_t n_out = (int64_t)d.pool_blocks * d.blk;
         st = index_score_launch(io->idx_q[l], w, io->idx_k, d.key_cap, io->lens, 1, s->pool, d.pool_blocks,
-                                d.blk, s->scores, n_out, d.n_seq, stream);
+                                d.blk, s->scores, n_out, d.n_seq, s->tw.hist, stream);
         if (st == CSA2_OK)
-          st = topk_launch(s->scores, n_out, nullptr, 1, d.topk, s->pool, d.pool_blocks, d.blk, idx,
+          st = topk_launch(s->scores, n_out, nullptr, 1, d.topk, s->pool, d.pool_blocks, d.blk, idx, s->tw, true,
                            d.n_seq, stream);
       } else {
-        st = index_score_launch(io->idx_q[l], w, io->idx_k, d.key_cap, io->lens, 1, nullptr, 0, 1,
-                                s->scores, d.key_cap, d.n_seq, stream);
+        st = index_score_launch(io->idx_q[l], w, io->idx_k, d.key_cap, io->lens, 1, nullptr, 0, 1, s->scores,
+                                d.key_cap, d.n_seq, s->tw.hist, stream);
         if (st == CSA2_OK)
-          st = topk_launch(s->scores, d.key_cap, io->lens, 1, d.topk, nullptr, 0, 1, idx, d.n_seq, stream);
+          st = topk_launch(s->scores, d.key_cap, io->lens, 1, d.topk, nullptr, 0, 1, idx, s->tw, true, d.n_seq,
+                           stream);
       }
     }
     if (st == CSA2_OK)

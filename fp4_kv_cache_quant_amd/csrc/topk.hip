@@ -2,70 +2,88 @@
 // ascending id order ([P1 "Compressed Sparse Attention 2 (CSA2)"]: a fresh
 // Top-512, and the hierarchical indexer's pool of 2,048 blocks).
 //
-// One 1024-thread workgroup per sequence.  Scores are mapped to an
-// order-preserving 32-bit key (0 = not a candidate) and the exact k-th key T
-// is found by a radix select over digits of 12, 12 and 8 bits:
-//   pass 1  LDS histogram of the top 12 bits over all candidates;
-//   pass 2  keys above the threshold bin go straight into a selection
-//           bitmap, keys inside it are buffered in LDS;
-//   then the two low digits are resolved from the buffer (or, if the bin
-//   holds more keys than the buffer, by further passes over the scores).
-// Keys above T are selected; of the keys equal to T, the ones with the
-// lowest slots are taken through a prefix count over a tie bitmap.  A final
-// prefix count over the selection bitmap writes ids in ascending order.
-// Everything is integer work on the keys, so the result is exact and
-// independent of thread timing.
+// Scores map to an order-preserving 32-bit key (0 = not a candidate).  The
+// exact k-th key T is found by a radix select over digits of 12, 12 and 8
+// bits, spread over up to three kernels so that the full-length passes run
+// on many workgroups:
+//   histogram  per-sequence counts of the top 12 key bits (global atomics of
+//              per-workgroup LDS histograms; the indexer-score kernel can
+//              produce it as a by-product, then this kernel is skipped);
+//   filter     (long inputs) every workgroup reads the histogram, finds the
+//              threshold bin b1, writes a selection bitmap of the keys above
+//              b1 and appends the keys inside b1 to a candidate buffer;
+//   final      one workgroup per sequence resolves the two low digits among
+//              the candidates, takes keys above T and the lowest-slot keys
+//              equal to T (prefix count over a tie bitmap), and writes the
+//              ids in ascending order from a prefix count over the bitmap.
+//              For short inputs it does the filter pass itself.
+// If the threshold bin holds more keys than the candidate buffer, the final
+// kernel resolves the low digits with passes over the scores instead.
+// Score loads use clamped, unconditional addresses so that a thread's batch
+// of loads is in flight together (a conditional load waits on its own).
+// All of it is integer work on the keys: exact and independent of timing.
 //
 // Citation key: [P1] "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M
 // Context, FP4 KV Cache, and Cross-Layer Attention Reuse".
 #include "common.hpp"
+#include "topk_ws.hpp"
 
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 4096;
-constexpr int kCandCap = 4096;
-constexpr int kMaxWords = CSA2_TOPK_NMAX / 32;
+constexpr int kFinalThreads = 1024;
+constexpr int kFinalWaves = kFinalThreads / 64;
+constexpr int kPassThreads = 256;
+constexpr int kBatch = 8;                         // slots per thread loaded together
+constexpr int kHistSlots = kPassThreads * 16;     // slots per histogram workgroup
+constexpr int kFilterSlots = kPassThreads * 8;    // slots per filter workgroup
+constexpr int kDirectMax = 32768;                 // final kernel filters inputs up to this length itself
 
-struct TopkSmem {
-  uint32_t hist[kBins];
-  uint32_t sel[kMaxWords];
-  uint32_t tie[kMaxWords];
-  uint32_t cand_key[kCandCap];
-  uint32_t cand_slot[kCandCap];
-  uint32_t wave_sum[kWaves];
-  uint32_t n_cand;
-  uint32_t found_bin;
-  uint32_t found_above;
-};
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Order-preserving key of a score; NaN and -inf (non-candidates) map to 0,
-// -0 and +0 map to the same key.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) == 0) u = 0;
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0;  // NaN
-  if (u == 0xFF800000u) return 0;                  // -inf
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, TopkSmem& sm, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int64_t valid_slots(int64_t n, const int32_t* lens, int32_t len_div, int b) {
+  if (!lens) return n;
+  const int64_t L = lens[b];
+  return min(n, L > 0 ? (L + len_div - 1) / len_div : 0);
+}
+
+// hist[bin] += 1 for every lane with `active`, one LDS atomic per distinct
+// bin of the wavefront: cheap when the wavefront's keys share few bins.
+// Called by all lanes of the wavefront.
+__device__ __forceinline__ void wave_hist_add_grouped(uint32_t* hist, uint32_t bin, bool active) {
+  uint64_t pending = __ballot(active);
+  while (pending) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const uint32_t lb = __shfl(bin, leader);
+    const uint64_t same = __ballot(active && bin == lb);
+    if (lane_id() == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    pending &= ~same;
+    active = active && bin != lb;
+  }
+}
+
+// Exclusive prefix sum over a workgroup of NT threads in thread order.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sum, uint32_t* total) {
+  constexpr int kW = NT / 64;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const uint32_t y = __shfl_up(x, d);
     if (lane >= d) x += y;
   }
-  if (lane == 63) sm.wave_sum[wave] = x;
+  if (lane == 63) wave_sum[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const uint32_t s = sm.wave_sum[i];
+  for (int i = 0; i < kW; ++i) {
+    const uint32_t s = wave_sum[i];
     before += (i < wave) ? s : 0u;
     all += s;
   }
@@ -74,148 +92,317 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, TopkSmem& s
   return before + x - v;
 }
 
-// Over hist[0..nbins), find the largest bin B with (count of bins >= B) >= need.
-// Writes B and the count of bins > B to sm.found_bin / sm.found_above.
-// Requires 1 <= need <= total count.
-__device__ void find_threshold_bin(TopkSmem& sm, int nbins, uint32_t need) {
-  const int per = (nbins + kThreads - 1) / kThreads;
+// Largest bin B of hist[0..nbins) with (count of bins >= B) >= need, and the
+// count of bins > B, written to out[0], out[1]; requires 1 <= need <= total.
+template <int NT>
+__device__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* wave_sum,
+                                   uint32_t* out) {
+  const int per = (nbins + NT - 1) / NT;
   const int t = threadIdx.x;
-  // Thread t owns bins [hi - per, hi) with hi = nbins - t*per (top bins first).
-  const int hi = nbins - t * per;
+  const int hi = nbins - t * per;  // thread t owns bins [hi - per, hi), top bins first
   const int lo = hi - per > 0 ? hi - per : 0;
   uint32_t mine = 0;
-  for (int i = lo; i < hi; ++i) mine += sm.hist[i];
+  for (int i = lo; i < hi; ++i) mine += hist[i];
   uint32_t total;
-  const uint32_t above = block_exclusive_scan(hi > 0 ? mine : 0u, sm, &total);
+  const uint32_t above = block_exclusive_scan<NT>(hi > 0 ? mine : 0u, wave_sum, &total);
   if (hi > 0 && above < need && above + mine >= need) {
     uint32_t acc = above;
     for (int i = hi - 1; i >= lo; --i) {
-      if (acc + sm.hist[i] >= need) {
-        sm.found_bin = (uint32_t)i;
-        sm.found_above = acc;
+      if (acc + hist[i] >= need) {
+        out[0] = (uint32_t)i;
+        out[1] = acc;
         break;
       }
-      acc += sm.hist[i];
+      acc += hist[i];
     }
   }
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores, int64_t n,
-                                                        const int32_t* __restrict__ lens, int32_t len_div,
-                                                        int32_t k, const int32_t* __restrict__ pool,
-                                                        int32_t n_pool, int32_t blk,
-                                                        int32_t* __restrict__ out) {
+// Threshold state every filter/final workgroup derives from the histogram.
+struct Threshold {
+  uint32_t total;   // candidates
+  uint32_t b1;      // threshold bin of the top digit (valid if total > k)
+  uint32_t need1;   // keys still to take from bin b1
+  uint32_t in_bin;  // keys in bin b1
+};
+
+template <int NT>
+__device__ Threshold load_threshold(const uint32_t* __restrict__ ghist, uint32_t* hist, uint32_t* wave_sum,
+                                    uint32_t* found, uint32_t k) {
+  constexpr int kPer = kTopkBins / NT;
+  uint32_t v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = ghist[threadIdx.x + NT * j];  // all loads in flight together
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    hist[threadIdx.x + NT * j] = v[j];
+    mine += v[j];
+  }
+  Threshold th;
+  block_exclusive_scan<NT>(mine, wave_sum, &th.total);  // syncs: hist complete
+  th.b1 = th.need1 = th.in_bin = 0;
+  if (th.total > k) {
+    find_threshold_bin<NT>(hist, kTopkBins, k, wave_sum, found);
+    th.b1 = found[0];
+    th.need1 = k - found[1];
+    th.in_bin = hist[th.b1];
+  }
+  return th;
+}
+
+// ---------------------------------------------------------------- kernels
+__global__ __launch_bounds__(kPassThreads) void topk_hist_kernel(const float* __restrict__ scores, int64_t n,
+                                                                 const int32_t* __restrict__ lens,
+                                                                 int32_t len_div, uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t hist[kTopkBins];
+  const int b = blockIdx.y;
+  const int64_t nv = valid_slots(n, lens, len_div, b);
+  const int64_t s0 = (int64_t)blockIdx.x * kHistSlots;
+  if (s0 >= nv) return;
+  for (int i = threadIdx.x; i < kTopkBins; i += kPassThreads) hist[i] = 0;
+  __syncthreads();
+  const float* sc = scores + (int64_t)b * n;
+  for (int j0 = 0; j0 < kHistSlots / kPassThreads; j0 += kBatch) {
+    uint32_t key[kBatch];
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = sc[min(s0 + (j0 + j) * kPassThreads + threadIdx.x, nv - 1)];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t i = s0 + (j0 + j) * kPassThreads + threadIdx.x;
+      key[j] = i < nv ? order_key(v[j]) : 0u;
+      if (key[j]) atomicAdd(&hist[key[j] >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = ghist + (int64_t)b * kTopkBins;
+  for (int i = threadIdx.x; i < kTopkBins; i += kPassThreads)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+__global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* __restrict__ scores, int64_t n,
+                                                                   const int32_t* __restrict__ lens,
+                                                                   int32_t len_div, int32_t k, TopkWs ws) {
+  constexpr int kPer = kFilterSlots / kPassThreads;  // slots per thread
+  __shared__ uint32_t hist[kTopkBins];
+  __shared__ uint32_t wave_sum[kPassThreads / 64];
+  __shared__ uint32_t found[2];
+  __shared__ uint32_t g_base;
+  const int b = blockIdx.y;
+  const int64_t nv = valid_slots(n, lens, len_div, b);
+  const int64_t s0 = (int64_t)blockIdx.x * kFilterSlots;
+  if (s0 >= nv) return;
+  const float* sc = scores + (int64_t)b * n + s0;
+  const int nloc = (int)min<int64_t>(nv - s0, kFilterSlots);  // valid slots of this workgroup
+  // All of this thread's slots are loaded up front (clamped addresses).
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = sc[min(j * kPassThreads + (int)threadIdx.x, nloc - 1)];
+  const Threshold th = load_threshold<kPassThreads>(ws.hist + (int64_t)b * kTopkBins, hist, wave_sum, found,
+                                                    (uint32_t)k);
+  const bool all = th.total <= (uint32_t)k;
+  const bool buffered = th.in_bin <= (uint32_t)kTopkCandCap;
+  uint32_t* bits = ws.bits + (int64_t)b * ws.words_cap;
+  uint32_t key[kPer];
+  uint32_t mine = 0;
+  uint32_t* wbits = bits + (s0 >> 5);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int il = j * kPassThreads + (int)threadIdx.x;  // slot within the workgroup
+    key[j] = il < nloc ? order_key(v[j]) : 0u;
+    const uint32_t d = key[j] >> 20;
+    const uint64_t mask = __ballot(key[j] != 0 && (all || d > th.b1));
+    // The wavefront's 64 slots are 64-aligned: lanes 0 and 32 write the two
+    // words (every word of the valid range is written exactly once).
+    const int w = (il - lane_id()) >> 5;  // word of lanes 0..31; lanes 32..63 use w + 1
+    if (lane_id() == 0 && (w << 5) < nloc) wbits[w] = (uint32_t)mask;
+    if (lane_id() == 32 && ((w + 1) << 5) < nloc) wbits[w + 1] = (uint32_t)(mask >> 32);
+    mine += (key[j] != 0 && d == th.b1) ? 1u : 0u;
+  }
+  if (all || !buffered) return;
+  // Candidates of bin b1: positions from a prefix count, one global
+  // reservation per workgroup.
+  uint32_t m;
+  uint32_t pos = block_exclusive_scan<kPassThreads>(mine, wave_sum, &m);
+  if (threadIdx.x == 0) g_base = m ? atomicAdd(ws.cnt + b, m) : 0u;
+  __syncthreads();
+  pos += g_base;
+  uint2* gc = ws.cand + (int64_t)b * kTopkCandCap;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (key[j] != 0 && (key[j] >> 20) == th.b1) {
+      if (pos < (uint32_t)kTopkCandCap) gc[pos] = make_uint2(key[j], (uint32_t)(s0 + j * kPassThreads + threadIdx.x));
+      ++pos;
+    }
+  }
+}
+
+struct FinalSmem {
+  int32_t pool[CSA2_TOPK_MAX];  // the sequence's pool block ids (pool mode)
+  uint32_t hist[kTopkBins];
+  uint32_t sel[kTopkMaxWords];
+  uint32_t tie[kTopkMaxWords];
+  uint32_t cand_key[kTopkCandCap];
+  uint32_t cand_slot[kTopkCandCap];
+  uint32_t wave_sum[kFinalWaves];
+  uint32_t found[2];
+};
+
+__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* __restrict__ scores, int64_t n,
+                                                                   const int32_t* __restrict__ lens,
+                                                                   int32_t len_div, int32_t k,
+                                                                   const int32_t* __restrict__ pool,
+                                                                   int32_t n_pool, int32_t blk, TopkWs ws,
+                                                                   int32_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
+  FinalSmem& sm = *reinterpret_cast<FinalSmem*>(smem_raw);
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  int64_t nv = n;
-  if (lens) {
-    const int64_t L = lens[b];
-    nv = min(n, L > 0 ? (L + len_div - 1) / len_div : 0);
-  }
-  const int nvalid = (int)nv;
+  const int nvalid = (int)valid_slots(n, lens, len_div, b);
   const int words = (nvalid + 31) / 32;
+  const bool direct = n <= kDirectMax;
   const float* sc = scores + (int64_t)b * n;
-
-  for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
-  for (int i = tid; i < words; i += kThreads) {
-    sm.sel[i] = 0;
-    sm.tie[i] = 0;
-  }
-  if (tid == 0) sm.n_cand = 0;
-  __syncthreads();
-
-  // Pass 1: histogram of the top digit.
-  for (int i = tid; i < nvalid; i += kThreads) {
-    const uint32_t key = order_key(sc[i]);
-    if (key) atomicAdd(&sm.hist[key >> 20], 1u);
-  }
-  __syncthreads();
-
-  uint32_t total = 0;
-  {
-    uint32_t mine = 0;
-    for (int i = tid; i < kBins; i += kThreads) mine += sm.hist[i];
-    block_exclusive_scan(mine, sm, &total);
-  }
   const uint32_t kk = (uint32_t)k;
-  uint32_t T = 0;       // selected: key > T, plus the first `ties` keys == T
-  uint32_t ties = 0;
+  uint32_t* gh = ws.hist + (int64_t)b * kTopkBins;
 
-  if (total <= kk) {
-    for (int i = tid; i < nvalid; i += kThreads)
-      if (order_key(sc[i])) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
+  // Direct path: this thread's scores are loaded first (clamped), overlapping
+  // the histogram and pool loads.
+  constexpr int kPerDirect = kDirectMax / kFinalThreads;
+  float dv[kPerDirect];
+  if (direct) {
+#pragma unroll
+    for (int j = 0; j < kPerDirect; ++j) dv[j] = sc[min(j * kFinalThreads + tid, max(nvalid - 1, 0))];
+  }
+  if (pool) {  // staged for the id mapping at the end (n_pool <= CSA2_TOPK_MAX)
+    const int32_t* pb = pool + (int64_t)b * n_pool;
+    int32_t pv[CSA2_TOPK_MAX / kFinalThreads];
+#pragma unroll
+    for (int j = 0; j < CSA2_TOPK_MAX / kFinalThreads; ++j) pv[j] = pb[min(tid + kFinalThreads * j, n_pool - 1)];
+#pragma unroll
+    for (int j = 0; j < CSA2_TOPK_MAX / kFinalThreads; ++j)
+      if (tid + kFinalThreads * j < n_pool) sm.pool[tid + kFinalThreads * j] = pv[j];
+  }
+  const Threshold th = load_threshold<kFinalThreads>(gh, sm.hist, sm.wave_sum, sm.found, kk);
+  // The global histogram and counter are consumed (the filter pass appended
+  // exactly th.in_bin candidates): leave them zero for the next call.
+  const uint32_t n_cand_global = direct ? 0u : th.in_bin;
+  for (int i = tid; i < kTopkBins; i += kFinalThreads) gh[i] = 0;
+  if (tid == 0) ws.cnt[b] = 0;
+
+  const bool all = th.total <= kk;
+  const bool buffered = th.in_bin <= (uint32_t)kTopkCandCap;
+  for (int i = tid; i < words; i += kFinalThreads) sm.tie[i] = 0;
+  if (direct) {
+    // Filter pass in this workgroup (scores already loaded).
+    constexpr int kPer = kPerDirect;
+    for (int i = tid; i < words; i += kFinalThreads) sm.sel[i] = 0;
+    __syncthreads();
+    uint32_t key[kPer];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = j * kFinalThreads + tid;
+      key[j] = i < nvalid ? order_key(dv[j]) : 0u;
+      const uint32_t d = key[j] >> 20;
+      const uint64_t mask = __ballot(key[j] != 0 && (all || d > th.b1));
+      const int w = (i - lane_id()) >> 5;
+      if (lane_id() == 0 && (uint32_t)mask) sm.sel[w] = (uint32_t)mask;
+      if (lane_id() == 32 && (uint32_t)(mask >> 32)) sm.sel[w + 1] = (uint32_t)(mask >> 32);
+      mine += (key[j] != 0 && d == th.b1) ? 1u : 0u;
+    }
+    if (!all && buffered) {
+      uint32_t dummy;
+      uint32_t pos = block_exclusive_scan<kFinalThreads>(mine, sm.wave_sum, &dummy);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        if (key[j] != 0 && (key[j] >> 20) == th.b1) {
+          sm.cand_key[pos] = key[j];
+          sm.cand_slot[pos] = (uint32_t)(j * kFinalThreads + tid);
+          ++pos;
+        }
+      }
+    }
   } else {
-    find_threshold_bin(sm, kBins, kk);
-    const uint32_t b1 = sm.found_bin;
-    const uint32_t need1 = kk - sm.found_above;
-    const uint32_t in_bin = sm.hist[b1];
-    __syncthreads();
-
-    // Pass 2: keys above bin b1 are selected; keys in it are buffered.
-    for (int i = tid; i < nvalid; i += kThreads) {
-      const uint32_t key = order_key(sc[i]);
-      const uint32_t d = key >> 20;
-      if (!key) continue;
-      if (d > b1) {
-        atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
-      } else if (d == b1 && in_bin <= (uint32_t)kCandCap) {
-        const uint32_t p = atomicAdd(&sm.n_cand, 1u);
-        sm.cand_key[p] = key;
-        sm.cand_slot[p] = (uint32_t)i;
+    // Bitmap and candidates of the filter pass; clamped loads, all in flight together.
+    const uint32_t* gb = ws.bits + (int64_t)b * ws.words_cap;
+    constexpr int kWordsPer = kTopkMaxWords / kFinalThreads;
+    uint32_t wv[kWordsPer];
+#pragma unroll
+    for (int j = 0; j < kWordsPer; ++j) wv[j] = gb[min(tid + kFinalThreads * j, max(words - 1, 0))];
+#pragma unroll
+    for (int j = 0; j < kWordsPer; ++j)
+      if (tid + kFinalThreads * j < words) sm.sel[tid + kFinalThreads * j] = wv[j];
+    if (!all && buffered && n_cand_global > 0) {
+      const uint2* gc = ws.cand + (int64_t)b * kTopkCandCap;
+      constexpr int kCandPer = kTopkCandCap / kFinalThreads;
+      uint2 cv[kCandPer];
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) cv[j] = gc[min<uint32_t>(tid + kFinalThreads * j, n_cand_global - 1)];
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) {
+        const uint32_t c = tid + kFinalThreads * j;
+        if (c < n_cand_global) {
+          sm.cand_key[c] = cv[j].x;
+          sm.cand_slot[c] = cv[j].y;
+        }
       }
     }
-    for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
-    __syncthreads();
+  }
+  __syncthreads();
 
-    const bool buffered = in_bin <= (uint32_t)kCandCap;
-    const int nc = (int)in_bin;
-    // Digit 2: bits 19..8 among keys of bin b1.
+  uint32_t ties = 0;
+  if (!all) {
+    const int nc = (int)th.in_bin;
+    const int nc_round = (nc + kFinalThreads - 1) / kFinalThreads * kFinalThreads;
+    for (int i = tid; i < kTopkBins; i += kFinalThreads) sm.hist[i] = 0;
+    __syncthreads();
+    // Digit 2: bits 19..8 among the keys of bin b1.
     if (buffered) {
-      for (int c = tid; c < nc; c += kThreads) atomicAdd(&sm.hist[(sm.cand_key[c] >> 8) & 0xFFFu], 1u);
+      for (int c = tid; c < nc; c += kFinalThreads) atomicAdd(&sm.hist[(sm.cand_key[c] >> 8) & 0xFFFu], 1u);
     } else {
-      for (int i = tid; i < nvalid; i += kThreads) {
+      for (int i = tid; i < nvalid; i += kFinalThreads) {
         const uint32_t key = order_key(sc[i]);
-        if (key && (key >> 20) == b1) atomicAdd(&sm.hist[(key >> 8) & 0xFFFu], 1u);
+        if (key && (key >> 20) == th.b1) atomicAdd(&sm.hist[(key >> 8) & 0xFFFu], 1u);
       }
     }
     __syncthreads();
-    find_threshold_bin(sm, kBins, need1);
-    const uint32_t b2 = sm.found_bin;
-    const uint32_t need2 = need1 - sm.found_above;
-    for (int i = tid; i < 256; i += kThreads) sm.hist[i] = 0;
+    find_threshold_bin<kFinalThreads>(sm.hist, kTopkBins, th.need1, sm.wave_sum, sm.found);
+    const uint32_t b2 = sm.found[0];
+    const uint32_t need2 = th.need1 - sm.found[1];
+    for (int i = tid; i < 256; i += kFinalThreads) sm.hist[i] = 0;
     __syncthreads();
-    const uint32_t pre2 = (b1 << 12) | b2;
-    // Digit 3: bits 7..0 among keys with the first two digits.
+    const uint32_t pre2 = (th.b1 << 12) | b2;
+    // Digit 3: bits 7..0 among keys with the first two digits (integer-valued
+    // scores share their low bits: group the atomics per wavefront).
     if (buffered) {
-      for (int c = tid; c < nc; c += kThreads) {
-        const uint32_t key = sm.cand_key[c];
-        if ((key >> 8) == pre2) atomicAdd(&sm.hist[key & 0xFFu], 1u);
+      for (int c = tid; c < nc_round; c += kFinalThreads) {
+        const uint32_t key = c < nc ? sm.cand_key[c] : 0u;
+        wave_hist_add_grouped(sm.hist, key & 0xFFu, c < nc && (key >> 8) == pre2);
       }
     } else {
-      for (int i = tid; i < nvalid; i += kThreads) {
-        const uint32_t key = order_key(sc[i]);
-        if (key && (key >> 8) == pre2) atomicAdd(&sm.hist[key & 0xFFu], 1u);
+      const int nv_round = (nvalid + kFinalThreads - 1) / kFinalThreads * kFinalThreads;
+      for (int i = tid; i < nv_round; i += kFinalThreads) {
+        const uint32_t key = i < nvalid ? order_key(sc[i]) : 0u;
+        wave_hist_add_grouped(sm.hist, key & 0xFFu, key != 0 && (key >> 8) == pre2);
       }
     }
     __syncthreads();
-    find_threshold_bin(sm, 256, need2);
-    T = (pre2 << 8) | sm.found_bin;
-    ties = need2 - sm.found_above;
-
+    find_threshold_bin<kFinalThreads>(sm.hist, 256, need2, sm.wave_sum, sm.found);
+    const uint32_t T = (pre2 << 8) | sm.found[0];
+    ties = need2 - sm.found[1];
     // Keys of bin b1 above T are selected, keys equal to T are tie candidates.
     if (buffered) {
-      for (int c = tid; c < nc; c += kThreads) {
+      for (int c = tid; c < nc; c += kFinalThreads) {
         const uint32_t key = sm.cand_key[c], i = sm.cand_slot[c];
         if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
         else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
       }
     } else {
-      for (int i = tid; i < nvalid; i += kThreads) {
+      for (int i = tid; i < nvalid; i += kFinalThreads) {
         const uint32_t key = order_key(sc[i]);
-        if ((key >> 20) != b1) continue;
+        if (!key || (key >> 20) != th.b1) continue;
         if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
         else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
       }
@@ -224,14 +411,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   }
 
   // Each thread owns a contiguous run of bitmap words.
-  const int per = (words + kThreads - 1) / kThreads;
+  const int per = (words + kFinalThreads - 1) / kFinalThreads;
   const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
-
   if (ties > 0) {
     uint32_t cnt = 0;
     for (int w = w0; w < w1; ++w) cnt += __popc(sm.tie[w]);
     uint32_t dummy;
-    uint32_t rank = block_exclusive_scan(cnt, sm, &dummy);
+    uint32_t rank = block_exclusive_scan<kFinalThreads>(cnt, sm.wave_sum, &dummy);
     for (int w = w0; w < w1 && rank < ties; ++w) {
       uint32_t x = sm.tie[w];
       const uint32_t pc = __popc(x);
@@ -254,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   uint32_t cnt = 0;
   for (int w = w0; w < w1; ++w) cnt += __popc(sm.sel[w]);
   uint32_t n_sel;
-  uint32_t pos = block_exclusive_scan(cnt, sm, &n_sel);
+  uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, sm.wave_sum, &n_sel);
   int32_t* ob = out + (int64_t)b * k;
   for (int w = w0; w < w1; ++w) {
     uint32_t x = sm.sel[w];
@@ -263,30 +449,56 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       x &= x - 1;
       const int64_t slot = (int64_t)w * 32 + bit;
       int64_t id = slot;
-      if (pool) id = (int64_t)pool[(int64_t)b * n_pool + slot / blk] * blk + slot % blk;
+      if (pool) id = (int64_t)sm.pool[slot / blk] * blk + slot % blk;
       if (pos < kk) ob[pos] = (int32_t)id;
       ++pos;
     }
   }
-  for (uint32_t i = n_sel + tid; i < kk; i += kThreads) ob[i] = -1;
+  for (uint32_t i = n_sel + tid; i < kk; i += kFinalThreads) ob[i] = -1;
 }
 
 }  // namespace
 
+size_t topk_workspace_bytes(int64_t n, int32_t n_seq) {
+  const int64_t words = (n + 31) / 32;
+  return (size_t)n_seq * (kTopkBins * sizeof(uint32_t) + sizeof(uint32_t) + words * sizeof(uint32_t) +
+                          kTopkCandCap * sizeof(uint2)) + 64;
+}
+
+TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq) {
+  TopkWs w;
+  char* p = reinterpret_cast<char*>(ws);
+  w.cand = reinterpret_cast<uint2*>(p);
+  p += (size_t)n_seq * kTopkCandCap * sizeof(uint2);
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)n_seq * kTopkBins * sizeof(uint32_t);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)n_seq * sizeof(uint32_t);
+  w.words_cap = (n + 31) / 32;
+  w.bits = reinterpret_cast<uint32_t*>(p);
+  return w;
+}
+
 csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
-                        const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, int32_t n_seq,
-                        hipStream_t stream) {
+                        const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, const TopkWs& ws,
+                        bool hist_ready, int32_t n_seq, hipStream_t stream) {
   if (n_seq == 0) return CSA2_OK;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_final_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sizeof(TopkSmem)) != hipSuccess)
+                            (int)sizeof(FinalSmem)) != hipSuccess)
       return launch_status("csa2_topk (shared memory attribute)");
     attr_set = true;
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(n_seq), dim3(kThreads), sizeof(TopkSmem), stream, scores, n,
-                     lens, len_div, k, pool, n_pool, blk, out);
+  if (!hist_ready && n > 0)
+    hipLaunchKernelGGL(topk_hist_kernel, dim3((uint32_t)((n + kHistSlots - 1) / kHistSlots), n_seq),
+                       dim3(kPassThreads), 0, stream, scores, n, lens, len_div, ws.hist);
+  if (n > kDirectMax)
+    hipLaunchKernelGGL(topk_filter_kernel, dim3((uint32_t)((n + kFilterSlots - 1) / kFilterSlots), n_seq),
+                       dim3(kPassThreads), 0, stream, scores, n, lens, len_div, k, ws);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(n_seq), dim3(kFinalThreads), sizeof(FinalSmem), stream, scores,
+                     n, lens, len_div, k, pool, n_pool, blk, ws, out);
   return launch_status("csa2_topk");
 }
 

@@ -1,0 +1,43 @@
+// Workspace of the Top-k pipeline (internal; see topk.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa2.h"
+
+namespace csa2 {
+
+constexpr int kTopkBins = 4096;                        // top-digit histogram (12 bits)
+constexpr int kTopkCandCap = 8192;                     // keys buffered from the threshold bin
+constexpr int kTopkMaxWords = CSA2_TOPK_NMAX / 32;     // selection bitmap words
+
+// Per-sequence regions of one workspace.  hist and cnt must be zero when a
+// Top-k call starts; the call leaves them zero.
+struct TopkWs {
+  uint32_t* hist;     // [n_seq][kTopkBins]
+  uint32_t* cnt;      // [n_seq] candidates appended by the filter pass
+  uint32_t* bits;     // [n_seq][words_cap] selection bitmap of the filter pass
+  uint2* cand;        // [n_seq][kTopkCandCap] (key, slot)
+  int64_t words_cap;
+};
+
+// Order-preserving key of a score; NaN and -inf (non-candidates) map to 0,
+// -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0;  // NaN
+  if (u == 0xFF800000u) return 0;                  // -inf
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+size_t topk_workspace_bytes(int64_t n, int32_t n_seq);
+TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq);
+// hist_ready: ws.hist already holds the histogram of these scores (written by
+// the indexer-score kernel), so the histogram pass is skipped.
+csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
+                        const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, const TopkWs& ws,
+                        bool hist_ready, int32_t n_seq, hipStream_t stream);
+
+}  // namespace csa2

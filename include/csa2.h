@@ -138,12 +138,17 @@ csa2_status csa2_index_score(const uint16_t* q, const float* w, const uint16_t* 
  * keep the min(k, #candidates) best by (score descending, slot ascending:
  * ties go to the lower position), and write their ids in ascending order to
  * out [n_seq][k], padding with -1.  The id of slot i is i, or with a pool
- * pool[b][i/blk]*blk + i%blk (pool [n_seq][n_pool], n == n_pool*blk; pool
- * ids ascending makes slot order = id order).  -0 and +0 are equal.
+ * pool[b][i/blk]*blk + i%blk (pool [n_seq][n_pool], n == n_pool*blk,
+ * n_pool <= CSA2_TOPK_MAX; pool ids ascending makes slot order = id order).
+ * -0 and +0 are equal.
+ * ws: device workspace of csa2_topk_workspace_size(n, n_seq) bytes,
+ * 16-byte aligned, zero-filled before its first use; every call leaves it
+ * ready for the next one (calls sharing a workspace must not overlap).
  * Limits: 1 <= k <= CSA2_TOPK_MAX, n <= CSA2_TOPK_NMAX. */
+size_t csa2_topk_workspace_size(int64_t n, int32_t n_seq);
 csa2_status csa2_topk(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
-                      const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, int32_t n_seq,
-                      void* stream);
+                      const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, void* ws,
+                      size_t ws_bytes, int32_t n_seq, void* stream);
 
 /* Steps (d)+(e): sparse + SWA attention of n_q queries.
  * [P1 "Compressed Sparse Attention 2 (CSA2)"]: each layer attends with its
@@ -159,7 +164,8 @@ csa2_status csa2_topk(const float* scores, int64_t n, const int32_t* lens, int32
  *   swa [*][512] bf16 rows;   swa_len [n_q] int32 (device), each <= swa_max
  *   out [n_q][16][512] f32
  *   ws  device workspace of csa2_sparse_attn_workspace_size(...) bytes,
- *       256-byte aligned, contents need no initialisation.
+ *       16-byte aligned; no initialisation needed.  Calls that share a
+ *       workspace must not overlap in time.
  * Limits: k_idx + swa_max >= 1, swa_max <= 4096. */
 size_t csa2_sparse_attn_workspace_size(int32_t n_q, int32_t k_idx, int32_t swa_max);
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,

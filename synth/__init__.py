@@ -117,15 +117,52 @@ def _values(h: np.ndarray, kind: int) -> np.ndarray:
     raise ValueError(f"unknown value kind {kind}")
 
 
-def gen_rows(seed: int, tid: int, kind: int, b, rows, dim: int) -> np.ndarray:
-    """bf16 bit patterns [len(b)][len(rows)][dim] of row-structured tensor ``tid``.
-
-    ``b`` and ``rows`` are integer sequences (sequence ids and row ids)."""
+def gen_rows_numpy(seed: int, tid: int, kind: int, b, rows, dim: int) -> np.ndarray:
+    """Definition of :func:`gen_rows` in numpy (slow for large tensors)."""
     b = np.asarray(b, dtype=np.uint64).reshape(-1, 1, 1)
     rows = np.asarray(rows, dtype=np.uint64).reshape(1, -1, 1)
     d = np.arange(dim, dtype=np.uint64).reshape(1, 1, -1)
     idx = ((b << np.uint64(24)) + rows) * np.uint64(dim) + d
     return _values(splitmix64_outputs(seed, tid, idx), kind)
+
+
+_HOST_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gen_host.c")
+_HOST_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2_synth_host.so")
+
+
+def build_host(force: bool = False) -> str:
+    """Compile the host generator (plain C, gcc)."""
+    import subprocess
+
+    if force or not os.path.exists(_HOST_LIB) or os.path.getmtime(_HOST_LIB) < os.path.getmtime(_HOST_SRC):
+        tmp = _HOST_LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-o", tmp, _HOST_SRC])
+        os.replace(tmp, _HOST_LIB)
+    return _HOST_LIB
+
+
+@lru_cache(maxsize=1)
+def _host_lib():
+    lib = ctypes.CDLL(build_host())
+    P = ctypes.c_void_p
+    lib.synth_gen_rows_host.argtypes = [ctypes.c_uint64, ctypes.c_int32, P, ctypes.c_int64, P,
+                                        ctypes.c_int64, ctypes.c_int32, P, P]
+    lib.synth_gen_rows_host.restype = None
+    return lib
+
+
+def gen_rows(seed: int, tid: int, kind: int, b, rows, dim: int) -> np.ndarray:
+    """bf16 bit patterns [len(b)][len(rows)][dim] of row-structured tensor ``tid``.
+
+    ``b`` and ``rows`` are integer sequences (sequence ids and row ids).
+    Computed by the C generator; equal to :func:`gen_rows_numpy`."""
+    bs = np.ascontiguousarray(np.asarray(b, dtype=np.int64).reshape(-1))
+    rs = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    out = np.empty((len(bs), len(rs), dim), np.uint16)
+    tab = ntab()
+    _host_lib().synth_gen_rows_host(stream_key(seed, tid), kind, bs.ctypes.data, len(bs), rs.ctypes.data,
+                                    len(rs), dim, tab.ctypes.data, out.ctypes.data)
+    return out
 
 
 def gen_flat(seed: int, tid: int, kind: int, n: int) -> np.ndarray:

@@ -42,14 +42,22 @@ FAKE = 0x100000  # never dereferenced: every call below fails validation first
 
 
 def test_topk_rejects_bad_k_and_n(csa2):
-    assert csa2._topk(FAKE, 100, None, 1, 0, None, 0, 8, FAKE, 1, None) == -2
-    assert "k must be" in _err(csa2)
-    assert csa2._topk(FAKE, 100, None, 1, 4096, None, 0, 8, FAKE, 1, None) == -2
-    assert csa2._topk(FAKE, 300000, None, 1, 512, None, 0, 8, FAKE, 1, None) == -2
-    assert csa2._topk(FAKE, 100, None, 1, 512, FAKE, 10, 8, FAKE, 1, None) == -2  # n != n_pool*blk
-    assert csa2._topk(None, 100, None, 1, 512, None, 0, 8, FAKE, 1, None) == -1
-    assert csa2._topk(FAKE, 100, None, 0, 512, None, 0, 8, FAKE, 1, None) == -1  # len_div
-    assert csa2._topk(None, 100, None, 1, 512, None, 0, 8, None, 0, None) == 0   # n_seq = 0: no-op
+    W = 1 << 30
+
+    def call(scores=FAKE, n=100, len_div=1, k=512, pool=None, n_pool=0, ws=FAKE, ws_bytes=W, n_seq=1):
+        return csa2._topk(scores, n, None, len_div, k, pool, n_pool, 8, FAKE, ws, ws_bytes, n_seq, None)
+
+    assert call(k=0) == -2 and "k must be" in _err(csa2)
+    assert call(k=4096) == -2
+    assert call(n=300000) == -2
+    assert call(pool=FAKE, n_pool=10) == -2          # n != n_pool * blk
+    assert call(scores=None) == -1
+    assert call(ws=None) == -1
+    assert call(ws=FAKE + 8) == -1                   # alignment
+    assert call(len_div=0) == -1
+    assert call(ws_bytes=csa2.topk_workspace_size(100, 1) - 1) == -3
+    assert call(scores=None, n_seq=0) == 0           # n_seq = 0: no-op
+    assert csa2.topk_workspace_size(100, 2) > csa2.topk_workspace_size(100, 1) > 0
 
 
 def test_index_score_rejects_bad_shapes(csa2):

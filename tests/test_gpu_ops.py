@@ -190,6 +190,23 @@ def test_topk_matches_oracle(csa2, n, k, levels, L):
         assert np.array_equal(got[b], ref), b
 
 
+def test_topk_workspace_reused_across_calls(csa2):
+    """One workspace, several calls of different lengths and paths: the
+    histogram and counters the calls leave behind must be zero."""
+    rng = np.random.default_rng(21)
+    n_seq = 3
+    n_max = 70000
+    ws = torch.zeros(csa2.topk_workspace_size(n_max, n_seq), dtype=torch.uint8, device="cuda")
+    print_case("topk shared workspace")
+    for n, k, levels in [(70000, 2048, 300), (5000, 512, 40), (70000, 512, 2), (1000, 512, 3)]:
+        sc = rng.integers(0, levels, size=(n_seq, n)).astype(np.float32)
+        out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+        csa2.topk(dev(sc), k, out, ws=ws[:csa2.topk_workspace_size(n, n_seq)])
+        got = out.cpu().numpy()
+        for b in range(n_seq):
+            assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), (n, k, b)
+
+
 def test_topk_signed_scores_and_zero_signs(csa2):
     rng = np.random.default_rng(11)
     sc = rng.standard_normal((1, 10000)).astype(np.float32)
@@ -278,3 +295,33 @@ def test_sparse_attn_all_positions_is_dense(csa2):
     p = np.exp(z - z.max(axis=1, keepdims=True))
     ref = (p / p.sum(axis=1, keepdims=True)) @ x
     assert_attention_close(out.cpu().numpy()[0], ref, "dense")
+
+
+def test_device_generator_matches_host_generator(csa2):
+    print_case("synth device fill")
+    for kind in (synth.INT9, synth.NORMAL):
+        t = torch.empty(3, 100, 64, dtype=torch.int16, device="cuda")
+        synth.fill_rows_device(t, 5, 77, kind, b0=2, row0=1000)
+        assert np.array_equal(host_u16(t), synth.gen_rows(5, 77, kind, [2, 3, 4], np.arange(1000, 1100), 64))
+
+
+def test_sparse_attn_workspace_reused_across_calls(csa2):
+    n_q, cap = 2, 600
+    src = kv_source(2, n_q, cap)
+    kv = _device_cache(csa2, src)
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 2), synth.NORMAL, range(n_q), np.arange(16), 512)
+    swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 2), synth.NORMAL, range(n_q), np.arange(128), 512)
+    ws = torch.zeros(csa2.sparse_attn_workspace_size(n_q, 512, 128), dtype=torch.uint8, device="cuda")
+    print_case("sparse_attn shared workspace")
+    outs = []
+    for rep in range(3):
+        idx = np.stack([np.sort(np.random.default_rng(rep * 10 + b).choice(cap, 512, replace=False))
+                        for b in range(n_q)]).astype(np.int32)
+        out = torch.empty(n_q, 16, 512, dtype=torch.float32, device="cuda")
+        csa2.sparse_attn(dev(q), kv, dev(idx), dev(swa), dev(np.array([128, 77], np.int32)), SM_SCALE, out, ws=ws)
+        outs.append((idx, out.cpu().numpy()))
+    for idx, got in outs:
+        for b in range(n_q):
+            codes, scales = oracle.quant_rows(src[b])
+            ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa[b], [128, 77][b], SM_SCALE)
+            assert_attention_close(got[b], ref)

@@ -28,6 +28,8 @@ CASES = {
     "hier_small": (C.HIER_1M.with_(n_seq=2, L0=8 * 3000 + 5), 1),
     "decoder20_small": (C.DECODER_20L_1M.with_(n_seq=2, L0=8 * 2500 + 3, q_sets=2), 3),
     "decoder20_short_ctx": (C.DECODER_20L_1M.with_(n_seq=2, L0=300, q_sets=2, pool_blocks=16), 2),
+    # more than 32K blocks: the multi-workgroup filter pass of the block Top-k
+    "hier_long": (C.HIER_1M.with_(n_seq=2, L0=8 * 40000 + 3), 1),
 }
 
 

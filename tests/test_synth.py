@@ -33,3 +33,11 @@ def test_rows_do_not_depend_on_buffer_shape():
     b = synth.gen_rows(3, 11, synth.NORMAL, [5], np.arange(4, 8), 512)
     assert np.array_equal(a[1, 4:8], b[0])
     assert not np.array_equal(a[0], a[1])
+
+
+def test_c_generator_equals_numpy_definition():
+    rows = np.array([0, 1, 5, 1 << 20, (1 << 24) - 1])
+    for kind in (synth.INT9, synth.NORMAL):
+        a = synth.gen_rows(7, 123, kind, [0, 3, 15], rows, 64)
+        b = synth.gen_rows_numpy(7, 123, kind, [0, 3, 15], rows, 64)
+        assert np.array_equal(a, b)
