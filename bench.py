@@ -27,6 +27,42 @@ import time
 METRIC = "CSA2 decode (seq·layer)-steps/s at 1M ctx + achieved HBM GB/s as % of peak"
 PEAK_HBM_GBPS = 8000.0
 
+# HBM bytes per call measured with the FETCH_SIZE and WRITE_SIZE counters
+# (scaled by a 1 GiB copy; see profiles/), keyed by op, with the SHA-256 of
+# the kernel sources they were taken on: a figure is reported only while
+# those sources are unchanged.
+MEASURED_TRAFFIC = {
+    "sparse_attn": {"bytes": 12814888, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+                    "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
+                                "b837a69f2edab4fe3081ef6e1e3259c5b87a45d602dbc4a7d20f6de078544985",
+                                "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                                "4b06a55aa18d35a33a75b38bfaddc7b47986a52faa4267ea1792d0ee40b3312f"}},
+    "block_scan": {"bytes": 279875254, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+                   "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                               "9bebab09e10532f6aebd4dfd2350e391aa610582dbe7cef53b68a995b5d96f0f",
+                               "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                               "4b06a55aa18d35a33a75b38bfaddc7b47986a52faa4267ea1792d0ee40b3312f"}},
+}
+
+
+def measured_traffic(op_key: str):
+    """Counter-measured HBM bytes per call of op_key, or None when unmeasured
+    or when its kernel sources changed since the counters were taken."""
+    import hashlib
+
+    rec = MEASURED_TRAFFIC.get(op_key)
+    if rec is None:
+        return None
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel, digest in rec["sources"].items():
+        try:
+            with open(os.path.join(root, rel), "rb") as fh:
+                if hashlib.sha256(fh.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
+    return rec["bytes"]
+
 
 def algorithmic_bytes(cfg, L: int) -> dict:
     """Bytes the method must move in one decode step (each distinct byte once).
@@ -85,6 +121,111 @@ def cpu_baseline(cfg, step: int, seqs, threads: int):
     return res, dt
 
 
+def _graph_time_us(fn, per_graph: int = 20, replays: int = 10, graph: bool = True) -> float:
+    """Average GPU time of fn() (a sequence of launches on the current
+    stream): per_graph calls captured in one HIP graph, replayed, timed with
+    HIP events on the stream (graph=False: the same calls launched eagerly)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    if not graph:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(per_graph * replays):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / (replays * per_graph)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(per_graph):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (replays * per_graph)
+
+
+def op_rooflines(cfg, inp, total_steps, graph: bool = True):
+    """Algorithmic bytes per call, time and GB/s of every op of the step, each
+    called through the C ABI on the step's own buffers (the scheduler fuses
+    the Top-k histogram into the score kernel; a standalone Top-k builds it
+    itself, so its figure here includes that pass).
+
+    Bytes per call (n = sequences): block scan n*ceil(L/8)*(128+4) (block
+    keys read, scores written); pool score n*16384*(128+4) (indexer keys of
+    the pool positions, scores); Top-k n*slots*4 (scores read once);
+    attention n*(512*4 + 512*288 + 128*1024 + 16*1024 + 16*512*4) (indices,
+    selected FP4 rows, SWA window, main Q, f32 output)."""
+    import torch
+
+    import fp4_kv_cache_quant_amd as csa2
+    from synth.configs import DECODE_CONFIGS
+
+    n = cfg.n_seq
+    L = int(inp.lens[0].item())
+    nblk = -(-L // cfg.blk)
+    blk_cap = cfg.blk_cap(total_steps)
+    pool_slots = cfg.pool_blocks * cfg.blk
+    q0 = inp.idx_q[0][0]
+    bscores = torch.empty(n, blk_cap, dtype=torch.float32, device="cuda")
+    pscores = torch.empty(n, pool_slots, dtype=torch.float32, device="cuda")
+    pool = torch.empty(n, cfg.pool_blocks, dtype=torch.int32, device="cuda")
+    idx = torch.empty(n, cfg.topk, dtype=torch.int32, device="cuda")
+    out = torch.empty(n, 16, 512, dtype=torch.float32, device="cuda")
+    tws = torch.zeros(csa2.topk_workspace_size(blk_cap, n), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(csa2.sparse_attn_workspace_size(n, cfg.topk, cfg.swa), dtype=torch.uint8, device="cuda")
+    csa2.index_score(q0, inp.blk_k, inp.lens, bscores, len_div=cfg.blk)
+    csa2.topk(bscores, cfg.pool_blocks, pool, lens=inp.lens, len_div=cfg.blk, ws=tws)
+    csa2.index_score(q0, inp.idx_k, inp.lens, pscores, pool=pool, blk=cfg.blk)
+    csa2.topk(pscores, cfg.topk, idx, pool=pool, blk=cfg.blk, ws=tws)
+    sel_layers = sum(1 for m, _, _ in cfg.layers if m != 2)
+    ops = [
+        ("block_scan", "block scan (index_score, block keys)", 1, n * nblk * 132,
+         lambda: csa2.index_score(q0, inp.blk_k, inp.lens, bscores, len_div=cfg.blk)),
+        ("block_topk", "block Top-2048 (topk)", 1, n * nblk * 4,
+         lambda: csa2.topk(bscores, cfg.pool_blocks, pool, lens=inp.lens, len_div=cfg.blk, ws=tws)),
+        ("pool_score", "pool score (index_score, pool)", sel_layers, n * pool_slots * 132,
+         lambda: csa2.index_score(q0, inp.idx_k, inp.lens, pscores, pool=pool, blk=cfg.blk)),
+        ("pool_topk", "pool Top-512 (topk)", sel_layers, n * pool_slots * 4,
+          lambda: csa2.topk(pscores, cfg.topk, idx, pool=pool, blk=cfg.blk, ws=tws)),
+        ("sparse_attn", "sparse+SWA attention (sparse_attn: chunk + combine kernels)", len(cfg.layers),
+         n * (cfg.topk * 4 + cfg.topk * 288 + cfg.swa * 1024 + 16 * 1024 + 16 * 512 * 4),
+         lambda: csa2.sparse_attn(inp.main_q[0][0], inp.kv[0], idx, inp.swa[0], inp.swa_len, 512 ** -0.5, out,
+                                  ws=aws)),
+    ]
+    res = []
+    for key, name, per_step, nbytes, fn in ops:
+        us = _graph_time_us(fn, graph=graph)
+        res.append({"key": key, "op": name, "launches_per_step": per_step, "bytes_per_launch": nbytes,
+                    "avg_us": round(us, 2), "us_per_step": round(us * per_step, 1),
+                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                    "traffic_bytes": measured_traffic(key) if cfg.name == DECODE_CONFIGS["decoder20_1m"].name else None})
+    return res
+
+
+def calibration_copy(nbytes: int = 1 << 30):
+    """A plain device copy of known size, for scaling the HBM-traffic
+    counters of a profile of this run (the copy reads and writes nbytes)."""
+    import torch
+
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def compare_step(cfg, gpu, ref) -> dict:
     """GPU step-0 results against the oracle sample: indices and pool
     bit-exact, attention rel. L2 <= 1e-3 and max abs <= 5e-3 per (seq, head)."""
@@ -116,6 +257,8 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--config", default="decoder20_1m")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a 1 GiB device copy (for scaling profiler traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the multi-GPU split of this path is designed but "
@@ -140,6 +283,9 @@ def main() -> int:
     build_s = time.perf_counter() - t_build
     nl = len(cfg.layers)
     stream = torch.cuda.current_stream()
+
+    if args.calibrate:
+        calibration_copy()
 
     # Step 0, eager: kept for the parity check against the oracle sample.
     sched.decode_step(ios[0])
@@ -189,35 +335,15 @@ def main() -> int:
     ab = algorithmic_bytes(cfg, L_mid)
     hbm_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
 
-    # Dominant kernel: the block-key scan of the hierarchical Full layer, the
-    # same launch the step makes (csa2_index_score over all block keys),
-    # timed with HIP events on the stream it runs on.
-    dom = None
-    if cfg.hierarchical:
-        blk_cap = cfg.blk_cap(total_steps)
-        scores = torch.empty(cfg.n_seq, blk_cap, dtype=torch.float32, device="cuda")
-        q0 = inp.idx_q[0][0]
-        for _ in range(3):
-            csa2.index_score(q0, inp.blk_k, inp.lens, scores, len_div=cfg.blk)
-        reps = max(10, K)
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record()
-        for _ in range(reps):
-            csa2.index_score(q0, inp.blk_k, inp.lens, scores, len_div=cfg.blk)
-        d1.record()
-        torch.cuda.synchronize()
-        dur_s = d0.elapsed_time(d1) * 1e-3 / reps
-        L_now = int(inp.lens[0].item())
-        nblk = -(-L_now // cfg.blk)
-        # keys read + scores written + indexer Q read, per launch
-        dom_bytes = cfg.n_seq * (nblk * 128 + nblk * 4 + 1024)
-        dom = {"kernel": "index_score_kernel<flat> (block keys)", "bytes_per_launch": dom_bytes,
-               "avg_us": dur_s * 1e6}
-        achieved = dom_bytes / dur_s / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
-    else:
-        roofline = None
+    # Per-op roofline: each op of the step on the step's buffers, timed with
+    # HIP events around graph replays on the stream the ops run on (no host
+    # launch gaps).  The op with the largest share of the step (time x calls
+    # per step) is the dominant one.
+    ops = op_rooflines(cfg, inp, total_steps, graph=not args.no_graph)
+    dom = max(ops, key=lambda o: o["us_per_step"])
+    roofline = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
+                "traffic": measured_traffic(dom["key"]) if cfg.name == DECODE_CONFIGS["decoder20_1m"].name else None}
 
     # CPU oracle on a bounded sample: step 0 of the first cpu_seqs sequences.
     cpu = parity = None
@@ -241,7 +367,7 @@ def main() -> int:
                    "swa": cfg.swa, "graph": bool(graphs)},
         "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": round(hbm_gbps, 1),
                 "frac_of_peak": round(hbm_gbps / PEAK_HBM_GBPS, 4), "parts": ab},
-        "roofline": roofline, "dominant_kernel": dom, "cpu_baseline": cpu, "parity_step0": parity,
+        "roofline": roofline, "dominant_op": dom, "ops": ops, "cpu_baseline": cpu, "parity_step0": parity,
         "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
     }
     print(json.dumps(line), flush=True)
