@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
     "sparse_attn", "sparse_attn_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
+    "prefill_index_score", "Prefill",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
 
@@ -53,6 +54,16 @@ class _StepIO(ctypes.Structure):
                 ("swa", _P), ("swa_len", _P), ("out", _P)]
 
 
+class _PrefillDesc(ctypes.Structure):
+    _fields_ = [("n_layers", _I32), ("layers", _P), ("n_entries", _I64), ("ratio", _I32), ("n_q", _I32),
+                ("t0", _I64), ("topk", _I32), ("swa", _I32), ("sm_scale", _F32)]
+
+
+class _PrefillIO(ctypes.Structure):
+    _fields_ = [("n_kv", _I32), ("kv", _P), ("entry_k", _P), ("idx_q", _P), ("idx_w", _P), ("main_q", _P),
+                ("swa", _P), ("out", _P), ("idx", _P)]
+
+
 def _sig(name, res, *args):
     f = getattr(_lib, name)
     f.restype = res
@@ -76,6 +87,10 @@ _sched_indices = _sig("csa2_sched_indices", _P, _P, _I32)
 _sched_pool = _sig("csa2_sched_pool", _P, _P)
 _sched_check = _sig("csa2_sched_check", _I32, _P, ctypes.POINTER(_I32))
 _sched_destroy = _sig("csa2_sched_destroy", None, _P)
+_prefill_score = _sig("csa2_prefill_index_score", _I32, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P)
+_prefill_ws = _sig("csa2_prefill_workspace_size", _SZ, ctypes.POINTER(_PrefillDesc))
+_prefill_chunk = _sig("csa2_prefill_chunk", _I32, ctypes.POINTER(_PrefillDesc), ctypes.POINTER(_PrefillIO),
+                      _P, _SZ, _P)
 
 
 class Csa2Error(RuntimeError):
@@ -253,6 +268,52 @@ class Sched:
         f = _I32()
         _check(_sched_check(self._h, ctypes.byref(f)))
         return f.value
+
+
+def prefill_index_score(q: torch.Tensor, keys: torch.Tensor, t0: int, ratio: int, scores: torch.Tensor,
+                        n_vis: torch.Tensor, w: Optional[torch.Tensor] = None, stream=None) -> None:
+    """q [n_q][8][64] bf16, keys [n_entries][64] bf16 -> scores [n_q][n_entries] f32, n_vis [n_q] int32."""
+    n_q, n_entries = scores.shape
+    assert q.numel() == n_q * IDX_HEADS * IDX_DIM and keys.numel() == n_entries * IDX_DIM
+    assert scores.dtype == torch.float32 and n_vis.dtype == torch.int32 and n_vis.numel() >= n_q
+    _check(_prefill_score(_ptr(q), _ptr(w), _ptr(keys), n_entries, t0, ratio, n_q, _ptr(scores), _ptr(n_vis),
+                          _stream(stream)))
+
+
+class Prefill:
+    """A causal prefill chunk of a layer group (csa2_prefill_chunk) with its
+    workspace (zero-filled once here, as the entry point requires)."""
+
+    def __init__(self, layers: Sequence[Layer], n_entries: int, ratio: int, n_q: int, t0: int, topk: int = 512,
+                 swa: int = 128, sm_scale: float = 512 ** -0.5):
+        self._arr = (_Layer * len(layers))(*[_Layer(l.mode, l.kv_id, int(l.hierarchical)) for l in layers])
+        self.desc = _PrefillDesc(len(layers), ctypes.cast(self._arr, _P), n_entries, ratio, n_q, t0, topk, swa,
+                                 sm_scale)
+        self.ws_bytes = int(_prefill_ws(ctypes.byref(self.desc)))
+        if self.ws_bytes == 0:
+            raise Csa2Error(-2, _last_error().decode(errors="replace"))
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.layers, self.n_q, self.topk = list(layers), n_q, topk
+
+    def prepare(self, kv: Sequence[FP4KV], entry_k, idx_q, main_q, swa, out, idx, idx_w=None) -> "_PrefillIO":
+        nl = len(self.layers)
+        kvs = (_FP4KV * len(kv))(*[k.c() for k in kv])
+        P = _P * nl
+
+        def arr(ts):
+            return P(*[_ptr(t) if t is not None else None for t in ts])
+
+        iq, mq, sw, ou, ix = arr(idx_q), arr(main_q), arr(swa), arr(out), arr(idx)
+        iw = arr(idx_w) if idx_w is not None else None
+        io = _PrefillIO(len(kv), ctypes.cast(kvs, _P), _ptr(entry_k), ctypes.cast(iq, _P),
+                        ctypes.cast(iw, _P) if iw is not None else None, ctypes.cast(mq, _P), ctypes.cast(sw, _P),
+                        ctypes.cast(ou, _P), ctypes.cast(ix, _P))
+        io._keep = (kvs, iq, mq, sw, ou, ix, iw, kv, entry_k, idx_q, main_q, swa, out, idx, idx_w)
+        return io
+
+    def run(self, io: "_PrefillIO", stream=None) -> None:
+        _check(_prefill_chunk(ctypes.byref(self.desc), ctypes.byref(io), _ptr(self.ws), self.ws_bytes,
+                              _stream(stream)))
 
 
 _hip = None

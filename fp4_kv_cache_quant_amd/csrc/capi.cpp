@@ -86,7 +86,7 @@ csa2_status check_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, in
                        int32_t swa_max, const float* out, const void* ws, size_t ws_bytes) {
   CSA2_REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ESHAPE, "csa2_sparse_attn: n_q must be in [0, 65535]");
   if (n_q == 0) return CSA2_OK;
-  CSA2_REQUIRE(q && kv && swa_len && out && ws, CSA2_EINVAL, "csa2_sparse_attn: null pointer");
+  CSA2_REQUIRE(q && kv && swa_len && out, CSA2_EINVAL, "csa2_sparse_attn: null pointer");
   CSA2_REQUIRE(k_idx >= 0 && swa_max >= 0 && k_idx + swa_max >= 1, CSA2_ESHAPE,
                "csa2_sparse_attn: need k_idx + swa_max >= 1");
   CSA2_REQUIRE(k_idx == 0 || idx, CSA2_EINVAL, "csa2_sparse_attn: null idx");
@@ -98,8 +98,9 @@ csa2_status check_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, in
   if (st != CSA2_OK) return st;
   CSA2_REQUIRE((n_q + q_per_seq - 1) / q_per_seq <= kv->n_seq, CSA2_ESHAPE,
                "csa2_sparse_attn: queries address more cache sequences than kv.n_seq");
-  CSA2_REQUIRE(ws_bytes >= attn_workspace_bytes(n_q, k_idx, swa_max), CSA2_ECAPACITY,
-               "csa2_sparse_attn: workspace too small");
+  const size_t need = attn_workspace_bytes(n_q, k_idx, swa_max);
+  CSA2_REQUIRE(need == 0 || ws, CSA2_EINVAL, "csa2_sparse_attn: null workspace");
+  CSA2_REQUIRE(ws_bytes >= need, CSA2_ECAPACITY, "csa2_sparse_attn: workspace too small");
   const uintptr_t a = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv->codes) |
                       reinterpret_cast<uintptr_t>(swa) | reinterpret_cast<uintptr_t>(out) |
                       reinterpret_cast<uintptr_t>(ws);

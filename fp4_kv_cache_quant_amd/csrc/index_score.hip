@@ -135,6 +135,104 @@ void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const float* w
                        key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, ghist);
 }
 
+// ------------------------------------------------------------------ prefill
+// Indexer scores of a causal prefill chunk: n_q queries (query i at token
+// t0 + i) against the keys of compressed entries, entry e visible to query i
+// iff e < vis_i = min(n_entries, (t0 + i + 1) / ratio).  This is a dense
+// contraction of (query, head) rows with entry keys, so both MFMA operands
+// carry real data: a 256-thread workgroup takes 32 queries (256 rows = 16
+// row tiles of 2 queries x 8 heads) against 512 entries (128 per
+// wavefront = 8 column tiles).  Each wavefront holds its entries' key
+// fragments in registers and walks the 16 row tiles, whose query fragments
+// come from LDS; per row tile the output lane holds heads 4(g%2)..+3 of
+// query 2*tile + g/2, so the same per-lane ReLU sum and one exchange
+// (xor 16) as the decode kernel give the score.  Scores go out through a
+// per-wavefront LDS transpose as two 512-byte rows.
+constexpr int kPfQ = 32;          // queries per workgroup
+constexpr int kPfE = 512;         // entries per workgroup
+constexpr int kPfCols = kPfE / (4 * 16);  // column tiles per wavefront (8)
+
+template <bool kWeights>
+__global__ __launch_bounds__(256) void prefill_score_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ keys,
+    int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q, float* __restrict__ scores,
+    int32_t* __restrict__ n_vis, int32_t* __restrict__ win_len, int32_t win) {
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kPfQ * 8 * 64];   // [query*8 + head][dim]
+  __shared__ __attribute__((aligned(16))) float stage[4][2 * 128];      // per wavefront [2][128]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t q0 = (int64_t)blockIdx.y * kPfQ;
+  const int64_t e_w = (int64_t)blockIdx.x * kPfE + wave * 128;  // this wavefront's first entry
+
+  // Key fragments of the wavefront's 8 column tiles (clamped rows; entries
+  // past n_entries are never stored).
+  u32x4 kf[kPfCols][2];
+#pragma unroll
+  for (int c = 0; c < kPfCols; ++c) {
+    const int64_t e = min(e_w + 16 * c + n, n_entries - 1);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(keys + e * 64 + 16 * g);
+    kf[c][0] = kp[0];
+    kf[c][1] = kp[1];
+  }
+  // The 32 queries' indexer Q into LDS (clamped rows past n_q).
+#pragma unroll
+  for (int i = 0; i < (kPfQ * 8 * 64) / (8 * 256); ++i) {
+    const int v = tid + 256 * i;              // 16-byte vector index
+    const int64_t qr = min(q0 + (v >> 6), (int64_t)n_q - 1);
+    *reinterpret_cast<u32x4*>(&qs[v * 8]) =
+        reinterpret_cast<const u32x4*>(q + qr * 8 * 64)[v & 63];
+  }
+  if (blockIdx.x == 0 && tid < kPfQ && q0 + tid < n_q) {
+    const int64_t t = t0 + q0 + tid;
+    if (n_vis) n_vis[q0 + tid] = (int32_t)min(n_entries, (t + 1) / ratio);
+    if (win_len) win_len[q0 + tid] = (int32_t)min((int64_t)win, t + 1);  // tokens max(0, t-win+1) .. t
+  }
+  __syncthreads();
+
+  float* st = stage[wave];
+  const bool vec_ok = (n_entries & 3) == 0;
+#pragma unroll 1
+  for (int rt = 0; rt < kPfQ / 2; ++rt) {
+    // Row m = n of this tile: query 2rt + n/8, head n%8, dims 16g..16g+15.
+    const u32x4* ap = reinterpret_cast<const u32x4*>(&qs[((2 * rt) * 8 + n) * 64 + 16 * g]);
+    const bf16x8 a0 = as_bf16x8(ap[0]), a1 = as_bf16x8(ap[1]);
+    const int64_t qi = q0 + 2 * rt + (g >> 1);   // query of this lane's output rows
+    float wh[4] = {1.f, 1.f, 1.f, 1.f};
+    if (kWeights) {
+      const int64_t qc = min(qi, (int64_t)n_q - 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wh[r] = w[qc * 8 + 4 * (g & 1) + r];
+    }
+    const int64_t vis = min(n_entries, (t0 + qi + 1) / ratio);
+#pragma unroll
+    for (int c = 0; c < kPfCols; ++c) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16x16x32(a0, as_bf16x8(kf[c][0]), acc);
+      acc = mfma16x16x32(a1, as_bf16x8(kf[c][1]), acc);
+      const float part = relu_wsum4(acc, wh);       // heads 4(g%2)..+3
+      const float other = __shfl_xor(part, 16);
+      const float score = (g & 1) ? other + part : part + other;  // lo + hi
+      if ((g & 1) == 0) st[(g >> 1) * 128 + 16 * c + n] = (e_w + 16 * c + n < vis) ? score : kNegInf;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // Two rows of 128 scores: lane l stores query 2rt + l/32, entries 4(l%32)..+3.
+    const int64_t qo = q0 + 2 * rt + (lane >> 5);
+    const int64_t eo = e_w + 4 * (lane & 31);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&st[(lane >> 5) * 128 + 4 * (lane & 31)]);
+    if (qo < n_q) {
+      float* dst = scores + qo * n_entries + eo;
+      if (vec_ok && eo + 3 < n_entries) {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (eo + j < n_entries) dst[j] = v[j];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 }  // namespace
 
 csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
@@ -157,6 +255,26 @@ csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t
     else launch_one<false, false>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out, ghist);
   }
   return launch_status("csa2_index_score");
+}
+
+}  // namespace csa2
+
+namespace csa2 {
+
+csa2_status prefill_score_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t n_entries,
+                                 int64_t t0, int32_t ratio, int32_t n_q, float* scores, int32_t* n_vis,
+                                 int32_t* win_len, int32_t win, hipStream_t stream) {
+  if (n_q == 0 || n_entries == 0) return CSA2_OK;
+  const int64_t gx = (n_entries + kPfE - 1) / kPfE, gy = (n_q + kPfQ - 1) / kPfQ;
+  CSA2_REQUIRE(gy <= 65535, CSA2_ESHAPE, "csa2_prefill_index_score: too many queries");
+  const dim3 grid((uint32_t)gx, (uint32_t)gy);
+  if (w)
+    hipLaunchKernelGGL(prefill_score_kernel<true>, grid, dim3(256), 0, stream, q, w, keys, n_entries, t0,
+                       ratio, n_q, scores, n_vis, win_len, win);
+  else
+    hipLaunchKernelGGL(prefill_score_kernel<false>, grid, dim3(256), 0, stream, q, w, keys, n_entries, t0,
+                       ratio, n_q, scores, n_vis, win_len, win);
+  return launch_status("csa2_prefill_index_score");
 }
 
 }  // namespace csa2

@@ -31,6 +31,8 @@
 // Citation keys: [P1] "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M
 // Context, FP4 KV Cache, and Cross-Layer Attention Reuse"; [P3]
 // "DeepSeek-V4.1 Flash: Pushing the Limits of KV Cache Compression".
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace csa2 {
@@ -87,19 +89,30 @@ struct AttnSmem {
   uint16_t ps[2][16 * kPPitch];             // P = hi + lo, bf16 [head][row]
   float red_m[kAttnWaves][16];
   float red_l[kAttnWaves][16];
+  float alpha[16];                          // rescale of the running O per head
+  float l_fin[16];                          // final softmax denominator per head
 };
 
-// The work of one wavefront-tile, specialised on the tile's kind (FP4 rows
-// or window rows) so that its loads are unconditional and issued together;
-// every wavefront runs the same barrier sequence.
+// Running state of one workgroup over its chunks: O for 16 heads x this
+// wavefront's 64 channels (column tile c = channels 64*wave + 4n + c, head
+// 4g + j in element j), the running max of head n, and (threads 0..15) the
+// running denominator of head tid.
+struct AttnState {
+  f32x4 o[4];
+  float m_run;
+  float l_run;
+};
+
+// One chunk of 8 tiles, the wavefront's tile specialised on its kind (FP4
+// rows or window rows) so that its loads are unconditional and issued
+// together; every wavefront runs the same barrier sequence.
 template <bool kSwa>
-__device__ __forceinline__ void attn_tile(
-    AttnSmem& sm, const u32x4 (&qreg)[1024 / (64 * kAttnWaves)], const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, int64_t cap, int32_t q_per_seq, const int32_t* __restrict__ idx,
-    int32_t k_idx, const uint16_t* __restrict__ swa, int64_t swa_q_stride_rows, int32_t n_swa, int row0,
-    bool tile_in_range, float scale_log2, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int32_t n_split) {
-  const int qb = blockIdx.y, split = blockIdx.x;
+__device__ __forceinline__ void attn_chunk(
+    AttnSmem& sm, AttnState& st, bool first, const u32x4 (&qreg)[1024 / (64 * kAttnWaves)],
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t cap, int32_t q_per_seq,
+    const int32_t* __restrict__ idx, int32_t k_idx, const uint16_t* __restrict__ swa,
+    int64_t swa_q_stride_rows, int32_t n_swa, int row0, bool tile_in_range, float scale_log2) {
+  const int qb = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -126,13 +139,15 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
     for (int t = 0; t < 16; ++t) raw[t] = sp[t];
   }
-  // Main Q (loaded by the caller before the row loads) into LDS.
+  if (first) {
+    // Main Q (loaded by the caller before the row loads) into LDS.
 #pragma unroll
-  for (int i = 0; i < 1024 / (64 * kAttnWaves); ++i) {
-    const int c = tid + 64 * kAttnWaves * i;
-    *reinterpret_cast<u32x4*>(&sm.qs[(c >> 6) * kXPitch + 8 * (c & 63)]) = qreg[i];
+    for (int i = 0; i < 1024 / (64 * kAttnWaves); ++i) {
+      const int c = tid + 64 * kAttnWaves * i;
+      *reinterpret_cast<u32x4*>(&sm.qs[(c >> 6) * kXPitch + 8 * (c & 63)]) = qreg[i];
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 2. dequantise, stage in LDS, and S^T[row][head] on MFMA
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -155,15 +170,16 @@ __device__ __forceinline__ void attn_tile(
 #pragma unroll
   for (int j = 0; j < 4; ++j) z[j] = ((rows_ok >> (4 * g + j)) & 1) ? s[j] * scale_log2 : kNegInf;
 
-  // ---- 3. softmax statistics of the chunk, per head n
+  // ---- 3. softmax statistics of the chunk, per head n, against the
+  // running max (online softmax across the workgroup's chunks)
   float m = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
   m = fmaxf(m, __shfl_xor(m, 16));
   m = fmaxf(m, __shfl_xor(m, 32));
   if (g == 0) sm.red_m[wave][n] = m;
   __syncthreads();
-  float M = sm.red_m[0][n];
+  float M = st.m_run;
 #pragma unroll
-  for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, sm.red_m[w][n]);
+  for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.red_m[w][n]);
   float lsum = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -177,13 +193,27 @@ __device__ __forceinline__ void attn_tile(
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (g == 0) sm.red_l[wave][n] = lsum;
+  if (tid < 16) sm.alpha[tid] = (st.m_run == kNegInf) ? 0.f : exp2f(st.m_run - M);
+  const float alpha_n = (st.m_run == kNegInf) ? 0.f : exp2f(st.m_run - M);
+  st.m_run = M;
   __syncthreads();
 
   // ---- 4. O[head][ch] for channels 64*wave .. +64 as 4 column tiles:
   // column tile c holds channels 64*wave + 4*n + c.
-  f32x4 o[4];
+  if (!first) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) {
+      const float a = sm.alpha[4 * g + j];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) st.o[c][j] *= a;
+    }
+  }
+  if (tid < 16) {
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) l += sm.red_l[w][tid];
+    st.l_run = st.l_run * alpha_n + l;
+  }
 #pragma unroll
   for (int ks = 0; ks < kAttnRows / 32; ++ks) {
     const bf16x8 ph = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.ps[0][n * kPPitch + 32 * ks + 8 * g]));
@@ -201,36 +231,27 @@ __device__ __forceinline__ void attn_tile(
         const uint32_t a1 = (c < 2) ? R[2 * p + 1].x : R[2 * p + 1].y;
         bc[p] = (c & 1) ? byte_perm(a1, a0, 0x07060302u) : byte_perm(a1, a0, 0x05040100u);
       }
-      o[c] = mfma16x16x32(ph, as_bf16x8(bc), o[c]);
-      o[c] = mfma16x16x32(pl, as_bf16x8(bc), o[c]);
+      st.o[c] = mfma16x16x32(ph, as_bf16x8(bc), st.o[c]);
+      st.o[c] = mfma16x16x32(pl, as_bf16x8(bc), st.o[c]);
     }
-  }
-
-  // ---- 5. chunk results: unnormalised O and (max, sum) per head
-  float* po = part_o + ((int64_t)qb * n_split + split) * (16 * CSA2_LATENT);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int head = 4 * g + j;
-    *reinterpret_cast<f32x4*>(po + head * CSA2_LATENT + 64 * wave + 4 * n) =
-        f32x4{o[0][j], o[1][j], o[2][j], o[3][j]};
-  }
-  if (tid < 16) {
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) l += sm.red_l[w][tid];
-    part_ml[((int64_t)qb * n_split + split) * 16 + tid] = make_float2(M, l);
   }
 }
 
+// One workgroup = chunks [split * per_split, ...) of query blockIdx.y.  With
+// one split the workgroup covers the whole query and writes the normalised
+// output; otherwise it writes its unnormalised O and (max, sum) per head
+// for the combine kernel.
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t cap, int32_t q_per_seq,
     const int32_t* __restrict__ idx, int32_t k_idx, const uint16_t* __restrict__ swa,
     int64_t swa_q_stride_rows, const int32_t* __restrict__ swa_len, int32_t swa_max,
-    float scale_log2, float* __restrict__ part_o, float2* __restrict__ part_ml, int32_t n_split) {
+    float scale_log2, int32_t per_split, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    int32_t n_split, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) AttnSmem sm;
   const int qb = blockIdx.y, split = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
   // Main Q first: its loads overlap the index and row loads.
   u32x4 qreg[1024 / (64 * kAttnWaves)];
   {
@@ -241,19 +262,51 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(
   const int32_t n_swa = min(swa_len[qb], swa_max);
   // The query's tiles: FP4 tiles of 16 selected rows and window tiles of 16
   // rows, the window tiles spread evenly over the chunks so that every
-  // workgroup moves about the same bytes.  Each wavefront owns one tile.
+  // chunk moves about the same bytes.  Each wavefront owns one tile of a chunk.
   const int fp4_tiles = (k_idx + 15) / 16, swa_tiles = (swa_max + 15) / 16;
   const int n_tiles = fp4_tiles + swa_tiles;
-  const int tile = split * kAttnWaves + wave;
-  const int swa_before = (int)(((int64_t)tile * swa_tiles) / n_tiles);
-  const bool in_range = tile < n_tiles;
-  const bool swa_tile = in_range && ((int64_t)(tile + 1) * swa_tiles) / n_tiles > swa_before;
-  if (swa_tile)
-    attn_tile<true>(sm, qreg, codes, scales, cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, n_swa,
-                    swa_before * 16, in_range, scale_log2, part_o, part_ml, n_split);
-  else
-    attn_tile<false>(sm, qreg, codes, scales, cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, n_swa,
-                     (tile - swa_before) * 16, in_range, scale_log2, part_o, part_ml, n_split);
+  const int n_chunks = (n_tiles + kAttnWaves - 1) / kAttnWaves;
+  const int c_begin = split * per_split, c_end = min(n_chunks, c_begin + per_split);
+  AttnState st;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = kNegInf;
+  st.l_run = 0.f;
+  for (int ch = c_begin; ch < c_end; ++ch) {
+    if (ch != c_begin) __syncthreads();  // the previous chunk's LDS reads are done
+    const int tile = ch * kAttnWaves + wave;
+    const int swa_before = (int)(((int64_t)tile * swa_tiles) / n_tiles);
+    const bool in_range = tile < n_tiles;
+    const bool swa_tile = in_range && ((int64_t)(tile + 1) * swa_tiles) / n_tiles > swa_before;
+    if (swa_tile)
+      attn_chunk<true>(sm, st, ch == c_begin, qreg, codes, scales, cap, q_per_seq, idx, k_idx, swa,
+                       swa_q_stride_rows, n_swa, swa_before * 16, in_range, scale_log2);
+    else
+      attn_chunk<false>(sm, st, ch == c_begin, qreg, codes, scales, cap, q_per_seq, idx, k_idx, swa,
+                        swa_q_stride_rows, n_swa, (tile - swa_before) * 16, in_range, scale_log2);
+  }
+
+  if (n_split == 1) {
+    if (tid < 16) sm.l_fin[tid] = st.l_run;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int head = 4 * g + j;
+      const float l = sm.l_fin[head];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      *reinterpret_cast<f32x4*>(out + ((int64_t)qb * 16 + head) * CSA2_LATENT + 64 * wave + 4 * n) =
+          f32x4{st.o[0][j] * inv, st.o[1][j] * inv, st.o[2][j] * inv, st.o[3][j] * inv};
+    }
+    return;
+  }
+  float* po = part_o + ((int64_t)qb * n_split + split) * (16 * CSA2_LATENT);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int head = 4 * g + j;
+    *reinterpret_cast<f32x4*>(po + head * CSA2_LATENT + 64 * wave + 4 * n) =
+        f32x4{st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]};
+  }
+  if (tid < 16) part_ml[((int64_t)qb * n_split + split) * 16 + tid] = make_float2(st.m_run, st.l_run);
 }
 
 // Merge the chunks of one (head, query) with log-sum-exp weights:
@@ -293,8 +346,20 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 
 }  // namespace
 
+// Workgroups per query: enough to fill the chip when there are few
+// queries (split-K over chunks + a combine kernel), one per query otherwise
+// (no partials).
+static void attn_split_plan(int32_t n_q, int32_t k_idx, int32_t swa_max, int* splits, int* per_split) {
+  const int n_chunks = attn_splits(k_idx, swa_max);
+  const int want = std::max(1, std::min(n_chunks, (int)((1024 + (int64_t)n_q - 1) / std::max(1, n_q))));
+  *per_split = (n_chunks + want - 1) / want;
+  *splits = (n_chunks + *per_split - 1) / *per_split;
+}
+
 size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
-  const size_t splits = (size_t)attn_splits(k_idx, swa_max);
+  int splits, per_split;
+  attn_split_plan(n_q, k_idx, swa_max, &splits, &per_split);
+  if (splits == 1) return 0;
   const size_t o_bytes = (size_t)n_q * splits * 16 * CSA2_LATENT * sizeof(float);
   const size_t ml_bytes = (size_t)n_q * splits * 16 * sizeof(float2);
   return o_bytes + ml_bytes;
@@ -305,16 +370,22 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
                         const int32_t* swa_len, int32_t swa_max, float sm_scale, float* out, void* ws,
                         hipStream_t stream) {
   if (n_q == 0) return CSA2_OK;
-  const int splits = attn_splits(k_idx, swa_max);
-  char* base = reinterpret_cast<char*>(ws);
-  float* part_o = reinterpret_cast<float*>(base);
-  base += (size_t)n_q * splits * 16 * CSA2_LATENT * sizeof(float);
-  float2* part_ml = reinterpret_cast<float2*>(base);
+  int splits, per_split;
+  attn_split_plan(n_q, k_idx, swa_max, &splits, &per_split);
+  float* part_o = nullptr;
+  float2* part_ml = nullptr;
+  if (splits > 1) {
+    char* base = reinterpret_cast<char*>(ws);
+    part_o = reinterpret_cast<float*>(base);
+    base += (size_t)n_q * splits * 16 * CSA2_LATENT * sizeof(float);
+    part_ml = reinterpret_cast<float2*>(base);
+  }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_kernel, dim3(splits, n_q), dim3(64 * kAttnWaves), 0, stream, q, kv.codes, kv.scales, kv.cap,
-                     q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, scale_log2, part_o,
-                     part_ml, splits);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, splits, out);
+  hipLaunchKernelGGL(attn_kernel, dim3(splits, n_q), dim3(64 * kAttnWaves), 0, stream, q, kv.codes, kv.scales,
+                     kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, scale_log2,
+                     per_split, part_o, part_ml, splits, out);
+  if (splits > 1)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, splits, out);
   return launch_status("csa2_sparse_attn");
 }
 

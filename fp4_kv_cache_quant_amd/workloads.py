@@ -1,4 +1,4 @@
-"""Device-resident inputs of a decode workload (see synth/configs.py).
+"""Device-resident inputs of a decode or prefill workload (see synth/configs.py).
 
 Every tensor is generated on the GPU by the seeded generator (synth's fill
 kernel) and the FP4 caches are quantised on the GPU with csa2_quant_rows,
@@ -14,9 +14,9 @@ from typing import List, Optional
 import torch
 
 import synth
-from synth.configs import DecodeConfig
+from synth.configs import DecodeConfig, PrefillConfig
 
-from . import FP4KV, LATENT, Layer, Sched, quant_rows
+from . import FP4KV, LATENT, Layer, Prefill, Sched, quant_rows
 
 
 def _fill(shape, tid_kind, seed=0):
@@ -109,3 +109,49 @@ def step_ios(sched: Sched, inp: DecodeInputs):
                           swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q[s], blk_k=inp.blk_k,
                           new_row=inp.new_row[s], append_kv=inp.cfg.append_kv)
             for s in range(inp.cfg.q_sets)]
+
+
+# ---------------------------------------------------------------- prefill
+@dataclass
+class PrefillInputs:
+    cfg: PrefillConfig
+    kv: List[FP4KV]                       # one tensor, n_seq 1, cap n_entries
+    entry_k: torch.Tensor                 # [n_entries][64]
+    idx_q: List[Optional[torch.Tensor]]   # [layer]: [n_q][8][64] (Reuse: None)
+    main_q: List[torch.Tensor]            # [layer]: [n_q][16][512]
+    swa: List[torch.Tensor]               # [layer]: [n_q + swa - 1][512], row j = token t0 - swa + 1 + j
+    out: List[torch.Tensor]               # [layer]: [n_q][16][512] f32
+    idx: List[Optional[torch.Tensor]]     # [layer]: [n_q][topk] int32 (Reuse: None)
+
+
+def build_prefill_inputs(cfg: PrefillConfig) -> PrefillInputs:
+    """Allocate and fill every input of one prefill chunk of cfg."""
+    seed, nq, nl = cfg.seed, cfg.n_q, len(cfg.layers)
+    kv = FP4KV.empty(1, cfg.n_entries)
+    fill_kv_rows(kv, 0, 0, cfg.n_entries, cfg.entry_src(), seed)
+    entry_k = _fill((1, cfg.n_entries, 64), cfg.entry_k(), seed=seed)[0]
+    idx_q = [_fill((nq, 8, 64), cfg.idx_q(l), seed=seed) if m != 2 else None
+             for l, (m, _, _) in enumerate(cfg.layers)]
+    main_q = [_fill((nq, 16, LATENT), cfg.main_q(l), seed=seed) for l in range(nl)]
+    swa = []
+    for l in range(nl):
+        t = torch.empty(cfg.swa_rows_total, LATENT, dtype=torch.int16, device="cuda")
+        tid, kind = cfg.swa_tok(l)
+        synth.fill_rows_device(t.view(1, cfg.swa_rows_total, LATENT), seed, tid, kind, b0=0, row0=cfg.swa_row0)
+        swa.append(t)
+    out = [torch.empty(nq, 16, LATENT, dtype=torch.float32, device="cuda") for _ in range(nl)]
+    idx = [torch.empty(nq, cfg.topk, dtype=torch.int32, device="cuda") if m != 2 else None
+           for m, _, _ in cfg.layers]
+    torch.cuda.synchronize()
+    return PrefillInputs(cfg=cfg, kv=[kv], entry_k=entry_k, idx_q=idx_q, main_q=main_q, swa=swa, out=out, idx=idx)
+
+
+def make_prefill(inp: PrefillInputs):
+    """The chunk runner and its prepared descriptor."""
+    cfg = inp.cfg
+    layers = [Layer(m, k, bool(h)) for m, k, h in cfg.layers]
+    pf = Prefill(layers, n_entries=cfg.n_entries, ratio=cfg.ratio, n_q=cfg.n_q, t0=cfg.t0, topk=cfg.topk,
+                 swa=cfg.swa)
+    io = pf.prepare(kv=inp.kv, entry_k=inp.entry_k, idx_q=inp.idx_q, main_q=inp.main_q, swa=inp.swa,
+                    out=inp.out, idx=inp.idx)
+    return pf, io

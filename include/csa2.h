@@ -243,6 +243,70 @@ const int32_t* csa2_sched_pool(const csa2_sched* s);
 csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags);
 void csa2_sched_destroy(csa2_sched* s);
 
+/* ------------------------------------------------------------ prefill
+ * A causal prefill chunk of an encoder layer group over compressed entries
+ * [P1 "Compressed Sparse Attention 2 (CSA2)"]: the encoder layers run CSA2
+ * at compression ratio 2 in groups of one Full and five Reuse layers; [P3]:
+ * the encoder merges adjacent positions.  READING: compressed entry e
+ * merges tokens ratio*e .. ratio*e + ratio-1 and is visible to the query at
+ * token t iff its last token is <= t, so query t sees entries
+ * e < vis(t) = min(n_entries, (t + 1) / ratio); its window is the 128
+ * tokens t-127 .. t.  Query i of a chunk sits at token t0 + i.  Every
+ * query selects on its own. */
+
+/* Indexer scores of the chunk's n_q queries against all entries (the
+ * formula of csa2_index_score, on MFMA with both operands dense):
+ *   q      [n_q][8][64] bf16; w [n_q][8] f32 or NULL (all 1)
+ *   keys   [n_entries][64] bf16 indexer K of the entries
+ *   scores [n_q][n_entries] f32 out, 16-byte aligned: scores[i][e] for
+ *          e < vis(t0 + i), -inf for the entries query i cannot see
+ *   n_vis  [n_q] int32 out (device): vis(t0 + i), usable as the `lens` of
+ *          csa2_topk (len_div 1) over these scores.
+ * Requires ratio >= 1, t0 >= 0, 1 <= n_q <= 2,097,120. */
+csa2_status csa2_prefill_index_score(const uint16_t* q, const float* w, const uint16_t* keys,
+                                     int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q,
+                                     float* scores, int32_t* n_vis, void* stream);
+
+typedef struct {
+  int32_t n_layers;
+  const csa2_layer* layers; /* host [n_layers]; Full / Reindex (flat) / Reuse */
+  int64_t n_entries;        /* compressed entries in the cache and indexer K */
+  int32_t ratio;            /* tokens per entry (2 in the encoder) */
+  int32_t n_q;              /* queries of the chunk */
+  int64_t t0;               /* token of query 0; needs t0 >= swa - 1 */
+  int32_t topk;             /* entries kept per query (512) */
+  int32_t swa;              /* window tokens per query (128) */
+  float sm_scale;
+} csa2_prefill_desc;
+
+typedef struct {
+  int32_t n_kv;
+  const csa2_fp4_kv* kv;          /* host [n_kv]; each n_seq = 1, cap >= n_entries */
+  const uint16_t* entry_k;        /* [n_entries][64] bf16 indexer K */
+  const uint16_t* const* idx_q;   /* host [n_layers]: [n_q][8][64] bf16 (Reuse: ignored) */
+  const float* const* idx_w;      /* host [n_layers] of [n_q][8] f32 or NULL; NULL array = all 1 */
+  const uint16_t* const* main_q;  /* host [n_layers]: [n_q][16][512] bf16 */
+  const uint16_t* const* swa;     /* host [n_layers]: [n_q + swa - 1][512] bf16, row j = token
+                                     t0 - swa + 1 + j */
+  float* const* out;              /* host [n_layers]: [n_q][16][512] f32 */
+  int32_t* const* idx;            /* host [n_layers]: [n_q][topk] int32 out for Full / Reindex
+                                     layers (ascending entry ids, -1 padded); Reuse: ignored */
+} csa2_prefill_io;
+
+/* Workspace of csa2_prefill_chunk (scores [n_q][n_entries] f32 dominate). */
+size_t csa2_prefill_workspace_size(const csa2_prefill_desc* desc);
+/* Run the layer table over the chunk: a Full or Reindex layer scores all
+ * visible entries with its own indexer Q and keeps a Top-`topk` per query
+ * (csa2_topk's order: score descending, lower entry first, ids ascending,
+ * -1 padded); a Reuse layer reuses the latest selection; every layer
+ * attends (csa2_sparse_attn) with its own main Q over its query's selected
+ * entries of tensor kv_id followed by the query's window rows.
+ * ws: csa2_prefill_workspace_size bytes, 256-byte aligned, zero-filled
+ * before its first use and left ready for the next call (calls sharing it
+ * must not overlap).  Asynchronous on `stream`; allocates nothing. */
+csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill_io* io, void* ws,
+                               size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

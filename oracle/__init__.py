@@ -309,19 +309,29 @@ def decode_layers(layers: Sequence[Layer], seq: SeqState, inputs: Sequence[Layer
 
 
 # ---------------------------------------------------------------- prefill
-def prefill_visible_entries(t: int, ratio: int) -> int:
+def prefill_visible_entries(t: int, ratio: int, n_entries: Optional[int] = None) -> int:
     """READING: compressed entry e merges tokens ratio*e .. ratio*e+ratio-1
     ([P3]: encoder-side merging of adjacent positions; [P1 "Compressed Sparse
     Attention 2 (CSA2)"]: encoder ratio 2) and is visible to the query at
-    token t once its last token is <= t."""
-    return (t + 1) // ratio
+    token t once its last token is <= t; a cache of n_entries entries holds
+    no more than those."""
+    v = (t + 1) // ratio
+    return v if n_entries is None else min(v, n_entries)
+
+
+def prefill_window(t: int, swa: int = SWA):
+    """READING: the query at token t attends to the window tokens
+    max(0, t-swa+1) .. t ([P1 "Causal Encoder-Decoder: Half the Prefill"]:
+    a 128-token sliding window in every layer); returns (first token, count)."""
+    lo = max(0, t - swa + 1)
+    return lo, t - lo + 1
 
 
 def prefill_query(layers: Sequence[Layer], t: int, ratio: int, entry_keys: np.ndarray,
                   kv_rows, inputs: Sequence[LayerInputs], sm_scale: float, k: int = TOPK):
     """All layers of one prefill query at token t over compressed entries.
     Each query selects independently; Reuse layers reuse that query's
-    indices.  ``inputs[l].swa`` holds the window tokens max(0,t-127)..t."""
-    n_vis = prefill_visible_entries(t, ratio)
+    indices.  ``inputs[l].swa`` holds the window tokens of prefill_window(t)."""
+    n_vis = prefill_visible_entries(t, ratio, entry_keys.shape[0])
     seq = SeqState(L=n_vis, tok_keys=entry_keys, kv_rows=kv_rows)
     return decode_layers(layers, seq, inputs, sm_scale, k)

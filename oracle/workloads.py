@@ -1,4 +1,4 @@
-"""TEST INFRASTRUCTURE: oracle results of a decode workload (synth/configs.py).
+"""TEST INFRASTRUCTURE: oracle results of a decode or prefill workload (synth/configs.py).
 
 Regenerates on the host, from the same seeds as the device builder, exactly
 the inputs one decode step of one sequence reads, and runs the oracle's
@@ -10,9 +10,10 @@ from __future__ import annotations
 import numpy as np
 
 import synth
-from synth.configs import REUSE, DecodeConfig
+from synth.configs import REUSE, DecodeConfig, PrefillConfig
 
-from . import Layer, LayerInputs, SeqState, decode_layers, quant_rows
+from . import (Layer, LayerInputs, SeqState, decode_layers, prefill_query, prefill_visible_entries,
+               prefill_window, quant_rows)
 
 SM_SCALE = 512 ** -0.5
 
@@ -66,3 +67,44 @@ def reference_step(cfg: DecodeConfig, step: int, b: int, attend=True):
     layers = [Layer(m, k, bool(h)) for m, k, h in cfg.layers]
     return decode_layers(layers, seq_state(cfg, b, step), layer_inputs(cfg, b, step), SM_SCALE,
                          k=cfg.topk, n_pool=cfg.pool_blocks, attend=attend)
+
+
+# ---------------------------------------------------------------- prefill
+def prefill_entry_keys(cfg: PrefillConfig) -> np.ndarray:
+    """Indexer K of every entry, [n_entries][64] bf16 bits."""
+    return _gen(cfg, cfg.entry_k(), 0, np.arange(cfg.n_entries), 64)
+
+
+def prefill_kv_rows(cfg: PrefillConfig):
+    def kv_rows(kv_id, ids):
+        ids = np.asarray(ids, dtype=np.int64)
+        src = np.zeros((len(ids), 512), np.uint16)
+        ok = ids >= 0
+        if ok.any():
+            src[ok] = _gen(cfg, cfg.entry_src(), 0, ids[ok], 512)
+        return quant_rows(src)
+    return kv_rows
+
+
+def prefill_layer_inputs(cfg: PrefillConfig, i: int):
+    """Per-layer inputs of query i (token t0 + i)."""
+    t = cfg.t0 + i
+    lo, cnt = prefill_window(t, cfg.swa)
+    ins = []
+    for l, (mode, _, _) in enumerate(cfg.layers):
+        iq = None if mode == REUSE else _gen(cfg, cfg.idx_q(l), i, np.arange(8), 64)
+        mq = _gen(cfg, cfg.main_q(l), i, np.arange(16), 512)
+        sw = _gen(cfg, cfg.swa_tok(l), 0, np.arange(lo, lo + cnt), 512)
+        ins.append(LayerInputs(idx_q=iq, main_q=mq, swa=sw, swa_len=cnt))
+    return ins
+
+
+def prefill_reference(cfg: PrefillConfig, i: int, entry_keys=None, attend=True):
+    """Oracle LayerResults of query i of the prefill chunk."""
+    layers = [Layer(m, k, bool(h)) for m, k, h in cfg.layers]
+    keys = prefill_entry_keys(cfg) if entry_keys is None else entry_keys
+    ins = prefill_layer_inputs(cfg, i)
+    if not attend:
+        n_vis = prefill_visible_entries(cfg.t0 + i, cfg.ratio, cfg.n_entries)
+        return decode_layers(layers, SeqState(L=n_vis, tok_keys=keys), ins, SM_SCALE, k=cfg.topk, attend=False)
+    return prefill_query(layers, cfg.t0 + i, cfg.ratio, keys, prefill_kv_rows(cfg), ins, SM_SCALE, k=cfg.topk)

@@ -98,3 +98,61 @@ DECODER_20L_1M = DecodeConfig(
 
 DECODE_CONFIGS = {"single_4k": SINGLE_LAYER_4K, "group_64k": GROUP_64K, "hier_1m": HIER_1M,
                   "decoder20_1m": DECODER_20L_1M}
+
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    """A causal prefill chunk of an encoder layer group over compressed
+    entries: entry e merges tokens ratio*e .. ratio*e+ratio-1; the chunk's
+    query i sits at token t0 + i.  One FP4 main-KV tensor and one indexer K
+    (one row per entry) are shared by the group; every layer has its own
+    main Q and its own token-level SWA rows."""
+    name: str
+    n_entries: int
+    ratio: int
+    n_q: int
+    t0: int
+    layers: Tuple[Tuple[int, int, int], ...]
+    topk: int = 512
+    swa: int = 128
+    seed: int = 0
+
+    def with_(self, **kw) -> "PrefillConfig":
+        return replace(self, **kw)
+
+    @property
+    def swa_row0(self) -> int:
+        """Token of the first SWA row held: the window of query 0 starts here."""
+        return self.t0 - self.swa + 1
+
+    @property
+    def swa_rows_total(self) -> int:
+        return self.n_q + self.swa - 1
+
+    # ---- synthetic tensors (tensor id, value kind); entry and SWA rows use
+    # sequence 0 and the entry / token index as the row, query tensors use
+    # the query index as the sequence.
+    def entry_src(self):
+        return tensor_id(KIND_KV_SRC, 0, 1), NORMAL
+
+    def entry_k(self):
+        return tensor_id(KIND_IDX_K, 0, 1), INT9
+
+    def idx_q(self, layer: int):
+        return tensor_id(KIND_IDX_Q, layer, 1), INT9
+
+    def main_q(self, layer: int):
+        return tensor_id(KIND_MAIN_Q, layer, 1), NORMAL
+
+    def swa_tok(self, layer: int):
+        return tensor_id(KIND_SWA, layer, 1), NORMAL
+
+
+# Encoder group at ratio 2: Full + 5 Reuse over 128K tokens held as 64K
+# compressed entries, a 4,096-query causal prefill chunk at the end of the
+# context (queries at tokens 126,976 .. 131,071).
+ENCODER_PREFILL_128K = PrefillConfig(
+    name="encoder group Full+5 Reuse at ratio 2, 64K entries (128K tokens), 4,096-query prefill chunk",
+    n_entries=1 << 16, ratio=2, n_q=4096, t0=(1 << 17) - 4096, layers=_group(FULL, 0, 0, 5))
+
+PREFILL_CONFIGS = {"encoder_prefill_128k": ENCODER_PREFILL_128K}

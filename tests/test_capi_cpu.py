@@ -112,3 +112,40 @@ def test_scheduler_rejects_invalid_tables(csa2):
     with pytest.raises(csa2.Csa2Error) as e:  # hierarchical: blocks must cover key_cap
         csa2.Sched([L(csa2.FULL, 0, True)], n_seq=1, key_cap=1 << 20, blk_cap=1000)
     assert e.value.code == -2
+
+
+def _prefill_desc(csa2, layers=None, **kw):
+    layers = layers or [csa2.Layer(csa2.FULL)] + [csa2.Layer(csa2.REUSE)] * 5
+    arr = (csa2._Layer * len(layers))(*[csa2._Layer(l.mode, l.kv_id, int(l.hierarchical)) for l in layers])
+    a = dict(n_entries=65536, ratio=2, n_q=4096, t0=131072 - 4096, topk=512, swa=128)
+    a.update(kw)
+    d = csa2._PrefillDesc(len(layers), ctypes.cast(arr, ctypes.c_void_p), a["n_entries"], a["ratio"], a["n_q"],
+                          a["t0"], a["topk"], a["swa"], 512 ** -0.5)
+    d._keep = arr
+    return d
+
+
+def test_prefill_workspace_and_table_validation(csa2):
+    ws = lambda d: csa2._prefill_ws(ctypes.byref(d))
+    full = ws(_prefill_desc(csa2))
+    assert full >= 4096 * 65536 * 4          # the score matrix dominates
+    assert ws(_prefill_desc(csa2, t0=126)) == 0 and "t0" in _err(csa2)
+    assert ws(_prefill_desc(csa2, t0=127)) > 0
+    assert ws(_prefill_desc(csa2, n_q=0)) == 0
+    assert ws(_prefill_desc(csa2, n_entries=300000)) == 0
+    assert ws(_prefill_desc(csa2, layers=[csa2.Layer(csa2.REUSE)])) == 0 and "Reuse" in _err(csa2)
+    assert ws(_prefill_desc(csa2, layers=[csa2.Layer(csa2.FULL, 0, True)])) == 0 and "hierarchical" in _err(csa2)
+    assert ws(_prefill_desc(csa2, layers=[csa2.Layer(csa2.FULL), csa2.Layer(csa2.REINDEX)])) == full
+
+
+def test_prefill_calls_reject_bad_arguments(csa2):
+    assert csa2._prefill_score(FAKE, None, FAKE, 100, 0, 2, 10, FAKE, None, None) == -1      # n_vis null
+    assert csa2._prefill_score(FAKE + 2, None, FAKE, 100, 0, 2, 10, FAKE, FAKE, None) == -1  # alignment
+    assert csa2._prefill_score(FAKE, None, FAKE, 100, 0, 0, 10, FAKE, FAKE, None) == -1      # ratio 0
+    assert csa2._prefill_score(None, None, None, 100, 0, 2, 0, None, None, None) == 0        # n_q = 0: no-op
+    d = _prefill_desc(csa2, n_entries=1000, n_q=16, t0=1984)
+    need = csa2._prefill_ws(ctypes.byref(d))
+    io = csa2._PrefillIO()
+    assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE, need - 1, None) == -3
+    assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE + 16, need, None) == -1
+    assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE, need, None) == -1    # io pointers null

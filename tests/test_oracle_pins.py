@@ -387,3 +387,19 @@ def test_table_validation():
 def test_prefill_visibility_ratio_two():
     # entry e = tokens {2e, 2e+1}: visible once token 2e+1 has been seen
     assert [oracle.prefill_visible_entries(t, 2) for t in range(6)] == [0, 1, 1, 2, 2, 3]
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 3])
+def test_prefill_visibility_by_enumeration(ratio):
+    # brute force: count the entries whose every token is at or before t
+    for t in range(40):
+        for n_entries in (5, 1000):
+            want = sum(1 for e in range(n_entries) if all(ratio * e + j <= t for j in range(ratio)))
+            assert oracle.prefill_visible_entries(t, ratio, n_entries) == want, (t, ratio, n_entries)
+
+
+def test_prefill_window_by_enumeration():
+    for swa in (1, 4, 128):
+        for t in range(300):
+            toks = [u for u in range(t + 1) if t - u < swa]
+            assert oracle.prefill_window(t, swa) == (toks[0], len(toks))
