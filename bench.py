@@ -9,12 +9,14 @@ attention for all 20 layers.
 
 Prints one JSON line: (seq.layer)-steps/s, ms per step, the step's
 algorithmic HBM bytes as GB/s and fraction of the 8 TB/s peak, the
-roofline of the dominant kernel (timed with HIP events), the CPU oracle on a
-bounded sample of the same workload, and a parity check of one step
-against that oracle sample.
+roofline of the dominant op (timed with HIP events), the CPU oracle on a
+bounded sample of the same workload, a parity check of one step against
+that oracle sample, and (key "prefill") the ratio-2 causal prefill chunk of
+the encoder group: time per 4,096-query chunk, MFMA rate of its scoring and
+attention kernels, sampled parity and the oracle's rate.
 
 usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-graph]
-                       [--cpu-seqs 16] [--no-cpu]
+                       [--cpu-seqs 16] [--no-cpu] [--no-prefill] [--prefill-reps 5]
 """
 from __future__ import annotations
 
@@ -226,6 +228,97 @@ def calibration_copy(nbytes: int = 1 << 30):
     torch.cuda.synchronize()
 
 
+PEAK_MFMA_BF16_TFLOPS = 2500.0
+
+
+def prefill_bench(args) -> dict:
+    """The causal prefill chunk of the encoder group (ratio 2, 64K entries,
+    4,096 queries, Full + 5 Reuse): time per chunk, MFMA rate of the scoring
+    and attention kernels against the dense bf16 peak, parity of sampled
+    queries against the oracle, and the oracle's own rate on them."""
+    import numpy as np
+    import torch
+
+    import fp4_kv_cache_quant_amd as csa2
+    from fp4_kv_cache_quant_amd import workloads as wl
+    from synth.configs import PREFILL_CONFIGS
+
+    cfg = PREFILL_CONFIGS["encoder_prefill_128k"]
+    nq, E, nl = cfg.n_q, cfg.n_entries, len(cfg.layers)
+    inp = wl.build_prefill_inputs(cfg)
+    pf, io = wl.make_prefill(inp)
+    pf.run(io)
+    torch.cuda.synchronize()
+    idx0 = inp.idx[0].cpu().numpy()
+    outs_sample = {}
+    sample = [0, nq // 2 + 1, nq - 1]
+    for i in sample:
+        outs_sample[i] = [inp.out[l][i].cpu().numpy() for l in range(nl)]
+    reps = max(1, args.prefill_reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pf.run(io)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+
+    # The chunk's three ops on their own, launched as the chunk launches them.
+    q0 = inp.idx_q[0]
+    scores = torch.empty(nq, E, dtype=torch.float32, device="cuda")
+    n_vis = torch.empty(nq, dtype=torch.int32, device="cuda")
+    idx = torch.empty(nq, cfg.topk, dtype=torch.int32, device="cuda")
+    out = torch.empty(nq, 16, 512, dtype=torch.float32, device="cuda")
+    tws = torch.zeros(csa2.topk_workspace_size(E, nq), dtype=torch.uint8, device="cuda")
+    win = torch.full((nq,), cfg.swa, dtype=torch.int32, device="cuda")
+    csa2.prefill_index_score(q0, inp.entry_k, cfg.t0, cfg.ratio, scores, n_vis)
+    csa2.topk(scores, cfg.topk, idx, lens=n_vis, ws=tws)
+    ops = [
+        ("prefill_score", lambda: csa2.prefill_index_score(q0, inp.entry_k, cfg.t0, cfg.ratio, scores, n_vis),
+         2.0 * nq * 8 * 64 * E, nq * E * 4 + E * 128 + nq * 1024),
+        ("prefill_topk", lambda: csa2.topk(scores, cfg.topk, idx, lens=n_vis, ws=tws), 0.0, nq * E * 4),
+        ("prefill_attn", lambda: csa2.sparse_attn(inp.main_q[0], inp.kv[0], idx, inp.swa[0], win, 512 ** -0.5, out,
+                                                  q_per_seq=nq, swa_q_stride_rows=1, swa_max=cfg.swa),
+         2.0 * 2 * nq * 16 * (cfg.topk + cfg.swa) * 512,
+         nq * (16 * 1024 + 16 * 512 * 4 + cfg.topk * 4) + E * 288 + cfg.swa_rows_total * 1024),
+    ]
+    op_res = []
+    for key, fn, flops, nbytes in ops:
+        us = _graph_time_us(fn, per_graph=2, replays=3, graph=not args.no_graph)
+        r = {"key": key, "avg_us": round(us, 1), "bytes": int(nbytes), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        if flops:
+            tf = flops / (us * 1e-6) / 1e12
+            r.update({"flops": flops, "TFLOPs": round(tf, 1), "mfma_frac_of_bf16_peak": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)})
+        op_res.append(r)
+
+    # Parity and the oracle's rate on the sampled queries.
+    from oracle import workloads as ow
+
+    keys = ow.prefill_entry_keys(cfg)
+    t0 = time.perf_counter()
+    refs = {i: ow.prefill_reference(cfg, i, entry_keys=keys) for i in sample}
+    cpu_s = time.perf_counter() - t0
+    ok_idx = all(np.array_equal(idx0[i], refs[i][0].idx) for i in sample)
+    worst_rel = worst_abs = 0.0
+    for i in sample:
+        for l in range(nl):
+            o, r = outs_sample[i][l].astype(np.float64), refs[i][l].out.astype(np.float64)
+            err = np.linalg.norm(o - r, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-30)
+            worst_rel = max(worst_rel, float(err.max()))
+            worst_abs = max(worst_abs, float(np.abs(o - r).max()))
+    return {
+        "workload": cfg.name, "n_entries": E, "ratio": cfg.ratio, "n_q": nq, "t0": cfg.t0, "layers": nl,
+        "ms_per_chunk": round(ms, 3), "query_layers_per_s": round(nq * nl / (ms * 1e-3), 1),
+        "reps": reps, "ops": op_res,
+        "parity_sample": {"queries": sample, "indices_bit_exact": bool(ok_idx), "attn_max_rel_l2": worst_rel,
+                          "attn_max_abs": worst_abs,
+                          "ok": bool(ok_idx and worst_rel <= 1e-3 and worst_abs <= 5e-3)},
+        "cpu_baseline": {"value": round(len(sample) * nl / cpu_s, 2), "unit": "(query·layer)/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"{len(sample)} queries x {nl} layers of the chunk, {cpu_s:.1f} s"},
+    }
+
+
 def compare_step(cfg, gpu, ref) -> dict:
     """GPU step-0 results against the oracle sample: indices and pool
     bit-exact, attention rel. L2 <= 1e-3 and max abs <= 5e-3 per (seq, head)."""
@@ -257,6 +350,8 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--config", default="decoder20_1m")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--prefill-reps", type=int, default=5, help="timed prefill chunks")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for scaling profiler traffic counters)")
     args = ap.parse_args()
@@ -357,6 +452,10 @@ def main() -> int:
                          f"(hierarchical select, 4 Reindex rescorings, {nl} attentions), {dt:.1f} s"}
         parity = compare_step(cfg, gpu0, res)
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_bench(args)
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "(seq·layer)-steps/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -368,6 +467,7 @@ def main() -> int:
         "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": round(hbm_gbps, 1),
                 "frac_of_peak": round(hbm_gbps / PEAK_HBM_GBPS, 4), "parts": ab},
         "roofline": roofline, "dominant_op": dom, "ops": ops, "cpu_baseline": cpu, "parity_step0": parity,
+        "prefill": prefill,
         "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
     }
     print(json.dumps(line), flush=True)
