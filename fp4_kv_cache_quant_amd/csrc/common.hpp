@@ -32,13 +32,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // D = A(16x32) * B(32x16) + C on one wavefront (gfx950).  Lane l holds
 // A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and returns
 // C[4*(l/16) .. +3][l%16].
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same shape with f16 operands (v_mfma_f32_16x16x32_f16).
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // --------------------------------------------------------------- bf16/f32
@@ -74,6 +83,13 @@ __host__ __device__ __forceinline__ float e2m1_mag_value(uint32_t m) {
 __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
+
+// Workgroup barrier for an LDS hand-off only: waits for this wavefront's
+// LDS operations, then for every wavefront, but leaves its global loads in
+// flight (__syncthreads() also waits for all outstanding global memory
+// operations, which would drain a prefetch).  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Scores that are not candidates.
 constexpr float kNegInf = -__builtin_huge_valf();

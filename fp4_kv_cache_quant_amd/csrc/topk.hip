@@ -239,6 +239,58 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
   }
 }
 
+// Selection bitmap sel (and, if ties > 0, the tie bitmap tie: keys equal to
+// the threshold) of one sequence in LDS -> the ids in ascending order:
+// the lowest `ties` tie slots join the selection, then every thread owns a
+// contiguous run of words and writes its ids at its prefix-count position;
+// -1 pads the row to k.  Ends with the caller's LDS free to reuse only
+// after a barrier.
+__device__ void finish_output(uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
+                              const int32_t* pool_lds, int32_t blk, uint32_t* wave_sum, int32_t* __restrict__ ob) {
+  const int tid = threadIdx.x;
+  const int per = (words + kFinalThreads - 1) / kFinalThreads;
+  const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+  if (ties > 0) {
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(tie[w]);
+    uint32_t dummy;
+    uint32_t rank = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &dummy);
+    for (int w = w0; w < w1 && rank < ties; ++w) {
+      uint32_t x = tie[w];
+      const uint32_t pc = __popc(x);
+      if (rank + pc <= ties) {
+        sel[w] |= x;
+      } else {
+        uint32_t keep = 0;
+        for (uint32_t m = rank; m < ties; ++m) {
+          keep |= x & (0u - x);
+          x &= x - 1;
+        }
+        sel[w] |= keep;
+      }
+      rank += pc;
+    }
+    __syncthreads();
+  }
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+  uint32_t n_sel;
+  uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &n_sel);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t x = sel[w];
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      x &= x - 1;
+      const int64_t slot = (int64_t)w * 32 + bit;
+      int64_t id = slot;
+      if (pool_lds) id = (int64_t)pool_lds[slot / blk] * blk + slot % blk;
+      if (pos < kk) ob[pos] = (int32_t)id;
+      ++pos;
+    }
+  }
+  for (uint32_t i = n_sel + tid; i < kk; i += kFinalThreads) ob[i] = -1;
+}
+
 struct FinalSmem {
   int32_t pool[CSA2_TOPK_MAX];  // the sequence's pool block ids (pool mode)
   uint32_t hist[kTopkBins];
@@ -410,51 +462,121 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
     __syncthreads();
   }
 
-  // Each thread owns a contiguous run of bitmap words.
-  const int per = (words + kFinalThreads - 1) / kFinalThreads;
-  const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
-  if (ties > 0) {
-    uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(sm.tie[w]);
-    uint32_t dummy;
-    uint32_t rank = block_exclusive_scan<kFinalThreads>(cnt, sm.wave_sum, &dummy);
-    for (int w = w0; w < w1 && rank < ties; ++w) {
-      uint32_t x = sm.tie[w];
-      const uint32_t pc = __popc(x);
-      if (rank + pc <= ties) {
-        sm.sel[w] |= x;
-      } else {
-        uint32_t keep = 0;
-        for (uint32_t m = rank; m < ties; ++m) {
-          keep |= x & (0u - x);
-          x &= x - 1;
-        }
-        sm.sel[w] |= keep;
-      }
-      rank += pc;
-    }
-    __syncthreads();
-  }
+  finish_output(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+                out + (int64_t)b * k);
+}
 
-  // Ordered output.
-  uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(sm.sel[w]);
-  uint32_t n_sel;
-  uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, sm.wave_sum, &n_sel);
-  int32_t* ob = out + (int64_t)b * k;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t x = sm.sel[w];
-    while (x) {
-      const int bit = __ffs(x) - 1;
-      x &= x - 1;
-      const int64_t slot = (int64_t)w * 32 + bit;
-      int64_t id = slot;
-      if (pool) id = (int64_t)sm.pool[slot / blk] * blk + slot % blk;
-      if (pos < kk) ob[pos] = (int32_t)id;
-      ++pos;
+
+// Whole selection of one sequence of at most kRowsMax slots in one
+// workgroup, the scores held in registers (kPer per thread): three histogram
+// passes over the keys in LDS (digits of 12, 12 and 8 bits) find the exact
+// k-th key T, then selection and tie bitmaps are written by ballots and
+// finish_output emits the ids.  Reads every score once; used when no
+// histogram was produced upstream (many sequences of moderate length).
+constexpr int kRowsMax = 64 * kFinalThreads;  // 65,536 slots
+
+struct RowsSmem {
+  int32_t pool[CSA2_TOPK_MAX];
+  uint32_t hist[kTopkBins];
+  uint32_t sel[kRowsMax / 32];
+  uint32_t tie[kRowsMax / 32];
+  uint32_t wave_sum[kFinalWaves];
+  uint32_t found[2];
+};
+
+template <int kRowsPer>
+__global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* __restrict__ scores, int64_t n,
+                                                                  const int32_t* __restrict__ lens,
+                                                                  int32_t len_div, int32_t k,
+                                                                  const int32_t* __restrict__ pool,
+                                                                  int32_t n_pool, int32_t blk,
+                                                                  int32_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvalid = (int)valid_slots(n, lens, len_div, b);
+  const int words = (nvalid + 31) / 32;
+  const float* sc = scores + (int64_t)b * n;
+  const uint32_t kk = (uint32_t)k;
+
+  // Slot of register j of this thread: j * kFinalThreads + tid (a
+  // wavefront's 64 slots are contiguous and 64-aligned).
+  uint32_t key[kRowsPer];
+  {
+    float v[kRowsPer];
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) v[j] = sc[min(j * kFinalThreads + tid, max(nvalid - 1, 0))];
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) key[j] = (j * kFinalThreads + tid < nvalid) ? order_key(v[j]) : 0u;
+  }
+  if (pool) {
+    const int32_t* pb = pool + (int64_t)b * n_pool;
+    for (int i = tid; i < n_pool; i += kFinalThreads) sm.pool[i] = pb[i];
+  }
+  for (int i = tid; i < kTopkBins; i += kFinalThreads) sm.hist[i] = 0;
+  __syncthreads();
+
+  // Digit 1: bits 31..20.
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kRowsPer; ++j) {
+    if (key[j]) {
+      atomicAdd(&sm.hist[key[j] >> 20], 1u);
+      ++mine;
     }
   }
-  for (uint32_t i = n_sel + tid; i < kk; i += kFinalThreads) ob[i] = -1;
+  uint32_t total;
+  block_exclusive_scan<kFinalThreads>(mine, sm.wave_sum, &total);  // syncs: histogram complete
+  uint32_t T = 1u, ties = 0;  // with every candidate selected: key >= 1
+  if (total > kk) {
+    find_threshold_bin<kFinalThreads>(sm.hist, kTopkBins, kk, sm.wave_sum, sm.found);
+    const uint32_t b1 = sm.found[0];
+    const uint32_t need1 = kk - sm.found[1];
+    for (int i = tid; i < kTopkBins; i += kFinalThreads) sm.hist[i] = 0;
+    __syncthreads();
+    // Digit 2: bits 19..8 among the keys of bin b1.
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j)
+      if (key[j] && (key[j] >> 20) == b1) atomicAdd(&sm.hist[(key[j] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    find_threshold_bin<kFinalThreads>(sm.hist, kTopkBins, need1, sm.wave_sum, sm.found);
+    const uint32_t b2 = sm.found[0];
+    const uint32_t need2 = need1 - sm.found[1];
+    for (int i = tid; i < 256; i += kFinalThreads) sm.hist[i] = 0;
+    __syncthreads();
+    const uint32_t pre2 = (b1 << 12) | b2;
+    // Digit 3: bits 7..0 (integer-valued scores share their low bits: the
+    // atomics are grouped per wavefront).
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) wave_hist_add_grouped(sm.hist, key[j] & 0xFFu, key[j] && (key[j] >> 8) == pre2);
+    __syncthreads();
+    find_threshold_bin<kFinalThreads>(sm.hist, 256, need2, sm.wave_sum, sm.found);
+    T = (pre2 << 8) | sm.found[0];
+    ties = need2 - sm.found[1];
+  }
+  // Keys above T are selected; keys equal to T are tie candidates (only the
+  // lowest `ties` of them are kept).  Lanes 0 and 32 write the two words of
+  // their wavefront's 64 slots; every word of the valid range is written.
+#pragma unroll
+  for (int j = 0; j < kRowsPer; ++j) {
+    const int i = j * kFinalThreads + tid;
+    const bool take = ties > 0 ? key[j] > T : key[j] >= T;
+    const uint64_t ms = __ballot(take);
+    const uint64_t mt = __ballot(ties > 0 && key[j] == T);
+    const int w = (i - lane_id()) >> 5;
+    if (lane_id() == 0 && w < words) {
+      sm.sel[w] = (uint32_t)ms;
+      sm.tie[w] = (uint32_t)mt;
+    }
+    if (lane_id() == 32 && w + 1 < words) {
+      sm.sel[w + 1] = (uint32_t)(ms >> 32);
+      sm.tie[w + 1] = (uint32_t)(mt >> 32);
+    }
+  }
+  __syncthreads();
+  finish_output(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+                out + (int64_t)b * k);
 }
 
 }  // namespace
@@ -487,9 +609,27 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_final_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sizeof(FinalSmem)) != hipSuccess)
+                            (int)sizeof(FinalSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<64>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess)
       return launch_status("csa2_topk (shared memory attribute)");
     attr_set = true;
+  }
+  if (!hist_ready && n <= kRowsMax) {
+    if (n <= 16 * kFinalThreads)
+      hipLaunchKernelGGL(topk_rows_kernel<16>, dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream, scores,
+                         n, lens, len_div, k, pool, n_pool, blk, out);
+    else if (n <= 32 * kFinalThreads)
+      hipLaunchKernelGGL(topk_rows_kernel<32>, dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream, scores,
+                         n, lens, len_div, k, pool, n_pool, blk, out);
+    else
+      hipLaunchKernelGGL(topk_rows_kernel<64>, dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream, scores,
+                         n, lens, len_div, k, pool, n_pool, blk, out);
+    return launch_status("csa2_topk");
   }
   if (!hist_ready && n > 0)
     hipLaunchKernelGGL(topk_hist_kernel, dim3((uint32_t)((n + kHistSlots - 1) / kHistSlots), n_seq),

@@ -34,8 +34,10 @@
  *     Argument errors are detected on the host; device-side conditions
  *     (appending past capacity) are reported through a device flag.
  *   - Numerics: quantised bytes, scores of integer-valued indexer inputs and
- *     selected indices are exact and deterministic; attention is computed
- *     with bf16 MFMA inputs and fp32 accumulation.
+ *     selected indices are exact and deterministic.  Attention runs on f16
+ *     matrix-core inputs with fp32 accumulation: dequantised FP4 values are
+ *     exact in f16; main Q and window rows are rounded to f16 toward zero
+ *     (exact for |x| in [2^-14, 65504]; larger magnitudes saturate).
  */
 #ifndef CSA2_H
 #define CSA2_H

@@ -325,3 +325,32 @@ def test_sparse_attn_workspace_reused_across_calls(csa2):
             codes, scales = oracle.quant_rows(src[b])
             ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa[b], [128, 77][b], SM_SCALE)
             assert_attention_close(got[b], ref)
+
+
+@pytest.mark.parametrize("n_q", [300, 1100])
+def test_sparse_attn_many_queries_one_cache(csa2, n_q):
+    """Many queries over one cache sequence with per-query window offsets
+    (the prefill layout): 300 queries run multi-chunk splits plus the
+    combine; 1,100 run one 4-wavefront workgroup per query over all its
+    chunks.  Ragged k_idx and window lengths; sampled queries vs the oracle."""
+    cap, k_idx, swa_max = 3000, 500, 100
+    src = kv_source(3, 1, cap)
+    kv = _device_cache(csa2, src)
+    rng = np.random.default_rng(n_q)
+    idx = np.stack([np.sort(rng.choice(cap, k_idx, replace=False)) for _ in range(n_q)]).astype(np.int32)
+    idx[5, 300:] = -1
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 3), synth.NORMAL, range(n_q), np.arange(16), 512)
+    swa_rows = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 3), synth.NORMAL, [0],
+                              np.arange(n_q + swa_max - 1), 512)[0]
+    swa_len = rng.integers(0, swa_max + 1, size=n_q).astype(np.int32)
+    swa_len[0], swa_len[1] = swa_max, 0
+    print_case(f"sparse_attn many queries n_q={n_q}")
+    out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+    csa2.sparse_attn(dev(q), kv, dev(idx), dev(swa_rows), dev(swa_len), SM_SCALE, out, q_per_seq=n_q,
+                     swa_q_stride_rows=1, swa_max=swa_max)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    codes, scales = oracle.quant_rows(src[0])
+    for b in sorted({0, 1, 5, n_q // 2, n_q - 1, *rng.integers(0, n_q, 6).tolist()}):
+        ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa_rows[b:b + swa_max], swa_len[b], SM_SCALE)
+        assert_attention_close(got[b], ref, f"query {b}")

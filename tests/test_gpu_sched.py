@@ -78,3 +78,46 @@ def test_reuse_layers_share_indices_and_append_overflow_flag(wl):
     assert sched.check() == 1 and inp.lens.cpu().tolist() == [501, 501]
     assert sched.check() == 0
     sched.close()
+
+
+FULL_SIZE = {
+    # the workloads at their full sizes, in the launch configuration the
+    # benchmark times (native scheduler, one call per step); sampled
+    # sequences against the oracle, every appended row checked bit-exact
+    "group_64k_b32": (C.GROUP_64K, 2, [0, 31]),
+    "hier_1m_b8": (C.HIER_1M, 1, [0, 7]),
+    "decoder20_1m_b16": (C.DECODER_20L_1M, 3, [0, 9, 15]),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SIZE))
+def test_full_size_steps_sampled_sequences(wl, name):
+    cfg, steps, seqs = FULL_SIZE[name]
+    print_case(f"sched full size {name}: n_seq={cfg.n_seq} L0={cfg.L0} steps={steps} seqs={seqs}")
+    inp = wl.build_decode_inputs(cfg, steps)
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    for step in range(steps):
+        sched.decode_step(ios[step % cfg.q_sets])
+        idx = [sched.indices(l).cpu().numpy() for l in range(len(cfg.layers))]
+        pool = sched.pool()
+        pool = pool.cpu().numpy() if pool is not None else None
+        outs = [o.cpu().numpy() for o in inp.out]
+        for b in seqs:
+            ref = ow.reference_step(cfg, step, b)
+            for l, r in enumerate(ref):
+                assert np.array_equal(idx[l][b], r.idx), f"step {step} seq {b} layer {l} indices"
+                if r.pool is not None and cfg.layers[l][0] == C.FULL:
+                    assert np.array_equal(pool[b], r.pool), f"step {step} seq {b} pool"
+                assert_attention_close(outs[l][b], r.out, f"step {step} seq {b} layer {l}")
+    assert sched.check() == 0
+    if cfg.append:
+        kv = inp.kv[cfg.append_kv]
+        pos = np.arange(cfg.L0, cfg.L0 + steps)
+        for b in range(cfg.n_seq):
+            codes, scales = oracle.quant_rows(ow.kv_source_rows(cfg, cfg.append_kv, b, pos))
+            assert np.array_equal(kv.codes[b, cfg.L0:cfg.L0 + steps].cpu().numpy(), codes)
+            assert np.array_equal(kv.scales[b, cfg.L0:cfg.L0 + steps].cpu().numpy(), scales)
+    sched.close()
+    del inp
+    torch.cuda.empty_cache()
