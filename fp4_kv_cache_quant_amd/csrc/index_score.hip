@@ -240,11 +240,11 @@ csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t
                                int32_t n_pool, int32_t blk, float* scores, int64_t n_out, int32_t n_seq,
                                uint32_t* ghist, hipStream_t stream) {
   if (n_seq == 0 || n_out == 0) return CSA2_OK;
-  // About two workgroups per CU in total; each loops over chunks of 512
+  // About four workgroups per CU in total; each loops over chunks of 512
   // keys, so a fused histogram is flushed by few workgroups (its hot bins
   // see one global atomic per workgroup).
   const int64_t chunks = (n_out + kKeysPerWG - 1) / kKeysPerWG;
-  const int64_t per_seq = std::max<int64_t>(1, std::min<int64_t>(chunks, (512 + n_seq - 1) / n_seq));
+  const int64_t per_seq = std::max<int64_t>(1, std::min<int64_t>(chunks, (1024 + n_seq - 1) / n_seq));
   CSA2_REQUIRE(n_seq <= 65535, CSA2_ESHAPE, "csa2_index_score: grid too large");
   const dim3 grid((uint32_t)per_seq, (uint32_t)n_seq);
   if (pool) {

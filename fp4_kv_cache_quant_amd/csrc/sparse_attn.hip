@@ -143,6 +143,7 @@ struct AttnTile {
 };
 
 struct AttnArgs {
+  int qb;  // the query this workgroup attends for
   const uint8_t* codes;
   const uint8_t* scales;
   int64_t cap;
@@ -169,13 +170,13 @@ __device__ __forceinline__ void tile_begin(AttnTile& t, const AttnArgs& a, int c
   t.id = -1;
   if (!t.swa) {
     const int r = t.row0 + n;
-    t.id = (t.in_range && r < a.k_idx) ? a.idx[(int64_t)blockIdx.y * a.k_idx + r] : -1;
+    t.id = (t.in_range && r < a.k_idx) ? a.idx[(int64_t)a.qb * a.k_idx + r] : -1;
   }
 }
 
 // The row loads of a tile (unconditional, clamped addresses: all in flight together).
 __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n, int g) {
-  const int qb = blockIdx.y;
+  const int qb = a.qb;
   if (!t.swa) {
     t.ok = t.id >= 0 && t.id < a.cap;
     const int64_t row = (int64_t)(qb / a.q_per_seq) * a.cap + (t.ok ? t.id : 0);
@@ -324,9 +325,19 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   using Cfg = AttnCfg<W>;
   __shared__ __attribute__((aligned(16))) AttnSmem<W> sm;
   constexpr int kSlices = Cfg::kSlices;
-  const int qb = blockIdx.y, split = blockIdx.x;
+  const int split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
+  // Workgroups are dealt to the 8 XCDs round-robin (linear id mod 8).  With
+  // one workgroup per query, XCD x takes a contiguous run of queries, so
+  // that neighbouring queries -- whose windows overlap in all but one row
+  // when they are consecutive tokens -- share that XCD's L2.
+  int qb = blockIdx.y;
+  if (gridDim.x == 1) {
+    const int nq = gridDim.y, per = nq / 8, rem = nq % 8;
+    const int x = blockIdx.y % 8, i = blockIdx.y / 8;
+    qb = x * per + min(x, rem) + i;
+  }
 
   // Main Q: loaded first so that its loads overlap the index and row loads.
   // Registers: lane (n, g) holds head n, channels 128g..128g+127 (the B
@@ -346,6 +357,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   }
 
   AttnArgs a;
+  a.qb = qb;
   a.codes = codes;
   a.scales = scales;
   a.cap = cap;
@@ -392,10 +404,14 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
       });
       if (has_next) cur = nxt;
     } else {
+      // The next chunk's indices are loaded now, its rows after this chunk:
+      // one of its two dependent round trips overlaps this chunk's work.
+      AttnTile nxt;
+      if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);
       attn_chunk<W>(sm, st, ch == c_begin, cur, qb_operand, scale_log2, []() {});
       if (has_next) {
-        tile_begin<W>(cur, a, ch + 1, wave, n);
-        tile_load(cur, a, n, g);
+        tile_load(nxt, a, n, g);
+        cur = nxt;
       }
     }
   }
