@@ -233,18 +233,23 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       use_pool = s->layers[s->full_of_layer[l]].hierarchical != 0;
     }
     if (st == CSA2_OK && L.mode != CSA2_REUSE) {
+      // Up to kTopkRowsMax slots the selection reads the scores once in
+      // registers (no histogram from the score kernel); longer inputs get the
+      // histogram fused into the scoring pass.
       if (use_pool) {
         const int64_t n_out = (int64_t)d.pool_blocks * d.blk;
+        const bool fused = n_out > kTopkRowsMax;
         st = index_score_launch(io->idx_q[l], w, io->idx_k, d.key_cap, io->lens, 1, s->pool, d.pool_blocks,
-                                d.blk, s->scores, n_out, d.n_seq, s->tw.hist, stream);
+                                d.blk, s->scores, n_out, d.n_seq, fused ? s->tw.hist : nullptr, stream);
         if (st == CSA2_OK)
-          st = topk_launch(s->scores, n_out, nullptr, 1, d.topk, s->pool, d.pool_blocks, d.blk, idx, s->tw, true,
+          st = topk_launch(s->scores, n_out, nullptr, 1, d.topk, s->pool, d.pool_blocks, d.blk, idx, s->tw, fused,
                            d.n_seq, stream);
       } else {
+        const bool fused = d.key_cap > kTopkRowsMax;
         st = index_score_launch(io->idx_q[l], w, io->idx_k, d.key_cap, io->lens, 1, nullptr, 0, 1, s->scores,
-                                d.key_cap, d.n_seq, s->tw.hist, stream);
+                                d.key_cap, d.n_seq, fused ? s->tw.hist : nullptr, stream);
         if (st == CSA2_OK)
-          st = topk_launch(s->scores, d.key_cap, io->lens, 1, d.topk, nullptr, 0, 1, idx, s->tw, true, d.n_seq,
+          st = topk_launch(s->scores, d.key_cap, io->lens, 1, d.topk, nullptr, 0, 1, idx, s->tw, fused, d.n_seq,
                            stream);
       }
     }

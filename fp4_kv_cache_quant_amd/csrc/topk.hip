@@ -474,6 +474,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
 // finish_output emits the ids.  Reads every score once; used when no
 // histogram was produced upstream (many sequences of moderate length).
 constexpr int kRowsMax = 64 * kFinalThreads;  // 65,536 slots
+static_assert(kRowsMax == kTopkRowsMax, "register-resident selection length");
 
 struct RowsSmem {
   int32_t pool[CSA2_TOPK_MAX];

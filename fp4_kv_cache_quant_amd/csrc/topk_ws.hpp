@@ -32,6 +32,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inputs of at most this many slots per sequence are selected by one
+// workgroup per sequence with the scores held in registers, unless a
+// histogram was produced upstream.
+constexpr int64_t kTopkRowsMax = 65536;
+
 size_t topk_workspace_bytes(int64_t n, int32_t n_seq);
 TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq);
 // hist_ready: ws.hist already holds the histogram of these scores (written by
