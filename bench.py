@@ -34,16 +34,16 @@ PEAK_HBM_GBPS = 8000.0
 # the kernel sources they were taken on: a figure is reported only while
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
-    "sparse_attn": {"bytes": 12814888, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+    "sparse_attn": {"bytes": 12767720, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
                     "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                                "b837a69f2edab4fe3081ef6e1e3259c5b87a45d602dbc4a7d20f6de078544985",
+                                "e048ff920a55b78fcc23a9bed24e46539ccc4d466116c4af3fc4c57d098f1932",
                                 "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                                "4b06a55aa18d35a33a75b38bfaddc7b47986a52faa4267ea1792d0ee40b3312f"}},
-    "block_scan": {"bytes": 279875254, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+                                "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
+    "block_scan": {"bytes": 280649850, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
                    "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                               "9bebab09e10532f6aebd4dfd2350e391aa610582dbe7cef53b68a995b5d96f0f",
+                               "2805cdc75311ed99d69ed6cc28b98a17c2d8618c448ac40e07f5dd6cccddb000",
                                "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                               "4b06a55aa18d35a33a75b38bfaddc7b47986a52faa4267ea1792d0ee40b3312f"}},
+                               "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
 }
 
 
