@@ -56,6 +56,8 @@ PINS = {
     "orc_pool_blocks/orc_pool_select": "hierarchical == flat when blocks <= pool; subset/size invariants",
     "orc_sparse_attn": "k >= L equals torch CPU float64 dense softmax attention; 1 key, equal keys, q = 0",
     "decode_step": "Reuse reproduces the latest Full/Reindex indices; Reindex with Full's Q == Full",
+    "orc_fp8_code": "all 65,536 bf16 patterns vs torch's float8_e4m3fn cast in range, saturation and NaN beyond; golden ties",
+    "orc_sparse_attn_fp8w": "equals orc_sparse_attn on window rows that FP8 represents exactly (bf16 of E4M3 values)",
 }
 
 
@@ -105,6 +107,12 @@ def lib() -> ctypes.CDLL:
         L.orc_pool_select.restype = i64
         L.orc_sparse_attn.argtypes = [P, P, P, P, i64, P, i64, ctypes.c_double, P]
         L.orc_sparse_attn.restype = None
+        L.orc_fp8_code.argtypes = [ctypes.c_uint16]
+        L.orc_fp8_code.restype = ctypes.c_uint8
+        L.orc_fp8_rows.argtypes = [P, i64, P]
+        L.orc_fp8_rows.restype = None
+        L.orc_sparse_attn_fp8w.argtypes = [P, P, P, P, i64, P, i64, ctypes.c_double, P]
+        L.orc_sparse_attn_fp8w.restype = None
         _lib = L
     return _lib
 
@@ -211,12 +219,44 @@ def sparse_attn(q, codes, scales, idx, swa, swa_len: int, sm_scale: float) -> np
     return out
 
 
-def sparse_attn_gathered(q, rows_codes, rows_scales, idx, swa, swa_len, sm_scale):
+def sparse_attn_gathered(q, rows_codes, rows_scales, idx, swa, swa_len, sm_scale, swa8=None):
     """Like :func:`sparse_attn` for a compact cache: ``rows_*[i]`` holds the
-    row of position ``idx[i]`` (used when the full cache is not on the host)."""
+    row of position ``idx[i]`` (used when the full cache is not on the host).
+    With ``swa8`` the window rows are those FP8 codes (``swa`` is ignored)."""
     idx = np.asarray(idx, dtype=np.int64)
     local = np.where(idx >= 0, np.arange(len(idx)), -1)
+    if swa8 is not None:
+        return sparse_attn_fp8w(q, rows_codes, rows_scales, local, swa8, swa_len, sm_scale)
     return sparse_attn(q, rows_codes, rows_scales, local, swa, swa_len, sm_scale)
+
+
+# ------------------------------------------------------------ FP8 window
+def fp8_code(b: int) -> int:
+    """E4M3 code of one bf16 bit pattern (round to nearest even, saturating)."""
+    return int(lib().orc_fp8_code(int(b) & 0xFFFF))
+
+
+def fp8_rows(x_bf16: np.ndarray) -> np.ndarray:
+    """bf16 rows [n][512] -> E4M3 codes [n][512] (uint8)."""
+    x = _u16(x_bf16).reshape(-1, D)
+    out = np.zeros(x.shape, np.uint8)
+    lib().orc_fp8_rows(_p(x), x.shape[0], _p(out))
+    return out
+
+
+def sparse_attn_fp8w(q, codes, scales, idx, swa8, swa_len: int, sm_scale: float) -> np.ndarray:
+    """:func:`sparse_attn` with the window rows given as E4M3 codes [>= swa_len][512]."""
+    q = _u16(q).reshape(HEADS, D)
+    codes = np.ascontiguousarray(codes, np.uint8).reshape(-1, CODE_BYTES)
+    scales = np.ascontiguousarray(scales, np.uint8).reshape(-1, SCALE_BYTES)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    assert idx.max(initial=-1) < codes.shape[0]
+    swa8 = np.ascontiguousarray(swa8, np.uint8).reshape(-1, D)
+    assert swa_len <= swa8.shape[0]
+    out = np.zeros((HEADS, D), np.float32)
+    lib().orc_sparse_attn_fp8w(_p(q), _p(codes), _p(scales), _p(idx), len(idx), _p(swa8), swa_len,
+                               float(sm_scale), _p(out))
+    return out
 
 
 # ------------------------------------------------------------- layer walk
@@ -258,9 +298,10 @@ class SeqState:
 class LayerInputs:
     idx_q: Optional[np.ndarray]   # [8][64] for Full/Reindex layers
     main_q: np.ndarray            # [16][512]
-    swa: np.ndarray               # [>= swa_len][512]
+    swa: np.ndarray               # [>= swa_len][512] bf16 bits
     swa_len: int
     w: Optional[np.ndarray] = None
+    swa8: Optional[np.ndarray] = None  # the window as E4M3 codes instead of swa
 
 
 @dataclass
@@ -303,7 +344,7 @@ def decode_layers(layers: Sequence[Layer], seq: SeqState, inputs: Sequence[Layer
         out = None
         if attend:
             codes, scales = seq.kv_rows(layer.kv_id, idx)
-            out = sparse_attn_gathered(inp.main_q, codes, scales, idx, inp.swa, inp.swa_len, sm_scale)
+            out = sparse_attn_gathered(inp.main_q, codes, scales, idx, inp.swa, inp.swa_len, sm_scale, inp.swa8)
         res.append(LayerResult(idx=idx.copy(), pool=None if pool is None else pool.copy(), out=out))
     return res
 

@@ -291,23 +291,11 @@ int64_t orc_pool_select(const uint16_t* q, const float* w, const uint16_t* tok_k
  * (READING: one softmax over the concatenation, no de-duplication).
  * For each head h: z_j = sm_scale * (q_h . x_j), p = softmax(z),
  * o_h = sum_j p_j x_j, rounded to binary32.  An empty set gives o_h = 0. */
-void orc_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                     const int64_t* idx, int64_t n_idx, const uint16_t* swa, int64_t swa_len,
-                     double sm_scale, float* out) {
-  int64_t n_sel = 0;
-  for (int64_t i = 0; i < n_idx; ++i) n_sel += idx[i] >= 0;
-  int64_t n = n_sel + (swa_len > 0 ? swa_len : 0);
-  double* x = (double*)malloc((size_t)(n > 0 ? n : 1) * D_LATENT * sizeof(double));
+/* Attention of 16 heads over n value rows x [n][512] (double): for each
+ * head h, z_j = sm_scale * (q_h . x_j), p = softmax(z), o_h = sum_j p_j x_j,
+ * rounded to binary32; an empty set gives o_h = 0. */
+static void attn_over_rows(const uint16_t* q, const double* x, int64_t n, double sm_scale, float* out) {
   double* z = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
-  int64_t r = 0;
-  for (int64_t i = 0; i < n_idx; ++i) {
-    if (idx[i] < 0) continue;
-    orc_dequant_row(codes + idx[i] * CODE_BYTES, scales + idx[i] * N_GROUPS, x + r * D_LATENT);
-    ++r;
-  }
-  for (int64_t j = 0; j < swa_len; ++j, ++r)
-    for (int d = 0; d < D_LATENT; ++d) x[r * D_LATENT + d] = orc_bf16_value(swa[j * D_LATENT + d]);
-
   for (int h = 0; h < MAIN_HEADS; ++h) {
     double zmax = -INFINITY, denom = 0.0;
     for (int64_t j = 0; j < n; ++j) {
@@ -326,6 +314,67 @@ void orc_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* sca
       out[h * D_LATENT + d] = (n > 0) ? (float)(acc / denom) : 0.0f;
     }
   }
-  free(x);
   free(z);
+}
+
+/* The selected rows idx[i] >= 0 of the FP4 cache, dequantised, into x;
+ * returns how many. */
+static int64_t gather_rows(const uint8_t* codes, const uint8_t* scales, const int64_t* idx, int64_t n_idx,
+                           double* x) {
+  int64_t r = 0;
+  for (int64_t i = 0; i < n_idx; ++i) {
+    if (idx[i] < 0) continue;
+    orc_dequant_row(codes + idx[i] * CODE_BYTES, scales + idx[i] * N_GROUPS, x + r * D_LATENT);
+    ++r;
+  }
+  return r;
+}
+
+static int64_t count_selected(const int64_t* idx, int64_t n_idx) {
+  int64_t n_sel = 0;
+  for (int64_t i = 0; i < n_idx; ++i) n_sel += idx[i] >= 0;
+  return n_sel;
+}
+
+void orc_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                     const int64_t* idx, int64_t n_idx, const uint16_t* swa, int64_t swa_len,
+                     double sm_scale, float* out) {
+  const int64_t n = count_selected(idx, n_idx) + (swa_len > 0 ? swa_len : 0);
+  double* x = (double*)malloc((size_t)(n > 0 ? n : 1) * D_LATENT * sizeof(double));
+  int64_t r = gather_rows(codes, scales, idx, n_idx, x);
+  for (int64_t j = 0; j < swa_len; ++j, ++r)
+    for (int d = 0; d < D_LATENT; ++d) x[r * D_LATENT + d] = orc_bf16_value(swa[j * D_LATENT + d]);
+  attn_over_rows(q, x, n, sm_scale, out);
+  free(x);
+}
+
+/* ------------------------------------------------------------ FP8 window */
+
+/* [P4] summary: the sliding-window KV is kept in FP8.  READING: OCP E4M3FN
+ * elements, one byte per channel, no scale: the E4M3 round-to-nearest-even
+ * of the bf16 value with ties to the even code, saturating at +-448; the
+ * sign bit is copied (also for zero); NaN stays NaN (S.1111.111). */
+uint8_t orc_fp8_code(uint16_t b) {
+  const double x = orc_bf16_value(b);
+  const int neg = (b >> 15) & 1;
+  if (isnan(x)) return (uint8_t)((neg << 7) | 0x7F);
+  return (uint8_t)((neg << 7) | nearest_even_index(fabs(x), 1.0, g_e4m3_pos, 127));
+}
+
+void orc_fp8_rows(const uint16_t* x, int64_t n_rows, uint8_t* out) {
+  for (int64_t i = 0; i < n_rows * D_LATENT; ++i) out[i] = orc_fp8_code(x[i]);
+}
+
+/* orc_sparse_attn with FP8 window rows: window row j's channel d is
+ * E4M3(swa8[j][d]) (exact). */
+void orc_sparse_attn_fp8w(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                          const int64_t* idx, int64_t n_idx, const uint8_t* swa8, int64_t swa_len,
+                          double sm_scale, float* out) {
+  const int64_t n = count_selected(idx, n_idx) + (swa_len > 0 ? swa_len : 0);
+  double* x = (double*)malloc((size_t)(n > 0 ? n : 1) * D_LATENT * sizeof(double));
+  int64_t r = gather_rows(codes, scales, idx, n_idx, x);
+  for (int64_t j = 0; j < swa_len; ++j, ++r)
+    for (int d = 0; d < D_LATENT; ++d) x[r * D_LATENT + d] = orc_e4m3_value(swa8[j * D_LATENT + d]);
+  attn_over_rows(q, x, n, sm_scale, out);
+  free(x);
 }

@@ -12,8 +12,8 @@ import numpy as np
 import synth
 from synth.configs import REUSE, DecodeConfig, PrefillConfig
 
-from . import (Layer, LayerInputs, SeqState, decode_layers, prefill_query, prefill_visible_entries,
-               prefill_window, quant_rows)
+from . import (Layer, LayerInputs, SeqState, decode_layers, fp8_rows, prefill_query,
+               prefill_visible_entries, prefill_window, quant_rows)
 
 SM_SCALE = 512 ** -0.5
 
@@ -58,7 +58,8 @@ def layer_inputs(cfg: DecodeConfig, b: int, step: int):
         iq = None if mode == REUSE else _gen(cfg, cfg.idx_q(l, step), b, np.arange(8), 64)
         mq = _gen(cfg, cfg.main_q(l, step), b, np.arange(16), 512)
         sw = _gen(cfg, cfg.swa_rows(l), b, np.arange(cfg.swa), 512)
-        ins.append(LayerInputs(idx_q=iq, main_q=mq, swa=sw, swa_len=cfg.swa))
+        sw8 = fp8_rows(sw) if cfg.swa_fp8 else None
+        ins.append(LayerInputs(idx_q=iq, main_q=mq, swa=sw, swa_len=cfg.swa, swa8=sw8))
     return ins
 
 

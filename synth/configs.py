@@ -30,6 +30,7 @@ class DecodeConfig:
     swa: int = 128
     q_sets: int = 4                           # step s uses query set s % q_sets
     seed: int = 0
+    swa_fp8: bool = False                     # window rows stored as E4M3 (FP8) codes
 
     def cap(self, steps: int) -> int:
         """Rows per sequence of every main-KV tensor and of indexer K."""
@@ -96,8 +97,12 @@ DECODER_20L_1M = DecodeConfig(
     layers=_group(FULL, 0, 1, 3) + sum((_group(REINDEX, g, 0, 3) for g in range(1, 5)), ()),
     n_kv=5, append=True)
 
+# The same schedule with FP8 window rows.
+DECODER_20L_1M_FP8_WINDOW = DECODER_20L_1M.with_(
+    name="20-layer decoder schedule, 1M positions, batch 16, FP8 window rows", swa_fp8=True)
+
 DECODE_CONFIGS = {"single_4k": SINGLE_LAYER_4K, "group_64k": GROUP_64K, "hier_1m": HIER_1M,
-                  "decoder20_1m": DECODER_20L_1M}
+                  "decoder20_1m": DECODER_20L_1M, "decoder20_1m_fp8win": DECODER_20L_1M_FP8_WINDOW}
 
 
 @dataclass(frozen=True)

@@ -1,0 +1,85 @@
+"""HIP-graph replays of whole decode steps and prefill chunks: a captured
+step is replayed several times, with the program's own eager work and
+synchronisations in between, and every replay must reproduce the eager
+result bit for bit (the same kernels on the same inputs; nothing in a step
+may depend on state a replay does not restore)."""
+import numpy as np
+import pytest
+import torch
+
+from synth import configs as C
+from gpu_helpers import print_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp4_kv_cache_quant_amd import workloads
+    return workloads
+
+
+def _capture(fn):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    return g
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("hier_small", C.HIER_1M.with_(n_seq=3, L0=8 * 20000 + 5, q_sets=1)),
+    ("decoder20_small", C.DECODER_20L_1M.with_(n_seq=2, L0=8 * 3000 + 1, q_sets=1, append=False)),
+    ("group_flat", C.GROUP_64K.with_(n_seq=4, L0=5000, q_sets=1, append=False)),
+])
+def test_decode_step_graph_replays_match_eager(wl, name, cfg):
+    print_case(f"graph decode {name}")
+    inp = wl.build_decode_inputs(cfg, 1)
+    sched = wl.make_sched(inp)
+    io = wl.step_ios(sched, inp)[0]
+    nl = len(cfg.layers)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return ([sched.indices(l).cpu().numpy() for l in range(nl)],
+                [o.cpu().numpy().copy() for o in inp.out])
+
+    sched.decode_step(io)
+    ref_idx, ref_out = snapshot()
+    g = _capture(lambda: sched.decode_step(io))
+    for rep in range(3):
+        for o in inp.out:  # eager work between replays
+            o.fill_(float("nan"))
+        g.replay()
+        idx, out = snapshot()
+        for l in range(nl):
+            assert np.array_equal(idx[l], ref_idx[l]), f"replay {rep} layer {l} indices"
+            assert np.array_equal(out[l], ref_out[l]), f"replay {rep} layer {l} output"
+    assert sched.check() == 0
+    sched.close()
+
+
+def test_prefill_chunk_graph_replays_match_eager(wl):
+    cfg = C.ENCODER_PREFILL_128K.with_(n_entries=2000, n_q=40, t0=2 * 2000 - 40)
+    print_case("graph prefill chunk")
+    inp = wl.build_prefill_inputs(cfg)
+    pf, io = wl.make_prefill(inp)
+    pf.run(io)
+    torch.cuda.synchronize()
+    ref_idx = inp.idx[0].cpu().numpy()
+    ref_out = [o.cpu().numpy().copy() for o in inp.out]
+    g = _capture(lambda: pf.run(io))
+    for rep in range(3):
+        inp.idx[0].fill_(-7)
+        for o in inp.out:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(inp.idx[0].cpu().numpy(), ref_idx), f"replay {rep} indices"
+        for l, o in enumerate(inp.out):
+            assert np.array_equal(o.cpu().numpy(), ref_out[l]), f"replay {rep} layer {l}"

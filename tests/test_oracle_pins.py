@@ -403,3 +403,44 @@ def test_prefill_window_by_enumeration():
         for t in range(300):
             toks = [u for u in range(t + 1) if t - u < swa]
             assert oracle.prefill_window(t, swa) == (toks[0], len(toks))
+
+
+# ------------------------------------------------------------- FP8 window
+def test_fp8_code_golden_worked_values():
+    for h, _value, code, *_ in _golden_lines("fp8_e4m3_rne.txt"):
+        assert oracle.fp8_code(int(h, 16)) == int(code, 16), h
+
+
+def test_fp8_codes_of_all_bf16_vs_torch_cast():
+    """Every bf16 pattern: where torch's float -> float8_e4m3fn cast does not
+    overflow (|x| < 464, half-way past 448) the codes agree bit for bit,
+    signed zeros included; beyond, the oracle saturates to +-448; NaN maps
+    to NaN with the sign kept."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = synth.bf16_to_f32(bits).astype(np.float32)
+    got = oracle.fp8_rows(bits.reshape(-1, 512)).reshape(-1)   # 128 rows of 512
+    nan = np.isnan(x)
+    fits = ~nan & (np.abs(x) < 464.0)
+    ref = torch.from_numpy(x[fits]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got[fits], ref)
+    big = ~nan & ~fits
+    assert np.all(got[big] == np.where(x[big] > 0, 0x7E, 0xFE))
+    assert np.all((got[nan] & 0x7F) == 0x7F) and np.all((got[nan] >> 7) == (bits[nan] >> 15))
+
+
+def test_fp8_window_attention_equals_bf16_window_on_exact_rows():
+    """With window rows whose values FP8 holds exactly, attention over the
+    FP8 window equals attention over the same rows in bf16."""
+    rng = np.random.default_rng(11)
+    codes8 = rng.integers(0, 256, size=(40, 512)).astype(np.uint8)
+    codes8[(codes8 & 0x7F) == 0x7F] = 0x3C                     # no NaN
+    vals = np.array([oracle.lib().orc_e4m3_value(int(c)) for c in range(256)])
+    rows_bf16 = f32_to_bf16(vals[codes8].astype(np.float32))   # exact: E4M3 values are bf16 values
+    assert np.array_equal(oracle.fp8_rows(rows_bf16), codes8)
+    src = synth.gen_rows(0, 99, synth.NORMAL, [0], np.arange(50), 512)[0]
+    codes, scales = oracle.quant_rows(src)
+    q = synth.gen_rows(0, 98, synth.NORMAL, [0], np.arange(16), 512)[0]
+    idx = np.array([3, 7, -1, 20, 49], np.int64)
+    a = oracle.sparse_attn(q, codes, scales, idx, rows_bf16, 37, 512 ** -0.5)
+    b = oracle.sparse_attn_fp8w(q, codes, scales, idx, codes8, 37, 512 ** -0.5)
+    assert np.array_equal(a, b)
