@@ -13,10 +13,12 @@ roofline of the dominant op (timed with HIP events), the CPU oracle on a
 bounded sample of the same workload, a parity check of one step against
 that oracle sample, and (key "prefill") the ratio-2 causal prefill chunk of
 the encoder group: time per 4,096-query chunk, MFMA rate of its scoring and
-attention kernels, sampled parity and the oracle's rate.
+attention kernels, sampled parity and the oracle's rate; and (key
+"fp8_window") the same decode step with the window rows stored as E4M3.
 
 usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-graph]
                        [--cpu-seqs 16] [--no-cpu] [--no-prefill] [--prefill-reps 5]
+                       [--no-fp8-window] [--config NAME]
 """
 from __future__ import annotations
 
@@ -72,7 +74,7 @@ def algorithmic_bytes(cfg, L: int) -> dict:
     Per sequence: the block keys of all ceil(L/8) blocks (128 B each), the
     indexer keys of the pool's positions (128 B each; shared by the Full and
     Reindex layers), the selected FP4 rows of each main-KV tensor (512 x 288
-    B), every layer's SWA window (128 x 1 KiB), main Q (16 KiB) and f32
+    B), every layer's SWA window (128 x 1 KiB, or 512 B rows in FP8), main Q (16 KiB) and f32
     output (32 KiB), each selecting layer's indexer Q (1 KiB) and indices
     (2 KiB), and the append (1 KiB read, 288 B written)."""
     n = cfg.n_seq
@@ -85,7 +87,7 @@ def algorithmic_bytes(cfg, L: int) -> dict:
         "block_keys": n * nblk * 128 if cfg.hierarchical else 0,
         "indexer_keys": n * pool_pos * 128,
         "fp4_rows": n * groups * cfg.topk * 288,
-        "swa": n * nl * cfg.swa * 1024,
+        "swa": n * nl * cfg.swa * (512 if cfg.swa_fp8 else 1024),
         "main_q": n * nl * 16 * 1024,
         "out": n * nl * 16 * 512 * 4,
         "indexer_q_and_indices": n * sel_layers * (1024 + cfg.topk * 4),
@@ -202,7 +204,7 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
         ("pool_topk", "pool Top-512 (topk)", sel_layers, n * pool_slots * 4,
           lambda: csa2.topk(pscores, cfg.topk, idx, pool=pool, blk=cfg.blk, ws=tws)),
         ("sparse_attn", "sparse+SWA attention (sparse_attn: chunk + combine kernels)", len(cfg.layers),
-         n * (cfg.topk * 4 + cfg.topk * 288 + cfg.swa * 1024 + 16 * 1024 + 16 * 512 * 4),
+         n * (cfg.topk * 4 + cfg.topk * 288 + cfg.swa * (512 if cfg.swa_fp8 else 1024) + 16 * 1024 + 16 * 512 * 4),
          lambda: csa2.sparse_attn(inp.main_q[0][0], inp.kv[0], idx, inp.swa[0], inp.swa_len, 512 ** -0.5, out,
                                   ws=aws)),
     ]
@@ -319,6 +321,66 @@ def prefill_bench(args) -> dict:
     }
 
 
+def fp8_window_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
+    """The same step with the window rows stored as E4M3 (FP8): the window
+    tensors are quantised from the bf16 ones, every other input is shared;
+    lengths are reset so the appends rewrite the same rows."""
+    import torch
+
+    import fp4_kv_cache_quant_amd as csa2
+    from fp4_kv_cache_quant_amd import workloads as wl
+
+    c8 = cfg.with_(swa_fp8=True, name=cfg.name + ", FP8 window rows")
+    swa8 = []
+    for t in inp.swa:
+        t8 = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
+        csa2.quant_fp8_rows(t, t8)
+        swa8.append(t8)
+    inp8 = wl.DecodeInputs(cfg=c8, steps=inp.steps, kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, blk_k=inp.blk_k,
+                           swa=swa8, swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q, main_q=inp.main_q,
+                           new_row=inp.new_row)
+    inp8.reset_lens()
+    sched = wl.make_sched(inp8)
+    ios = wl.step_ios(sched, inp8)
+    stream = torch.cuda.current_stream()
+    sched.decode_step(ios[0])
+    graphs = []
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for s_ in range(c8.q_sets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    sched.decode_step(ios[s_])
+                graphs.append(g)
+        stream.wait_stream(side)
+
+    def run_step(s_):
+        if graphs:
+            graphs[s_ % c8.q_sets].replay()
+        else:
+            sched.decode_step(ios[s_ % c8.q_sets])
+
+    for s_ in range(1, 1 + W):
+        run_step(s_)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s_ in range(1 + W, 1 + W + K):
+        run_step(s_)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    flag = sched.check()
+    sched.close()
+    ab = algorithmic_bytes(c8, c8.lens_at(1 + W + K // 2))
+    return {"workload": c8.name, "ms_per_step": round(ms, 4),
+            "value": round(c8.n_seq * len(c8.layers) / (ms * 1e-3), 1), "unit": "(seq·layer)-steps/s",
+            "algorithmic_bytes_per_step": ab["total"], "GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
+            "append_overflow": bool(flag)}
+
+
 def compare_step(cfg, gpu, ref) -> dict:
     """GPU step-0 results against the oracle sample: indices and pool
     bit-exact, attention rel. L2 <= 1e-3 and max abs <= 5e-3 per (seq, head)."""
@@ -351,6 +413,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--config", default="decoder20_1m")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--no-fp8-window", action="store_true", help="skip the FP8-window variant of the step")
     ap.add_argument("--prefill-reps", type=int, default=5, help="timed prefill chunks")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for scaling profiler traffic counters)")
@@ -452,6 +515,10 @@ def main() -> int:
                          f"(hierarchical select, 4 Reindex rescorings, {nl} attentions), {dt:.1f} s"}
         parity = compare_step(cfg, gpu0, res)
 
+    fp8w = None
+    if not args.no_fp8_window and not cfg.swa_fp8:
+        fp8w = fp8_window_leg(cfg, inp, K, W, graph=not args.no_graph)
+
     prefill = None
     if not args.no_prefill:
         prefill = prefill_bench(args)
@@ -467,7 +534,7 @@ def main() -> int:
         "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": round(hbm_gbps, 1),
                 "frac_of_peak": round(hbm_gbps / PEAK_HBM_GBPS, 4), "parts": ab},
         "roofline": roofline, "dominant_op": dom, "ops": ops, "cpu_baseline": cpu, "parity_step0": parity,
-        "prefill": prefill,
+        "fp8_window": fp8w, "prefill": prefill,
         "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
     }
     print(json.dumps(line), flush=True)

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
     "sparse_attn", "sparse_attn_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
-    "prefill_index_score", "Prefill",
+    "prefill_index_score", "Prefill", "quant_fp8_rows",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
 
@@ -45,7 +45,7 @@ class _Layer(ctypes.Structure):
 class _SchedDesc(ctypes.Structure):
     _fields_ = [("n_seq", _I32), ("n_layers", _I32), ("layers", _P), ("key_cap", _I64),
                 ("blk_cap", _I64), ("topk", _I32), ("pool_blocks", _I32), ("blk", _I32),
-                ("swa_max", _I32), ("sm_scale", _F32)]
+                ("swa_max", _I32), ("sm_scale", _F32), ("swa_fp8", _I32)]
 
 
 class _StepIO(ctypes.Structure):
@@ -79,6 +79,9 @@ _index_score = _sig("csa2_index_score", _I32, _P, _P, _P, _I64, _P, _I32, _P, _I
 _topk_ws = _sig("csa2_topk_workspace_size", _SZ, _I64, _I32)
 _topk = _sig("csa2_topk", _I32, _P, _I64, _P, _I32, _I32, _P, _I32, _I32, _P, _P, _SZ, _I32, _P)
 _attn_ws = _sig("csa2_sparse_attn_workspace_size", _SZ, _I32, _I32, _I32)
+_attn_f8w = _sig("csa2_sparse_attn_f8w", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
+                 _I32, _F32, _P, _P, _SZ, _P)
+_quant_fp8 = _sig("csa2_quant_fp8_rows", _I32, _P, _I64, _P, _P)
 _attn = _sig("csa2_sparse_attn", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
              _I32, _F32, _P, _P, _SZ, _P)
 _sched_create = _sig("csa2_sched_create", _I32, ctypes.POINTER(_SchedDesc), ctypes.POINTER(_P))
@@ -151,6 +154,13 @@ def quant_rows(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, str
     _check(_quant_rows(_ptr(src), n, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
+def quant_fp8_rows(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Window rows src [n][512] bf16 -> dst [n][512] uint8 E4M3 codes."""
+    n = src.numel() // LATENT
+    assert dst.dtype == torch.uint8 and dst.numel() >= n * LATENT
+    _check(_quant_fp8(_ptr(src), n, _ptr(dst), _stream(stream)))
+
+
 def quant_append(src: torch.Tensor, kv: FP4KV, lens: torch.Tensor, err_flag: Optional[torch.Tensor] = None,
                  stream=None) -> None:
     assert src.numel() == kv.n_seq * LATENT and lens.dtype == torch.int32 and lens.numel() == kv.n_seq
@@ -192,7 +202,8 @@ def sparse_attn_workspace_size(n_q: int, k_idx: int, swa_max: int) -> int:
 def sparse_attn(q: torch.Tensor, kv: FP4KV, idx: torch.Tensor, swa: torch.Tensor, swa_len: torch.Tensor,
                 sm_scale: float, out: torch.Tensor, ws: Optional[torch.Tensor] = None, q_per_seq: int = 1,
                 swa_q_stride_rows: Optional[int] = None, swa_max: Optional[int] = None, stream=None) -> None:
-    """q [n_q][16][512] bf16; idx [n_q][k_idx] int32; swa rows [..][512] bf16; out [n_q][16][512] f32."""
+    """q [n_q][16][512] bf16; idx [n_q][k_idx] int32; swa rows [..][512] bf16, or uint8 E4M3 codes
+    (the FP8 window, csa2_sparse_attn_f8w); out [n_q][16][512] f32."""
     n_q = q.shape[0]
     k_idx = idx.shape[1] if idx is not None and idx.dim() == 2 else 0
     if swa_max is None:
@@ -203,8 +214,9 @@ def sparse_attn(q: torch.Tensor, kv: FP4KV, idx: torch.Tensor, swa: torch.Tensor
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     kvc = kv.c()
-    _check(_attn(_ptr(q), n_q, ctypes.byref(kvc), q_per_seq, _ptr(idx), k_idx, _ptr(swa), swa_q_stride_rows,
-                 _ptr(swa_len), swa_max, sm_scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    fn = _attn_f8w if (swa is not None and swa.dtype == torch.uint8) else _attn  # E4M3 window rows
+    _check(fn(_ptr(q), n_q, ctypes.byref(kvc), q_per_seq, _ptr(idx), k_idx, _ptr(swa), swa_q_stride_rows,
+              _ptr(swa_len), swa_max, sm_scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 class Layer:
@@ -216,10 +228,11 @@ class Sched:
     """The native layer-group scheduler (csa2_sched_*)."""
 
     def __init__(self, layers: Sequence[Layer], n_seq: int, key_cap: int, blk_cap: int = 0, topk: int = 512,
-                 pool_blocks: int = 2048, blk: int = 8, swa_max: int = 128, sm_scale: float = 512 ** -0.5):
+                 pool_blocks: int = 2048, blk: int = 8, swa_max: int = 128, sm_scale: float = 512 ** -0.5,
+                 swa_fp8: bool = False):
         arr = (_Layer * len(layers))(*[_Layer(l.mode, l.kv_id, int(l.hierarchical)) for l in layers])
         desc = _SchedDesc(n_seq, len(layers), ctypes.cast(arr, _P), key_cap, blk_cap, topk, pool_blocks, blk,
-                          swa_max, sm_scale)
+                          swa_max, sm_scale, int(swa_fp8))
         h = _P()
         _check(_sched_create(ctypes.byref(desc), ctypes.byref(h)))
         self._h = h

@@ -12,13 +12,13 @@ namespace csa2 {
 
 csa2_status quant_rows_launch(const uint16_t*, int64_t, uint8_t*, uint8_t*, hipStream_t);
 csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, int32_t*, hipStream_t);
+csa2_status quant_fp8_launch(const uint16_t*, int64_t, uint8_t*, hipStream_t);
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
                                uint32_t*, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const uint16_t*, int64_t, const int32_t*, int32_t, float, float*, void*,
-                        hipStream_t);
+                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
 
 namespace {
 thread_local std::string g_error;
@@ -82,7 +82,7 @@ csa2_status check_topk(const float* scores, int64_t n, int32_t len_div, int32_t 
 }
 
 csa2_status check_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
-                       const int32_t* idx, int32_t k_idx, const uint16_t* swa, const int32_t* swa_len,
+                       const int32_t* idx, int32_t k_idx, const void* swa, const int32_t* swa_len,
                        int32_t swa_max, const float* out, const void* ws, size_t ws_bytes) {
   CSA2_REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ESHAPE, "csa2_sparse_attn: n_q must be in [0, 65535]");
   if (n_q == 0) return CSA2_OK;
@@ -117,7 +117,7 @@ extern "C" {
 
 const char* csa2_last_error(void) { return g_error.c_str(); }
 
-int32_t csa2_abi_version(void) { return 1; }
+int32_t csa2_abi_version(void) { return 2; }
 
 csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                             void* stream) {
@@ -180,8 +180,29 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
   clear_error();
   csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_len, swa_max, out, ws, ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;
-  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, false, swa_q_stride_rows, swa_len, swa_max,
                      sm_scale, out, ws, as_stream(stream));
+}
+
+csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                                 const int32_t* idx, int32_t k_idx, const uint8_t* swa,
+                                 int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                                 float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_len, swa_max, out, ws, ws_bytes);
+  if (st != CSA2_OK || n_q == 0) return st;
+  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, true, swa_q_stride_rows, swa_len, swa_max,
+                     sm_scale, out, ws, as_stream(stream));
+}
+
+csa2_status csa2_quant_fp8_rows(const uint16_t* src, int64_t n_rows, uint8_t* dst, void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_rows >= 0, CSA2_ESHAPE, "csa2_quant_fp8_rows: negative n_rows");
+  if (n_rows == 0) return CSA2_OK;
+  CSA2_REQUIRE(src && dst, CSA2_EINVAL, "csa2_quant_fp8_rows: null pointer");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 7) == 0,
+               CSA2_EINVAL, "csa2_quant_fp8_rows: src must be 16-byte and dst 8-byte aligned");
+  return quant_fp8_launch(src, n_rows, dst, as_stream(stream));
 }
 
 }  // extern "C"

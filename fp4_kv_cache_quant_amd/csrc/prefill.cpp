@@ -21,8 +21,7 @@ csa2_status prefill_score_launch(const uint16_t*, const float*, const uint16_t*,
                                  int32_t, float*, int32_t*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const uint16_t*, int64_t, const int32_t*, int32_t, float, float*, void*,
-                        hipStream_t);
+                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
 
 namespace {
@@ -174,8 +173,8 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
       cur = io->idx[l];
     }
     // Query i's window rows start at row i of the layer's SWA buffer.
-    st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, io->swa[l], 1, w.win_len, d.swa,
-                     d.sm_scale, io->out[l], w.attn, stream);
+    st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, io->swa[l], false, 1, w.win_len,
+                     d.swa, d.sm_scale, io->out[l], w.attn, stream);
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;

@@ -49,6 +49,44 @@ __device__ __forceinline__ uint32_t mag_code(float ax, float s) {
   return m;
 }
 
+// E4M3 code of one bf16 value (bits b): round-to-nearest-even of x onto
+// the E4M3FN grid, saturating at +-448 (0x7E), sign copied (also for 0),
+// NaN kept (S.1111.111).  Same exact search as scale_code with factor 1:
+// the largest code c with v(c) <= |x|, then |x| against the midpoint.
+__device__ __forceinline__ uint32_t fp8_code(uint32_t b) {
+  const uint32_t sign = (b >> 8) & 0x80u;
+  const float ax = bf16_to_f32(b & 0x7FFFu);
+  if (ax != ax) return sign | 0x7Fu;
+  uint32_t lo = 0, hi = 126;  // invariant: v(lo) <= ax (v(0) = 0)
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    if (e4m3_pos_value(mid) <= ax) lo = mid; else hi = mid - 1;
+  }
+  uint32_t c = lo;
+  if (lo < 126) {
+    const float t = 0.5f * (e4m3_pos_value(lo) + e4m3_pos_value(lo + 1));  // exact midpoint
+    if (ax > t || (ax == t && (lo & 1u))) c = lo + 1;
+  }
+  return sign | c;
+}
+
+// FP8 window rows: 8 channels per thread (16 bytes in, 8 bytes out).
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ src, int64_t n_vec,
+                                                        uint8_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_vec) return;
+  const u32x4 raw = reinterpret_cast<const u32x4*>(src)[i];
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    lo |= fp8_code(raw[k] & 0xFFFFu) << (16 * k);
+    lo |= fp8_code(raw[k] >> 16) << (16 * k + 8);
+    hi |= fp8_code(raw[k + 2] & 0xFFFFu) << (16 * k);
+    hi |= fp8_code(raw[k + 2] >> 16) << (16 * k + 8);
+  }
+  reinterpret_cast<uint2*>(dst)[i] = make_uint2(lo, hi);
+}
+
 // Quantise the 512 bf16 values at src into one packed row (one wavefront).
 __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ src,
                                                uint8_t* __restrict__ codes,
@@ -115,6 +153,15 @@ csa2_status quant_rows_launch(const uint16_t* src, int64_t n_rows, uint8_t* code
   hipLaunchKernelGGL(quant_rows_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, src, n_rows,
                      codes, scales);
   return launch_status("csa2_quant_rows");
+}
+
+csa2_status quant_fp8_launch(const uint16_t* src, int64_t n_rows, uint8_t* dst, hipStream_t stream) {
+  if (n_rows == 0) return CSA2_OK;
+  const int64_t n_vec = n_rows * (CSA2_LATENT / 8);
+  const int64_t blocks = (n_vec + 255) / 256;
+  CSA2_REQUIRE(blocks <= 0x7FFFFFFF, CSA2_ESHAPE, "csa2_quant_fp8_rows: too many rows for one launch");
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, src, n_vec, dst);
+  return launch_status("csa2_quant_fp8_rows");
 }
 
 csa2_status quant_append_launch(const uint16_t* src, const csa2_fp4_kv& kv, int32_t* lens,

@@ -23,8 +23,7 @@ csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, i
                                uint32_t*, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const uint16_t*, int64_t, const int32_t*, int32_t, float, float*, void*,
-                        hipStream_t);
+                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
 }  // namespace csa2
 
@@ -116,6 +115,7 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
                "csa2_sched_create: bad key_cap / topk");
   CSA2_REQUIRE(d.swa_max >= 0 && d.swa_max <= 4096 && d.topk + d.swa_max <= 8192, CSA2_ESHAPE,
                "csa2_sched_create: bad swa_max");
+  CSA2_REQUIRE(d.swa_fp8 == 0 || d.swa_fp8 == 1, CSA2_EINVAL, "csa2_sched_create: swa_fp8 must be 0 or 1");
 
   csa2_sched* s = new csa2_sched();
   s->desc = d;
@@ -254,8 +254,8 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       }
     }
     if (st == CSA2_OK)
-      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l], d.swa_max,
-                       io->swa_len, d.swa_max, d.sm_scale, io->out[l], s->attn_ws, stream);
+      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l], d.swa_fp8 != 0,
+                       d.swa_max, io->swa_len, d.swa_max, d.sm_scale, io->out[l], s->attn_ws, stream);
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;

@@ -150,7 +150,7 @@ struct AttnArgs {
   int32_t q_per_seq;
   const int32_t* idx;
   int32_t k_idx;
-  const uint16_t* swa;
+  const uint8_t* swa;  // window rows: bf16 (1,024 B) or E4M3 (512 B) per row
   int64_t swa_q_stride_rows;
   int32_t n_swa;
   int n_tiles, swa_tiles;
@@ -174,7 +174,10 @@ __device__ __forceinline__ void tile_begin(AttnTile& t, const AttnArgs& a, int c
   }
 }
 
-// The row loads of a tile (unconditional, clamped addresses: all in flight together).
+// The row loads of a tile (unconditional, clamped addresses: all in flight
+// together).  Window rows are bf16 (16 loads of 16 bytes per lane) or, with
+// kWin8, E4M3 bytes (8 loads).
+template <bool kWin8>
 __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n, int g) {
   const int qb = a.qb;
   if (!t.swa) {
@@ -190,16 +193,25 @@ __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n,
   } else {
     const int j = t.row0 + n;
     t.ok = t.in_range && j < a.n_swa;
+    constexpr int kRowBytes = kWin8 ? CSA2_LATENT : 2 * CSA2_LATENT;
     const u32x4* sp = reinterpret_cast<const u32x4*>(
-        a.swa + ((int64_t)qb * a.swa_q_stride_rows + (t.ok ? j : 0)) * CSA2_LATENT + 128 * g);
+        a.swa + ((int64_t)qb * a.swa_q_stride_rows + (t.ok ? j : 0)) * kRowBytes + (kRowBytes / 4) * g);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t.raw[i] = sp[i];
+    for (int i = 0; i < (kWin8 ? 8 : 16); ++i) t.raw[i] = sp[i];
   }
+}
+
+// Eight E4M3 bytes (two dwords) as four f16 pairs (exact).
+__device__ __forceinline__ u32x4 fp8x8_to_f16x8(uint32_t d0, uint32_t d1) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true))};
 }
 
 // Compute one chunk from the loaded tile (`between` runs after the softmax
 // statistics, before the PV product: the next chunk's loads go there).
-template <int W, typename QB, typename Between>
+template <int W, bool kWin8, typename QB, typename Between>
 __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bool first, const AttnTile& t,
                                            const QB& qb_operand, float scale_log2, Between between) {
   constexpr int kRows = AttnCfg<W>::kRows, kPPitch = AttnCfg<W>::kPPitch, kSlices = AttnCfg<W>::kSlices;
@@ -221,7 +233,8 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bo
   } else {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      u32x4 x = bf16x8_to_f16x8(t.raw[k]);
+      u32x4 x = kWin8 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
+                      : bf16x8_to_f16x8(t.raw[k]);
       if (!t.ok) x = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
       s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
@@ -314,11 +327,11 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bo
 // one split the workgroup covers the whole query and writes the normalised
 // output; otherwise it writes its unnormalised O and (max, sum) per head
 // for the combine kernel.
-template <int W>
+template <int W, bool kWin8>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t cap, int32_t q_per_seq,
-    const int32_t* __restrict__ idx, int32_t k_idx, const uint16_t* __restrict__ swa,
+    const int32_t* __restrict__ idx, int32_t k_idx, const uint8_t* __restrict__ swa,
     int64_t swa_q_stride_rows, const int32_t* __restrict__ swa_len, int32_t swa_max,
     float scale_log2, int32_t per_split, float* __restrict__ part_o, float2* __restrict__ part_ml,
     int32_t n_split, float* __restrict__ out) {
@@ -374,7 +387,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
 
   AttnTile cur;
   tile_begin<W>(cur, a, c_begin, wave, n);
-  tile_load(cur, a, n, g);
+  tile_load<kWin8>(cur, a, n, g);
   if (Cfg::kQLds) {
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
@@ -399,8 +412,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     if (Cfg::kPrefetch) {
       AttnTile nxt;
       if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);  // index loads of the next chunk
-      attn_chunk<W>(sm, st, ch == c_begin, cur, qb_operand, scale_log2, [&]() {
-        if (has_next) tile_load(nxt, a, n, g);  // its row loads overlap this chunk's PV
+      attn_chunk<W, kWin8>(sm, st, ch == c_begin, cur, qb_operand, scale_log2, [&]() {
+        if (has_next) tile_load<kWin8>(nxt, a, n, g);  // its row loads overlap this chunk's PV
       });
       if (has_next) cur = nxt;
     } else {
@@ -408,9 +421,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
       // one of its two dependent round trips overlaps this chunk's work.
       AttnTile nxt;
       if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);
-      attn_chunk<W>(sm, st, ch == c_begin, cur, qb_operand, scale_log2, []() {});
+      attn_chunk<W, kWin8>(sm, st, ch == c_begin, cur, qb_operand, scale_log2, []() {});
       if (has_next) {
-        tile_load(nxt, a, n, g);
+        tile_load<kWin8>(nxt, a, n, g);
         cur = nxt;
       }
     }
@@ -525,10 +538,26 @@ size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
   return o_bytes + ml_bytes;
 }
 
+template <bool kWin8>
+static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, const csa2_fp4_kv& kv,
+                          int32_t q_per_seq, const int32_t* idx, int32_t k_idx, const uint8_t* swa,
+                          int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
+                          float* part_o, float2* part_ml, float* out, hipStream_t stream) {
+  if (p.waves == 8)
+    hipLaunchKernelGGL((attn_kernel<8, kWin8>), dim3(p.splits, n_q), dim3(64 * 8), 0, stream, q, kv.codes,
+                       kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+                       scale_log2, p.per_split, part_o, part_ml, p.splits, out);
+  else
+    hipLaunchKernelGGL((attn_kernel<4, kWin8>), dim3(p.splits, n_q), dim3(64 * 4), 0, stream, q, kv.codes,
+                       kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+                       scale_log2, p.per_split, part_o, part_ml, p.splits, out);
+}
+
+// swa_fp8: window rows are E4M3 bytes [*][512] instead of bf16 [*][512].
 csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
-                        const int32_t* idx, int32_t k_idx, const uint16_t* swa, int64_t swa_q_stride_rows,
-                        const int32_t* swa_len, int32_t swa_max, float sm_scale, float* out, void* ws,
-                        hipStream_t stream) {
+                        const int32_t* idx, int32_t k_idx, const void* swa, bool swa_fp8,
+                        int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float sm_scale,
+                        float* out, void* ws, hipStream_t stream) {
   if (n_q == 0) return CSA2_OK;
   const AttnPlan p = attn_plan(n_q, k_idx, swa_max);
   float* part_o = nullptr;
@@ -540,14 +569,13 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
     part_ml = reinterpret_cast<float2*>(base);
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  if (p.waves == 8)
-    hipLaunchKernelGGL(attn_kernel<8>, dim3(p.splits, n_q), dim3(64 * 8), 0, stream, q, kv.codes, kv.scales,
-                       kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, scale_log2,
-                       p.per_split, part_o, part_ml, p.splits, out);
+  const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
+  if (swa_fp8)
+    attn_dispatch<true>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max, scale_log2,
+                        part_o, part_ml, out, stream);
   else
-    hipLaunchKernelGGL(attn_kernel<4>, dim3(p.splits, n_q), dim3(64 * 4), 0, stream, q, kv.codes, kv.scales,
-                       kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, scale_log2,
-                       p.per_split, part_o, part_ml, p.splits, out);
+    attn_dispatch<false>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                         scale_log2, part_o, part_ml, out, stream);
   if (p.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, p.splits, out);
   return launch_status("csa2_sparse_attn");

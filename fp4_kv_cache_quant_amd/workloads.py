@@ -16,7 +16,7 @@ import torch
 import synth
 from synth.configs import DecodeConfig, PrefillConfig
 
-from . import FP4KV, LATENT, Layer, Prefill, Sched, quant_rows
+from . import FP4KV, LATENT, Layer, Prefill, Sched, quant_fp8_rows, quant_rows
 
 
 def _fill(shape, tid_kind, seed=0):
@@ -81,6 +81,13 @@ def build_decode_inputs(cfg: DecodeConfig, steps: int) -> DecodeInputs:
     idx_k = _fill((n, cap, 64), cfg.idx_k(), seed=seed)
     blk_k = _fill((n, cfg.blk_cap(steps), 64), cfg.blk_k(), seed=seed) if cfg.hierarchical else None
     swa = [_fill((n, cfg.swa, LATENT), cfg.swa_rows(l), seed=seed) for l in range(nl)]
+    if cfg.swa_fp8:  # the window rows as E4M3 codes
+        swa8 = []
+        for t in swa:
+            t8 = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
+            quant_fp8_rows(t, t8)
+            swa8.append(t8)
+        swa = swa8
     inp = DecodeInputs(cfg=cfg, steps=steps, kv=kv,
                        lens=torch.full((n,), cfg.L0, dtype=torch.int32, device="cuda"),
                        idx_k=idx_k, blk_k=blk_k, swa=swa,
@@ -100,7 +107,7 @@ def make_sched(inp: DecodeInputs) -> Sched:
     layers = [Layer(m, k, bool(h)) for m, k, h in cfg.layers]
     return Sched(layers, n_seq=cfg.n_seq, key_cap=inp.cap,
                  blk_cap=cfg.blk_cap(inp.steps) if cfg.hierarchical else 0, topk=cfg.topk,
-                 pool_blocks=cfg.pool_blocks, blk=cfg.blk, swa_max=cfg.swa)
+                 pool_blocks=cfg.pool_blocks, blk=cfg.blk, swa_max=cfg.swa, swa_fp8=cfg.swa_fp8)
 
 
 def step_ios(sched: Sched, inp: DecodeInputs):

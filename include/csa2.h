@@ -71,7 +71,8 @@ typedef int32_t csa2_status;
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* csa2_last_error(void);
-/* Version of this ABI (bumped on any signature change). */
+/* Version of this ABI (bumped on any signature or struct change; 2 added
+ * the FP8 window). */
 int32_t csa2_abi_version(void);
 
 /* ------------------------------------------------------------ FP4 cache
@@ -175,6 +176,20 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                              float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* FP8 window rows ([P4] summary: the sliding-window KV is kept in FP8).
+ * READING: OCP E4M3FN elements, one byte per channel, no scale; a bf16 value
+ * becomes its round-to-nearest-even E4M3 code (ties to the even code),
+ * saturating at +-448, with the sign copied (also for zero) and NaN kept.
+ * csa2_quant_fp8_rows converts src [n_rows][512] bf16 into dst [n_rows][512]
+ * E4M3 (exact decisions); csa2_sparse_attn_f8w is csa2_sparse_attn with the
+ * window rows swa [*][512] given as those E4M3 bytes (dequantised exactly).
+ * src 16-byte, dst 8-byte aligned. */
+csa2_status csa2_quant_fp8_rows(const uint16_t* src, int64_t n_rows, uint8_t* dst, void* stream);
+csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                                 const int32_t* idx, int32_t k_idx, const uint8_t* swa,
+                                 int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                                 float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ scheduler
  * Static layer-mode table [P1 "Compressed Sparse Attention 2 (CSA2)"]:
  *   Full    computes its own selection: a fresh Top-k over all positions,
@@ -207,6 +222,7 @@ typedef struct {
   int32_t blk;              /* positions per block (8) */
   int32_t swa_max;          /* rows per sequence of each SWA buffer (128) */
   float sm_scale;           /* softmax scale (READING: 1/sqrt(512)) */
+  int32_t swa_fp8;          /* 1: window rows are E4M3 bytes (see csa2_quant_fp8_rows) */
 } csa2_sched_desc;
 
 /* Per-step inputs/outputs.  Arrays marked "host" hold device pointers. */
@@ -221,7 +237,8 @@ typedef struct {
   const uint16_t* const* idx_q; /* host [n_layers]: [n_seq][8][64] (Reuse: ignored) */
   const float* const* idx_w;    /* host [n_layers] of [n_seq][8] f32 or NULL; NULL array = all 1 */
   const uint16_t* const* main_q; /* host [n_layers]: [n_seq][16][512] bf16 */
-  const uint16_t* const* swa;   /* host [n_layers]: [n_seq][swa_max][512] bf16 */
+  const void* const* swa;       /* host [n_layers]: [n_seq][swa_max][512] bf16, or E4M3
+                                   bytes when desc.swa_fp8 */
   const int32_t* swa_len;       /* [n_seq] valid SWA rows (<= swa_max) */
   float* const* out;            /* host [n_layers]: [n_seq][16][512] f32 */
 } csa2_step_io;

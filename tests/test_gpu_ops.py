@@ -354,3 +354,37 @@ def test_sparse_attn_many_queries_one_cache(csa2, n_q):
     for b in sorted({0, 1, 5, n_q // 2, n_q - 1, *rng.integers(0, n_q, 6).tolist()}):
         ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa_rows[b:b + swa_max], swa_len[b], SM_SCALE)
         assert_attention_close(got[b], ref, f"query {b}")
+
+
+# ------------------------------------------------------------- FP8 window
+def test_quant_fp8_rows_all_bf16_patterns(csa2):
+    """Every bf16 bit pattern (128 rows of 512) -> E4M3 codes, bit-exact with
+    the oracle (ties to even, saturation, signed zeros, NaN)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(128, 512)
+    print_case("quant_fp8_rows all bf16")
+    dst = torch.empty(128, 512, dtype=torch.uint8, device="cuda")
+    csa2.quant_fp8_rows(dev(bits), dst)
+    assert np.array_equal(dst.cpu().numpy(), oracle.fp8_rows(bits))
+
+
+@pytest.mark.parametrize("k_idx,swa_lens", [(512, [128, 77, 0]), (0, [128, 5, 1]), (300, [64, 128, 128])])
+def test_sparse_attn_fp8_window_matches_oracle(csa2, k_idx, swa_lens):
+    n_q, cap = 3, 2500
+    src = kv_source(4, n_q, cap)
+    kv = _device_cache(csa2, src)
+    rng = np.random.default_rng(k_idx + 7 * sum(swa_lens))
+    idx = np.stack([np.sort(rng.choice(cap, k_idx, replace=False)) for _ in range(n_q)]).astype(np.int32) \
+        if k_idx else np.zeros((n_q, 0), np.int32)
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 4), synth.NORMAL, range(n_q), np.arange(16), 512)
+    swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 4), synth.NORMAL, range(n_q), np.arange(128), 512)
+    swa8 = np.stack([oracle.fp8_rows(swa[b]) for b in range(n_q)])
+    swa_len = np.array(swa_lens, np.int32)
+    print_case(f"sparse_attn fp8 window k_idx={k_idx} swa={swa_lens}")
+    out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+    csa2.sparse_attn(dev(q), kv, dev(idx) if k_idx else None, torch.from_numpy(swa8).cuda(), dev(swa_len),
+                     SM_SCALE, out)
+    got = out.cpu().numpy()
+    for b in range(n_q):
+        codes, scales = oracle.quant_rows(src[b])
+        ref = oracle.sparse_attn_fp8w(q[b], codes, scales, idx[b], swa8[b], swa_len[b], SM_SCALE)
+        assert_attention_close(got[b], ref, f"query {b}")

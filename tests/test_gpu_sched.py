@@ -30,6 +30,8 @@ CASES = {
     "decoder20_short_ctx": (C.DECODER_20L_1M.with_(n_seq=2, L0=300, q_sets=2, pool_blocks=16), 2),
     # more than 32K blocks: the multi-workgroup filter pass of the block Top-k
     "hier_long": (C.HIER_1M.with_(n_seq=2, L0=8 * 40000 + 3), 1),
+    # window rows stored as E4M3 (FP8)
+    "decoder20_fp8_window": (C.DECODER_20L_1M.with_(n_seq=2, L0=8 * 2500 + 3, q_sets=2, swa_fp8=True), 2),
 }
 
 
@@ -87,6 +89,7 @@ FULL_SIZE = {
     "group_64k_b32": (C.GROUP_64K, 2, [0, 31]),
     "hier_1m_b8": (C.HIER_1M, 1, [0, 7]),
     "decoder20_1m_b16": (C.DECODER_20L_1M, 3, [0, 9, 15]),
+    "decoder20_1m_b16_fp8_window": (C.DECODER_20L_1M_FP8_WINDOW, 2, [0, 15]),
 }
 
 
