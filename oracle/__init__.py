@@ -58,6 +58,7 @@ PINS = {
     "decode_step": "Reuse reproduces the latest Full/Reindex indices; Reindex with Full's Q == Full",
     "orc_fp8_code": "all 65,536 bf16 patterns vs torch's float8_e4m3fn cast in range, saturation and NaN beyond; golden ties",
     "orc_sparse_attn_fp8w": "equals orc_sparse_attn on window rows that FP8 represents exactly (bf16 of E4M3 values)",
+    "orc_block_key": "numpy int64 sums of integer keys per block, partial last block; one-hot closed forms",
 }
 
 
@@ -113,6 +114,8 @@ def lib() -> ctypes.CDLL:
         L.orc_fp8_rows.restype = None
         L.orc_sparse_attn_fp8w.argtypes = [P, P, P, P, i64, P, i64, ctypes.c_double, P]
         L.orc_sparse_attn_fp8w.restype = None
+        L.orc_block_key.argtypes = [P, i64, i64, i64, P]
+        L.orc_block_key.restype = None
         _lib = L
     return _lib
 
@@ -228,6 +231,17 @@ def sparse_attn_gathered(q, rows_codes, rows_scales, idx, swa, swa_len, sm_scale
     if swa8 is not None:
         return sparse_attn_fp8w(q, rows_codes, rows_scales, local, swa8, swa_len, sm_scale)
     return sparse_attn(q, rows_codes, rows_scales, local, swa, swa_len, sm_scale)
+
+
+# ------------------------------------------------- block-key maintenance
+def block_keys(tok_keys: np.ndarray, L: int, blk: int = BLK) -> np.ndarray:
+    """Block keys [ceil(L/blk)][64] (bf16 bits) of the first L positions."""
+    tok = _u16(tok_keys).reshape(-1, IDX_DIM)
+    nb = -(-L // blk)
+    out = np.zeros((nb, IDX_DIM), np.uint16)
+    for b in range(nb):
+        lib().orc_block_key(_p(tok), L, blk, b, _p(out[b]))
+    return out
 
 
 # ------------------------------------------------------------ FP8 window

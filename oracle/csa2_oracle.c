@@ -378,3 +378,23 @@ void orc_sparse_attn_fp8w(const uint16_t* q, const uint8_t* codes, const uint8_t
   attn_over_rows(q, x, n, sm_scale, out);
   free(x);
 }
+
+/* ------------------------------------------------- block-key maintenance */
+
+/* Key of block b (positions blk*b .. blk*b + blk-1) over the first L
+ * positions of indexer K tok_keys [*][64].  The pages say the hierarchical
+ * pool needs a key per block of 8 but not how it is formed ([P1 "Compressed
+ * Sparse Attention 2 (CSA2)"]).  READING: the sum of the indexer keys of the
+ * block's positions that exist (< L), rounded once to bf16 (RNE); for
+ * integer-valued keys with |sum| <= 256 the sum is exact. */
+void orc_block_key(const uint16_t* tok_keys, int64_t L, int64_t blk, int64_t b, uint16_t* out) {
+  for (int d = 0; d < IDX_DIM; ++d) {
+    double acc = 0.0;
+    for (int64_t i = blk * b; i < blk * (b + 1) && i < L; ++i) acc += orc_bf16_value(tok_keys[i * IDX_DIM + d]);
+    float f = (float)acc;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16; /* RNE to bf16 (finite) */
+    out[d] = (uint16_t)u;
+  }
+}

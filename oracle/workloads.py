@@ -12,7 +12,7 @@ import numpy as np
 import synth
 from synth.configs import REUSE, DecodeConfig, PrefillConfig
 
-from . import (Layer, LayerInputs, SeqState, decode_layers, fp8_rows, prefill_query,
+from . import (Layer, LayerInputs, SeqState, block_keys, decode_layers, fp8_rows, prefill_query,
                prefill_visible_entries, prefill_window, quant_rows)
 
 SM_SCALE = 512 ** -0.5
@@ -36,10 +36,23 @@ def kv_source_rows(cfg: DecodeConfig, kv_id: int, b: int, ids: np.ndarray) -> np
     return out
 
 
+def index_key_rows(cfg: DecodeConfig, b: int, L: int) -> np.ndarray:
+    """Indexer K of positions 0..L-1 of sequence b: the pre-filled rows, and
+    with maintained keys the appended positions' own keys."""
+    if not (cfg.maintain_keys and cfg.append) or L <= cfg.L0:
+        return _gen(cfg, cfg.idx_k(), b, np.arange(L), 64)
+    tok = _gen(cfg, cfg.idx_k(), b, np.arange(cfg.L0), 64)
+    new = [_gen(cfg, cfg.new_idx_k(p - cfg.L0), b, [0], 64) for p in range(cfg.L0, L)]
+    return np.concatenate([tok] + new)
+
+
 def seq_state(cfg: DecodeConfig, b: int, step: int) -> SeqState:
     L = cfg.lens_at(step)
-    tok = _gen(cfg, cfg.idx_k(), b, np.arange(L), 64)
-    blk = _gen(cfg, cfg.blk_k(), b, np.arange(-(-L // cfg.blk)), 64) if cfg.hierarchical else None
+    tok = index_key_rows(cfg, b, L)
+    blk = None
+    if cfg.hierarchical:
+        blk = (block_keys(tok, L, cfg.blk) if cfg.maintain_keys
+               else _gen(cfg, cfg.blk_k(), b, np.arange(-(-L // cfg.blk)), 64))
 
     def kv_rows(kv_id, ids):
         ids = np.asarray(ids, dtype=np.int64)

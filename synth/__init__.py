@@ -54,6 +54,7 @@ KIND_MAIN_Q = 5      # main Q; a = layer, b = step
 KIND_SWA = 6         # SWA rows; a = layer, b = step (0 = initial window)
 KIND_NEW_ROW = 7     # appended latent row; a = kv tensor id, b = step
 KIND_IDX_W = 8       # optional indexer head weights; a = layer, b = step
+KIND_NEW_IDX_K = 9   # indexer key of an appended position; b = step
 
 
 def tensor_id(kind: int, a: int = 0, b: int = 0) -> int:

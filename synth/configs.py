@@ -10,7 +10,7 @@ from dataclasses import dataclass, replace
 from typing import Tuple
 
 from . import (INT9, NORMAL, KIND_BLK_K, KIND_IDX_K, KIND_IDX_Q, KIND_KV_SRC, KIND_MAIN_Q,
-               KIND_NEW_ROW, KIND_SWA, tensor_id)
+               KIND_NEW_IDX_K, KIND_NEW_ROW, KIND_SWA, tensor_id)
 
 FULL, REINDEX, REUSE = 0, 1, 2
 
@@ -31,6 +31,7 @@ class DecodeConfig:
     q_sets: int = 4                           # step s uses query set s % q_sets
     seed: int = 0
     swa_fp8: bool = False                     # window rows stored as E4M3 (FP8) codes
+    maintain_keys: bool = False               # block keys = sums of indexer keys, kept current on append
 
     def cap(self, steps: int) -> int:
         """Rows per sequence of every main-KV tensor and of indexer K."""
@@ -59,6 +60,9 @@ class DecodeConfig:
 
     def idx_k(self):
         return tensor_id(KIND_IDX_K), INT9
+
+    def new_idx_k(self, step: int):
+        return tensor_id(KIND_NEW_IDX_K, 0, step % self.q_sets), INT9
 
     def blk_k(self):
         return tensor_id(KIND_BLK_K), INT9
@@ -97,12 +101,19 @@ DECODER_20L_1M = DecodeConfig(
     layers=_group(FULL, 0, 1, 3) + sum((_group(REINDEX, g, 0, 3) for g in range(1, 5)), ()),
     n_kv=5, append=True)
 
+# The same schedule with the block keys maintained on append (sums of the
+# blocks' indexer keys; appended positions bring their own indexer key).
+DECODER_20L_1M_KEYS = DECODER_20L_1M.with_(
+    name="20-layer decoder schedule, 1M positions, batch 16, block keys maintained on append",
+    maintain_keys=True)
+
 # The same schedule with FP8 window rows.
 DECODER_20L_1M_FP8_WINDOW = DECODER_20L_1M.with_(
     name="20-layer decoder schedule, 1M positions, batch 16, FP8 window rows", swa_fp8=True)
 
 DECODE_CONFIGS = {"single_4k": SINGLE_LAYER_4K, "group_64k": GROUP_64K, "hier_1m": HIER_1M,
-                  "decoder20_1m": DECODER_20L_1M, "decoder20_1m_fp8win": DECODER_20L_1M_FP8_WINDOW}
+                  "decoder20_1m": DECODER_20L_1M, "decoder20_1m_fp8win": DECODER_20L_1M_FP8_WINDOW,
+                  "decoder20_1m_keys": DECODER_20L_1M_KEYS}
 
 
 @dataclass(frozen=True)

@@ -444,3 +444,29 @@ def test_fp8_window_attention_equals_bf16_window_on_exact_rows():
     a = oracle.sparse_attn(q, codes, scales, idx, rows_bf16, 37, 512 ** -0.5)
     b = oracle.sparse_attn_fp8w(q, codes, scales, idx, codes8, 37, 512 ** -0.5)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------- block-key maintenance
+@pytest.mark.parametrize("L", [1, 8, 9, 63, 64, 200])
+def test_block_keys_are_sums_of_integer_keys(L):
+    """Integer-valued keys: each block key is the exact int64 sum of its
+    positions' keys (numpy), the partial last block summing only positions
+    < L; a block never includes a position of its neighbours."""
+    keys = synth.gen_rows(0, 4242, synth.INT9, [0], np.arange(208), 64)[0]
+    ints = synth.bf16_to_f32(keys).astype(np.int64)
+    got = synth.bf16_to_f32(oracle.block_keys(keys, L, 8)).astype(np.int64)
+    nb = -(-L // 8)
+    want = np.stack([ints[8 * b:min(8 * b + 8, L)].sum(axis=0) for b in range(nb)])
+    assert np.array_equal(got, want)
+
+
+def test_block_key_one_hot():
+    keys = np.zeros((16, 64), np.float32)
+    keys[9, 5] = 3.0       # block 1, dimension 5
+    keys[15, 5] = -1.0     # block 1, dimension 5
+    keys[7, 0] = 2.0       # block 0, dimension 0
+    bk = synth.bf16_to_f32(oracle.block_keys(f32_to_bf16(keys), 16, 8))
+    expect = np.zeros((2, 64), np.float32)
+    expect[1, 5] = 2.0
+    expect[0, 0] = 2.0
+    assert np.array_equal(bk, expect)
