@@ -13,12 +13,13 @@ roofline of the dominant op (timed with HIP events), the CPU oracle on a
 bounded sample of the same workload, a parity check of one step against
 that oracle sample, and (key "prefill") the ratio-2 causal prefill chunk of
 the encoder group: time per 4,096-query chunk, MFMA rate of its scoring and
-attention kernels, sampled parity and the oracle's rate; and (key
-"fp8_window") the same decode step with the window rows stored as E4M3.
+attention kernels, sampled parity and the oracle's rate; and (keys
+"fp8_window", "maintained_keys") the same decode step with the window rows
+stored as E4M3, and with the block keys maintained on append.
 
 usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-graph]
                        [--cpu-seqs 16] [--no-cpu] [--no-prefill] [--prefill-reps 5]
-                       [--no-fp8-window] [--config NAME]
+                       [--no-fp8-window] [--no-keys] [--config NAME]
 """
 from __future__ import annotations
 
@@ -321,10 +322,59 @@ def prefill_bench(args) -> dict:
     }
 
 
+def _time_steps(c, inp, K: int, W: int, graph: bool) -> dict:
+    """Time K steps (after W warm-up steps) of workload c on the inputs inp,
+    with a scheduler of its own; lengths are reset first so that the appends
+    rewrite the same rows."""
+    import torch
+
+    from fp4_kv_cache_quant_amd import workloads as wl
+
+    inp.reset_lens()
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    stream = torch.cuda.current_stream()
+    sched.decode_step(ios[0])
+    graphs = []
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for s_ in range(c.q_sets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    sched.decode_step(ios[s_])
+                graphs.append(g)
+        stream.wait_stream(side)
+
+    def run_step(s_):
+        if graphs:
+            graphs[s_ % c.q_sets].replay()
+        else:
+            sched.decode_step(ios[s_ % c.q_sets])
+
+    for s_ in range(1, 1 + W):
+        run_step(s_)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s_ in range(1 + W, 1 + W + K):
+        run_step(s_)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    flag = sched.check()
+    sched.close()
+    ab = algorithmic_bytes(c, c.lens_at(1 + W + K // 2))
+    return {"workload": c.name, "ms_per_step": round(ms, 4),
+            "value": round(c.n_seq * len(c.layers) / (ms * 1e-3), 1), "unit": "(seq·layer)-steps/s",
+            "algorithmic_bytes_per_step": ab["total"], "GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
+            "device_flags": int(flag)}
+
+
 def fp8_window_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
     """The same step with the window rows stored as E4M3 (FP8): the window
-    tensors are quantised from the bf16 ones, every other input is shared;
-    lengths are reset so the appends rewrite the same rows."""
+    tensors are quantised from the bf16 ones, every other input is shared."""
     import torch
 
     import fp4_kv_cache_quant_amd as csa2
@@ -339,46 +389,25 @@ def fp8_window_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
     inp8 = wl.DecodeInputs(cfg=c8, steps=inp.steps, kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, blk_k=inp.blk_k,
                            swa=swa8, swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q, main_q=inp.main_q,
                            new_row=inp.new_row)
-    inp8.reset_lens()
-    sched = wl.make_sched(inp8)
-    ios = wl.step_ios(sched, inp8)
-    stream = torch.cuda.current_stream()
-    sched.decode_step(ios[0])
-    graphs = []
-    if graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for s_ in range(c8.q_sets):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    sched.decode_step(ios[s_])
-                graphs.append(g)
-        stream.wait_stream(side)
+    return _time_steps(c8, inp8, K, W, graph)
 
-    def run_step(s_):
-        if graphs:
-            graphs[s_ % c8.q_sets].replay()
-        else:
-            sched.decode_step(ios[s_ % c8.q_sets])
 
-    for s_ in range(1, 1 + W):
-        run_step(s_)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for s_ in range(1 + W, 1 + W + K):
-        run_step(s_)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / K
-    flag = sched.check()
-    sched.close()
-    ab = algorithmic_bytes(c8, c8.lens_at(1 + W + K // 2))
-    return {"workload": c8.name, "ms_per_step": round(ms, 4),
-            "value": round(c8.n_seq * len(c8.layers) / (ms * 1e-3), 1), "unit": "(seq·layer)-steps/s",
-            "algorithmic_bytes_per_step": ab["total"], "GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
-            "append_overflow": bool(flag)}
+def maintained_keys_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
+    """The same step with block keys maintained on append: the block keys
+    are re-formed as sums of the prefilled indexer keys, and every step
+    appends its position's indexer key and updates its block's key.
+    Overwrites the block keys and appended indexer-key rows of inp."""
+    import fp4_kv_cache_quant_amd as csa2
+    from fp4_kv_cache_quant_amd import workloads as wl
+
+    ck = cfg.with_(maintain_keys=True, name=cfg.name + ", block keys maintained on append")
+    inp.reset_lens()
+    csa2.block_keys(inp.idx_k, inp.lens, inp.blk_k, ck.blk)
+    new_k = [wl.fill_tensor((ck.n_seq, 1, 64), ck.new_idx_k(s_), seed=ck.seed) for s_ in range(ck.q_sets)]
+    inpk = wl.DecodeInputs(cfg=ck, steps=inp.steps, kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, blk_k=inp.blk_k,
+                           swa=inp.swa, swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q, main_q=inp.main_q,
+                           new_row=inp.new_row, new_idx_k=new_k)
+    return _time_steps(ck, inpk, K, W, graph)
 
 
 def compare_step(cfg, gpu, ref) -> dict:
@@ -414,6 +443,7 @@ def main() -> int:
     ap.add_argument("--config", default="decoder20_1m")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--no-fp8-window", action="store_true", help="skip the FP8-window variant of the step")
+    ap.add_argument("--no-keys", action="store_true", help="skip the maintained-block-keys variant of the step")
     ap.add_argument("--prefill-reps", type=int, default=5, help="timed prefill chunks")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for scaling profiler traffic counters)")
@@ -515,9 +545,11 @@ def main() -> int:
                          f"(hierarchical select, 4 Reindex rescorings, {nl} attentions), {dt:.1f} s"}
         parity = compare_step(cfg, gpu0, res)
 
-    fp8w = None
+    fp8w = keys = None
     if not args.no_fp8_window and not cfg.swa_fp8:
         fp8w = fp8_window_leg(cfg, inp, K, W, graph=not args.no_graph)
+    if not args.no_keys and cfg.hierarchical and cfg.append and not cfg.maintain_keys:
+        keys = maintained_keys_leg(cfg, inp, K, W, graph=not args.no_graph)
 
     prefill = None
     if not args.no_prefill:
@@ -534,7 +566,7 @@ def main() -> int:
         "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": round(hbm_gbps, 1),
                 "frac_of_peak": round(hbm_gbps / PEAK_HBM_GBPS, 4), "parts": ab},
         "roofline": roofline, "dominant_op": dom, "ops": ops, "cpu_baseline": cpu, "parity_step0": parity,
-        "fp8_window": fp8w, "prefill": prefill,
+        "fp8_window": fp8w, "maintained_keys": keys, "prefill": prefill,
         "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
     }
     print(json.dumps(line), flush=True)

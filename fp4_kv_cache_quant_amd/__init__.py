@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
     "sparse_attn", "sparse_attn_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
-    "prefill_index_score", "Prefill", "quant_fp8_rows",
+    "prefill_index_score", "Prefill", "quant_fp8_rows", "block_keys", "append_index_keys",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
 
@@ -51,7 +51,7 @@ class _SchedDesc(ctypes.Structure):
 class _StepIO(ctypes.Structure):
     _fields_ = [("n_kv", _I32), ("kv", _P), ("lens", _P), ("new_row", _P), ("append_kv", _I32),
                 ("idx_k", _P), ("blk_k", _P), ("idx_q", _P), ("idx_w", _P), ("main_q", _P),
-                ("swa", _P), ("swa_len", _P), ("out", _P)]
+                ("swa", _P), ("swa_len", _P), ("out", _P), ("new_idx_k", _P)]
 
 
 class _PrefillDesc(ctypes.Structure):
@@ -82,6 +82,8 @@ _attn_ws = _sig("csa2_sparse_attn_workspace_size", _SZ, _I32, _I32, _I32)
 _attn_f8w = _sig("csa2_sparse_attn_f8w", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
                  _I32, _F32, _P, _P, _SZ, _P)
 _quant_fp8 = _sig("csa2_quant_fp8_rows", _I32, _P, _I64, _P, _P)
+_block_keys = _sig("csa2_block_keys", _I32, _P, _I64, _P, _I32, _P, _I64, _I32, _P)
+_append_keys = _sig("csa2_append_index_keys", _I32, _P, _P, _I64, _P, _I64, _I32, _P, _P, _I32, _P)
 _attn = _sig("csa2_sparse_attn", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
              _I32, _F32, _P, _P, _SZ, _P)
 _sched_create = _sig("csa2_sched_create", _I32, ctypes.POINTER(_SchedDesc), ctypes.POINTER(_P))
@@ -159,6 +161,21 @@ def quant_fp8_rows(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     n = src.numel() // LATENT
     assert dst.dtype == torch.uint8 and dst.numel() >= n * LATENT
     _check(_quant_fp8(_ptr(src), n, _ptr(dst), _stream(stream)))
+
+
+def block_keys(idx_k: torch.Tensor, lens: torch.Tensor, blk_k: torch.Tensor, blk: int = 8, stream=None) -> None:
+    """idx_k [n_seq][key_cap][64] -> blk_k [n_seq][blk_cap][64]: sums of the blocks' keys (bf16)."""
+    n_seq, key_cap = idx_k.shape[0], idx_k.shape[1]
+    _check(_block_keys(_ptr(idx_k), key_cap, _ptr(lens), blk, _ptr(blk_k), blk_k.shape[1], n_seq, _stream(stream)))
+
+
+def append_index_keys(new_k: torch.Tensor, idx_k: torch.Tensor, lens: torch.Tensor,
+                      blk_k: Optional[torch.Tensor] = None, blk: int = 8, err_flag: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Write new_k [n_seq][64] at row lens[b] of idx_k and add it to its block's key."""
+    n_seq, key_cap = idx_k.shape[0], idx_k.shape[1]
+    _check(_append_keys(_ptr(new_k), _ptr(idx_k), key_cap, _ptr(blk_k), blk_k.shape[1] if blk_k is not None else 0,
+                        blk, _ptr(lens), _ptr(err_flag), n_seq, _stream(stream)))
 
 
 def quant_append(src: torch.Tensor, kv: FP4KV, lens: torch.Tensor, err_flag: Optional[torch.Tensor] = None,
@@ -248,7 +265,7 @@ class Sched:
         self.close()
 
     def prepare(self, kv: Sequence[FP4KV], lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k=None,
-                new_row=None, append_kv: int = 0, idx_w=None) -> "_StepIO":
+                new_row=None, append_kv: int = 0, idx_w=None, new_idx_k=None) -> "_StepIO":
         """Build (and keep alive) the step descriptor for a fixed set of tensors."""
         nl = len(self.layers)
         kvs = (_FP4KV * len(kv))(*[k.c() for k in kv])
@@ -258,9 +275,10 @@ class Sched:
         mq, sw, ou = P(*[_ptr(t) for t in main_q]), P(*[_ptr(t) for t in swa]), P(*[_ptr(t) for t in out])
         io = _StepIO(len(kv), ctypes.cast(kvs, _P), _ptr(lens), _ptr(new_row), append_kv, _ptr(idx_k),
                      _ptr(blk_k), ctypes.cast(iq, _P), ctypes.cast(iw, _P) if iw is not None else None,
-                     ctypes.cast(mq, _P), ctypes.cast(sw, _P), _ptr(swa_len), ctypes.cast(ou, _P))
+                     ctypes.cast(mq, _P), ctypes.cast(sw, _P), _ptr(swa_len), ctypes.cast(ou, _P),
+                     _ptr(new_idx_k))
         io._keep = (kvs, iq, iw, mq, sw, ou, kv, lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k,
-                    new_row, idx_w)
+                    new_row, idx_w, new_idx_k)
         return io
 
     def decode_step(self, io: "_StepIO", stream=None) -> None:

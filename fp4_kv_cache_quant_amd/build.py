@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["quant.hip", "index_score.hip", "topk.hip", "sparse_attn.hip", "capi.cpp", "sched.cpp", "prefill.cpp"]
+SOURCES = ["quant.hip", "keys.hip", "index_score.hip", "topk.hip", "sparse_attn.hip", "capi.cpp", "sched.cpp",
+           "prefill.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are switched off (the compiler would form them from

@@ -13,6 +13,10 @@ namespace csa2 {
 csa2_status quant_rows_launch(const uint16_t*, int64_t, uint8_t*, uint8_t*, hipStream_t);
 csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, int32_t*, hipStream_t);
 csa2_status quant_fp8_launch(const uint16_t*, int64_t, uint8_t*, hipStream_t);
+csa2_status block_keys_launch(const uint16_t*, int64_t, const int32_t*, int32_t, uint16_t*, int64_t, int32_t,
+                              hipStream_t);
+csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, int64_t, int32_t, const int32_t*,
+                               int32_t*, int32_t, hipStream_t);
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
                                uint32_t*, hipStream_t);
@@ -117,7 +121,7 @@ extern "C" {
 
 const char* csa2_last_error(void) { return g_error.c_str(); }
 
-int32_t csa2_abi_version(void) { return 2; }
+int32_t csa2_abi_version(void) { return 3; }
 
 csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                             void* stream) {
@@ -193,6 +197,29 @@ csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_
   if (st != CSA2_OK || n_q == 0) return st;
   return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, true, swa_q_stride_rows, swa_len, swa_max,
                      sm_scale, out, ws, as_stream(stream));
+}
+
+csa2_status csa2_block_keys(const uint16_t* idx_k, int64_t key_cap, const int32_t* lens, int32_t blk,
+                            uint16_t* blk_k, int64_t blk_cap, int32_t n_seq, void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_seq >= 0 && n_seq <= 65535, CSA2_ESHAPE, "csa2_block_keys: n_seq must be in [0, 65535]");
+  if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(idx_k && lens && blk_k, CSA2_EINVAL, "csa2_block_keys: null pointer");
+  CSA2_REQUIRE(key_cap >= 1 && blk >= 1 && blk_cap >= 1 && blk_cap * blk >= key_cap, CSA2_ESHAPE,
+               "csa2_block_keys: need blk >= 1 and blk_cap * blk >= key_cap");
+  return block_keys_launch(idx_k, key_cap, lens, blk, blk_k, blk_cap, n_seq, as_stream(stream));
+}
+
+csa2_status csa2_append_index_keys(const uint16_t* new_k, uint16_t* idx_k, int64_t key_cap, uint16_t* blk_k,
+                                   int64_t blk_cap, int32_t blk, const int32_t* lens, int32_t* err_flag,
+                                   int32_t n_seq, void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_seq >= 0 && n_seq <= 65535, CSA2_ESHAPE, "csa2_append_index_keys: n_seq must be in [0, 65535]");
+  if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(new_k && idx_k && lens, CSA2_EINVAL, "csa2_append_index_keys: null pointer");
+  CSA2_REQUIRE(key_cap >= 1 && (!blk_k || (blk >= 1 && blk_cap >= 1)), CSA2_ESHAPE,
+               "csa2_append_index_keys: bad key_cap / blk / blk_cap");
+  return append_keys_launch(new_k, idx_k, key_cap, blk_k, blk_cap, blk, lens, err_flag, n_seq, as_stream(stream));
 }
 
 csa2_status csa2_quant_fp8_rows(const uint16_t* src, int64_t n_rows, uint8_t* dst, void* stream) {

@@ -24,6 +24,8 @@ csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, i
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, int64_t, int32_t, const int32_t*,
+                               int32_t*, int32_t, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
 }  // namespace csa2
 
@@ -206,6 +208,13 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
                  "csa2_sched_decode_step: missing indexer Q for layer " + std::to_string(l));
     CSA2_REQUIRE(io->main_q[l] && io->swa[l] && io->out[l], CSA2_EINVAL,
                  "csa2_sched_decode_step: missing main Q / SWA / out for layer " + std::to_string(l));
+  }
+  if (io->new_idx_k) {
+    // The appended position's indexer key, and its block's key: before the
+    // latent append, which advances lens.
+    csa2_status st = append_keys_launch(io->new_idx_k, io->idx_k, d.key_cap, s->any_hier ? io->blk_k : nullptr,
+                                        d.blk_cap, d.blk, io->lens, s->err, d.n_seq, stream);
+    if (st != CSA2_OK) return st;
   }
   if (io->new_row) {
     CSA2_REQUIRE(io->append_kv >= 0 && io->append_kv < io->n_kv, CSA2_EINVAL,

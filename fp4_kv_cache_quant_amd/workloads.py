@@ -16,10 +16,10 @@ import torch
 import synth
 from synth.configs import DecodeConfig, PrefillConfig
 
-from . import FP4KV, LATENT, Layer, Prefill, Sched, quant_fp8_rows, quant_rows
+from . import FP4KV, LATENT, Layer, Prefill, Sched, block_keys, quant_fp8_rows, quant_rows
 
 
-def _fill(shape, tid_kind, seed=0):
+def fill_tensor(shape, tid_kind, seed=0):
     """A new bf16 tensor [n_seq][rows][dim] holding rows 0.. of each sequence."""
     tid, kind = tid_kind
     t = torch.empty(shape, dtype=torch.int16, device="cuda")
@@ -56,6 +56,7 @@ class DecodeInputs:
     idx_q: List[List[Optional[torch.Tensor]]] = field(default_factory=list)   # [set][layer]
     main_q: List[List[torch.Tensor]] = field(default_factory=list)            # [set][layer]
     new_row: List[Optional[torch.Tensor]] = field(default_factory=list)       # [set]
+    new_idx_k: List[Optional[torch.Tensor]] = field(default_factory=list)     # [set], maintained keys
 
     @property
     def cap(self):
@@ -78,9 +79,9 @@ def build_decode_inputs(cfg: DecodeConfig, steps: int) -> DecodeInputs:
             fill_kv_rows(t, b, 0, rows, cfg.kv_src(k), seed, staging=staging)
         kv.append(t)
     del staging
-    idx_k = _fill((n, cap, 64), cfg.idx_k(), seed=seed)
-    blk_k = _fill((n, cfg.blk_cap(steps), 64), cfg.blk_k(), seed=seed) if cfg.hierarchical else None
-    swa = [_fill((n, cfg.swa, LATENT), cfg.swa_rows(l), seed=seed) for l in range(nl)]
+    idx_k = fill_tensor((n, cap, 64), cfg.idx_k(), seed=seed)
+    blk_k = fill_tensor((n, cfg.blk_cap(steps), 64), cfg.blk_k(), seed=seed) if cfg.hierarchical else None
+    swa = [fill_tensor((n, cfg.swa, LATENT), cfg.swa_rows(l), seed=seed) for l in range(nl)]
     if cfg.swa_fp8:  # the window rows as E4M3 codes
         swa8 = []
         for t in swa:
@@ -94,10 +95,14 @@ def build_decode_inputs(cfg: DecodeConfig, steps: int) -> DecodeInputs:
                        swa_len=torch.full((n,), cfg.swa, dtype=torch.int32, device="cuda"),
                        out=[torch.empty(n, 16, LATENT, dtype=torch.float32, device="cuda") for _ in range(nl)])
     for s in range(cfg.q_sets):
-        inp.idx_q.append([_fill((n, 8, 64), cfg.idx_q(l, s), seed=seed) if cfg.layers[l][0] != 2 else None
+        inp.idx_q.append([fill_tensor((n, 8, 64), cfg.idx_q(l, s), seed=seed) if cfg.layers[l][0] != 2 else None
                           for l in range(nl)])
-        inp.main_q.append([_fill((n, 16, LATENT), cfg.main_q(l, s), seed=seed) for l in range(nl)])
-        inp.new_row.append(_fill((n, 1, LATENT), cfg.new_row(s), seed=seed) if cfg.append else None)
+        inp.main_q.append([fill_tensor((n, 16, LATENT), cfg.main_q(l, s), seed=seed) for l in range(nl)])
+        inp.new_row.append(fill_tensor((n, 1, LATENT), cfg.new_row(s), seed=seed) if cfg.append else None)
+        inp.new_idx_k.append(fill_tensor((n, 1, 64), cfg.new_idx_k(s), seed=seed)
+                             if (cfg.maintain_keys and cfg.append) else None)
+    if cfg.maintain_keys and blk_k is not None:  # keys of the prefilled blocks, from indexer K
+        block_keys(idx_k, inp.lens, blk_k, cfg.blk)
     torch.cuda.synchronize()
     return inp
 
@@ -114,7 +119,8 @@ def step_ios(sched: Sched, inp: DecodeInputs):
     """One prepared step descriptor per query set (step s uses ios[s % q_sets])."""
     return [sched.prepare(kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, main_q=inp.main_q[s], swa=inp.swa,
                           swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q[s], blk_k=inp.blk_k,
-                          new_row=inp.new_row[s], append_kv=inp.cfg.append_kv)
+                          new_row=inp.new_row[s], append_kv=inp.cfg.append_kv,
+                          new_idx_k=inp.new_idx_k[s] if inp.new_idx_k else None)
             for s in range(inp.cfg.q_sets)]
 
 
@@ -136,10 +142,10 @@ def build_prefill_inputs(cfg: PrefillConfig) -> PrefillInputs:
     seed, nq, nl = cfg.seed, cfg.n_q, len(cfg.layers)
     kv = FP4KV.empty(1, cfg.n_entries)
     fill_kv_rows(kv, 0, 0, cfg.n_entries, cfg.entry_src(), seed)
-    entry_k = _fill((1, cfg.n_entries, 64), cfg.entry_k(), seed=seed)[0]
-    idx_q = [_fill((nq, 8, 64), cfg.idx_q(l), seed=seed) if m != 2 else None
+    entry_k = fill_tensor((1, cfg.n_entries, 64), cfg.entry_k(), seed=seed)[0]
+    idx_q = [fill_tensor((nq, 8, 64), cfg.idx_q(l), seed=seed) if m != 2 else None
              for l, (m, _, _) in enumerate(cfg.layers)]
-    main_q = [_fill((nq, 16, LATENT), cfg.main_q(l), seed=seed) for l in range(nl)]
+    main_q = [fill_tensor((nq, 16, LATENT), cfg.main_q(l), seed=seed) for l in range(nl)]
     swa = []
     for l in range(nl):
         t = torch.empty(cfg.swa_rows_total, LATENT, dtype=torch.int16, device="cuda")

@@ -72,7 +72,7 @@ typedef int32_t csa2_status;
 /* Message of the last failing call on this thread ("" if none). */
 const char* csa2_last_error(void);
 /* Version of this ABI (bumped on any signature or struct change; 2 added
- * the FP8 window). */
+ * the FP8 window, 3 the key maintenance on append). */
 int32_t csa2_abi_version(void);
 
 /* ------------------------------------------------------------ FP4 cache
@@ -190,6 +190,28 @@ csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_
                                  int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                                  float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Indexer-key and block-key maintenance ([P1 "Compressed Sparse Attention 2
+ * (CSA2)"]: the hierarchical pool needs a key per block of blk positions;
+ * the pages do not say how it is formed).  READING: a block's key is the
+ * sum of the indexer keys of its existing positions, in bf16.
+ *   csa2_block_keys: blk_k [n_seq][blk_cap][64] = the key of every block of
+ *     idx_k [n_seq][key_cap][64] over its first lens[b] positions (summed in
+ *     binary32, rounded once to bf16); blocks past the last are written 0.
+ *   csa2_append_index_keys: for each sequence b, with row = lens[b] (read
+ *     before csa2_quant_append advances it): idx_k[b][row] = new_k[b], and
+ *     if blk_k != NULL the key of block row/blk becomes new_k[b] (first
+ *     position of the block) or its previous value + new_k[b], rounded to
+ *     bf16.  The running sum equals the once-rounded sum while every
+ *     partial sum is exact in bf16 (integer-valued keys, |sum| <= 256).
+ *     A row past key_cap (or a block past blk_cap) writes nothing and ORs 2
+ *     into *err_flag (if not NULL).
+ * new_k [n_seq][64] bf16; lens [n_seq] int32 (device). */
+csa2_status csa2_block_keys(const uint16_t* idx_k, int64_t key_cap, const int32_t* lens, int32_t blk,
+                            uint16_t* blk_k, int64_t blk_cap, int32_t n_seq, void* stream);
+csa2_status csa2_append_index_keys(const uint16_t* new_k, uint16_t* idx_k, int64_t key_cap, uint16_t* blk_k,
+                                   int64_t blk_cap, int32_t blk, const int32_t* lens, int32_t* err_flag,
+                                   int32_t n_seq, void* stream);
+
 /* ------------------------------------------------------------ scheduler
  * Static layer-mode table [P1 "Compressed Sparse Attention 2 (CSA2)"]:
  *   Full    computes its own selection: a fresh Top-k over all positions,
@@ -232,8 +254,9 @@ typedef struct {
   int32_t* lens;                /* [n_seq] positions, shared by all tensors */
   const uint16_t* new_row;      /* [n_seq][512] bf16 row to append, or NULL */
   int32_t append_kv;            /* tensor that receives the appended row */
-  const uint16_t* idx_k;        /* [n_seq][key_cap][64] bf16 indexer K */
-  const uint16_t* blk_k;        /* [n_seq][blk_cap][64] bf16 block keys, or NULL */
+  uint16_t* idx_k;              /* [n_seq][key_cap][64] bf16 indexer K (written with new_idx_k) */
+  uint16_t* blk_k;              /* [n_seq][blk_cap][64] bf16 block keys, or NULL (written with
+                                   new_idx_k) */
   const uint16_t* const* idx_q; /* host [n_layers]: [n_seq][8][64] (Reuse: ignored) */
   const float* const* idx_w;    /* host [n_layers] of [n_seq][8] f32 or NULL; NULL array = all 1 */
   const uint16_t* const* main_q; /* host [n_layers]: [n_seq][16][512] bf16 */
@@ -241,14 +264,19 @@ typedef struct {
                                    bytes when desc.swa_fp8 */
   const int32_t* swa_len;       /* [n_seq] valid SWA rows (<= swa_max) */
   float* const* out;            /* host [n_layers]: [n_seq][16][512] f32 */
+  const uint16_t* new_idx_k;    /* [n_seq][64] bf16 indexer key of the appended position, or
+                                   NULL: with it the step first appends the key to idx_k and
+                                   its block's key (csa2_append_index_keys) */
 } csa2_step_io;
 
 typedef struct csa2_sched csa2_sched;
 
 /* Validate the table and allocate the scheduler's device workspace. */
 csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out);
-/* One decode step on `stream`: the append (if io.new_row), then every layer
- * in table order.  Asynchronous; capturable in a HIP graph. */
+/* One decode step on `stream`: the key append (if io.new_idx_k), the
+ * latent append (if io.new_row), then every layer in table order.
+ * Asynchronous; capturable in a HIP graph.  Device flags (csa2_sched_check):
+ * bit 0 an append found a full cache, bit 1 a key append found one. */
 csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* stream);
 /* Device pointer to the indices [n_seq][topk] int32 that layer `layer`
  * attended over in the last step (Reuse layers share their source's

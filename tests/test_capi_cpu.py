@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(csa2):
 
 
 def test_abi_version(csa2):
-    assert csa2.abi_version() == 2
+    assert csa2.abi_version() == 3
 
 
 def _err(csa2):
@@ -149,3 +149,12 @@ def test_prefill_calls_reject_bad_arguments(csa2):
     assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE, need - 1, None) == -3
     assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE + 16, need, None) == -1
     assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE, need, None) == -1    # io pointers null
+
+
+def test_key_maintenance_rejects_bad_arguments(csa2):
+    assert csa2._block_keys(FAKE, 100, FAKE, 8, FAKE, 12, 1, None) == -2        # 12 * 8 < 100
+    assert csa2._block_keys(None, 100, FAKE, 8, FAKE, 13, 1, None) == -1
+    assert csa2._block_keys(None, 100, None, 8, None, 13, 0, None) == 0        # n_seq = 0: no-op
+    assert csa2._append_keys(FAKE, FAKE, 0, None, 0, 8, FAKE, None, 1, None) == -2
+    assert csa2._append_keys(FAKE, FAKE, 100, FAKE, 0, 8, FAKE, None, 1, None) == -2
+    assert csa2._append_keys(None, FAKE, 100, None, 0, 8, FAKE, None, 1, None) == -1

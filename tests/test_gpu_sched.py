@@ -90,6 +90,7 @@ FULL_SIZE = {
     "hier_1m_b8": (C.HIER_1M, 1, [0, 7]),
     "decoder20_1m_b16": (C.DECODER_20L_1M, 3, [0, 9, 15]),
     "decoder20_1m_b16_fp8_window": (C.DECODER_20L_1M_FP8_WINDOW, 2, [0, 15]),
+    "decoder20_1m_b16_maintained_keys": (C.DECODER_20L_1M_KEYS, 3, [0, 15]),
 }
 
 
@@ -124,3 +125,43 @@ def test_full_size_steps_sampled_sequences(wl, name):
     sched.close()
     del inp
     torch.cuda.empty_cache()
+
+
+KEY_CASES = {
+    # hierarchical selection over maintained block keys: more than 2,048
+    # blocks, the appends start and extend partial blocks
+    "hier_keys": (C.HIER_1M.with_(n_seq=2, L0=8 * 3000 + 5, append=True, maintain_keys=True, q_sets=3), 5),
+    "decoder20_keys": (C.DECODER_20L_1M.with_(n_seq=2, L0=8 * 2500 + 6, q_sets=3, maintain_keys=True), 4),
+}
+
+
+@pytest.mark.parametrize("name", list(KEY_CASES))
+def test_decode_steps_with_maintained_keys(wl, name):
+    """Every step appends the new position's indexer key and updates its
+    block's key on the GPU; indexer K rows, block keys, pools, indices and
+    outputs match the oracle, which forms block keys as sums."""
+    cfg, steps = KEY_CASES[name]
+    print_case(f"sched maintained keys {name}: n_seq={cfg.n_seq} L0={cfg.L0} steps={steps}")
+    inp = wl.build_decode_inputs(cfg, steps)
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    for step in range(steps):
+        sched.decode_step(ios[step % cfg.q_sets])
+        L = cfg.lens_at(step)
+        idx = [sched.indices(l).cpu().numpy() for l in range(len(cfg.layers))]
+        pool = sched.pool().cpu().numpy()
+        outs = [o.cpu().numpy() for o in inp.out]
+        for b in range(cfg.n_seq):
+            tok = ow.index_key_rows(cfg, b, L)
+            assert np.array_equal(inp.idx_k[b, :L].cpu().numpy().view(np.uint16), tok), f"step {step} idx_k"
+            nb = -(-L // cfg.blk)
+            assert np.array_equal(inp.blk_k[b, :nb].cpu().numpy().view(np.uint16),
+                                  oracle.block_keys(tok, L, cfg.blk)), f"step {step} seq {b} block keys"
+            ref = ow.reference_step(cfg, step, b)
+            for l, r in enumerate(ref):
+                assert np.array_equal(idx[l][b], r.idx), f"step {step} seq {b} layer {l} indices"
+                if cfg.layers[l][0] == C.FULL:
+                    assert np.array_equal(pool[b], r.pool), f"step {step} seq {b} pool"
+                assert_attention_close(outs[l][b], r.out, f"step {step} seq {b} layer {l}")
+    assert sched.check() == 0
+    sched.close()
