@@ -388,3 +388,57 @@ def test_sparse_attn_fp8_window_matches_oracle(csa2, k_idx, swa_lens):
         codes, scales = oracle.quant_rows(src[b])
         ref = oracle.sparse_attn_fp8w(q[b], codes, scales, idx[b], swa8[b], swa_len[b], SM_SCALE)
         assert_attention_close(got[b], ref, f"query {b}")
+
+
+# ------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("n,k", [(1, 1), (2, 2048), (70000, 1), (3000, 2048), (40000, 2048)])
+def test_topk_extreme_k_and_special_scores(csa2, n, k):
+    """k = 1 and k = 2048, lengths below, inside and above the register
+    path; NaN and -inf are not candidates, +inf is the largest score."""
+    n_seq = 2
+    rng = np.random.default_rng(n * 7 + k)
+    sc = rng.integers(-3, 4, size=(n_seq, n)).astype(np.float32)
+    sc[0, ::5] = np.nan
+    sc[1, 1::7] = -np.inf
+    sc[1, ::11] = np.inf
+    print_case(f"topk extremes n={n} k={k}")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    csa2.topk(dev(sc), k, out)
+    got = out.cpu().numpy()
+    for b in range(n_seq):
+        cand = ~np.isnan(sc[b]) & (sc[b] != -np.inf)
+        ids = np.arange(n)[cand]
+        ref = oracle.select(sc[b][cand], ids, k)
+        assert np.array_equal(got[b], ref), b
+
+
+def test_zero_sized_calls_are_no_ops(csa2):
+    """n_seq = 0 / n_q = 0 / n_rows = 0 enqueue nothing and succeed."""
+    empty16 = torch.empty(0, dtype=torch.int16, device="cuda")
+    csa2.quant_rows(empty16.view(0, 512), torch.empty(0, 256, dtype=torch.uint8, device="cuda"),
+                    torch.empty(0, 32, dtype=torch.uint8, device="cuda"))
+    csa2.quant_fp8_rows(empty16.view(0, 512), torch.empty(0, 512, dtype=torch.uint8, device="cuda"))
+    assert csa2._topk(None, 100, None, 1, 512, None, 0, 8, None, None, 0, 0, None) == 0
+    assert csa2._index_score(None, None, None, 100, None, 1, None, 0, 8, None, 50, 0, None) == 0
+    torch.cuda.synchronize()
+
+
+def test_sparse_attn_maximum_rows(csa2):
+    """The largest attended set one call accepts: 8,064 selected rows + a
+    128-row window = 8,192 rows (64 chunks, 64 split workgroups)."""
+    n_q, cap, k_idx = 2, 9000, 8064
+    src = kv_source(5, n_q, cap)
+    kv = _device_cache(csa2, src)
+    rng = np.random.default_rng(5)
+    idx = np.stack([np.sort(rng.choice(cap, k_idx, replace=False)) for _ in range(n_q)]).astype(np.int32)
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 5), synth.NORMAL, range(n_q), np.arange(16), 512)
+    swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 5), synth.NORMAL, range(n_q), np.arange(128), 512)
+    swa_len = np.array([128, 31], np.int32)
+    print_case("sparse_attn 8,192 rows")
+    out = torch.empty(n_q, 16, 512, dtype=torch.float32, device="cuda")
+    csa2.sparse_attn(dev(q), kv, dev(idx), dev(swa), dev(swa_len), SM_SCALE, out)
+    got = out.cpu().numpy()
+    for b in range(n_q):
+        codes, scales = oracle.quant_rows(src[b])
+        ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa[b], swa_len[b], SM_SCALE)
+        assert_attention_close(got[b], ref, f"query {b}")

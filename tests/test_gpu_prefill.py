@@ -68,6 +68,12 @@ CHUNKS = {
                       layers=((C.FULL, 0, 0), (C.REUSE, 0, 0), (C.REINDEX, 0, 0), (C.REUSE, 0, 0))),
     # ratio 1 (every token an entry), window shorter than 128
     "ratio1_swa16": _small(n_entries=900, n_q=33, t0=900 - 33, ratio=1, swa=16),
+    # the earliest chunk start a 128-token window allows (t0 = 127), ratio 3:
+    # 42 .. 65 visible entries, fewer than k
+    "start_ratio3": _small(n_entries=400, n_q=70, t0=127, ratio=3),
+    # a one-token window from token 0: the first queries see no entry at all
+    # (the window alone is attended)
+    "no_entries_swa1": _small(n_entries=50, n_q=40, t0=0, ratio=3, swa=1),
 }
 
 
