@@ -74,7 +74,7 @@ def algorithmic_bytes(cfg, L: int) -> dict:
 
     Per sequence: the block keys of all ceil(L/8) blocks (128 B each), the
     indexer keys of the pool's positions (128 B each; shared by the Full and
-    Reindex layers), the selected FP4 rows of each main-KV tensor (512 x 288
+    Reindex layers; once more for every Full layer with its own keys), the selected FP4 rows of each main-KV tensor (512 x 288
     B), every layer's SWA window (128 x 1 KiB, or 512 B rows in FP8), main Q (16 KiB) and f32
     output (32 KiB), each selecting layer's indexer Q (1 KiB) and indices
     (2 KiB), and the append (1 KiB read, 288 B written)."""
@@ -82,11 +82,12 @@ def algorithmic_bytes(cfg, L: int) -> dict:
     nl = len(cfg.layers)
     sel_layers = sum(1 for m, _, _ in cfg.layers if m != 2)
     groups = len({k for _, k, _ in cfg.layers})
+    key_sets = 1 + sum(1 for l in range(nl) if cfg.own_keys(l))
     nblk = -(-L // cfg.blk)
     pool_pos = min(L, cfg.pool_blocks * cfg.blk) if cfg.hierarchical else L
     parts = {
         "block_keys": n * nblk * 128 if cfg.hierarchical else 0,
-        "indexer_keys": n * pool_pos * 128,
+        "indexer_keys": n * pool_pos * 128 * key_sets,
         "fp4_rows": n * groups * cfg.topk * 288,
         "swa": n * nl * cfg.swa * (512 if cfg.swa_fp8 else 1024),
         "main_q": n * nl * 16 * 1024,
@@ -217,6 +218,46 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                     "traffic_bytes": measured_traffic(key) if cfg.name == DECODE_CONFIGS["decoder20_1m"].name else None})
+    return res
+
+
+def flat_op_rooflines(cfg, inp, graph: bool = True):
+    """The ops of a flat-selection step (every Full layer scores all L
+    positions), as op_rooflines does for the hierarchical one.  Bytes per
+    call: flat score n*L*(128+4) (indexer keys read, scores written); Top-512
+    n*L*4 (scores read once); attention as in op_rooflines."""
+    import torch
+
+    import fp4_kv_cache_quant_amd as csa2
+
+    n = cfg.n_seq
+    L = int(inp.lens[0].item())
+    q0 = inp.idx_q[0][0]
+    sc = torch.empty(n, inp.cap, dtype=torch.float32, device="cuda")
+    idx = torch.empty(n, cfg.topk, dtype=torch.int32, device="cuda")
+    out = torch.empty(n, 16, 512, dtype=torch.float32, device="cuda")
+    tws = torch.zeros(csa2.topk_workspace_size(inp.cap, n), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(csa2.sparse_attn_workspace_size(n, cfg.topk, cfg.swa), dtype=torch.uint8, device="cuda")
+    csa2.index_score(q0, inp.idx_k, inp.lens, sc)
+    csa2.topk(sc, cfg.topk, idx, lens=inp.lens, ws=tws)
+    sel_layers = sum(1 for m, _, _ in cfg.layers if m != 2)
+    ops = [
+        ("flat_score", "flat score (index_score, all positions)", sel_layers, n * L * 132,
+         lambda: csa2.index_score(q0, inp.idx_k, inp.lens, sc)),
+        ("flat_topk", "flat Top-512 (topk)", sel_layers, n * L * 4,
+         lambda: csa2.topk(sc, cfg.topk, idx, lens=inp.lens, ws=tws)),
+        ("sparse_attn", "sparse+SWA attention (sparse_attn: chunk + combine kernels)", len(cfg.layers),
+         n * (cfg.topk * 4 + cfg.topk * 288 + cfg.swa * (512 if cfg.swa_fp8 else 1024) + 16 * 1024 + 16 * 512 * 4),
+         lambda: csa2.sparse_attn(inp.main_q[0][0], inp.kv[0], idx, inp.swa[0], inp.swa_len, 512 ** -0.5, out,
+                                  ws=aws)),
+    ]
+    res = []
+    for key, name, per_step, nbytes, fn in ops:
+        us = _graph_time_us(fn, graph=graph)
+        res.append({"key": key, "op": name, "launches_per_step": per_step, "bytes_per_launch": nbytes,
+                    "avg_us": round(us, 2), "us_per_step": round(us * per_step, 1),
+                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
     return res
 
 
@@ -410,6 +451,40 @@ def maintained_keys_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
     return _time_steps(ck, inpk, K, W, graph)
 
 
+def encoder_decode_leg(K: int, W: int, graph: bool, cpu_seqs: int) -> dict:
+    """The encoder's 18 layers at ratio 2 in decode (3 groups of Full + 5
+    Reuse over 512K entries, batch 16, each Full layer with its own indexer
+    K): step time, the flat ops' rooflines, and step 0 of a few sequences
+    against the oracle (also timed as its CPU rate)."""
+    import torch
+
+    from fp4_kv_cache_quant_amd import workloads as wl
+    from synth.configs import DECODE_CONFIGS
+
+    cfg = DECODE_CONFIGS["encoder_1m"]
+    nl = len(cfg.layers)
+    inp = wl.build_decode_inputs(cfg, 1 + W + K)
+    sched = wl.make_sched(inp)
+    sched.decode_step(wl.step_ios(sched, inp)[0])
+    torch.cuda.synchronize()
+    gpu0 = {"idx": [sched.indices(l).cpu().numpy() for l in range(nl)], "pool": None,
+            "out": [o.cpu().numpy() for o in inp.out]}
+    sched.close()
+    r = _time_steps(cfg, inp, K, W, graph)
+    r["ops"] = flat_op_rooflines(cfg, inp, graph=graph)
+    if cpu_seqs > 0:
+        seqs = sorted({0, cfg.n_seq - 1} if cpu_seqs > 1 else {0})
+        threads = max(1, min(len(seqs), len(os.sched_getaffinity(0)), 16))
+        res, dt = cpu_baseline(cfg, 0, seqs, threads)
+        r["parity_step0"] = compare_step(cfg, gpu0, res)
+        r["cpu_baseline"] = {"value": round(len(seqs) * nl / dt, 2), "unit": "(seq·layer)-steps/s",
+                             "cores": threads, "kind": "oracle",
+                             "sample": f"decode step 0 of sequences {seqs}, all {nl} layers, {dt:.1f} s"}
+    del inp
+    torch.cuda.empty_cache()
+    return r
+
+
 def compare_step(cfg, gpu, ref) -> dict:
     """GPU step-0 results against the oracle sample: indices and pool
     bit-exact, attention rel. L2 <= 1e-3 and max abs <= 5e-3 per (seq, head)."""
@@ -444,6 +519,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--no-fp8-window", action="store_true", help="skip the FP8-window variant of the step")
     ap.add_argument("--no-keys", action="store_true", help="skip the maintained-block-keys variant of the step")
+    ap.add_argument("--no-encoder", action="store_true", help="skip the encoder ratio-2 decode leg")
     ap.add_argument("--prefill-reps", type=int, default=5, help="timed prefill chunks")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for scaling profiler traffic counters)")
@@ -527,7 +603,8 @@ def main() -> int:
     # HIP events around graph replays on the stream the ops run on (no host
     # launch gaps).  The op with the largest share of the step (time x calls
     # per step) is the dominant one.
-    ops = op_rooflines(cfg, inp, total_steps, graph=not args.no_graph)
+    ops = (op_rooflines(cfg, inp, total_steps, graph=not args.no_graph) if cfg.hierarchical
+           else flat_op_rooflines(cfg, inp, graph=not args.no_graph))
     dom = max(ops, key=lambda o: o["us_per_step"])
     roofline = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
@@ -542,7 +619,8 @@ def main() -> int:
         cpu = {"value": round(len(seqs) * nl / dt, 2), "unit": "(seq·layer)-steps/s", "cores": threads,
                "kind": "oracle",
                "sample": f"decode step 0 of {len(seqs)} of {cfg.n_seq} sequences, all {nl} layers "
-                         f"(hierarchical select, 4 Reindex rescorings, {nl} attentions), {dt:.1f} s"}
+                         f"({sum(1 for m, _, _ in cfg.layers if m != 2)} selecting layers, {nl} attentions), "
+                         f"{dt:.1f} s"}
         parity = compare_step(cfg, gpu0, res)
 
     fp8w = keys = None
@@ -550,6 +628,10 @@ def main() -> int:
         fp8w = fp8_window_leg(cfg, inp, K, W, graph=not args.no_graph)
     if not args.no_keys and cfg.hierarchical and cfg.append and not cfg.maintain_keys:
         keys = maintained_keys_leg(cfg, inp, K, W, graph=not args.no_graph)
+
+    encoder = None
+    if not args.no_encoder and args.config != "encoder_1m":
+        encoder = encoder_decode_leg(K, W, graph=not args.no_graph, cpu_seqs=0 if args.no_cpu else 2)
 
     prefill = None
     if not args.no_prefill:
@@ -566,7 +648,7 @@ def main() -> int:
         "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": round(hbm_gbps, 1),
                 "frac_of_peak": round(hbm_gbps / PEAK_HBM_GBPS, 4), "parts": ab},
         "roofline": roofline, "dominant_op": dom, "ops": ops, "cpu_baseline": cpu, "parity_step0": parity,
-        "fp8_window": fp8w, "maintained_keys": keys, "prefill": prefill,
+        "fp8_window": fp8w, "maintained_keys": keys, "encoder_decode": encoder, "prefill": prefill,
         "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
     }
     print(json.dumps(line), flush=True)

@@ -51,7 +51,7 @@ class _SchedDesc(ctypes.Structure):
 class _StepIO(ctypes.Structure):
     _fields_ = [("n_kv", _I32), ("kv", _P), ("lens", _P), ("new_row", _P), ("append_kv", _I32),
                 ("idx_k", _P), ("blk_k", _P), ("idx_q", _P), ("idx_w", _P), ("main_q", _P),
-                ("swa", _P), ("swa_len", _P), ("out", _P), ("new_idx_k", _P)]
+                ("swa", _P), ("swa_len", _P), ("out", _P), ("new_idx_k", _P), ("layer_idx_k", _P)]
 
 
 class _PrefillDesc(ctypes.Structure):
@@ -265,20 +265,23 @@ class Sched:
         self.close()
 
     def prepare(self, kv: Sequence[FP4KV], lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k=None,
-                new_row=None, append_kv: int = 0, idx_w=None, new_idx_k=None) -> "_StepIO":
-        """Build (and keep alive) the step descriptor for a fixed set of tensors."""
+                new_row=None, append_kv: int = 0, idx_w=None, new_idx_k=None, layer_idx_k=None) -> "_StepIO":
+        """Build (and keep alive) the step descriptor for a fixed set of tensors.
+        layer_idx_k: None, or per layer the own indexer K of a flat Full layer
+        (None entries: idx_k)."""
         nl = len(self.layers)
         kvs = (_FP4KV * len(kv))(*[k.c() for k in kv])
         P = _P * nl
         iq = P(*[_ptr(t) if t is not None else None for t in idx_q])
         iw = P(*[_ptr(t) for t in idx_w]) if idx_w is not None else None
         mq, sw, ou = P(*[_ptr(t) for t in main_q]), P(*[_ptr(t) for t in swa]), P(*[_ptr(t) for t in out])
+        lk = P(*[_ptr(t) if t is not None else None for t in layer_idx_k]) if layer_idx_k is not None else None
         io = _StepIO(len(kv), ctypes.cast(kvs, _P), _ptr(lens), _ptr(new_row), append_kv, _ptr(idx_k),
                      _ptr(blk_k), ctypes.cast(iq, _P), ctypes.cast(iw, _P) if iw is not None else None,
                      ctypes.cast(mq, _P), ctypes.cast(sw, _P), _ptr(swa_len), ctypes.cast(ou, _P),
-                     _ptr(new_idx_k))
-        io._keep = (kvs, iq, iw, mq, sw, ou, kv, lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k,
-                    new_row, idx_w, new_idx_k)
+                     _ptr(new_idx_k), ctypes.cast(lk, _P) if lk is not None else None)
+        io._keep = (kvs, iq, iw, mq, sw, ou, lk, kv, lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k,
+                    new_row, idx_w, new_idx_k, layer_idx_k)
         return io
 
     def decode_step(self, io: "_StepIO", stream=None) -> None:

@@ -75,7 +75,7 @@ csa2_status check_topk(const float* scores, int64_t n, int32_t len_div, int32_t 
   CSA2_REQUIRE(scores && out && ws, CSA2_EINVAL, "csa2_topk: null pointer");
   CSA2_REQUIRE((reinterpret_cast<uintptr_t>(ws) & 15) == 0, CSA2_EINVAL, "csa2_topk: ws must be 16-byte aligned");
   CSA2_REQUIRE(k >= 1 && k <= CSA2_TOPK_MAX, CSA2_ESHAPE, "csa2_topk: k must be in [1, 2048]");
-  CSA2_REQUIRE(n >= 0 && n <= CSA2_TOPK_NMAX, CSA2_ESHAPE, "csa2_topk: n must be in [0, 262144]");
+  CSA2_REQUIRE(n >= 0 && n <= CSA2_TOPK_NMAX, CSA2_ESHAPE, "csa2_topk: n must be in [0, 1048576]");
   CSA2_REQUIRE(len_div > 0, CSA2_EINVAL, "csa2_topk: len_div must be positive");
   if (pool) {
     CSA2_REQUIRE(n_pool > 0 && n_pool <= CSA2_TOPK_MAX && blk > 0 && n == (int64_t)n_pool * blk, CSA2_ESHAPE,
@@ -121,7 +121,7 @@ extern "C" {
 
 const char* csa2_last_error(void) { return g_error.c_str(); }
 
-int32_t csa2_abi_version(void) { return 3; }
+int32_t csa2_abi_version(void) { return 4; }
 
 csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                             void* stream) {

@@ -62,7 +62,7 @@ csa2_status check_prefill_desc(const csa2_prefill_desc* d) {
   CSA2_REQUIRE(d && d->layers && d->n_layers >= 1, CSA2_EINVAL, "csa2_prefill: null descriptor or empty table");
   CSA2_REQUIRE(d->n_q >= 1 && d->n_q <= 65535, CSA2_ESHAPE, "csa2_prefill: n_q must be in [1, 65535]");
   CSA2_REQUIRE(d->n_entries >= 1 && d->n_entries <= CSA2_TOPK_NMAX, CSA2_ESHAPE,
-               "csa2_prefill: n_entries must be in [1, 262144]");
+               "csa2_prefill: n_entries must be in [1, 1048576]");
   CSA2_REQUIRE(d->ratio >= 1, CSA2_EINVAL, "csa2_prefill: ratio must be >= 1");
   CSA2_REQUIRE(d->topk >= 1 && d->topk <= CSA2_TOPK_MAX, CSA2_ESHAPE, "csa2_prefill: topk must be in [1, 2048]");
   CSA2_REQUIRE(d->swa >= 0 && d->swa <= 4096 && (int64_t)d->topk + d->swa <= 8192, CSA2_ESHAPE,

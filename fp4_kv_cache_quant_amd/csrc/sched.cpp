@@ -147,7 +147,7 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
           d.blk_cap * d.blk >= d.key_cap)) {
       free_sched(s);
       set_error("csa2_sched_create: hierarchical layers need 1 <= pool_blocks <= 2048, blk >= 1, "
-                "pool_blocks*blk <= 262144, blk_cap*blk >= key_cap and blk_cap <= 262144");
+                "pool_blocks*blk <= 1048576, blk_cap*blk >= key_cap and blk_cap <= 1048576");
       return CSA2_ESHAPE;
     }
     s->scores_n = std::max<int64_t>(d.blk_cap, (int64_t)d.pool_blocks * d.blk);
@@ -155,7 +155,7 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
   if (s->any_flat) {
     if (d.key_cap > CSA2_TOPK_NMAX) {
       free_sched(s);
-      set_error("csa2_sched_create: flat selection supports key_cap <= 262144");
+      set_error("csa2_sched_create: flat selection supports key_cap <= 1048576");
       return CSA2_ESHAPE;
     }
     s->scores_n = std::max<int64_t>(s->scores_n, d.key_cap);
@@ -208,6 +208,9 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
                  "csa2_sched_decode_step: missing indexer Q for layer " + std::to_string(l));
     CSA2_REQUIRE(io->main_q[l] && io->swa[l] && io->out[l], CSA2_EINVAL,
                  "csa2_sched_decode_step: missing main Q / SWA / out for layer " + std::to_string(l));
+    CSA2_REQUIRE(!io->layer_idx_k || !io->layer_idx_k[l] || (L.mode == CSA2_FULL && !L.hierarchical), CSA2_EINVAL,
+                 "csa2_sched_decode_step: layer_idx_k entry " + std::to_string(l) +
+                     " must be NULL (only flat Full layers own indexer K)");
   }
   if (io->new_idx_k) {
     // The appended position's indexer key, and its block's key: before the
@@ -227,6 +230,10 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
   for (int l = 0; l < d.n_layers; ++l) {
     const csa2_layer& L = s->layers[l];
     int32_t* idx = s->idx_bufs + idx_stride * s->idx_buf_of_layer[l];
+    // Indexer K of this layer's Full layer (itself, or the one a Reindex
+    // follows); Reuse layers read no keys.
+    const int32_t full = L.mode == CSA2_FULL ? l : s->full_of_layer[l];
+    const uint16_t* keys = (full >= 0 && io->layer_idx_k && io->layer_idx_k[full]) ? io->layer_idx_k[full] : io->idx_k;
     const float* w = io->idx_w ? io->idx_w[l] : nullptr;
     csa2_status st = CSA2_OK;
     bool use_pool = false;
@@ -248,14 +255,14 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       if (use_pool) {
         const int64_t n_out = (int64_t)d.pool_blocks * d.blk;
         const bool fused = n_out > kTopkRowsMax;
-        st = index_score_launch(io->idx_q[l], w, io->idx_k, d.key_cap, io->lens, 1, s->pool, d.pool_blocks,
+        st = index_score_launch(io->idx_q[l], w, keys, d.key_cap, io->lens, 1, s->pool, d.pool_blocks,
                                 d.blk, s->scores, n_out, d.n_seq, fused ? s->tw.hist : nullptr, stream);
         if (st == CSA2_OK)
           st = topk_launch(s->scores, n_out, nullptr, 1, d.topk, s->pool, d.pool_blocks, d.blk, idx, s->tw, fused,
                            d.n_seq, stream);
       } else {
         const bool fused = d.key_cap > kTopkRowsMax;
-        st = index_score_launch(io->idx_q[l], w, io->idx_k, d.key_cap, io->lens, 1, nullptr, 0, 1, s->scores,
+        st = index_score_launch(io->idx_q[l], w, keys, d.key_cap, io->lens, 1, nullptr, 0, 1, s->scores,
                                 d.key_cap, d.n_seq, fused ? s->tw.hist : nullptr, stream);
         if (st == CSA2_OK)
           st = topk_launch(s->scores, d.key_cap, io->lens, 1, d.topk, nullptr, 0, 1, idx, s->tw, fused, d.n_seq,

@@ -239,45 +239,62 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
   }
 }
 
+// Word access to the selection and tie bitmaps: LDS, or global memory at
+// device scope (bypassing the per-CU cache, so that other threads' atomic
+// updates of the same call are seen).
+template <bool kGlobal>
+__device__ __forceinline__ uint32_t bm_load(const uint32_t* p) {
+  if (kGlobal) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool kGlobal>
+__device__ __forceinline__ void bm_store(uint32_t* p, uint32_t v) {
+  if (kGlobal) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
 // Selection bitmap sel (and, if ties > 0, the tie bitmap tie: keys equal to
-// the threshold) of one sequence in LDS -> the ids in ascending order:
-// the lowest `ties` tie slots join the selection, then every thread owns a
-// contiguous run of words and writes its ids at its prefix-count position;
-// -1 pads the row to k.  Ends with the caller's LDS free to reuse only
-// after a barrier.
-__device__ void finish_output(uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
+// the threshold) of one sequence -> the ids in ascending order: the lowest
+// `ties` tie slots join the selection, then every thread owns a contiguous
+// run of words and writes its ids at its prefix-count position; -1 pads the
+// row to k.  The bitmaps are in LDS or (kGlobal) in global memory; a global
+// tie bitmap is left zero.
+template <bool kGlobal>
+__device__ void finish_output(uint32_t* sel, uint32_t* tie, int words, uint32_t ties, uint32_t kk,
                               const int32_t* pool_lds, int32_t blk, uint32_t* wave_sum, int32_t* __restrict__ ob) {
   const int tid = threadIdx.x;
   const int per = (words + kFinalThreads - 1) / kFinalThreads;
   const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
   if (ties > 0) {
     uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(tie[w]);
+    for (int w = w0; w < w1; ++w) cnt += __popc(bm_load<kGlobal>(&tie[w]));
     uint32_t dummy;
     uint32_t rank = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &dummy);
     for (int w = w0; w < w1 && rank < ties; ++w) {
-      uint32_t x = tie[w];
+      uint32_t x = bm_load<kGlobal>(&tie[w]);
       const uint32_t pc = __popc(x);
       if (rank + pc <= ties) {
-        sel[w] |= x;
+        bm_store<kGlobal>(&sel[w], bm_load<kGlobal>(&sel[w]) | x);
       } else {
         uint32_t keep = 0;
         for (uint32_t m = rank; m < ties; ++m) {
           keep |= x & (0u - x);
           x &= x - 1;
         }
-        sel[w] |= keep;
+        bm_store<kGlobal>(&sel[w], bm_load<kGlobal>(&sel[w]) | keep);
       }
       rank += pc;
     }
+    if (kGlobal)
+      for (int w = w0; w < w1; ++w) bm_store<true>(&tie[w], 0u);
     __syncthreads();
   }
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+  for (int w = w0; w < w1; ++w) cnt += __popc(bm_load<kGlobal>(&sel[w]));
   uint32_t n_sel;
   uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &n_sel);
   for (int w = w0; w < w1; ++w) {
-    uint32_t x = sel[w];
+    uint32_t x = bm_load<kGlobal>(&sel[w]);
     while (x) {
       const int bit = __ffs(x) - 1;
       x &= x - 1;
@@ -294,14 +311,18 @@ __device__ void finish_output(uint32_t* sel, const uint32_t* tie, int words, uin
 struct FinalSmem {
   int32_t pool[CSA2_TOPK_MAX];  // the sequence's pool block ids (pool mode)
   uint32_t hist[kTopkBins];
-  uint32_t sel[kTopkMaxWords];
-  uint32_t tie[kTopkMaxWords];
+  uint32_t sel[kTopkLdsWords];
+  uint32_t tie[kTopkLdsWords];
   uint32_t cand_key[kTopkCandCap];
   uint32_t cand_slot[kTopkCandCap];
   uint32_t wave_sum[kFinalWaves];
   uint32_t found[2];
 };
 
+// kGlobal: the selection and tie bitmaps stay in global memory (inputs of
+// more than kTopkLdsWords * 32 slots): the filter pass's bitmap is marked in
+// place and the tie bitmap is cleared here and left clear.
+template <bool kGlobal>
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* __restrict__ scores, int64_t n,
                                                                    const int32_t* __restrict__ lens,
                                                                    int32_t len_div, int32_t k,
@@ -345,7 +366,9 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
 
   const bool all = th.total <= kk;
   const bool buffered = th.in_bin <= (uint32_t)kTopkCandCap;
-  for (int i = tid; i < words; i += kFinalThreads) sm.tie[i] = 0;
+  uint32_t* sel = kGlobal ? ws.bits + (int64_t)b * ws.words_cap : sm.sel;
+  uint32_t* tie = kGlobal ? ws.tie + (int64_t)b * ws.words_cap : sm.tie;
+  for (int i = tid; i < words; i += kFinalThreads) bm_store<kGlobal>(&tie[i], 0u);
   if (direct) {
     // Filter pass in this workgroup (scores already loaded).
     constexpr int kPer = kPerDirect;
@@ -377,15 +400,18 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
       }
     }
   } else {
-    // Bitmap and candidates of the filter pass; clamped loads, all in flight together.
-    const uint32_t* gb = ws.bits + (int64_t)b * ws.words_cap;
-    constexpr int kWordsPer = kTopkMaxWords / kFinalThreads;
-    uint32_t wv[kWordsPer];
+    // Bitmap (into LDS unless kGlobal) and candidates of the filter pass;
+    // clamped loads, all in flight together.
+    if (!kGlobal) {
+      const uint32_t* gb = ws.bits + (int64_t)b * ws.words_cap;
+      constexpr int kWordsPer = kTopkLdsWords / kFinalThreads;
+      uint32_t wv[kWordsPer];
 #pragma unroll
-    for (int j = 0; j < kWordsPer; ++j) wv[j] = gb[min(tid + kFinalThreads * j, max(words - 1, 0))];
+      for (int j = 0; j < kWordsPer; ++j) wv[j] = gb[min(tid + kFinalThreads * j, max(words - 1, 0))];
 #pragma unroll
-    for (int j = 0; j < kWordsPer; ++j)
-      if (tid + kFinalThreads * j < words) sm.sel[tid + kFinalThreads * j] = wv[j];
+      for (int j = 0; j < kWordsPer; ++j)
+        if (tid + kFinalThreads * j < words) sm.sel[tid + kFinalThreads * j] = wv[j];
+    }
     if (!all && buffered && n_cand_global > 0) {
       const uint2* gc = ws.cand + (int64_t)b * kTopkCandCap;
       constexpr int kCandPer = kTopkCandCap / kFinalThreads;
@@ -448,22 +474,22 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
     if (buffered) {
       for (int c = tid; c < nc; c += kFinalThreads) {
         const uint32_t key = sm.cand_key[c], i = sm.cand_slot[c];
-        if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
-        else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
+        if (key > T) atomicOr(&sel[i >> 5], 1u << (i & 31));
+        else if (key == T) atomicOr(&tie[i >> 5], 1u << (i & 31));
       }
     } else {
       for (int i = tid; i < nvalid; i += kFinalThreads) {
         const uint32_t key = order_key(sc[i]);
         if (!key || (key >> 20) != th.b1) continue;
-        if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
-        else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
+        if (key > T) atomicOr(&sel[i >> 5], 1u << (i & 31));
+        else if (key == T) atomicOr(&tie[i >> 5], 1u << (i & 31));
       }
     }
     __syncthreads();
   }
 
-  finish_output(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
-                out + (int64_t)b * k);
+  finish_output<kGlobal>(sel, tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+                         out + (int64_t)b * k);
 }
 
 
@@ -576,15 +602,16 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
     }
   }
   __syncthreads();
-  finish_output(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
-                out + (int64_t)b * k);
+  finish_output<false>(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+                       out + (int64_t)b * k);
 }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t n, int32_t n_seq) {
   const int64_t words = (n + 31) / 32;
-  return (size_t)n_seq * (kTopkBins * sizeof(uint32_t) + sizeof(uint32_t) + words * sizeof(uint32_t) +
+  const int64_t tie_words = words > kTopkLdsWords ? words : 0;
+  return (size_t)n_seq * (kTopkBins * sizeof(uint32_t) + sizeof(uint32_t) + (words + tie_words) * sizeof(uint32_t) +
                           kTopkCandCap * sizeof(uint2)) + 64;
 }
 
@@ -599,6 +626,8 @@ TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq) {
   p += (size_t)n_seq * sizeof(uint32_t);
   w.words_cap = (n + 31) / 32;
   w.bits = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)n_seq * w.words_cap * sizeof(uint32_t);
+  w.tie = reinterpret_cast<uint32_t*>(p);  // used (and sized) only past kTopkLdsWords words
   return w;
 }
 
@@ -608,7 +637,10 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
   if (n_seq == 0) return CSA2_OK;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_final_kernel),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_final_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sizeof(FinalSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_final_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sizeof(FinalSmem)) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<16>),
@@ -638,8 +670,12 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
   if (n > kDirectMax)
     hipLaunchKernelGGL(topk_filter_kernel, dim3((uint32_t)((n + kFilterSlots - 1) / kFilterSlots), n_seq),
                        dim3(kPassThreads), 0, stream, scores, n, lens, len_div, k, ws);
-  hipLaunchKernelGGL(topk_final_kernel, dim3(n_seq), dim3(kFinalThreads), sizeof(FinalSmem), stream, scores,
-                     n, lens, len_div, k, pool, n_pool, blk, ws, out);
+  if ((n + 31) / 32 > kTopkLdsWords)
+    hipLaunchKernelGGL(topk_final_kernel<true>, dim3(n_seq), dim3(kFinalThreads), sizeof(FinalSmem), stream,
+                       scores, n, lens, len_div, k, pool, n_pool, blk, ws, out);
+  else
+    hipLaunchKernelGGL(topk_final_kernel<false>, dim3(n_seq), dim3(kFinalThreads), sizeof(FinalSmem), stream,
+                       scores, n, lens, len_div, k, pool, n_pool, blk, ws, out);
   return launch_status("csa2_topk");
 }
 

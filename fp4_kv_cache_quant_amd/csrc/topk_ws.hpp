@@ -10,7 +10,7 @@ namespace csa2 {
 
 constexpr int kTopkBins = 4096;                        // top-digit histogram (12 bits)
 constexpr int kTopkCandCap = 8192;                     // keys buffered from the threshold bin
-constexpr int kTopkMaxWords = CSA2_TOPK_NMAX / 32;     // selection bitmap words
+constexpr int kTopkLdsWords = 262144 / 32;            // bitmaps kept in LDS up to this many words
 
 // Per-sequence regions of one workspace.  hist and cnt must be zero when a
 // Top-k call starts; the call leaves them zero.
@@ -18,6 +18,7 @@ struct TopkWs {
   uint32_t* hist;     // [n_seq][kTopkBins]
   uint32_t* cnt;      // [n_seq] candidates appended by the filter pass
   uint32_t* bits;     // [n_seq][words_cap] selection bitmap of the filter pass
+  uint32_t* tie;      // [n_seq][words_cap] tie bitmap (inputs longer than kTopkLdsWords * 32)
   uint2* cand;        // [n_seq][kTopkCandCap] (key, slot)
   int64_t words_cap;
 };

@@ -57,6 +57,7 @@ class DecodeInputs:
     main_q: List[List[torch.Tensor]] = field(default_factory=list)            # [set][layer]
     new_row: List[Optional[torch.Tensor]] = field(default_factory=list)       # [set]
     new_idx_k: List[Optional[torch.Tensor]] = field(default_factory=list)     # [set], maintained keys
+    layer_idx_k: Optional[List[Optional[torch.Tensor]]] = None                 # [layer]: own indexer K
 
     @property
     def cap(self):
@@ -101,6 +102,9 @@ def build_decode_inputs(cfg: DecodeConfig, steps: int) -> DecodeInputs:
         inp.new_row.append(fill_tensor((n, 1, LATENT), cfg.new_row(s), seed=seed) if cfg.append else None)
         inp.new_idx_k.append(fill_tensor((n, 1, 64), cfg.new_idx_k(s), seed=seed)
                              if (cfg.maintain_keys and cfg.append) else None)
+    if cfg.layer_keys:
+        inp.layer_idx_k = [fill_tensor((n, cap, 64), cfg.layer_idx_k(l), seed=seed) if cfg.own_keys(l) else None
+                           for l in range(nl)]
     if cfg.maintain_keys and blk_k is not None:  # keys of the prefilled blocks, from indexer K
         block_keys(idx_k, inp.lens, blk_k, cfg.blk)
     torch.cuda.synchronize()
@@ -120,7 +124,8 @@ def step_ios(sched: Sched, inp: DecodeInputs):
     return [sched.prepare(kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, main_q=inp.main_q[s], swa=inp.swa,
                           swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q[s], blk_k=inp.blk_k,
                           new_row=inp.new_row[s], append_kv=inp.cfg.append_kv,
-                          new_idx_k=inp.new_idx_k[s] if inp.new_idx_k else None)
+                          new_idx_k=inp.new_idx_k[s] if inp.new_idx_k else None,
+                          layer_idx_k=inp.layer_idx_k)
             for s in range(inp.cfg.q_sets)]
 
 

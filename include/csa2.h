@@ -67,7 +67,7 @@ typedef int32_t csa2_status;
 #define CSA2_IDX_DIM 64     /* indexer head dimension */
 #define CSA2_SWA_MAX 128    /* [P1 "Causal Encoder-Decoder..."]: 128-token window */
 #define CSA2_TOPK_MAX 2048  /* largest k of one csa2_topk call */
-#define CSA2_TOPK_NMAX 262144 /* most candidates per sequence of one csa2_topk call */
+#define CSA2_TOPK_NMAX 1048576 /* most candidates per sequence of one csa2_topk call */
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* csa2_last_error(void);
@@ -267,6 +267,12 @@ typedef struct {
   const uint16_t* new_idx_k;    /* [n_seq][64] bf16 indexer key of the appended position, or
                                    NULL: with it the step first appends the key to idx_k and
                                    its block's key (csa2_append_index_keys) */
+  const uint16_t* const* layer_idx_k; /* host [n_layers] or NULL: entry l = the own indexer K
+                                   [n_seq][key_cap][64] bf16 of flat Full layer l (each Full
+                                   layer projects its keys); the Reindex layers after it rescore
+                                   the same keys.  A NULL array or entry means idx_k; entries of
+                                   other layers must be NULL (else CSA2_EINVAL), and hierarchical
+                                   Full layers always use idx_k with blk_k. */
 } csa2_step_io;
 
 typedef struct csa2_sched csa2_sched;

@@ -306,6 +306,7 @@ class SeqState:
     tok_keys: np.ndarray                    # indexer K rows [>= L][64] bf16 bits
     blk_keys: Optional[np.ndarray] = None   # block keys [>= ceil(L/8)][64]
     kv_rows: Optional[callable] = None      # kv_rows(kv_id, ids) -> (codes, scales) of those rows
+    layer_keys: Optional[dict] = None       # Full layer -> its own indexer K rows (else tok_keys)
 
 
 @dataclass
@@ -334,25 +335,31 @@ def decode_layers(layers: Sequence[Layer], seq: SeqState, inputs: Sequence[Layer
     (through the block pool when hierarchical); Reindex rescores the last Full
     layer's pool (or all L positions when that Full layer is flat) with its
     own indexer Q; Reuse reuses the latest indices; every layer attends with
-    its own main Q and SWA window."""
+    its own main Q and SWA window.  A Full layer scores its own indexer K when
+    seq.layer_keys holds one for it (each Full layer projects its keys), and
+    the Reindex layers after it rescore those."""
     check_table(layers)
     res: List[LayerResult] = []
     idx = pool = None
     last_full_pool = None
+    keys = seq.tok_keys
     for l, (layer, inp) in enumerate(zip(layers, inputs)):
         if layer.mode == FULL:
+            keys = seq.tok_keys
+            if seq.layer_keys is not None and l in seq.layer_keys:
+                keys = seq.layer_keys[l]
             if layer.hierarchical:
                 pool = pool_blocks(inp.idx_q, seq.blk_keys, seq.L, n_pool, BLK, inp.w)
-                idx = pool_select(inp.idx_q, seq.tok_keys, seq.L, pool, k, BLK, inp.w)
+                idx = pool_select(inp.idx_q, keys, seq.L, pool, k, BLK, inp.w)
             else:
                 pool = None
-                idx = flat_select(inp.idx_q, seq.tok_keys, seq.L, k, inp.w)
+                idx = flat_select(inp.idx_q, keys, seq.L, k, inp.w)
             last_full_pool = pool
         elif layer.mode == REINDEX:
             if last_full_pool is not None:
-                idx = pool_select(inp.idx_q, seq.tok_keys, seq.L, last_full_pool, k, BLK, inp.w)
+                idx = pool_select(inp.idx_q, keys, seq.L, last_full_pool, k, BLK, inp.w)
             else:
-                idx = flat_select(inp.idx_q, seq.tok_keys, seq.L, k, inp.w)
+                idx = flat_select(inp.idx_q, keys, seq.L, k, inp.w)
             pool = last_full_pool
         # REUSE: idx and pool stay as they are.
         out = None

@@ -62,7 +62,9 @@ def seq_state(cfg: DecodeConfig, b: int, step: int) -> SeqState:
             src[ok] = kv_source_rows(cfg, kv_id, b, ids[ok])
         return quant_rows(src)
 
-    return SeqState(L=L, tok_keys=tok, blk_keys=blk, kv_rows=kv_rows)
+    own = {l: _gen(cfg, cfg.layer_idx_k(l), b, np.arange(L), 64)
+           for l in range(len(cfg.layers)) if cfg.own_keys(l)}
+    return SeqState(L=L, tok_keys=tok, blk_keys=blk, kv_rows=kv_rows, layer_keys=own or None)
 
 
 def layer_inputs(cfg: DecodeConfig, b: int, step: int):

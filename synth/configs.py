@@ -32,6 +32,7 @@ class DecodeConfig:
     seed: int = 0
     swa_fp8: bool = False                     # window rows stored as E4M3 (FP8) codes
     maintain_keys: bool = False               # block keys = sums of indexer keys, kept current on append
+    layer_keys: bool = False                  # every flat Full layer after layer 0 has its own indexer K
 
     def cap(self, steps: int) -> int:
         """Rows per sequence of every main-KV tensor and of indexer K."""
@@ -60,6 +61,14 @@ class DecodeConfig:
 
     def idx_k(self):
         return tensor_id(KIND_IDX_K), INT9
+
+    def own_keys(self, layer: int) -> bool:
+        """Whether Full layer `layer` scores its own indexer K (else idx_k)."""
+        mode, _, hier = self.layers[layer]
+        return self.layer_keys and layer > 0 and mode == FULL and not hier
+
+    def layer_idx_k(self, layer: int):
+        return tensor_id(KIND_IDX_K, layer, 0), INT9
 
     def new_idx_k(self, step: int):
         return tensor_id(KIND_NEW_IDX_K, 0, step % self.q_sets), INT9
@@ -111,9 +120,18 @@ DECODER_20L_1M_KEYS = DECODER_20L_1M.with_(
 DECODER_20L_1M_FP8_WINDOW = DECODER_20L_1M.with_(
     name="20-layer decoder schedule, 1M positions, batch 16, FP8 window rows", swa_fp8=True)
 
+# The encoder's 18 CSA2 layers at ratio 2 in decode: three groups of Full +
+# 5 Reuse, each group with its own FP4 main-KV tensor and its Full layer with
+# its own indexer K, over 524,288 compressed entries (1M tokens), batch 16.
+# Every entry is complete; the token being decoded is in the windows.
+ENCODER_DECODE_1M = DecodeConfig(
+    name="encoder schedule at ratio 2 (3 groups of Full + 5 Reuse), 512K entries (1M tokens), batch 16",
+    n_seq=16, L0=1 << 19, layers=sum((_group(FULL, g, 0, 5) for g in range(3)), ()), n_kv=3,
+    layer_keys=True)
+
 DECODE_CONFIGS = {"single_4k": SINGLE_LAYER_4K, "group_64k": GROUP_64K, "hier_1m": HIER_1M,
                   "decoder20_1m": DECODER_20L_1M, "decoder20_1m_fp8win": DECODER_20L_1M_FP8_WINDOW,
-                  "decoder20_1m_keys": DECODER_20L_1M_KEYS}
+                  "decoder20_1m_keys": DECODER_20L_1M_KEYS, "encoder_1m": ENCODER_DECODE_1M}
 
 
 @dataclass(frozen=True)

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(csa2):
 
 
 def test_abi_version(csa2):
-    assert csa2.abi_version() == 3
+    assert csa2.abi_version() == 4
 
 
 def _err(csa2):
@@ -49,7 +49,7 @@ def test_topk_rejects_bad_k_and_n(csa2):
 
     assert call(k=0) == -2 and "k must be" in _err(csa2)
     assert call(k=4096) == -2
-    assert call(n=300000) == -2
+    assert call(n=2_000_000) == -2
     assert call(pool=FAKE, n_pool=10) == -2          # n != n_pool * blk
     assert call(scores=None) == -1
     assert call(ws=None) == -1
@@ -107,7 +107,7 @@ def test_scheduler_rejects_invalid_tables(csa2):
         csa2.Sched([L(csa2.FULL), L(7)], n_seq=1, key_cap=100)
     assert e.value.code == -4
     with pytest.raises(csa2.Csa2Error) as e:  # flat selection over too many positions
-        csa2.Sched([L(csa2.FULL)], n_seq=1, key_cap=1 << 20)
+        csa2.Sched([L(csa2.FULL)], n_seq=1, key_cap=(1 << 20) + 1)
     assert e.value.code == -2
     with pytest.raises(csa2.Csa2Error) as e:  # hierarchical: blocks must cover key_cap
         csa2.Sched([L(csa2.FULL, 0, True)], n_seq=1, key_cap=1 << 20, blk_cap=1000)
@@ -132,7 +132,7 @@ def test_prefill_workspace_and_table_validation(csa2):
     assert ws(_prefill_desc(csa2, t0=126)) == 0 and "t0" in _err(csa2)
     assert ws(_prefill_desc(csa2, t0=127)) > 0
     assert ws(_prefill_desc(csa2, n_q=0)) == 0
-    assert ws(_prefill_desc(csa2, n_entries=300000)) == 0
+    assert ws(_prefill_desc(csa2, n_entries=2_000_000)) == 0
     assert ws(_prefill_desc(csa2, layers=[csa2.Layer(csa2.REUSE)])) == 0 and "Reuse" in _err(csa2)
     assert ws(_prefill_desc(csa2, layers=[csa2.Layer(csa2.FULL, 0, True)])) == 0 and "hierarchical" in _err(csa2)
     assert ws(_prefill_desc(csa2, layers=[csa2.Layer(csa2.FULL), csa2.Layer(csa2.REINDEX)])) == full

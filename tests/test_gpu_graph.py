@@ -36,6 +36,8 @@ def _capture(fn):
     ("hier_small", C.HIER_1M.with_(n_seq=3, L0=8 * 20000 + 5, q_sets=1)),
     ("decoder20_small", C.DECODER_20L_1M.with_(n_seq=2, L0=8 * 3000 + 1, q_sets=1, append=False)),
     ("group_flat", C.GROUP_64K.with_(n_seq=4, L0=5000, q_sets=1, append=False)),
+    # flat selection past 262,144 entries: bitmaps in global memory
+    ("encoder_long", C.ENCODER_DECODE_1M.with_(n_seq=2, L0=300001, q_sets=1)),
 ])
 def test_decode_step_graph_replays_match_eager(wl, name, cfg):
     print_case(f"graph decode {name}")

@@ -171,7 +171,10 @@ def test_index_score_blocks_len_div_and_pool_mode(csa2):
 @pytest.mark.parametrize("n,k,levels,L", [
     (4096, 512, 9000, 4096), (4096, 512, 3, 4096), (65537, 512, 50, 65537), (131073, 2048, 400, 131073),
     (131085, 2048, 10 ** 6, 131073), (300, 512, 4, 300), (5000, 512, 1, 5000), (5000, 512, 2, 1),
-    (20000, 512, 1, 19999), (262144, 2048, 7, 262144)])
+    (20000, 512, 1, 19999), (262144, 2048, 7, 262144),
+    # past 262,144 slots the selection and tie bitmaps live in global memory
+    (262145, 512, 3, 262145), (524288, 2048, 13, 524288), (700001, 2048, 2, 650000),
+    (1048576, 512, 10 ** 6, 1048576 - 5)])
 def test_topk_matches_oracle(csa2, n, k, levels, L):
     n_seq = 2
     rng = np.random.default_rng(n + k + levels)
@@ -199,6 +202,22 @@ def test_topk_workspace_reused_across_calls(csa2):
     ws = torch.zeros(csa2.topk_workspace_size(n_max, n_seq), dtype=torch.uint8, device="cuda")
     print_case("topk shared workspace")
     for n, k, levels in [(70000, 2048, 300), (5000, 512, 40), (70000, 512, 2), (1000, 512, 3)]:
+        sc = rng.integers(0, levels, size=(n_seq, n)).astype(np.float32)
+        out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+        csa2.topk(dev(sc), k, out, ws=ws[:csa2.topk_workspace_size(n, n_seq)])
+        got = out.cpu().numpy()
+        for b in range(n_seq):
+            assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), (n, k, b)
+
+
+def test_topk_global_bitmaps_reused_across_calls(csa2):
+    """Inputs longer than the LDS bitmaps: one workspace for calls of
+    different lengths, the tie bitmap left clear for the next call."""
+    rng = np.random.default_rng(23)
+    n_seq, n_max = 2, 600000
+    ws = torch.zeros(csa2.topk_workspace_size(n_max, n_seq), dtype=torch.uint8, device="cuda")
+    print_case("topk global bitmaps, shared workspace")
+    for n, k, levels in [(600000, 2048, 3), (600000, 512, 5000), (400000, 2048, 1), (100000, 512, 4)]:
         sc = rng.integers(0, levels, size=(n_seq, n)).astype(np.float32)
         out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
         csa2.topk(dev(sc), k, out, ws=ws[:csa2.topk_workspace_size(n, n_seq)])

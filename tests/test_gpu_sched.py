@@ -32,6 +32,10 @@ CASES = {
     "hier_long": (C.HIER_1M.with_(n_seq=2, L0=8 * 40000 + 3), 1),
     # window rows stored as E4M3 (FP8)
     "decoder20_fp8_window": (C.DECODER_20L_1M.with_(n_seq=2, L0=8 * 2500 + 3, q_sets=2, swa_fp8=True), 2),
+    # encoder groups at ratio 2, each Full layer with its own indexer K
+    "encoder_small": (C.ENCODER_DECODE_1M.with_(n_seq=2, L0=3001, q_sets=2), 2),
+    # more entries than the selection bitmaps held in LDS (262,144)
+    "encoder_long": (C.ENCODER_DECODE_1M.with_(n_seq=2, L0=300001, q_sets=1), 1),
 }
 
 
@@ -91,6 +95,7 @@ FULL_SIZE = {
     "decoder20_1m_b16": (C.DECODER_20L_1M, 3, [0, 9, 15]),
     "decoder20_1m_b16_fp8_window": (C.DECODER_20L_1M_FP8_WINDOW, 2, [0, 15]),
     "decoder20_1m_b16_maintained_keys": (C.DECODER_20L_1M_KEYS, 3, [0, 15]),
+    "encoder_1m_b16": (C.ENCODER_DECODE_1M, 2, [0, 15]),
 }
 
 
@@ -164,4 +169,20 @@ def test_decode_steps_with_maintained_keys(wl, name):
                     assert np.array_equal(pool[b], r.pool), f"step {step} seq {b} pool"
                 assert_attention_close(outs[l][b], r.out, f"step {step} seq {b} layer {l}")
     assert sched.check() == 0
+    sched.close()
+
+
+def test_layer_keys_only_on_flat_full_layers(wl):
+    """An own indexer K given for a Reuse layer is rejected before any launch."""
+    import fp4_kv_cache_quant_amd as csa2
+    cfg = C.ENCODER_DECODE_1M.with_(n_seq=1, L0=600, q_sets=1)
+    print_case("sched layer keys validation")
+    inp = wl.build_decode_inputs(cfg, 1)
+    sched = wl.make_sched(inp)
+    bad = list(inp.layer_idx_k)
+    bad[1] = inp.idx_k
+    io = sched.prepare(kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, main_q=inp.main_q[0], swa=inp.swa,
+                       swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q[0], layer_idx_k=bad)
+    with pytest.raises(csa2.Csa2Error, match="layer_idx_k"):
+        sched.decode_step(io)
     sched.close()

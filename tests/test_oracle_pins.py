@@ -376,6 +376,38 @@ def test_reuse_layers_reproduce_latest_indices_and_reindex_with_full_q_equals_fu
     assert not np.allclose(res[1].out, res[0].out)
 
 
+def test_full_layer_with_own_keys_and_its_reindex():
+    """A Full layer with its own indexer K selects over those keys, the
+    Reindex layer after it rescores the same keys, and earlier layers keep the
+    shared keys; own keys equal to the shared ones change nothing."""
+    L = 3000
+    tk, _, _ = _synthetic_seq(9, L)
+    k2 = synth.gen_rows(9, synth.tensor_id(synth.KIND_IDX_K, 2), synth.INT9, [0], np.arange(L), 64)[0]
+    codes, scales = _random_cache(9, L)
+    modes = [oracle.FULL, oracle.REUSE, oracle.FULL, oracle.REINDEX]
+    layers = [oracle.Layer(m, 0, False) for m in modes]
+    ins = _layer_inputs(9, len(layers), modes)
+
+    def walk(layer_keys):
+        seq = oracle.SeqState(L=L, tok_keys=tk, kv_rows=lambda kv, ids: (codes, scales), layer_keys=layer_keys)
+        return oracle.decode_layers(layers, seq, ins, 1 / math.sqrt(512), attend=False)
+
+    def brute(q, keys):  # every position scored, the top 512 by (score desc, id asc)
+        sc = oracle.index_score(q, keys, np.arange(L))
+        order = np.lexsort((np.arange(L), -sc.astype(np.float64)))
+        return np.sort(order[:512])
+
+    res = walk({2: k2})
+    assert np.array_equal(res[0].idx, brute(ins[0].idx_q, tk))
+    assert np.array_equal(res[2].idx, brute(ins[2].idx_q, k2))
+    assert np.array_equal(res[3].idx, brute(ins[3].idx_q, k2))
+    assert not np.array_equal(res[3].idx, brute(ins[3].idx_q, tk))
+    same = walk({2: tk})
+    plain = walk(None)
+    for a, b in zip(same, plain):
+        assert np.array_equal(a.idx, b.idx)
+
+
 def test_table_validation():
     with pytest.raises(ValueError):
         oracle.check_table([oracle.Layer(oracle.REUSE)])
