@@ -36,8 +36,9 @@ constexpr int kFinalWaves = kFinalThreads / 64;
 constexpr int kPassThreads = 256;
 constexpr int kBatch = 8;                         // slots per thread loaded together
 constexpr int kHistSlots = kPassThreads * 16;     // slots per histogram workgroup
-constexpr int kFilterSlots = kPassThreads * 8;    // slots per filter workgroup
+constexpr int kFilterSlots = kPassThreads * 32;   // slots per filter workgroup
 constexpr int kDirectMax = 32768;                 // final kernel filters inputs up to this length itself
+constexpr size_t kCandBytes = kTopkCandCap * sizeof(uint2);  // candidate buffer per sequence
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -239,62 +240,66 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
   }
 }
 
-// Word access to the selection and tie bitmaps: LDS, or global memory at
-// device scope (bypassing the per-CU cache, so that other threads' atomic
-// updates of the same call are seen).
-template <bool kGlobal>
-__device__ __forceinline__ uint32_t bm_load(const uint32_t* p) {
-  if (kGlobal) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return *p;
-}
-template <bool kGlobal>
-__device__ __forceinline__ void bm_store(uint32_t* p, uint32_t v) {
-  if (kGlobal) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
+// Words w0 + kG*kQc*r + i (i < kG*kQc) of a bitmap: kQc groups of kG words
+// (kG = 4: 16-byte loads) of round r of a thread's run, loaded together
+// (clamped to the last group, which exists), words at or past w1 read as 0.
+template <int kG, int kQc>
+__device__ __forceinline__ void load_round(const uint32_t* bm, int q0, int r, int qmax, int w0, int w1,
+                                           uint32_t (&wv)[kG * kQc]) {
+#pragma unroll
+  for (int j = 0; j < kQc; ++j) {
+    const int q = min(q0 + kQc * r + j, qmax);
+    if constexpr (kG == 4) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(bm)[q];
+      wv[4 * j] = v[0], wv[4 * j + 1] = v[1], wv[4 * j + 2] = v[2], wv[4 * j + 3] = v[3];
+    } else {
+      wv[j] = bm[q];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kG * kQc; ++i)
+    if (w0 + kG * kQc * r + i >= w1) wv[i] = 0u;
 }
 
 // Selection bitmap sel (and, if ties > 0, the tie bitmap tie: keys equal to
-// the threshold) of one sequence -> the ids in ascending order: the lowest
-// `ties` tie slots join the selection, then every thread owns a contiguous
-// run of words and writes its ids at its prefix-count position; -1 pads the
-// row to k.  The bitmaps are in LDS or (kGlobal) in global memory; a global
-// tie bitmap is left zero.
-template <bool kGlobal>
-__device__ void finish_output(uint32_t* sel, uint32_t* tie, int words, uint32_t ties, uint32_t kk,
-                              const int32_t* pool_lds, int32_t blk, uint32_t* wave_sum, int32_t* __restrict__ ob) {
+// the threshold) of one sequence, in LDS -> the ids in ascending order: the
+// lowest `ties` tie slots join the selection, then every thread owns a
+// contiguous run of words and writes its ids at its prefix-count position;
+// -1 pads the row to k.
+__device__ void finish_output_lds(uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
+                                  const int32_t* pool_lds, int32_t blk, uint32_t* wave_sum,
+                                  int32_t* __restrict__ ob) {
   const int tid = threadIdx.x;
   const int per = (words + kFinalThreads - 1) / kFinalThreads;
   const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
   if (ties > 0) {
     uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(bm_load<kGlobal>(&tie[w]));
+    for (int w = w0; w < w1; ++w) cnt += __popc(tie[w]);
     uint32_t dummy;
     uint32_t rank = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &dummy);
     for (int w = w0; w < w1 && rank < ties; ++w) {
-      uint32_t x = bm_load<kGlobal>(&tie[w]);
+      uint32_t x = tie[w];
       const uint32_t pc = __popc(x);
       if (rank + pc <= ties) {
-        bm_store<kGlobal>(&sel[w], bm_load<kGlobal>(&sel[w]) | x);
+        sel[w] |= x;
       } else {
         uint32_t keep = 0;
         for (uint32_t m = rank; m < ties; ++m) {
           keep |= x & (0u - x);
           x &= x - 1;
         }
-        bm_store<kGlobal>(&sel[w], bm_load<kGlobal>(&sel[w]) | keep);
+        sel[w] |= keep;
       }
       rank += pc;
     }
-    if (kGlobal)
-      for (int w = w0; w < w1; ++w) bm_store<true>(&tie[w], 0u);
     __syncthreads();
   }
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(bm_load<kGlobal>(&sel[w]));
+  for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
   uint32_t n_sel;
   uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &n_sel);
   for (int w = w0; w < w1; ++w) {
-    uint32_t x = bm_load<kGlobal>(&sel[w]);
+    uint32_t x = sel[w];
     while (x) {
       const int bit = __ffs(x) - 1;
       x &= x - 1;
@@ -303,6 +308,100 @@ __device__ void finish_output(uint32_t* sel, uint32_t* tie, int words, uint32_t 
       if (pool_lds) id = (int64_t)pool_lds[slot / blk] * blk + slot % blk;
       if (pos < kk) ob[pos] = (int32_t)id;
       ++pos;
+    }
+  }
+  for (uint32_t i = n_sel + tid; i < kk; i += kFinalThreads) ob[i] = -1;
+}
+
+// Words w0 + 16*r + i (i < 16) of a global bitmap: four 16-byte groups of
+// round r of a thread's run, loaded together (clamped to the last group,
+// which exists), words at or past w1 read as 0.
+__device__ __forceinline__ void load_round(const uint32_t* bm, int q0, int r, int qmax, int w0, int w1,
+                                           uint32_t (&wv)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(bm)[min(q0 + 4 * r + j, qmax)];
+    wv[4 * j] = v[0], wv[4 * j + 1] = v[1], wv[4 * j + 2] = v[2], wv[4 * j + 3] = v[3];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (w0 + 16 * r + i >= w1) wv[i] = 0u;
+}
+
+// The same for bitmaps in global memory (16-byte aligned; inputs longer
+// than the LDS bitmaps), last written by other threads of this workgroup
+// before a barrier or by an earlier kernel.  Every thread owns a contiguous
+// run of 16-byte groups, read in rounds of four groups whose loads are in
+// flight together: a prefix count over the tie words adds the lowest `ties`
+// tie slots to the thread's own sel words, then a prefix count over the sel
+// words gives each thread the output position of its ids.
+__device__ void finish_output_global(uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
+                                     const int32_t* pool_lds, int32_t blk, uint32_t* wave_sum,
+                                     int32_t* __restrict__ ob) {
+  const int tid = threadIdx.x;
+  const int nq = (words + 3) / 4;
+  const int perq = (nq + kFinalThreads - 1) / kFinalThreads;
+  const int rounds = (perq + 3) / 4;
+  const int q0 = min(nq, tid * perq);
+  const int qmax = max(nq - 1, 0);
+  const int w0 = 4 * q0, w1 = min(words, 4 * (q0 + perq));  // this thread's words
+  uint32_t wv[16];
+  if (ties > 0) {
+    uint32_t cnt = 0;
+#pragma unroll 1
+    for (int r = 0; r < rounds; ++r) {
+      load_round(tie, q0, r, qmax, w0, w1, wv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cnt += __popc(wv[i]);
+    }
+    uint32_t dummy;
+    uint32_t rank = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &dummy);
+#pragma unroll 1
+    for (int r = 0; r < rounds && rank < ties; ++r) {
+      load_round(tie, q0, r, qmax, w0, w1, wv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t x = wv[i];
+        const uint32_t pc = __popc(x);
+        if (rank < ties && x) {
+          uint32_t keep = x;
+          if (rank + pc > ties) {
+            keep = 0;
+            for (uint32_t m = rank; m < ties; ++m) {
+              keep |= x & (0u - x);
+              x &= x - 1;
+            }
+          }
+          sel[w0 + 16 * r + i] |= keep;  // the thread's own word
+        }
+        rank += pc;
+      }
+    }
+  }
+  uint32_t cnt = 0;
+#pragma unroll 1
+  for (int r = 0; r < rounds; ++r) {
+    load_round(sel, q0, r, qmax, w0, w1, wv);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cnt += __popc(wv[i]);
+  }
+  uint32_t n_sel;
+  uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &n_sel);
+#pragma unroll 1
+  for (int r = 0; r < rounds && pos < kk; ++r) {
+    load_round(sel, q0, r, qmax, w0, w1, wv);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t x = wv[i];
+      while (x) {
+        const int bit = __ffs(x) - 1;
+        x &= x - 1;
+        const int64_t slot = (int64_t)(w0 + 16 * r + i) * 32 + bit;
+        int64_t id = slot;
+        if (pool_lds) id = (int64_t)pool_lds[slot / blk] * blk + slot % blk;
+        if (pos < kk) ob[pos] = (int32_t)id;
+        ++pos;
+      }
     }
   }
   for (uint32_t i = n_sel + tid; i < kk; i += kFinalThreads) ob[i] = -1;
@@ -321,7 +420,7 @@ struct FinalSmem {
 
 // kGlobal: the selection and tie bitmaps stay in global memory (inputs of
 // more than kTopkLdsWords * 32 slots): the filter pass's bitmap is marked in
-// place and the tie bitmap is cleared here and left clear.
+// place and the tie bitmap is cleared here first.
 template <bool kGlobal>
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* __restrict__ scores, int64_t n,
                                                                    const int32_t* __restrict__ lens,
@@ -335,7 +434,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
   const int tid = threadIdx.x;
   const int nvalid = (int)valid_slots(n, lens, len_div, b);
   const int words = (nvalid + 31) / 32;
-  const bool direct = n <= kDirectMax;
+  const bool direct = !kGlobal && n <= kDirectMax;  // kGlobal inputs are longer
   const float* sc = scores + (int64_t)b * n;
   const uint32_t kk = (uint32_t)k;
   uint32_t* gh = ws.hist + (int64_t)b * kTopkBins;
@@ -368,7 +467,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
   const bool buffered = th.in_bin <= (uint32_t)kTopkCandCap;
   uint32_t* sel = kGlobal ? ws.bits + (int64_t)b * ws.words_cap : sm.sel;
   uint32_t* tie = kGlobal ? ws.tie + (int64_t)b * ws.words_cap : sm.tie;
-  for (int i = tid; i < words; i += kFinalThreads) bm_store<kGlobal>(&tie[i], 0u);
+  for (int i = tid; i < words; i += kFinalThreads) tie[i] = 0u;
   if (direct) {
     // Filter pass in this workgroup (scores already loaded).
     constexpr int kPer = kPerDirect;
@@ -488,8 +587,10 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
     __syncthreads();
   }
 
-  finish_output<kGlobal>(sel, tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
-                         out + (int64_t)b * k);
+  if constexpr (kGlobal)
+    finish_output_global(sel, tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum, out + (int64_t)b * k);
+  else
+    finish_output_lds(sel, tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum, out + (int64_t)b * k);
 }
 
 
@@ -497,7 +598,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
 // workgroup, the scores held in registers (kPer per thread): three histogram
 // passes over the keys in LDS (digits of 12, 12 and 8 bits) find the exact
 // k-th key T, then selection and tie bitmaps are written by ballots and
-// finish_output emits the ids.  Reads every score once; used when no
+// finish_output_lds emits the ids.  Reads every score once; used when no
 // histogram was produced upstream (many sequences of moderate length).
 constexpr int kRowsMax = 64 * kFinalThreads;  // 65,536 slots
 static_assert(kRowsMax == kTopkRowsMax, "register-resident selection length");
@@ -602,32 +703,37 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
     }
   }
   __syncthreads();
-  finish_output<false>(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
-                       out + (int64_t)b * k);
+  finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+                    out + (int64_t)b * k);
 }
 
 }  // namespace
 
+// Bitmap words per sequence: a multiple of 4, so that every sequence's
+// bitmap is 16-byte aligned.
+static int64_t bitmap_words(int64_t n) { return ((n + 31) / 32 + 3) / 4 * 4; }
+
 size_t topk_workspace_bytes(int64_t n, int32_t n_seq) {
-  const int64_t words = (n + 31) / 32;
-  const int64_t tie_words = words > kTopkLdsWords ? words : 0;
-  return (size_t)n_seq * (kTopkBins * sizeof(uint32_t) + sizeof(uint32_t) + (words + tie_words) * sizeof(uint32_t) +
-                          kTopkCandCap * sizeof(uint2)) + 64;
+  const int64_t words = bitmap_words(n);
+  const int64_t tie_words = (n + 31) / 32 > kTopkLdsWords ? words : 0;
+  return (size_t)n_seq * (kCandBytes + kTopkBins * sizeof(uint32_t) + (words + tie_words) * sizeof(uint32_t) +
+                          sizeof(uint32_t)) + 64;
 }
 
+// Layout: cand, hist, bits, tie (long inputs), cnt; ws is 16-byte aligned.
 TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq) {
   TopkWs w;
   char* p = reinterpret_cast<char*>(ws);
   w.cand = reinterpret_cast<uint2*>(p);
-  p += (size_t)n_seq * kTopkCandCap * sizeof(uint2);
+  p += (size_t)n_seq * kCandBytes;
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += (size_t)n_seq * kTopkBins * sizeof(uint32_t);
-  w.cnt = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)n_seq * sizeof(uint32_t);
-  w.words_cap = (n + 31) / 32;
+  w.words_cap = bitmap_words(n);
   w.bits = reinterpret_cast<uint32_t*>(p);
   p += (size_t)n_seq * w.words_cap * sizeof(uint32_t);
   w.tie = reinterpret_cast<uint32_t*>(p);  // used (and sized) only past kTopkLdsWords words
+  if ((n + 31) / 32 > kTopkLdsWords) p += (size_t)n_seq * w.words_cap * sizeof(uint32_t);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
