@@ -94,18 +94,4 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // Scores that are not candidates.
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// ------------------------------------------------------- layer batches
-// Layers that attend over the same indices and main KV -- a layer and the
-// Reuse layers right after it on the same tensor -- run as one attention
-// launch of up to kAttnMaxLayers layers.  Returns one past the last layer
-// of the batch that starts at layer l.
-constexpr int kAttnMaxLayers = 8;
-inline int attn_batch_end(const csa2_layer* layers, int n_layers, int l) {
-  int e = l + 1;
-  while (e < n_layers && e - l < kAttnMaxLayers && layers[e].mode == CSA2_REUSE &&
-         layers[e].kv_id == layers[l].kv_id)
-    ++e;
-  return e;
-}
-
 }  // namespace csa2

@@ -10,7 +10,6 @@
 // Limits of KV Cache Compression".
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
 #include <string>
 
 #include "common.hpp"
@@ -21,9 +20,8 @@ namespace csa2 {
 csa2_status prefill_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, int64_t, int32_t,
                                  int32_t, float*, int32_t*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
-csa2_status attn_launch_layers(int32_t, const uint16_t* const*, int32_t, const csa2_fp4_kv&, int32_t,
-                               const int32_t*, int32_t, const void* const*, bool, int64_t, const int32_t*, int32_t,
-                               float, float* const*, void*, hipStream_t);
+csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
+                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
 
 namespace {
@@ -55,13 +53,7 @@ PrefillWs prefill_ws_layout(const csa2_prefill_desc& d, void* base) {
   w.topk = reinterpret_cast<void*>(p + off);
   off += align_up(topk_workspace_bytes(d.n_entries, d.n_q));
   w.attn = reinterpret_cast<void*>(p + off);
-  size_t attn_bytes = 0;  // partials of the largest layer batch
-  for (int l = 0; l < d.n_layers;) {
-    const int e = attn_batch_end(d.layers, d.n_layers, l);
-    for (int m = 1; m <= e - l; ++m) attn_bytes = std::max(attn_bytes, attn_workspace_bytes(d.n_q * m, d.topk, d.swa));
-    l = e;
-  }
-  off += align_up(attn_bytes);
+  off += align_up(attn_workspace_bytes(d.n_q, d.topk, d.swa));
   w.bytes = off;
   return w;
 }
@@ -167,7 +159,7 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
   const hipStream_t stream = as_stream(stream_v);
   const TopkWs tw = topk_ws_carve(w.topk, d.n_entries, d.n_q);
   const int32_t* cur = nullptr;
-  for (int l = 0; l < d.n_layers;) {
+  for (int l = 0; l < d.n_layers; ++l) {
     const csa2_layer& L = d.layers[l];
     if (L.mode != CSA2_REUSE) {
       // Full and Reindex both score every visible entry with their own Q.
@@ -180,15 +172,10 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
       if (st != CSA2_OK) return st;
       cur = io->idx[l];
     }
-    // This layer and the Reuse layers after it on the same tensor attend in
-    // one launch; query i's window rows start at row i of each layer's SWA
-    // buffer.
-    const int e = attn_batch_end(d.layers, d.n_layers, l);
-    st = attn_launch_layers(e - l, io->main_q + l, d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk,
-                            reinterpret_cast<const void* const*>(io->swa + l), false,
-                            1, w.win_len, d.swa, d.sm_scale, io->out + l, w.attn, stream);
+    // Query i's window rows start at row i of the layer's SWA buffer.
+    st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, io->swa[l], false, 1, w.win_len,
+                     d.swa, d.sm_scale, io->out[l], w.attn, stream);
     if (st != CSA2_OK) return st;
-    l = e;
   }
   return CSA2_OK;
 }

@@ -22,9 +22,8 @@ csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, i
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
                                uint32_t*, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
-csa2_status attn_launch_layers(int32_t, const uint16_t* const*, int32_t, const csa2_fp4_kv&, int32_t,
-                               const int32_t*, int32_t, const void* const*, bool, int64_t, const int32_t*, int32_t,
-                               float, float* const*, void*, hipStream_t);
+csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
+                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
 csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, int64_t, int32_t, const int32_t*,
                                int32_t*, int32_t, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
@@ -161,13 +160,7 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
     }
     s->scores_n = std::max<int64_t>(s->scores_n, d.key_cap);
   }
-  // Partials of the largest attention batch (its queries: n_seq per layer).
-  for (int l = 0; l < d.n_layers;) {
-    const int e = attn_batch_end(s->layers.data(), d.n_layers, l);
-    for (int m = 1; m <= e - l; ++m)
-      s->attn_ws_bytes = std::max(s->attn_ws_bytes, attn_workspace_bytes(d.n_seq * m, d.topk, d.swa_max));
-    l = e;
-  }
+  s->attn_ws_bytes = attn_workspace_bytes(d.n_seq, d.topk, d.swa_max);
   s->topk_ws_bytes = topk_workspace_bytes(s->scores_n, d.n_seq);
   const size_t n = (size_t)d.n_seq;
   if ((st = dev_alloc(&s->idx_bufs, (size_t)s->n_idx_bufs * n * d.topk * sizeof(int32_t))) != CSA2_OK ||
@@ -234,7 +227,7 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
   }
 
   const size_t idx_stride = (size_t)d.n_seq * d.topk;
-  for (int l = 0; l < d.n_layers;) {
+  for (int l = 0; l < d.n_layers; ++l) {
     const csa2_layer& L = s->layers[l];
     int32_t* idx = s->idx_bufs + idx_stride * s->idx_buf_of_layer[l];
     // Indexer K of this layer's Full layer (itself, or the one a Reindex
@@ -276,15 +269,10 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
                            stream);
       }
     }
-    // This layer and the Reuse layers after it on the same tensor attend in
-    // one launch.
-    const int e = attn_batch_end(s->layers.data(), d.n_layers, l);
     if (st == CSA2_OK)
-      st = attn_launch_layers(e - l, io->main_q + l, d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa + l,
-                              d.swa_fp8 != 0, d.swa_max, io->swa_len, d.swa_max, d.sm_scale, io->out + l,
-                              s->attn_ws, stream);
+      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l], d.swa_fp8 != 0,
+                       d.swa_max, io->swa_len, d.swa_max, d.sm_scale, io->out[l], s->attn_ws, stream);
     if (st != CSA2_OK) return st;
-    l = e;
   }
   return CSA2_OK;
 }

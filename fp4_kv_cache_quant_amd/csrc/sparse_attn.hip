@@ -142,14 +142,6 @@ struct AttnTile {
   bool swa, in_range, ok;
 };
 
-// Per-layer tensors of a batch of layers that attend over the same indices
-// and main KV (a selecting layer and the Reuse layers that follow it).
-struct AttnLayers {
-  const uint16_t* q[kAttnMaxLayers];
-  const uint8_t* swa[kAttnMaxLayers];
-  float* out[kAttnMaxLayers];
-};
-
 struct AttnArgs {
   int qb;  // the query this workgroup attends for
   const uint8_t* codes;
@@ -335,21 +327,15 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bo
 // one split the workgroup covers the whole query and writes the normalised
 // output; otherwise it writes its unnormalised O and (max, sum) per head
 // for the combine kernel.
-// Grid (splits, n_q, layers): blockIdx.z picks the layer of the batch,
-// whose main Q, window rows and output come from `lay`; the indices, main
-// KV and window lengths are shared by the layers of the batch.
 template <int W, bool kWin8>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
-    AttnLayers lay, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t cap, int32_t q_per_seq,
-    const int32_t* __restrict__ idx, int32_t k_idx,
+    const int32_t* __restrict__ idx, int32_t k_idx, const uint8_t* __restrict__ swa,
     int64_t swa_q_stride_rows, const int32_t* __restrict__ swa_len, int32_t swa_max,
     float scale_log2, int32_t per_split, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int32_t n_split) {
+    int32_t n_split, float* __restrict__ out) {
   using Cfg = AttnCfg<W>;
-  const uint16_t* __restrict__ q = lay.q[blockIdx.z];
-  const uint8_t* __restrict__ swa = lay.swa[blockIdx.z];
-  float* __restrict__ out = lay.out[blockIdx.z];
   __shared__ __attribute__((aligned(16))) AttnSmem<W> sm;
   constexpr int kSlices = Cfg::kSlices;
   const int split = blockIdx.x;
@@ -461,8 +447,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     }
     return;
   }
-  const int64_t qg = (int64_t)blockIdx.z * gridDim.y + qb;  // query of the batch
-  float* po = part_o + (qg * n_split + split) * (16 * CSA2_LATENT);
+  float* po = part_o + ((int64_t)qb * n_split + split) * (16 * CSA2_LATENT);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int head = 4 * g + j;
@@ -473,23 +458,21 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
           f32x4{st.o[4 * sl][j], st.o[4 * sl + 1][j], st.o[4 * sl + 2][j], st.o[4 * sl + 3][j]};
     }
   }
-  if (tid < 16) part_ml[(qg * n_split + split) * 16 + tid] = make_float2(st.m_run, st.l_run);
+  if (tid < 16) part_ml[((int64_t)qb * n_split + split) * 16 + tid] = make_float2(st.m_run, st.l_run);
 }
 
 // Merge the chunks of one (head, query) with log-sum-exp weights:
 //   o_h = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
-// One 128-thread workgroup per (head, query, layer), one float4 of the
-// head's 512 channels per thread.  The chunks are taken in batches of 16
-// whose loads (partial O and (m, l), clamped addresses) are all issued
-// together; a running maximum rescales across batches.
+// One 128-thread workgroup per (head, query), one float4 of the head's 512
+// channels per thread.  The chunks are taken in batches of 16 whose loads
+// (partial O and (m, l), clamped addresses) are all issued together; a
+// running maximum rescales across batches.
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml,
-                                                           int32_t n_split, AttnLayers lay) {
+                                                           int32_t n_split, float* __restrict__ out) {
   const int h = blockIdx.x, qb = blockIdx.y, tid = threadIdx.x;
-  float* __restrict__ out = lay.out[blockIdx.z];
-  const int64_t qg = (int64_t)blockIdx.z * gridDim.y + qb;
-  const float2* ml = part_ml + qg * n_split * 16 + h;
-  const f32x4* pall = reinterpret_cast<const f32x4*>(part_o + qg * n_split * (16 * CSA2_LATENT) + h * CSA2_LATENT) + tid;
+  const float2* ml = part_ml + (int64_t)qb * n_split * 16 + h;
+  const f32x4* pall = reinterpret_cast<const f32x4*>(part_o + (int64_t)qb * n_split * (16 * CSA2_LATENT) + h * CSA2_LATENT) + tid;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f, Mq = kNegInf;
   constexpr int kB = 16;
@@ -547,7 +530,6 @@ static AttnPlan attn_plan(int32_t n_q, int32_t k_idx, int32_t swa_max) {
   return p;
 }
 
-// n_q: queries of all layers of a call (queries per layer x layers).
 size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
   const AttnPlan p = attn_plan(n_q, k_idx, swa_max);
   if (p.splits == 1) return 0;
@@ -557,67 +539,46 @@ size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
 }
 
 template <bool kWin8>
-static void attn_dispatch(const AttnPlan& p, int32_t n_q, int32_t n_layers, const AttnLayers& lay,
-                          const csa2_fp4_kv& kv, int32_t q_per_seq, const int32_t* idx, int32_t k_idx,
+static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, const csa2_fp4_kv& kv,
+                          int32_t q_per_seq, const int32_t* idx, int32_t k_idx, const uint8_t* swa,
                           int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
-                          float* part_o, float2* part_ml, hipStream_t stream) {
-  const dim3 grid(p.splits, n_q, n_layers);
+                          float* part_o, float2* part_ml, float* out, hipStream_t stream) {
   if (p.waves == 8)
-    hipLaunchKernelGGL((attn_kernel<8, kWin8>), grid, dim3(64 * 8), 0, stream, lay, kv.codes, kv.scales, kv.cap,
-                       q_per_seq, idx, k_idx, swa_q_stride_rows, swa_len, swa_max, scale_log2, p.per_split, part_o,
-                       part_ml, p.splits);
+    hipLaunchKernelGGL((attn_kernel<8, kWin8>), dim3(p.splits, n_q), dim3(64 * 8), 0, stream, q, kv.codes,
+                       kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+                       scale_log2, p.per_split, part_o, part_ml, p.splits, out);
   else
-    hipLaunchKernelGGL((attn_kernel<4, kWin8>), grid, dim3(64 * 4), 0, stream, lay, kv.codes, kv.scales, kv.cap,
-                       q_per_seq, idx, k_idx, swa_q_stride_rows, swa_len, swa_max, scale_log2, p.per_split, part_o,
-                       part_ml, p.splits);
+    hipLaunchKernelGGL((attn_kernel<4, kWin8>), dim3(p.splits, n_q), dim3(64 * 4), 0, stream, q, kv.codes,
+                       kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+                       scale_log2, p.per_split, part_o, part_ml, p.splits, out);
 }
 
-// n_layers (1 .. kAttnMaxLayers) layers attend in one launch: layer l has
-// its own main Q q[l] [n_q][16][512], window rows swa[l] and output out[l];
-// all share idx, the main KV and swa_len.  ws holds the partials of
-// n_q * n_layers queries.  swa_fp8: window rows are E4M3 bytes [*][512]
-// instead of bf16 [*][512].
-csa2_status attn_launch_layers(int32_t n_layers, const uint16_t* const* q, int32_t n_q, const csa2_fp4_kv& kv,
-                               int32_t q_per_seq, const int32_t* idx, int32_t k_idx, const void* const* swa,
-                               bool swa_fp8, int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
-                               float sm_scale, float* const* out, void* ws, hipStream_t stream) {
-  if (n_q == 0 || n_layers == 0) return CSA2_OK;
-  CSA2_REQUIRE(n_layers >= 1 && n_layers <= kAttnMaxLayers, CSA2_EINVAL, "attention: too many layers in one batch");
-  AttnLayers lay{};
-  for (int l = 0; l < n_layers; ++l) {
-    lay.q[l] = q[l];
-    lay.swa[l] = reinterpret_cast<const uint8_t*>(swa[l]);
-    lay.out[l] = out[l];
-  }
-  const int32_t n_all = n_q * n_layers;
-  const AttnPlan p = attn_plan(n_all, k_idx, swa_max);
+// swa_fp8: window rows are E4M3 bytes [*][512] instead of bf16 [*][512].
+csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
+                        const int32_t* idx, int32_t k_idx, const void* swa, bool swa_fp8,
+                        int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float sm_scale,
+                        float* out, void* ws, hipStream_t stream) {
+  if (n_q == 0) return CSA2_OK;
+  const AttnPlan p = attn_plan(n_q, k_idx, swa_max);
   float* part_o = nullptr;
   float2* part_ml = nullptr;
   if (p.splits > 1) {
     char* base = reinterpret_cast<char*>(ws);
     part_o = reinterpret_cast<float*>(base);
-    base += (size_t)n_all * p.splits * 16 * CSA2_LATENT * sizeof(float);
+    base += (size_t)n_q * p.splits * 16 * CSA2_LATENT * sizeof(float);
     part_ml = reinterpret_cast<float2*>(base);
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
   if (swa_fp8)
-    attn_dispatch<true>(p, n_q, n_layers, lay, kv, q_per_seq, idx, k_idx, swa_q_stride_rows, swa_len, swa_max,
-                        scale_log2, part_o, part_ml, stream);
+    attn_dispatch<true>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max, scale_log2,
+                        part_o, part_ml, out, stream);
   else
-    attn_dispatch<false>(p, n_q, n_layers, lay, kv, q_per_seq, idx, k_idx, swa_q_stride_rows, swa_len, swa_max,
-                         scale_log2, part_o, part_ml, stream);
+    attn_dispatch<false>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                         scale_log2, part_o, part_ml, out, stream);
   if (p.splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q, n_layers), dim3(128), 0, stream, part_o, part_ml,
-                       p.splits, lay);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, p.splits, out);
   return launch_status("csa2_sparse_attn");
-}
-
-csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
-                        const int32_t* idx, int32_t k_idx, const void* swa, bool swa_fp8,
-                        int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float sm_scale,
-                        float* out, void* ws, hipStream_t stream) {
-  return attn_launch_layers(1, &q, n_q, kv, q_per_seq, idx, k_idx, &swa, swa_fp8, swa_q_stride_rows, swa_len,
-                            swa_max, sm_scale, &out, ws, stream);
 }
 
 }  // namespace csa2

@@ -74,7 +74,7 @@ CHUNKS = {
     # a one-token window from token 0: the first queries see no entry at all
     # (the window alone is attended)
     "no_entries_swa1": _small(n_entries=50, n_q=40, t0=0, ratio=3, swa=1),
-    # a Reuse run longer than one attention launch (8 layers)
+    # a long Reuse run
     "long_reuse": _small(n_entries=700, n_q=30, t0=2 * 700 - 30,
                          layers=((C.FULL, 0, 0),) + ((C.REUSE, 0, 0),) * 9),
 }
