@@ -37,22 +37,38 @@ PEAK_HBM_GBPS = 8000.0
 # the kernel sources they were taken on: a figure is reported only while
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
-    "sparse_attn": {"bytes": 12767720, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
-                    "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                                "e048ff920a55b78fcc23a9bed24e46539ccc4d466116c4af3fc4c57d098f1932",
-                                "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                                "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
-    "block_scan": {"bytes": 280649850, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
-                   "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                               "2805cdc75311ed99d69ed6cc28b98a17c2d8618c448ac40e07f5dd6cccddb000",
-                               "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                               "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
+    "decoder20_1m/sparse_attn": {
+        "bytes": 12761571, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
+                    "63835a0e06c0fb5eb4e1981412f7b45241c67e900a25e7de599ec2584e830b43",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
+    "decoder20_1m/block_scan": {
+        "bytes": 280622264, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                    "2805cdc75311ed99d69ed6cc28b98a17c2d8618c448ac40e07f5dd6cccddb000",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
+    "encoder_1m/flat_score": {
+        "bytes": 1126701607, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                    "2805cdc75311ed99d69ed6cc28b98a17c2d8618c448ac40e07f5dd6cccddb000",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
 }
 
 
+def config_key(cfg):
+    """The DECODE_CONFIGS key of cfg (matched by name), or None."""
+    from synth.configs import DECODE_CONFIGS
+
+    return next((k for k, c in DECODE_CONFIGS.items() if c.name == cfg.name), None)
+
+
 def measured_traffic(op_key: str):
-    """Counter-measured HBM bytes per call of op_key, or None when unmeasured
-    or when its kernel sources changed since the counters were taken."""
+    """Counter-measured HBM bytes per call of op_key ("workload/op"), or None
+    when unmeasured or when its kernel sources changed since the counters
+    were taken."""
     import hashlib
 
     rec = MEASURED_TRAFFIC.get(op_key)
@@ -99,9 +115,10 @@ def algorithmic_bytes(cfg, L: int) -> dict:
     return parts
 
 
-def cpu_baseline(cfg, step: int, seqs, threads: int):
+def cpu_baseline(cfg, step: int, seqs, threads: int, reps: int = 1):
     """Oracle (as it stands) on one full decode step of `seqs`: inputs are
-    regenerated first (not timed), then the oracle's layer walk is timed."""
+    regenerated first (not timed), then the oracle's layer walk over all of
+    them is timed `reps` times (dt is the total)."""
     from concurrent.futures import ThreadPoolExecutor
 
     from oracle import workloads as ow
@@ -122,7 +139,8 @@ def cpu_baseline(cfg, step: int, seqs, threads: int):
 
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
-        res = dict(ex.map(run, seqs))
+        for _ in range(reps):
+            res = dict(ex.map(run, seqs))
     dt = time.perf_counter() - t0
     return res, dt
 
@@ -217,7 +235,7 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
                     "avg_us": round(us, 2), "us_per_step": round(us * per_step, 1),
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                    "traffic_bytes": measured_traffic(key) if cfg.name == DECODE_CONFIGS["decoder20_1m"].name else None})
+                    "traffic_bytes": measured_traffic(f"{config_key(cfg)}/{key}")})
     return res
 
 
@@ -257,7 +275,8 @@ def flat_op_rooflines(cfg, inp, graph: bool = True):
         res.append({"key": key, "op": name, "launches_per_step": per_step, "bytes_per_launch": nbytes,
                     "avg_us": round(us, 2), "us_per_step": round(us * per_step, 1),
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-                    "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
+                    "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                    "traffic_bytes": measured_traffic(f"{config_key(cfg)}/{key}")})
     return res
 
 
@@ -472,6 +491,10 @@ def encoder_decode_leg(K: int, W: int, graph: bool, cpu_seqs: int) -> dict:
     sched.close()
     r = _time_steps(cfg, inp, K, W, graph)
     r["ops"] = flat_op_rooflines(cfg, inp, graph=graph)
+    dom = max(r["ops"], key=lambda o: o["us_per_step"])
+    r["roofline"] = {"op": dom["key"], "bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": dom["traffic_bytes"]}
     if cpu_seqs > 0:
         seqs = sorted({0, cfg.n_seq - 1} if cpu_seqs > 1 else {0})
         threads = max(1, min(len(seqs), len(os.sched_getaffinity(0)), 16))
@@ -515,6 +538,7 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch each step eagerly")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-reps", type=int, default=8, help="times the CPU oracle sample is timed")
     ap.add_argument("--config", default="decoder20_1m")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--no-fp8-window", action="store_true", help="skip the FP8-window variant of the step")
@@ -608,19 +632,19 @@ def main() -> int:
     dom = max(ops, key=lambda o: o["us_per_step"])
     roofline = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
-                "traffic": measured_traffic(dom["key"]) if cfg.name == DECODE_CONFIGS["decoder20_1m"].name else None}
+                "traffic": measured_traffic(f"{config_key(cfg)}/{dom['key']}")}
 
     # CPU oracle on a bounded sample: step 0 of the first cpu_seqs sequences.
     cpu = parity = None
     if not args.no_cpu:
         threads = max(1, min(args.cpu_seqs, len(os.sched_getaffinity(0)), 16))
         seqs = list(range(min(args.cpu_seqs, cfg.n_seq)))
-        res, dt = cpu_baseline(cfg, 0, seqs, threads)
-        cpu = {"value": round(len(seqs) * nl / dt, 2), "unit": "(seq·layer)-steps/s", "cores": threads,
-               "kind": "oracle",
+        res, dt = cpu_baseline(cfg, 0, seqs, threads, reps=args.cpu_reps)
+        cpu = {"value": round(args.cpu_reps * len(seqs) * nl / dt, 2), "unit": "(seq·layer)-steps/s",
+               "cores": threads, "kind": "oracle",
                "sample": f"decode step 0 of {len(seqs)} of {cfg.n_seq} sequences, all {nl} layers "
                          f"({sum(1 for m, _, _ in cfg.layers if m != 2)} selecting layers, {nl} attentions), "
-                         f"{dt:.1f} s"}
+                         f"timed {args.cpu_reps} times: {dt:.1f} s"}
         parity = compare_step(cfg, gpu0, res)
 
     fp8w = keys = None
