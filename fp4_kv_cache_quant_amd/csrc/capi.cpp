@@ -22,7 +22,7 @@ csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, i
                                uint32_t*, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+                        const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
 
 namespace {
 thread_local std::string g_error;
@@ -184,7 +184,7 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
   clear_error();
   csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_len, swa_max, out, ws, ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;
-  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, false, swa_q_stride_rows, swa_len, swa_max,
+  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinBf16, swa_q_stride_rows, swa_len, swa_max,
                      sm_scale, out, ws, as_stream(stream));
 }
 
@@ -195,7 +195,7 @@ csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_
   clear_error();
   csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_len, swa_max, out, ws, ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;
-  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, true, swa_q_stride_rows, swa_len, swa_max,
+  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinE4m3, swa_q_stride_rows, swa_len, swa_max,
                      sm_scale, out, ws, as_stream(stream));
 }
 

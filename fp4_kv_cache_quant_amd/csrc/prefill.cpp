@@ -21,7 +21,8 @@ csa2_status prefill_score_launch(const uint16_t*, const float*, const uint16_t*,
                                  int32_t, float*, int32_t*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+                        const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+csa2_status win_f16_launch(const uint16_t*, int64_t, uint16_t*, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
 
 namespace {
@@ -30,13 +31,16 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout: scores [n_q][n_entries] f32 | n_vis [n_q] | win_len
-// [n_q] | Top-k workspace | attention workspace.
+// [n_q] | Top-k workspace | attention workspace | the layer's window rows
+// as f16 [n_q + swa - 1][512] (each row serves up to swa queries, so it is
+// converted once per layer instead of once per query).
 struct PrefillWs {
   float* scores;
   int32_t* n_vis;
   int32_t* win_len;
   void* topk;
   void* attn;
+  uint16_t* win16;
   size_t bytes;
 };
 
@@ -54,6 +58,8 @@ PrefillWs prefill_ws_layout(const csa2_prefill_desc& d, void* base) {
   off += align_up(topk_workspace_bytes(d.n_entries, d.n_q));
   w.attn = reinterpret_cast<void*>(p + off);
   off += align_up(attn_workspace_bytes(d.n_q, d.topk, d.swa));
+  w.win16 = reinterpret_cast<uint16_t*>(p + off);
+  off += align_up(((size_t)d.n_q + d.swa - 1) * CSA2_LATENT * sizeof(uint16_t));
   w.bytes = off;
   return w;
 }
@@ -172,9 +178,12 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
       if (st != CSA2_OK) return st;
       cur = io->idx[l];
     }
-    // Query i's window rows start at row i of the layer's SWA buffer.
-    st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, io->swa[l], false, 1, w.win_len,
-                     d.swa, d.sm_scale, io->out[l], w.attn, stream);
+    // Query i's window rows start at row i of the layer's SWA buffer; the
+    // rows go to f16 once for all the queries that share them.
+    st = win_f16_launch(io->swa[l], (int64_t)d.n_q + d.swa - 1, w.win16, stream);
+    if (st == CSA2_OK)
+      st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, w.win16, kWinF16, 1, w.win_len,
+                       d.swa, d.sm_scale, io->out[l], w.attn, stream);
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;

@@ -23,7 +23,7 @@ csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, i
                                uint32_t*, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const void*, bool, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+                        const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
 csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, int64_t, int32_t, const int32_t*,
                                int32_t*, int32_t, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
@@ -270,7 +270,7 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       }
     }
     if (st == CSA2_OK)
-      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l], d.swa_fp8 != 0,
+      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l], d.swa_fp8 ? kWinE4m3 : kWinBf16,
                        d.swa_max, io->swa_len, d.swa_max, d.sm_scale, io->out[l], s->attn_ws, stream);
     if (st != CSA2_OK) return st;
   }

@@ -77,24 +77,6 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
 }
 
-// E4M3FN scale byte as binary32 (sign, NaN for S.1111.111), without
-// branches: exponent field 0 is subnormal (m * 2^-9), otherwise the
-// binary32 pattern is ((e + 120) << 23) | (m << 20).
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const uint32_t normal = ((e + 120u) << 23) | (m << 20);
-  const uint32_t sub = __builtin_bit_cast(uint32_t, (float)m * 0.001953125f);
-  uint32_t bits = e ? normal : sub;
-  bits = ((c & 0x7Fu) == 0x7Fu) ? 0x7FC00000u : bits;
-  return __builtin_bit_cast(float, bits | ((c & 0x80u) << 24));
-}
-
-// The E4M3 scale as an f16 pair (exact: every E4M3 value is an f16 normal).
-__device__ __forceinline__ f16x2 e4m3_f16x2(uint32_t c) {
-  const _Float16 h = (_Float16)e4m3_value(c);
-  return f16x2{h, h};
-}
-
 // With 8 wavefronts (one workgroup per CU) main Q is staged once in LDS and
 // the next chunk's rows are loaded while the current one is computed; with
 // 4 wavefronts (two workgroups per CU) Q stays in registers and the other
@@ -176,8 +158,8 @@ __device__ __forceinline__ void tile_begin(AttnTile& t, const AttnArgs& a, int c
 
 // The row loads of a tile (unconditional, clamped addresses: all in flight
 // together).  Window rows are bf16 (16 loads of 16 bytes per lane) or, with
-// kWin8, E4M3 bytes (8 loads).
-template <bool kWin8>
+// kWin == kWinE4m3, E4M3 bytes (8 loads).
+template <int kWin>
 __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n, int g) {
   const int qb = a.qb;
   if (!t.swa) {
@@ -193,11 +175,11 @@ __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n,
   } else {
     const int j = t.row0 + n;
     t.ok = t.in_range && j < a.n_swa;
-    constexpr int kRowBytes = kWin8 ? CSA2_LATENT : 2 * CSA2_LATENT;
+    constexpr int kRowBytes = kWin == kWinE4m3 ? CSA2_LATENT : 2 * CSA2_LATENT;
     const u32x4* sp = reinterpret_cast<const u32x4*>(
         a.swa + ((int64_t)qb * a.swa_q_stride_rows + (t.ok ? j : 0)) * kRowBytes + (kRowBytes / 4) * g);
 #pragma unroll
-    for (int i = 0; i < (kWin8 ? 8 : 16); ++i) t.raw[i] = sp[i];
+    for (int i = 0; i < (kWin == kWinE4m3 ? 8 : 16); ++i) t.raw[i] = sp[i];
   }
 }
 
@@ -211,8 +193,8 @@ __device__ __forceinline__ u32x4 fp8x8_to_f16x8(uint32_t d0, uint32_t d1) {
 
 // Compute one chunk from the loaded tile (`between` runs after the softmax
 // statistics, before the PV product: the next chunk's loads go there).
-template <int W, bool kWin8, typename QB, typename Between>
-__device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bool first, const AttnTile& t,
+template <int W, int kWin, typename QB, typename Between>
+__device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, const AttnTile& t,
                                            const QB& qb_operand, float scale_log2, Between between) {
   constexpr int kRows = AttnCfg<W>::kRows, kPPitch = AttnCfg<W>::kPPitch, kSlices = AttnCfg<W>::kSlices;
   const int tid = threadIdx.x;
@@ -223,18 +205,30 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bo
   // ---- dequantise, stage in LDS, and S^T[row][head] on MFMA
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   if (!t.swa) {
+    // The lane's 8 scale bytes as f16 (exact E4M3 conversions, two per
+    // instruction): sc[i] holds scale bytes 2i (low half) and 2i + 1.
+    uint32_t sc[4];
+    sc[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.x, 1.0f, false));
+    sc[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.x, 1.0f, true));
+    sc[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.y, 1.0f, false));
+    sc[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.y, 1.0f, true));
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const uint32_t sword = (k < 8) ? t.s8.x : t.s8.y;
-      const u32x4 x = dequant8_f16(t.raw[k >> 2][k & 3], e4m3_f16x2((sword >> (8 * ((k >> 1) & 3))) & 0xFFu));
+      // Channels 8k .. 8k+7 of the lane's 128 use scale byte k / 2, splat
+      // into both halves.
+      const uint32_t w = sc[k >> 2];
+      const f16x2 s2 = __builtin_bit_cast(f16x2, ((k >> 1) & 1) ? byte_perm(w, w, 0x03020302u)
+                                                                 : byte_perm(w, w, 0x01000100u));
+      const u32x4 x = dequant8_f16(t.raw[k >> 2][k & 3], s2);
       *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
       s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
     }
   } else {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      u32x4 x = kWin8 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
-                      : bf16x8_to_f16x8(t.raw[k]);
+      u32x4 x = kWin == kWinE4m3 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
+                : kWin == kWinF16 ? t.raw[k]
+                                  : bf16x8_to_f16x8(t.raw[k]);
       if (!t.ok) x = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
       s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
@@ -281,14 +275,14 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bo
   lds_barrier();
   between();
 
-  // ---- O = O * alpha + P X for this wavefront's channel slices
-  if (!first) {
+  // ---- O = O * alpha + P X for this wavefront's channel slices (on the
+  // first chunk O = 0 and alpha = 0: no special case, so that the chunk
+  // loop is not peeled)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a = sm.alpha[4 * g + j];
+  for (int j = 0; j < 4; ++j) {
+    const float a = sm.alpha[4 * g + j];
 #pragma unroll
-      for (int c = 0; c < AttnCfg<W>::kCT; ++c) st.o[c][j] *= a;
-    }
+    for (int c = 0; c < AttnCfg<W>::kCT; ++c) st.o[c][j] *= a;
   }
   if (tid < 16) {
     float l = 0.f;
@@ -327,7 +321,7 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, bo
 // one split the workgroup covers the whole query and writes the normalised
 // output; otherwise it writes its unnormalised O and (max, sum) per head
 // for the combine kernel.
-template <int W, bool kWin8>
+template <int W, int kWin>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t cap, int32_t q_per_seq,
@@ -387,7 +381,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
 
   AttnTile cur;
   tile_begin<W>(cur, a, c_begin, wave, n);
-  tile_load<kWin8>(cur, a, n, g);
+  tile_load<kWin>(cur, a, n, g);
   if (Cfg::kQLds) {
 #pragma unroll
     for (int i = 0; i < kQPer; ++i) {
@@ -406,14 +400,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   for (int c = 0; c < Cfg::kCT; ++c) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_run = kNegInf;
   st.l_run = 0.f;
+#pragma unroll 1
   for (int ch = c_begin; ch < c_end; ++ch) {
     const bool has_next = ch + 1 < c_end;
     if (ch != c_begin) lds_barrier();  // the previous chunk's LDS reads are done
     if (Cfg::kPrefetch) {
       AttnTile nxt;
       if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);  // index loads of the next chunk
-      attn_chunk<W, kWin8>(sm, st, ch == c_begin, cur, qb_operand, scale_log2, [&]() {
-        if (has_next) tile_load<kWin8>(nxt, a, n, g);  // its row loads overlap this chunk's PV
+      attn_chunk<W, kWin>(sm, st, cur, qb_operand, scale_log2, [&]() {
+        if (has_next) tile_load<kWin>(nxt, a, n, g);  // its row loads overlap this chunk's PV
       });
       if (has_next) cur = nxt;
     } else {
@@ -421,9 +416,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
       // one of its two dependent round trips overlaps this chunk's work.
       AttnTile nxt;
       if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);
-      attn_chunk<W, kWin8>(sm, st, ch == c_begin, cur, qb_operand, scale_log2, []() {});
+      attn_chunk<W, kWin>(sm, st, cur, qb_operand, scale_log2, []() {});
       if (has_next) {
-        tile_load<kWin8>(nxt, a, n, g);
+        tile_load<kWin>(nxt, a, n, g);
         cur = nxt;
       }
     }
@@ -538,24 +533,26 @@ size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
   return o_bytes + ml_bytes;
 }
 
-template <bool kWin8>
+template <int kWin>
 static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, const csa2_fp4_kv& kv,
                           int32_t q_per_seq, const int32_t* idx, int32_t k_idx, const uint8_t* swa,
                           int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
                           float* part_o, float2* part_ml, float* out, hipStream_t stream) {
   if (p.waves == 8)
-    hipLaunchKernelGGL((attn_kernel<8, kWin8>), dim3(p.splits, n_q), dim3(64 * 8), 0, stream, q, kv.codes,
+    hipLaunchKernelGGL((attn_kernel<8, kWin>), dim3(p.splits, n_q), dim3(64 * 8), 0, stream, q, kv.codes,
                        kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
                        scale_log2, p.per_split, part_o, part_ml, p.splits, out);
   else
-    hipLaunchKernelGGL((attn_kernel<4, kWin8>), dim3(p.splits, n_q), dim3(64 * 4), 0, stream, q, kv.codes,
+    hipLaunchKernelGGL((attn_kernel<4, kWin>), dim3(p.splits, n_q), dim3(64 * 4), 0, stream, q, kv.codes,
                        kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
                        scale_log2, p.per_split, part_o, part_ml, p.splits, out);
 }
 
-// swa_fp8: window rows are E4M3 bytes [*][512] instead of bf16 [*][512].
+// win: the window rows' element type -- kWinBf16 (bf16 [*][512], converted
+// to f16 toward zero in the kernel), kWinE4m3 (E4M3 bytes [*][512]) or
+// kWinF16 (f16 [*][512], already converted as kWinBf16 would).
 csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
-                        const int32_t* idx, int32_t k_idx, const void* swa, bool swa_fp8,
+                        const int32_t* idx, int32_t k_idx, const void* swa, int win,
                         int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float sm_scale,
                         float* out, void* ws, hipStream_t stream) {
   if (n_q == 0) return CSA2_OK;
@@ -570,15 +567,37 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
-  if (swa_fp8)
-    attn_dispatch<true>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max, scale_log2,
-                        part_o, part_ml, out, stream);
+  if (win == kWinE4m3)
+    attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                            scale_log2, part_o, part_ml, out, stream);
+  else if (win == kWinF16)
+    attn_dispatch<kWinF16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                           scale_log2, part_o, part_ml, out, stream);
   else
-    attn_dispatch<false>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                         scale_log2, part_o, part_ml, out, stream);
+    attn_dispatch<kWinBf16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                            scale_log2, part_o, part_ml, out, stream);
   if (p.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, p.splits, out);
   return launch_status("csa2_sparse_attn");
+}
+
+// Window rows bf16 -> f16 toward zero (the conversion the attention kernel
+// applies to bf16 rows), for rows that many queries share: 8 values per
+// thread.
+namespace {
+__global__ __launch_bounds__(256) void win_f16_kernel(const u32x4* __restrict__ src, int64_t n_vec,
+                                                      u32x4* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n_vec) dst[i] = bf16x8_to_f16x8(src[i]);
+}
+}  // namespace
+
+csa2_status win_f16_launch(const uint16_t* src, int64_t n_rows, uint16_t* dst, hipStream_t stream) {
+  const int64_t n_vec = n_rows * (CSA2_LATENT / 8);
+  if (n_vec == 0) return CSA2_OK;
+  hipLaunchKernelGGL(win_f16_kernel, dim3((uint32_t)((n_vec + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(src), n_vec, reinterpret_cast<u32x4*>(dst));
+  return launch_status("window f16 conversion");
 }
 
 }  // namespace csa2
