@@ -36,7 +36,8 @@ constexpr int kFinalWaves = kFinalThreads / 64;
 constexpr int kPassThreads = 256;
 constexpr int kBatch = 8;                         // slots per thread loaded together
 constexpr int kHistSlots = kPassThreads * 16;     // slots per histogram workgroup
-constexpr int kFilterSlots = kPassThreads * 32;   // slots per filter workgroup
+constexpr int kFilterSlots = kTopkFilterSlots;     // slots per filter workgroup
+static_assert(kFilterSlots == kPassThreads * 32, "filter: 32 slots per thread");
 constexpr int kDirectMax = 32768;                 // final kernel filters inputs up to this length itself
 constexpr size_t kCandBytes = kTopkCandCap * sizeof(uint2);  // candidate buffer per sequence
 
@@ -190,7 +191,6 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
   __shared__ uint32_t hist[kTopkBins];
   __shared__ uint32_t wave_sum[kPassThreads / 64];
   __shared__ uint32_t found[2];
-  __shared__ uint32_t g_base;
   const int b = blockIdx.y;
   const int64_t nv = valid_slots(n, lens, len_div, b);
   const int64_t s0 = (int64_t)blockIdx.x * kFilterSlots;
@@ -223,18 +223,19 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
     mine += (key[j] != 0 && d == th.b1) ? 1u : 0u;
   }
   if (all || !buffered) return;
-  // Candidates of bin b1: positions from a prefix count, one global
-  // reservation per workgroup.
+  // Candidates of bin b1 go to this workgroup's own region of the
+  // sequence's buffer, positions from a prefix count (no global counter);
+  // the count found is written even when the region is too small, and the
+  // final pass then rescans the scores instead.
   uint32_t m;
   uint32_t pos = block_exclusive_scan<kPassThreads>(mine, wave_sum, &m);
-  if (threadIdx.x == 0) g_base = m ? atomicAdd(ws.cnt + b, m) : 0u;
-  __syncthreads();
-  pos += g_base;
-  uint2* gc = ws.cand + (int64_t)b * kTopkCandCap;
+  const uint32_t per_wg = kTopkCandCap / gridDim.x;
+  if (threadIdx.x == 0) ws.wcnt[(int64_t)b * kTopkFilterWgMax + blockIdx.x] = m;
+  uint2* gc = ws.cand + (int64_t)b * kTopkCandCap + (int64_t)blockIdx.x * per_wg;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     if (key[j] != 0 && (key[j] >> 20) == th.b1) {
-      if (pos < (uint32_t)kTopkCandCap) gc[pos] = make_uint2(key[j], (uint32_t)(s0 + j * kPassThreads + threadIdx.x));
+      if (pos < per_wg) gc[pos] = make_uint2(key[j], (uint32_t)(s0 + j * kPassThreads + threadIdx.x));
       ++pos;
     }
   }
@@ -414,6 +415,8 @@ struct FinalSmem {
   uint32_t tie[kTopkLdsWords];
   uint32_t cand_key[kTopkCandCap];
   uint32_t cand_slot[kTopkCandCap];
+  uint32_t wc_off[kTopkFilterWgMax];  // first LDS candidate of each filter workgroup
+  uint32_t wc_cnt[kTopkFilterWgMax];  // its candidate count
   uint32_t wave_sum[kFinalWaves];
   uint32_t found[2];
 };
@@ -457,14 +460,11 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
       if (tid + kFinalThreads * j < n_pool) sm.pool[tid + kFinalThreads * j] = pv[j];
   }
   const Threshold th = load_threshold<kFinalThreads>(gh, sm.hist, sm.wave_sum, sm.found, kk);
-  // The global histogram and counter are consumed (the filter pass appended
-  // exactly th.in_bin candidates): leave them zero for the next call.
-  const uint32_t n_cand_global = direct ? 0u : th.in_bin;
+  // The global histogram is consumed: leave it zero for the next call.
   for (int i = tid; i < kTopkBins; i += kFinalThreads) gh[i] = 0;
-  if (tid == 0) ws.cnt[b] = 0;
 
   const bool all = th.total <= kk;
-  const bool buffered = th.in_bin <= (uint32_t)kTopkCandCap;
+  bool buffered = th.in_bin <= (uint32_t)kTopkCandCap;
   uint32_t* sel = kGlobal ? ws.bits + (int64_t)b * ws.words_cap : sm.sel;
   uint32_t* tie = kGlobal ? ws.tie + (int64_t)b * ws.words_cap : sm.tie;
   for (int i = tid; i < words; i += kFinalThreads) tie[i] = 0u;
@@ -511,18 +511,42 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
       for (int j = 0; j < kWordsPer; ++j)
         if (tid + kFinalThreads * j < words) sm.sel[tid + kFinalThreads * j] = wv[j];
     }
-    if (!all && buffered && n_cand_global > 0) {
-      const uint2* gc = ws.cand + (int64_t)b * kTopkCandCap;
-      constexpr int kCandPer = kTopkCandCap / kFinalThreads;
-      uint2 cv[kCandPer];
+    if (!all && buffered) {
+      // Candidates of the filter pass: filter workgroup w kept up to per_wg
+      // of them in its own region.  Their counts' prefix sum places them in
+      // LDS (eight threads per workgroup region); if a region overflowed, or
+      // the counts do not add up to the histogram's, the scores are rescanned.
+      const int nw = (int)((n + kFilterSlots - 1) / kFilterSlots);
+      const int nwv = (nvalid + kFilterSlots - 1) / kFilterSlots;
+      const uint32_t per_wg = kTopkCandCap / nw;
+      const uint32_t c = tid < nwv ? ws.wcnt[(int64_t)b * kTopkFilterWgMax + tid] : 0u;
+      uint32_t total;
+      const uint32_t off = block_exclusive_scan<kFinalThreads>(c, sm.wave_sum, &total);
+      if (tid < nwv) {
+        sm.wc_off[tid] = off;
+        sm.wc_cnt[tid] = c;
+      }
+      buffered = __syncthreads_or(c > per_wg) == 0 && total == th.in_bin;
+      if (buffered) {
+        const int w = tid >> 3;
+        if (w < nwv) {
+          const uint32_t cw = sm.wc_cnt[w], ow = sm.wc_off[w];
+          const uint2* gc = ws.cand + (int64_t)b * kTopkCandCap + (int64_t)w * per_wg;
+          // 64 candidates of the region per pass, eight loads per thread in
+          // flight together (clamped to the region's last candidate).
+          for (uint32_t i0 = 0; i0 < cw; i0 += 64) {
+            uint2 v[8];
 #pragma unroll
-      for (int j = 0; j < kCandPer; ++j) cv[j] = gc[min<uint32_t>(tid + kFinalThreads * j, n_cand_global - 1)];
+            for (int r = 0; r < 8; ++r) v[r] = gc[min(i0 + (tid & 7) + 8 * r, cw - 1)];
 #pragma unroll
-      for (int j = 0; j < kCandPer; ++j) {
-        const uint32_t c = tid + kFinalThreads * j;
-        if (c < n_cand_global) {
-          sm.cand_key[c] = cv[j].x;
-          sm.cand_slot[c] = cv[j].y;
+            for (int r = 0; r < 8; ++r) {
+              const uint32_t i = i0 + (tid & 7) + 8 * r;
+              if (i < cw) {
+                sm.cand_key[ow + i] = v[r].x;
+                sm.cand_slot[ow + i] = v[r].y;
+              }
+            }
+          }
         }
       }
     }
@@ -717,10 +741,10 @@ size_t topk_workspace_bytes(int64_t n, int32_t n_seq) {
   const int64_t words = bitmap_words(n);
   const int64_t tie_words = (n + 31) / 32 > kTopkLdsWords ? words : 0;
   return (size_t)n_seq * (kCandBytes + kTopkBins * sizeof(uint32_t) + (words + tie_words) * sizeof(uint32_t) +
-                          sizeof(uint32_t)) + 64;
+                          kTopkFilterWgMax * sizeof(uint32_t)) + 64;
 }
 
-// Layout: cand, hist, bits, tie (long inputs), cnt; ws is 16-byte aligned.
+// Layout: cand, hist, bits, tie (long inputs), wcnt; ws is 16-byte aligned.
 TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq) {
   TopkWs w;
   char* p = reinterpret_cast<char*>(ws);
@@ -733,7 +757,7 @@ TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq) {
   p += (size_t)n_seq * w.words_cap * sizeof(uint32_t);
   w.tie = reinterpret_cast<uint32_t*>(p);  // used (and sized) only past kTopkLdsWords words
   if ((n + 31) / 32 > kTopkLdsWords) p += (size_t)n_seq * w.words_cap * sizeof(uint32_t);
-  w.cnt = reinterpret_cast<uint32_t*>(p);
+  w.wcnt = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 

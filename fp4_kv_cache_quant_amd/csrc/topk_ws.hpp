@@ -11,12 +11,17 @@ namespace csa2 {
 constexpr int kTopkBins = 4096;                        // top-digit histogram (12 bits)
 constexpr int kTopkCandCap = 8192;                     // keys buffered from the threshold bin
 constexpr int kTopkLdsWords = 262144 / 32;            // bitmaps kept in LDS up to this many words
+constexpr int kTopkFilterSlots = 8192;                 // slots per filter workgroup
+constexpr int kTopkFilterWgMax = CSA2_TOPK_NMAX / kTopkFilterSlots;  // filter workgroups per sequence
 
-// Per-sequence regions of one workspace.  hist and cnt must be zero when a
-// Top-k call starts; the call leaves them zero.
+// Per-sequence regions of one workspace.  hist must be zero when a Top-k
+// call starts; the call leaves it zero.  Filter workgroup w of a sequence
+// owns candidate slots [w * kTopkCandCap / nw, (w + 1) * kTopkCandCap / nw)
+// of its sequence's buffer (nw = the sequence's filter workgroups) and
+// writes how many candidates it found (possibly more than it could keep).
 struct TopkWs {
   uint32_t* hist;     // [n_seq][kTopkBins]
-  uint32_t* cnt;      // [n_seq] candidates appended by the filter pass
+  uint32_t* wcnt;     // [n_seq][kTopkFilterWgMax] candidates found per filter workgroup
   uint32_t* bits;     // [n_seq][words_cap] selection bitmap of the filter pass
   uint32_t* tie;      // [n_seq][words_cap] tie bitmap (inputs longer than kTopkLdsWords * 32)
   uint2* cand;        // [n_seq][kTopkCandCap] (key, slot)

@@ -226,6 +226,26 @@ def test_topk_global_bitmaps_reused_across_calls(csa2):
             assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), (n, k, b)
 
 
+@pytest.mark.parametrize("n,k,cluster", [(131072, 512, 600), (524288, 512, 1000), (524288, 2048, 3000),
+                                         (100000, 2048, 8000)])
+def test_topk_threshold_bin_clustered_in_one_region(csa2, n, k, cluster):
+    """The threshold bin's keys all sit in one filter workgroup's slots:
+    more than that workgroup's share of the candidate buffer, so the final
+    pass rescans the scores."""
+    n_seq = 2
+    rng = np.random.default_rng(n + cluster)
+    sc = rng.integers(0, 100, size=(n_seq, n)).astype(np.float32)
+    base = 9000 if n > 100000 else 50
+    sc[0, base:base + cluster] = 1e6 + rng.integers(0, 1000, size=cluster)   # one top-digit bin
+    sc[1, n - cluster:] = 1e6 + np.arange(cluster) % 7                        # heavy ties, last region
+    print_case(f"topk clustered threshold bin n={n} k={k} cluster={cluster}")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    csa2.topk(dev(sc), k, out)
+    got = out.cpu().numpy()
+    for b in range(n_seq):
+        assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), b
+
+
 def test_topk_signed_scores_and_zero_signs(csa2):
     rng = np.random.default_rng(11)
     sc = rng.standard_normal((1, 10000)).astype(np.float32)
