@@ -80,15 +80,25 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const int64_t base = chunk * kKeysPerWG + (int64_t)wave * (kTilesPerWave * 16);
     u32x4 kv[kTilesPerWave][2];
     bool valid[kTilesPerWave];
+    // Pool mode: every tile's block id first (clamped slots, all loads in
+    // flight together; slot < n_out = n_pool * blk <= 2^20 fits 32 bits),
+    // then the key rows they name.
+    int32_t blk_id[kTilesPerWave];
+    if (kPool) {
+#pragma unroll
+      for (int t = 0; t < kTilesPerWave; ++t) {
+        const uint32_t s32 = (uint32_t)min(base + t * 16 + n, n_out - 1);
+        blk_id[t] = pool[(int64_t)b * n_pool + s32 / (uint32_t)blk];
+      }
+    }
 #pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t) {
       const int64_t slot = base + t * 16 + n;
       int64_t row = slot;
       bool ok = slot < n_valid;
-      if (kPool && ok) {
-        const int32_t blk_id = pool[(int64_t)b * n_pool + slot / blk];  // slot < n_out = n_pool * blk
-        row = (int64_t)blk_id * blk + slot % blk;
-        ok = blk_id >= 0 && row < L && row < key_cap;
+      if (kPool) {
+        row = (int64_t)blk_id[t] * blk + (int64_t)((uint32_t)slot % (uint32_t)blk);
+        ok = ok && blk_id[t] >= 0 && row < L && row < key_cap;
       }
       valid[t] = ok;
       // Unconditional load of a clamped row (an invalid slot reads row 0 and
