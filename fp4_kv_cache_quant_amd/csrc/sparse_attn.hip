@@ -129,6 +129,7 @@ struct AttnArgs {
   const uint8_t* codes;
   const uint8_t* scales;
   int64_t cap;
+  int64_t kv_row0;  // first row of the query's cache sequence (qb / q_per_seq) * cap
   int32_t q_per_seq;
   const int32_t* idx;
   int32_t k_idx;
@@ -145,9 +146,9 @@ struct AttnArgs {
 template <int W>
 __device__ __forceinline__ void tile_begin(AttnTile& t, const AttnArgs& a, int ch, int wave, int n) {
   const int tile = ch * W + wave;
-  const int swa_before = (int)(((int64_t)tile * a.swa_tiles) / a.n_tiles);
+  const int swa_before = (tile * a.swa_tiles) / a.n_tiles;  // < 2^20: 32-bit
   t.in_range = tile < a.n_tiles;
-  t.swa = t.in_range && ((int64_t)(tile + 1) * a.swa_tiles) / a.n_tiles > swa_before;
+  t.swa = t.in_range && ((tile + 1) * a.swa_tiles) / a.n_tiles > swa_before;
   t.row0 = t.swa ? swa_before * 16 : (tile - swa_before) * 16;
   t.id = -1;
   if (!t.swa) {
@@ -164,14 +165,14 @@ __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n,
   const int qb = a.qb;
   if (!t.swa) {
     t.ok = t.id >= 0 && t.id < a.cap;
-    const int64_t row = (int64_t)(qb / a.q_per_seq) * a.cap + (t.ok ? t.id : 0);
+    const int64_t row = a.kv_row0 + (t.ok ? t.id : 0);
     const u32x4* cp = reinterpret_cast<const u32x4*>(a.codes + row * CSA2_CODE_BYTES + 64 * g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) t.raw[i] = cp[i];
+    // (A row that is not attended over reads a clamped address; its scales
+    // are taken as 0 where they are used, not here, so that this load does
+    // not have to complete before the next ones are issued.)
     t.s8 = *reinterpret_cast<const uint2*>(a.scales + row * CSA2_SCALE_BYTES + 8 * g);
-    // A row that is not attended over (clamped address) dequantises to
-    // zeros: its scales read as 0.
-    if (!t.ok) t.s8 = uint2{0u, 0u};
   } else {
     const int j = t.row0 + n;
     t.ok = t.in_range && j < a.n_swa;
@@ -207,11 +208,13 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
   if (!t.swa) {
     // The lane's 8 scale bytes as f16 (exact E4M3 conversions, two per
     // instruction): sc[i] holds scale bytes 2i (low half) and 2i + 1.
+    // A row that is not attended over dequantises to zeros: scales 0.
+    const uint32_t s8x = t.ok ? t.s8.x : 0u, s8y = t.ok ? t.s8.y : 0u;
     uint32_t sc[4];
-    sc[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.x, 1.0f, false));
-    sc[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.x, 1.0f, true));
-    sc[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.y, 1.0f, false));
-    sc[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t.s8.y, 1.0f, true));
+    sc[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8x, 1.0f, false));
+    sc[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8x, 1.0f, true));
+    sc[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8y, 1.0f, false));
+    sc[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s8y, 1.0f, true));
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       // Channels 8k .. 8k+7 of the lane's 128 use scale byte k / 2, splat
@@ -368,6 +371,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   a.codes = codes;
   a.scales = scales;
   a.cap = cap;
+  a.kv_row0 = (int64_t)(qb / q_per_seq) * cap;
   a.q_per_seq = q_per_seq;
   a.idx = idx;
   a.k_idx = k_idx;
