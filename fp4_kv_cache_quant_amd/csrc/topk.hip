@@ -627,14 +627,55 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
 constexpr int kRowsMax = 64 * kFinalThreads;  // 65,536 slots
 static_assert(kRowsMax == kTopkRowsMax, "register-resident selection length");
 
+constexpr int kRowsCand = 8192;  // keys kept by the sampled first pass
+
 struct RowsSmem {
   int32_t pool[CSA2_TOPK_MAX];
   uint32_t hist[kTopkBins];
   uint32_t sel[kRowsMax / 32];
   uint32_t tie[kRowsMax / 32];
+  uint32_t cand_key[kRowsCand];
+  uint32_t cand_slot[kRowsCand];
   uint32_t wave_sum[kFinalWaves];
   uint32_t found[2];
 };
+
+// The exact kk-th largest key T among the nc keys ck[0..nc) (1 <= kk <= nc)
+// and how many keys equal to T are taken (ties): radix select over digits
+// of 12, 12 and 8 bits with LDS histograms, every thread taking keys
+// tid, tid + NT, ...  Called by the whole workgroup.
+template <int NT>
+__device__ void select_among(const uint32_t* ck, int nc, uint32_t kk, uint32_t* hist, uint32_t* wave_sum,
+                             uint32_t* found, uint32_t& T, uint32_t& ties) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int c = tid; c < nc; c += NT) atomicAdd(&hist[ck[c] >> 20], 1u);
+  __syncthreads();
+  find_threshold_bin<NT>(hist, kTopkBins, kk, wave_sum, found);
+  const uint32_t b1 = found[0];
+  const uint32_t need1 = kk - found[1];
+  for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int c = tid; c < nc; c += NT) {
+    const uint32_t key = ck[c];
+    if ((key >> 20) == b1) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
+  }
+  __syncthreads();
+  find_threshold_bin<NT>(hist, kTopkBins, need1, wave_sum, found);
+  const uint32_t pre2 = (b1 << 12) | found[0];
+  const uint32_t need2 = need1 - found[1];
+  for (int i = tid; i < 256; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int c = tid; c < nc; c += NT) {
+    const uint32_t key = ck[c];
+    if ((key >> 8) == pre2) atomicAdd(&hist[key & 0xFFu], 1u);
+  }
+  __syncthreads();
+  find_threshold_bin<NT>(hist, 256, need2, wave_sum, found);
+  T = (pre2 << 8) | found[0];
+  ties = need2 - found[1];
+}
 
 template <int kRowsPer>
 __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* __restrict__ scores, int64_t n,
@@ -668,6 +709,62 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
   }
   for (int i = tid; i < kTopkBins; i += kFinalThreads) sm.hist[i] = 0;
   __syncthreads();
+
+  // Sampled first pass.  One key per thread (slot (tid % kRowsPer) * NT +
+  // tid, spread over the row) estimates a lower bound B for the top digit
+  // of the k-th key: the bin where the samples counted from the top reach
+  // r, about twice the samples that k keys would give.  Every key in bins
+  // >= B then goes to an LDS list, from which the exact threshold is
+  // selected -- if the list holds at least k keys (so it contains the k
+  // largest) and fits.  Otherwise the full passes below run.
+  {
+    const int r = (int)(((int64_t)2 * kk * kFinalThreads + nvalid - 1) / max(nvalid, 1)) + 8;
+    if (nvalid >= 4 * (int)kk && r <= kFinalThreads / 4) {  // uniform over the workgroup
+      uint32_t smp = 0;
+#pragma unroll
+      for (int j = 0; j < kRowsPer; ++j)
+        if (j == tid % kRowsPer) smp = key[j];
+      if (smp) atomicAdd(&sm.hist[smp >> 20], 1u);
+      uint32_t n_smp;
+      block_exclusive_scan<kFinalThreads>(smp ? 1u : 0u, sm.wave_sum, &n_smp);  // syncs: histogram complete
+      if (n_smp >= (uint32_t)r) {
+        find_threshold_bin<kFinalThreads>(sm.hist, kTopkBins, (uint32_t)r, sm.wave_sum, sm.found);
+        const uint32_t lo = sm.found[0] << 20;  // keys >= lo are kept
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kRowsPer; ++j) cnt += (key[j] >= lo && key[j] != 0) ? 1u : 0u;
+        uint32_t n_cand;
+        uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, sm.wave_sum, &n_cand);
+        if (n_cand >= kk && n_cand <= (uint32_t)kRowsCand) {
+#pragma unroll
+          for (int j = 0; j < kRowsPer; ++j) {
+            if (key[j] >= lo && key[j] != 0) {
+              sm.cand_key[pos] = key[j];
+              sm.cand_slot[pos] = (uint32_t)(j * kFinalThreads + tid);
+              ++pos;
+            }
+          }
+          for (int i = tid; i < words; i += kFinalThreads) sm.sel[i] = sm.tie[i] = 0;
+          __syncthreads();
+          uint32_t T, ties;
+          select_among<kFinalThreads>(sm.cand_key, (int)n_cand, kk, sm.hist, sm.wave_sum, sm.found, T, ties);
+          for (int c = tid; c < (int)n_cand; c += kFinalThreads) {
+            const uint32_t key = sm.cand_key[c], i = sm.cand_slot[c];
+            if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
+            else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
+          }
+          __syncthreads();
+          finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+                            out + (int64_t)b * k);
+          return;
+        }
+      }
+      // The estimate did not hold: clear the sample histogram and run the
+      // full passes.
+      for (int i = tid; i < kTopkBins; i += kFinalThreads) sm.hist[i] = 0;
+      __syncthreads();
+    }
+  }
 
   // Digit 1: bits 31..20.
   uint32_t mine = 0;

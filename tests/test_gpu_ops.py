@@ -246,6 +246,33 @@ def test_topk_threshold_bin_clustered_in_one_region(csa2, n, k, cluster):
         assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), b
 
 
+@pytest.mark.parametrize("case", ["continuous", "wide_bin", "top_unsampled"])
+def test_topk_sampled_first_pass_and_fallback(csa2, case):
+    """Single-workgroup selection with its sampled first pass: continuous
+    scores (the pass holds), 9,000 keys in the threshold's top-digit bin
+    (too many to keep: the full passes run), and the top keys placed off
+    the sampled slots."""
+    n, k, n_seq = 60000, 512, 2
+    rng = np.random.default_rng({"continuous": 1, "wide_bin": 2, "top_unsampled": 3}[case])
+    if case == "continuous":
+        sc = rng.standard_normal((n_seq, n)).astype(np.float32)
+    elif case == "wide_bin":
+        sc = rng.integers(0, 3, size=(n_seq, n)).astype(np.float32)
+        sc[:, rng.choice(n, 9000, replace=False)] = 5.0 + rng.integers(0, 2, size=9000) * 0.25
+    else:
+        sc = rng.integers(0, 1000, size=(n_seq, n)).astype(np.float32)
+        slots = np.arange(n)
+        sampled = (slots % 1024) % 64 == slots // 1024     # slot = (t % 64) * 1024 + t
+        top = rng.choice(slots[~sampled], 600, replace=False)
+        sc[:, top] = 5000 + rng.integers(0, 50, size=600)
+    print_case(f"topk sampled first pass {case}")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    csa2.topk(dev(sc), k, out)
+    got = out.cpu().numpy()
+    for b in range(n_seq):
+        assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), b
+
+
 def test_topk_signed_scores_and_zero_signs(csa2):
     rng = np.random.default_rng(11)
     sc = rng.standard_normal((1, 10000)).astype(np.float32)
