@@ -38,23 +38,23 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12761571, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12723702, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "63835a0e06c0fb5eb4e1981412f7b45241c67e900a25e7de599ec2584e830b43",
+                    "991309ea238dda775e1d2f8fe2792014ac15dd5b85e69a39c9f57fc29b62eeea",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
+                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
     "decoder20_1m/block_scan": {
-        "bytes": 280622264, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 280505480, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "2805cdc75311ed99d69ed6cc28b98a17c2d8618c448ac40e07f5dd6cccddb000",
+                    "09113af17f5d097f1846767696db3f52df3c62a024bc9ad0131063f1fb518436",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
+                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
     "encoder_1m/flat_score": {
-        "bytes": 1126701607, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "bytes": 1126548223, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "2805cdc75311ed99d69ed6cc28b98a17c2d8618c448ac40e07f5dd6cccddb000",
+                    "09113af17f5d097f1846767696db3f52df3c62a024bc9ad0131063f1fb518436",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "1828156b3471b912f4bb089196755184d8966f66a927b4131dd2bc12675f4a4a"}},
+                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
 }
 
 
