@@ -104,7 +104,7 @@ struct AttnSmem {
 
 // Running state of one workgroup over its chunks: O for 16 heads x this
 // wavefront's 512/W channels (column tile c: channels 64*(S*wave + c/4) +
-// 4n + c%4, head 4g + j in element j), the running max of head n, and
+// 16*(c%4) + n, head 4g + j in element j), the running max of head n, and
 // (threads 0..15) the running denominator of head tid.
 template <int W>
 struct AttnState {
@@ -299,22 +299,26 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
     const f16x8 pl = as_f16x8(*reinterpret_cast<const u32x4*>(&sm.ps[1][n * kPPitch + 32 * ks + 8 * g]));
 #pragma unroll
     for (int sl = 0; sl < kSlices; ++sl) {
-      const int ch0 = 64 * (kSlices * wave + sl) + 4 * n;
-      uint2 R[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        R[i] = *reinterpret_cast<const uint2*>(&sm.xs[(32 * ks + 8 * g + i) * kXPitch + ch0]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        u32x4 bc;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t a0 = (c < 2) ? R[2 * p].x : R[2 * p].y;
-          const uint32_t a1 = (c < 2) ? R[2 * p + 1].x : R[2 * p + 1].y;
-          bc[p] = (c & 1) ? byte_perm(a1, a0, 0x07060302u) : byte_perm(a1, a0, 0x05040100u);
-        }
-        st.o[4 * sl + c] = mfma16x16x32_f16(ph, as_f16x8(bc), st.o[4 * sl + c]);
-        st.o[4 * sl + c] = mfma16x16x32_f16(pl, as_f16x8(bc), st.o[4 * sl + c]);
+        // B = X[rows 32ks + 8g .. +7][channels ch .. ch+15] by two transposing
+        // LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane i
+        // receives element i%4 of the 4-channel pieces addressed by lanes
+        // 4e + i/4 (e = 0..3), so lane n addresses row 4h + n/4 of the
+        // half, channels ch + 4(n%4) .. +3, and receives channel ch + n of
+        // rows 4h .. 4h+3.
+        const int ch = 64 * (kSlices * wave + sl) + 16 * c;
+        const int r0 = 32 * ks + 8 * g + (n >> 2);
+        const uint16_t* a0 = &sm.xs[r0 * kXPitch + ch + 4 * (n & 3)];
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(a0));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(a0 + 4 * kXPitch));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const f16x8 bc = as_f16x8(u32x4{l2.x, l2.y, h2.x, h2.y});
+        st.o[4 * sl + c] = mfma16x16x32_f16(ph, bc, st.o[4 * sl + c]);
+        st.o[4 * sl + c] = mfma16x16x32_f16(pl, bc, st.o[4 * sl + c]);
       }
     }
   }
@@ -437,12 +441,11 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
       const float l = sm.l_fin[head];
       const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int sl = 0; sl < kSlices; ++sl) {
-        const int ch0 = 64 * (kSlices * wave + sl) + 4 * n;
-        *reinterpret_cast<f32x4*>(out + ((int64_t)qb * 16 + head) * CSA2_LATENT + ch0) =
-            f32x4{st.o[4 * sl][j] * inv, st.o[4 * sl + 1][j] * inv, st.o[4 * sl + 2][j] * inv,
-                  st.o[4 * sl + 3][j] * inv};
-      }
+      for (int sl = 0; sl < kSlices; ++sl)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          out[((int64_t)qb * 16 + head) * CSA2_LATENT + 64 * (kSlices * wave + sl) + 16 * c + n] =
+              st.o[4 * sl + c][j] * inv;
     }
     return;
   }
@@ -451,11 +454,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   for (int j = 0; j < 4; ++j) {
     const int head = 4 * g + j;
 #pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) {
-      const int ch0 = 64 * (kSlices * wave + sl) + 4 * n;
-      *reinterpret_cast<f32x4*>(po + head * CSA2_LATENT + ch0) =
-          f32x4{st.o[4 * sl][j], st.o[4 * sl + 1][j], st.o[4 * sl + 2][j], st.o[4 * sl + 3][j]};
-    }
+    for (int sl = 0; sl < kSlices; ++sl)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) po[head * CSA2_LATENT + 64 * (kSlices * wave + sl) + 16 * c + n] = st.o[4 * sl + c][j];
   }
   if (tid < 16) part_ml[((int64_t)qb * n_split + split) * 16 + tid] = make_float2(st.m_run, st.l_run);
 }
