@@ -227,14 +227,25 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
       s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
     }
   } else {
+    // Rows past the window read a clamped address and are zeroed; for
+    // rows already in f16 or E4M3 the masking is skipped when every row of
+    // the tile is in the window.
+    auto window_rows = [&](bool mask) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      u32x4 x = kWin == kWinE4m3 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
-                : kWin == kWinF16 ? t.raw[k]
-                                  : bf16x8_to_f16x8(t.raw[k]);
-      if (!t.ok) x = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
-      s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
+      for (int k = 0; k < 16; ++k) {
+        u32x4 x = kWin == kWinE4m3 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
+                  : kWin == kWinF16 ? t.raw[k]
+                                    : bf16x8_to_f16x8(t.raw[k]);
+        if (mask && !t.ok) x = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
+        s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
+      }
+    };
+    if constexpr (kWin == kWinBf16) {
+      window_rows(true);  // (two copies of the converting loop cost registers)
+    } else {
+      if (__all(t.ok)) window_rows(false);
+      else window_rows(true);
     }
   }
   const uint64_t rows_ok = __ballot(t.ok);  // bit n (lanes 0..15) = row n of this wavefront
