@@ -49,12 +49,6 @@ MEASURED_TRAFFIC = {
                     "09113af17f5d097f1846767696db3f52df3c62a024bc9ad0131063f1fb518436",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
-    "encoder_1m/flat_score": {
-        "bytes": 1126548223, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
-        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "09113af17f5d097f1846767696db3f52df3c62a024bc9ad0131063f1fb518436",
-                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
 }
 
 
@@ -240,10 +234,12 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
 
 
 def flat_op_rooflines(cfg, inp, graph: bool = True):
-    """The ops of a flat-selection step (every Full layer scores all L
-    positions), as op_rooflines does for the hierarchical one.  Bytes per
-    call: flat score n*L*(128+4) (indexer keys read, scores written); Top-512
-    n*L*4 (scores read once); attention as in op_rooflines."""
+    """The ops of a flat-selection step (every selecting layer takes a fresh
+    Top-k over all L positions), as op_rooflines does for the hierarchical
+    one.  Bytes per call: flat select n*(L*128 + 1024 + k*4) (every indexer
+    key read once, indexer Q, indices written; csa2_flat_select keeps
+    per-workgroup candidates instead of writing the scores); attention as in
+    op_rooflines."""
     import torch
 
     import fp4_kv_cache_quant_amd as csa2
@@ -251,19 +247,16 @@ def flat_op_rooflines(cfg, inp, graph: bool = True):
     n = cfg.n_seq
     L = int(inp.lens[0].item())
     q0 = inp.idx_q[0][0]
-    sc = torch.empty(n, inp.cap, dtype=torch.float32, device="cuda")
     idx = torch.empty(n, cfg.topk, dtype=torch.int32, device="cuda")
     out = torch.empty(n, 16, 512, dtype=torch.float32, device="cuda")
-    tws = torch.zeros(csa2.topk_workspace_size(inp.cap, n), dtype=torch.uint8, device="cuda")
+    fws = torch.zeros(csa2.flat_select_workspace_size(inp.cap, cfg.topk, n), dtype=torch.uint8, device="cuda")
     aws = torch.empty(csa2.sparse_attn_workspace_size(n, cfg.topk, cfg.swa), dtype=torch.uint8, device="cuda")
-    csa2.index_score(q0, inp.idx_k, inp.lens, sc)
-    csa2.topk(sc, cfg.topk, idx, lens=inp.lens, ws=tws)
+    csa2.flat_select(q0, inp.idx_k, inp.lens, cfg.topk, idx, ws=fws)
     sel_layers = sum(1 for m, _, _ in cfg.layers if m != 2)
     ops = [
-        ("flat_score", "flat score (index_score, all positions)", sel_layers, n * L * 132,
-         lambda: csa2.index_score(q0, inp.idx_k, inp.lens, sc)),
-        ("flat_topk", "flat Top-512 (topk)", sel_layers, n * L * 4,
-         lambda: csa2.topk(sc, cfg.topk, idx, lens=inp.lens, ws=tws)),
+        ("flat_select", "flat select (flat_select: scores + Top-k of all positions)", sel_layers,
+         n * (L * 128 + 1024 + cfg.topk * 4),
+         lambda: csa2.flat_select(q0, inp.idx_k, inp.lens, cfg.topk, idx, ws=fws)),
         ("sparse_attn", "sparse+SWA attention (sparse_attn: chunk + combine kernels)", len(cfg.layers),
          n * (cfg.topk * 4 + cfg.topk * 288 + cfg.swa * (512 if cfg.swa_fp8 else 1024) + 16 * 1024 + 16 * 512 * 4),
          lambda: csa2.sparse_attn(inp.main_q[0][0], inp.kv[0], idx, inp.swa[0], inp.swa_len, 512 ** -0.5, out,

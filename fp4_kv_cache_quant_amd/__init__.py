@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
-    "sparse_attn", "sparse_attn_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
+    "sparse_attn", "sparse_attn_workspace_size", "flat_select", "flat_select_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
     "prefill_index_score", "Prefill", "quant_fp8_rows", "block_keys", "append_index_keys",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
@@ -78,6 +78,8 @@ _quant_append = _sig("csa2_quant_append", _I32, _P, _FP4KV, _P, _P, _P)
 _index_score = _sig("csa2_index_score", _I32, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _I64, _I32, _P)
 _topk_ws = _sig("csa2_topk_workspace_size", _SZ, _I64, _I32)
 _topk = _sig("csa2_topk", _I32, _P, _I64, _P, _I32, _I32, _P, _I32, _I32, _P, _P, _SZ, _I32, _P)
+_flat_ws = _sig("csa2_flat_select_workspace_size", _SZ, _I64, _I32, _I32)
+_flat_select = _sig("csa2_flat_select", _I32, _P, _P, _P, _I64, _P, _I32, _P, _P, _SZ, _I32, _P)
 _attn_ws = _sig("csa2_sparse_attn_workspace_size", _SZ, _I32, _I32, _I32)
 _attn_f8w = _sig("csa2_sparse_attn_f8w", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
                  _I32, _F32, _P, _P, _SZ, _P)
@@ -210,6 +212,23 @@ def topk(scores: torch.Tensor, k: int, out: torch.Tensor, lens: Optional[torch.T
         ws = torch.zeros(max(topk_workspace_size(n, n_seq), 1), dtype=torch.uint8, device=scores.device)
     _check(_topk(_ptr(scores), n, _ptr(lens), len_div, k, _ptr(pool), n_pool, blk, _ptr(out), _ptr(ws),
                  ws.numel(), n_seq, _stream(stream)))
+
+
+def flat_select_workspace_size(key_cap: int, k: int, n_seq: int) -> int:
+    return int(_flat_ws(key_cap, k, n_seq))
+
+
+def flat_select(q: torch.Tensor, keys: torch.Tensor, lens: torch.Tensor, k: int, out: torch.Tensor,
+                w: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """q [n_seq][8][64], keys [n_seq][key_cap][64] bf16 -> out [n_seq][k] int32: the Top-k positions by
+    indexer score over all positions (csa2_flat_select).  ws: a zero-filled workspace reused across calls
+    (a fresh one if None)."""
+    n_seq, key_cap = keys.shape[0], keys.shape[1]
+    if ws is None:
+        ws = torch.zeros(max(flat_select_workspace_size(key_cap, k, n_seq), 1), dtype=torch.uint8,
+                         device=keys.device)
+    _check(_flat_select(_ptr(q), _ptr(w), _ptr(keys), key_cap, _ptr(lens), k, _ptr(out), _ptr(ws), ws.numel(),
+                        n_seq, _stream(stream)))
 
 
 def sparse_attn_workspace_size(n_q: int, k_idx: int, swa_max: int) -> int:

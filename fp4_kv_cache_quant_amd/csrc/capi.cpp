@@ -20,6 +20,9 @@ csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, i
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
                                uint32_t*, hipStream_t);
+int64_t index_score_local_groups(int64_t key_cap);
+csa2_status index_score_local_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*, int32_t,
+                                     float*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
@@ -65,6 +68,47 @@ csa2_status check_index_score(const uint16_t* q, const uint16_t* keys, int64_t k
   CSA2_REQUIRE((reinterpret_cast<uintptr_t>(q) & 15) == 0 && (reinterpret_cast<uintptr_t>(keys) & 15) == 0,
                CSA2_EINVAL, "csa2_index_score: q and keys must be 16-byte aligned");
   return CSA2_OK;
+}
+
+// ------------------------------------------------------------ flat select
+// Workspace of a flat selection: scores (or the per-workgroup candidates'
+// scores) | candidate positions | Top-k workspace, 256-byte aligned parts.
+FlatSelectWs flat_select_ws(int64_t key_cap, int32_t k, int32_t n_seq, void* base) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  FlatSelectWs f{};
+  const int64_t groups = index_score_local_groups(key_cap);
+  f.local_groups = (key_cap > kTopkRowsMax && groups * k <= kTopkRowsMax) ? groups : 0;
+  f.n_scores = f.local_groups ? groups * k : key_cap;
+  char* p = reinterpret_cast<char*>(base);
+  size_t off = 0;
+  f.scores = reinterpret_cast<float*>(p + off);
+  off += up((size_t)n_seq * f.n_scores * sizeof(float));
+  f.cand = reinterpret_cast<int32_t*>(p + off);
+  off += up(f.local_groups ? (size_t)n_seq * f.n_scores * sizeof(int32_t) : 0);
+  f.tw = base ? topk_ws_carve(p + off, f.n_scores, n_seq) : TopkWs{};
+  off += topk_workspace_bytes(f.n_scores, n_seq);
+  f.bytes = off;
+  return f;
+}
+
+csa2_status flat_select_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                               const int32_t* lens, int32_t k, int32_t* out, const FlatSelectWs& f, int32_t n_seq,
+                               hipStream_t stream) {
+  if (f.local_groups > 0) {
+    // Each scoring workgroup keeps the Top-k of its positions; the Top-k of
+    // those candidates (ids = their positions) is the sequence's.
+    csa2_status st = index_score_local_launch(q, w, keys, key_cap, lens, k, f.scores, f.cand, n_seq, stream);
+    if (st != CSA2_OK) return st;
+    return topk_launch(f.scores, f.n_scores, nullptr, 1, k, nullptr, 0, 1, out, f.tw, false, n_seq, stream, f.cand);
+  }
+  // Up to kTopkRowsMax positions the selection reads the scores once in
+  // registers (no histogram from the score kernel); longer inputs get the
+  // histogram fused into the scoring pass.
+  const bool fused = key_cap > kTopkRowsMax;
+  csa2_status st = index_score_launch(q, w, keys, key_cap, lens, 1, nullptr, 0, 1, f.scores, key_cap, n_seq,
+                                      fused ? f.tw.hist : nullptr, stream);
+  if (st != CSA2_OK) return st;
+  return topk_launch(f.scores, key_cap, lens, 1, k, nullptr, 0, 1, out, f.tw, fused, n_seq, stream);
 }
 
 csa2_status check_topk(const float* scores, int64_t n, int32_t len_div, int32_t k, const int32_t* pool,
@@ -155,6 +199,29 @@ csa2_status csa2_index_score(const uint16_t* q, const float* w, const uint16_t* 
   if (st != CSA2_OK || n_seq == 0) return st;
   return index_score_launch(q, w, keys, key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, n_seq,
                             nullptr, as_stream(stream));
+}
+
+size_t csa2_flat_select_workspace_size(int64_t key_cap, int32_t k, int32_t n_seq) {
+  if (key_cap <= 0 || key_cap > CSA2_TOPK_NMAX || k < 1 || k > CSA2_TOPK_MAX || n_seq <= 0 || n_seq > 65535)
+    return 0;
+  return flat_select_ws(key_cap, k, n_seq, nullptr).bytes;
+}
+
+csa2_status csa2_flat_select(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, int32_t k, int32_t* out, void* ws, size_t ws_bytes, int32_t n_seq,
+                             void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_seq >= 0 && n_seq <= 65535, CSA2_ESHAPE, "csa2_flat_select: n_seq must be in [0, 65535]");
+  if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(q && keys && lens && out && ws, CSA2_EINVAL, "csa2_flat_select: null pointer");
+  CSA2_REQUIRE(key_cap >= 1 && key_cap <= CSA2_TOPK_NMAX, CSA2_ESHAPE, "csa2_flat_select: key_cap must be in [1, 1048576]");
+  CSA2_REQUIRE(k >= 1 && k <= CSA2_TOPK_MAX, CSA2_ESHAPE, "csa2_flat_select: k must be in [1, 2048]");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(q) & 15) == 0 && (reinterpret_cast<uintptr_t>(keys) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(ws) & 255) == 0,
+               CSA2_EINVAL, "csa2_flat_select: q and keys need 16-byte, ws 256-byte alignment");
+  const FlatSelectWs f = flat_select_ws(key_cap, k, n_seq, ws);
+  CSA2_REQUIRE(ws_bytes >= f.bytes, CSA2_ECAPACITY, "csa2_flat_select: workspace too small");
+  return flat_select_launch(q, w, keys, key_cap, lens, k, out, f, n_seq, as_stream(stream));
 }
 
 size_t csa2_topk_workspace_size(int64_t n, int32_t n_seq) {

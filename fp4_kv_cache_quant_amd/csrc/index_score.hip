@@ -18,6 +18,7 @@
 
 #include "common.hpp"
 #include "topk_ws.hpp"
+#include "select_dev.hpp"
 
 namespace csa2 {
 namespace {
@@ -243,6 +244,175 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
   }
 }
 
+
+// ------------------------------------------------------- flat, local Top-k
+// Flat scoring with a selection per workgroup: workgroup w of a sequence
+// scores the contiguous slots [w * kLocalSlots, (w + 1) * kLocalSlots) into
+// LDS (no score leaves the workgroup) and keeps its own Top-k by (score
+// descending, slot ascending).  The sequence's Top-k lies in the union of
+// these, so it is the Top-k of the G * k candidates, ties to the lower
+// candidate index, which is the lower slot: candidates are written in slot
+// order, workgroup after workgroup, as (score, slot) at
+// cand[b][w * k .. w * k + k), padded with -inf.
+constexpr int kLocalChunks = 16;
+constexpr int kLocalSlots = kLocalChunks * kKeysPerWG;  // 8,192 slots per workgroup
+
+template <bool kWeights>
+__global__ __launch_bounds__(256) void index_score_local_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ keys,
+    int64_t key_cap, const int32_t* __restrict__ lens, int32_t k, float* __restrict__ cand_score,
+    int32_t* __restrict__ cand_slot) {
+  __shared__ uint32_t lk[kLocalSlots];  // order keys of the range (0: not a candidate)
+  __shared__ uint32_t hist[kTopkBins];
+  __shared__ uint32_t selw[kLocalSlots / 32], tiew[kLocalSlots / 32];
+  __shared__ uint32_t wave_sum[4];
+  __shared__ uint32_t found[2];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t n_valid = min(key_cap, (int64_t)lens[b]);
+  const int64_t s_begin = (int64_t)blockIdx.x * kLocalSlots;
+
+  bf16x8 qa[2];
+  {
+    u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
+    if (n < 8) {
+      const u32x4* qp = reinterpret_cast<const u32x4*>(q + ((int64_t)b * 8 + n) * 64 + 16 * g);
+      v0 = qp[0];
+      v1 = qp[1];
+    }
+    qa[0] = as_bf16x8(v0);
+    qa[1] = as_bf16x8(v1);
+  }
+  float wh[4] = {1.f, 1.f, 1.f, 1.f};
+  if (kWeights && g < 2) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wh[r] = w[(int64_t)b * 8 + 4 * g + r];
+  }
+  const uint16_t* kb = keys + (int64_t)b * key_cap * 64;
+#pragma unroll 1
+  for (int c = 0; c < kLocalChunks; ++c) {
+    const int local0 = c * kKeysPerWG + wave * (kTilesPerWave * 16);
+    u32x4 kv[kTilesPerWave][2];
+    bool valid[kTilesPerWave];
+#pragma unroll
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int64_t slot = s_begin + local0 + t * 16 + n;
+      valid[t] = slot < n_valid;
+      const u32x4* kp = reinterpret_cast<const u32x4*>(kb + (valid[t] ? slot : 0) * 64 + 16 * g);
+      kv[t][0] = __builtin_nontemporal_load(kp);
+      kv[t][1] = __builtin_nontemporal_load(kp + 1);
+    }
+#pragma unroll
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      if (!valid[t]) kv[t][0] = kv[t][1] = u32x4{0, 0, 0, 0};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16x16x32(qa[0], as_bf16x8(kv[t][0]), acc);
+      acc = mfma16x16x32(qa[1], as_bf16x8(kv[t][1]), acc);
+      const float part = relu_wsum4(acc, wh);
+      const float other = __shfl_xor(part, 16);
+      if (g == 0) lk[local0 + t * 16 + n] = valid[t] ? order_key(part + other) : 0u;
+    }
+  }
+  __syncthreads();
+
+  // The range's k-th key T (radix select over digits of 12, 12 and 8 bits)
+  // and how many keys equal to T are taken; every candidate if at most k.
+  const uint32_t kk = (uint32_t)k;
+  constexpr int kPer = kLocalSlots / 256;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) cnt += lk[tid + 256 * j] != 0u ? 1u : 0u;
+  uint32_t total;
+  block_exclusive_scan<256>(cnt, wave_sum, &total);
+  uint32_t T = 1u, ties = 0u;
+  if (total > kk) {
+    for (int i = tid; i < kTopkBins; i += 256) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t key = lk[tid + 256 * j];
+      if (key) atomicAdd(&hist[key >> 20], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin<256>(hist, kTopkBins, kk, wave_sum, found);
+    const uint32_t b1 = found[0], need1 = kk - found[1];
+    for (int i = tid; i < kTopkBins; i += 256) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t key = lk[tid + 256 * j];
+      if (key && (key >> 20) == b1) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin<256>(hist, kTopkBins, need1, wave_sum, found);
+    const uint32_t pre2 = (b1 << 12) | found[0], need2 = need1 - found[1];
+    for (int i = tid; i < 256; i += 256) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t key = lk[tid + 256 * j];
+      if (key && (key >> 8) == pre2) atomicAdd(&hist[key & 0xFFu], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin<256>(hist, 256, need2, wave_sum, found);
+    T = (pre2 << 8) | found[0];
+    ties = need2 - found[1];
+  }
+  // Selection and tie bitmaps of the range by ballots over 64-slot groups.
+#pragma unroll 4
+  for (int r = 0; r < kLocalSlots / 256; ++r) {
+    const int s0 = (wave + 4 * r) * 64;
+    const uint32_t key = lk[s0 + lane];
+    const uint64_t ms = __ballot(ties > 0 ? key > T : key >= T);  // T >= 1: key 0 never taken
+    const uint64_t mt = __ballot(ties > 0 && key == T);
+    if (lane == 0) {
+      selw[s0 >> 5] = (uint32_t)ms;
+      tiew[s0 >> 5] = (uint32_t)mt;
+    } else if (lane == 32) {
+      selw[(s0 >> 5) + 1] = (uint32_t)(ms >> 32);
+      tiew[(s0 >> 5) + 1] = (uint32_t)(mt >> 32);
+    }
+  }
+  __syncthreads();
+  // Thread tid owns word tid (slots 32 tid .. +31): the lowest `ties` tie
+  // slots join, then the candidates go out in slot order.
+  uint32_t sw = selw[tid];
+  if (ties > 0) {
+    uint32_t x = tiew[tid];
+    uint32_t dummy;
+    const uint32_t rank = block_exclusive_scan<256>(__popc(x), wave_sum, &dummy);
+    if (rank < ties) {
+      if (rank + __popc(x) > ties)
+        for (uint32_t m = rank; m < ties; ++m) {
+          sw |= x & (0u - x);
+          x &= x - 1;
+        }
+      else
+        sw |= x;
+    }
+  }
+  uint32_t n_sel;
+  uint32_t pos = block_exclusive_scan<256>(__popc(sw), wave_sum, &n_sel);
+  const int64_t c0 = ((int64_t)b * gridDim.x + blockIdx.x) * kk;
+  float* cs = cand_score + c0;
+  int32_t* ci = cand_slot + c0;
+  while (sw) {
+    const int bit = __ffs(sw) - 1;
+    sw &= sw - 1;
+    const int local = 32 * tid + bit;
+    if (pos < kk) {
+      cs[pos] = order_key_value(lk[local]);
+      ci[pos] = (int32_t)(s_begin + local);
+    }
+    ++pos;
+  }
+  for (uint32_t i = n_sel + tid; i < kk; i += 256) {
+    cs[i] = kNegInf;
+    ci[i] = 0;
+  }
+}
+
 }  // namespace
 
 csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
@@ -270,6 +440,26 @@ csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t
 }  // namespace csa2
 
 namespace csa2 {
+
+// Workgroups per sequence of the flat scoring with local selection.
+int64_t index_score_local_groups(int64_t key_cap) { return (key_cap + kLocalSlots - 1) / kLocalSlots; }
+
+csa2_status index_score_local_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                                     const int32_t* lens, int32_t k, float* cand_score, int32_t* cand_slot,
+                                     int32_t n_seq, hipStream_t stream) {
+  if (n_seq == 0 || key_cap == 0) return CSA2_OK;
+  const int64_t groups = index_score_local_groups(key_cap);
+  CSA2_REQUIRE(groups <= 0x7FFFFFFF && n_seq <= 65535 && k >= 1 && k <= CSA2_TOPK_MAX, CSA2_ESHAPE,
+               "flat local selection: bad shape");
+  const dim3 grid((uint32_t)groups, (uint32_t)n_seq);
+  if (w)
+    hipLaunchKernelGGL(index_score_local_kernel<true>, grid, dim3(256), 0, stream, q, w, keys, key_cap, lens, k,
+                       cand_score, cand_slot);
+  else
+    hipLaunchKernelGGL(index_score_local_kernel<false>, grid, dim3(256), 0, stream, q, w, keys, key_cap, lens, k,
+                       cand_score, cand_slot);
+  return launch_status("csa2_index_score (local selection)");
+}
 
 csa2_status prefill_score_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t n_entries,
                                  int64_t t0, int32_t ratio, int32_t n_q, float* scores, int32_t* n_vis,

@@ -21,6 +21,7 @@ csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, i
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
                                uint32_t*, hipStream_t);
+int64_t index_score_local_groups(int64_t key_cap);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
@@ -43,6 +44,11 @@ struct csa2_sched {
   int32_t* pool = nullptr;      // [n_seq][pool_blocks]
   float* scores = nullptr;      // [n_seq][scores_n]
   int64_t scores_n = 0;
+  // Flat selection over more than kTopkRowsMax positions: per-workgroup
+  // Top-k candidates (local_groups * topk per sequence, scores in `scores`,
+  // positions here), then one selection over them.
+  int64_t local_groups = 0;
+  int32_t* cand_slot = nullptr;  // [n_seq][local_groups * topk]
   void* attn_ws = nullptr;
   size_t attn_ws_bytes = 0;
   void* topk_ws = nullptr;      // Top-k workspace (histogram, counters, bitmap, candidates)
@@ -58,6 +64,7 @@ void free_sched(csa2_sched* s) {
   hipFree(s->idx_bufs);
   hipFree(s->pool);
   hipFree(s->scores);
+  hipFree(s->cand_slot);
   hipFree(s->attn_ws);
   hipFree(s->topk_ws);
   hipFree(s->err);
@@ -159,6 +166,8 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
       return CSA2_ESHAPE;
     }
     s->scores_n = std::max<int64_t>(s->scores_n, d.key_cap);
+    const int64_t groups = index_score_local_groups(d.key_cap);
+    if (d.key_cap > kTopkRowsMax && groups * d.topk <= kTopkRowsMax) s->local_groups = groups;
   }
   s->attn_ws_bytes = attn_workspace_bytes(d.n_seq, d.topk, d.swa_max);
   s->topk_ws_bytes = topk_workspace_bytes(s->scores_n, d.n_seq);
@@ -166,6 +175,7 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
   if ((st = dev_alloc(&s->idx_bufs, (size_t)s->n_idx_bufs * n * d.topk * sizeof(int32_t))) != CSA2_OK ||
       (st = dev_alloc(&s->pool, s->any_hier ? n * d.pool_blocks * sizeof(int32_t) : 0)) != CSA2_OK ||
       (st = dev_alloc(&s->scores, n * (size_t)s->scores_n * sizeof(float))) != CSA2_OK ||
+      (st = dev_alloc(&s->cand_slot, n * (size_t)(s->local_groups * d.topk) * sizeof(int32_t))) != CSA2_OK ||
       (st = dev_alloc(&s->attn_ws, s->attn_ws_bytes)) != CSA2_OK ||
       (st = dev_alloc(&s->topk_ws, s->topk_ws_bytes)) != CSA2_OK ||
       (st = dev_alloc(&s->err, sizeof(int32_t))) != CSA2_OK) {
@@ -261,12 +271,14 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
           st = topk_launch(s->scores, n_out, nullptr, 1, d.topk, s->pool, d.pool_blocks, d.blk, idx, s->tw, fused,
                            d.n_seq, stream);
       } else {
-        const bool fused = d.key_cap > kTopkRowsMax;
-        st = index_score_launch(io->idx_q[l], w, keys, d.key_cap, io->lens, 1, nullptr, 0, 1, s->scores,
-                                d.key_cap, d.n_seq, fused ? s->tw.hist : nullptr, stream);
-        if (st == CSA2_OK)
-          st = topk_launch(s->scores, d.key_cap, io->lens, 1, d.topk, nullptr, 0, 1, idx, s->tw, fused, d.n_seq,
-                           stream);
+        // Flat: all positions (csa2_flat_select's path, on the scheduler's buffers).
+        FlatSelectWs f{};
+        f.local_groups = s->local_groups;
+        f.n_scores = s->local_groups ? s->local_groups * d.topk : d.key_cap;
+        f.scores = s->scores;
+        f.cand = s->cand_slot;
+        f.tw = s->tw;
+        st = flat_select_launch(io->idx_q[l], w, keys, d.key_cap, io->lens, d.topk, idx, f, d.n_seq, stream);
       }
     }
     if (st == CSA2_OK)

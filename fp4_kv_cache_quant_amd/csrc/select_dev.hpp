@@ -1,0 +1,69 @@
+// Workgroup-wide building blocks of the radix selections (internal; used by
+// the Top-k kernels and by the scoring kernel's per-workgroup selection).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Exclusive prefix sum over a workgroup of NT threads in thread order.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sum, uint32_t* total) {
+  constexpr int kW = NT / 64;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_sum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kW; ++i) {
+    const uint32_t s = wave_sum[i];
+    before += (i < wave) ? s : 0u;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// Largest bin B of hist[0..nbins) with (count of bins >= B) >= need, and the
+// count of bins > B, written to out[0], out[1]; requires 1 <= need <= total.
+template <int NT>
+__device__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* wave_sum,
+                                   uint32_t* out) {
+  const int per = (nbins + NT - 1) / NT;
+  const int t = threadIdx.x;
+  const int hi = nbins - t * per;  // thread t owns bins [hi - per, hi), top bins first
+  const int lo = hi - per > 0 ? hi - per : 0;
+  uint32_t mine = 0;
+  for (int i = lo; i < hi; ++i) mine += hist[i];
+  uint32_t total;
+  const uint32_t above = block_exclusive_scan<NT>(hi > 0 ? mine : 0u, wave_sum, &total);
+  if (hi > 0 && above < need && above + mine >= need) {
+    uint32_t acc = above;
+    for (int i = hi - 1; i >= lo; --i) {
+      if (acc + hist[i] >= need) {
+        out[0] = (uint32_t)i;
+        out[1] = acc;
+        break;
+      }
+      acc += hist[i];
+    }
+  }
+  __syncthreads();
+}
+
+// The score whose order key (order_key in topk_ws.hpp) is key != 0.
+__device__ __forceinline__ float order_key_value(uint32_t key) {
+  return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+}  // namespace csa2

@@ -27,6 +27,7 @@
 // Context, FP4 KV Cache, and Cross-Layer Attention Reuse".
 #include "common.hpp"
 #include "topk_ws.hpp"
+#include "select_dev.hpp"
 
 namespace csa2 {
 namespace {
@@ -40,13 +41,6 @@ constexpr int kFilterSlots = kTopkFilterSlots;     // slots per filter workgroup
 static_assert(kFilterSlots == kPassThreads * 32, "filter: 32 slots per thread");
 constexpr int kDirectMax = 32768;                 // final kernel filters inputs up to this length itself
 constexpr size_t kCandBytes = kTopkCandCap * sizeof(uint2);  // candidate buffer per sequence
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-__device__ __forceinline__ uint64_t lanes_below() {
-  const int l = lane_id();
-  return l == 0 ? 0ull : (~0ull >> (64 - l));
-}
 
 __device__ __forceinline__ int64_t valid_slots(int64_t n, const int32_t* lens, int32_t len_div, int b) {
   if (!lens) return n;
@@ -67,58 +61,6 @@ __device__ __forceinline__ void wave_hist_add_grouped(uint32_t* hist, uint32_t b
     pending &= ~same;
     active = active && bin != lb;
   }
-}
-
-// Exclusive prefix sum over a workgroup of NT threads in thread order.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sum, uint32_t* total) {
-  constexpr int kW = NT / 64;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wave_sum[wave] = x;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < kW; ++i) {
-    const uint32_t s = wave_sum[i];
-    before += (i < wave) ? s : 0u;
-    all += s;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
-}
-
-// Largest bin B of hist[0..nbins) with (count of bins >= B) >= need, and the
-// count of bins > B, written to out[0], out[1]; requires 1 <= need <= total.
-template <int NT>
-__device__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* wave_sum,
-                                   uint32_t* out) {
-  const int per = (nbins + NT - 1) / NT;
-  const int t = threadIdx.x;
-  const int hi = nbins - t * per;  // thread t owns bins [hi - per, hi), top bins first
-  const int lo = hi - per > 0 ? hi - per : 0;
-  uint32_t mine = 0;
-  for (int i = lo; i < hi; ++i) mine += hist[i];
-  uint32_t total;
-  const uint32_t above = block_exclusive_scan<NT>(hi > 0 ? mine : 0u, wave_sum, &total);
-  if (hi > 0 && above < need && above + mine >= need) {
-    uint32_t acc = above;
-    for (int i = hi - 1; i >= lo; --i) {
-      if (acc + hist[i] >= need) {
-        out[0] = (uint32_t)i;
-        out[1] = acc;
-        break;
-      }
-      acc += hist[i];
-    }
-  }
-  __syncthreads();
 }
 
 // Threshold state every filter/final workgroup derives from the histogram.
@@ -269,7 +211,7 @@ __device__ __forceinline__ void load_round(const uint32_t* bm, int q0, int r, in
 // -1 pads the row to k.
 __device__ void finish_output_lds(uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
                                   const int32_t* pool_lds, int32_t blk, uint32_t* wave_sum,
-                                  int32_t* __restrict__ ob) {
+                                  int32_t* __restrict__ ob, const int32_t* __restrict__ gid = nullptr) {
   const int tid = threadIdx.x;
   const int per = (words + kFinalThreads - 1) / kFinalThreads;
   const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
@@ -307,6 +249,7 @@ __device__ void finish_output_lds(uint32_t* sel, const uint32_t* tie, int words,
       const int64_t slot = (int64_t)w * 32 + bit;
       int64_t id = slot;
       if (pool_lds) id = (int64_t)pool_lds[slot / blk] * blk + slot % blk;
+      if (gid) id = gid[slot];
       if (pos < kk) ob[pos] = (int32_t)id;
       ++pos;
     }
@@ -683,9 +626,12 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
                                                                   int32_t len_div, int32_t k,
                                                                   const int32_t* __restrict__ pool,
                                                                   int32_t n_pool, int32_t blk,
-                                                                  int32_t* __restrict__ out) {
+                                                                  int32_t* __restrict__ out,
+                                                                  const int32_t* __restrict__ gids) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
+  // gids: [n_seq][n] ids emitted for the slots (else the slot, or the pool's)
+  const int32_t* gid = gids ? gids + (int64_t)blockIdx.x * n : nullptr;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int nvalid = (int)valid_slots(n, lens, len_div, b);
@@ -755,7 +701,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
           }
           __syncthreads();
           finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
-                            out + (int64_t)b * k);
+                            out + (int64_t)b * k, gid);
           return;
         }
       }
@@ -825,7 +771,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
   }
   __syncthreads();
   finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
-                    out + (int64_t)b * k);
+                    out + (int64_t)b * k, gid);
 }
 
 }  // namespace
@@ -860,8 +806,10 @@ TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq) {
 
 csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
                         const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, const TopkWs& ws,
-                        bool hist_ready, int32_t n_seq, hipStream_t stream) {
+                        bool hist_ready, int32_t n_seq, hipStream_t stream, const int32_t* gids) {
   if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(!gids || (!hist_ready && !pool && n <= kRowsMax), CSA2_EINVAL,
+               "csa2_topk: emitted ids need the single-workgroup selection");
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_final_kernel<false>),
@@ -882,13 +830,13 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
   if (!hist_ready && n <= kRowsMax) {
     if (n <= 16 * kFinalThreads)
       hipLaunchKernelGGL(topk_rows_kernel<16>, dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream, scores,
-                         n, lens, len_div, k, pool, n_pool, blk, out);
+                         n, lens, len_div, k, pool, n_pool, blk, out, gids);
     else if (n <= 32 * kFinalThreads)
       hipLaunchKernelGGL(topk_rows_kernel<32>, dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream, scores,
-                         n, lens, len_div, k, pool, n_pool, blk, out);
+                         n, lens, len_div, k, pool, n_pool, blk, out, gids);
     else
       hipLaunchKernelGGL(topk_rows_kernel<64>, dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream, scores,
-                         n, lens, len_div, k, pool, n_pool, blk, out);
+                         n, lens, len_div, k, pool, n_pool, blk, out, gids);
     return launch_status("csa2_topk");
   }
   if (!hist_ready && n > 0)

@@ -46,9 +46,26 @@ constexpr int64_t kTopkRowsMax = 65536;
 size_t topk_workspace_bytes(int64_t n, int32_t n_seq);
 TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq);
 // hist_ready: ws.hist already holds the histogram of these scores (written by
-// the indexer-score kernel), so the histogram pass is skipped.
+// the indexer-score kernel), so the histogram pass is skipped.  gids: if not
+// NULL, [n_seq][n] ids emitted in place of the slots (inputs of at most
+// kTopkRowsMax slots, no pool, no ready histogram).
 csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
                         const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, const TopkWs& ws,
-                        bool hist_ready, int32_t n_seq, hipStream_t stream);
+                        bool hist_ready, int32_t n_seq, hipStream_t stream, const int32_t* gids = nullptr);
+
+// A flat Full layer's selection (scores + Top-k) and its workspace
+// (csa2_flat_select; the scheduler's flat layers).
+struct FlatSelectWs {
+  int64_t local_groups;  // > 0: per-workgroup candidates (ceil(key_cap / 8192) groups)
+  int64_t n_scores;      // scores per sequence: local_groups * k, or key_cap
+  float* scores;         // [n_seq][n_scores]
+  int32_t* cand;         // [n_seq][n_scores] candidate positions (local mode)
+  TopkWs tw;
+  size_t bytes;
+};
+FlatSelectWs flat_select_ws(int64_t key_cap, int32_t k, int32_t n_seq, void* base);
+csa2_status flat_select_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                               const int32_t* lens, int32_t k, int32_t* out, const FlatSelectWs& f, int32_t n_seq,
+                               hipStream_t stream);
 
 }  // namespace csa2

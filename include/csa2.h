@@ -153,6 +153,26 @@ csa2_status csa2_topk(const float* scores, int64_t n, const int32_t* lens, int32
                       const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, void* ws,
                       size_t ws_bytes, int32_t n_seq, void* stream);
 
+/* Steps (b)+(c) of a flat Full layer in one call [P1 "Compressed Sparse
+ * Attention 2 (CSA2)"]: a fresh Top-k over all positions.  The result equals
+ * csa2_index_score (flat, len_div 1, n_out = key_cap) followed by csa2_topk
+ * (n = key_cap, lens): out [n_seq][k] int32, ascending positions, -1
+ * padded.  For key_cap > 65,536 with ceil(key_cap / 8,192) * k <= 65,536
+ * the scores are not written out: every scoring workgroup keeps the Top-k
+ * (score descending, position ascending) of its 8,192 positions, and one
+ * selection runs over those candidates; otherwise the scores go through
+ * csa2_topk's passes.
+ *   q [n_seq][8][64] bf16, w [n_seq][8] f32 or NULL, keys [n_seq][key_cap][64]
+ *   bf16 (q, keys 16-byte aligned), lens [n_seq] int32 (device)
+ *   ws: csa2_flat_select_workspace_size(key_cap, k, n_seq) bytes, 256-byte
+ *   aligned, zero-filled before its first use and left ready for the next
+ *   call (calls sharing it must not overlap).
+ * Limits: 1 <= k <= CSA2_TOPK_MAX, 1 <= key_cap <= CSA2_TOPK_NMAX. */
+size_t csa2_flat_select_workspace_size(int64_t key_cap, int32_t k, int32_t n_seq);
+csa2_status csa2_flat_select(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, int32_t k, int32_t* out, void* ws, size_t ws_bytes, int32_t n_seq,
+                             void* stream);
+
 /* Steps (d)+(e): sparse + SWA attention of n_q queries.
  * [P1 "Compressed Sparse Attention 2 (CSA2)"]: each layer attends with its
  * own main Q over the selected main-KV rows; [P1 "Causal Encoder-Decoder:

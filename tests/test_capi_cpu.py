@@ -158,3 +158,19 @@ def test_key_maintenance_rejects_bad_arguments(csa2):
     assert csa2._append_keys(FAKE, FAKE, 0, None, 0, 8, FAKE, None, 1, None) == -2
     assert csa2._append_keys(FAKE, FAKE, 100, FAKE, 0, 8, FAKE, None, 1, None) == -2
     assert csa2._append_keys(None, FAKE, 100, None, 0, 8, FAKE, None, 1, None) == -1
+
+
+def test_flat_select_rejects_bad_arguments(csa2):
+    def call(q=FAKE, keys=FAKE, key_cap=1000, lens=FAKE, k=512, out=FAKE, ws=FAKE * 16, ws_bytes=1 << 30, n_seq=1):
+        return csa2._flat_select(q, None, keys, key_cap, lens, k, out, ws, ws_bytes, n_seq, None)
+
+    assert call(n_seq=0, q=None) == 0
+    assert call(q=None) == -1 and "null" in _err(csa2)
+    assert call(key_cap=0) == -2 and call(key_cap=(1 << 20) + 1) == -2
+    assert call(k=0) == -2 and call(k=4096) == -2
+    assert call(ws=FAKE * 16 + 16) == -1 and "alignment" in _err(csa2)
+    assert call(ws_bytes=csa2.flat_select_workspace_size(1000, 512, 1) - 1) == -3
+    assert csa2.flat_select_workspace_size(0, 512, 1) == 0
+    assert csa2.flat_select_workspace_size(1000, 0, 1) == 0
+    # long inputs keep per-workgroup candidates instead of every score
+    assert csa2.flat_select_workspace_size(1 << 19, 512, 1) < csa2.flat_select_workspace_size(1 << 19, 2048, 1)

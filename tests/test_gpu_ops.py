@@ -273,6 +273,34 @@ def test_topk_sampled_first_pass_and_fallback(csa2, case):
         assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), b
 
 
+@pytest.mark.parametrize("key_cap,k,lens,weights", [
+    (5000, 512, (5000, 1234), False),           # scores in registers
+    (300001, 512, (300001, 150000), False),     # per-workgroup candidates
+    (300001, 512, (299999, 8192), True),
+    (300001, 2048, (300001, 100), False),       # too many candidates: multi-workgroup passes
+    (1 << 20, 512, (1 << 20, 700001), False),   # the largest input, 65,536 candidates
+])
+def test_flat_select_matches_oracle(csa2, key_cap, k, lens, weights):
+    """Scoring + Top-k of a flat Full layer in one call against the oracle's
+    flat selection (every position scored, ties to the lower position)."""
+    n_seq = 2
+    rng = np.random.default_rng(key_cap + k + int(weights))
+    keys = _bf16_of(rng.integers(-4, 5, size=(n_seq, key_cap, 64)))
+    q = _bf16_of(rng.integers(-4, 5, size=(n_seq, 8, 64)))
+    w = (rng.integers(-2, 5, size=(n_seq, 8)) * 0.25).astype(np.float32) if weights else None
+    L = np.array(lens, np.int32)
+    print_case(f"flat_select key_cap={key_cap} k={k} lens={lens} weights={weights}")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(csa2.flat_select_workspace_size(key_cap, k, n_seq), dtype=torch.uint8, device="cuda")
+    for rep in range(2):  # the workspace is left ready for the next call
+        out.fill_(-7)
+        csa2.flat_select(dev(q), dev(keys), dev(L), k, out, w=dev(w) if weights else None, ws=ws)
+        got = out.cpu().numpy()
+        for b in range(n_seq):
+            ref = oracle.flat_select(q[b], keys[b], int(L[b]), k, None if w is None else w[b])
+            assert np.array_equal(got[b], ref), (rep, b)
+
+
 def test_topk_signed_scores_and_zero_signs(csa2):
     rng = np.random.default_rng(11)
     sc = rng.standard_normal((1, 10000)).astype(np.float32)

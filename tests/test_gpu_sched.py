@@ -36,6 +36,9 @@ CASES = {
     "encoder_small": (C.ENCODER_DECODE_1M.with_(n_seq=2, L0=3001, q_sets=2), 2),
     # more entries than the selection bitmaps held in LDS (262,144)
     "encoder_long": (C.ENCODER_DECODE_1M.with_(n_seq=2, L0=300001, q_sets=1), 1),
+    # Top-2048 over 300K entries: too many per-workgroup candidates, so the
+    # scores go through the multi-workgroup selection instead
+    "encoder_long_k2048": (C.ENCODER_DECODE_1M.with_(n_seq=2, L0=300001, q_sets=1, topk=2048), 1),
     # a long Reuse run, and Reuse layers on another main-KV tensor
     "long_reuse_runs": (C.GROUP_64K.with_(n_seq=3, L0=2000, n_kv=2, q_sets=1,
                                           layers=((C.FULL, 0, 0),) + ((C.REUSE, 0, 0),) * 9
