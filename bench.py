@@ -38,15 +38,29 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12723702, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12717585, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "991309ea238dda775e1d2f8fe2792014ac15dd5b85e69a39c9f57fc29b62eeea",
+                    "508c46d92b6016cc852a4a7794e7ba9213529cf20c9c659cd5e5d6635cc4147f",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
     "decoder20_1m/block_scan": {
-        "bytes": 280505480, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 280629996, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "09113af17f5d097f1846767696db3f52df3c62a024bc9ad0131063f1fb518436",
+                    "af29e44c8007dccd689393411e9d26d8ad567080bde04a206c3fbc78cf6e522a",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f",
+                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
+                    "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd"}},
+    "encoder_1m/flat_select": {
+        "bytes": 1092880833, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                    "af29e44c8007dccd689393411e9d26d8ad567080bde04a206c3fbc78cf6e522a",
+                    "fp4_kv_cache_quant_amd/csrc/topk.hip":
+                    "6d46b15f2af93b25f3ba2fd475d2ef028189ee174e5a5ebb5177bd7688413025",
+                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
+                    "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd",
+                    "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
+                    "0cf1a9d6daa7131df4a77d382313cdef8022ac6ffe96aaf1f554de38066f1737",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
 }
