@@ -34,6 +34,58 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return before + x - v;
 }
 
+// The same scan with a single barrier: wave_sum (kW words) must not be
+// written again by this workgroup -- each call site owns its slot.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan_once(uint32_t v, uint32_t* wave_sum, uint32_t* total) {
+  constexpr int kW = NT / 64;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_sum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kW; ++i) {
+    const uint32_t s = wave_sum[i];
+    before += (i < wave) ? s : 0u;
+    all += s;
+  }
+  *total = all;
+  return before + x - v;
+}
+
+// Two exclusive prefix sums at once (a.x and a.y), one barrier; wave_sum
+// holds 2 * NT / 64 words owned by the call site as above.
+template <int NT>
+__device__ __forceinline__ uint2 block_exclusive_scan2_once(uint2 v, uint32_t* wave_sum, uint2* total) {
+  constexpr int kW = NT / 64;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  uint32_t x = v.x, y = v.y;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t xs = __shfl_up(x, d), ys = __shfl_up(y, d);
+    if (lane >= d) x += xs, y += ys;
+  }
+  if (lane == 63) wave_sum[wave] = x, wave_sum[kW + wave] = y;
+  __syncthreads();
+  uint2 before = make_uint2(0u, 0u), all = make_uint2(0u, 0u);
+#pragma unroll
+  for (int i = 0; i < kW; ++i) {
+    const uint32_t sx = wave_sum[i], sy = wave_sum[kW + i];
+    before.x += (i < wave) ? sx : 0u;
+    before.y += (i < wave) ? sy : 0u;
+    all.x += sx;
+    all.y += sy;
+  }
+  *total = all;
+  return make_uint2(before.x + x - v.x, before.y + y - v.y);
+}
+
 // Largest bin B of hist[0..nbins) with (count of bins >= B) >= need, and the
 // count of bins > B, written to out[0], out[1]; requires 1 <= need <= total.
 template <int NT>
@@ -47,6 +99,33 @@ __device__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t nee
   for (int i = lo; i < hi; ++i) mine += hist[i];
   uint32_t total;
   const uint32_t above = block_exclusive_scan<NT>(hi > 0 ? mine : 0u, wave_sum, &total);
+  if (hi > 0 && above < need && above + mine >= need) {
+    uint32_t acc = above;
+    for (int i = hi - 1; i >= lo; --i) {
+      if (acc + hist[i] >= need) {
+        out[0] = (uint32_t)i;
+        out[1] = acc;
+        break;
+      }
+      acc += hist[i];
+    }
+  }
+  __syncthreads();
+}
+
+// find_threshold_bin in two barriers: wave_sum (NT / 64 words) is owned by
+// the call site and never reused in the workgroup.
+template <int NT>
+__device__ void find_threshold_bin_once(const uint32_t* hist, int nbins, uint32_t need, uint32_t* wave_sum,
+                                        uint32_t* out) {
+  const int per = (nbins + NT - 1) / NT;
+  const int t = threadIdx.x;
+  const int hi = nbins - t * per;
+  const int lo = hi - per > 0 ? hi - per : 0;
+  uint32_t mine = 0;
+  for (int i = lo; i < hi; ++i) mine += hist[i];
+  uint32_t total;
+  const uint32_t above = block_exclusive_scan_once<NT>(hi > 0 ? mine : 0u, wave_sum, &total);
   if (hi > 0 && above < need && above + mine >= need) {
     uint32_t acc = above;
     for (int i = hi - 1; i >= lo; --i) {

@@ -205,44 +205,43 @@ __device__ __forceinline__ void load_round(const uint32_t* bm, int q0, int r, in
 }
 
 // Selection bitmap sel (and, if ties > 0, the tie bitmap tie: keys equal to
-// the threshold) of one sequence, in LDS -> the ids in ascending order: the
-// lowest `ties` tie slots join the selection, then every thread owns a
-// contiguous run of words and writes its ids at its prefix-count position;
-// -1 pads the row to k.
-__device__ void finish_output_lds(uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
-                                  const int32_t* pool_lds, int32_t blk, uint32_t* wave_sum,
+// the threshold) of one sequence, in LDS -> the ids in ascending order.
+// Every thread owns a contiguous run of words; one scan gives, per run, the
+// selected and the tie bits before it.  The lowest `ties` tie bits join the
+// selection, so a run's first output position is (selected before) +
+// min(ties before, ties).  -1 pads the row to k.  fin_sum: 2 * kFinalWaves
+// words used by nothing else; the caller has synchronised after its last
+// write of sel / tie.
+__device__ void finish_output_lds(const uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
+                                  const int32_t* pool_lds, int32_t blk, uint32_t* fin_sum,
                                   int32_t* __restrict__ ob, const int32_t* __restrict__ gid = nullptr) {
   const int tid = threadIdx.x;
   const int per = (words + kFinalThreads - 1) / kFinalThreads;
   const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
-  if (ties > 0) {
-    uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(tie[w]);
-    uint32_t dummy;
-    uint32_t rank = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &dummy);
-    for (int w = w0; w < w1 && rank < ties; ++w) {
-      uint32_t x = tie[w];
-      const uint32_t pc = __popc(x);
-      if (rank + pc <= ties) {
-        sel[w] |= x;
-      } else {
-        uint32_t keep = 0;
-        for (uint32_t m = rank; m < ties; ++m) {
-          keep |= x & (0u - x);
-          x &= x - 1;
-        }
-        sel[w] |= keep;
-      }
-      rank += pc;
-    }
-    __syncthreads();
+  uint2 cnt = make_uint2(0u, 0u);
+  for (int w = w0; w < w1; ++w) {
+    cnt.x += __popc(sel[w]);
+    if (ties > 0) cnt.y += __popc(tie[w]);
   }
-  uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
-  uint32_t n_sel;
-  uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, wave_sum, &n_sel);
+  uint2 tot;
+  const uint2 before = block_exclusive_scan2_once<kFinalThreads>(cnt, fin_sum, &tot);
+  uint32_t pos = before.x + min(before.y, ties);
+  uint32_t trank = before.y;  // tie bits before the current word
   for (int w = w0; w < w1; ++w) {
     uint32_t x = sel[w];
+    if (ties > 0 && trank < ties) {
+      uint32_t t = tie[w];
+      const uint32_t pc = __popc(t);
+      if (trank + pc <= ties) {
+        x |= t;
+      } else {
+        for (uint32_t m = trank; m < ties; ++m) {
+          x |= t & (0u - t);
+          t &= t - 1;
+        }
+      }
+      trank += pc;
+    }
     while (x) {
       const int bit = __ffs(x) - 1;
       x &= x - 1;
@@ -254,6 +253,7 @@ __device__ void finish_output_lds(uint32_t* sel, const uint32_t* tie, int words,
       ++pos;
     }
   }
+  const uint32_t n_sel = tot.x + min(tot.y, ties);
   for (uint32_t i = n_sel + tid; i < kk; i += kFinalThreads) ob[i] = -1;
 }
 
@@ -361,6 +361,7 @@ struct FinalSmem {
   uint32_t wc_off[kTopkFilterWgMax];  // first LDS candidate of each filter workgroup
   uint32_t wc_cnt[kTopkFilterWgMax];  // its candidate count
   uint32_t wave_sum[kFinalWaves];
+  uint32_t fin_sum[2 * kFinalWaves];  // the output scan's own
   uint32_t found[2];
 };
 
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const float* 
   if constexpr (kGlobal)
     finish_output_global(sel, tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum, out + (int64_t)b * k);
   else
-    finish_output_lds(sel, tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum, out + (int64_t)b * k);
+    finish_output_lds(sel, tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.fin_sum, out + (int64_t)b * k);
 }
 
 
@@ -574,48 +575,50 @@ constexpr int kRowsCand = 8192;  // keys kept by the sampled first pass
 
 struct RowsSmem {
   int32_t pool[CSA2_TOPK_MAX];
-  uint32_t hist[kTopkBins];
+  uint32_t hist[kTopkBins];   // the samples' top digits; the full passes' digits
+  uint32_t hist1[kTopkBins];  // top digit of the candidates
+  uint32_t hist2[kTopkBins];  // middle digit of the candidates in the threshold bin
+  uint32_t hist3[256];        // low digit
   uint32_t sel[kRowsMax / 32];
   uint32_t tie[kRowsMax / 32];
   uint32_t cand_key[kRowsCand];
   uint32_t cand_slot[kRowsCand];
   uint32_t wave_sum[kFinalWaves];
+  uint32_t scan_sum[4][kFinalWaves];  // one per scan of the sampled path (never reused)
+  uint32_t fin_sum[2 * kFinalWaves];  // the output scan's own
+  uint32_t counter[2];                // sampled keys, candidates
   uint32_t found[2];
 };
 
-// The exact kk-th largest key T among the nc keys ck[0..nc) (1 <= kk <= nc)
-// and how many keys equal to T are taken (ties): radix select over digits
-// of 12, 12 and 8 bits with LDS histograms, every thread taking keys
+static_assert(sizeof(RowsSmem) <= 160 * 1024, "one workgroup's LDS");
+
+// The exact kk-th largest key T among the nc candidate keys ck[0..nc)
+// (1 <= kk <= nc) and how many keys equal to T are taken (ties), given the
+// candidates' top-digit histogram hist1 (complete, and hist2 / hist3 zero):
+// radix select over digits of 12, 12 and 8 bits, every thread taking keys
 // tid, tid + NT, ...  Called by the whole workgroup.
 template <int NT>
-__device__ void select_among(const uint32_t* ck, int nc, uint32_t kk, uint32_t* hist, uint32_t* wave_sum,
-                             uint32_t* found, uint32_t& T, uint32_t& ties) {
+__device__ void select_candidates(const uint32_t* ck, int nc, uint32_t kk, const uint32_t* hist1,
+                                  uint32_t* hist2, uint32_t* hist3, uint32_t (*scan_sum)[NT / 64],
+                                  uint32_t* found, uint32_t& T, uint32_t& ties) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
-  __syncthreads();
-  for (int c = tid; c < nc; c += NT) atomicAdd(&hist[ck[c] >> 20], 1u);
-  __syncthreads();
-  find_threshold_bin<NT>(hist, kTopkBins, kk, wave_sum, found);
+  find_threshold_bin_once<NT>(hist1, kTopkBins, kk, scan_sum[1], found);
   const uint32_t b1 = found[0];
   const uint32_t need1 = kk - found[1];
-  for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
-  __syncthreads();
   for (int c = tid; c < nc; c += NT) {
     const uint32_t key = ck[c];
-    if ((key >> 20) == b1) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
+    if ((key >> 20) == b1) atomicAdd(&hist2[(key >> 8) & 0xFFFu], 1u);
   }
   __syncthreads();
-  find_threshold_bin<NT>(hist, kTopkBins, need1, wave_sum, found);
+  find_threshold_bin_once<NT>(hist2, kTopkBins, need1, scan_sum[2], found);
   const uint32_t pre2 = (b1 << 12) | found[0];
   const uint32_t need2 = need1 - found[1];
-  for (int i = tid; i < 256; i += NT) hist[i] = 0;
-  __syncthreads();
   for (int c = tid; c < nc; c += NT) {
     const uint32_t key = ck[c];
-    if ((key >> 8) == pre2) atomicAdd(&hist[key & 0xFFu], 1u);
+    if ((key >> 8) == pre2) atomicAdd(&hist3[key & 0xFFu], 1u);
   }
   __syncthreads();
-  find_threshold_bin<NT>(hist, 256, need2, wave_sum, found);
+  find_threshold_bin_once<NT>(hist3, 256, need2, scan_sum[3], found);
   T = (pre2 << 8) | found[0];
   ties = need2 - found[1];
 }
@@ -653,16 +656,23 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
     const int32_t* pb = pool + (int64_t)b * n_pool;
     for (int i = tid; i < n_pool; i += kFinalThreads) sm.pool[i] = pb[i];
   }
-  for (int i = tid; i < kTopkBins; i += kFinalThreads) sm.hist[i] = 0;
+  for (int i = tid; i < kTopkBins; i += kFinalThreads) sm.hist[i] = sm.hist1[i] = sm.hist2[i] = 0;
+  if (tid < 256) sm.hist3[tid] = 0;
+  for (int i = tid; i < words; i += kFinalThreads) sm.sel[i] = sm.tie[i] = 0;
+  if (tid < 2) sm.counter[tid] = 0;
   __syncthreads();
 
   // Sampled first pass.  One key per thread (slot (tid % kRowsPer) * NT +
   // tid, spread over the row) estimates a lower bound B for the top digit
   // of the k-th key: the bin where the samples counted from the top reach
   // r, about twice the samples that k keys would give.  Every key in bins
-  // >= B then goes to an LDS list, from which the exact threshold is
-  // selected -- if the list holds at least k keys (so it contains the k
-  // largest) and fits.  Otherwise the full passes below run.
+  // >= B then goes to an LDS list (positions from a wavefront scan and one
+  // LDS atomic per wavefront, so the list is unordered; the top-digit
+  // histogram of the list is counted on the way), from which the exact
+  // threshold is selected -- if the list holds at least k keys (so it
+  // contains the k largest) and fits.  Otherwise the full passes below run.
+  // Each scan here has its own wave-sum slot, so none needs a second
+  // barrier.
   {
     const int r = (int)(((int64_t)2 * kk * kFinalThreads + nvalid - 1) / max(nvalid, 1)) + 8;
     if (nvalid >= 4 * (int)kk && r <= kFinalThreads / 4) {  // uniform over the workgroup
@@ -671,36 +681,48 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
       for (int j = 0; j < kRowsPer; ++j)
         if (j == tid % kRowsPer) smp = key[j];
       if (smp) atomicAdd(&sm.hist[smp >> 20], 1u);
-      uint32_t n_smp;
-      block_exclusive_scan<kFinalThreads>(smp ? 1u : 0u, sm.wave_sum, &n_smp);  // syncs: histogram complete
-      if (n_smp >= (uint32_t)r) {
-        find_threshold_bin<kFinalThreads>(sm.hist, kTopkBins, (uint32_t)r, sm.wave_sum, sm.found);
+      const uint64_t has = __ballot(smp != 0);
+      if (lane_id() == 0) atomicAdd(&sm.counter[0], (uint32_t)__popcll(has));
+      __syncthreads();  // sample histogram and count complete
+      if (sm.counter[0] >= (uint32_t)r) {
+        find_threshold_bin_once<kFinalThreads>(sm.hist, kTopkBins, (uint32_t)r, sm.scan_sum[0], sm.found);
         const uint32_t lo = sm.found[0] << 20;  // keys >= lo are kept
         uint32_t cnt = 0;
 #pragma unroll
         for (int j = 0; j < kRowsPer; ++j) cnt += (key[j] >= lo && key[j] != 0) ? 1u : 0u;
-        uint32_t n_cand;
-        uint32_t pos = block_exclusive_scan<kFinalThreads>(cnt, sm.wave_sum, &n_cand);
-        if (n_cand >= kk && n_cand <= (uint32_t)kRowsCand) {
+        uint32_t incl = cnt;
 #pragma unroll
-          for (int j = 0; j < kRowsPer; ++j) {
-            if (key[j] >= lo && key[j] != 0) {
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint32_t y = __shfl_up(incl, d);
+          if (lane_id() >= d) incl += y;
+        }
+        uint32_t base = 0;
+        if (lane_id() == 63) base = atomicAdd(&sm.counter[1], incl);
+        uint32_t pos = __shfl(base, 63) + incl - cnt;
+#pragma unroll
+        for (int j = 0; j < kRowsPer; ++j) {
+          if (key[j] >= lo && key[j] != 0) {
+            if (pos < (uint32_t)kRowsCand) {
               sm.cand_key[pos] = key[j];
               sm.cand_slot[pos] = (uint32_t)(j * kFinalThreads + tid);
-              ++pos;
             }
+            atomicAdd(&sm.hist1[key[j] >> 20], 1u);
+            ++pos;
           }
-          for (int i = tid; i < words; i += kFinalThreads) sm.sel[i] = sm.tie[i] = 0;
-          __syncthreads();
+        }
+        __syncthreads();  // list, its histogram and its length complete
+        const uint32_t n_cand = sm.counter[1];
+        if (n_cand >= kk && n_cand <= (uint32_t)kRowsCand) {
           uint32_t T, ties;
-          select_among<kFinalThreads>(sm.cand_key, (int)n_cand, kk, sm.hist, sm.wave_sum, sm.found, T, ties);
+          select_candidates<kFinalThreads>(sm.cand_key, (int)n_cand, kk, sm.hist1, sm.hist2, sm.hist3,
+                                           sm.scan_sum, sm.found, T, ties);
           for (int c = tid; c < (int)n_cand; c += kFinalThreads) {
             const uint32_t key = sm.cand_key[c], i = sm.cand_slot[c];
             if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
             else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
           }
           __syncthreads();
-          finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+          finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.fin_sum,
                             out + (int64_t)b * k, gid);
           return;
         }
@@ -770,7 +792,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
     }
   }
   __syncthreads();
-  finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.wave_sum,
+  finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.fin_sum,
                     out + (int64_t)b * k, gid);
 }
 
