@@ -9,17 +9,28 @@ namespace csa2 {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront on DPP moves (no
+// LDS round trips): shifts right by 1, 2, 4 and 8 lanes inside each row of
+// 16 lanes (lanes shifted in from outside the row add 0), then the last
+// lane of row 0 is added to row 1 and that of row 2 to row 3 (row_bcast:15),
+// then the last lane of row 1 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)x;
+}
+
 // Exclusive prefix sum over a workgroup of NT threads in thread order.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sum, uint32_t* total) {
   constexpr int kW = NT / 64;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) wave_sum[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -40,12 +51,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan_once(uint32_t v, uint32_t* wave_sum, uint32_t* total) {
   constexpr int kW = NT / 64;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) wave_sum[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -65,12 +71,7 @@ template <int NT>
 __device__ __forceinline__ uint2 block_exclusive_scan2_once(uint2 v, uint32_t* wave_sum, uint2* total) {
   constexpr int kW = NT / 64;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  uint32_t x = v.x, y = v.y;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t xs = __shfl_up(x, d), ys = __shfl_up(y, d);
-    if (lane >= d) x += xs, y += ys;
-  }
+  const uint32_t x = wave_inclusive_scan(v.x), y = wave_inclusive_scan(v.y);
   if (lane == 63) wave_sum[wave] = x, wave_sum[kW + wave] = y;
   __syncthreads();
   uint2 before = make_uint2(0u, 0u), all = make_uint2(0u, 0u);

@@ -690,15 +690,10 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
         uint32_t cnt = 0;
 #pragma unroll
         for (int j = 0; j < kRowsPer; ++j) cnt += (key[j] >= lo && key[j] != 0) ? 1u : 0u;
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t y = __shfl_up(incl, d);
-          if (lane_id() >= d) incl += y;
-        }
+        const uint32_t incl = wave_inclusive_scan(cnt);
         uint32_t base = 0;
         if (lane_id() == 63) base = atomicAdd(&sm.counter[1], incl);
-        uint32_t pos = __shfl(base, 63) + incl - cnt;
+        uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)base, 63) + incl - cnt;
 #pragma unroll
         for (int j = 0; j < kRowsPer; ++j) {
           if (key[j] >= lo && key[j] != 0) {
