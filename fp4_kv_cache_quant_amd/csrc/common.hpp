@@ -89,6 +89,31 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t
 // flight (__syncthreads() also waits for all outstanding global memory
 // operations, which would drain a prefetch).  The memory clobber keeps the
 // compiler from moving memory accesses across it.
+// Cross-lane folds on VALU moves instead of LDS-crossbar shuffles: lane i
+// gets op(x[i], x[i ^ d]) for d = 16 (v_permlane16_swap: odd and even rows of
+// 16 lanes exchanged), d = 32 (v_permlane32_swap: the halves exchanged) and
+// d = 1 (DPP quad_perm [1, 0, 3, 2]).  The swaps return both exchanged
+// copies, and op is commutative, so the result is that of the shuffle.
+__device__ __forceinline__ float fold16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float fold32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float fold16_add(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float fold32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float fold1_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+}
+
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Scores that are not candidates.

@@ -116,10 +116,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       acc = mfma16x16x32(qa[1], as_bf16x8(kv[t][1]), acc);
       // acc[r] = q_{4g+r} . key n.
       const float part = relu_wsum4(acc, wh);
-      const float other = __shfl_xor(part, 16);
+      const float score = fold16_add(part);  // heads 0..3 + heads 4..7
       const int64_t slot = base + t * 16 + n;
       if (g == 0 && slot < n_out) {
-        const float score = part + other;
         sb[slot] = valid[t] ? score : kNegInf;
         const uint32_t key = order_key(score);
         if (kHist && valid[t] && key) atomicAdd(&hist[key >> 20], 1u);
@@ -221,8 +220,7 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       acc = mfma16x16x32(a0, as_bf16x8(kf[c][0]), acc);
       acc = mfma16x16x32(a1, as_bf16x8(kf[c][1]), acc);
       const float part = relu_wsum4(acc, wh);       // heads 4(g%2)..+3
-      const float other = __shfl_xor(part, 16);
-      const float score = (g & 1) ? other + part : part + other;  // lo + hi
+      const float score = fold16_add(part);  // lo + hi
       if ((g & 1) == 0) st[(g >> 1) * 128 + 16 * c + n] = (e_w + 16 * c + n < vis) ? score : kNegInf;
     }
     __builtin_amdgcn_wave_barrier();
@@ -310,8 +308,8 @@ __global__ __launch_bounds__(256) void index_score_local_kernel(
       acc = mfma16x16x32(qa[0], as_bf16x8(kv[t][0]), acc);
       acc = mfma16x16x32(qa[1], as_bf16x8(kv[t][1]), acc);
       const float part = relu_wsum4(acc, wh);
-      const float other = __shfl_xor(part, 16);
-      if (g == 0) lk[local0 + t * 16 + n] = valid[t] ? order_key(part + other) : 0u;
+      const float score = fold16_add(part);  // heads 0..3 + heads 4..7
+      if (g == 0) lk[local0 + t * 16 + n] = valid[t] ? order_key(score) : 0u;
     }
   }
   __syncthreads();

@@ -101,7 +101,7 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ src,
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, bf16_to_f32(bits[i] & 0x7FFFu));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fold1_max(amax);
   const uint32_t sc = scale_code(amax);
   const float s = e4m3_pos_value(sc);
   uint32_t packed = 0;

@@ -256,8 +256,7 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
   // ---- softmax statistics of the chunk, per head n, against the running
   // max (online softmax across the workgroup's chunks)
   float m = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = fold32_max(fold16_max(m));
   if (g == 0) sm.red_m[wave][n] = m;
   lds_barrier();
   float M = st.m_run;
@@ -280,8 +279,7 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
     *reinterpret_cast<uint2*>(&sm.ps[0][o]) = uint2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
     *reinterpret_cast<uint2*>(&sm.ps[1][o]) = uint2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = fold32_add(fold16_add(lsum));
   if (g == 0) sm.red_l[wave][n] = lsum;
   const float alpha_n = (st.m_run == kNegInf) ? 0.f : exp2f(st.m_run - M);
   if (tid < 16) sm.alpha[tid] = alpha_n;

@@ -55,7 +55,7 @@ __device__ __forceinline__ void wave_hist_add_grouped(uint32_t* hist, uint32_t b
   uint64_t pending = __ballot(active);
   while (pending) {
     const int leader = __ffsll((unsigned long long)pending) - 1;
-    const uint32_t lb = __shfl(bin, leader);
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
     const uint64_t same = __ballot(active && bin == lb);
     if (lane_id() == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
     pending &= ~same;
