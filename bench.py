@@ -38,31 +38,33 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12717585, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12716550, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "508c46d92b6016cc852a4a7794e7ba9213529cf20c9c659cd5e5d6635cc4147f",
+                    "1556e6dddda673b009db45d1b727d118bab54a6273368cffc55c45b15be0bbd9",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/block_scan": {
-        "bytes": 280629996, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 279892400, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "af29e44c8007dccd689393411e9d26d8ad567080bde04a206c3fbc78cf6e522a",
+                    "f8d83160eb6d6014c3ed01a682f1a8f6fc13e0b35cca2b89aed32da6f513199b",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f",
-                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd"}},
-    "encoder_1m/flat_select": {
-        "bytes": 1092880833, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
-        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "af29e44c8007dccd689393411e9d26d8ad567080bde04a206c3fbc78cf6e522a",
-                    "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "6d46b15f2af93b25f3ba2fd475d2ef028189ee174e5a5ebb5177bd7688413025",
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
                     "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
-                    "0cf1a9d6daa7131df4a77d382313cdef8022ac6ffe96aaf1f554de38066f1737",
+                    "a6b9172621f3d03f20519b4513831baaf8301db1063e28fef2e42cb10c075217"}},
+    "encoder_1m/flat_select": {
+        "bytes": 1092869886, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                    "f8d83160eb6d6014c3ed01a682f1a8f6fc13e0b35cca2b89aed32da6f513199b",
+                    "fp4_kv_cache_quant_amd/csrc/topk.hip":
+                    "98a3b2c2f2c5cd25f211e8289f3f2359f012b3826e991834a20130bc52f9c41d",
+                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
+                    "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd",
+                    "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
+                    "a6b9172621f3d03f20519b4513831baaf8301db1063e28fef2e42cb10c075217",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "bc2240b5758e4397d06ad58f083e36eb25b36f0605e46b306a75b7dc4c416c5f"}},
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
 }
 
 
