@@ -77,14 +77,12 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
 }
 
-// With 8 wavefronts (one workgroup per CU) main Q is staged once in LDS and
-// the next chunk's rows are loaded while the current one is computed; with
-// 4 wavefronts (two workgroups per CU) Q stays in registers and the other
-// workgroup on the CU hides the loads.
+// With 8 wavefronts (one workgroup per CU) main Q is staged once in LDS;
+// with 4 wavefronts (two workgroups per CU) Q stays in registers.  Either
+// way the next chunk's rows are loaded while the current one is computed.
 template <int W>
 struct AttnCfg {
   static constexpr bool kQLds = (W == 8);
-  static constexpr bool kPrefetch = (W == 8);
   static constexpr int kRows = 16 * W;           // rows per chunk
   static constexpr int kPPitch = kRows + 8;      // P pitch, f16 elements
   static constexpr int kCT = 4 * (8 / W);        // column tiles per wavefront
@@ -421,24 +419,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   for (int ch = c_begin; ch < c_end; ++ch) {
     const bool has_next = ch + 1 < c_end;
     if (ch != c_begin) lds_barrier();  // the previous chunk's LDS reads are done
-    if (Cfg::kPrefetch) {
-      AttnTile nxt;
-      if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);  // index loads of the next chunk
-      attn_chunk<W, kWin>(sm, st, cur, qb_operand, scale_log2, [&]() {
-        if (has_next) tile_load<kWin>(nxt, a, n, g);  // its row loads overlap this chunk's PV
-      });
-      if (has_next) cur = nxt;
-    } else {
-      // The next chunk's indices are loaded now, its rows after this chunk:
-      // one of its two dependent round trips overlaps this chunk's work.
-      AttnTile nxt;
-      if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);
-      attn_chunk<W, kWin>(sm, st, cur, qb_operand, scale_log2, []() {});
-      if (has_next) {
-        tile_load<kWin>(nxt, a, n, g);
-        cur = nxt;
-      }
-    }
+    AttnTile nxt;
+    if (has_next) tile_begin<W>(nxt, a, ch + 1, wave, n);  // index loads of the next chunk
+    attn_chunk<W, kWin>(sm, st, cur, qb_operand, scale_log2, [&]() {
+      if (has_next) tile_load<kWin>(nxt, a, n, g);  // its row loads overlap this chunk's PV
+    });
+    if (has_next) cur = nxt;
   }
 
   if (n_split == 1) {
