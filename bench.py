@@ -40,7 +40,7 @@ MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
         "bytes": 12712439, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "18e6316617910cc4604302b732a5becbb847bb33a4b2b5cea4b546c457fb92f6",
+                    "6cf6052b8a8c9b43a1ecaf3793bc1d4c7b6fadfecb3ccd69b43b443a0d85e6b3",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/block_scan": {
@@ -58,7 +58,7 @@ MEASURED_TRAFFIC = {
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "f8d83160eb6d6014c3ed01a682f1a8f6fc13e0b35cca2b89aed32da6f513199b",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "98a3b2c2f2c5cd25f211e8289f3f2359f012b3826e991834a20130bc52f9c41d",
+                    "6ab22304bd6174d1d2b9f1c787c530c56bac173b307bfc3eec55f6ce530bdbef",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
                     "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":

@@ -20,7 +20,10 @@
 //      and one packed f16 multiply by the E4M3 scale, which is exact (a
 //      product of 2- and 4-bit significands inside the f16 normal range);
 //      a bf16 window pair is widened and packed to f16 (round toward zero:
-//      exact for |x| in [2^-14, 65504], larger magnitudes saturate);
+//      exact for |x| in [2^-14, 65504], larger magnitudes saturate), an
+//      E4M3 window pair is one exact v_cvt_scalef32_pk_f16_fp8, and f16
+//      window rows (converted once per layer for many queries) are used as
+//      loaded;
 //   2. S^T = X Q^T on v_mfma_f32_16x16x32_f16 (16 steps over 512 channels),
 //      the converted registers being the A operand and the main Q (rounded
 //      to f16 the same way) the B operand; the rows also go to LDS for the
@@ -29,8 +32,9 @@
 //      exp2 and sum); P is split into f16 hi + lo parts (P ~ hi + lo to
 //      about 2^-21) so the PV product keeps fp32-level accuracy;
 //   4. O = O * 2^(m_old - m_new) + P X: each wavefront owns 512/W channels
-//      as column tiles whose B operands come from 8-byte LDS reads of 8
-//      rows, split into per-column vectors.
+//      as column tiles of 16 channels whose B operands (8 rows x 16
+//      channels) are two transposing LDS reads (ds_read_b64_tr_b16); the
+//      next chunk's rows are loaded meanwhile.
 // With one workgroup per query the normalised output is written directly;
 // otherwise each workgroup writes its unnormalised O and (max, sum) per
 // head and a second kernel merges them (log-sum-exp weights).

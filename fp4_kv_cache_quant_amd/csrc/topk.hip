@@ -11,7 +11,8 @@
 //              produce it as a by-product, then this kernel is skipped);
 //   filter     (long inputs) every workgroup reads the histogram, finds the
 //              threshold bin b1, writes a selection bitmap of the keys above
-//              b1 and appends the keys inside b1 to a candidate buffer;
+//              b1 and the keys inside b1 to its own region of a candidate
+//              buffer;
 //   final      one workgroup per sequence resolves the two low digits among
 //              the candidates, takes keys above T and the lowest-slot keys
 //              equal to T (prefix count over a tie bitmap), and writes the
@@ -19,6 +20,11 @@
 //              For short inputs it does the filter pass itself.
 // If the threshold bin holds more keys than the candidate buffer, the final
 // kernel resolves the low digits with passes over the scores instead.
+// Inputs of at most 65,536 slots with no histogram given take one kernel,
+// rows: a workgroup per sequence holds the scores in registers, estimates
+// the threshold's top digit from a sample, and selects exactly among the
+// keys at or above it (or, if the estimate fails, runs the three digit
+// passes over all keys).
 // Score loads use clamped, unconditional addresses so that a thread's batch
 // of loads is in flight together (a conditional load waits on its own).
 // All of it is integer work on the keys: exact and independent of timing.
