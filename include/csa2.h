@@ -72,7 +72,8 @@ typedef int32_t csa2_status;
 /* Message of the last failing call on this thread ("" if none). */
 const char* csa2_last_error(void);
 /* Version of this ABI (bumped on any signature or struct change; 2 added
- * the FP8 window, 3 the key maintenance on append). */
+ * the FP8 window, 3 the key maintenance on append, 4 the per-layer indexer
+ * K of flat Full layers and csa2_flat_select). */
 int32_t csa2_abi_version(void);
 
 /* ------------------------------------------------------------ FP4 cache
@@ -189,7 +190,8 @@ csa2_status csa2_flat_select(const uint16_t* q, const float* w, const uint16_t* 
  *   ws  device workspace of csa2_sparse_attn_workspace_size(...) bytes,
  *       16-byte aligned; no initialisation needed.  Calls that share a
  *       workspace must not overlap in time.
- * Limits: k_idx + swa_max >= 1, swa_max <= 4096. */
+ * Limits: 1 <= k_idx + swa_max <= 8192, swa_max <= 4096, n_q <= 65535;
+ * q, kv->codes, swa, out and ws 16-byte aligned, kv->scales 8-byte. */
 size_t csa2_sparse_attn_workspace_size(int32_t n_q, int32_t k_idx, int32_t swa_max);
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
                              const int32_t* idx, int32_t k_idx, const uint16_t* swa,
@@ -311,8 +313,9 @@ const int32_t* csa2_sched_indices(const csa2_sched* s, int32_t layer);
 /* Device pointer to the pool [n_seq][pool_blocks] int32 built by the last
  * hierarchical Full layer, or NULL if the table has none. */
 const int32_t* csa2_sched_pool(const csa2_sched* s);
-/* Blocking: read and clear the device error flags (bit 0: an append found a
- * full cache).  Returns CSA2_OK and stores the flags in *flags. */
+/* Blocking: read and clear the device error flags (bit 0: a latent append
+ * found a full cache; bit 1: a key append did).  Returns CSA2_OK and stores
+ * the flags in *flags. */
 csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags);
 void csa2_sched_destroy(csa2_sched* s);
 
