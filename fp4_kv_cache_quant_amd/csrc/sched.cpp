@@ -203,9 +203,16 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
   CSA2_REQUIRE(io->lens && io->idx_k && io->main_q && io->swa && io->swa_len && io->out, CSA2_EINVAL,
                "csa2_sched_decode_step: null pointer in io");
   CSA2_REQUIRE(!s->any_hier || io->blk_k, CSA2_EINVAL, "csa2_sched_decode_step: hierarchical table needs blk_k");
+  // The kernels read keys, queries, window rows and the appended row, and
+  // write the outputs, in 16-byte pieces (FP4 scales in 8-byte pieces).
+  auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  CSA2_REQUIRE(a16(io->idx_k) && a16(io->blk_k) && a16(io->new_row), CSA2_EINVAL,
+               "csa2_sched_decode_step: idx_k, blk_k and new_row must be 16-byte aligned");
   for (int i = 0; i < io->n_kv; ++i) {
     csa2_status st = check_kv(io->kv[i], "csa2_sched_decode_step");
     if (st != CSA2_OK) return st;
+    CSA2_REQUIRE(a16(io->kv[i].codes) && (reinterpret_cast<uintptr_t>(io->kv[i].scales) & 7) == 0, CSA2_EINVAL,
+                 "csa2_sched_decode_step: kv codes need 16-byte and scales 8-byte alignment");
     CSA2_REQUIRE(io->kv[i].n_seq == d.n_seq && io->kv[i].cap <= d.key_cap, CSA2_ESHAPE,
                  "csa2_sched_decode_step: kv tensor " + std::to_string(i) +
                      " must hold n_seq sequences and cap <= key_cap");
@@ -221,6 +228,11 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
     CSA2_REQUIRE(!io->layer_idx_k || !io->layer_idx_k[l] || (L.mode == CSA2_FULL && !L.hierarchical), CSA2_EINVAL,
                  "csa2_sched_decode_step: layer_idx_k entry " + std::to_string(l) +
                      " must be NULL (only flat Full layers own indexer K)");
+    CSA2_REQUIRE(a16(io->main_q[l]) && a16(io->swa[l]) && a16(io->out[l]) &&
+                     (L.mode == CSA2_REUSE || a16(io->idx_q[l])) && (!io->layer_idx_k || a16(io->layer_idx_k[l])),
+                 CSA2_EINVAL,
+                 "csa2_sched_decode_step: main Q, SWA, out, indexer Q and K of layer " + std::to_string(l) +
+                     " must be 16-byte aligned");
   }
   if (io->new_idx_k) {
     // The appended position's indexer key, and its block's key: before the

@@ -193,3 +193,22 @@ def test_layer_keys_only_on_flat_full_layers(wl):
     with pytest.raises(csa2.Csa2Error, match="layer_idx_k"):
         sched.decode_step(io)
     sched.close()
+
+
+def test_step_rejects_misaligned_tensors(wl):
+    """A main Q that is not 16-byte aligned is rejected before any launch."""
+    import torch
+
+    import fp4_kv_cache_quant_amd as csa2
+    cfg = C.ENCODER_DECODE_1M.with_(n_seq=1, L0=600, q_sets=1)
+    print_case("sched alignment validation")
+    inp = wl.build_decode_inputs(cfg, 1)
+    sched = wl.make_sched(inp)
+    mq = list(inp.main_q[0])
+    base = torch.empty(mq[2].numel() + 8, dtype=mq[2].dtype, device=mq[2].device)
+    mq[2] = base[1:1 + mq[2].numel()].view(mq[2].shape)          # 2 bytes off
+    io = sched.prepare(kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, main_q=mq, swa=inp.swa,
+                       swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q[0], layer_idx_k=inp.layer_idx_k)
+    with pytest.raises(csa2.Csa2Error, match="16-byte aligned"):
+        sched.decode_step(io)
+    sched.close()
