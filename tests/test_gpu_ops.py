@@ -357,9 +357,12 @@ def test_sparse_attn_matches_oracle(csa2, k_idx, swa_lens):
     q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q), synth.NORMAL, range(n_q), np.arange(16), 512)
     swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA), synth.NORMAL, range(n_q), np.arange(128), 512)
     swa_len = np.array(swa_lens, np.int32)
+    swa_dev = swa.copy()
+    for b in range(n_q):
+        swa_dev[b, swa_len[b]:] = 0x7FC0       # rows past the window hold NaN: never used
     print_case(f"sparse_attn k_idx={k_idx} swa={swa_lens}")
     out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
-    csa2.sparse_attn(dev(q), kv, dev(idx) if k_idx else None, dev(swa), dev(swa_len), SM_SCALE, out)
+    csa2.sparse_attn(dev(q), kv, dev(idx) if k_idx else None, dev(swa_dev), dev(swa_len), SM_SCALE, out)
     got = out.cpu().numpy()
     for b in range(n_q):
         codes, scales = oracle.quant_rows(src[b])
@@ -473,9 +476,12 @@ def test_sparse_attn_fp8_window_matches_oracle(csa2, k_idx, swa_lens):
     swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 4), synth.NORMAL, range(n_q), np.arange(128), 512)
     swa8 = np.stack([oracle.fp8_rows(swa[b]) for b in range(n_q)])
     swa_len = np.array(swa_lens, np.int32)
+    swa8_dev = swa8.copy()
+    for b in range(n_q):
+        swa8_dev[b, swa_len[b]:] = 0x7F        # E4M3 NaN past the window: never used
     print_case(f"sparse_attn fp8 window k_idx={k_idx} swa={swa_lens}")
     out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
-    csa2.sparse_attn(dev(q), kv, dev(idx) if k_idx else None, torch.from_numpy(swa8).cuda(), dev(swa_len),
+    csa2.sparse_attn(dev(q), kv, dev(idx) if k_idx else None, torch.from_numpy(swa8_dev).cuda(), dev(swa_len),
                      SM_SCALE, out)
     got = out.cpu().numpy()
     for b in range(n_q):
