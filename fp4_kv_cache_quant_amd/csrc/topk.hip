@@ -189,6 +189,133 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
   }
 }
 
+// Many rows of at most kTopkRowsMax slots (a prefill chunk: one row per
+// query): the single-workgroup selection would stream each row through one
+// CU.  Instead topk_sample_kernel takes each row's threshold estimate from
+// kSamples sampled slots (one workgroup per row), and every filter
+// workgroup of the row (8,192 slots each) writes the keys at or above it
+// (bins >= B) to its own region of the row's candidate buffer, with their
+// count.  When the estimate cannot be taken the threshold and the counts
+// are kNoEstimate; topk_rows_kernel then selects among the candidates, or
+// runs its full passes over the row when an estimate is missing, a region
+// overflowed, or the candidates are fewer than k or more than it can hold.
+// The row's threshold is kept in the last entry of its wcnt row, which
+// filters of at most kTopkRowsMax slots never use.
+constexpr int kSamples = 1024;
+constexpr uint32_t kNoEstimate = 0xFFFFFFFFu;
+constexpr int kThresholdSlot = kTopkFilterWgMax - 1;
+static_assert(kTopkRowsMax / kTopkFilterSlots < kThresholdSlot, "threshold slot unused by the filter regions");
+
+// Sampled slot i of a row of n >= 1,024 slots (i < kSamples): 64 runs of 16
+// contiguous slots, one at the start of each 64th of the row (a
+// wavefront's samples are four runs: few cache lines per load).
+__device__ __forceinline__ int sample_slot(int i, int64_t n) {
+  return (i >> 4) * (int)(n >> 6) + (i & 15);
+}
+
+__global__ __launch_bounds__(kPassThreads) void topk_sample_kernel(const float* __restrict__ scores, int64_t n,
+                                                                   const int32_t* __restrict__ lens,
+                                                                   int32_t len_div, int32_t k, TopkWs ws) {
+  constexpr int kSmpPer = kSamples / kPassThreads;  // samples per thread
+  __shared__ uint32_t hist[kTopkBins];
+  __shared__ uint32_t wave_sum[kPassThreads / 64];
+  __shared__ uint32_t found[2];
+  __shared__ uint32_t n_smp;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int nv = (int)valid_slots(n, lens, len_div, b);
+  const float* sc = scores + (int64_t)b * n;
+  const uint32_t kk = (uint32_t)k;
+  float sv[kSmpPer];
+#pragma unroll
+  for (int j = 0; j < kSmpPer; ++j) sv[j] = sc[min(sample_slot(tid + kPassThreads * j, n), (int)n - 1)];
+  for (int i = tid; i < kTopkBins; i += kPassThreads) hist[i] = 0;
+  if (tid == 0) n_smp = 0;
+  __syncthreads();
+  // The estimate (as in topk_rows_kernel): the top-digit bin B where the
+  // samples counted from the top reach r, about twice the samples that k
+  // keys would give.
+  const int r = (int)(((int64_t)2 * kk * kSamples + nv - 1) / max(nv, 1)) + 8;
+  uint32_t lo = kNoEstimate;
+  if (nv >= 4 * (int)kk && r <= kSamples / 4) {  // uniform over the workgroup
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kSmpPer; ++j) {
+      const uint32_t key = sample_slot(tid + kPassThreads * j, n) < nv ? order_key(sv[j]) : 0u;
+      if (key) {
+        atomicAdd(&hist[key >> 20], 1u);
+        ++mine;
+      }
+    }
+    const uint32_t wave_n = (uint32_t)wave_inclusive_scan(mine);
+    if (lane_id() == 63 && wave_n) atomicAdd(&n_smp, wave_n);
+    __syncthreads();
+    if (n_smp >= (uint32_t)r) {
+      find_threshold_bin<kPassThreads>(hist, kTopkBins, (uint32_t)r, wave_sum, found);
+      lo = found[0] << 20;
+    }
+  }
+  if (tid == 0) ws.wcnt[(int64_t)b * kTopkFilterWgMax + kThresholdSlot] = lo;
+}
+
+// kVec: rows start 16-byte aligned (n % 4 == 0, aligned scores), so each
+// thread loads runs of four slots; slot of register j: s0 + 4 * (j / 4 *
+// NT + tid) + j % 4 (else s0 + j * NT + tid).
+template <bool kVec>
+__global__ __launch_bounds__(kPassThreads) void topk_sample_filter_kernel(const float* __restrict__ scores,
+                                                                          int64_t n,
+                                                                          const int32_t* __restrict__ lens,
+                                                                          int32_t len_div, TopkWs ws) {
+  constexpr int kPer = kFilterSlots / kPassThreads;  // slots per thread
+  __shared__ uint32_t wave_sum[kPassThreads / 64];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int nv = (int)valid_slots(n, lens, len_div, b);
+  const int s0 = blockIdx.x * kFilterSlots;
+  const int nloc = min(max(nv - s0, 0), kFilterSlots);  // valid slots of this workgroup
+  const float* sc = scores + (int64_t)b * n;
+  uint32_t* wrow = ws.wcnt + (int64_t)b * kTopkFilterWgMax;
+  auto slot_of = [&](int j) {
+    return kVec ? 4 * ((j >> 2) * kPassThreads + tid) + (j & 3) : j * kPassThreads + tid;
+  };
+  float v[kPer];
+  if constexpr (kVec) {
+    const int last = max(nloc - 1, 0) >> 2;  // last 16-byte group with a valid slot
+#pragma unroll
+    for (int j = 0; j < kPer / 4; ++j) {
+      const f32x4 x = reinterpret_cast<const f32x4*>(sc + s0)[min(j * kPassThreads + tid, last)];
+      v[4 * j] = x[0], v[4 * j + 1] = x[1], v[4 * j + 2] = x[2], v[4 * j + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = sc[s0 + min(slot_of(j), max(nloc - 1, 0))];
+  }
+  const uint32_t lo = wrow[kThresholdSlot];
+  if (lo == kNoEstimate) {
+    if (tid == 0) wrow[blockIdx.x] = kNoEstimate;
+    return;
+  }
+  uint32_t key[kPer];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    key[j] = slot_of(j) < nloc ? order_key(v[j]) : 0u;
+    cnt += (key[j] >= lo && key[j] != 0) ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan<kPassThreads>(cnt, wave_sum, &total);
+  const uint32_t per_wg = kTopkCandCap / gridDim.x;
+  if (tid == 0) wrow[blockIdx.x] = total;
+  uint2* gc = ws.cand + (int64_t)b * kTopkCandCap + (int64_t)blockIdx.x * per_wg;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (key[j] >= lo && key[j] != 0) {
+      if (pos < per_wg) gc[pos] = make_uint2(key[j], (uint32_t)(s0 + slot_of(j)));
+      ++pos;
+    }
+  }
+}
+
 // Words w0 + kG*kQc*r + i (i < kG*kQc) of a bitmap: kQc groups of kG words
 // (kG = 4: 16-byte loads) of round r of a thread's run, loaded together
 // (clamped to the last group, which exists), words at or past w1 read as 0.
@@ -578,6 +705,7 @@ constexpr int kRowsMax = 64 * kFinalThreads;  // 65,536 slots
 static_assert(kRowsMax == kTopkRowsMax, "register-resident selection length");
 
 constexpr int kRowsCand = 8192;  // keys kept by the sampled first pass
+constexpr int kManyRows = 256;   // rows from which long rows take the multi-workgroup filter
 
 struct RowsSmem {
   int32_t pool[CSA2_TOPK_MAX];
@@ -629,14 +757,20 @@ __device__ void select_candidates(const uint32_t* ck, int nc, uint32_t kk, const
   ties = need2 - found[1];
 }
 
-template <int kRowsPer>
+// kCandIn: the row's candidates come from topk_sample_filter_kernel (cand_in
+// [n_seq][kTopkCandCap], wcnt_in [n_seq][kTopkFilterWgMax]) instead of the
+// sampled first pass here; the scores are loaded only if the full passes
+// have to run.
+template <int kRowsPer, bool kCandIn = false>
 __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* __restrict__ scores, int64_t n,
                                                                   const int32_t* __restrict__ lens,
                                                                   int32_t len_div, int32_t k,
                                                                   const int32_t* __restrict__ pool,
                                                                   int32_t n_pool, int32_t blk,
                                                                   int32_t* __restrict__ out,
-                                                                  const int32_t* __restrict__ gids) {
+                                                                  const int32_t* __restrict__ gids,
+                                                                  const uint2* __restrict__ cand_in = nullptr,
+                                                                  const uint32_t* __restrict__ wcnt_in = nullptr) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
   // gids: [n_seq][n] ids emitted for the slots (else the slot, or the pool's)
@@ -651,13 +785,14 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
   // Slot of register j of this thread: j * kFinalThreads + tid (a
   // wavefront's 64 slots are contiguous and 64-aligned).
   uint32_t key[kRowsPer];
-  {
+  auto load_keys = [&]() {
     float v[kRowsPer];
 #pragma unroll
     for (int j = 0; j < kRowsPer; ++j) v[j] = sc[min(j * kFinalThreads + tid, max(nvalid - 1, 0))];
 #pragma unroll
     for (int j = 0; j < kRowsPer; ++j) key[j] = (j * kFinalThreads + tid < nvalid) ? order_key(v[j]) : 0u;
-  }
+  };
+  if constexpr (!kCandIn) load_keys();
   if (pool) {
     const int32_t* pb = pool + (int64_t)b * n_pool;
     for (int i = tid; i < n_pool; i += kFinalThreads) sm.pool[i] = pb[i];
@@ -667,6 +802,63 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
   for (int i = tid; i < words; i += kFinalThreads) sm.sel[i] = sm.tie[i] = 0;
   if (tid < 2) sm.counter[tid] = 0;
   __syncthreads();
+
+  if constexpr (kCandIn) {
+    // Candidates from the filter workgroups' regions: usable if every
+    // region holds its whole count and together they are k .. kRowsCand.
+    const int n_wg = (int)((n + kFilterSlots - 1) / kFilterSlots);
+    static_assert(kRowsMax / kTopkFilterSlots == 8, "at most 8 filter regions per row");
+    const uint32_t per_wg = kTopkCandCap / n_wg;
+    const uint32_t* wc = wcnt_in + (int64_t)b * kTopkFilterWgMax;
+    uint32_t cw[8], off[8], total = 0;
+    bool ok = true;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      cw[w] = w < n_wg ? wc[w] : 0u;
+      ok = ok && cw[w] != kNoEstimate && cw[w] <= per_wg;
+      off[w] = total;
+      total += ok ? cw[w] : 0u;
+    }
+    if (ok && total >= kk && total <= (uint32_t)kRowsCand) {  // uniform over the workgroup
+      // Candidate c = tid + j * NT of the concatenated regions: all of a
+      // thread's loads in flight together (clamped addresses).
+      const uint2* gc = cand_in + (int64_t)b * kTopkCandCap;
+      constexpr int kCandPer = kRowsCand / kFinalThreads;
+      uint2 e[kCandPer];
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) {
+        const uint32_t c = tid + j * kFinalThreads;
+        uint32_t src = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          if (c >= off[w] && c < off[w] + cw[w]) src = w * per_wg + (c - off[w]);
+        e[j] = gc[src];
+      }
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) {
+        const uint32_t c = tid + j * kFinalThreads;
+        if (c < total) {
+          sm.cand_key[c] = e[j].x;
+          sm.cand_slot[c] = e[j].y;
+          atomicAdd(&sm.hist1[e[j].x >> 20], 1u);
+        }
+      }
+      __syncthreads();
+      uint32_t T, ties;
+      select_candidates<kFinalThreads>(sm.cand_key, (int)total, kk, sm.hist1, sm.hist2, sm.hist3, sm.scan_sum,
+                                       sm.found, T, ties);
+      for (int c = tid; c < (int)total; c += kFinalThreads) {
+        const uint32_t key = sm.cand_key[c], i = sm.cand_slot[c];
+        if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
+        else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
+      }
+      __syncthreads();
+      finish_output_lds(sm.sel, sm.tie, words, ties, kk, pool ? sm.pool : nullptr, blk, sm.fin_sum,
+                        out + (int64_t)b * k, gid);
+      return;
+    }
+    load_keys();
+  }
 
   // Sampled first pass.  One key per thread (slot (tid % kRowsPer) * NT +
   // tid, spread over the row) estimates a lower bound B for the top digit
@@ -679,7 +871,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
   // contains the k largest) and fits.  Otherwise the full passes below run.
   // Each scan here has its own wave-sum slot, so none needs a second
   // barrier.
-  {
+  if constexpr (!kCandIn) {
     const int r = (int)(((int64_t)2 * kk * kFinalThreads + nvalid - 1) / max(nvalid, 1)) + 8;
     if (nvalid >= 4 * (int)kk && r <= kFinalThreads / 4) {  // uniform over the workgroup
       uint32_t smp = 0;
@@ -846,9 +1038,27 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<32>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<64>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<64, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess)
       return launch_status("csa2_topk (shared memory attribute)");
     attr_set = true;
+  }
+  if (!hist_ready && n > 32 * kFinalThreads && n <= kRowsMax && n_seq >= kManyRows) {
+    // Many long rows: the threshold estimate and the candidates on many
+    // workgroups per row, then the selection per row.
+    hipLaunchKernelGGL(topk_sample_kernel, dim3(n_seq), dim3(kPassThreads), 0, stream, scores, n, lens, len_div,
+                       k, ws);
+    const dim3 grid((uint32_t)((n + kFilterSlots - 1) / kFilterSlots), n_seq);
+    if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0)
+      hipLaunchKernelGGL(topk_sample_filter_kernel<true>, grid, dim3(kPassThreads), 0, stream, scores, n, lens,
+                         len_div, ws);
+    else
+      hipLaunchKernelGGL(topk_sample_filter_kernel<false>, grid, dim3(kPassThreads), 0, stream, scores, n, lens,
+                         len_div, ws);
+    hipLaunchKernelGGL((topk_rows_kernel<64, true>), dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream,
+                       scores, n, lens, len_div, k, pool, n_pool, blk, out, gids, ws.cand, ws.wcnt);
+    return launch_status("csa2_topk");
   }
   if (!hist_ready && n <= kRowsMax) {
     if (n <= 16 * kFinalThreads)

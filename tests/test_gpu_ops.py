@@ -246,6 +246,40 @@ def test_topk_threshold_bin_clustered_in_one_region(csa2, n, k, cluster):
         assert np.array_equal(got[b], oracle.select(sc[b], np.arange(n), k)), b
 
 
+@pytest.mark.parametrize("n,k", [(65536, 512), (40000, 512), (65536, 2048)])
+def test_topk_many_long_rows(csa2, n, k):
+    """Many rows of more than 32,768 slots (a prefill chunk's queries): the
+    threshold estimate taken by every filter workgroup of a row, candidates
+    per workgroup region, then the selection per row -- with rows whose
+    estimate holds (integer-valued and continuous scores), a row whose
+    threshold bin overflows a region, rows too short to estimate, an empty
+    row and ragged lengths, all of which must equal the oracle."""
+    n_seq = 300
+    rng = np.random.default_rng(n + k)
+    q = rng.integers(-4, 5, size=(8, 64))
+    sc = np.empty((n_seq, n), np.float32)
+    for b in range(n_seq):
+        if b % 3 == 0:
+            sc[b] = rng.standard_normal(n).astype(np.float32)
+        else:
+            keys = rng.integers(-4, 5, size=(n, 64))
+            sc[b] = np.maximum(keys @ q.T, 0).sum(1).astype(np.float32)
+    sc[7, :9000] = 1e5 + (np.arange(9000) % 3)        # 9,000 keys in one bin, in one region
+    sc[8, :] = -np.inf                                  # no candidate
+    lens = np.full(n_seq, n, np.int32)
+    lens[9], lens[10], lens[11] = 3 * k, 1000, 4 * k + 5   # too short to estimate / just enough
+    lens[12:40] = rng.integers(4 * k, n, size=28)
+    print_case(f"topk many long rows n={n} k={k}")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    csa2.topk(dev(sc), k, out, lens=dev(lens))
+    got = out.cpu().numpy()
+    for b in sorted({0, 1, 2, 7, 8, 9, 10, 11, 12, 13, 39, 150, n_seq - 1}):
+        nv = lens[b]
+        ok = np.isfinite(sc[b, :nv])
+        ref = oracle.select(sc[b, :nv][ok], np.arange(nv)[ok], k)
+        assert np.array_equal(got[b], ref), b
+
+
 @pytest.mark.parametrize("case", ["continuous", "wide_bin", "top_unsampled"])
 def test_topk_sampled_first_pass_and_fallback(csa2, case):
     """Single-workgroup selection with its sampled first pass: continuous
