@@ -50,6 +50,10 @@ namespace csa2 {
 
 constexpr int kXPitch = CSA2_LATENT + 8;       // LDS row pitch, f16 elements
 
+// One window row of zeros (bf16 / f16 / E4M3 all read 0 from it): the
+// address of every window row past a query's window.
+__device__ __attribute__((aligned(16))) const uint32_t kZeroRow[2 * CSA2_LATENT / 4] = {};
+
 inline int attn_tiles(int32_t k_idx, int32_t swa_max) { return (k_idx + 15) / 16 + (swa_max + 15) / 16; }
 inline int attn_chunks(int32_t k_idx, int32_t swa_max, int waves) {
   return (attn_tiles(k_idx, swa_max) + waves - 1) / waves;
@@ -179,8 +183,11 @@ __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n,
     const int j = t.row0 + n;
     t.ok = t.in_range && j < a.n_swa;
     constexpr int kRowBytes = kWin == kWinE4m3 ? CSA2_LATENT : 2 * CSA2_LATENT;
-    const u32x4* sp = reinterpret_cast<const u32x4*>(
-        a.swa + ((int64_t)qb * a.swa_q_stride_rows + (t.ok ? j : 0)) * kRowBytes + (kRowBytes / 4) * g);
+    // A row past the window reads the zero row instead (its values then
+    // convert to 0 and need no masking).
+    const uint8_t* row = t.ok ? a.swa + ((int64_t)qb * a.swa_q_stride_rows + j) * kRowBytes
+                              : reinterpret_cast<const uint8_t*>(kZeroRow);
+    const u32x4* sp = reinterpret_cast<const u32x4*>(row + (kRowBytes / 4) * g);
 #pragma unroll
     for (int i = 0; i < (kWin == kWinE4m3 ? 8 : 16); ++i) t.raw[i] = sp[i];
   }
@@ -229,25 +236,14 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
       s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
     }
   } else {
-    // Rows past the window read a clamped address and are zeroed; for
-    // rows already in f16 or E4M3 the masking is skipped when every row of
-    // the tile is in the window.
-    auto window_rows = [&](bool mask) {
+    // (Rows past the window were loaded from the zero row.)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        u32x4 x = kWin == kWinE4m3 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
-                  : kWin == kWinF16 ? t.raw[k]
-                                    : bf16x8_to_f16x8(t.raw[k]);
-        if (mask && !t.ok) x = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
-        s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
-      }
-    };
-    if constexpr (kWin == kWinBf16) {
-      window_rows(true);  // (two copies of the converting loop cost registers)
-    } else {
-      if (__all(t.ok)) window_rows(false);
-      else window_rows(true);
+    for (int k = 0; k < 16; ++k) {
+      const u32x4 x = kWin == kWinE4m3 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
+                      : kWin == kWinF16 ? t.raw[k]
+                                        : bf16x8_to_f16x8(t.raw[k]);
+      *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
+      s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
     }
   }
   const uint64_t rows_ok = __ballot(t.ok);  // bit n (lanes 0..15) = row n of this wavefront
