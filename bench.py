@@ -38,13 +38,13 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12712433, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12694644, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "6cf6052b8a8c9b43a1ecaf3793bc1d4c7b6fadfecb3ccd69b43b443a0d85e6b3",
+                    "a3cde2d3d12b1ebf48ca75df8bc97f845f788e412ba884ef028cef3a93e53615",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/block_scan": {
-        "bytes": 280021324, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 279948950, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "f8d83160eb6d6014c3ed01a682f1a8f6fc13e0b35cca2b89aed32da6f513199b",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "a6b9172621f3d03f20519b4513831baaf8301db1063e28fef2e42cb10c075217"}},
     "encoder_1m/flat_select": {
-        "bytes": 1092811378, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "bytes": 1092870389, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "f8d83160eb6d6014c3ed01a682f1a8f6fc13e0b35cca2b89aed32da6f513199b",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
