@@ -31,6 +31,8 @@
 //
 // Citation key: [P1] "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M
 // Context, FP4 KV Cache, and Cross-Layer Attention Reuse".
+#include <algorithm>
+
 #include "common.hpp"
 #include "topk_ws.hpp"
 #include "select_dev.hpp"
@@ -205,6 +207,14 @@ constexpr int kSamples = 1024;
 constexpr uint32_t kNoEstimate = 0xFFFFFFFFu;
 constexpr int kThresholdSlot = kTopkFilterWgMax - 1;
 static_assert(kTopkRowsMax / kTopkFilterSlots < kThresholdSlot, "threshold slot unused by the filter regions");
+// Slots of the wcnt rows no filter region uses (at most 8 per row here):
+// entry i of the list of rows left to the fallback sits in row i's
+// kFallbackSlot; row 0 also holds the list's length and the fallback
+// workgroups' claim counter (both zeroed by topk_sample_kernel).
+constexpr int kFallbackSlot = kTopkFilterWgMax - 2;
+constexpr int kCountSlot = kTopkFilterWgMax - 3;
+constexpr int kClaimSlot = kTopkFilterWgMax - 4;
+static_assert(kTopkRowsMax / kTopkFilterSlots < kClaimSlot, "list slots unused by the filter regions");
 
 // Sampled slot i of a row of n >= 1,024 slots (i < kSamples): 64 runs of 16
 // contiguous slots, one at the start of each 64th of the row (a
@@ -256,6 +266,7 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_kernel(const float* 
     }
   }
   if (tid == 0) ws.wcnt[(int64_t)b * kTopkFilterWgMax + kThresholdSlot] = lo;
+  if (b == 0 && tid == 0) ws.wcnt[kCountSlot] = ws.wcnt[kClaimSlot] = 0u;
 }
 
 // kVec: rows start 16-byte aligned (n % 4 == 0, aligned scores), so each
@@ -342,14 +353,15 @@ __device__ __forceinline__ void load_round(const uint32_t* bm, int q0, int r, in
 // Every thread owns a contiguous run of words; one scan gives, per run, the
 // selected and the tie bits before it.  The lowest `ties` tie bits join the
 // selection, so a run's first output position is (selected before) +
-// min(ties before, ties).  -1 pads the row to k.  fin_sum: 2 * kFinalWaves
+// min(ties before, ties).  -1 pads the row to k.  fin_sum: 2 * NT / 64
 // words used by nothing else; the caller has synchronised after its last
-// write of sel / tie.
+// write of sel / tie.  Called by all NT threads of the workgroup.
+template <int NT = kFinalThreads>
 __device__ void finish_output_lds(const uint32_t* sel, const uint32_t* tie, int words, uint32_t ties, uint32_t kk,
                                   const int32_t* pool_lds, int32_t blk, uint32_t* fin_sum,
                                   int32_t* __restrict__ ob, const int32_t* __restrict__ gid = nullptr) {
   const int tid = threadIdx.x;
-  const int per = (words + kFinalThreads - 1) / kFinalThreads;
+  const int per = (words + NT - 1) / NT;
   const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
   uint2 cnt = make_uint2(0u, 0u);
   for (int w = w0; w < w1; ++w) {
@@ -357,7 +369,7 @@ __device__ void finish_output_lds(const uint32_t* sel, const uint32_t* tie, int 
     if (ties > 0) cnt.y += __popc(tie[w]);
   }
   uint2 tot;
-  const uint2 before = block_exclusive_scan2_once<kFinalThreads>(cnt, fin_sum, &tot);
+  const uint2 before = block_exclusive_scan2_once<NT>(cnt, fin_sum, &tot);
   uint32_t pos = before.x + min(before.y, ties);
   uint32_t trank = before.y;  // tie bits before the current word
   for (int w = w0; w < w1; ++w) {
@@ -387,7 +399,7 @@ __device__ void finish_output_lds(const uint32_t* sel, const uint32_t* tie, int 
     }
   }
   const uint32_t n_sel = tot.x + min(tot.y, ties);
-  for (uint32_t i = n_sel + tid; i < kk; i += kFinalThreads) ob[i] = -1;
+  for (uint32_t i = n_sel + tid; i < kk; i += NT) ob[i] = -1;
 }
 
 // Words w0 + 16*r + i (i < 16) of a global bitmap: four 16-byte groups of
@@ -706,6 +718,7 @@ static_assert(kRowsMax == kTopkRowsMax, "register-resident selection length");
 
 constexpr int kRowsCand = 8192;  // keys kept by the sampled first pass
 constexpr int kManyRows = 256;   // rows from which long rows take the multi-workgroup filter
+constexpr int kFlaggedGrid = 256;  // workgroups walking the rows that need the full selection
 
 struct RowsSmem {
   int32_t pool[CSA2_TOPK_MAX];
@@ -761,21 +774,15 @@ __device__ void select_candidates(const uint32_t* ck, int nc, uint32_t kk, const
 // [n_seq][kTopkCandCap], wcnt_in [n_seq][kTopkFilterWgMax]) instead of the
 // sampled first pass here; the scores are loaded only if the full passes
 // have to run.
-template <int kRowsPer, bool kCandIn = false>
-__global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* __restrict__ scores, int64_t n,
-                                                                  const int32_t* __restrict__ lens,
-                                                                  int32_t len_div, int32_t k,
-                                                                  const int32_t* __restrict__ pool,
-                                                                  int32_t n_pool, int32_t blk,
-                                                                  int32_t* __restrict__ out,
-                                                                  const int32_t* __restrict__ gids,
-                                                                  const uint2* __restrict__ cand_in = nullptr,
-                                                                  const uint32_t* __restrict__ wcnt_in = nullptr) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
+// The selection of row b by the whole workgroup (kFinalThreads threads).
+template <int kRowsPer, bool kCandIn>
+__device__ void rows_select(RowsSmem& sm, const int b, const float* __restrict__ scores, int64_t n,
+                            const int32_t* __restrict__ lens, int32_t len_div, int32_t k,
+                            const int32_t* __restrict__ pool, int32_t n_pool, int32_t blk, int32_t* __restrict__ out,
+                            const int32_t* __restrict__ gids, const uint2* __restrict__ cand_in,
+                            const uint32_t* __restrict__ wcnt_in) {
   // gids: [n_seq][n] ids emitted for the slots (else the slot, or the pool's)
-  const int32_t* gid = gids ? gids + (int64_t)blockIdx.x * n : nullptr;
-  const int b = blockIdx.x;
+  const int32_t* gid = gids ? gids + (int64_t)b * n : nullptr;
   const int tid = threadIdx.x;
   const int nvalid = (int)valid_slots(n, lens, len_div, b);
   const int words = (nvalid + 31) / 32;
@@ -989,6 +996,141 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* _
                     out + (int64_t)b * k, gid);
 }
 
+
+template <int kRowsPer, bool kCandIn = false>
+__global__ __launch_bounds__(kFinalThreads) void topk_rows_kernel(const float* __restrict__ scores, int64_t n,
+                                                                  const int32_t* __restrict__ lens,
+                                                                  int32_t len_div, int32_t k,
+                                                                  const int32_t* __restrict__ pool,
+                                                                  int32_t n_pool, int32_t blk,
+                                                                  int32_t* __restrict__ out,
+                                                                  const int32_t* __restrict__ gids,
+                                                                  const uint2* __restrict__ cand_in = nullptr,
+                                                                  const uint32_t* __restrict__ wcnt_in = nullptr) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  rows_select<kRowsPer, kCandIn>(*reinterpret_cast<RowsSmem*>(smem_raw), blockIdx.x, scores, n, lens, len_div, k,
+                                 pool, n_pool, blk, out, gids, cand_in, wcnt_in);
+}
+
+// Many long rows with k <= kLeanK and no pool: the selection among each
+// row's filter candidates in a 512-thread workgroup with LDS for 3,072 of
+// them, so that two rows run per CU.  A row it cannot take (no estimate, a
+// region overflow, fewer than k or more than kLeanCand candidates) is
+// flagged in its wcnt row and left to topk_rows_flagged_kernel.
+constexpr int kLeanThreads = 512;
+constexpr int kLeanCand = 3072;
+constexpr int kLeanK = 512;
+
+struct LeanSmem {
+  uint32_t cand_key[kLeanCand];
+  uint32_t cand_slot[kLeanCand];
+  uint32_t hist1[kTopkBins];
+  uint32_t hist2[kTopkBins];
+  uint32_t hist3[256];
+  uint32_t sel[kRowsMax / 32];
+  uint32_t tie[kRowsMax / 32];
+  uint32_t scan_sum[4][kLeanThreads / 64];
+  uint32_t fin_sum[2 * kLeanThreads / 64];
+  uint32_t found[2];
+};
+static_assert(sizeof(LeanSmem) <= 80 * 1024, "two workgroups per CU");
+
+__global__ __launch_bounds__(kLeanThreads, 2) void topk_cand_select_kernel(int64_t n, const int32_t* __restrict__ lens,
+                                                                         int32_t len_div, int32_t k,
+                                                                         int32_t* __restrict__ out,
+                                                                         const uint2* __restrict__ cand_in,
+                                                                         uint32_t* __restrict__ wcnt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  LeanSmem& sm = *reinterpret_cast<LeanSmem*>(smem_raw);
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvalid = (int)valid_slots(n, lens, len_div, b);
+  const int words = (nvalid + 31) / 32;
+  const uint32_t kk = (uint32_t)k;
+  uint32_t* wrow = wcnt + (int64_t)b * kTopkFilterWgMax;
+  const int n_wg = (int)((n + kFilterSlots - 1) / kFilterSlots);
+  const uint32_t per_wg = kTopkCandCap / n_wg;
+  uint32_t cw[8], off[8], total = 0;
+  bool ok = true;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    cw[w] = w < n_wg ? wrow[w] : 0u;
+    ok = ok && cw[w] != kNoEstimate && cw[w] <= per_wg;
+    off[w] = total;
+    total += ok ? cw[w] : 0u;
+  }
+  if (!(ok && total >= kk && total <= (uint32_t)kLeanCand)) {  // uniform over the workgroup
+    if (tid == 0) {
+      const uint32_t pos = atomicAdd(&wcnt[kCountSlot], 1u);
+      wcnt[(int64_t)pos * kTopkFilterWgMax + kFallbackSlot] = (uint32_t)b;
+    }
+    return;
+  }
+  for (int i = tid; i < kTopkBins; i += kLeanThreads) sm.hist1[i] = sm.hist2[i] = 0;
+  if (tid < 256) sm.hist3[tid] = 0;
+  for (int i = tid; i < words; i += kLeanThreads) sm.sel[i] = sm.tie[i] = 0;
+  // Candidate c = tid + j * NT of the concatenated regions: all of a
+  // thread's loads in flight together (clamped addresses).
+  const uint2* gc = cand_in + (int64_t)b * kTopkCandCap;
+  constexpr int kCandPer = kLeanCand / kLeanThreads;
+  uint2 e[kCandPer];
+#pragma unroll
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint32_t c = tid + j * kLeanThreads;
+    uint32_t src = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      if (c >= off[w] && c < off[w] + cw[w]) src = w * per_wg + (c - off[w]);
+    e[j] = gc[src];
+  }
+  __syncthreads();  // the histograms are clear
+#pragma unroll
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint32_t c = tid + j * kLeanThreads;
+    if (c < total) {
+      sm.cand_key[c] = e[j].x;
+      sm.cand_slot[c] = e[j].y;
+      atomicAdd(&sm.hist1[e[j].x >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t T, ties;
+  select_candidates<kLeanThreads>(sm.cand_key, (int)total, kk, sm.hist1, sm.hist2, sm.hist3, sm.scan_sum, sm.found,
+                                  T, ties);
+  for (int c = tid; c < (int)total; c += kLeanThreads) {
+    const uint32_t key = sm.cand_key[c], i = sm.cand_slot[c];
+    if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
+    else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  finish_output_lds<kLeanThreads>(sm.sel, sm.tie, words, ties, kk, nullptr, 1, sm.fin_sum, out + (int64_t)b * k);
+}
+
+// The rows topk_cand_select_kernel left, by the selection among up to
+// 8,192 candidates (else the full passes over the row): a grid of one
+// workgroup per CU claims the listed rows one by one until the list is
+// exhausted.
+__global__ __launch_bounds__(kFinalThreads) void topk_rows_flagged_kernel(const float* __restrict__ scores, int64_t n,
+                                                                          const int32_t* __restrict__ lens,
+                                                                          int32_t len_div, int32_t k,
+                                                                          int32_t* __restrict__ out,
+                                                                          const uint2* __restrict__ cand_in,
+                                                                          uint32_t* __restrict__ wcnt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
+  __shared__ uint32_t claimed;
+  const uint32_t count = wcnt[kCountSlot];
+  for (;;) {
+    if (threadIdx.x == 0) claimed = atomicAdd(&wcnt[kClaimSlot], 1u);
+    __syncthreads();
+    const uint32_t i = claimed;
+    __syncthreads();
+    if (i >= count) break;  // uniform
+    const int b = (int)wcnt[(int64_t)i * kTopkFilterWgMax + kFallbackSlot];
+    rows_select<64, true>(sm, b, scores, n, lens, len_div, k, nullptr, 0, 1, out, nullptr, cand_in, wcnt);
+    __syncthreads();  // LDS is reused by the next row
+  }
+}
 }  // namespace
 
 // Bitmap words per sequence: a multiple of 4, so that every sequence's
@@ -1040,7 +1182,11 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<64>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<64, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_flagged_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_cand_select_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(LeanSmem)) != hipSuccess)
       return launch_status("csa2_topk (shared memory attribute)");
     attr_set = true;
   }
@@ -1056,8 +1202,15 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
     else
       hipLaunchKernelGGL(topk_sample_filter_kernel<false>, grid, dim3(kPassThreads), 0, stream, scores, n, lens,
                          len_div, ws);
-    hipLaunchKernelGGL((topk_rows_kernel<64, true>), dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream,
-                       scores, n, lens, len_div, k, pool, n_pool, blk, out, gids, ws.cand, ws.wcnt);
+    if (k <= kLeanK && !pool && !gids) {
+      hipLaunchKernelGGL(topk_cand_select_kernel, dim3(n_seq), dim3(kLeanThreads), sizeof(LeanSmem), stream, n, lens,
+                         len_div, k, out, ws.cand, ws.wcnt);
+      hipLaunchKernelGGL(topk_rows_flagged_kernel, dim3(std::min(n_seq, kFlaggedGrid)), dim3(kFinalThreads),
+                         sizeof(RowsSmem), stream, scores, n, lens, len_div, k, out, ws.cand, ws.wcnt);
+    } else {
+      hipLaunchKernelGGL((topk_rows_kernel<64, true>), dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream,
+                         scores, n, lens, len_div, k, pool, n_pool, blk, out, gids, ws.cand, ws.wcnt);
+    }
     return launch_status("csa2_topk");
   }
   if (!hist_ready && n <= kRowsMax) {
