@@ -196,8 +196,7 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
 // CU.  Instead topk_sample_kernel takes each row's threshold estimate from
 // kSamples sampled slots (one workgroup per row), and every filter
 // workgroup of the row (8,192 slots each) writes the keys at or above it
-// (bins >= B) to its own region of the row's candidate buffer, with their
-// count.  When the estimate cannot be taken the threshold and the counts
+// to its own region of the row's candidate buffer, with their count.  When the estimate cannot be taken the threshold and the counts
 // are kNoEstimate; topk_rows_kernel then selects among the candidates, or
 // runs its full passes over the row when an estimate is missing, a region
 // overflowed, or the candidates are fewer than k or more than it can hold.
@@ -230,7 +229,8 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_kernel(const float* 
   __shared__ uint32_t hist[kTopkBins];
   __shared__ uint32_t wave_sum[kPassThreads / 64];
   __shared__ uint32_t found[2];
-  __shared__ uint32_t n_smp;
+  __shared__ uint32_t n_smp, n_bin, thr_key;
+  __shared__ uint32_t bin_keys[kSamples];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int nv = (int)valid_slots(n, lens, len_div, b);
@@ -240,20 +240,22 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_kernel(const float* 
 #pragma unroll
   for (int j = 0; j < kSmpPer; ++j) sv[j] = sc[min(sample_slot(tid + kPassThreads * j, n), (int)n - 1)];
   for (int i = tid; i < kTopkBins; i += kPassThreads) hist[i] = 0;
-  if (tid == 0) n_smp = 0;
+  if (tid == 0) n_smp = n_bin = 0;
   __syncthreads();
-  // The estimate (as in topk_rows_kernel): the top-digit bin B where the
-  // samples counted from the top reach r, about twice the samples that k
-  // keys would give.
+  // The estimate: the r-th largest sampled key, r about twice the samples
+  // that k keys would give -- found as the top-digit bin B where the
+  // samples counted from the top reach r, then the exact key among the
+  // samples of that bin.
   const int r = (int)(((int64_t)2 * kk * kSamples + nv - 1) / max(nv, 1)) + 8;
   uint32_t lo = kNoEstimate;
   if (nv >= 4 * (int)kk && r <= kSamples / 4) {  // uniform over the workgroup
+    uint32_t key[kSmpPer];
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < kSmpPer; ++j) {
-      const uint32_t key = sample_slot(tid + kPassThreads * j, n) < nv ? order_key(sv[j]) : 0u;
-      if (key) {
-        atomicAdd(&hist[key >> 20], 1u);
+      key[j] = sample_slot(tid + kPassThreads * j, n) < nv ? order_key(sv[j]) : 0u;
+      if (key[j]) {
+        atomicAdd(&hist[key[j] >> 20], 1u);
         ++mine;
       }
     }
@@ -262,7 +264,24 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_kernel(const float* 
     __syncthreads();
     if (n_smp >= (uint32_t)r) {
       find_threshold_bin<kPassThreads>(hist, kTopkBins, (uint32_t)r, wave_sum, found);
-      lo = found[0] << 20;
+      const uint32_t bin = found[0], need = (uint32_t)r - found[1];  // 1 <= need <= samples in the bin
+#pragma unroll
+      for (int j = 0; j < kSmpPer; ++j)
+        if (key[j] && (key[j] >> 20) == bin) bin_keys[atomicAdd(&n_bin, 1u)] = key[j];
+      __syncthreads();
+      const uint32_t m = n_bin;
+      for (uint32_t i = tid; i < m; i += kPassThreads) {
+        const uint32_t v = bin_keys[i];
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t t = 0; t < m; ++t) {
+          const uint32_t u = bin_keys[t];
+          gt += u > v ? 1u : 0u;
+          ge += u >= v ? 1u : 0u;
+        }
+        if (gt < need && ge >= need) thr_key = v;  // the need-th largest (equal keys write the same value)
+      }
+      __syncthreads();
+      lo = thr_key;
     }
   }
   if (tid == 0) ws.wcnt[(int64_t)b * kTopkFilterWgMax + kThresholdSlot] = lo;
