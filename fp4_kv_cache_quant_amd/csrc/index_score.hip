@@ -169,6 +169,7 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     int32_t* __restrict__ n_vis, int32_t* __restrict__ win_len, int32_t win) {
   __shared__ __attribute__((aligned(16))) uint16_t qs[kPfQ * 8 * 64];   // [query*8 + head][dim]
   __shared__ __attribute__((aligned(16))) float stage[4][2 * 128];      // per wavefront [2][128]
+  __shared__ int32_t vis_s[kPfQ];                                       // visible entries per query
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t q0 = (int64_t)blockIdx.y * kPfQ;
@@ -192,28 +193,39 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     *reinterpret_cast<u32x4*>(&qs[v * 8]) =
         reinterpret_cast<const u32x4*>(q + qr * 8 * 64)[v & 63];
   }
-  if (blockIdx.x == 0 && tid < kPfQ && q0 + tid < n_q) {
+  if (tid < kPfQ) {
     const int64_t t = t0 + q0 + tid;
-    if (n_vis) n_vis[q0 + tid] = (int32_t)min(n_entries, (t + 1) / ratio);
-    if (win_len) win_len[q0 + tid] = (int32_t)min((int64_t)win, t + 1);  // tokens max(0, t-win+1) .. t
+    const int32_t vis = (int32_t)min(n_entries, (t + 1) / ratio);
+    vis_s[tid] = vis;
+    if (blockIdx.x == 0 && q0 + tid < n_q) {
+      if (n_vis) n_vis[q0 + tid] = vis;
+      if (win_len) win_len[q0 + tid] = (int32_t)min((int64_t)win, t + 1);  // tokens max(0, t-win+1) .. t
+    }
   }
   __syncthreads();
 
+  // Entry indices fit in 32 bits (n_entries < 2^31); the store pointer of
+  // this lane advances by two query rows per row tile.
   float* st = stage[wave];
   const bool vec_ok = (n_entries & 3) == 0;
+  const int e_lane = (int)e_w + n;                    // entry of column tile 0 for this lane
+  const int eo = (int)e_w + 4 * (lane & 31);           // first entry this lane stores
+  const int ne = (int)n_entries;
+  const bool store_vec = vec_ok && eo + 3 < ne;
+  const int q_left = (int)min<int64_t>(n_q - q0, kPfQ) - (lane >> 5);  // rows this lane may store: 2rt < q_left
+  float* dst = scores + (q0 + (lane >> 5)) * n_entries + eo;
 #pragma unroll 1
   for (int rt = 0; rt < kPfQ / 2; ++rt) {
     // Row m = n of this tile: query 2rt + n/8, head n%8, dims 16g..16g+15.
     const u32x4* ap = reinterpret_cast<const u32x4*>(&qs[((2 * rt) * 8 + n) * 64 + 16 * g]);
     const bf16x8 a0 = as_bf16x8(ap[0]), a1 = as_bf16x8(ap[1]);
-    const int64_t qi = q0 + 2 * rt + (g >> 1);   // query of this lane's output rows
     float wh[4] = {1.f, 1.f, 1.f, 1.f};
     if (kWeights) {
-      const int64_t qc = min(qi, (int64_t)n_q - 1);
+      const int64_t qc = min(q0 + 2 * rt + (g >> 1), (int64_t)n_q - 1);  // query of this lane's output rows
 #pragma unroll
       for (int r = 0; r < 4; ++r) wh[r] = w[qc * 8 + 4 * (g & 1) + r];
     }
-    const int64_t vis = min(n_entries, (t0 + qi + 1) / ratio);
+    const int vis = vis_s[2 * rt + (g >> 1)];
 #pragma unroll
     for (int c = 0; c < kPfCols; ++c) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -221,23 +233,21 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       acc = mfma16x16x32(a1, as_bf16x8(kf[c][1]), acc);
       const float part = relu_wsum4(acc, wh);       // heads 4(g%2)..+3
       const float score = fold16_add(part);  // lo + hi
-      if ((g & 1) == 0) st[(g >> 1) * 128 + 16 * c + n] = (e_w + 16 * c + n < vis) ? score : kNegInf;
+      if ((g & 1) == 0) st[(g >> 1) * 128 + 16 * c + n] = (e_lane + 16 * c < vis) ? score : kNegInf;
     }
     __builtin_amdgcn_wave_barrier();
     // Two rows of 128 scores: lane l stores query 2rt + l/32, entries 4(l%32)..+3.
-    const int64_t qo = q0 + 2 * rt + (lane >> 5);
-    const int64_t eo = e_w + 4 * (lane & 31);
     const f32x4 v = *reinterpret_cast<const f32x4*>(&st[(lane >> 5) * 128 + 4 * (lane & 31)]);
-    if (qo < n_q) {
-      float* dst = scores + qo * n_entries + eo;
-      if (vec_ok && eo + 3 < n_entries) {
+    if (2 * rt < q_left) {
+      if (store_vec) {
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (eo + j < n_entries) dst[j] = v[j];
+          if (eo + j < ne) dst[j] = v[j];
       }
     }
+    dst += 2 * n_entries;
     __builtin_amdgcn_wave_barrier();
   }
 }

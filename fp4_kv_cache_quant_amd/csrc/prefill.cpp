@@ -108,8 +108,8 @@ csa2_status csa2_prefill_index_score(const uint16_t* q, const float* w, const ui
   CSA2_REQUIRE(n_q >= 0 && n_q <= 2097120, CSA2_ESHAPE, "csa2_prefill_index_score: n_q must be in [0, 2097120]");
   if (n_q == 0) return CSA2_OK;
   CSA2_REQUIRE(q && keys && scores && n_vis, CSA2_EINVAL, "csa2_prefill_index_score: null pointer");
-  CSA2_REQUIRE(n_entries >= 1 && n_entries < (int64_t(1) << 31), CSA2_ESHAPE,
-               "csa2_prefill_index_score: n_entries must be in [1, 2^31)");
+  CSA2_REQUIRE(n_entries >= 1 && n_entries <= (int64_t(1) << 30), CSA2_ESHAPE,
+               "csa2_prefill_index_score: n_entries must be in [1, 2^30]");
   CSA2_REQUIRE(ratio >= 1 && t0 >= 0, CSA2_EINVAL, "csa2_prefill_index_score: need ratio >= 1 and t0 >= 0");
   const uintptr_t a = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(keys) |
                       reinterpret_cast<uintptr_t>(scores);

@@ -338,7 +338,7 @@ void csa2_sched_destroy(csa2_sched* s);
  *          e < vis(t0 + i), -inf for the entries query i cannot see
  *   n_vis  [n_q] int32 out (device): vis(t0 + i), usable as the `lens` of
  *          csa2_topk (len_div 1) over these scores.
- * Requires ratio >= 1, t0 >= 0, 1 <= n_q <= 2,097,120. */
+ * Requires ratio >= 1, t0 >= 0, 1 <= n_q <= 2,097,120, n_entries <= 2^30. */
 csa2_status csa2_prefill_index_score(const uint16_t* q, const float* w, const uint16_t* keys,
                                      int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q,
                                      float* scores, int32_t* n_vis, void* stream);

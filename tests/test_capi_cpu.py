@@ -143,6 +143,7 @@ def test_prefill_calls_reject_bad_arguments(csa2):
     assert csa2._prefill_score(FAKE + 2, None, FAKE, 100, 0, 2, 10, FAKE, FAKE, None) == -1  # alignment
     assert csa2._prefill_score(FAKE, None, FAKE, 100, 0, 0, 10, FAKE, FAKE, None) == -1      # ratio 0
     assert csa2._prefill_score(None, None, None, 100, 0, 2, 0, None, None, None) == 0        # n_q = 0: no-op
+    assert csa2._prefill_score(FAKE, None, FAKE, (1 << 30) + 1, 0, 2, 10, FAKE, FAKE, None) == -2  # entries
     d = _prefill_desc(csa2, n_entries=1000, n_q=16, t0=1984)
     need = csa2._prefill_ws(ctypes.byref(d))
     io = csa2._PrefillIO()
