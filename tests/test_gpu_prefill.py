@@ -124,3 +124,34 @@ def test_prefill_full_chunk_sampled_queries(wl):
         assert np.array_equal(idx0[i], ref[0].idx), f"query {i} indices"
         for l in range(len(cfg.layers)):
             assert_attention_close(inp.out[l][i].cpu().numpy(), ref[l].out, f"query {i} layer {l}")
+
+
+MANY_ROWS = {
+    # 300 queries over a 40,000-entry cache (rows long enough for the
+    # many-row selection) of which each query sees about half: half of the
+    # sampled slots lie past the visible range
+    "half_visible": _small(n_entries=40000, n_q=300, t0=40000),
+    # ratio 1, 4,101 .. 4,400 visible entries: a row needs 4,229 of them for
+    # a threshold estimate (the r-th largest of 1,024 samples with r <= 256),
+    # so queries 0..127 take the fallback and 128..299 the estimate
+    "estimate_edge": _small(n_entries=40000, n_q=300, t0=4100, ratio=1),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_ROWS))
+def test_prefill_many_rows_partial_visibility(wl, name):
+    cfg = MANY_ROWS[name]
+    print_case(f"prefill many rows {name}: n_entries={cfg.n_entries} n_q={cfg.n_q} t0={cfg.t0} ratio={cfg.ratio}")
+    inp = wl.build_prefill_inputs(cfg)
+    pf, io = wl.make_prefill(inp)
+    pf.run(io)
+    torch.cuda.synchronize()
+    keys = ow.prefill_entry_keys(cfg)
+    rng = np.random.default_rng(11)
+    sample = sorted({0, 1, 126, 127, 128, 129, 255, 256, 298, 299, *rng.integers(0, cfg.n_q, 4).tolist()})
+    idx0 = inp.idx[0].cpu().numpy()
+    for i in sample:
+        ref = ow.prefill_reference(cfg, i, entry_keys=keys)
+        assert np.array_equal(idx0[i], ref[0].idx), f"query {i} indices"
+        for l in range(len(cfg.layers)):
+            assert_attention_close(inp.out[l][i].cpu().numpy(), ref[l].out, f"query {i} layer {l}")
