@@ -130,8 +130,9 @@ csa2_status check_topk(const float* scores, int64_t n, int32_t len_div, int32_t 
 }
 
 csa2_status check_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
-                       const int32_t* idx, int32_t k_idx, const void* swa, const int32_t* swa_len,
-                       int32_t swa_max, const float* out, const void* ws, size_t ws_bytes) {
+                       const int32_t* idx, int32_t k_idx, const void* swa, int64_t swa_q_stride_rows,
+                       const int32_t* swa_len, int32_t swa_max, const float* out, const void* ws,
+                       size_t ws_bytes) {
   CSA2_REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ESHAPE, "csa2_sparse_attn: n_q must be in [0, 65535]");
   if (n_q == 0) return CSA2_OK;
   CSA2_REQUIRE(q && kv && swa_len && out, CSA2_EINVAL, "csa2_sparse_attn: null pointer");
@@ -139,6 +140,8 @@ csa2_status check_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, in
                "csa2_sparse_attn: need k_idx + swa_max >= 1");
   CSA2_REQUIRE(k_idx == 0 || idx, CSA2_EINVAL, "csa2_sparse_attn: null idx");
   CSA2_REQUIRE(swa_max == 0 || swa, CSA2_EINVAL, "csa2_sparse_attn: null swa");
+  CSA2_REQUIRE(swa_max == 0 || swa_q_stride_rows >= 0, CSA2_EINVAL,
+               "csa2_sparse_attn: swa_q_stride_rows must be >= 0");
   CSA2_REQUIRE(swa_max <= 4096 && (int64_t)k_idx + swa_max <= 128 * 64, CSA2_ESHAPE,
                "csa2_sparse_attn: k_idx + swa_max must be <= 8192 and swa_max <= 4096");
   CSA2_REQUIRE(q_per_seq >= 1, CSA2_EINVAL, "csa2_sparse_attn: q_per_seq must be >= 1");
@@ -249,7 +252,8 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                              float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_len, swa_max, out, ws, ws_bytes);
+  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, out, ws,
+                              ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;
   return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinBf16, swa_q_stride_rows, swa_len, swa_max,
                      sm_scale, out, ws, as_stream(stream));
@@ -260,7 +264,8 @@ csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_
                                  int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                                  float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_len, swa_max, out, ws, ws_bytes);
+  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, out, ws,
+                              ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;
   return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinE4m3, swa_q_stride_rows, swa_len, swa_max,
                      sm_scale, out, ws, as_stream(stream));

@@ -186,6 +186,9 @@ csa2_status csa2_flat_select(const uint16_t* q, const float* w, const uint16_t* 
  * An empty set gives o_h = 0.
  *   q   [n_q][16][512] bf16;  idx [n_q][k_idx] int32
  *   swa [*][512] bf16 rows;   swa_len [n_q] int32 (device), each <= swa_max
+ *   swa_q_stride_rows >= 0: rows between the windows of consecutive queries
+ *       (swa_max for separate windows, 1 for the overlapping windows of
+ *       consecutive prefill tokens); a negative stride is rejected
  *   out [n_q][16][512] f32
  *   ws  device workspace of csa2_sparse_attn_workspace_size(...) bytes,
  *       16-byte aligned; no initialisation needed.  Calls that share a

@@ -85,6 +85,7 @@ def test_attention_rejects_small_workspace_and_bad_sizes(csa2):
     assert call(need, k_idx=0, swa_max=0) == -2
     assert call(need, n_q=2) == -2  # two queries, one cache sequence
     assert call(need, q=FAKE + 8) == -1
+    assert call(need, st=-1) == -1 and "stride" in _err(csa2)
 
 
 def test_quant_calls_reject_bad_arguments(csa2):
