@@ -179,8 +179,9 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
       cur = io->idx[l];
     }
     // Query i's window rows start at row i of the layer's SWA buffer; the
-    // rows go to f16 once for all the queries that share them.
-    st = win_f16_launch(io->swa[l], (int64_t)d.n_q + d.swa - 1, w.win16, stream);
+    // rows go to f16 once for all the queries that share them (none are
+    // read without a window).
+    st = d.swa > 0 ? win_f16_launch(io->swa[l], (int64_t)d.n_q + d.swa - 1, w.win16, stream) : CSA2_OK;
     if (st == CSA2_OK)
       st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, w.win16, kWinF16, 1, w.win_len,
                        d.swa, d.sm_scale, io->out[l], w.attn, stream);

@@ -74,6 +74,8 @@ CHUNKS = {
     # a one-token window from token 0: the first queries see no entry at all
     # (the window alone is attended)
     "no_entries_swa1": _small(n_entries=50, n_q=40, t0=0, ratio=3, swa=1),
+    # no sliding window: the selected entries alone are attended
+    "no_window": _small(n_entries=600, n_q=25, t0=2 * 600 - 25, swa=0),
     # a long Reuse run
     "long_reuse": _small(n_entries=700, n_q=30, t0=2 * 700 - 30,
                          layers=((C.FULL, 0, 0),) + ((C.REUSE, 0, 0),) * 9),
