@@ -197,6 +197,9 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
 csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* stream_v) {
   clear_error();
   CSA2_REQUIRE(s && io, CSA2_EINVAL, "csa2_sched_decode_step: null pointer");
+  int cur = -1;
+  CSA2_REQUIRE(hipGetDevice(&cur) == hipSuccess && cur == s->device, CSA2_EINVAL,
+               "csa2_sched_decode_step: the current device is not the one the scheduler was created on");
   const csa2_sched_desc& d = s->desc;
   const hipStream_t stream = as_stream(stream_v);
   CSA2_REQUIRE(io->n_kv >= 1 && io->kv, CSA2_EINVAL, "csa2_sched_decode_step: no main-KV tensors");
@@ -311,6 +314,9 @@ const int32_t* csa2_sched_pool(const csa2_sched* s) { return (s && s->any_hier) 
 csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags) {
   clear_error();
   CSA2_REQUIRE(s && flags, CSA2_EINVAL, "csa2_sched_check: null pointer");
+  int cur = -1;
+  CSA2_REQUIRE(hipGetDevice(&cur) == hipSuccess && cur == s->device, CSA2_EINVAL,
+               "csa2_sched_check: the current device is not the one the scheduler was created on");
   int32_t h = 0;
   if (hipMemcpy(&h, s->err, sizeof h, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemset(s->err, 0, sizeof h) != hipSuccess) {

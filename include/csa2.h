@@ -302,7 +302,9 @@ typedef struct {
 
 typedef struct csa2_sched csa2_sched;
 
-/* Validate the table and allocate the scheduler's device workspace. */
+/* Validate the table and allocate the scheduler's device workspace on the
+ * current device; csa2_sched_decode_step and csa2_sched_check must be called
+ * with that device current (else CSA2_EINVAL). */
 csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out);
 /* One decode step on `stream`: the key append (if io.new_idx_k), the
  * latent append (if io.new_row), then every layer in table order.
