@@ -288,6 +288,16 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_kernel(const float* 
   if (b == 0 && tid == 0) ws.wcnt[kCountSlot] = ws.wcnt[kClaimSlot] = 0u;
 }
 
+// The smallest score whose order key is >= lo, for a threshold key lo that
+// is 0, a key of a non-NaN score, or kNoEstimate: key(x) >= lo and
+// key(x) != 0 hold exactly when x >= key_threshold(lo) (-0 and +0 share a
+// key and compare equal; lo = 0 admits every score but NaN and -inf; the
+// NaN for kNoEstimate admits none).
+__device__ __forceinline__ float key_threshold(uint32_t lo) {
+  if (lo == 0) return -__FLT_MAX__;
+  return __builtin_bit_cast(float, (lo & 0x80000000u) ? (lo & 0x7FFFFFFFu) : ~lo);
+}
+
 // kVec: rows start 16-byte aligned (n % 4 == 0, aligned scores), so each
 // thread loads runs of four slots; slot of register j: s0 + 4 * (j / 4 *
 // NT + tid) + j % 4 (else s0 + j * NT + tid).
@@ -300,9 +310,10 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_filter_kernel(const 
   __shared__ uint32_t wave_sum[kPassThreads / 64];
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
-  const int nv = (int)valid_slots(n, lens, len_div, b);
   const int s0 = blockIdx.x * kFilterSlots;
-  const int nloc = min(max(nv - s0, 0), kFilterSlots);  // valid slots of this workgroup
+  // Loads are clamped to the row (n slots), not to the visible part, so
+  // that they need no value from memory; visibility applies afterwards.
+  const int nrow = min((int)n - s0, kFilterSlots);
   const float* sc = scores + (int64_t)b * n;
   uint32_t* wrow = ws.wcnt + (int64_t)b * kTopkFilterWgMax;
   auto slot_of = [&](int j) {
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_filter_kernel(const 
   };
   float v[kPer];
   if constexpr (kVec) {
-    const int last = max(nloc - 1, 0) >> 2;  // last 16-byte group with a valid slot
+    const int last = (nrow - 1) >> 2;  // last 16-byte group of the row
 #pragma unroll
     for (int j = 0; j < kPer / 4; ++j) {
       const f32x4 x = reinterpret_cast<const f32x4*>(sc + s0)[min(j * kPassThreads + tid, last)];
@@ -318,29 +329,28 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_filter_kernel(const 
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = sc[s0 + min(slot_of(j), max(nloc - 1, 0))];
+    for (int j = 0; j < kPer; ++j) v[j] = sc[s0 + min(slot_of(j), nrow - 1)];
   }
+  const int nv = (int)valid_slots(n, lens, len_div, b);
+  const int nloc = min(max(nv - s0, 0), kFilterSlots);  // valid slots of this workgroup
   const uint32_t lo = wrow[kThresholdSlot];
-  if (lo == kNoEstimate) {
-    if (tid == 0) wrow[blockIdx.x] = kNoEstimate;
-    return;
-  }
-  uint32_t key[kPer];
+  // A slot is a candidate when its key is nonzero and >= lo, i.e. when its
+  // score is >= the float whose key lo is (one compare per slot; NaN
+  // compares false).  No early return on a missing estimate: its threshold
+  // is a NaN, which nothing passes.
+  const float t = key_threshold(lo);
   uint32_t cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    key[j] = slot_of(j) < nloc ? order_key(v[j]) : 0u;
-    cnt += (key[j] >= lo && key[j] != 0) ? 1u : 0u;
-  }
+  for (int j = 0; j < kPer; ++j) cnt += (v[j] >= t && slot_of(j) < nloc) ? 1u : 0u;
   uint32_t total;
   uint32_t pos = block_exclusive_scan<kPassThreads>(cnt, wave_sum, &total);
   const uint32_t per_wg = kTopkCandCap / gridDim.x;
-  if (tid == 0) wrow[blockIdx.x] = total;
+  if (tid == 0) wrow[blockIdx.x] = lo == kNoEstimate ? kNoEstimate : total;
   uint2* gc = ws.cand + (int64_t)b * kTopkCandCap + (int64_t)blockIdx.x * per_wg;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    if (key[j] >= lo && key[j] != 0) {
-      if (pos < per_wg) gc[pos] = make_uint2(key[j], (uint32_t)(s0 + slot_of(j)));
+    if (v[j] >= t && slot_of(j) < nloc) {
+      if (pos < per_wg) gc[pos] = make_uint2(order_key(v[j]), (uint32_t)(s0 + slot_of(j)));
       ++pos;
     }
   }

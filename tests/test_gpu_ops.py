@@ -253,7 +253,8 @@ def test_topk_many_long_rows(csa2, n, k):
     per workgroup region, then the selection per row -- with rows whose
     estimate holds (integer-valued and continuous scores), a row whose
     threshold bin overflows a region, rows too short to estimate, an empty
-    row and ragged lengths, all of which must equal the oracle."""
+    row, NaN scores, an all-negative row, signed zeros and ragged lengths,
+    all of which must equal the oracle."""
     n_seq = 300
     rng = np.random.default_rng(n + k)
     q = rng.integers(-4, 5, size=(8, 64))
@@ -266,6 +267,11 @@ def test_topk_many_long_rows(csa2, n, k):
             sc[b] = np.maximum(keys @ q.T, 0).sum(1).astype(np.float32)
     sc[7, :9000] = 1e5 + (np.arange(9000) % 3)        # 9,000 keys in one bin, in one region
     sc[8, :] = -np.inf                                  # no candidate
+    sc[40, ::7] = np.nan                                # NaN is never a candidate
+    sc[41] = -np.abs(sc[41]) - 1.0                      # all scores (and the threshold) negative
+    sc[42] = -np.abs(sc[42]) - 1.0                      # the top scores: -0 and +0, which tie
+    sc[42, ::5] = -0.0
+    sc[42, 1::5] = 0.0
     lens = np.full(n_seq, n, np.int32)
     lens[9], lens[10], lens[11] = 3 * k, 1000, 4 * k + 5   # too short to estimate / just enough
     lens[12:40] = rng.integers(4 * k, n, size=28)
@@ -273,9 +279,9 @@ def test_topk_many_long_rows(csa2, n, k):
     out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
     csa2.topk(dev(sc), k, out, lens=dev(lens))
     got = out.cpu().numpy()
-    for b in sorted({0, 1, 2, 7, 8, 9, 10, 11, 12, 13, 39, 150, n_seq - 1}):
+    for b in sorted({0, 1, 2, 7, 8, 9, 10, 11, 12, 13, 39, 40, 41, 42, 150, n_seq - 1}):
         nv = lens[b]
-        ok = np.isfinite(sc[b, :nv])
+        ok = ~np.isnan(sc[b, :nv]) & (sc[b, :nv] != -np.inf)
         ref = oracle.select(sc[b, :nv][ok], np.arange(nv)[ok], k)
         assert np.array_equal(got[b], ref), b
 
