@@ -27,12 +27,18 @@ constexpr int kTilesPerWave = 8;                       // 16 keys per tile
 constexpr int kKeysPerWG = 4 * kTilesPerWave * 16;     // 512 keys, 4 wavefronts
 
 // Weighted ReLU sum of four heads, ((w0 r0 + w1 r1) + w2 r2) + w3 r3, every
-// product and sum rounded on its own (no fused multiply-add).
+// product and sum rounded on its own (no fused multiply-add).  ReLU is the
+// median of (x, 0, +inf): one v_med3_f32, equal to fmaxf(x, 0) for every
+// value an MFMA produces (a quiet NaN gives 0), where fmaxf costs a
+// canonicalising max in front of its own.  The +inf bound is hidden from
+// constant folding, which would turn the median back into fmaxf.
 __device__ __forceinline__ float relu_wsum4(const f32x4& acc, const float* wh) {
 #pragma clang fp contract(off)
-  float part = wh[0] * fmaxf(acc[0], 0.f);
+  float inf = __builtin_inff();
+  asm("" : "+s"(inf));
+  float part = wh[0] * __builtin_amdgcn_fmed3f(acc[0], 0.f, inf);
 #pragma unroll
-  for (int r = 1; r < 4; ++r) part = part + wh[r] * fmaxf(acc[r], 0.f);
+  for (int r = 1; r < 4; ++r) part = part + wh[r] * __builtin_amdgcn_fmed3f(acc[r], 0.f, inf);
   return part;
 }
 
@@ -233,7 +239,11 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       acc = mfma16x16x32(a1, as_bf16x8(kf[c][1]), acc);
       const float part = relu_wsum4(acc, wh);       // heads 4(g%2)..+3
       const float score = fold16_add(part);  // lo + hi
-      if ((g & 1) == 0) st[(g >> 1) * 128 + 16 * c + n] = (e_lane + 16 * c < vis) ? score : kNegInf;
+      // Lanes g and g^1 hold the same sum (the fold adds the two halves in
+      // either order) and write it to the same address; with no lane
+      // condition the column tiles form one block whose MFMAs and epilogues
+      // the compiler interleaves.
+      st[(g >> 1) * 128 + 16 * c + n] = (e_lane + 16 * c < vis) ? score : kNegInf;
     }
     __builtin_amdgcn_wave_barrier();
     // Two rows of 128 scores: lane l stores query 2rt + l/32, entries 4(l%32)..+3.
