@@ -38,15 +38,15 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12694647, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12694629, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
                     "a3cde2d3d12b1ebf48ca75df8bc97f845f788e412ba884ef028cef3a93e53615",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/block_scan": {
-        "bytes": 279933591, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 279956055, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "7fda4950423024c267ca9cbdb945e520fe7a3513557eeaa6a1be25d8ad0c7220",
+                    "6d1a3259d2ecb38b6d5bcfa94c14686bd1a9a43086a023f866271d69e3dde088",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
@@ -54,9 +54,9 @@ MEASURED_TRAFFIC = {
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "a6b9172621f3d03f20519b4513831baaf8301db1063e28fef2e42cb10c075217"}},
     "encoder_1m/flat_select": {
-        "bytes": 1092903317, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "bytes": 1092888005, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "7fda4950423024c267ca9cbdb945e520fe7a3513557eeaa6a1be25d8ad0c7220",
+                    "6d1a3259d2ecb38b6d5bcfa94c14686bd1a9a43086a023f866271d69e3dde088",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
                     "9c3b97d689555148c95531679d825a56836e7364b62ded2785b2bc277ea9a737",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
