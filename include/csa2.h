@@ -117,9 +117,11 @@ csa2_status csa2_quant_append(const uint16_t* src, csa2_fp4_kv kv, int32_t* lens
  * block pool; Reindex: rescoring with its own Q).  The pages print no
  * formula; the score of key k is
  *     score = sum_h w_h * max(0, q_h . k),   h < 8 indexer heads,
- * (w == NULL means w_h = 1; with w the sum is taken in binary32 as
- * ((w0r0 + w1r1) + w2r2) + w3r3, the same for heads 4..7, then lo + hi).
- * Exact when q, k are integer-valued with |partial sums| < 2^24.
+ * (w == NULL means w_h = 1).  The result is the real sum rounded once to
+ * binary32 -- exact -- when q, k are integer-valued (|q_h . k| < 2^24) and,
+ * with w, every product w_h r_h and every partial sum is representable in
+ * binary32 (e.g. weights that are small multiples of 1/8); with other
+ * weights the sum is a binary32 sum in an unspecified order.
  *   q      [n_seq][8][64] bf16; w [n_seq][8] f32 or NULL
  *   keys   [n_seq][key_cap][64] bf16
  *   lens   [n_seq] int32 (device): positions per sequence

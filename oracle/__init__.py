@@ -50,9 +50,11 @@ PINS = {
     "orc_e2m1_value": "E2M1 grid {0,.5,1,1.5,2,3,4,6} (golden file)",
     "orc_scale_code": "all 65,536 bf16 amax vs exact-rational nearest-even by Fraction bisection",
     "orc_e2m1_code": "all bf16 magnitudes x all 126 nonzero scales vs float64 quotient + numpy half-even",
-    "orc_quant_row": "byte layout golden row; dequant(quant(grid*s)) == grid*s",
-    "orc_index_score_one": "one-hot closed forms, sign/ReLU cases, numpy int64 matmul on integer inputs",
-    "orc_select": "brute force via numpy lexsort; tie-heavy inputs; -1 padding",
+    "orc_quant_row": "byte layout golden row; dequant(quant(grid*s)) == grid*s; every reachable (bf16 magnitude, "
+                     "scale) pair in both signs and every bf16 amax vs numpy/torch (tests/quant_sweep.py)",
+    "orc_index_score_one": "one-hot closed forms, sign/ReLU cases, numpy int64 matmul on integer inputs, "
+                           "weighted sums against exact rational (Fraction) arithmetic rounded once",
+    "orc_select": "brute force via numpy lexsort; tie-heavy inputs; -1 padding; NaN/-inf never selected, -0 == +0",
     "orc_pool_blocks/orc_pool_select": "hierarchical == flat when blocks <= pool; subset/size invariants",
     "orc_sparse_attn": "k >= L equals torch CPU float64 dense softmax attention; 1 key, equal keys, q = 0",
     "decode_step": "Reuse reproduces the latest Full/Reindex indices; Reindex with Full's Q == Full",

@@ -6,7 +6,8 @@
  *
  * Every function is written from the definition of what it computes, scalar,
  * without blocking or reordering, so that it can be checked by eye.  Floating
- * point is double unless stated; the quantiser compares exact products.
+ * point is double, rounded once to binary32 where a result is stored as
+ * binary32; the quantiser compares exact products.
  *
  * Citations name the page and its section:
  *   [P1] "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M Context, FP4 KV
@@ -154,30 +155,24 @@ void orc_dequant_row(const uint8_t* codes, const uint8_t* scales, double* out) {
 
 /* Indexer score of one key [P1 "Compressed Sparse Attention 2 (CSA2)"]: the
  * pages name an indexer Q scored against indexer K but print no formula.
- * READING: per indexer head h, r_h = max(0, q_h . k); score = sum_h w_h r_h.
- * Without weights (w == NULL) every w_h = 1 and the score is the exact sum.
- * With weights the sum is taken in binary32 in a fixed order:
- * ((w0 r0 + w1 r1) + w2 r2) + w3 r3, the same for heads 4..7, then the two
- * partial sums are added. */
+ * READING: per indexer head h, r_h = max(0, q_h . k); score = sum_h w_h r_h
+ * (w == NULL: every w_h = 1), the real sum rounded once to binary32.
+ * Every bf16 product is exact in double and so is each w_h r_h (a binary32
+ * weight times an r_h of at most 17 significant bits for integer-valued
+ * inputs); the double sums below are exact whenever the terms span fewer
+ * than 53 bits, which holds for integer-valued q, k and for weights with
+ * short significands -- the inputs for which the library claims exact
+ * scores.  No order of summation is implied by the definition. */
 float orc_index_score_one(const uint16_t* q, const float* w, const uint16_t* k) {
-  double r[IDX_HEADS];
+  double s = 0.0;
   for (int h = 0; h < IDX_HEADS; ++h) {
     double dot = 0.0;
     for (int d = 0; d < IDX_DIM; ++d)
       dot += orc_bf16_value(q[h * IDX_DIM + d]) * orc_bf16_value(k[d]);
-    r[h] = dot > 0.0 ? dot : 0.0;
+    const double r = dot > 0.0 ? dot : 0.0;
+    s += (w ? (double)w[h] : 1.0) * r;
   }
-  if (!w) {
-    double s = 0.0;
-    for (int h = 0; h < IDX_HEADS; ++h) s += r[h];
-    return (float)s;
-  } else {
-    float lo = (float)w[0] * (float)r[0];
-    for (int h = 1; h < 4; ++h) lo = lo + (float)w[h] * (float)r[h];
-    float hi = (float)w[4] * (float)r[4];
-    for (int h = 5; h < 8; ++h) hi = hi + (float)w[h] * (float)r[h];
-    return lo + hi;
-  }
+  return (float)s;
 }
 
 /* Scores of n keys given by row ids into a key array [*][64]. */
@@ -193,8 +188,9 @@ typedef struct {
   int64_t id;
 } cand_t;
 
-/* Larger score first; equal scores: lower id first (READING: ties go to the
- * lower position; the pages give no tie rule). */
+/* Larger score first; equal scores (-0 == +0 under these comparisons): lower
+ * id first (READING: ties go to the lower position; the pages give no tie
+ * rule). */
 static int cand_order(const void* pa, const void* pb) {
   const cand_t* a = (const cand_t*)pa;
   const cand_t* b = (const cand_t*)pb;
@@ -209,17 +205,22 @@ static int id_order(const void* pa, const void* pb) {
 }
 
 /* Top-k of n candidates [P1 "Compressed Sparse Attention 2 (CSA2)"]: keep the
- * min(k, n) best by (score desc, id asc); write their ids ascending into
- * out[0..k-1], padding with -1 (READING: output order and padding).
- * Returns the number selected. */
+ * min(k, #candidates) best by (score desc, id asc); write their ids ascending
+ * into out[0..k-1], padding with -1 (READING: output order and padding).
+ * READING (non-candidates): a NaN or -inf score never takes part -- it marks
+ * a slot with nothing to select (a position past the sequence, an empty pool
+ * block) -- and -0 equals +0.  Returns the number selected. */
 int64_t orc_select(const float* scores, const int64_t* ids, int64_t n, int64_t k, int64_t* out) {
   cand_t* c = (cand_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(cand_t));
-  int64_t take = n < k ? n : k;
+  int64_t m = 0;
   for (int64_t i = 0; i < n; ++i) {
-    c[i].score = scores[i];
-    c[i].id = ids[i];
+    if (isnan(scores[i]) || scores[i] == -INFINITY) continue;
+    c[m].score = scores[i];
+    c[m].id = ids[i];
+    ++m;
   }
-  qsort(c, (size_t)n, sizeof(cand_t), cand_order);
+  const int64_t take = m < k ? m : k;
+  qsort(c, (size_t)m, sizeof(cand_t), cand_order);
   for (int64_t i = 0; i < take; ++i) out[i] = c[i].id;
   qsort(out, (size_t)take, sizeof(int64_t), id_order);
   for (int64_t i = take; i < k; ++i) out[i] = -1;

@@ -119,7 +119,7 @@ def test_element_codes_all_bf16_times_all_scales():
     correctly rounded, and it is exactly a grid midpoint iff x is) followed
     by numpy's half-to-even rounding on each uniform stretch of the grid."""
     _, x = _all_positive_finite_bf16()
-    x = x[::7]  # every 7th magnitude: 4,663 values x 126 scales
+    # all 32,640 magnitudes x 126 scales (unreachable pairs included: x > 6.375 s saturates)
     lib = oracle.lib()
     for sc in range(1, 127):
         s = oracle.e4m3_value(sc)
@@ -130,6 +130,19 @@ def test_element_codes_all_bf16_times_all_scales():
         ref = np.minimum(ref, 7).astype(np.int64)
         got = np.array([lib.orc_e2m1_code(v, 0, s) for v in x], dtype=np.int64)
         assert np.array_equal(got, ref), sc
+
+
+def test_quant_rows_exhaustive_sweep():
+    """Every (bf16 magnitude, scale) pair the quantiser can meet, in both
+    signs, and every bf16 magnitude as a group's amax (tests/quant_sweep.py:
+    expected codes from numpy float64 and torch's E4M3 cast): the oracle's
+    quantised bytes equal them all."""
+    from quant_sweep import sweep
+
+    rows, codes, scales = sweep()
+    rc, rs = oracle.quant_rows(rows)
+    assert np.array_equal(rs, scales)
+    assert np.array_equal(rc, codes)
 
 
 def test_quant_row_worked_example():
@@ -212,29 +225,49 @@ def test_score_matches_int64_matmul_relu_sum():
     assert np.any(want != np.maximum((kv[ids] @ qv.T).sum(axis=1), 0))
 
 
-def test_score_weights_order_and_values():
+def _exact_weighted_score(qv, kv_row, w):
+    """sum_h w_h * max(0, q_h . k) in exact rational arithmetic, rounded once
+    to binary32 (Fraction -> float is correctly rounded to double; the value
+    is a short dyadic or the double is then rounded to binary32 by numpy)."""
+    total = Fraction(0)
+    for h in range(8):
+        dot = sum(int(a) * int(b) for a, b in zip(qv[h], kv_row))
+        total += Fraction(float(w[h])) * max(dot, 0)
+    return np.float32(float(total))
+
+
+def test_score_weights_exact_rational():
+    """Weighted scores against exact rational arithmetic (fractions.Fraction):
+    dyadic weights, whose products and partial sums are exact in binary32 (the
+    inputs the library scores bit-exactly), negative ones included; and
+    N(0,1) binary32 weights, where the oracle's sum must still be the real sum
+    rounded once."""
     rng = np.random.default_rng(3)
     qb, qv = _int_bf16(rng, (8, 64))
-    kb, kv = _int_bf16(rng, (500, 64))
-    r = np.maximum(kv @ qv.T, 0).astype(np.float32)           # [500][8]
-    w_int = np.array([1, 2, 0, 3, 1, 1, 4, 2], np.float32)    # exact case
-    s = oracle.index_score(qb, kb, np.arange(500), w=w_int)
-    assert np.array_equal(s, (r * w_int).sum(axis=1).astype(np.float32))
-    w = rng.standard_normal(8).astype(np.float32)
-    s = oracle.index_score(qb, kb, np.arange(500), w=w)
-    lo = r[:, 0] * w[0]
-    for h in range(1, 4):
-        lo = (lo + r[:, h] * w[h]).astype(np.float32)
-    hi = r[:, 4] * w[4]
-    for h in range(5, 8):
-        hi = (hi + r[:, h] * w[h]).astype(np.float32)
-    assert np.array_equal(s, (lo + hi).astype(np.float32))
+    kb, kv = _int_bf16(rng, (300, 64))
+    for w in (np.array([1, 2, 0, 3, 1, 1, 4, 2], np.float32),
+              (rng.integers(-16, 17, size=8) / 8).astype(np.float32),
+              (rng.integers(-3, 40, size=8) * 0.25).astype(np.float32),
+              rng.standard_normal(8).astype(np.float32)):
+        s = oracle.index_score(qb, kb, np.arange(300), w=w)
+        want = np.array([_exact_weighted_score(qv, kv[i], w) for i in range(300)], np.float32)
+        assert np.array_equal(s, want), w
+    # unit weights are the unweighted score
+    ones = np.ones(8, np.float32)
+    assert np.array_equal(oracle.index_score(qb, kb, np.arange(300), w=ones), oracle.index_score(qb, kb, np.arange(300)))
 
 
 # ---------------------------------------------------------------- selection
 def _brute_select(scores, ids, k):
-    order = np.lexsort((ids, -scores.astype(np.float64)))  # score desc, id asc
-    keep = np.sort(ids[order[:k]])
+    """Top-k by a full sort: NaN and -inf are not candidates; among the rest
+    score descending (float64 keys, so -0 and +0 compare equal), then id
+    ascending; ids written ascending, -1 padded."""
+    scores = np.asarray(scores, np.float32)
+    ids = np.asarray(ids, np.int64)
+    cand = ~np.isnan(scores) & (scores != -np.inf)
+    s, i = scores[cand].astype(np.float64), ids[cand]
+    order = np.lexsort((i, -s))  # score desc, id asc
+    keep = np.sort(i[order[:k]])
     return np.concatenate([keep, -np.ones(k - len(keep), np.int64)])
 
 
@@ -245,6 +278,31 @@ def test_select_matches_lexsort(n, k, levels):
     scores = rng.integers(0, levels, size=n).astype(np.float32)
     ids = rng.permutation(10 * n + 1)[:n].astype(np.int64)
     assert np.array_equal(oracle.select(scores, ids, k), _brute_select(scores, ids, k))
+
+
+@pytest.mark.parametrize("k", [1, 50, 512, 3000])
+def test_select_non_candidates_and_signed_zeros(k):
+    """NaN and -inf scores are never selected (also when fewer than k finite
+    scores remain: the rest is -1), +inf is the largest score, and -0 ties
+    with +0 (the lower id wins)."""
+    rng = np.random.default_rng(k)
+    n = 4000
+    scores = rng.integers(-3, 4, size=n).astype(np.float32)
+    scores[::5] = np.nan
+    scores[1::7] = -np.inf
+    scores[2::11] = np.inf
+    scores[3:600:9] = -0.0
+    scores[4:600:9] = 0.0
+    ids = rng.permutation(3 * n)[:n].astype(np.int64)
+    got = oracle.select(scores, ids, k)
+    assert np.array_equal(got, _brute_select(scores, ids, k))
+    assert not np.any(np.isin(got, ids[np.isnan(scores) | (scores == -np.inf)]))
+    # only NaN / -inf: nothing is selected
+    bad = np.where(np.arange(100) % 2 == 0, np.nan, -np.inf).astype(np.float32)
+    assert np.all(oracle.select(bad, np.arange(100), 8) == -1)
+    # -0 and +0 tie: the lower id is kept whatever the sign
+    z = np.array([0.0, -0.0, 0.0, -0.0], np.float32)
+    assert list(oracle.select(z, [7, 3, 5, 1], 2)) == [1, 3]
 
 
 def test_select_ties_take_lower_ids():
