@@ -51,7 +51,8 @@ class _SchedDesc(ctypes.Structure):
 class _StepIO(ctypes.Structure):
     _fields_ = [("n_kv", _I32), ("kv", _P), ("lens", _P), ("new_row", _P), ("append_kv", _I32),
                 ("idx_k", _P), ("blk_k", _P), ("idx_q", _P), ("idx_w", _P), ("main_q", _P),
-                ("swa", _P), ("swa_len", _P), ("out", _P), ("new_idx_k", _P), ("layer_idx_k", _P)]
+                ("swa", _P), ("swa_len", _P), ("out", _P), ("new_idx_k", _P), ("layer_idx_k", _P),
+                ("new_swa_row", _P)]
 
 
 class _PrefillDesc(ctypes.Structure):
@@ -92,7 +93,7 @@ _sched_create = _sig("csa2_sched_create", _I32, ctypes.POINTER(_SchedDesc), ctyp
 _sched_step = _sig("csa2_sched_decode_step", _I32, _P, ctypes.POINTER(_StepIO), _P)
 _sched_indices = _sig("csa2_sched_indices", _P, _P, _I32)
 _sched_pool = _sig("csa2_sched_pool", _P, _P)
-_sched_check = _sig("csa2_sched_check", _I32, _P, ctypes.POINTER(_I32))
+_sched_check = _sig("csa2_sched_check", _I32, _P, ctypes.POINTER(_I32), _P)
 _sched_destroy = _sig("csa2_sched_destroy", None, _P)
 _prefill_score = _sig("csa2_prefill_index_score", _I32, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P)
 _prefill_ws = _sig("csa2_prefill_workspace_size", _SZ, ctypes.POINTER(_PrefillDesc))
@@ -284,10 +285,13 @@ class Sched:
         self.close()
 
     def prepare(self, kv: Sequence[FP4KV], lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k=None,
-                new_row=None, append_kv: int = 0, idx_w=None, new_idx_k=None, layer_idx_k=None) -> "_StepIO":
+                new_row=None, append_kv: int = 0, idx_w=None, new_idx_k=None, layer_idx_k=None,
+                new_swa_row=None) -> "_StepIO":
         """Build (and keep alive) the step descriptor for a fixed set of tensors.
         layer_idx_k: None, or per layer the own indexer K of a flat Full layer
-        (None entries: idx_k)."""
+        (None entries: idx_k).  new_swa_row: None, or per layer the step token's
+        window rows [n_seq][512], stored into window slot (lens[b] - 1) % swa_max
+        as the layer runs."""
         nl = len(self.layers)
         kvs = (_FP4KV * len(kv))(*[k.c() for k in kv])
         P = _P * nl
@@ -295,12 +299,14 @@ class Sched:
         iw = P(*[_ptr(t) for t in idx_w]) if idx_w is not None else None
         mq, sw, ou = P(*[_ptr(t) for t in main_q]), P(*[_ptr(t) for t in swa]), P(*[_ptr(t) for t in out])
         lk = P(*[_ptr(t) if t is not None else None for t in layer_idx_k]) if layer_idx_k is not None else None
+        nw = P(*[_ptr(t) for t in new_swa_row]) if new_swa_row is not None else None
         io = _StepIO(len(kv), ctypes.cast(kvs, _P), _ptr(lens), _ptr(new_row), append_kv, _ptr(idx_k),
                      _ptr(blk_k), ctypes.cast(iq, _P), ctypes.cast(iw, _P) if iw is not None else None,
                      ctypes.cast(mq, _P), ctypes.cast(sw, _P), _ptr(swa_len), ctypes.cast(ou, _P),
-                     _ptr(new_idx_k), ctypes.cast(lk, _P) if lk is not None else None)
-        io._keep = (kvs, iq, iw, mq, sw, ou, lk, kv, lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k,
-                    new_row, idx_w, new_idx_k, layer_idx_k)
+                     _ptr(new_idx_k), ctypes.cast(lk, _P) if lk is not None else None,
+                     ctypes.cast(nw, _P) if nw is not None else None)
+        io._keep = (kvs, iq, iw, mq, sw, ou, lk, nw, kv, lens, idx_k, main_q, swa, swa_len, out, idx_q, blk_k,
+                    new_row, idx_w, new_idx_k, layer_idx_k, new_swa_row)
         return io
 
     def decode_step(self, io: "_StepIO", stream=None) -> None:
@@ -317,9 +323,11 @@ class Sched:
             return None
         return _device_copy_int32(p, self.n_seq * self.pool_blocks).view(self.n_seq, self.pool_blocks)
 
-    def check(self) -> int:
+    def check(self, stream=None) -> int:
+        """Read and clear the device flags on `stream` (default: the current stream), after
+        the steps enqueued there."""
         f = _I32()
-        _check(_sched_check(self._h, ctypes.byref(f)))
+        _check(_sched_check(self._h, ctypes.byref(f), _stream(stream)))
         return f.value
 
 

@@ -25,7 +25,8 @@ csa2_status index_score_local_launch(const uint16_t*, const float*, const uint16
                                      float*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+                        const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
+                        float*, void*, hipStream_t);
 
 namespace {
 thread_local std::string g_error;
@@ -168,7 +169,7 @@ extern "C" {
 
 const char* csa2_last_error(void) { return g_error.c_str(); }
 
-int32_t csa2_abi_version(void) { return 4; }
+int32_t csa2_abi_version(void) { return 5; }
 
 csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                             void* stream) {
@@ -256,7 +257,7 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
                               ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;
   return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinBf16, swa_q_stride_rows, swa_len, swa_max,
-                     sm_scale, out, ws, as_stream(stream));
+                     nullptr, nullptr, sm_scale, out, ws, as_stream(stream));
 }
 
 csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
@@ -268,7 +269,7 @@ csa2_status csa2_sparse_attn_f8w(const uint16_t* q, int32_t n_q, const csa2_fp4_
                               ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;
   return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinE4m3, swa_q_stride_rows, swa_len, swa_max,
-                     sm_scale, out, ws, as_stream(stream));
+                     nullptr, nullptr, sm_scale, out, ws, as_stream(stream));
 }
 
 csa2_status csa2_block_keys(const uint16_t* idx_k, int64_t key_cap, const int32_t* lens, int32_t blk,

@@ -21,7 +21,8 @@ csa2_status prefill_score_launch(const uint16_t*, const float*, const uint16_t*,
                                  int32_t, float*, int32_t*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+                        const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
+                        float*, void*, hipStream_t);
 csa2_status win_f16_launch(const uint16_t*, int64_t, uint16_t*, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
 
@@ -184,7 +185,7 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
     st = d.swa > 0 ? win_f16_launch(io->swa[l], (int64_t)d.n_q + d.swa - 1, w.win16, stream) : CSA2_OK;
     if (st == CSA2_OK)
       st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, w.win16, kWinF16, 1, w.win_len,
-                       d.swa, d.sm_scale, io->out[l], w.attn, stream);
+                       d.swa, nullptr, nullptr, d.sm_scale, io->out[l], w.attn, stream);
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;

@@ -24,7 +24,8 @@ csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, i
 int64_t index_score_local_groups(int64_t key_cap);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                        const void*, int, int64_t, const int32_t*, int32_t, float, float*, void*, hipStream_t);
+                        const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
+                        float*, void*, hipStream_t);
 csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, int64_t, int32_t, const int32_t*,
                                int32_t*, int32_t, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
@@ -231,6 +232,9 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
     CSA2_REQUIRE(!io->layer_idx_k || !io->layer_idx_k[l] || (L.mode == CSA2_FULL && !L.hierarchical), CSA2_EINVAL,
                  "csa2_sched_decode_step: layer_idx_k entry " + std::to_string(l) +
                      " must be NULL (only flat Full layers own indexer K)");
+    CSA2_REQUIRE(!io->new_swa_row || (io->new_swa_row[l] && a16(io->new_swa_row[l])), CSA2_EINVAL,
+                 "csa2_sched_decode_step: new_swa_row entry " + std::to_string(l) +
+                     " must be a 16-byte aligned row block");
     CSA2_REQUIRE(a16(io->main_q[l]) && a16(io->swa[l]) && a16(io->out[l]) &&
                      (L.mode == CSA2_REUSE || a16(io->idx_q[l])) && (!io->layer_idx_k || a16(io->layer_idx_k[l])),
                  CSA2_EINVAL,
@@ -297,8 +301,10 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       }
     }
     if (st == CSA2_OK)
-      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l], d.swa_fp8 ? kWinE4m3 : kWinBf16,
-                       d.swa_max, io->swa_len, d.swa_max, d.sm_scale, io->out[l], s->attn_ws, stream);
+      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l],
+                       d.swa_fp8 ? kWinE4m3 : kWinBf16, d.swa_max, io->swa_len, d.swa_max,
+                       io->new_swa_row ? io->new_swa_row[l] : nullptr, io->lens, d.sm_scale, io->out[l],
+                       s->attn_ws, stream);
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;
@@ -311,15 +317,19 @@ const int32_t* csa2_sched_indices(const csa2_sched* s, int32_t layer) {
 
 const int32_t* csa2_sched_pool(const csa2_sched* s) { return (s && s->any_hier) ? s->pool : nullptr; }
 
-csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags) {
+csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags, void* stream_v) {
   clear_error();
   CSA2_REQUIRE(s && flags, CSA2_EINVAL, "csa2_sched_check: null pointer");
   int cur = -1;
   CSA2_REQUIRE(hipGetDevice(&cur) == hipSuccess && cur == s->device, CSA2_EINVAL,
                "csa2_sched_check: the current device is not the one the scheduler was created on");
+  // Read and clear in order on the stream the steps ran on: the read sees
+  // every step enqueued there before, and the clear cannot overtake a flag
+  // that one of them raises.
+  const hipStream_t stream = as_stream(stream_v);
   int32_t h = 0;
-  if (hipMemcpy(&h, s->err, sizeof h, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemset(s->err, 0, sizeof h) != hipSuccess) {
+  if (hipMemcpyAsync(&h, s->err, sizeof h, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemsetAsync(s->err, 0, sizeof h, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess) {
     set_error(std::string("csa2_sched_check: ") + hipGetErrorString(hipGetLastError()));
     return CSA2_EHIP;
   }

@@ -125,6 +125,7 @@ struct AttnState {
 struct AttnTile {
   u32x4 raw[16];
   uint2 s8;
+  uint8_t* dst;  // window slot that receives the step's new row (read from elsewhere), or null
   int32_t id;
   int row0;
   bool swa, in_range, ok;
@@ -142,6 +143,8 @@ struct AttnArgs {
   const uint8_t* swa;  // window rows: bf16 (1,024 B) or E4M3 (512 B) per row
   int64_t swa_q_stride_rows;
   int32_t n_swa;
+  const uint8_t* new_win;  // the step's new window row of this query's sequence, or null
+  int32_t slot;            // its window slot, (lens - 1) % swa_max (-1: none)
   int n_tiles, swa_tiles;
 };
 
@@ -184,9 +187,12 @@ __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n,
     t.ok = t.in_range && j < a.n_swa;
     constexpr int kRowBytes = kWin == kWinE4m3 ? CSA2_LATENT : 2 * CSA2_LATENT;
     // A row past the window reads the zero row instead (its values then
-    // convert to 0 and need no masking).
-    const uint8_t* row = t.ok ? a.swa + ((int64_t)qb * a.swa_q_stride_rows + j) * kRowBytes
-                              : reinterpret_cast<const uint8_t*>(kZeroRow);
+    // convert to 0 and need no masking).  The slot of the step's token reads
+    // the new row, which the chunk then stores into that slot.
+    const uint8_t* ring = a.swa + ((int64_t)qb * a.swa_q_stride_rows + j) * kRowBytes;
+    const bool fresh = t.ok && j == a.slot;
+    t.dst = fresh ? const_cast<uint8_t*>(ring) + (kRowBytes / 4) * g : nullptr;
+    const uint8_t* row = fresh ? a.new_win : t.ok ? ring : reinterpret_cast<const uint8_t*>(kZeroRow);
     const u32x4* sp = reinterpret_cast<const u32x4*>(row + (kRowBytes / 4) * g);
 #pragma unroll
     for (int i = 0; i < (kWin == kWinE4m3 ? 8 : 16); ++i) t.raw[i] = sp[i];
@@ -236,7 +242,13 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
       s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
     }
   } else {
-    // (Rows past the window were loaded from the zero row.)
+    // (Rows past the window were loaded from the zero row.)  The step's new
+    // window row joins the ring here: the lanes that hold it store it.
+    if (t.dst) {
+      u32x4* d = reinterpret_cast<u32x4*>(t.dst);
+#pragma unroll
+      for (int i = 0; i < (kWin == kWinE4m3 ? 8 : 16); ++i) d[i] = t.raw[i];
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const u32x4 x = kWin == kWinE4m3 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
@@ -339,10 +351,10 @@ template <int W, int kWin>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t cap, int32_t q_per_seq,
-    const int32_t* __restrict__ idx, int32_t k_idx, const uint8_t* __restrict__ swa,
-    int64_t swa_q_stride_rows, const int32_t* __restrict__ swa_len, int32_t swa_max,
-    float scale_log2, int32_t per_split, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int32_t n_split, float* __restrict__ out) {
+    const int32_t* __restrict__ idx, int32_t k_idx, const uint8_t* swa, int64_t swa_q_stride_rows,
+    const int32_t* __restrict__ swa_len, int32_t swa_max, const uint8_t* __restrict__ new_win,
+    const int32_t* __restrict__ win_lens, float scale_log2, int32_t per_split, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, int32_t n_split, float* __restrict__ out) {
   using Cfg = AttnCfg<W>;
   __shared__ __attribute__((aligned(16))) AttnSmem<W> sm;
   constexpr int kSlices = Cfg::kSlices;
@@ -389,6 +401,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   a.swa = swa;
   a.swa_q_stride_rows = swa_q_stride_rows;
   a.n_swa = min(swa_len[qb], swa_max);
+  constexpr int kWinRowBytes = kWin == kWinE4m3 ? CSA2_LATENT : 2 * CSA2_LATENT;
+  a.new_win = new_win ? new_win + (int64_t)(qb / q_per_seq) * kWinRowBytes : nullptr;
+  a.slot = new_win ? (win_lens[qb / q_per_seq] - 1) % max(swa_max, 1) : -1;
   a.swa_tiles = (swa_max + 15) / 16;
   a.n_tiles = (k_idx + 15) / 16 + a.swa_tiles;
   const int n_chunks = (a.n_tiles + W - 1) / W;
@@ -536,25 +551,29 @@ size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
 template <int kWin>
 static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, const csa2_fp4_kv& kv,
                           int32_t q_per_seq, const int32_t* idx, int32_t k_idx, const uint8_t* swa,
-                          int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
-                          float* part_o, float2* part_ml, float* out, hipStream_t stream) {
+                          int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                          const uint8_t* new_win, const int32_t* win_lens, float scale_log2, float* part_o,
+                          float2* part_ml, float* out, hipStream_t stream) {
   if (p.waves == 8)
     hipLaunchKernelGGL((attn_kernel<8, kWin>), dim3(p.splits, n_q), dim3(64 * 8), 0, stream, q, kv.codes,
                        kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
-                       scale_log2, p.per_split, part_o, part_ml, p.splits, out);
+                       new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out);
   else
     hipLaunchKernelGGL((attn_kernel<4, kWin>), dim3(p.splits, n_q), dim3(64 * 4), 0, stream, q, kv.codes,
                        kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
-                       scale_log2, p.per_split, part_o, part_ml, p.splits, out);
+                       new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out);
 }
 
 // win: the window rows' element type -- kWinBf16 (bf16 [*][512], converted
 // to f16 toward zero in the kernel), kWinE4m3 (E4M3 bytes [*][512]) or
 // kWinF16 (f16 [*][512], already converted as kWinBf16 would).
+// new_win / win_lens: the step's new window row per sequence ([*][512] in
+// the window's element type), or null, and the sequences' positions after
+// the step's append: the new row goes to window slot (lens - 1) % swa_max.
 csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
                         const int32_t* idx, int32_t k_idx, const void* swa, int win,
-                        int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float sm_scale,
-                        float* out, void* ws, hipStream_t stream) {
+                        int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, const void* new_win,
+                        const int32_t* win_lens, float sm_scale, float* out, void* ws, hipStream_t stream) {
   if (n_q == 0) return CSA2_OK;
   const AttnPlan p = attn_plan(n_q, k_idx, swa_max);
   float* part_o = nullptr;
@@ -567,15 +586,16 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
+  const uint8_t* nw = reinterpret_cast<const uint8_t*>(new_win);
   if (win == kWinE4m3)
     attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                            scale_log2, part_o, part_ml, out, stream);
+                            nw, win_lens, scale_log2, part_o, part_ml, out, stream);
   else if (win == kWinF16)
     attn_dispatch<kWinF16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                           scale_log2, part_o, part_ml, out, stream);
+                           nw, win_lens, scale_log2, part_o, part_ml, out, stream);
   else
     attn_dispatch<kWinBf16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                            scale_log2, part_o, part_ml, out, stream);
+                            nw, win_lens, scale_log2, part_o, part_ml, out, stream);
   if (p.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, p.splits, out);
   return launch_status("csa2_sparse_attn");

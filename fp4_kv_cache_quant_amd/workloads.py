@@ -57,6 +57,7 @@ class DecodeInputs:
     main_q: List[List[torch.Tensor]] = field(default_factory=list)            # [set][layer]
     new_row: List[Optional[torch.Tensor]] = field(default_factory=list)       # [set]
     new_idx_k: List[Optional[torch.Tensor]] = field(default_factory=list)     # [set], maintained keys
+    new_swa_row: List[Optional[List[torch.Tensor]]] = field(default_factory=list)  # [set][layer], window rows
     layer_idx_k: Optional[List[Optional[torch.Tensor]]] = None                 # [layer]: own indexer K
 
     @property
@@ -102,6 +103,17 @@ def build_decode_inputs(cfg: DecodeConfig, steps: int) -> DecodeInputs:
         inp.new_row.append(fill_tensor((n, 1, LATENT), cfg.new_row(s), seed=seed) if cfg.append else None)
         inp.new_idx_k.append(fill_tensor((n, 1, 64), cfg.new_idx_k(s), seed=seed)
                              if (cfg.maintain_keys and cfg.append) else None)
+        rows = None
+        if cfg.window_writes:
+            rows = [fill_tensor((n, 1, LATENT), cfg.new_swa_row(l, s), seed=seed) for l in range(nl)]
+            if cfg.swa_fp8:
+                rows8 = []
+                for t in rows:
+                    t8 = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
+                    quant_fp8_rows(t.view(n, LATENT), t8.view(n, LATENT))
+                    rows8.append(t8)
+                rows = rows8
+        inp.new_swa_row.append(rows)
     if cfg.layer_keys:
         inp.layer_idx_k = [fill_tensor((n, cap, 64), cfg.layer_idx_k(l), seed=seed) if cfg.own_keys(l) else None
                            for l in range(nl)]
@@ -125,7 +137,8 @@ def step_ios(sched: Sched, inp: DecodeInputs):
                           swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q[s], blk_k=inp.blk_k,
                           new_row=inp.new_row[s], append_kv=inp.cfg.append_kv,
                           new_idx_k=inp.new_idx_k[s] if inp.new_idx_k else None,
-                          layer_idx_k=inp.layer_idx_k)
+                          layer_idx_k=inp.layer_idx_k,
+                          new_swa_row=inp.new_swa_row[s] if inp.new_swa_row else None)
             for s in range(inp.cfg.q_sets)]
 
 

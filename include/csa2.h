@@ -73,7 +73,8 @@ typedef int32_t csa2_status;
 const char* csa2_last_error(void);
 /* Version of this ABI (bumped on any signature or struct change; 2 added
  * the FP8 window, 3 the key maintenance on append, 4 the per-layer indexer
- * K of flat Full layers and csa2_flat_select). */
+ * K of flat Full layers and csa2_flat_select, 5 the stream argument of
+ * csa2_sched_check and the per-step window rows of csa2_step_io). */
 int32_t csa2_abi_version(void);
 
 /* ------------------------------------------------------------ FP4 cache
@@ -300,6 +301,15 @@ typedef struct {
                                    the same keys.  A NULL array or entry means idx_k; entries of
                                    other layers must be NULL (else CSA2_EINVAL), and hierarchical
                                    Full layers always use idx_k with blk_k. */
+  const void* const* new_swa_row; /* host [n_layers] or NULL: entry l = [n_seq][512] window row of
+                                   the step's token for layer l (bf16, or E4M3 bytes when
+                                   desc.swa_fp8), 16-byte aligned.  READING: each window is a ring
+                                   of swa_max rows, position p in slot p % swa_max, and the step's
+                                   token is position lens[b] - 1 (after the step's append).  Layer
+                                   l's attention reads this row in place of that slot and stores it
+                                   there, so that it joins the window as the layer runs; a slot at
+                                   or past swa_len[b] is neither read nor written.  NULL: the
+                                   windows are read as they are. */
 } csa2_step_io;
 
 typedef struct csa2_sched csa2_sched;
@@ -320,10 +330,13 @@ const int32_t* csa2_sched_indices(const csa2_sched* s, int32_t layer);
 /* Device pointer to the pool [n_seq][pool_blocks] int32 built by the last
  * hierarchical Full layer, or NULL if the table has none. */
 const int32_t* csa2_sched_pool(const csa2_sched* s);
-/* Blocking: read and clear the device error flags (bit 0: a latent append
- * found a full cache; bit 1: a key append did).  Returns CSA2_OK and stores
- * the flags in *flags. */
-csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags);
+/* Blocking: on `stream` (the stream the steps ran on), read and clear the
+ * device error flags (bit 0: a latent append found a full cache; bit 1: a
+ * key append did), then wait for the stream.  The flags reflect every step
+ * enqueued on that stream before the call; steps still running on other
+ * streams are not waited for.  Returns CSA2_OK and stores the flags in
+ * *flags.  Not capturable (it synchronises). */
+csa2_status csa2_sched_check(csa2_sched* s, int32_t* flags, void* stream);
 void csa2_sched_destroy(csa2_sched* s);
 
 /* ------------------------------------------------------------ prefill

@@ -67,12 +67,23 @@ def seq_state(cfg: DecodeConfig, b: int, step: int) -> SeqState:
     return SeqState(L=L, tok_keys=tok, blk_keys=blk, kv_rows=kv_rows, layer_keys=own or None)
 
 
+def window_rows(cfg: DecodeConfig, l: int, b: int, step: int) -> np.ndarray:
+    """Layer l's window of sequence b as decode step `step` attends over it:
+    the initial rows, with every step s <= step having written its token's
+    row into that token's ring slot (when the workload writes windows)."""
+    sw = _gen(cfg, cfg.swa_rows(l), b, np.arange(cfg.swa), 512)
+    if cfg.window_writes:
+        for s in range(step + 1):
+            sw[cfg.swa_slot(s)] = _gen(cfg, cfg.new_swa_row(l, s), b, [0], 512)[0]
+    return sw
+
+
 def layer_inputs(cfg: DecodeConfig, b: int, step: int):
     ins = []
     for l, (mode, _, _) in enumerate(cfg.layers):
         iq = None if mode == REUSE else _gen(cfg, cfg.idx_q(l, step), b, np.arange(8), 64)
         mq = _gen(cfg, cfg.main_q(l, step), b, np.arange(16), 512)
-        sw = _gen(cfg, cfg.swa_rows(l), b, np.arange(cfg.swa), 512)
+        sw = window_rows(cfg, l, b, step)
         sw8 = fp8_rows(sw) if cfg.swa_fp8 else None
         ins.append(LayerInputs(idx_q=iq, main_q=mq, swa=sw, swa_len=cfg.swa, swa8=sw8))
     return ins

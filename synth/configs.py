@@ -33,6 +33,7 @@ class DecodeConfig:
     swa_fp8: bool = False                     # window rows stored as E4M3 (FP8) codes
     maintain_keys: bool = False               # block keys = sums of indexer keys, kept current on append
     layer_keys: bool = False                  # every flat Full layer after layer 0 has its own indexer K
+    window_writes: bool = True                # every step writes its token's window row in every layer
 
     def cap(self, steps: int) -> int:
         """Rows per sequence of every main-KV tensor and of indexer K."""
@@ -84,6 +85,15 @@ class DecodeConfig:
 
     def swa_rows(self, layer: int):
         return tensor_id(KIND_SWA, layer, 0), NORMAL
+
+    def new_swa_row(self, layer: int, step: int):
+        """The window row of step `step`'s token in layer `layer`."""
+        return tensor_id(KIND_SWA, layer, 1 + step % self.q_sets), NORMAL
+
+    def swa_slot(self, step: int) -> int:
+        """Window slot of step `step`'s token: windows are rings of `swa` rows,
+        position p in slot p % swa, and the token is the last position."""
+        return (self.lens_at(step) - 1) % self.swa
 
 
 def _group(mode0: int, kv: int, hier: int, n_reuse: int):

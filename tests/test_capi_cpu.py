@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(csa2):
 
 
 def test_abi_version(csa2):
-    assert csa2.abi_version() == 4
+    assert csa2.abi_version() == 5
 
 
 def _err(csa2):

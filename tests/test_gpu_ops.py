@@ -550,3 +550,51 @@ def test_sparse_attn_maximum_rows(csa2):
         codes, scales = oracle.quant_rows(src[b])
         ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa[b], swa_len[b], SM_SCALE)
         assert_attention_close(got[b], ref, f"query {b}")
+
+
+def _f16_toward_zero(x):
+    """bf16/f32 values as the attention kernel reads main Q and window rows:
+    converted to f16 rounding toward zero, saturating at +-65504 (the
+    documented contract of csa2_sparse_attn)."""
+    x = np.clip(np.asarray(x, np.float64), -65504.0, 65504.0)
+    y = x.astype(np.float16)                       # nearest even ...
+    away = np.abs(y.astype(np.float64)) > np.abs(x)
+    y[away] = np.nextafter(y[away], np.float16(0))  # ... stepped back toward zero
+    return y.astype(np.float64)
+
+
+def test_sparse_attn_f16_conversion_of_large_and_tiny_values(csa2):
+    """Main Q and window values outside f16's normal range are neither
+    rejected nor flagged: they are converted to f16 toward zero (saturating
+    at 65504, subnormal below 2^-14), as csa2.h documents.  The output must
+    match dense softmax attention over the converted values, and differ
+    clearly from attention over the unconverted ones."""
+    rng = np.random.default_rng(17)
+    n_rows = 64
+    x = rng.standard_normal((n_rows, 512)).astype(np.float32)
+    x[:, 5] *= 1e-4
+    x[10, 11], x[20, 12], x[30, 13], x[40, 14] = 1.0e5, -3.0e5, 1.0e-7, 3.0e-6
+    q = rng.standard_normal((16, 512)).astype(np.float32)
+    q[0, 5], q[1, 5] = 1.0e5, -7.0e4          # saturate
+    q[2] = rng.standard_normal(512) * 1e-6     # f16 subnormals
+    q[3, 11] = 3.0e-3                          # picks up window row 10's large value
+    qb, xb = _bf16_of(q), _bf16_of(x)
+    qv, xv = synth.bf16_to_f32(qb).astype(np.float64), synth.bf16_to_f32(xb).astype(np.float64)
+    kv = csa2.FP4KV.empty(1, 16)
+    print_case("sparse_attn f16 conversion of out-of-range values")
+    out = torch.empty(1, 16, 512, dtype=torch.float32, device="cuda")
+    idx = np.full((1, 16), -1, np.int32)       # window rows only
+    swa = xb[None]
+    csa2.sparse_attn(dev(qb[None]), kv, dev(idx), dev(swa), dev(np.array([n_rows], np.int32)), SM_SCALE, out)
+    got = out.cpu().numpy()[0]
+
+    def dense(qf, xf):
+        z = SM_SCALE * qf @ xf.T
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        return (p / p.sum(axis=1, keepdims=True)) @ xf
+
+    ref = dense(_f16_toward_zero(qv), _f16_toward_zero(xv))
+    assert_attention_close(got, ref, "converted")
+    raw = dense(qv, xv)
+    rel = np.linalg.norm(raw - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert rel[[0, 1, 3]].min() > 1e-2, rel[:4]  # the conversion is visible in the heads that meet it

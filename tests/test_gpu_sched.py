@@ -90,6 +90,16 @@ def test_reuse_layers_share_indices_and_append_overflow_flag(wl):
     sched.decode_step(io)  # cache is full now: the append reports and leaves lens alone
     assert sched.check() == 1 and inp.lens.cpu().tolist() == [501, 501]
     assert sched.check() == 0
+    # Steps on a side stream, checked on that stream without a device-wide
+    # synchronisation: the read waits for the steps enqueued before it.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            sched.decode_step(io)
+        assert sched.check(side) == 1
+        assert sched.check(side) == 0
+    torch.cuda.synchronize()
     sched.close()
 
 
@@ -212,3 +222,64 @@ def test_step_rejects_misaligned_tensors(wl):
     with pytest.raises(csa2.Csa2Error, match="16-byte aligned"):
         sched.decode_step(io)
     sched.close()
+
+
+def test_checkpoint_and_resume_reproduces_the_steps(wl):
+    """Everything a decode step carries across steps -- the FP4 caches,
+    lengths, indexer K, (maintained) block keys and the window rings --
+    copied to host memory after 3 steps, restored into new device buffers
+    under a new scheduler, and stepped on: steps 3..5 give bit-identical
+    indices, pool and outputs to an uninterrupted run."""
+    cfg = C.DECODER_20L_1M_KEYS.with_(n_seq=2, L0=8 * 900 + 3, q_sets=6)
+    steps, cut = 6, 3
+    nl = len(cfg.layers)
+
+    def snapshot(sched, inp):
+        return ([sched.indices(l).cpu().numpy() for l in range(nl)], sched.pool().cpu().numpy(),
+                [o.cpu().numpy() for o in inp.out])
+
+    print_case("checkpoint / resume, 20-layer table with maintained keys")
+    inp = wl.build_decode_inputs(cfg, steps)
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    ref = []
+    for s in range(steps):
+        sched.decode_step(ios[s])
+        if s >= cut:
+            ref.append(snapshot(sched, inp))
+    assert sched.check() == 0
+    sched.close()
+    del inp, ios, sched
+
+    inp = wl.build_decode_inputs(cfg, steps)
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    for s in range(cut):
+        sched.decode_step(ios[s])
+    torch.cuda.synchronize()
+    saved = {"kv": [(t.codes.cpu(), t.scales.cpu()) for t in inp.kv], "lens": inp.lens.cpu(),
+             "idx_k": inp.idx_k.cpu(), "blk_k": inp.blk_k.cpu(), "swa": [t.cpu() for t in inp.swa]}
+    sched.close()
+    del ios, sched
+    # restore into new buffers (the old ones are dropped) and a new scheduler
+    inp.kv = [csa2_fp4(c.cuda(), s_.cuda()) for c, s_ in saved["kv"]]
+    inp.lens, inp.idx_k, inp.blk_k = saved["lens"].cuda(), saved["idx_k"].cuda(), saved["blk_k"].cuda()
+    inp.swa = [t.cuda() for t in saved["swa"]]
+    torch.cuda.synchronize()
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    for i, s in enumerate(range(cut, steps)):
+        sched.decode_step(ios[s])
+        idx, pool, out = snapshot(sched, inp)
+        r_idx, r_pool, r_out = ref[i]
+        assert np.array_equal(pool, r_pool), s
+        for l in range(nl):
+            assert np.array_equal(idx[l], r_idx[l]), (s, l)
+            assert np.array_equal(out[l], r_out[l]), (s, l)
+    assert sched.check() == 0 and inp.lens.cpu().tolist() == [cfg.L0 + steps] * cfg.n_seq
+    sched.close()
+
+
+def csa2_fp4(codes, scales):
+    import fp4_kv_cache_quant_amd as csa2
+    return csa2.FP4KV(codes, scales)
