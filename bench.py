@@ -1,25 +1,31 @@
 """Benchmark of the CSA2 FP4-KV decode step on one MI355X.
 
-Workload: the 20-layer decoder schedule at 1M positions, batch 16 (group 1 =
-hierarchical Full + 3 Reuse, groups 2-5 = Reindex + 3 Reuse, five FP4 main-KV
-tensors, one FP4 append per sequence per step), seeded synthetic inputs
-resident in HBM.  A step is one pass of the whole path: append, indexer
-scoring, Top-512 with the 2,048 x 8 pool, gather + dequant, sparse + SWA
-attention for all 20 layers.
+Workload (the headline): the 20-layer decoder schedule at 1M positions,
+batch 16 (group 1 = hierarchical Full + 3 Reuse, groups 2-5 = Reindex + 3
+Reuse, five FP4 main-KV tensors, one FP4 append per sequence per step),
+seeded synthetic inputs resident in HBM.  A step is one pass of the whole
+path: append, indexer scoring, Top-512 with the 2,048 x 8 pool, gather +
+dequant, sparse + SWA attention for all 20 layers.  Every step has its own
+main Q, indexer Q, appended row and window rows (each layer writes its
+token's window row as it runs), so no step replays another's selections out
+of the caches.
 
 Prints one JSON line: (seq.layer)-steps/s, ms per step, the step's
-algorithmic HBM bytes as GB/s and fraction of the 8 TB/s peak, the
-roofline of the dominant op (timed with HIP events), the CPU oracle on a
-bounded sample of the same workload, a parity check of one step against
-that oracle sample, and (key "prefill") the ratio-2 causal prefill chunk of
-the encoder group: time per 4,096-query chunk, MFMA rate of its scoring and
-attention kernels, sampled parity and the oracle's rate; and (keys
-"fp8_window", "maintained_keys") the same decode step with the window rows
-stored as E4M3, and with the block keys maintained on append.
+algorithmic HBM bytes as GB/s and fraction of the 8 TB/s peak, the roofline
+of the dominant op (HIP events; the kernel-trace time beside it when the
+sources match a committed trace), the CPU oracle on a bounded sample of the
+same workload (all host cores, plus one core), parity of step 0 and of the
+last timed step against that sample and of every appended row; the other
+decode workloads (key "configs": one Full layer at 4K positions, the Full +
+3 Reuse group at 64K x 32, hierarchical Full + Reindex at 1M x 8) measured
+and checked the same way; and (keys "fp8_window", "maintained_keys",
+"encoder_decode", "prefill") the step with E4M3 window rows, with block keys
+maintained on append, the encoder's ratio-2 decode and the ratio-2 causal
+prefill chunk.
 
-usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-graph]
-                       [--cpu-seqs 16] [--no-cpu] [--no-prefill] [--prefill-reps 5]
-                       [--no-fp8-window] [--no-keys] [--config NAME]
+usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-graph] [--no-cpu]
+                       [--config NAME] [--no-configs] [--no-prefill] [--prefill-reps 5]
+                       [--no-fp8-window] [--no-keys] [--no-encoder] [--calibrate]
 """
 from __future__ import annotations
 
@@ -93,6 +99,32 @@ def measured_traffic(op_key: str):
         except OSError:
             return None
     return rec["bytes"]
+
+
+# Average kernel time per call of an op in a rocprofv3 kernel trace of the
+# same workload (the kernels of one call summed), with the SHA-256 of the
+# sources it was taken on: reported next to the HIP-event time while those
+# sources are unchanged.
+KERNEL_TRACE = {}
+
+
+def kernel_trace_us(op_key: str):
+    """Kernel-trace microseconds per call of op_key, or None (unmeasured, or
+    the sources changed since the trace was taken)."""
+    import hashlib
+
+    rec = KERNEL_TRACE.get(op_key)
+    if rec is None:
+        return None
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel, digest in rec["sources"].items():
+        try:
+            with open(os.path.join(root, rel), "rb") as fh:
+                if hashlib.sha256(fh.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
+    return rec["us"]
 
 
 def algorithmic_bytes(cfg, L: int) -> dict:
@@ -391,36 +423,47 @@ def prefill_bench(args) -> dict:
     }
 
 
+def _capture_steps(sched, ios, steps, graph: bool):
+    """One captured HIP graph per step (each step has its own inputs)."""
+    import torch
+
+    if not graph:
+        return None
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graphs = {}
+    with torch.cuda.stream(side):
+        for s_ in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                sched.decode_step(ios[s_])
+            graphs[s_] = g
+    stream.wait_stream(side)
+    return graphs
+
+
 def _time_steps(c, inp, K: int, W: int, graph: bool) -> dict:
     """Time K steps (after W warm-up steps) of workload c on the inputs inp,
     with a scheduler of its own; lengths are reset first so that the appends
-    rewrite the same rows."""
+    rewrite the same rows (step s uses query set s, so inp must hold
+    1 + W + K of them)."""
     import torch
 
     from fp4_kv_cache_quant_amd import workloads as wl
 
+    assert c.q_sets >= 1 + W + K
     inp.reset_lens()
     sched = wl.make_sched(inp)
     ios = wl.step_ios(sched, inp)
-    stream = torch.cuda.current_stream()
     sched.decode_step(ios[0])
-    graphs = []
-    if graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for s_ in range(c.q_sets):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    sched.decode_step(ios[s_])
-                graphs.append(g)
-        stream.wait_stream(side)
+    graphs = _capture_steps(sched, ios, range(1, 1 + W + K), graph)
 
     def run_step(s_):
         if graphs:
-            graphs[s_ % c.q_sets].replay()
+            graphs[s_].replay()
         else:
-            sched.decode_step(ios[s_ % c.q_sets])
+            sched.decode_step(ios[s_])
 
     for s_ in range(1, 1 + W):
         run_step(s_)
@@ -450,15 +493,20 @@ def fp8_window_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
     from fp4_kv_cache_quant_amd import workloads as wl
 
     c8 = cfg.with_(swa_fp8=True, name=cfg.name + ", FP8 window rows")
-    swa8 = []
-    for t in inp.swa:
+
+    def fp8(t):
         t8 = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
-        csa2.quant_fp8_rows(t, t8)
-        swa8.append(t8)
+        csa2.quant_fp8_rows(t.view(-1, 512), t8.view(-1, 512))
+        return t8
+
+    swa8 = [fp8(t) for t in inp.swa]
+    new8 = [[fp8(t) for t in rows] if rows is not None else None for rows in inp.new_swa_row]
     inp8 = wl.DecodeInputs(cfg=c8, steps=inp.steps, kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, blk_k=inp.blk_k,
                            swa=swa8, swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q, main_q=inp.main_q,
-                           new_row=inp.new_row)
-    return _time_steps(c8, inp8, K, W, graph)
+                           new_row=inp.new_row, new_swa_row=new8)
+    r = _time_steps(c8, inp8, K, W, graph)
+    del swa8, new8, inp8
+    return r
 
 
 def maintained_keys_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
@@ -475,7 +523,7 @@ def maintained_keys_leg(cfg, inp, K: int, W: int, graph: bool) -> dict:
     new_k = [wl.fill_tensor((ck.n_seq, 1, 64), ck.new_idx_k(s_), seed=ck.seed) for s_ in range(ck.q_sets)]
     inpk = wl.DecodeInputs(cfg=ck, steps=inp.steps, kv=inp.kv, lens=inp.lens, idx_k=inp.idx_k, blk_k=inp.blk_k,
                            swa=inp.swa, swa_len=inp.swa_len, out=inp.out, idx_q=inp.idx_q, main_q=inp.main_q,
-                           new_row=inp.new_row, new_idx_k=new_k)
+                           new_row=inp.new_row, new_idx_k=new_k, new_swa_row=inp.new_swa_row)
     return _time_steps(ck, inpk, K, W, graph)
 
 
@@ -489,7 +537,7 @@ def encoder_decode_leg(K: int, W: int, graph: bool, cpu_seqs: int) -> dict:
     from fp4_kv_cache_quant_amd import workloads as wl
     from synth.configs import DECODE_CONFIGS
 
-    cfg = DECODE_CONFIGS["encoder_1m"]
+    cfg = DECODE_CONFIGS["encoder_1m"].with_(q_sets=1 + W + K)
     nl = len(cfg.layers)
     inp = wl.build_decode_inputs(cfg, 1 + W + K)
     sched = wl.make_sched(inp)
@@ -506,7 +554,7 @@ def encoder_decode_leg(K: int, W: int, graph: bool, cpu_seqs: int) -> dict:
                      "traffic": dom["traffic_bytes"]}
     if cpu_seqs > 0:
         seqs = sorted({0, cfg.n_seq - 1} if cpu_seqs > 1 else {0})
-        threads = max(1, min(len(seqs), len(os.sched_getaffinity(0)), 16))
+        threads = max(1, len(os.sched_getaffinity(0)))
         res, dt = cpu_baseline(cfg, 0, seqs, threads)
         r["parity_step0"] = compare_step(cfg, gpu0, res)
         r["cpu_baseline"] = {"value": round(len(seqs) * nl / dt, 2), "unit": "(seq·layer)-steps/s",
@@ -539,16 +587,143 @@ def compare_step(cfg, gpu, ref) -> dict:
             "attn_max_rel_l2": worst_rel, "attn_max_abs": worst_abs, "seqs": len(ref)}
 
 
+def _snapshot(sched, inp, nl: int, hierarchical: bool) -> dict:
+    """Indices, pool and outputs of the step that ran last (host copies)."""
+    import torch
+
+    torch.cuda.synchronize()
+    return {"idx": [sched.indices(l).cpu().numpy() for l in range(nl)],
+            "pool": sched.pool().cpu().numpy() if hierarchical else None,
+            "out": [o.cpu().numpy().copy() for o in inp.out]}
+
+
+def appended_rows_exact(cfg, inp, n_steps: int) -> bool:
+    """Every row appended by the n_steps steps, every sequence: the device's
+    FP4 bytes equal the oracle's quantisation of the appended source rows."""
+    import numpy as np
+
+    import oracle
+    from oracle import workloads as ow
+
+    if not cfg.append:
+        return True
+    kv = inp.kv[cfg.append_kv]
+    pos = np.arange(cfg.L0, cfg.L0 + n_steps)
+    codes = kv.codes[:, cfg.L0:cfg.L0 + n_steps].cpu().numpy()
+    scales = kv.scales[:, cfg.L0:cfg.L0 + n_steps].cpu().numpy()
+    ok = True
+    for b in range(cfg.n_seq):
+        rc, rs = oracle.quant_rows(ow.kv_source_rows(cfg, cfg.append_kv, b, pos))
+        ok &= bool(np.array_equal(codes[b], rc) and np.array_equal(scales[b], rs))
+    return ok
+
+
+def roofline_of(ops, op_key_prefix: str) -> dict:
+    """The roofline entry of the op with the largest share of the step."""
+    dom = max(ops, key=lambda o: o["us_per_step"])
+    r = {"op": dom["key"], "bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+         "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4), "traffic": dom["traffic_bytes"],
+         "timing": "HIP events around graph replays of the op on its stream"}
+    kt = kernel_trace_us(f"{op_key_prefix}/{dom['key']}")
+    if kt is not None:
+        r["kernel_trace_us"] = kt
+        r["achieved_kernel_trace"] = round(dom["bytes_per_launch"] / (kt * 1e-6) / 1e9, 1)
+    return r, dom
+
+
+def decode_leg(cfg, K: int, W: int, graph: bool, parity_seqs, cpu: bool, single_core: bool = False,
+               keep_inputs: bool = False):
+    """One decode workload: step 0 eagerly, then W warm-up and K timed steps
+    replayed from one captured graph per step -- every step has its own main
+    Q, indexer Q, appended row and window rows, so no step repeats another's
+    selections -- timed with HIP events on the stream.  Step 0 and the last
+    timed step are checked against the oracle on parity_seqs (all appended
+    rows of all sequences bit-exact), and the oracle's time on that sample
+    is the CPU baseline (host threads = the cores this process may use)."""
+    import torch
+
+    from fp4_kv_cache_quant_amd import workloads as wl
+
+    total = 1 + W + K
+    c = cfg.with_(q_sets=total)
+    nl = len(c.layers)
+    t_build = time.perf_counter()
+    inp = wl.build_decode_inputs(c, total)
+    sched = wl.make_sched(inp)
+    ios = wl.step_ios(sched, inp)
+    build_s = time.perf_counter() - t_build
+    sched.decode_step(ios[0])
+    gpu0 = _snapshot(sched, inp, nl, c.hierarchical)
+    graphs = _capture_steps(sched, ios, range(1, total), graph)
+
+    def run_step(s_):
+        if graphs:
+            graphs[s_].replay()
+        else:
+            sched.decode_step(ios[s_])
+
+    for s_ in range(1, 1 + W):
+        run_step(s_)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for s_ in range(1 + W, total):
+        run_step(s_)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / K
+    gpu_last = _snapshot(sched, inp, nl, c.hierarchical)
+    flags = sched.check()
+    sched.close()
+    del graphs
+    ab = algorithmic_bytes(c, c.lens_at(1 + W + K // 2))
+    r = {"workload": c.name, "n_seq": c.n_seq, "positions": c.L0, "layers": nl,
+         "ms_per_step": round(ms, 4), "value": round(c.n_seq * nl / (ms * 1e-3), 1),
+         "unit": "(seq·layer)-steps/s", "algorithmic_bytes_per_step": ab["total"],
+         "GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
+         "frac_of_peak": round(ab["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "parts": ab,
+         "device_flags": int(flags), "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
+         "appended_rows_bit_exact": appended_rows_exact(c, inp, total)}
+    ops = (op_rooflines(c, inp, total, graph=graph) if c.hierarchical else flat_op_rooflines(c, inp, graph=graph))
+    r["roofline"], r["dominant_op"] = roofline_of(ops, config_key(cfg) or c.name)
+    r["ops"] = ops
+    if cpu:
+        threads = max(1, len(os.sched_getaffinity(0)))
+        seqs = list(parity_seqs)
+        res0, dt0 = cpu_baseline(c, 0, seqs, threads)
+        resl, dtl = cpu_baseline(c, total - 1, seqs, threads)
+        r["parity"] = {"step_0": compare_step(c, gpu0, res0), f"step_{total - 1}": compare_step(c, gpu_last, resl),
+                       "appended_rows_bit_exact": r["appended_rows_bit_exact"]}
+        r["parity"]["ok"] = bool(r["parity"]["step_0"]["ok"] and r["parity"][f"step_{total - 1}"]["ok"]
+                                 and r["appended_rows_bit_exact"])
+        r["cpu_baseline"] = {"value": round(2 * len(seqs) * nl / (dt0 + dtl), 2), "unit": "(seq·layer)-steps/s",
+                             "cores": threads, "kind": "oracle",
+                             "sample": f"decode steps 0 and {total - 1} of sequences {seqs[0]}..{seqs[-1]} "
+                                       f"({len(seqs)} of {c.n_seq}), all {nl} layers, {threads} threads: "
+                                       f"{dt0 + dtl:.1f} s"}
+        if single_core:
+            _, dt1 = cpu_baseline(c, 0, seqs[:1], 1)
+            r["cpu_baseline"]["single_core"] = {"value": round(nl / dt1, 2), "unit": "(seq·layer)-steps/s",
+                                                "sample": f"decode step 0 of sequence {seqs[0]}, all {nl} layers, "
+                                                          f"1 thread: {dt1:.1f} s"}
+    if keep_inputs:
+        return r, c, inp
+    del inp
+    torch.cuda.empty_cache()
+    return r, c, None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-graph", action="store_true", help="launch each step eagerly")
-    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the CPU oracle sample")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--cpu-reps", type=int, default=8, help="times the CPU oracle sample is timed")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (parity and baseline)")
     ap.add_argument("--config", default="decoder20_1m")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other decode workloads (C1, C2, C4)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--no-fp8-window", action="store_true", help="skip the FP8-window variant of the step")
     ap.add_argument("--no-keys", action="store_true", help="skip the maintained-block-keys variant of the step")
@@ -562,130 +737,70 @@ def main() -> int:
               "not built, so only --gpus 1 is supported", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    import fp4_kv_cache_quant_amd as csa2
-    from fp4_kv_cache_quant_amd import workloads as wl
     from synth.configs import DECODE_CONFIGS
 
     cfg = DECODE_CONFIGS[args.config]
     K, W = args.steps, args.warmup
-    total_steps = 1 + W + K          # step 0 (parity) + warmup + timed
+    graph = not args.no_graph
     torch.cuda.init()
-    t_build = time.perf_counter()
-    inp = wl.build_decode_inputs(cfg, total_steps)
-    sched = wl.make_sched(inp)
-    ios = wl.step_ios(sched, inp)
-    build_s = time.perf_counter() - t_build
-    nl = len(cfg.layers)
-    stream = torch.cuda.current_stream()
-
     if args.calibrate:
         calibration_copy()
+    progress = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    # Step 0, eager: kept for the parity check against the oracle sample.
-    sched.decode_step(ios[0])
-    torch.cuda.synchronize()
-    gpu0 = {"idx": [sched.indices(l).cpu().numpy() for l in range(nl)],
-            "pool": sched.pool().cpu().numpy() if cfg.hierarchical else None,
-            "out": [o.cpu().numpy() for o in inp.out]}
-
-    # One captured graph per query set; step s replays graph s % q_sets.
-    graphs = []
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for s in range(cfg.q_sets):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    sched.decode_step(ios[s])
-                graphs.append(g)
-        stream.wait_stream(side)
-
-    def run_step(s):
-        if graphs:
-            graphs[s % cfg.q_sets].replay()
-        else:
-            sched.decode_step(ios[s % cfg.q_sets])
-
-    for s in range(1, 1 + W):
-        run_step(s)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for s in range(1 + W, 1 + W + K):
-        run_step(s)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    if sched.check() != 0:
+    progress(f"headline {cfg.name}")
+    head, c, inp = decode_leg(cfg, K, W, graph, range(cfg.n_seq), cpu=not args.no_cpu, single_core=True,
+                              keep_inputs=True)
+    if head["device_flags"] != 0:
         print("an append found a full cache during the timed steps", file=sys.stderr)
         return 1
-    ms_per_step = gpu_ms / K
-    units_per_step = cfg.n_seq * nl
-    value = units_per_step / (ms_per_step * 1e-3)
-    L_mid = cfg.lens_at(1 + W + K // 2)
-    ab = algorithmic_bytes(cfg, L_mid)
-    hbm_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
-
-    # Per-op roofline: each op of the step on the step's buffers, timed with
-    # HIP events around graph replays on the stream the ops run on (no host
-    # launch gaps).  The op with the largest share of the step (time x calls
-    # per step) is the dominant one.
-    ops = (op_rooflines(cfg, inp, total_steps, graph=not args.no_graph) if cfg.hierarchical
-           else flat_op_rooflines(cfg, inp, graph=not args.no_graph))
-    dom = max(ops, key=lambda o: o["us_per_step"])
-    roofline = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
-                "traffic": measured_traffic(f"{config_key(cfg)}/{dom['key']}")}
-
-    # CPU oracle on a bounded sample: step 0 of the first cpu_seqs sequences.
-    cpu = parity = None
-    if not args.no_cpu:
-        threads = max(1, min(args.cpu_seqs, len(os.sched_getaffinity(0)), 16))
-        seqs = list(range(min(args.cpu_seqs, cfg.n_seq)))
-        res, dt = cpu_baseline(cfg, 0, seqs, threads, reps=args.cpu_reps)
-        cpu = {"value": round(args.cpu_reps * len(seqs) * nl / dt, 2), "unit": "(seq·layer)-steps/s",
-               "cores": threads, "kind": "oracle",
-               "sample": f"decode step 0 of {len(seqs)} of {cfg.n_seq} sequences, all {nl} layers "
-                         f"({sum(1 for m, _, _ in cfg.layers if m != 2)} selecting layers, {nl} attentions), "
-                         f"timed {args.cpu_reps} times: {dt:.1f} s"}
-        parity = compare_step(cfg, gpu0, res)
 
     fp8w = keys = None
-    if not args.no_fp8_window and not cfg.swa_fp8:
-        fp8w = fp8_window_leg(cfg, inp, K, W, graph=not args.no_graph)
-    if not args.no_keys and cfg.hierarchical and cfg.append and not cfg.maintain_keys:
-        keys = maintained_keys_leg(cfg, inp, K, W, graph=not args.no_graph)
+    if not args.no_fp8_window and not c.swa_fp8:
+        progress("FP8 window leg")
+        fp8w = fp8_window_leg(c, inp, K, W, graph)
+    if not args.no_keys and c.hierarchical and c.append and not c.maintain_keys:
+        progress("maintained keys leg")
+        keys = maintained_keys_leg(c, inp, K, W, graph)
+    del inp
+    torch.cuda.empty_cache()
+
+    configs = {}
+    if not args.no_configs and args.config == "decoder20_1m":
+        for key, seqs in (("single_4k", [0]), ("group_64k", [0, 31]), ("hier_1m", [0, 7])):
+            progress(f"config {key}")
+            r, _, _ = decode_leg(DECODE_CONFIGS[key], K, W, graph, seqs, cpu=not args.no_cpu)
+            configs[key] = r
 
     encoder = None
     if not args.no_encoder and args.config != "encoder_1m":
-        encoder = encoder_decode_leg(K, W, graph=not args.no_graph, cpu_seqs=0 if args.no_cpu else 2)
+        progress("encoder decode leg")
+        encoder = encoder_decode_leg(K, W, graph=graph, cpu_seqs=0 if args.no_cpu else 2)
 
     prefill = None
     if not args.no_prefill:
+        progress("prefill chunk")
         prefill = prefill_bench(args)
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "(seq·layer)-steps/s", "n_gpus": 1,
-        "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "metric": METRIC, "value": head["value"], "unit": "(seq·layer)-steps/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; FP4 E2M1 + E4M3/16 main KV, integer indexer Q/K, N(0,1) bf16 latents)",
-        "config": {"workload": cfg.name, "n_seq": cfg.n_seq, "positions": cfg.L0, "layers": nl,
-                   "fp4_kv_tensors": cfg.n_kv, "topk": cfg.topk, "pool": f"{cfg.pool_blocks}x{cfg.blk}",
-                   "swa": cfg.swa, "graph": bool(graphs)},
-        "hbm": {"algorithmic_bytes_per_step": ab["total"], "GBps": round(hbm_gbps, 1),
-                "frac_of_peak": round(hbm_gbps / PEAK_HBM_GBPS, 4), "parts": ab},
-        "roofline": roofline, "dominant_op": dom, "ops": ops, "cpu_baseline": cpu, "parity_step0": parity,
-        "fp8_window": fp8w, "maintained_keys": keys, "encoder_decode": encoder, "prefill": prefill,
-        "wall_s_timed": round(wall, 3), "build_s": round(build_s, 1),
+        "data": "synthetic (seeded; FP4 E2M1 + E4M3/16 main KV, integer indexer Q/K, N(0,1) bf16 latents; "
+                "every step its own main Q, indexer Q, appended row and window rows)",
+        "config": {"workload": c.name, "n_seq": c.n_seq, "positions": c.L0, "layers": len(c.layers),
+                   "fp4_kv_tensors": c.n_kv, "topk": c.topk, "pool": f"{c.pool_blocks}x{c.blk}",
+                   "swa": c.swa, "graph": graph},
+        "hbm": {"algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"], "GBps": head["GBps"],
+                "frac_of_peak": head["frac_of_peak"], "parts": head["parts"]},
+        "roofline": head["roofline"], "dominant_op": head["dominant_op"], "ops": head["ops"],
+        "cpu_baseline": head.get("cpu_baseline"), "parity": head.get("parity"),
+        "appended_rows_bit_exact": head["appended_rows_bit_exact"],
+        "configs": configs, "fp8_window": fp8w, "maintained_keys": keys, "encoder_decode": encoder,
+        "prefill": prefill, "wall_s_timed": head["wall_s_timed"], "build_s": head["build_s"],
     }
     print(json.dumps(line), flush=True)
-    sched.close()
     return 0
 
 
