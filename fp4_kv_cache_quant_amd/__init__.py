@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
-    "sparse_attn", "sparse_attn_workspace_size", "flat_select", "flat_select_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
+    "sparse_attn", "sparse_attn_workspace_size", "sparse_attn_noalloc", "flat_select", "flat_select_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
     "prefill_index_score", "Prefill", "quant_fp8_rows", "block_keys", "append_index_keys",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
@@ -89,6 +89,8 @@ _block_keys = _sig("csa2_block_keys", _I32, _P, _I64, _P, _I32, _P, _I64, _I32, 
 _append_keys = _sig("csa2_append_index_keys", _I32, _P, _P, _I64, _P, _I64, _I32, _P, _P, _I32, _P)
 _attn = _sig("csa2_sparse_attn", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
              _I32, _F32, _P, _P, _SZ, _P)
+_attn_noalloc = _sig("csa2_sparse_attn_noalloc", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64,
+                     _P, _I32, _F32, _P, _P)
 _sched_create = _sig("csa2_sched_create", _I32, ctypes.POINTER(_SchedDesc), ctypes.POINTER(_P))
 _sched_step = _sig("csa2_sched_decode_step", _I32, _P, ctypes.POINTER(_StepIO), _P)
 _sched_indices = _sig("csa2_sched_indices", _P, _P, _I32)
@@ -234,6 +236,22 @@ def flat_select(q: torch.Tensor, keys: torch.Tensor, lens: torch.Tensor, k: int,
 
 def sparse_attn_workspace_size(n_q: int, k_idx: int, swa_max: int) -> int:
     return int(_attn_ws(n_q, k_idx, swa_max))
+
+
+def sparse_attn_noalloc(q: torch.Tensor, kv: FP4KV, idx: torch.Tensor, swa: torch.Tensor, swa_len: torch.Tensor,
+                        sm_scale: float, out: torch.Tensor, q_per_seq: int = 1,
+                        swa_q_stride_rows: Optional[int] = None, swa_max: Optional[int] = None, stream=None) -> None:
+    """csa2_sparse_attn_noalloc: sparse_attn (bf16 window rows) with its split partials in the library's
+    static scratch instead of a workspace; allocates nothing."""
+    n_q = q.shape[0]
+    k_idx = idx.shape[1] if idx is not None and idx.dim() == 2 else 0
+    if swa_max is None:
+        swa_max = swa.shape[1] if swa.dim() == 3 else 0
+    if swa_q_stride_rows is None:
+        swa_q_stride_rows = swa_max
+    kvc = kv.c()
+    _check(_attn_noalloc(_ptr(q), n_q, ctypes.byref(kvc), q_per_seq, _ptr(idx), k_idx, _ptr(swa), swa_q_stride_rows,
+                         _ptr(swa_len), swa_max, sm_scale, _ptr(out), _stream(stream)))
 
 
 def sparse_attn(q: torch.Tensor, kv: FP4KV, idx: torch.Tensor, swa: torch.Tensor, swa_len: torch.Tensor,

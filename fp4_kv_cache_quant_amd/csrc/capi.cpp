@@ -24,6 +24,7 @@ int64_t index_score_local_groups(int64_t key_cap);
 csa2_status index_score_local_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*, int32_t,
                                      float*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
+csa2_status attn_scratch(void** ptr, size_t* bytes);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
                         float*, void*, hipStream_t);
@@ -253,6 +254,29 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                              float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
+  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, out, ws,
+                              ws_bytes);
+  if (st != CSA2_OK || n_q == 0) return st;
+  return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinBf16, swa_q_stride_rows, swa_len, swa_max,
+                     nullptr, nullptr, sm_scale, out, ws, as_stream(stream));
+}
+
+csa2_status csa2_sparse_attn_noalloc(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                                     const int32_t* idx, int32_t k_idx, const uint16_t* swa,
+                                     int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                                     float sm_scale, float* out, void* stream) {
+  clear_error();
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (n_q > 0) {
+    csa2_status st = attn_scratch(&ws, &ws_bytes);
+    if (st != CSA2_OK) return st;
+    const size_t need = attn_workspace_bytes(n_q, k_idx, swa_max);
+    CSA2_REQUIRE(need <= ws_bytes, CSA2_ECAPACITY,
+                 "csa2_sparse_attn_noalloc: this call needs " + std::to_string(need) +
+                     " bytes of split partials; the static scratch holds " + std::to_string(ws_bytes) +
+                     " (use csa2_sparse_attn with a workspace)");
+  }
   csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, out, ws,
                               ws_bytes);
   if (st != CSA2_OK || n_q == 0) return st;

@@ -43,6 +43,8 @@
 // Context, FP4 KV Cache, and Cross-Layer Attention Reuse"; [P3]
 // "DeepSeek-V4.1 Flash: Pushing the Limits of KV Cache Compression".
 #include <algorithm>
+#include <mutex>
+#include <string>
 
 #include "common.hpp"
 
@@ -599,6 +601,42 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
   if (p.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, p.splits, out);
   return launch_status("csa2_sparse_attn");
+}
+
+// ------------------------------------------------- static scratch
+// For callers that cannot allocate: the split partials of
+// csa2_sparse_attn_noalloc live in this file-scope array (one copy per GPU
+// the library runs on, held until the process ends).  Host code never
+// passes the array's name to a kernel -- on the host it is only a stand-in
+// for the symbol -- but the device address that hipGetSymbolAddress returns
+// for the current device, looked up once per device and kept.
+constexpr size_t kAttnScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+}  // namespace
+
+csa2_status attn_scratch(void** ptr, size_t* bytes) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    set_error("csa2_sparse_attn_noalloc: no current device (or device index >= 64)");
+    return CSA2_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error(std::string("csa2_sparse_attn_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+      return CSA2_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kAttnScratchBytes;
+  return CSA2_OK;
 }
 
 // Window rows bf16 -> f16 toward zero (the conversion the attention kernel

@@ -204,6 +204,21 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                              float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* csa2_sparse_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and arguments without a workspace.  The
+ * split partials live in a static scratch array of 16 MiB per GPU (held
+ * until the process ends); a call whose csa2_sparse_attn_workspace_size
+ * exceeds it fails with CSA2_ECAPACITY before anything is enqueued (batch
+ * 16 at 512 selected + 128 window rows needs about 2.6 MB).  Allocates
+ * nothing.  Every call on one GPU uses that GPU's one scratch array, so
+ * calls that overlap in time on one GPU (concurrent streams, threads)
+ * race; calls in order on one stream do not. */
+csa2_status csa2_sparse_attn_noalloc(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                                     const int32_t* idx, int32_t k_idx, const uint16_t* swa,
+                                     int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                                     float sm_scale, float* out, void* stream);
+
 /* FP8 window rows ([P4] summary: the sliding-window KV is kept in FP8).
  * READING: OCP E4M3FN elements, one byte per channel, no scale; a bf16 value
  * becomes its round-to-nearest-even E4M3 code (ties to the even code),
