@@ -229,8 +229,9 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
     itself, so its figure here includes that pass).
 
     Bytes per call (n = sequences): block scan n*ceil(L/8)*(128+4) (block
-    keys read, scores written); pool score n*16384*(128+4) (indexer keys of
-    the pool positions, scores); Top-k n*slots*4 (scores read once);
+    keys read, scores written); block Top-k n*slots*4 (scores read once);
+    pool select n*16384*(128+4) (indexer keys of the pool positions, scores
+    written and read back once: counted once);
     attention n*(512*4 + 512*288 + 128*1024 + 16*1024 + 16*512*4) (indices,
     selected FP4 rows, SWA window, main Q, f32 output)."""
     import torch
@@ -245,26 +246,23 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
     pool_slots = cfg.pool_blocks * cfg.blk
     q0 = inp.idx_q[0][0]
     bscores = torch.empty(n, blk_cap, dtype=torch.float32, device="cuda")
-    pscores = torch.empty(n, pool_slots, dtype=torch.float32, device="cuda")
     pool = torch.empty(n, cfg.pool_blocks, dtype=torch.int32, device="cuda")
     idx = torch.empty(n, cfg.topk, dtype=torch.int32, device="cuda")
     out = torch.empty(n, 16, 512, dtype=torch.float32, device="cuda")
     tws = torch.zeros(csa2.topk_workspace_size(blk_cap, n), dtype=torch.uint8, device="cuda")
+    pws = torch.zeros(csa2.pool_select_workspace_size(cfg.pool_blocks, cfg.blk, n), dtype=torch.uint8, device="cuda")
     aws = torch.empty(csa2.sparse_attn_workspace_size(n, cfg.topk, cfg.swa), dtype=torch.uint8, device="cuda")
     csa2.index_score(q0, inp.blk_k, inp.lens, bscores, len_div=cfg.blk)
     csa2.topk(bscores, cfg.pool_blocks, pool, lens=inp.lens, len_div=cfg.blk, ws=tws)
-    csa2.index_score(q0, inp.idx_k, inp.lens, pscores, pool=pool, blk=cfg.blk)
-    csa2.topk(pscores, cfg.topk, idx, pool=pool, blk=cfg.blk, ws=tws)
+    csa2.pool_select(q0, inp.idx_k, inp.lens, pool, cfg.topk, idx, blk=cfg.blk, ws=pws)
     sel_layers = sum(1 for m, _, _ in cfg.layers if m != 2)
     ops = [
         ("block_scan", "block scan (index_score, block keys)", 1, n * nblk * 132,
          lambda: csa2.index_score(q0, inp.blk_k, inp.lens, bscores, len_div=cfg.blk)),
         ("block_topk", "block Top-2048 (topk)", 1, n * nblk * 4,
          lambda: csa2.topk(bscores, cfg.pool_blocks, pool, lens=inp.lens, len_div=cfg.blk, ws=tws)),
-        ("pool_score", "pool score (index_score, pool)", sel_layers, n * pool_slots * 132,
-         lambda: csa2.index_score(q0, inp.idx_k, inp.lens, pscores, pool=pool, blk=cfg.blk)),
-        ("pool_topk", "pool Top-512 (topk)", sel_layers, n * pool_slots * 4,
-          lambda: csa2.topk(pscores, cfg.topk, idx, pool=pool, blk=cfg.blk, ws=tws)),
+        ("pool_select", "pool score + Top-512 (pool_select)", sel_layers, n * pool_slots * (128 + 4),
+         lambda: csa2.pool_select(q0, inp.idx_k, inp.lens, pool, cfg.topk, idx, blk=cfg.blk, ws=pws)),
         ("sparse_attn", "sparse+SWA attention (sparse_attn: chunk + combine kernels)", len(cfg.layers),
          n * (cfg.topk * 4 + cfg.topk * 288 + cfg.swa * (512 if cfg.swa_fp8 else 1024) + 16 * 1024 + 16 * 512 * 4),
          lambda: csa2.sparse_attn(inp.main_q[0][0], inp.kv[0], idx, inp.swa[0], inp.swa_len, 512 ** -0.5, out,

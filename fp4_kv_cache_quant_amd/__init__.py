@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
-    "sparse_attn", "sparse_attn_workspace_size", "sparse_attn_noalloc", "flat_select", "flat_select_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
+    "sparse_attn", "sparse_attn_workspace_size", "sparse_attn_noalloc", "pool_select", "pool_select_workspace_size", "flat_select", "flat_select_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
     "prefill_index_score", "Prefill", "quant_fp8_rows", "block_keys", "append_index_keys",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
@@ -81,6 +81,8 @@ _topk_ws = _sig("csa2_topk_workspace_size", _SZ, _I64, _I32)
 _topk = _sig("csa2_topk", _I32, _P, _I64, _P, _I32, _I32, _P, _I32, _I32, _P, _P, _SZ, _I32, _P)
 _flat_ws = _sig("csa2_flat_select_workspace_size", _SZ, _I64, _I32, _I32)
 _flat_select = _sig("csa2_flat_select", _I32, _P, _P, _P, _I64, _P, _I32, _P, _P, _SZ, _I32, _P)
+_pool_ws = _sig("csa2_pool_select_workspace_size", _SZ, _I32, _I32, _I32)
+_pool_select = _sig("csa2_pool_select", _I32, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _I32, _P)
 _attn_ws = _sig("csa2_sparse_attn_workspace_size", _SZ, _I32, _I32, _I32)
 _attn_f8w = _sig("csa2_sparse_attn_f8w", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
                  _I32, _F32, _P, _P, _SZ, _P)
@@ -232,6 +234,25 @@ def flat_select(q: torch.Tensor, keys: torch.Tensor, lens: torch.Tensor, k: int,
                          device=keys.device)
     _check(_flat_select(_ptr(q), _ptr(w), _ptr(keys), key_cap, _ptr(lens), k, _ptr(out), _ptr(ws), ws.numel(),
                         n_seq, _stream(stream)))
+
+
+def pool_select_workspace_size(n_pool: int, blk: int, n_seq: int) -> int:
+    return int(_pool_ws(n_pool, blk, n_seq))
+
+
+def pool_select(q: torch.Tensor, keys: torch.Tensor, lens: torch.Tensor, pool: torch.Tensor, k: int,
+                out: torch.Tensor, blk: int = 8, w: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """q [n_seq][8][64], keys [n_seq][key_cap][64] bf16, pool [n_seq][n_pool] int32 -> out [n_seq][k] int32:
+    the Top-k positions of the pool's blocks by indexer score (csa2_pool_select).  ws: a zero-filled
+    workspace reused across calls (a fresh one if None)."""
+    n_seq, key_cap = keys.shape[0], keys.shape[1]
+    n_pool = pool.shape[1]
+    if ws is None:
+        ws = torch.zeros(max(pool_select_workspace_size(n_pool, blk, n_seq), 1), dtype=torch.uint8,
+                         device=keys.device)
+    _check(_pool_select(_ptr(q), _ptr(w), _ptr(keys), key_cap, _ptr(lens), _ptr(pool), n_pool, blk, k, _ptr(out),
+                        _ptr(ws), ws.numel(), n_seq, _stream(stream)))
 
 
 def sparse_attn_workspace_size(n_q: int, k_idx: int, swa_max: int) -> int:

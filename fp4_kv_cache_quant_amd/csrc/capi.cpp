@@ -19,7 +19,7 @@ csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, i
                                int32_t*, int32_t, hipStream_t);
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
-                               uint32_t*, hipStream_t);
+                               uint32_t*, hipStream_t, uint32_t* bound_inv = nullptr, int32_t bound_k = 0);
 int64_t index_score_local_groups(int64_t key_cap);
 csa2_status index_score_local_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*, int32_t,
                                      float*, int32_t*, int32_t, hipStream_t);
@@ -111,6 +111,40 @@ csa2_status flat_select_launch(const uint16_t* q, const float* w, const uint16_t
                                       fused ? f.tw.hist : nullptr, stream);
   if (st != CSA2_OK) return st;
   return topk_launch(f.scores, key_cap, lens, 1, k, nullptr, 0, 1, out, f.tw, fused, n_seq, stream);
+}
+
+// ------------------------------------------------------------ pool select
+// Workspace of a pool selection: scores [n_seq][n_pool * blk] | Top-k
+// workspace, 256-byte aligned parts.
+PoolSelectWs pool_select_ws(int32_t n_pool, int32_t blk, int32_t n_seq, void* base) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  PoolSelectWs f{};
+  f.n = (int64_t)n_pool * blk;
+  char* p = reinterpret_cast<char*>(base);
+  f.scores = reinterpret_cast<float*>(p);
+  const size_t off = up((size_t)n_seq * f.n * sizeof(float));
+  f.tw = base ? topk_ws_carve(p + off, f.n, n_seq) : TopkWs{};
+  f.bytes = off + topk_workspace_bytes(f.n, n_seq);
+  return f;
+}
+
+csa2_status pool_select_path(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, const int32_t* pool, int32_t n_pool, int32_t blk, int32_t k,
+                             int32_t* out, float* scores, const TopkWs& tw, int32_t n_seq, hipStream_t stream) {
+  const int64_t n = (int64_t)n_pool * blk;
+  if (n <= kPoolSelectMax) {
+    // Scoring leaves a lower bound of each sequence's k-th key; the
+    // selection takes the keys above it into LDS.
+    csa2_status st = index_score_launch(q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n, n_seq, nullptr,
+                                        stream, tw.bound, k);
+    if (st != CSA2_OK) return st;
+    return pool_select_launch(scores, n, k, pool, n_pool, blk, tw, out, n_seq, stream);
+  }
+  const bool fused = n > kTopkRowsMax;
+  csa2_status st = index_score_launch(q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n, n_seq,
+                                      fused ? tw.hist : nullptr, stream);
+  if (st != CSA2_OK) return st;
+  return topk_launch(scores, n, nullptr, 1, k, pool, n_pool, blk, out, tw, fused, n_seq, stream);
 }
 
 csa2_status check_topk(const float* scores, int64_t n, int32_t len_div, int32_t k, const int32_t* pool,
@@ -227,6 +261,33 @@ csa2_status csa2_flat_select(const uint16_t* q, const float* w, const uint16_t* 
   const FlatSelectWs f = flat_select_ws(key_cap, k, n_seq, ws);
   CSA2_REQUIRE(ws_bytes >= f.bytes, CSA2_ECAPACITY, "csa2_flat_select: workspace too small");
   return flat_select_launch(q, w, keys, key_cap, lens, k, out, f, n_seq, as_stream(stream));
+}
+
+size_t csa2_pool_select_workspace_size(int32_t n_pool, int32_t blk, int32_t n_seq) {
+  if (n_pool < 1 || n_pool > CSA2_TOPK_MAX || blk < 1 || (int64_t)n_pool * blk > CSA2_TOPK_NMAX || n_seq <= 0 ||
+      n_seq > 65535)
+    return 0;
+  return pool_select_ws(n_pool, blk, n_seq, nullptr).bytes;
+}
+
+csa2_status csa2_pool_select(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, const int32_t* pool, int32_t n_pool, int32_t blk, int32_t k,
+                             int32_t* out, void* ws, size_t ws_bytes, int32_t n_seq, void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_seq >= 0 && n_seq <= 65535, CSA2_ESHAPE, "csa2_pool_select: n_seq must be in [0, 65535]");
+  if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(q && keys && lens && pool && out && ws, CSA2_EINVAL, "csa2_pool_select: null pointer");
+  CSA2_REQUIRE(key_cap >= 1, CSA2_ESHAPE, "csa2_pool_select: key_cap must be >= 1");
+  CSA2_REQUIRE(n_pool >= 1 && n_pool <= CSA2_TOPK_MAX && blk >= 1 && (int64_t)n_pool * blk <= CSA2_TOPK_NMAX,
+               CSA2_ESHAPE, "csa2_pool_select: need 1 <= n_pool <= 2048 and n_pool * blk <= 1048576");
+  CSA2_REQUIRE(k >= 1 && k <= CSA2_TOPK_MAX, CSA2_ESHAPE, "csa2_pool_select: k must be in [1, 2048]");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(q) & 15) == 0 && (reinterpret_cast<uintptr_t>(keys) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(ws) & 255) == 0,
+               CSA2_EINVAL, "csa2_pool_select: q and keys need 16-byte, ws 256-byte alignment");
+  const PoolSelectWs f = pool_select_ws(n_pool, blk, n_seq, ws);
+  CSA2_REQUIRE(ws_bytes >= f.bytes, CSA2_ECAPACITY, "csa2_pool_select: workspace too small");
+  return pool_select_path(q, w, keys, key_cap, lens, pool, n_pool, blk, k, out, f.scores, f.tw, n_seq,
+                          as_stream(stream));
 }
 
 size_t csa2_topk_workspace_size(int64_t n, int32_t n_seq) {

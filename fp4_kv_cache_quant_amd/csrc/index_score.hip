@@ -42,14 +42,51 @@ __device__ __forceinline__ float relu_wsum4(const f32x4& acc, const float* wh) {
   return part;
 }
 
+// The j-th largest (with multiplicity) of the 64 x 8 order keys k[] of a
+// wavefront (0 if fewer than j are nonzero): j - 1 times the largest is
+// removed (one copy, from the lowest lane holding it), then the largest
+// left is taken.
+__device__ __forceinline__ uint32_t wave_jth_largest(uint32_t (&k)[8], int j) {
+  const int lane = threadIdx.x & 63;
+  for (int p = 1; p < j; ++p) {
+    uint32_t lm = k[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) lm = max(lm, k[t]);
+    const uint32_t wm = wave_max_u32(lm);
+    if (wm == 0) return 0;
+    const uint64_t who = __ballot(lm == wm);
+    if (lane == __ffsll((unsigned long long)who) - 1) {
+      bool done = false;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (!done && k[t] == wm) {
+          k[t] = 0;
+          done = true;
+        }
+    }
+  }
+  uint32_t lm = k[0];
+#pragma unroll
+  for (int t = 1; t < 8; ++t) lm = max(lm, k[t]);
+  return wave_max_u32(lm);
+}
+
 // kHist: also add the scores' top key digits into a per-sequence histogram
 // (ghist [n_seq][4096]) for the Top-k that follows.
+// tile_bound (pool mode, may be null): for the selection that follows, the
+// j-th largest order key of every tile of 128 slots, j = ceil(k / tiles),
+// in tile_bound[b][tile] (0 when the tile has fewer than j keys or j >
+// kBoundJMax).  The least of a sequence's tile values, B, is a lower bound
+// of its k-th largest key: every tile has j keys >= B, so at least k keys
+// are >= B.
+constexpr int kBoundJMax = 16;
+
 template <bool kPool, bool kWeights, bool kHist>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ keys,
     int64_t key_cap, const int32_t* __restrict__ lens, int32_t len_div,
     const int32_t* __restrict__ pool, int32_t n_pool, int32_t blk, float* __restrict__ scores,
-    int64_t n_out, uint32_t* __restrict__ ghist) {
+    int64_t n_out, uint32_t* __restrict__ ghist, uint32_t* __restrict__ tile_bound, int32_t bound_j) {
   __shared__ uint32_t hist[kHist ? kTopkBins : 1];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -82,6 +119,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 
   const uint16_t* kb = keys + (int64_t)b * key_cap * 64;
   float* sb = scores + (int64_t)b * n_out;
+  const bool bound = kPool && tile_bound != nullptr;
+  const int64_t n_tiles = (n_out + 127) / 128;
   // Grid-stride over chunks of kKeysPerWG keys (one histogram flush per workgroup).
   for (int64_t chunk = blockIdx.x; chunk * kKeysPerWG < n_out; chunk += gridDim.x) {
     const int64_t base = chunk * kKeysPerWG + (int64_t)wave * (kTilesPerWave * 16);
@@ -114,6 +153,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       kv[t][0] = __builtin_nontemporal_load(kp);
       kv[t][1] = __builtin_nontemporal_load(kp + 1);
     }
+    uint32_t okeys[kTilesPerWave];
 #pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t) {
       if (!valid[t]) kv[t][0] = kv[t][1] = u32x4{0, 0, 0, 0};
@@ -124,11 +164,18 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       const float part = relu_wsum4(acc, wh);
       const float score = fold16_add(part);  // heads 0..3 + heads 4..7
       const int64_t slot = base + t * 16 + n;
+      okeys[t] = 0u;
       if (g == 0 && slot < n_out) {
         sb[slot] = valid[t] ? score : kNegInf;
         const uint32_t key = order_key(score);
         if (kHist && valid[t] && key) atomicAdd(&hist[key >> 20], 1u);
+        okeys[t] = valid[t] ? key : 0u;
       }
+    }
+    if (bound) {
+      const uint32_t tb = bound_j <= kBoundJMax ? wave_jth_largest(okeys, bound_j) : 0u;
+      const int64_t tile = base / 128;  // this wavefront's 128 slots
+      if ((threadIdx.x & 63) == 0 && tile < n_tiles) tile_bound[(int64_t)b * n_tiles + tile] = tb;
     }
   }
   if (kHist) {
@@ -142,13 +189,14 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 template <bool kPool, bool kWeights>
 void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const float* w, const uint16_t* keys,
                 int64_t key_cap, const int32_t* lens, int32_t len_div, const int32_t* pool,
-                int32_t n_pool, int32_t blk, float* scores, int64_t n_out, uint32_t* ghist) {
+                int32_t n_pool, int32_t blk, float* scores, int64_t n_out, uint32_t* ghist, uint32_t* bound_inv,
+                int32_t bound_j) {
   if (ghist)
     hipLaunchKernelGGL((index_score_kernel<kPool, kWeights, true>), grid, dim3(256), 0, stream, q, w, keys,
-                       key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, ghist);
+                       key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, ghist, bound_inv, bound_j);
   else
     hipLaunchKernelGGL((index_score_kernel<kPool, kWeights, false>), grid, dim3(256), 0, stream, q, w, keys,
-                       key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, ghist);
+                       key_cap, lens, len_div, pool, n_pool, blk, scores, n_out, ghist, bound_inv, bound_j);
 }
 
 // ------------------------------------------------------------------ prefill
@@ -433,10 +481,12 @@ __global__ __launch_bounds__(256) void index_score_local_kernel(
 
 }  // namespace
 
+// tile_bound / bound_k (pool mode): also the tile bounds of the bound_k-th
+// largest key described at index_score_kernel.
 csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
                                const int32_t* lens, int32_t len_div, const int32_t* pool,
                                int32_t n_pool, int32_t blk, float* scores, int64_t n_out, int32_t n_seq,
-                               uint32_t* ghist, hipStream_t stream) {
+                               uint32_t* ghist, hipStream_t stream, uint32_t* tile_bound, int32_t bound_k) {
   if (n_seq == 0 || n_out == 0) return CSA2_OK;
   // About four workgroups per CU in total; each loops over chunks of 512
   // keys, so a fused histogram is flushed by few workgroups (its hot bins
@@ -445,12 +495,22 @@ csa2_status index_score_launch(const uint16_t* q, const float* w, const uint16_t
   const int64_t per_seq = std::max<int64_t>(1, std::min<int64_t>(chunks, (1024 + n_seq - 1) / n_seq));
   CSA2_REQUIRE(n_seq <= 65535, CSA2_ESHAPE, "csa2_index_score: grid too large");
   const dim3 grid((uint32_t)per_seq, (uint32_t)n_seq);
+  const int64_t tiles = (n_out + 127) / 128;  // 128-slot tiles, one per wavefront pass
+  const int32_t bound_j = tile_bound ? (int32_t)std::min<int64_t>((bound_k + tiles - 1) / tiles, kBoundJMax + 1) : 0;
   if (pool) {
-    if (w) launch_one<true, true>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out, ghist);
-    else launch_one<true, false>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out, ghist);
+    if (w)
+      launch_one<true, true>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out, ghist,
+                             tile_bound, bound_j);
+    else
+      launch_one<true, false>(grid, stream, q, w, keys, key_cap, lens, 1, pool, n_pool, blk, scores, n_out, ghist,
+                              tile_bound, bound_j);
   } else {
-    if (w) launch_one<false, true>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out, ghist);
-    else launch_one<false, false>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out, ghist);
+    if (w)
+      launch_one<false, true>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out, ghist,
+                              nullptr, 0);
+    else
+      launch_one<false, false>(grid, stream, q, w, keys, key_cap, lens, len_div, pool, 0, 1, scores, n_out, ghist,
+                               nullptr, 0);
   }
   return launch_status("csa2_index_score");
 }

@@ -20,7 +20,7 @@ namespace csa2 {
 csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, int32_t*, hipStream_t);
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
-                               uint32_t*, hipStream_t);
+                               uint32_t*, hipStream_t, uint32_t* bound_inv = nullptr, int32_t bound_k = 0);
 int64_t index_score_local_groups(int64_t key_cap);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
@@ -282,13 +282,8 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       // registers (no histogram from the score kernel); longer inputs get the
       // histogram fused into the scoring pass.
       if (use_pool) {
-        const int64_t n_out = (int64_t)d.pool_blocks * d.blk;
-        const bool fused = n_out > kTopkRowsMax;
-        st = index_score_launch(io->idx_q[l], w, keys, d.key_cap, io->lens, 1, s->pool, d.pool_blocks,
-                                d.blk, s->scores, n_out, d.n_seq, fused ? s->tw.hist : nullptr, stream);
-        if (st == CSA2_OK)
-          st = topk_launch(s->scores, n_out, nullptr, 1, d.topk, s->pool, d.pool_blocks, d.blk, idx, s->tw, fused,
-                           d.n_seq, stream);
+        st = pool_select_path(io->idx_q[l], w, keys, d.key_cap, io->lens, s->pool, d.pool_blocks, d.blk, d.topk,
+                              idx, s->scores, s->tw, d.n_seq, stream);
       } else {
         // Flat: all positions (csa2_flat_select's path, on the scheduler's buffers).
         FlatSelectWs f{};

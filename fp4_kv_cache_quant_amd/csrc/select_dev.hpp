@@ -141,6 +141,25 @@ __device__ void find_threshold_bin_once(const uint32_t* hist, int nbins, uint32_
   __syncthreads();
 }
 
+// Largest (smallest) of a wavefront's 64 values, on VALU moves: DPP quad_perm swaps of
+// neighbours and pairs, row_half_mirror and row_mirror (lane i with 7 - i
+// and 15 - i of its 8 / 16 lanes), then v_permlane16_swap / 32_swap.
+template <bool kMax>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return kMax ? max(a, b) : min(a, b); };
+  int x = (int)v;
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = (int)op((uint32_t)r16[0], (uint32_t)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return op((uint32_t)r32[0], (uint32_t)r32[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_reduce_u32<true>(v); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_reduce_u32<false>(v); }
+
 // The score whose order key (order_key in topk_ws.hpp) is key != 0.
 __device__ __forceinline__ float order_key_value(uint32_t key) {
   return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);

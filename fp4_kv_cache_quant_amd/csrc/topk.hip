@@ -772,8 +772,11 @@ static_assert(sizeof(RowsSmem) <= 160 * 1024, "one workgroup's LDS");
 // (1 <= kk <= nc) and how many keys equal to T are taken (ties), given the
 // candidates' top-digit histogram hist1 (complete, and hist2 / hist3 zero):
 // radix select over digits of 12, 12 and 8 bits, every thread taking keys
-// tid, tid + NT, ...  Called by the whole workgroup.
-template <int NT>
+// tid, tid + NT, ...  kGrouped: one LDS atomic per distinct bin and
+// wavefront (wave_hist_add_grouped) instead of one per key -- for keys that
+// crowd into few bins, such as integer-valued scores, whose low bits are
+// all equal.  Called by the whole workgroup.
+template <int NT, bool kGrouped = false>
 __device__ void select_candidates(const uint32_t* ck, int nc, uint32_t kk, const uint32_t* hist1,
                                   uint32_t* hist2, uint32_t* hist3, uint32_t (*scan_sum)[NT / 64],
                                   uint32_t* found, uint32_t& T, uint32_t& ties) {
@@ -781,17 +784,33 @@ __device__ void select_candidates(const uint32_t* ck, int nc, uint32_t kk, const
   find_threshold_bin_once<NT>(hist1, kTopkBins, kk, scan_sum[1], found);
   const uint32_t b1 = found[0];
   const uint32_t need1 = kk - found[1];
-  for (int c = tid; c < nc; c += NT) {
-    const uint32_t key = ck[c];
-    if ((key >> 20) == b1) atomicAdd(&hist2[(key >> 8) & 0xFFFu], 1u);
+  if (kGrouped) {
+    for (int base = tid - lane_id(); base < nc; base += NT) {  // uniform over each wavefront
+      const int c = base + lane_id();
+      const uint32_t key = c < nc ? ck[c] : 0u;
+      wave_hist_add_grouped(hist2, (key >> 8) & 0xFFFu, c < nc && (key >> 20) == b1);
+    }
+  } else {
+    for (int c = tid; c < nc; c += NT) {
+      const uint32_t key = ck[c];
+      if ((key >> 20) == b1) atomicAdd(&hist2[(key >> 8) & 0xFFFu], 1u);
+    }
   }
   __syncthreads();
   find_threshold_bin_once<NT>(hist2, kTopkBins, need1, scan_sum[2], found);
   const uint32_t pre2 = (b1 << 12) | found[0];
   const uint32_t need2 = need1 - found[1];
-  for (int c = tid; c < nc; c += NT) {
-    const uint32_t key = ck[c];
-    if ((key >> 8) == pre2) atomicAdd(&hist3[key & 0xFFu], 1u);
+  if (kGrouped) {
+    for (int base = tid - lane_id(); base < nc; base += NT) {
+      const int c = base + lane_id();
+      const uint32_t key = c < nc ? ck[c] : 0u;
+      wave_hist_add_grouped(hist3, key & 0xFFu, c < nc && (key >> 8) == pre2);
+    }
+  } else {
+    for (int c = tid; c < nc; c += NT) {
+      const uint32_t key = ck[c];
+      if ((key >> 8) == pre2) atomicAdd(&hist3[key & 0xFFu], 1u);
+    }
   }
   __syncthreads();
   find_threshold_bin_once<NT>(hist3, 256, need2, scan_sum[3], found);
@@ -1164,13 +1183,207 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_flagged_kernel(const 
 
 // Bitmap words per sequence: a multiple of 4, so that every sequence's
 // bitmap is 16-byte aligned.
+// ------------------------------------------------------ pool selection
+// The Top-k of a hierarchical layer's pool slots (at most 16,384 per
+// sequence), after the pool scoring kernel has left the j-th largest key
+// of every 128-slot tile (tile_bound [n_seq][tiles]; see index_score.hip),
+// whose least, B, is a lower bound of the sequence's k-th largest key.
+// One 1,024-thread workgroup per sequence; thread t holds slots 16t ..
+// 16t + 15.  The keys >= B -- at least k of them when B is a bound, and
+// usually few more -- go to an LDS list in slot order (one scan), the exact
+// k-th key and its ties are selected among them (radix select over digits
+// of 12, 12 and 8 bits), and the list's selected entries are written in
+// slot order, which is id order.  When B leaves fewer than k or more than
+// kPoolCap keys, the same radix select runs over all the keys.
+#ifndef CSA2_POOL_SELECT_THREADS
+#define CSA2_POOL_SELECT_THREADS 1024
+#endif
+constexpr int kPoolSelThreads = CSA2_POOL_SELECT_THREADS;
+constexpr int kPoolSelWaves = kPoolSelThreads / 64;
+constexpr int kPoolSelMax = 16384;
+constexpr int kPoolSelPer = kPoolSelMax / kPoolSelThreads;  // slots per thread
+constexpr int kPoolCap = 4096;                               // keys selected from the LDS list
+
+struct PoolSmem {
+  int32_t pool[CSA2_TOPK_MAX];
+  uint32_t hist1[kTopkBins];
+  uint32_t hist2[kTopkBins];
+  uint32_t hist3[kTopkBins];
+  uint32_t key[kPoolCap];
+  uint32_t slot[kPoolCap];
+  uint32_t scan_sum[4][kPoolSelWaves];  // the list selection's scans (slots 1..3)
+  uint32_t full_sum[3][kPoolSelWaves];  // the scans over all keys
+  uint32_t cnt_sum[2 * kPoolSelWaves];
+  uint32_t out_sum[2 * kPoolSelWaves];
+  uint32_t bmin[kPoolSelWaves];
+  uint32_t bmax[kPoolSelWaves];
+  uint32_t found[2];
+};
+
+__global__ __launch_bounds__(kPoolSelThreads) void pool_select_kernel(const float* __restrict__ scores, int32_t n,
+                                                                   int32_t k, const int32_t* __restrict__ pool,
+                                                                   int32_t n_pool, int32_t blk,
+                                                                   const uint32_t* __restrict__ tile_bound,
+                                                                   int32_t* __restrict__ out) {
+  constexpr int NT = kPoolSelThreads;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  PoolSmem& sm = *reinterpret_cast<PoolSmem*>(smem_raw);
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const uint32_t kk = (uint32_t)k;
+  const int n_tiles = (n + 127) / 128;
+  const uint32_t tb = tid < n_tiles ? tile_bound[(int64_t)b * n_tiles + tid] : 0xFFFFFFFFu;
+  const float* sc = scores + (int64_t)b * n;
+  const int s0 = kPoolSelPer * tid;
+  uint32_t key[kPoolSelPer];
+  if ((n & 3) == 0 && s0 + kPoolSelPer <= n) {
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(sc + s0);
+    f32x4 v[kPoolSelPer / 4];
+#pragma unroll
+    for (int i = 0; i < kPoolSelPer / 4; ++i) v[i] = p4[i];
+#pragma unroll
+    for (int i = 0; i < kPoolSelPer / 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * i + e] = order_key(v[i][e]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPoolSelPer; ++j) key[j] = s0 + j < n ? order_key(sc[s0 + j]) : 0u;
+  }
+  if (pool)
+    for (int i = tid; i < n_pool; i += NT) sm.pool[i] = pool[(int64_t)b * n_pool + i];
+  for (int i = tid; i < kTopkBins; i += NT) sm.hist1[i] = sm.hist2[i] = sm.hist3[i] = 0u;
+  {
+    uint32_t lm = 0u;
+#pragma unroll
+    for (int j = 0; j < kPoolSelPer; ++j) lm = max(lm, key[j]);
+    const uint32_t wm = wave_min_u32(tb), wx = wave_max_u32(lm);
+    if ((tid & 63) == 0) sm.bmin[tid >> 6] = wm, sm.bmax[tid >> 6] = wx;
+  }
+  __syncthreads();
+  uint32_t B = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < kPoolSelWaves; ++i) B = min(B, sm.bmin[i]), kmax = max(kmax, sm.bmax[i]);
+  uint2 cnt = make_uint2(0u, 0u);  // (keys >= B, keys)
+#pragma unroll
+  for (int j = 0; j < kPoolSelPer; ++j) {
+    cnt.x += (key[j] != 0u && key[j] >= B) ? 1u : 0u;
+    cnt.y += key[j] != 0u ? 1u : 0u;
+  }
+  uint2 tot;
+  const uint2 before = block_exclusive_scan2_once<NT>(cnt, sm.cnt_sum, &tot);
+  // Selection: keys > T, and the lowest `ties` slots with key == T (T = 0:
+  // every key is taken).
+  uint32_t T = 0u, ties = 0u;
+  const bool list = tot.y > kk && tot.x >= kk && tot.x <= (uint32_t)kPoolCap;  // uniform
+  if (list) {
+    uint32_t pos = before.x;
+#pragma unroll
+    for (int j = 0; j < kPoolSelPer; ++j) {
+      if (key[j] != 0u && key[j] >= B) {
+        sm.key[pos] = key[j];
+        sm.slot[pos] = (uint32_t)(s0 + j);
+        ++pos;
+      }
+    }
+    __syncthreads();
+    // The exact kk-th largest among the list by a radix select whose digits
+    // are taken over the list's own key range [B, max]: 12 bits at a time
+    // from the top of the span, so that keys crowded in a narrow range (the
+    // usual case) spread over the bins.
+    // Each pass counts the keys in [base, base + width) by bits shift.. of
+    // key - base (at most 4,096 bins), and narrows the range to the bin
+    // that holds the need-th largest.
+    uint32_t base = B, need = kk;
+    uint64_t width = (uint64_t)(kmax - B) + 1;
+    int shift = max(0, 32 - __clz(kmax - B) - 12);
+    uint32_t* hist[3] = {sm.hist1, sm.hist2, sm.hist3};
+    for (int pass = 0; pass < 3; ++pass) {
+      for (int c = tid; c < (int)tot.x; c += NT) {
+        const uint32_t kv = sm.key[c];
+        if (kv >= base && (uint64_t)(kv - base) < width) atomicAdd(&hist[pass][(kv - base) >> shift], 1u);
+      }
+      __syncthreads();
+      find_threshold_bin_once<NT>(hist[pass], kTopkBins, need, sm.scan_sum[pass + 1], sm.found);
+      base += sm.found[0] << shift;
+      need -= sm.found[1];
+      if (shift == 0) break;
+      width = (uint64_t)1 << shift;
+      shift = max(0, shift - 12);
+    }
+    T = base;
+    ties = need;
+  } else if (tot.y > kk) {
+#pragma unroll
+    for (int j = 0; j < kPoolSelPer; ++j) wave_hist_add_grouped(sm.hist1, key[j] >> 20, key[j] != 0u);
+    __syncthreads();
+    find_threshold_bin_once<NT>(sm.hist1, kTopkBins, kk, sm.full_sum[0], sm.found);
+    const uint32_t b1 = sm.found[0], need1 = kk - sm.found[1];
+#pragma unroll
+    for (int j = 0; j < kPoolSelPer; ++j)
+      wave_hist_add_grouped(sm.hist2, (key[j] >> 8) & 0xFFFu, key[j] != 0u && (key[j] >> 20) == b1);
+    __syncthreads();
+    find_threshold_bin_once<NT>(sm.hist2, kTopkBins, need1, sm.full_sum[1], sm.found);
+    const uint32_t pre2 = (b1 << 12) | sm.found[0], need2 = need1 - sm.found[1];
+#pragma unroll
+    for (int j = 0; j < kPoolSelPer; ++j)
+      wave_hist_add_grouped(sm.hist3, key[j] & 0xFFu, key[j] && (key[j] >> 8) == pre2);
+    __syncthreads();
+    find_threshold_bin_once<NT>(sm.hist3, 256, need2, sm.full_sum[2], sm.found);
+    T = (pre2 << 8) | sm.found[0];
+    ties = need2 - sm.found[1];
+  }
+  // Output in slot order: the list entries [e0, e1) of this thread, or its
+  // own 16 slots.  A taken key's position = keys above T before it + ties
+  // taken before it.
+  const int32_t* pl = pool ? sm.pool : nullptr;
+  int32_t* ob = out + (int64_t)b * k;
+  const int per = list ? ((int)tot.x + NT - 1) / NT : kPoolSelPer;
+  const int e0 = list ? min((int)tot.x, tid * per) : 0, e1 = list ? min((int)tot.x, e0 + per) : kPoolSelPer;
+  auto item = [&](int e, uint32_t& kv, uint32_t& slot) {
+    if (list) {
+      kv = sm.key[e];
+      slot = sm.slot[e];
+    } else {
+      kv = 0u;
+#pragma unroll
+      for (int j = 0; j < kPoolSelPer; ++j)
+        if (j == e) kv = key[j];
+      slot = (uint32_t)(s0 + e);
+    }
+  };
+  uint2 c2 = make_uint2(0u, 0u);  // (keys > T, keys == T)
+  for (int e = e0; e < e1; ++e) {
+    uint32_t kv, slot;
+    item(e, kv, slot);
+    c2.x += kv > T ? 1u : 0u;
+    c2.y += (T != 0u && kv == T) ? 1u : 0u;
+  }
+  uint2 t2;
+  const uint2 b2 = block_exclusive_scan2_once<NT>(c2, sm.out_sum, &t2);
+  uint32_t pgt = b2.x, peq = b2.y;
+  for (int e = e0; e < e1; ++e) {
+    uint32_t kv, slot;
+    item(e, kv, slot);
+    int32_t pos = -1;
+    if (kv > T) {
+      pos = (int32_t)(pgt + min(peq, ties));
+      ++pgt;
+    } else if (T != 0u && kv == T) {
+      if (peq < ties) pos = (int32_t)(pgt + peq);
+      ++peq;
+    }
+    if (pos >= 0 && pos < k) ob[pos] = pl ? pl[slot / blk] * blk + (int32_t)(slot % blk) : (int32_t)slot;
+  }
+  const uint32_t n_sel = t2.x + min(t2.y, ties);
+  for (uint32_t i = n_sel + tid; i < kk; i += NT) ob[i] = -1;
+}
+
 static int64_t bitmap_words(int64_t n) { return ((n + 31) / 32 + 3) / 4 * 4; }
 
 size_t topk_workspace_bytes(int64_t n, int32_t n_seq) {
   const int64_t words = bitmap_words(n);
   const int64_t tie_words = (n + 31) / 32 > kTopkLdsWords ? words : 0;
   return (size_t)n_seq * (kCandBytes + kTopkBins * sizeof(uint32_t) + (words + tie_words) * sizeof(uint32_t) +
-                          kTopkFilterWgMax * sizeof(uint32_t)) + 64;
+                          kTopkFilterWgMax * sizeof(uint32_t) + kPoolTiles * sizeof(uint32_t)) + 64;
 }
 
 // Layout: cand, hist, bits, tie (long inputs), wcnt; ws is 16-byte aligned.
@@ -1187,6 +1400,8 @@ TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq) {
   w.tie = reinterpret_cast<uint32_t*>(p);  // used (and sized) only past kTopkLdsWords words
   if ((n + 31) / 32 > kTopkLdsWords) p += (size_t)n_seq * w.words_cap * sizeof(uint32_t);
   w.wcnt = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)n_seq * kTopkFilterWgMax * sizeof(uint32_t);
+  w.bound = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
@@ -1215,7 +1430,9 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_flagged_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_cand_select_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(LeanSmem)) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(LeanSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(pool_select_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PoolSmem)) != hipSuccess)
       return launch_status("csa2_topk (shared memory attribute)");
     attr_set = true;
   }
@@ -1267,6 +1484,27 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
     hipLaunchKernelGGL(topk_final_kernel<false>, dim3(n_seq), dim3(kFinalThreads), sizeof(FinalSmem), stream,
                        scores, n, lens, len_div, k, pool, n_pool, blk, ws, out);
   return launch_status("csa2_topk");
+}
+
+// The pool Top-k after bounded pool scoring (pool_select_kernel): n <=
+// kPoolSelMax slots per sequence, k <= CSA2_TOPK_MAX; ws.bound holds the
+// scoring kernel's tile bounds.
+csa2_status pool_select_launch(const float* scores, int64_t n, int32_t k, const int32_t* pool, int32_t n_pool,
+                               int32_t blk, const TopkWs& ws, int32_t* out, int32_t n_seq, hipStream_t stream) {
+  if (n_seq == 0) return CSA2_OK;
+  CSA2_REQUIRE(n >= 1 && n <= kPoolSelMax && k >= 1 && k <= CSA2_TOPK_MAX && n_pool <= CSA2_TOPK_MAX &&
+                   (reinterpret_cast<uintptr_t>(scores) & 15) == 0,
+               CSA2_ESHAPE, "pool selection: bad shape");
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(pool_select_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PoolSmem)) != hipSuccess)
+      return launch_status("pool selection (shared memory attribute)");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(pool_select_kernel, dim3(n_seq), dim3(kPoolSelThreads), sizeof(PoolSmem), stream, scores,
+                     (int32_t)n, k, pool, n_pool, blk, static_cast<const uint32_t*>(ws.bound), out);
+  return launch_status("pool selection");
 }
 
 }  // namespace csa2

@@ -25,6 +25,7 @@ struct TopkWs {
   uint32_t* bits;     // [n_seq][words_cap] selection bitmap of the filter pass
   uint32_t* tie;      // [n_seq][words_cap] tie bitmap (inputs longer than kTopkLdsWords * 32)
   uint2* cand;        // [n_seq][kTopkCandCap] (key, slot)
+  uint32_t* bound;    // [n_seq][kPoolTiles] per-tile key bounds left by bounded pool scoring
   int64_t words_cap;
 };
 
@@ -52,6 +53,26 @@ TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq);
 csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
                         const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, const TopkWs& ws,
                         bool hist_ready, int32_t n_seq, hipStream_t stream, const int32_t* gids = nullptr);
+
+// Pool slots of a hierarchical layer selected after scoring that left
+// ws.bound (index_score_launch with tile_bound = ws.bound); n <= 16,384.
+constexpr int64_t kPoolSelectMax = 16384;
+constexpr int kPoolTiles = kPoolSelectMax / 128;  // 128-slot tiles with a bound each
+csa2_status pool_select_launch(const float* scores, int64_t n, int32_t k, const int32_t* pool, int32_t n_pool,
+                               int32_t blk, const TopkWs& ws, int32_t* out, int32_t n_seq, hipStream_t stream);
+
+// A hierarchical layer's pool selection (scores of the pool's positions +
+// Top-k; csa2_pool_select and the scheduler's pool layers).
+struct PoolSelectWs {
+  int64_t n;       // slots per sequence, n_pool * blk
+  float* scores;   // [n_seq][n]
+  TopkWs tw;
+  size_t bytes;
+};
+PoolSelectWs pool_select_ws(int32_t n_pool, int32_t blk, int32_t n_seq, void* base);
+csa2_status pool_select_path(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, const int32_t* pool, int32_t n_pool, int32_t blk, int32_t k,
+                             int32_t* out, float* scores, const TopkWs& tw, int32_t n_seq, hipStream_t stream);
 
 // A flat Full layer's selection (scores + Top-k) and its workspace
 // (csa2_flat_select; the scheduler's flat layers).

@@ -74,7 +74,8 @@ const char* csa2_last_error(void);
 /* Version of this ABI (bumped on any signature or struct change; 2 added
  * the FP8 window, 3 the key maintenance on append, 4 the per-layer indexer
  * K of flat Full layers and csa2_flat_select, 5 the stream argument of
- * csa2_sched_check and the per-step window rows of csa2_step_io). */
+ * csa2_sched_check, the per-step window rows of csa2_step_io and
+ * csa2_pool_select). */
 int32_t csa2_abi_version(void);
 
 /* ------------------------------------------------------------ FP4 cache
@@ -176,6 +177,29 @@ size_t csa2_flat_select_workspace_size(int64_t key_cap, int32_t k, int32_t n_seq
 csa2_status csa2_flat_select(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
                              const int32_t* lens, int32_t k, int32_t* out, void* ws, size_t ws_bytes, int32_t n_seq,
                              void* stream);
+
+/* Steps (b)+(c) of a hierarchical layer's pool in one call [P1 "Compressed
+ * Sparse Attention 2 (CSA2)"]: the hierarchical Full layer and the Reindex
+ * layers after it keep a fresh Top-k among the positions of a pool of up to
+ * 2,048 blocks of blk positions.  The result equals csa2_index_score (pool
+ * mode, n_out = n_pool * blk) followed by csa2_topk (the same pool, lens =
+ * NULL): out [n_seq][k] int32, the ascending positions, -1 padded.  For
+ * n_pool * blk <= 16,384 the scoring also leaves a lower bound of each
+ * sequence's k-th score (every wavefront's j-th largest of its 128 slots,
+ * j = ceil(k / tiles), the least of them), and the selection keeps only the
+ * scores at or above it.
+ *   q [n_seq][8][64] bf16, w [n_seq][8] f32 or NULL, keys [n_seq][key_cap][64]
+ *   bf16 (q, keys 16-byte aligned), lens [n_seq] int32 (device), pool
+ *   [n_seq][n_pool] int32 ascending block ids (-1 = empty)
+ *   ws: csa2_pool_select_workspace_size(n_pool, blk, n_seq) bytes, 256-byte
+ *   aligned, zero-filled before its first use and left ready for the next
+ *   call (calls sharing it must not overlap).
+ * Limits: 1 <= k <= CSA2_TOPK_MAX, 1 <= n_pool <= CSA2_TOPK_MAX,
+ * n_pool * blk <= CSA2_TOPK_NMAX. */
+size_t csa2_pool_select_workspace_size(int32_t n_pool, int32_t blk, int32_t n_seq);
+csa2_status csa2_pool_select(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
+                             const int32_t* lens, const int32_t* pool, int32_t n_pool, int32_t blk, int32_t k,
+                             int32_t* out, void* ws, size_t ws_bytes, int32_t n_seq, void* stream);
 
 /* Steps (d)+(e): sparse + SWA attention of n_q queries.
  * [P1 "Compressed Sparse Attention 2 (CSA2)"]: each layer attends with its

@@ -598,3 +598,44 @@ def test_sparse_attn_f16_conversion_of_large_and_tiny_values(csa2):
     raw = dense(qv, xv)
     rel = np.linalg.norm(raw - ref, axis=1) / np.linalg.norm(ref, axis=1)
     assert rel[[0, 1, 3]].min() > 1e-2, rel[:4]  # the conversion is visible in the heads that meet it
+
+
+@pytest.mark.parametrize("case", ["full_pool", "ragged_pool", "short", "weights", "blk16", "ties"])
+def test_pool_select_matches_oracle(csa2, case):
+    """Scores + Top-k of a pool's positions in one call (csa2_pool_select)
+    against the oracle's pool selection: a full 2,048-block pool, a pool
+    with empty blocks and blocks past the sequence, fewer candidates than k,
+    dyadic head weights, 16-position blocks (32,768 slots: the path without
+    the bound), and integer keys of three values (ties everywhere)."""
+    n_seq, k = 3, 512
+    rng = np.random.default_rng(hash(case) % 1000)
+    blk = 16 if case == "blk16" else 8
+    key_cap = 8 * 20000 + 3
+    lens = np.array([key_cap, key_cap - 7, 8 * 1500 + 5], np.int32)
+    if case == "short":
+        lens = np.array([300, 9, 4000], np.int32)
+    lo, hi = (-1, 1) if case == "ties" else (-4, 4)
+    keys = _bf16_of(rng.integers(lo, hi + 1, size=(n_seq, key_cap, 64)))
+    q = _bf16_of(rng.integers(-4, 5, size=(n_seq, 8, 64)))
+    w = (rng.integers(-16, 17, size=(n_seq, 8)) / 8).astype(np.float32) if case == "weights" else None
+    n_pool = 2048
+    pool = np.full((n_seq, n_pool), -1, np.int32)
+    for b in range(n_seq):
+        nb = -(-int(lens[b]) // blk)
+        m = min(n_pool, nb + 40)                  # some blocks past the sequence's end
+        cand = np.sort(rng.choice(max(nb + 40, m), m, replace=False))
+        pool[b, :m] = cand
+        if case == "ragged_pool":
+            pool[b, m // 2:] = -1                 # empty blocks (the tail of the list)
+            pool[b, :m // 2] = np.sort(rng.choice(nb, m // 2, replace=False))
+    print_case(f"pool_select {case}")
+    out = torch.full((n_seq, k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(csa2.pool_select_workspace_size(n_pool, blk, n_seq), dtype=torch.uint8, device="cuda")
+    for rep in range(2):  # the workspace is left ready for the next call
+        csa2.pool_select(dev(q), dev(keys), dev(lens), dev(pool), k, out, blk=blk,
+                         w=dev(w) if w is not None else None, ws=ws)
+        got = out.cpu().numpy()
+        for b in range(n_seq):
+            ref = oracle.pool_select(q[b], keys[b], int(lens[b]), pool[b].astype(np.int64), k, blk,
+                                     None if w is None else w[b])
+            assert np.array_equal(got[b], ref), (case, rep, b)

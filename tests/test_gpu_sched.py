@@ -283,3 +283,33 @@ def test_checkpoint_and_resume_reproduces_the_steps(wl):
 def csa2_fp4(codes, scales):
     import fp4_kv_cache_quant_amd as csa2
     return csa2.FP4KV(codes, scales)
+
+
+def test_pool_selection_all_ties_and_partly_tied_rows(wl):
+    """The hierarchical path with its pool Top-k after bounded scoring, when
+    the bound admits more keys than the selection's LDS list: a zero indexer
+    Q makes every block and pool score 0 (ties everywhere: the first 2,048
+    blocks, then the first 512 positions), and a Reindex Q of zeros in one
+    sequence only; indices, pool and outputs against the oracle."""
+    import oracle as orc
+    cfg = C.HIER_1M.with_(n_seq=2, L0=8 * 3000 + 5, q_sets=1)
+    print_case("pool selection, all scores tied")
+    inp = wl.build_decode_inputs(cfg, 1)
+    inp.idx_q[0][0].zero_()        # Full layer, both sequences
+    inp.idx_q[0][1][1].zero_()     # Reindex layer, sequence 1
+    sched = wl.make_sched(inp)
+    sched.decode_step(wl.step_ios(sched, inp)[0])
+    torch.cuda.synchronize()
+    pool = sched.pool().cpu().numpy()
+    idx = [sched.indices(l).cpu().numpy() for l in range(2)]
+    for b in range(cfg.n_seq):
+        assert np.array_equal(pool[b], np.arange(2048)), b
+        assert np.array_equal(idx[0][b], np.arange(512)), b
+        st = ow.seq_state(cfg, b, 0)
+        q = inp.idx_q[0][1][b].cpu().numpy().view(np.uint16)
+        ref = orc.pool_select(q, st.tok_keys, st.L, pool[b].astype(np.int64))
+        assert np.array_equal(idx[1][b], ref), b
+        if b == 1:
+            assert np.array_equal(idx[1][b], np.arange(512))
+    assert sched.check() == 0
+    sched.close()
