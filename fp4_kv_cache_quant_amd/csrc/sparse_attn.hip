@@ -216,7 +216,7 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
                                            const QB& qb_operand, float scale_log2, Between between) {
   constexpr int kRows = AttnCfg<W>::kRows, kPPitch = AttnCfg<W>::kPPitch, kSlices = AttnCfg<W>::kSlices;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int row_local = wave * 16 + n;
 
@@ -262,8 +262,9 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
   }
   const uint64_t rows_ok = __ballot(t.ok);  // bit n (lanes 0..15) = row n of this wavefront
   float z[4];
+  const uint32_t ok4 = (uint32_t)(rows_ok >> (4 * g));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) z[j] = ((rows_ok >> (4 * g + j)) & 1) ? s[j] * scale_log2 : kNegInf;
+  for (int j = 0; j < 4; ++j) z[j] = ((ok4 >> j) & 1) ? s[j] * scale_log2 : kNegInf;
 
   // ---- softmax statistics of the chunk, per head n, against the running
   // max (online softmax across the workgroup's chunks)
@@ -278,7 +279,7 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
   float lsum = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    p[j] = (z[j] == kNegInf) ? 0.f : exp2f(z[j] - M);
+    p[j] = (z[j] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(z[j] - M);
     lsum += p[j];
   }
   {
@@ -293,7 +294,7 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
   }
   lsum = fold32_add(fold16_add(lsum));
   if (g == 0) sm.red_l[wave][n] = lsum;
-  const float alpha_n = (st.m_run == kNegInf) ? 0.f : exp2f(st.m_run - M);
+  const float alpha_n = (st.m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - M);
   if (tid < 16) sm.alpha[tid] = alpha_n;
   st.m_run = M;
   lds_barrier();
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   __shared__ __attribute__((aligned(16))) AttnSmem<W> sm;
   constexpr int kSlices = Cfg::kSlices;
   const int split = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   // Workgroups are dealt to the 8 XCDs round-robin (linear id mod 8).  With
   // one workgroup per query, XCD x takes a contiguous run of queries, so
