@@ -25,8 +25,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are switched off (the compiler would form them from
 # scalar float code); no fast-math: the quantiser's comparisons and the
 # indexer's rounding order are exact by construction and must stay so.
+# MFMA results go to ordinary VGPRs (-amdgpu-mfma-vgpr-form): the scoring
+# kernels read every accumulator with VALU code right away, and results left
+# in AGPRs would cost one v_accvgpr_read per value first.
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "--offload-arch=gfx950", f"-I{INCLUDE}",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:
