@@ -157,3 +157,42 @@ def test_prefill_many_rows_partial_visibility(wl, name):
         assert np.array_equal(idx0[i], ref[0].idx), f"query {i} indices"
         for l in range(len(cfg.layers)):
             assert_attention_close(inp.out[l][i].cpu().numpy(), ref[l].out, f"query {i} layer {l}")
+
+
+def _sampled_entries(n_entries: int) -> np.ndarray:
+    """The entries whose scores give a query's threshold estimate: 64 runs of
+    16 entries, one at the start of each 64th of the cache."""
+    i = np.arange(1024)
+    return (i >> 4) * (n_entries >> 6) + (i & 15)
+
+
+@pytest.mark.parametrize("planted", ["high", "zero"])
+def test_prefill_selection_when_the_estimate_fails(wl, planted):
+    """Many queries are selected from each query's candidates at or above a
+    threshold estimated on sampled entries.  Planted keys make the estimate
+    fail: 64.0 in every dim of 40 sampled entries (more than the estimate's
+    rank, about 34 here) puts the threshold above every other entry's
+    score, so fewer than k candidates pass; zero keys on all sampled entries
+    put it at 0, so every score passes and the candidate regions overflow.
+    Such queries take the full selection over their score rows; the indices
+    must still be the oracle's."""
+    cfg = _small(n_entries=40000, n_q=300, t0=2 * 40000 - 300)
+    print_case(f"prefill estimate failure ({planted}): n_entries={cfg.n_entries} n_q={cfg.n_q} t0={cfg.t0}")
+    inp = wl.build_prefill_inputs(cfg)
+    keys = ow.prefill_entry_keys(cfg).copy()
+    rows = _sampled_entries(cfg.n_entries)
+    if planted == "high":
+        keys[rows[:40]] = 0x4280                                # bf16 64.0
+    else:
+        keys[rows] = 0x0000                                     # bf16 +0.0
+    inp.entry_k.copy_(torch.from_numpy(keys.view(np.int16)).to(inp.entry_k.device).view(inp.entry_k.dtype))
+    pf, io = wl.make_prefill(inp)
+    pf.run(io)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    sample = sorted({0, 1, 150, 298, 299, *rng.integers(0, cfg.n_q, 3).tolist()})
+    idx0 = inp.idx[0].cpu().numpy()
+    for i in sample:
+        ref = ow.prefill_reference(cfg, i, entry_keys=keys)
+        assert np.array_equal(idx0[i], ref[0].idx), f"query {i} indices"
+        assert_attention_close(inp.out[0][i].cpu().numpy(), ref[0].out, f"query {i} layer 0")
