@@ -9,8 +9,8 @@
 //
 // Online softmax over chunks.  A query's attended rows (k_idx selected FP4
 // rows and swa_max window rows, in tiles of 16) are cut into chunks of W
-// tiles (W = wavefronts per workgroup: 8 when there are few queries, 4 when
-// there are many, so that two workgroups share a CU), the window tiles
+// tiles (W = wavefronts per workgroup: 8 when there are few queries, 2 when
+// there are many, so that four workgroups share a CU), the window tiles
 // spread evenly over the chunks.  A workgroup walks a run of chunks of one
 // query; per chunk:
 //   1. each wavefront owns one tile; lane (n = l%16, g = l/16) loads row n's
@@ -88,7 +88,7 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
 }
 
 // With 8 wavefronts (one workgroup per CU) main Q is staged once in LDS;
-// with 4 wavefronts (two workgroups per CU) Q stays in registers.  Either
+// with 2 wavefronts (four workgroups per CU) Q stays in registers.  Either
 // way the next chunk's rows are loaded while the current one is computed.
 template <int W>
 struct AttnCfg {
@@ -530,8 +530,8 @@ struct AttnPlan {
 static AttnPlan attn_plan(int32_t n_q, int32_t k_idx, int32_t swa_max) {
   AttnPlan p;
   if (n_q >= 1024) {
-    p.waves = 4;
-    p.per_split = attn_chunks(k_idx, swa_max, 4);
+    p.waves = 2;
+    p.per_split = attn_chunks(k_idx, swa_max, 2);
     p.splits = 1;
     return p;
   }
@@ -562,7 +562,7 @@ static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, con
                        kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
                        new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out);
   else
-    hipLaunchKernelGGL((attn_kernel<4, kWin>), dim3(p.splits, n_q), dim3(64 * 4), 0, stream, q, kv.codes,
+    hipLaunchKernelGGL((attn_kernel<2, kWin>), dim3(p.splits, n_q), dim3(64 * 2), 0, stream, q, kv.codes,
                        kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
                        new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out);
 }
