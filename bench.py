@@ -44,33 +44,45 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12694629, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12709000, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "a3cde2d3d12b1ebf48ca75df8bc97f845f788e412ba884ef028cef3a93e53615",
+                    "8440cbb82885107b914c9b0a58dcc4f97586761b2a2b00e05fec1ccbf0c6537e",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/block_scan": {
-        "bytes": 279956055, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 210269953, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "6d1a3259d2ecb38b6d5bcfa94c14686bd1a9a43086a023f866271d69e3dde088",
+                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd",
+                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
-                    "a6b9172621f3d03f20519b4513831baaf8301db1063e28fef2e42cb10c075217"}},
-    "encoder_1m/flat_select": {
-        "bytes": 1092888005, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+                    "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
+    "decoder20_1m/pool_select": {
+        "bytes": 36499619, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "6d1a3259d2ecb38b6d5bcfa94c14686bd1a9a43086a023f866271d69e3dde088",
+                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "9c3b97d689555148c95531679d825a56836e7364b62ded2785b2bc277ea9a737",
-                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "632749e361c7ab6dcc620b387bfc4cfffc93bdc46af81e78b6ddadf936b283bd",
-                    "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
-                    "a6b9172621f3d03f20519b4513831baaf8301db1063e28fef2e42cb10c075217",
+                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
+                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
+                    "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
+    "encoder_1m/flat_select": {
+        "bytes": 1092907280, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "fp4_kv_cache_quant_amd/csrc/topk.hip":
+                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
+                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
+                    "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
 }
 
 
@@ -105,7 +117,38 @@ def measured_traffic(op_key: str):
 # same workload (the kernels of one call summed), with the SHA-256 of the
 # sources it was taken on: reported next to the HIP-event time while those
 # sources are unchanged.
-KERNEL_TRACE = {}
+KERNEL_TRACE = {
+    "decoder20_1m/sparse_attn": {
+        "us": 12.72, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
+                    "8440cbb82885107b914c9b0a58dcc4f97586761b2a2b00e05fec1ccbf0c6537e",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
+    "decoder20_1m/pool_select": {
+        "us": 21.02, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "fp4_kv_cache_quant_amd/csrc/topk.hip":
+                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
+                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
+                    "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
+    "encoder_1m/flat_select": {
+        "us": 215.85, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
+                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "fp4_kv_cache_quant_amd/csrc/topk.hip":
+                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
+                    "fp4_kv_cache_quant_amd/csrc/common.hpp":
+                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
+                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
+                    "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
+}
 
 
 def kernel_trace_us(op_key: str):
@@ -275,7 +318,8 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
                     "avg_us": round(us, 2), "us_per_step": round(us * per_step, 1),
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                    "traffic_bytes": measured_traffic(f"{config_key(cfg)}/{key}")})
+                    "traffic_bytes": measured_traffic(f"{config_key(cfg)}/{key}"),
+                    "kernel_trace_us": kernel_trace_us(f"{config_key(cfg)}/{key}")})
     return res
 
 
@@ -315,7 +359,8 @@ def flat_op_rooflines(cfg, inp, graph: bool = True):
                     "avg_us": round(us, 2), "us_per_step": round(us * per_step, 1),
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                    "traffic_bytes": measured_traffic(f"{config_key(cfg)}/{key}")})
+                    "traffic_bytes": measured_traffic(f"{config_key(cfg)}/{key}"),
+                    "kernel_trace_us": kernel_trace_us(f"{config_key(cfg)}/{key}")})
     return res
 
 
