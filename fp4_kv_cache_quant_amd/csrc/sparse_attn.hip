@@ -46,6 +46,7 @@
 #include <mutex>
 #include <string>
 
+#include "attn_dev.hpp"
 #include "common.hpp"
 
 namespace csa2 {
@@ -62,30 +63,6 @@ inline int attn_chunks(int32_t k_idx, int32_t swa_max, int waves) {
 }
 
 namespace {
-
-// Dequantise 8 channels -- code dword dw, channel i in nibble i (byte j =
-// channels 2j (low nibble) and 2j+1) -- with the scale as an f16 pair s2:
-// four FP4-pair conversions at scale 1 (exact E2M1 values), each followed
-// by one packed f16 multiply (exact).  Returns 4 f16 pairs, channel order.
-__device__ __forceinline__ u32x4 dequant8_f16(uint32_t dw, f16x2 s2) {
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 0)) * s2);
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 1)) * s2);
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 2)) * s2);
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, 1.0f, 3)) * s2);
-  return r;
-}
-
-// Two bf16 values (one dword) as an f16 pair, rounding toward zero
-// (v_cvt_pkrtz_f16_f32: exact for |x| in [2^-14, 65504], saturating above).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
-  const float lo = __builtin_bit_cast(float, u << 16), hi = __builtin_bit_cast(float, u & 0xFFFF0000u);
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
-  return u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
-}
 
 // With 8 wavefronts (one workgroup per CU) main Q is staged once in LDS;
 // with 2 wavefronts (four workgroups per CU) Q stays in registers.  Either
@@ -199,14 +176,6 @@ __device__ __forceinline__ void tile_load(AttnTile& t, const AttnArgs& a, int n,
 #pragma unroll
     for (int i = 0; i < (kWin == kWinE4m3 ? 8 : 16); ++i) t.raw[i] = sp[i];
   }
-}
-
-// Eight E4M3 bytes (two dwords) as four f16 pairs (exact).
-__device__ __forceinline__ u32x4 fp8x8_to_f16x8(uint32_t d0, uint32_t d1) {
-  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true))};
 }
 
 // Compute one chunk from the loaded tile (`between` runs after the softmax
@@ -551,6 +520,11 @@ size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
   return o_bytes + ml_bytes;
 }
 
+csa2_status attn_wave_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
+                             const int32_t* idx, int32_t k_idx, const uint8_t* swa, int win,
+                             int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
+                             float* out, hipStream_t stream);
+
 template <int kWin>
 static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, const csa2_fp4_kv& kv,
                           int32_t q_per_seq, const int32_t* idx, int32_t k_idx, const uint8_t* swa,
@@ -590,6 +564,9 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
   const uint8_t* nw = reinterpret_cast<const uint8_t*>(new_win);
+  if (p.waves == 2 && !new_win && k_idx <= kAttnWaveMaxIdx && (win == kWinF16 || win == kWinBf16))
+    return attn_wave_launch(q, n_q, kv, q_per_seq, idx, k_idx, sw, win, swa_q_stride_rows, swa_len, swa_max,
+                            scale_log2, out, stream);
   if (win == kWinE4m3)
     attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
                             nw, win_lens, scale_log2, part_o, part_ml, out, stream);

@@ -463,6 +463,43 @@ def test_sparse_attn_many_queries_one_cache(csa2, n_q):
         assert_attention_close(got[b], ref, f"query {b}")
 
 
+@pytest.mark.parametrize("where", ["window", "selected"])
+def test_sparse_attn_many_queries_late_maximum(csa2, where):
+    """Many queries (one wavefront each) where a row late in a query's order
+    scores far above every earlier row (more than 2^15 in softmax weight):
+    the last window row, or the last selected row, is a large multiple of
+    the sign pattern of the query's head 0.  Sampled queries vs the oracle;
+    the queries without the row check the ordinary path beside them."""
+    cap, k_idx, swa_max, n_q = 3000, 512, 128, 1024
+    src = kv_source(6, 1, cap)
+    rng = np.random.default_rng(29)
+    idx = np.stack([np.sort(rng.choice(cap, k_idx, replace=False)) for _ in range(n_q)]).astype(np.int32)
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 6), synth.NORMAL, range(n_q), np.arange(16), 512)
+    swa_rows = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 6), synth.NORMAL, [0],
+                              np.arange(n_q + swa_max - 1), 512)[0]
+    swa_len = np.full(n_q, swa_max, np.int32)
+    hot = [0, 3, 700, n_q - 1]
+    sign0 = np.where(synth.bf16_to_f32(q[hot[0], 0]) >= 0, 1.0, -1.0)
+    if where == "window":
+        for b in hot:                       # window row 127 of query b is swa_rows[b + 127]
+            sgn = np.where(synth.bf16_to_f32(q[b, 0]) >= 0, 1.0, -1.0)
+            swa_rows[b + swa_max - 1] = _bf16_of(4.0 * sgn)
+    else:
+        hot = [0]                           # one cache row, last in query 0's selection
+        idx[0, -1] = cap - 1
+        src[0, cap - 1] = _bf16_of(4.0 * sign0)
+    kv = _device_cache(csa2, src)
+    print_case(f"sparse_attn many queries, late maximum in the {where}")
+    out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+    csa2.sparse_attn(dev(q), kv, dev(idx), dev(swa_rows), dev(swa_len), SM_SCALE, out, q_per_seq=n_q,
+                     swa_q_stride_rows=1, swa_max=swa_max)
+    got = out.cpu().numpy()
+    codes, scales = oracle.quant_rows(src[0])
+    for b in sorted(set(hot) | {1, 2, 500}):
+        ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa_rows[b:b + swa_max], swa_len[b], SM_SCALE)
+        assert_attention_close(got[b], ref, f"query {b}")
+
+
 # ------------------------------------------------------------- FP8 window
 def test_quant_fp8_rows_all_bf16_patterns(csa2):
     """Every bf16 bit pattern (128 rows of 512) -> E4M3 codes, bit-exact with
