@@ -104,6 +104,13 @@ __device__ __forceinline__ void wave_issue(WaveSlot& sl, const WaveArgs& a, int3
 
 // Sources of the next chunk's converted rows: tile t, channel group k (8
 // channels of the lane's 128).
+// No next chunk (the query's last).
+struct WaveNoSrc {
+  static constexpr bool kHas = false;
+  __device__ __forceinline__ void issue(int) {}
+  __device__ __forceinline__ u32x4 x(int, int) const { return u32x4{0u, 0u, 0u, 0u}; }
+};
+
 struct WaveFp4Src {
   static constexpr bool kHas = true;
   __device__ __forceinline__ void issue(int) {}
@@ -405,8 +412,8 @@ attend:
       if (bad) goto exceeded;
     }
     // The last chunk of selected rows, followed by the first window chunk
-    // (zero rows if there is no window).
-    if (n_fc > 0) {
+    // (if any).
+    if (n_fc > 0 && n_wc > 0) {
       u32x4 hi, lo;
       const bool fits = wave_softmax(st, s_cur, ok_cur, scale_log2, g, fixed, hi, lo);
       f32x4 s_next[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -416,18 +423,25 @@ attend:
       s_cur[1] = s_next[1];
       if (!fits) goto exceeded;
     }
-    // Window chunks: the current chunk is w.
+    // Window chunks but the last: the current chunk is w.
 #pragma unroll 1
-    for (int w = 0; w < n_wc; ++w) {
+    for (int w = 0; w + 1 < n_wc; ++w) {
       u32x4 hi, lo;
       const bool fits = wave_softmax(st, s_cur, ok_cur, scale_log2, g, fixed, hi, lo);
       f32x4 s_next[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      // (After the last chunk the next one is past the window: zero rows,
-      // never used; one code path keeps O in place.)
       wave_pv_next(st, xs, hi, lo, qv, win_src(w + 1), s_next, n, g);
       win_ok(w + 1, ok_cur);
       s_cur[0] = s_next[0];
       s_cur[1] = s_next[1];
+      if (!fits) goto exceeded;
+    }
+    // The query's last chunk (selected or window), after the loops: straight
+    // code, so that the loops keep one path each.
+    if (n_fc > 0 || n_wc > 0) {
+      u32x4 hi, lo;
+      const bool fits = wave_softmax(st, s_cur, ok_cur, scale_log2, g, fixed, hi, lo);
+      f32x4 s_next[2];
+      wave_pv_next(st, xs, hi, lo, qv, WaveNoSrc{}, s_next, n, g);
       if (!fits) goto exceeded;
     }
   }
