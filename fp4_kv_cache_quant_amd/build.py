@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["quant.hip", "keys.hip", "index_score.hip", "topk.hip", "sparse_attn.hip", "attn_wave.hip", "capi.cpp",
+SOURCES = ["quant.hip", "keys.hip", "index_score.hip", "topk.hip", "sparse_attn.hip", "attn_many.hip", "capi.cpp",
            "sched.cpp", "prefill.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,11 +30,8 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "--offload-arch=gfx950", f"-I{I
 # MFMA results go to ordinary VGPRs (-amdgpu-mfma-vgpr-form): the scoring
 # kernels read every accumulator with VALU code right away, and results left
 # in AGPRs would cost one v_accvgpr_read per value first (the same values
-# either way).  Not for attn_wave.hip, whose O accumulators (128 registers
-# per lane) live in AGPRs for a whole query.  An LLVM option: used when
-# this hipcc accepts it.
+# either way).  An LLVM option: used when this hipcc accepts it.
 MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-AGPR_SOURCES = {"attn_wave.hip"}
 
 
 def _accepts(flags) -> bool:
@@ -61,7 +58,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = MFMA_VGPR if _accepts(MFMA_VGPR) else []
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, [] if src in AGPR_SOURCES else extra), SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, extra), SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

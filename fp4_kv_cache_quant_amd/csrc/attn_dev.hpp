@@ -6,9 +6,9 @@
 
 namespace csa2 {
 
-// Selected rows per query that the one-wavefront-per-query attention kernel
-// takes (its row ids are staged in LDS); more go to the workgroup kernels.
-constexpr int kAttnWaveMaxIdx = 512;
+// Selected rows per query that the many-query attention kernel takes (its
+// row ids are staged in LDS); more go to the workgroup kernels.
+constexpr int kAttnManyMaxIdx = 512;
 
 // Dequantise 8 channels -- code dword dw, channel i in nibble i (byte j =
 // channels 2j (low nibble) and 2j+1) -- with the scale as an f16 pair s2:

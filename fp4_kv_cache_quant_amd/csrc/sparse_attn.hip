@@ -520,7 +520,7 @@ size_t attn_workspace_bytes(int32_t n_q, int32_t k_idx, int32_t swa_max) {
   return o_bytes + ml_bytes;
 }
 
-csa2_status attn_wave_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
+csa2_status attn_many_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
                              const int32_t* idx, int32_t k_idx, const uint8_t* swa, int win,
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
                              float* out, hipStream_t stream);
@@ -564,8 +564,10 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
   const uint8_t* nw = reinterpret_cast<const uint8_t*>(new_win);
-  if (p.waves == 2 && !new_win && k_idx <= kAttnWaveMaxIdx && (win == kWinF16 || win == kWinBf16))
-    return attn_wave_launch(q, n_q, kv, q_per_seq, idx, k_idx, sw, win, swa_q_stride_rows, swa_len, swa_max,
+  // Many queries over bf16 / f16 window rows with no step window row (the
+  // prefill chunk): the two-wavefronts-per-query kernel of attn_many.hip.
+  if (p.waves == 2 && !new_win && k_idx <= kAttnManyMaxIdx && (win == kWinF16 || win == kWinBf16))
+    return attn_many_launch(q, n_q, kv, q_per_seq, idx, k_idx, sw, win, swa_q_stride_rows, swa_len, swa_max,
                             scale_log2, out, stream);
   if (win == kWinE4m3)
     attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
