@@ -111,11 +111,14 @@ __device__ __forceinline__ bool wave_softmax(St& st, const f32x4 (&s)[2], const 
   const bool above = !fixed && __ballot(m > st.m_run + kLazyLog2) != 0;
   const bool unset = __ballot(st.m_run != kNegInf) == 0;
   st.m_run = (above && unset) ? m : st.m_run;
+  // Rows not attended over have z = -inf and weight exp2(-inf) = 0; the
+  // reference is -inf only while no row has been seen (then every z is).
+  const float mr = st.m_run == kNegInf ? 0.f : st.m_run;
   float p[8];
   float lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    p[i] = (z[i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(z[i] - st.m_run);
+    p[i] = __builtin_amdgcn_exp2f(z[i] - mr);
     lsum += p[i];
   }
   st.l_run += fold32_add(fold16_add(lsum));
