@@ -44,15 +44,15 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12708993, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12708979, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "3e9235c325b5cf2db64e91db8e77f36764256bbf374ff0225bf547502646790a",
+                    "938dfffb4d157c3808b5f01f3226865b13aec91416329f85f73c60980805e4ab",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
-                    "fe908546c73aab93d96ea10212ce7857945ef4affb16f9ba70e43f635c41dfcd",
+                    "f661423ba3cb7510492a0ac6c0be9cc00bcf54af70b4fc72973da1614caddf09",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/block_scan": {
-        "bytes": 210265130, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 210242319, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
@@ -74,7 +74,7 @@ MEASURED_TRAFFIC = {
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "bytes": 1092933381, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "bytes": 1092917707, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
@@ -121,15 +121,15 @@ def measured_traffic(op_key: str):
 # sources are unchanged.
 KERNEL_TRACE = {
     "decoder20_1m/sparse_attn": {
-        "us": 12.76, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 12.71, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "3e9235c325b5cf2db64e91db8e77f36764256bbf374ff0225bf547502646790a",
+                    "938dfffb4d157c3808b5f01f3226865b13aec91416329f85f73c60980805e4ab",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
-                    "fe908546c73aab93d96ea10212ce7857945ef4affb16f9ba70e43f635c41dfcd",
+                    "f661423ba3cb7510492a0ac6c0be9cc00bcf54af70b4fc72973da1614caddf09",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/pool_select": {
-        "us": 21.21, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 20.95, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
@@ -141,7 +141,7 @@ KERNEL_TRACE = {
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "us": 215.5, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "us": 215.37, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
