@@ -119,18 +119,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // Scores that are not candidates.
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// An attention call's split partials still to be merged (n_q == 0: none),
-// and which of a two-part workspace the next call writes (see
-// attn_launch_deferred in sparse_attn.hip).
-struct AttnPending {
-  const float* part_o = nullptr;
-  const float2* part_ml = nullptr;
-  int32_t n_split = 0;
-  float* out = nullptr;
-  int32_t n_q = 0;
-  int parity = 0;
-};
-
 // Element type of the window rows handed to the attention kernels.
 constexpr int kWinBf16 = 0;  // bf16, converted to f16 toward zero in the kernel
 constexpr int kWinE4m3 = 1;  // OCP E4M3FN bytes

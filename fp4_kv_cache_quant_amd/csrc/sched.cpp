@@ -23,10 +23,9 @@ csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, i
                                uint32_t*, hipStream_t, uint32_t* bound_inv = nullptr, int32_t bound_k = 0);
 int64_t index_score_local_groups(int64_t key_cap);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
-csa2_status attn_launch_deferred(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
-                                 const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*,
-                                 float, float*, void*, size_t, AttnPending*, hipStream_t);
-csa2_status attn_flush(AttnPending*, hipStream_t);
+csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
+                        const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
+                        float*, void*, hipStream_t);
 csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, int64_t, int32_t, const int32_t*,
                                int32_t*, int32_t, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
@@ -171,16 +170,14 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
     const int64_t groups = index_score_local_groups(d.key_cap);
     if (d.key_cap > kTopkRowsMax && groups * d.topk <= kTopkRowsMax) s->local_groups = groups;
   }
-  // Two partial sets: consecutive layers' attention calls alternate between
-  // them (each call's combine rides along with the next call's chunks).
-  s->attn_ws_bytes = (attn_workspace_bytes(d.n_seq, d.topk, d.swa_max) + 255) / 256 * 256;
+  s->attn_ws_bytes = attn_workspace_bytes(d.n_seq, d.topk, d.swa_max);
   s->topk_ws_bytes = topk_workspace_bytes(s->scores_n, d.n_seq);
   const size_t n = (size_t)d.n_seq;
   if ((st = dev_alloc(&s->idx_bufs, (size_t)s->n_idx_bufs * n * d.topk * sizeof(int32_t))) != CSA2_OK ||
       (st = dev_alloc(&s->pool, s->any_hier ? n * d.pool_blocks * sizeof(int32_t) : 0)) != CSA2_OK ||
       (st = dev_alloc(&s->scores, n * (size_t)s->scores_n * sizeof(float))) != CSA2_OK ||
       (st = dev_alloc(&s->cand_slot, n * (size_t)(s->local_groups * d.topk) * sizeof(int32_t))) != CSA2_OK ||
-      (st = dev_alloc(&s->attn_ws, 2 * s->attn_ws_bytes)) != CSA2_OK ||
+      (st = dev_alloc(&s->attn_ws, s->attn_ws_bytes)) != CSA2_OK ||
       (st = dev_alloc(&s->topk_ws, s->topk_ws_bytes)) != CSA2_OK ||
       (st = dev_alloc(&s->err, sizeof(int32_t))) != CSA2_OK) {
     free_sched(s);
@@ -259,7 +256,6 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
   }
 
   const size_t idx_stride = (size_t)d.n_seq * d.topk;
-  AttnPending pending;  // the previous layer's attention combine, merged by the next call's launch
   for (int l = 0; l < d.n_layers; ++l) {
     const csa2_layer& L = s->layers[l];
     int32_t* idx = s->idx_bufs + idx_stride * s->idx_buf_of_layer[l];
@@ -300,13 +296,13 @@ csa2_status csa2_sched_decode_step(csa2_sched* s, const csa2_step_io* io, void* 
       }
     }
     if (st == CSA2_OK)
-      st = attn_launch_deferred(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l],
-                                d.swa_fp8 ? kWinE4m3 : kWinBf16, d.swa_max, io->swa_len, d.swa_max,
-                                io->new_swa_row ? io->new_swa_row[l] : nullptr, io->lens, d.sm_scale, io->out[l],
-                                s->attn_ws, s->attn_ws_bytes, &pending, stream);
+      st = attn_launch(io->main_q[l], d.n_seq, io->kv[L.kv_id], 1, idx, d.topk, io->swa[l],
+                       d.swa_fp8 ? kWinE4m3 : kWinBf16, d.swa_max, io->swa_len, d.swa_max,
+                       io->new_swa_row ? io->new_swa_row[l] : nullptr, io->lens, d.sm_scale, io->out[l],
+                       s->attn_ws, stream);
     if (st != CSA2_OK) return st;
   }
-  return attn_flush(&pending, stream);
+  return CSA2_OK;
 }
 
 const int32_t* csa2_sched_indices(const csa2_sched* s, int32_t layer) {

@@ -315,56 +315,6 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
   }
 }
 
-// Merge the chunks of one (head, query) with log-sum-exp weights:
-//   o_h = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
-// One 128-thread workgroup per (head, query), one float4 of the head's 512
-// channels per thread.  The chunks are taken in batches of 16 whose loads
-// (partial O and (m, l), clamped addresses) are all issued together; a
-// running maximum rescales across batches.
-__device__ __forceinline__ void attn_combine_one(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-                                                 int32_t n_split, float* __restrict__ out, int h, int qb, int tid) {
-  const float2* ml = part_ml + (int64_t)qb * n_split * 16 + h;
-  const f32x4* pall = reinterpret_cast<const f32x4*>(part_o + (int64_t)qb * n_split * (16 * CSA2_LATENT) + h * CSA2_LATENT) + tid;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f, Mq = kNegInf;
-  constexpr int kB = 16;
-  for (int c0 = 0; c0 < n_split; c0 += kB) {
-    f32x4 v[kB];
-    float2 m[kB];
-#pragma unroll
-    for (int cb = 0; cb < kB; ++cb) {
-      const int c = min(c0 + cb, n_split - 1);
-      v[cb] = pall[(int64_t)c * (16 * CSA2_LATENT / 4)];
-      m[cb] = ml[c * 16];
-    }
-    float Mb = Mq;
-#pragma unroll
-    for (int cb = 0; cb < kB; ++cb) Mb = fmaxf(Mb, m[cb].x);
-    const float r = (Mq == kNegInf) ? 0.f : exp2f(Mq - Mb);
-    den *= r;
-    acc *= r;
-#pragma unroll
-    for (int cb = 0; cb < kB; ++cb) {
-      const float e = (c0 + cb >= n_split || m[cb].x == kNegInf) ? 0.f : exp2f(m[cb].x - Mb);
-      den += e * m[cb].y;
-      acc += e * v[cb];
-    }
-    Mq = Mb;
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  reinterpret_cast<f32x4*>(out + ((int64_t)qb * 16 + h) * CSA2_LATENT)[tid] = acc * inv;
-}
-
-// A previous attention call's split partials, merged by extra workgroups of
-// the next call's chunk kernel (n_q == 0: none).
-struct AttnCombineJob {
-  const float* part_o;
-  const float2* part_ml;
-  int32_t n_split;
-  float* out;
-  int32_t n_q;
-};
-
 // One workgroup = chunks [split * per_split, ...) of query blockIdx.y.  With
 // one split the workgroup covers the whole query and writes the normalised
 // output; otherwise it writes its unnormalised O and (max, sum) per head
@@ -376,18 +326,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     const int32_t* __restrict__ idx, int32_t k_idx, const uint8_t* swa, int64_t swa_q_stride_rows,
     const int32_t* __restrict__ swa_len, int32_t swa_max, const uint8_t* __restrict__ new_win,
     const int32_t* __restrict__ win_lens, float scale_log2, int32_t per_split, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, int32_t n_split, float* __restrict__ out, int32_t n_q_attn, AttnCombineJob cj) {
+    float2* __restrict__ part_ml, int32_t n_split, float* __restrict__ out) {
   using Cfg = AttnCfg<W>;
   __shared__ __attribute__((aligned(16))) AttnSmem<W> sm;
-  if ((int)blockIdx.y >= n_q_attn) {
-    // Rows past the queries: a previous call's combine riding along (see
-    // attn_launch_deferred), 128 threads per (head, query).
-    constexpr int kPer = 64 * W / 128;
-    const int pair = ((int)(blockIdx.y - n_q_attn) * (int)gridDim.x + (int)blockIdx.x) * kPer + (int)threadIdx.x / 128;
-    if (pair < 16 * cj.n_q)
-      attn_combine_one(cj.part_o, cj.part_ml, cj.n_split, cj.out, pair % 16, pair / 16, threadIdx.x % 128);
-    return;
-  }
   constexpr int kSlices = Cfg::kSlices;
   const int split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,7 +339,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   // when they are consecutive tokens -- share that XCD's L2.
   int qb = blockIdx.y;
   if (gridDim.x == 1) {
-    const int nq = n_q_attn, per = nq / 8, rem = nq % 8;
+    const int nq = gridDim.y, per = nq / 8, rem = nq % 8;
     const int x = blockIdx.y % 8, i = blockIdx.y / 8;
     qb = x * per + min(x, rem) + i;
   }
@@ -502,21 +443,55 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   if (tid < 16) part_ml[((int64_t)qb * n_split + split) * 16 + tid] = make_float2(st.m_run, st.l_run);
 }
 
-// The combine kernel: one 128-thread workgroup per (head, query).
+// Merge the chunks of one (head, query) with log-sum-exp weights:
+//   o_h = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
+// One 128-thread workgroup per (head, query), one float4 of the head's 512
+// channels per thread.  The chunks are taken in batches of 16 whose loads
+// (partial O and (m, l), clamped addresses) are all issued together; a
+// running maximum rescales across batches.
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml,
                                                            int32_t n_split, float* __restrict__ out) {
-  attn_combine_one(part_o, part_ml, n_split, out, blockIdx.x, blockIdx.y, threadIdx.x);
+  const int h = blockIdx.x, qb = blockIdx.y, tid = threadIdx.x;
+  const float2* ml = part_ml + (int64_t)qb * n_split * 16 + h;
+  const f32x4* pall = reinterpret_cast<const f32x4*>(part_o + (int64_t)qb * n_split * (16 * CSA2_LATENT) + h * CSA2_LATENT) + tid;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f, Mq = kNegInf;
+  constexpr int kB = 16;
+  for (int c0 = 0; c0 < n_split; c0 += kB) {
+    f32x4 v[kB];
+    float2 m[kB];
+#pragma unroll
+    for (int cb = 0; cb < kB; ++cb) {
+      const int c = min(c0 + cb, n_split - 1);
+      v[cb] = pall[(int64_t)c * (16 * CSA2_LATENT / 4)];
+      m[cb] = ml[c * 16];
+    }
+    float Mb = Mq;
+#pragma unroll
+    for (int cb = 0; cb < kB; ++cb) Mb = fmaxf(Mb, m[cb].x);
+    const float r = (Mq == kNegInf) ? 0.f : exp2f(Mq - Mb);
+    den *= r;
+    acc *= r;
+#pragma unroll
+    for (int cb = 0; cb < kB; ++cb) {
+      const float e = (c0 + cb >= n_split || m[cb].x == kNegInf) ? 0.f : exp2f(m[cb].x - Mb);
+      den += e * m[cb].y;
+      acc += e * v[cb];
+    }
+    Mq = Mb;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  reinterpret_cast<f32x4*>(out + ((int64_t)qb * 16 + h) * CSA2_LATENT)[tid] = acc * inv;
 }
 
 }  // namespace
 
 // Launch shape: 8-wavefront workgroups (128-row chunks) split over the
 // chunks of each query when there are few queries, so that the chip fills
-// (a combine kernel merges the splits); when there are many, the
-// two-wavefronts-per-query kernel of attn_many.hip, or for the cases it does
-// not take 2-wavefront workgroups (32-row chunks) covering a whole query
-// each (no partials).
+// (a combine kernel merges the splits); 4-wavefront workgroups (64-row
+// chunks, two per CU) covering a whole query each when there are many (no
+// partials).
 struct AttnPlan {
   int waves, splits, per_split;
 };
@@ -550,70 +525,20 @@ csa2_status attn_many_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& 
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
                              float* out, hipStream_t stream);
 
-// cj: a previous call's combine that rides along (cj.n_q == 0: none), on
-// extra rows of the grid past the queries.
 template <int kWin>
 static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, const csa2_fp4_kv& kv,
                           int32_t q_per_seq, const int32_t* idx, int32_t k_idx, const uint8_t* swa,
                           int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                           const uint8_t* new_win, const int32_t* win_lens, float scale_log2, float* part_o,
-                          float2* part_ml, float* out, const AttnCombineJob& cj, hipStream_t stream) {
-  const int per_wg = 64 * p.waves / 128;  // combine (head, query) pairs per workgroup
-  const int cj_wgs = (16 * cj.n_q + per_wg - 1) / per_wg;
-  const int extra_rows = (cj_wgs + p.splits - 1) / p.splits;
+                          float2* part_ml, float* out, hipStream_t stream) {
   if (p.waves == 8)
-    hipLaunchKernelGGL((attn_kernel<8, kWin>), dim3(p.splits, n_q + extra_rows), dim3(64 * 8), 0, stream, q,
-                       kv.codes, kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
-                       new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out, n_q, cj);
+    hipLaunchKernelGGL((attn_kernel<8, kWin>), dim3(p.splits, n_q), dim3(64 * 8), 0, stream, q, kv.codes,
+                       kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+                       new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out);
   else
-    hipLaunchKernelGGL((attn_kernel<2, kWin>), dim3(p.splits, n_q + extra_rows), dim3(64 * 2), 0, stream, q,
-                       kv.codes, kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
-                       new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out, n_q, cj);
-}
-
-// The chunk (and for the many-query kernel, the whole) launch of one call,
-// with a previous call's combine riding along (cj); returns this call's
-// own pending combine in *mine (n_q == 0 when it wrote final outputs).
-static csa2_status attn_chunks_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
-                                      const int32_t* idx, int32_t k_idx, const void* swa, int win,
-                                      int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
-                                      const void* new_win, const int32_t* win_lens, float sm_scale, float* out,
-                                      void* ws, const AttnCombineJob& cj, AttnCombineJob* mine, hipStream_t stream) {
-  const AttnPlan p = attn_plan(n_q, k_idx, swa_max);
-  float* part_o = nullptr;
-  float2* part_ml = nullptr;
-  if (p.splits > 1) {
-    char* base = reinterpret_cast<char*>(ws);
-    part_o = reinterpret_cast<float*>(base);
-    base += (size_t)n_q * p.splits * 16 * CSA2_LATENT * sizeof(float);
-    part_ml = reinterpret_cast<float2*>(base);
-  }
-  *mine = AttnCombineJob{part_o, part_ml, p.splits, out, p.splits > 1 ? n_q : 0};
-  const float scale_log2 = sm_scale * 1.4426950408889634f;
-  const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
-  const uint8_t* nw = reinterpret_cast<const uint8_t*>(new_win);
-  // Many queries over bf16 / f16 window rows with no step window row (the
-  // prefill chunk): the two-wavefronts-per-query kernel of attn_many.hip.
-  if (p.waves == 2 && !new_win && k_idx <= kAttnManyMaxIdx && (win == kWinF16 || win == kWinBf16) && cj.n_q == 0)
-    return attn_many_launch(q, n_q, kv, q_per_seq, idx, k_idx, sw, win, swa_q_stride_rows, swa_len, swa_max,
-                            scale_log2, out, stream);
-  if (win == kWinE4m3)
-    attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                            nw, win_lens, scale_log2, part_o, part_ml, out, cj, stream);
-  else if (win == kWinF16)
-    attn_dispatch<kWinF16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                           nw, win_lens, scale_log2, part_o, part_ml, out, cj, stream);
-  else
-    attn_dispatch<kWinBf16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                            nw, win_lens, scale_log2, part_o, part_ml, out, cj, stream);
-  return launch_status("csa2_sparse_attn");
-}
-
-static csa2_status attn_combine_launch(const AttnCombineJob& j, hipStream_t stream) {
-  if (j.n_q == 0) return CSA2_OK;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(16, j.n_q), dim3(128), 0, stream, j.part_o, j.part_ml, j.n_split,
-                     j.out);
-  return launch_status("csa2_sparse_attn (combine)");
+    hipLaunchKernelGGL((attn_kernel<2, kWin>), dim3(p.splits, n_q), dim3(64 * 2), 0, stream, q, kv.codes,
+                       kv.scales, kv.cap, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max,
+                       new_win, win_lens, scale_log2, p.per_split, part_o, part_ml, p.splits, out);
 }
 
 // win: the window rows' element type -- kWinBf16 (bf16 [*][512], converted
@@ -627,45 +552,35 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
                         int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, const void* new_win,
                         const int32_t* win_lens, float sm_scale, float* out, void* ws, hipStream_t stream) {
   if (n_q == 0) return CSA2_OK;
-  AttnCombineJob mine;
-  const csa2_status st = attn_chunks_launch(q, n_q, kv, q_per_seq, idx, k_idx, swa, win, swa_q_stride_rows, swa_len,
-                                            swa_max, new_win, win_lens, sm_scale, out, ws, AttnCombineJob{}, &mine,
-                                            stream);
-  return st == CSA2_OK ? attn_combine_launch(mine, stream) : st;
-}
-
-// Attention for a sequence of calls on one stream (a decode step's layers):
-// each call's combine is left pending and merged by extra workgroups of the
-// next call's chunk launch, which runs beside that call's chunk workgroups
-// on the CUs they leave free, instead of in a launch of its own; attn_flush
-// merges the last one.  ws holds two partial sets of attn_workspace_bytes
-// each, which consecutive calls alternate between.
-csa2_status attn_launch_deferred(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
-                                 const int32_t* idx, int32_t k_idx, const void* swa, int win,
-                                 int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
-                                 const void* new_win, const int32_t* win_lens, float sm_scale, float* out, void* ws2,
-                                 size_t ws_half, AttnPending* pending, hipStream_t stream) {
-  if (n_q == 0) return CSA2_OK;
-  void* ws = reinterpret_cast<char*>(ws2) + (pending->parity ? ws_half : 0);
-  AttnCombineJob prev{pending->part_o, pending->part_ml, pending->n_split, pending->out, pending->n_q};
-  AttnCombineJob mine;
-  const csa2_status st = attn_chunks_launch(q, n_q, kv, q_per_seq, idx, k_idx, swa, win, swa_q_stride_rows,
-                                            swa_len, swa_max, new_win, win_lens, sm_scale, out, ws, prev, &mine,
-                                            stream);
-  if (st != CSA2_OK) return st;
-  pending->part_o = mine.part_o;
-  pending->part_ml = mine.part_ml;
-  pending->n_split = mine.n_split;
-  pending->out = mine.out;
-  pending->n_q = mine.n_q;
-  pending->parity ^= 1;
-  return CSA2_OK;
-}
-
-csa2_status attn_flush(AttnPending* pending, hipStream_t stream) {
-  const AttnCombineJob j{pending->part_o, pending->part_ml, pending->n_split, pending->out, pending->n_q};
-  pending->n_q = 0;
-  return attn_combine_launch(j, stream);
+  const AttnPlan p = attn_plan(n_q, k_idx, swa_max);
+  float* part_o = nullptr;
+  float2* part_ml = nullptr;
+  if (p.splits > 1) {
+    char* base = reinterpret_cast<char*>(ws);
+    part_o = reinterpret_cast<float*>(base);
+    base += (size_t)n_q * p.splits * 16 * CSA2_LATENT * sizeof(float);
+    part_ml = reinterpret_cast<float2*>(base);
+  }
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
+  const uint8_t* nw = reinterpret_cast<const uint8_t*>(new_win);
+  // Many queries over bf16 / f16 window rows with no step window row (the
+  // prefill chunk): the two-wavefronts-per-query kernel of attn_many.hip.
+  if (p.waves == 2 && !new_win && k_idx <= kAttnManyMaxIdx && (win == kWinF16 || win == kWinBf16))
+    return attn_many_launch(q, n_q, kv, q_per_seq, idx, k_idx, sw, win, swa_q_stride_rows, swa_len, swa_max,
+                            scale_log2, out, stream);
+  if (win == kWinE4m3)
+    attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                            nw, win_lens, scale_log2, part_o, part_ml, out, stream);
+  else if (win == kWinF16)
+    attn_dispatch<kWinF16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                           nw, win_lens, scale_log2, part_o, part_ml, out, stream);
+  else
+    attn_dispatch<kWinBf16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
+                            nw, win_lens, scale_log2, part_o, part_ml, out, stream);
+  if (p.splits > 1)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, p.splits, out);
+  return launch_status("csa2_sparse_attn");
 }
 
 // ------------------------------------------------- static scratch
