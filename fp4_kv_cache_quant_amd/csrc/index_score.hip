@@ -204,37 +204,83 @@ void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const float* w
 // t0 + i) against the keys of compressed entries, entry e visible to query i
 // iff e < vis_i = min(n_entries, (t0 + i + 1) / ratio).  This is a dense
 // contraction of (query, head) rows with entry keys, so both MFMA operands
-// carry real data: a 256-thread workgroup takes 32 queries (256 rows = 16
-// row tiles of 2 queries x 8 heads) against 512 entries (128 per
-// wavefront = 8 column tiles).  Each wavefront holds its entries' key
-// fragments in registers and walks the 16 row tiles, whose query fragments
-// come from LDS; per row tile the output lane holds heads 4(g%2)..+3 of
-// query 2*tile + g/2, so the same per-lane ReLU sum and one exchange
-// (xor 16) as the decode kernel give the score.  Scores go out through a
-// per-wavefront LDS transpose as two 512-byte rows.
+// carry real data: a 256-thread workgroup takes 32 queries against 512
+// entries (128 per wavefront = 8 column tiles of 16).  Each wavefront holds
+// its entries' key fragments in registers and walks 8 groups of 4 queries,
+// whose query fragments come from LDS.  A group takes two row tiles per
+// column tile, rows 4i + h = (query i of the group, head h) and (query i,
+// head 4 + h), so that output lane (n, g) of the two products holds all 8
+// heads of query g and entry n: the ReLU sum over heads is local to the
+// lane, and the 64 lanes hold 64 different scores.  What happens to a score
+// depends on the mode:
+//   kPfAll      every score goes out (-inf past the query's visible entries);
+//   kPfSampled  the block is the 1,024 entries a row's threshold estimate
+//               reads (64 runs of 16, one at the start of each 64th of the
+//               entries; grid.x = 2; a column tile is one run) and only
+//               their scores go out;
+//   kPfCand     only the scores at or above the query's threshold (and
+//               inside its visible entries) go out, as (score bits, entry)
+//               pairs into the query's list for the workgroup's 512
+//               entries, each at a position taken from the query's LDS
+//               counter, and the count -- so the score matrix never reaches
+//               memory;
+//   kPfRescore  kPfAll for query blocks holding a row that the selection
+//               over the candidates could not take, up to the last visible
+//               entry of the block.
 constexpr int kPfQ = 32;          // queries per workgroup
 constexpr int kPfE = 512;         // entries per workgroup
 constexpr int kPfCols = kPfE / (4 * 16);  // column tiles per wavefront (8)
+constexpr int kPfAll = 0, kPfSampled = 1, kPfCand = 2, kPfRescore = 3;
+static_assert(kPfE == kCandBlock, "one candidate list per query and workgroup");
 
-template <bool kWeights>
-__global__ __launch_bounds__(256) void prefill_score_kernel(
+// Weighted ReLU sum of the 8 heads, head 0 first, each product and sum
+// rounded on its own; ReLU as in relu_wsum4.
+__device__ __forceinline__ float relu_wsum8(const f32x4& lo, const f32x4& hi, const float* wh) {
+#pragma clang fp contract(off)
+  float inf = __builtin_inff();
+  asm("" : "+s"(inf));
+  float sum = wh[0] * __builtin_amdgcn_fmed3f(lo[0], 0.f, inf);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) sum = sum + wh[r] * __builtin_amdgcn_fmed3f(lo[r], 0.f, inf);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sum = sum + wh[4 + r] * __builtin_amdgcn_fmed3f(hi[r], 0.f, inf);
+  return sum;
+}
+
+// Four workgroups per CU (32 KB of LDS each): at most 128 registers.
+template <bool kWeights, int kMode>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void prefill_score_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ keys,
     int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q, float* __restrict__ scores,
-    int32_t* __restrict__ n_vis, int32_t* __restrict__ win_len, int32_t win) {
+    int32_t* __restrict__ n_vis, int32_t* __restrict__ win_len, int32_t win, PrefillCandOut co) {
   __shared__ __attribute__((aligned(16))) uint16_t qs[kPfQ * 8 * 64];   // [query*8 + head][dim]
-  __shared__ __attribute__((aligned(16))) float stage[4][2 * 128];      // per wavefront [2][128]
   __shared__ int32_t vis_s[kPfQ];                                       // visible entries per query
+  __shared__ float thr_s[kPfQ];                                         // candidate threshold per query
+  __shared__ uint32_t cnt_s[kPfQ];                                      // candidates per query
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t q0 = (int64_t)blockIdx.y * kPfQ;
-  const int64_t e_w = (int64_t)blockIdx.x * kPfE + wave * 128;  // this wavefront's first entry
+  if constexpr (kMode == kPfRescore) {
+    // Visible counts grow with the query, so the block's last query sees
+    // the most entries.
+    const int64_t vis_last = min(n_entries, (t0 + min(q0 + kPfQ, (int64_t)n_q)) / ratio);
+    if (co.flags[blockIdx.y] == 0u || (int64_t)blockIdx.x * kPfE >= vis_last) return;  // uniform
+  }
+  const int64_t e_w = (int64_t)blockIdx.x * kPfE + wave * 128;  // this wavefront's first position
+  // Entry of position v of the block's entry range: v itself, or for the
+  // sampled block the v-th sampled entry (n_entries >= 1,024: the runs
+  // are disjoint and inside the range).
+  const int64_t run = n_entries >> 6;
+  auto entry_of = [&](int64_t v) -> int64_t {
+    return kMode == kPfSampled ? (v >> 4) * run + (v & 15) : v;
+  };
 
   // Key fragments of the wavefront's 8 column tiles (clamped rows; entries
   // past n_entries are never stored).
   u32x4 kf[kPfCols][2];
 #pragma unroll
   for (int c = 0; c < kPfCols; ++c) {
-    const int64_t e = min(e_w + 16 * c + n, n_entries - 1);
+    const int64_t e = min(entry_of(e_w + 16 * c + n), n_entries - 1);
     const u32x4* kp = reinterpret_cast<const u32x4*>(keys + e * 64 + 16 * g);
     kf[c][0] = kp[0];
     kf[c][1] = kp[1];
@@ -255,58 +301,70 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       if (n_vis) n_vis[q0 + tid] = vis;
       if (win_len) win_len[q0 + tid] = (int32_t)min((int64_t)win, t + 1);  // tokens max(0, t-win+1) .. t
     }
+    if constexpr (kMode == kPfCand) {
+      thr_s[tid] = q0 + tid < n_q ? key_threshold(co.thr[(q0 + tid) * co.thr_stride]) : __builtin_nanf("");
+      cnt_s[tid] = 0u;
+    }
   }
+  if constexpr (kMode == kPfCand)
+    if (blockIdx.x == 0 && tid == 0) co.flags[blockIdx.y] = 0u;
   __syncthreads();
 
-  // Entry indices fit in 32 bits (n_entries < 2^31); the store pointer of
-  // this lane advances by two query rows per row tile.
-  float* st = stage[wave];
-  const bool vec_ok = (n_entries & 3) == 0;
-  const int e_lane = (int)e_w + n;                    // entry of column tile 0 for this lane
-  const int eo = (int)e_w + 4 * (lane & 31);           // first entry this lane stores
+  // Entry of column tile c for this lane: e0 + 16 * c (a sampled tile is
+  // one run: run apart).  Entries fit in 32 bits (n_entries <= 2^30).
+  const int e0 = (int)entry_of(e_w + n);
+  const int e_step = kMode == kPfSampled ? (int)run : 16;
   const int ne = (int)n_entries;
-  const bool store_vec = vec_ok && eo + 3 < ne;
-  const int q_left = (int)min<int64_t>(n_q - q0, kPfQ) - (lane >> 5);  // rows this lane may store: 2rt < q_left
-  float* dst = scores + (q0 + (lane >> 5)) * n_entries + eo;
+  const int64_t list_pitch = (int64_t)co.n_blocks * kCandCap;
 #pragma unroll 1
-  for (int rt = 0; rt < kPfQ / 2; ++rt) {
-    // Row m = n of this tile: query 2rt + n/8, head n%8, dims 16g..16g+15.
-    const u32x4* ap = reinterpret_cast<const u32x4*>(&qs[((2 * rt) * 8 + n) * 64 + 16 * g]);
-    const bf16x8 a0 = as_bf16x8(ap[0]), a1 = as_bf16x8(ap[1]);
-    float wh[4] = {1.f, 1.f, 1.f, 1.f};
+  for (int qg = 0; qg < kPfQ / 4; ++qg) {
+    // Row m = n of the two row tiles: query 4qg + n/4, heads n%4 and 4 + n%4,
+    // dims 16g..16g+15.
+    const uint16_t* ar = &qs[((4 * qg + (n >> 2)) * 8 + (n & 3)) * 64 + 16 * g];
+    const bf16x8 a0 = as_bf16x8(reinterpret_cast<const u32x4*>(ar)[0]);
+    const bf16x8 a1 = as_bf16x8(reinterpret_cast<const u32x4*>(ar)[1]);
+    const bf16x8 b0 = as_bf16x8(reinterpret_cast<const u32x4*>(ar + 4 * 64)[0]);
+    const bf16x8 b1 = as_bf16x8(reinterpret_cast<const u32x4*>(ar + 4 * 64)[1]);
+    const int qi = 4 * qg + g;                 // this lane's query within the block
+    const int64_t qrow = q0 + qi;
+    float wh[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     if (kWeights) {
-      const int64_t qc = min(q0 + 2 * rt + (g >> 1), (int64_t)n_q - 1);  // query of this lane's output rows
+      const int64_t qc = min(qrow, (int64_t)n_q - 1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wh[r] = w[qc * 8 + 4 * (g & 1) + r];
+      for (int r = 0; r < 8; ++r) wh[r] = w[qc * 8 + r];
     }
-    const int vis = vis_s[2 * rt + (g >> 1)];
+    const int vis = vis_s[qi];
+    float t = 0.f;
+    uint2* ldst = nullptr;
+    if constexpr (kMode == kPfCand) {
+      t = thr_s[qi];  // NaN: no estimate, or a row past n_q -- admits nothing
+      ldst = co.cand + qrow * list_pitch + (int64_t)blockIdx.x * kCandCap;
+    }
+    const bool row_ok = qrow < n_q;
+    float* dst = scores + qrow * n_entries;
 #pragma unroll
     for (int c = 0; c < kPfCols; ++c) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16x16x32(a0, as_bf16x8(kf[c][0]), acc);
-      acc = mfma16x16x32(a1, as_bf16x8(kf[c][1]), acc);
-      const float part = relu_wsum4(acc, wh);       // heads 4(g%2)..+3
-      const float score = fold16_add(part);  // lo + hi
-      // Lanes g and g^1 hold the same sum (the fold adds the two halves in
-      // either order) and write it to the same address; with no lane
-      // condition the column tiles form one block whose MFMAs and epilogues
-      // the compiler interleaves.
-      st[(g >> 1) * 128 + 16 * c + n] = (e_lane + 16 * c < vis) ? score : kNegInf;
-    }
-    __builtin_amdgcn_wave_barrier();
-    // Two rows of 128 scores: lane l stores query 2rt + l/32, entries 4(l%32)..+3.
-    const f32x4 v = *reinterpret_cast<const f32x4*>(&st[(lane >> 5) * 128 + 4 * (lane & 31)]);
-    if (2 * rt < q_left) {
-      if (store_vec) {
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+      lo = mfma16x16x32(a0, as_bf16x8(kf[c][0]), lo);
+      hi = mfma16x16x32(b0, as_bf16x8(kf[c][0]), hi);
+      lo = mfma16x16x32(a1, as_bf16x8(kf[c][1]), lo);
+      hi = mfma16x16x32(b1, as_bf16x8(kf[c][1]), hi);
+      const float score = relu_wsum8(lo, hi, wh);
+      const int e = e0 + e_step * c;
+      if constexpr (kMode == kPfCand) {
+        if (score >= t && e < vis) {
+          const uint32_t pos = atomicAdd(&cnt_s[qi], 1u);
+          if (pos < (uint32_t)kCandCap) ldst[pos] = make_uint2(__builtin_bit_cast(uint32_t, score), (uint32_t)e);
+        }
       } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (eo + j < ne) dst[j] = v[j];
+        // 16 lanes store 16 consecutive entries of one query.
+        if (row_ok && e < ne) __builtin_nontemporal_store(e < vis ? score : kNegInf, dst + e);
       }
     }
-    dst += 2 * n_entries;
-    __builtin_amdgcn_wave_barrier();
+  }
+  if constexpr (kMode == kPfCand) {
+    __syncthreads();
+    if (tid < kPfQ && q0 + tid < n_q) co.cnt[(q0 + tid) * co.n_blocks + blockIdx.x] = cnt_s[tid];
   }
 }
 
@@ -539,20 +597,59 @@ csa2_status index_score_local_launch(const uint16_t* q, const float* w, const ui
   return launch_status("csa2_index_score (local selection)");
 }
 
+namespace {
+
+template <int kMode>
+void prefill_launch_mode(dim3 grid, hipStream_t stream, const uint16_t* q, const float* w, const uint16_t* keys,
+                         int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q, float* scores, int32_t* n_vis,
+                         int32_t* win_len, int32_t win, const PrefillCandOut& co) {
+  if (w)
+    hipLaunchKernelGGL((prefill_score_kernel<true, kMode>), grid, dim3(256), 0, stream, q, w, keys, n_entries, t0,
+                       ratio, n_q, scores, n_vis, win_len, win, co);
+  else
+    hipLaunchKernelGGL((prefill_score_kernel<false, kMode>), grid, dim3(256), 0, stream, q, w, keys, n_entries,
+                       t0, ratio, n_q, scores, n_vis, win_len, win, co);
+}
+
+}  // namespace
+
 csa2_status prefill_score_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t n_entries,
                                  int64_t t0, int32_t ratio, int32_t n_q, float* scores, int32_t* n_vis,
                                  int32_t* win_len, int32_t win, hipStream_t stream) {
   if (n_q == 0 || n_entries == 0) return CSA2_OK;
   const int64_t gx = (n_entries + kPfE - 1) / kPfE, gy = (n_q + kPfQ - 1) / kPfQ;
   CSA2_REQUIRE(gy <= 65535, CSA2_ESHAPE, "csa2_prefill_index_score: too many queries");
-  const dim3 grid((uint32_t)gx, (uint32_t)gy);
-  if (w)
-    hipLaunchKernelGGL(prefill_score_kernel<true>, grid, dim3(256), 0, stream, q, w, keys, n_entries, t0,
-                       ratio, n_q, scores, n_vis, win_len, win);
-  else
-    hipLaunchKernelGGL(prefill_score_kernel<false>, grid, dim3(256), 0, stream, q, w, keys, n_entries, t0,
-                       ratio, n_q, scores, n_vis, win_len, win);
+  prefill_launch_mode<kPfAll>(dim3((uint32_t)gx, (uint32_t)gy), stream, q, w, keys, n_entries, t0, ratio, n_q,
+                              scores, n_vis, win_len, win, PrefillCandOut{});
   return launch_status("csa2_prefill_index_score");
+}
+
+// The scoring passes of a prefill selection filtered while scoring:
+// stage 0 scores the sampled entries (and writes n_vis and win_len),
+// stage 1 writes the candidates at or above co.thr, stage 2 rescores the
+// query blocks flagged in co.flags.  1,024 <= n_entries <= kTopkRowsMax.
+csa2_status prefill_filter_launch(int stage, const uint16_t* q, const float* w, const uint16_t* keys,
+                                  int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q, float* scores,
+                                  int32_t* n_vis, int32_t* win_len, int32_t win, const PrefillCandOut& co,
+                                  hipStream_t stream) {
+  if (n_q == 0) return CSA2_OK;
+  CSA2_REQUIRE(n_entries >= 1024 && n_entries <= kTopkRowsMax && (n_q + kPfQ - 1) / kPfQ <= 65535, CSA2_ESHAPE,
+               "prefill selection: need 1,024 <= n_entries <= 65,536 and fewer than 2^21 queries");
+  CSA2_REQUIRE(stage == 0 || (co.cnt && co.cand && co.flags && co.n_blocks == (n_entries + kPfE - 1) / kPfE &&
+                              (stage == 2 || co.thr)),
+               CSA2_EINVAL, "prefill selection: candidate buffers missing");
+  const uint32_t gy = (uint32_t)((n_q + kPfQ - 1) / kPfQ);
+  const uint32_t gx = (uint32_t)((n_entries + kPfE - 1) / kPfE);
+  if (stage == 0)
+    prefill_launch_mode<kPfSampled>(dim3(1024 / kPfE, gy), stream, q, w, keys, n_entries, t0, ratio, n_q, scores,
+                                    n_vis, win_len, win, co);
+  else if (stage == 1)
+    prefill_launch_mode<kPfCand>(dim3(gx, gy), stream, q, w, keys, n_entries, t0, ratio, n_q, scores, nullptr,
+                                 nullptr, win, co);
+  else
+    prefill_launch_mode<kPfRescore>(dim3(gx, gy), stream, q, w, keys, n_entries, t0, ratio, n_q, scores, nullptr,
+                                    nullptr, win, co);
+  return launch_status("csa2_prefill_chunk (indexer scores)");
 }
 
 }  // namespace csa2

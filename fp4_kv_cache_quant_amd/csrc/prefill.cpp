@@ -19,6 +19,8 @@ namespace csa2 {
 
 csa2_status prefill_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, int64_t, int32_t,
                                  int32_t, float*, int32_t*, int32_t*, int32_t, hipStream_t);
+csa2_status prefill_filter_launch(int, const uint16_t*, const float*, const uint16_t*, int64_t, int64_t, int32_t,
+                                  int32_t, float*, int32_t*, int32_t*, int32_t, const PrefillCandOut&, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
@@ -34,7 +36,11 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Workspace layout: scores [n_q][n_entries] f32 | n_vis [n_q] | win_len
 // [n_q] | Top-k workspace | attention workspace | the layer's window rows
 // as f16 [n_q + swa - 1][512] (each row serves up to swa queries, so it is
-// converted once per layer instead of once per query).
+// converted once per layer instead of once per query) | when the selection
+// is filtered while scoring (prefill_filter_applies): candidate lists
+// [n_q][blocks][kCandCap] (score bits, entry), their counts [n_q][blocks]
+// u32 and the flags of the query blocks to rescore [ceil(n_q / 32)] u32
+// (blocks = ceil(n_entries / kCandBlock)).
 struct PrefillWs {
   float* scores;
   int32_t* n_vis;
@@ -42,6 +48,8 @@ struct PrefillWs {
   void* topk;
   void* attn;
   uint16_t* win16;
+  bool filtered;
+  PrefillCandOut co;
   size_t bytes;
 };
 
@@ -61,6 +69,17 @@ PrefillWs prefill_ws_layout(const csa2_prefill_desc& d, void* base) {
   off += align_up(attn_workspace_bytes(d.n_q, d.topk, d.swa));
   w.win16 = reinterpret_cast<uint16_t*>(p + off);
   off += align_up(((size_t)d.n_q + d.swa - 1) * CSA2_LATENT * sizeof(uint16_t));
+  w.filtered = prefill_filter_applies(d.n_entries, d.n_q, d.topk);
+  if (w.filtered) {
+    const int32_t blocks = (int32_t)((d.n_entries + kCandBlock - 1) / kCandBlock);
+    w.co.n_blocks = blocks;
+    w.co.cand = reinterpret_cast<uint2*>(p + off);
+    off += align_up((size_t)d.n_q * blocks * kCandCap * sizeof(uint2));
+    w.co.cnt = reinterpret_cast<uint32_t*>(p + off);
+    off += align_up((size_t)d.n_q * blocks * sizeof(uint32_t));
+    w.co.flags = reinterpret_cast<uint32_t*>(p + off);
+    off += align_up((size_t)(d.n_q + 31) / 32 * sizeof(uint32_t));
+  }
   w.bytes = off;
   return w;
 }
@@ -171,11 +190,27 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
     if (L.mode != CSA2_REUSE) {
       // Full and Reindex both score every visible entry with their own Q.
       const float* wq = io->idx_w ? io->idx_w[l] : nullptr;
-      st = prefill_score_launch(io->idx_q[l], wq, io->entry_k, d.n_entries, d.t0, d.ratio, d.n_q, w.scores,
-                                w.n_vis, w.win_len, d.swa, stream);
-      if (st == CSA2_OK)
-        st = topk_launch(w.scores, d.n_entries, w.n_vis, 1, d.topk, nullptr, 0, 1, io->idx[l], tw, false, d.n_q,
-                         stream);
+      if (w.filtered) {
+        // Sampled scores -> thresholds -> candidates -> selection among
+        // them; the rows that selection cannot take are scored again in
+        // full (their whole query blocks) and selected over all entries.
+        PrefillCandOut co = w.co;
+        co.thr = tw.wcnt + kThresholdSlot;
+        co.thr_stride = kTopkFilterWgMax;
+        for (int stage = 0; stage < 3 && st == CSA2_OK; ++stage) {
+          st = prefill_filter_launch(stage, io->idx_q[l], wq, io->entry_k, d.n_entries, d.t0, d.ratio, d.n_q,
+                                     w.scores, w.n_vis, w.win_len, d.swa, co, stream);
+          if (st == CSA2_OK)
+            st = prefill_select_launch(stage, w.scores, d.n_entries, w.n_vis, d.topk, io->idx[l], tw, co, d.n_q,
+                                       stream);
+        }
+      } else {
+        st = prefill_score_launch(io->idx_q[l], wq, io->entry_k, d.n_entries, d.t0, d.ratio, d.n_q, w.scores,
+                                  w.n_vis, w.win_len, d.swa, stream);
+        if (st == CSA2_OK)
+          st = topk_launch(w.scores, d.n_entries, w.n_vis, 1, d.topk, nullptr, 0, 1, io->idx[l], tw, false, d.n_q,
+                           stream);
+      }
       if (st != CSA2_OK) return st;
       cur = io->idx[l];
     }

@@ -203,8 +203,6 @@ __global__ __launch_bounds__(kPassThreads) void topk_filter_kernel(const float* 
 // The row's threshold is kept in the last entry of its wcnt row, which
 // filters of at most kTopkRowsMax slots never use.
 constexpr int kSamples = 1024;
-constexpr uint32_t kNoEstimate = 0xFFFFFFFFu;
-constexpr int kThresholdSlot = kTopkFilterWgMax - 1;
 static_assert(kTopkRowsMax / kTopkFilterSlots < kThresholdSlot, "threshold slot unused by the filter regions");
 // Slots of the wcnt rows no filter region uses (at most 8 per row here):
 // entry i of the list of rows left to the fallback sits in row i's
@@ -286,16 +284,6 @@ __global__ __launch_bounds__(kPassThreads) void topk_sample_kernel(const float* 
   }
   if (tid == 0) ws.wcnt[(int64_t)b * kTopkFilterWgMax + kThresholdSlot] = lo;
   if (b == 0 && tid == 0) ws.wcnt[kCountSlot] = ws.wcnt[kClaimSlot] = 0u;
-}
-
-// The smallest score whose order key is >= lo, for a threshold key lo that
-// is 0, a key of a non-NaN score, or kNoEstimate: key(x) >= lo and
-// key(x) != 0 hold exactly when x >= key_threshold(lo) (-0 and +0 share a
-// key and compare equal; lo = 0 admits every score but NaN and -inf; the
-// NaN for kNoEstimate admits none).
-__device__ __forceinline__ float key_threshold(uint32_t lo) {
-  if (lo == 0) return -__FLT_MAX__;
-  return __builtin_bit_cast(float, (lo & 0x80000000u) ? (lo & 0x7FFFFFFFu) : ~lo);
 }
 
 // kVec: rows start 16-byte aligned (n % 4 == 0, aligned scores), so each
@@ -1080,6 +1068,7 @@ struct LeanSmem {
   uint32_t scan_sum[4][kLeanThreads / 64];
   uint32_t fin_sum[2 * kLeanThreads / 64];
   uint32_t found[2];
+  uint32_t reg_off[kLeanThreads];  // first candidate of each region (topk_region_select_kernel)
 };
 static_assert(sizeof(LeanSmem) <= 80 * 1024, "two workgroups per CU");
 
@@ -1154,10 +1143,90 @@ __global__ __launch_bounds__(kLeanThreads, 2) void topk_cand_select_kernel(int64
   finish_output_lds<kLeanThreads>(sm.sel, sm.tie, words, ties, kk, nullptr, 1, sm.fin_sum, out + (int64_t)b * k);
 }
 
-// The rows topk_cand_select_kernel left, by the selection among up to
-// 8,192 candidates (else the full passes over the row): a grid of one
-// workgroup per CU claims the listed rows one by one until the list is
-// exhausted.
+// Many rows filtered while they were scored (PrefillCandOut; k <= kLeanK,
+// no pool): the selection among each row's candidates, one workgroup per
+// row as in topk_cand_select_kernel, with thread t taking the count of
+// block t (at most kLeanThreads blocks).  A row it cannot take (no
+// estimate, a block list that overflowed, fewer than k or more than
+// kLeanCand candidates) is listed for topk_rows_flagged_kernel<false> and
+// flagged in co.flags, so that its whole score row is written again first.
+__global__ __launch_bounds__(kLeanThreads, 2) void topk_region_select_kernel(int64_t n,
+                                                                           const int32_t* __restrict__ lens,
+                                                                           int32_t k, int32_t* __restrict__ out,
+                                                                           PrefillCandOut co,
+                                                                           uint32_t* __restrict__ wcnt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  LeanSmem& sm = *reinterpret_cast<LeanSmem*>(smem_raw);
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvalid = (int)valid_slots(n, lens, 1, b);
+  const int words = (nvalid + 31) / 32;
+  const uint32_t kk = (uint32_t)k;
+  const int nb = co.n_blocks;
+  const uint32_t lo = wcnt[(int64_t)b * kTopkFilterWgMax + kThresholdSlot];
+  const uint32_t cnt = tid < nb ? co.cnt[(int64_t)b * nb + tid] : 0u;
+  uint32_t total;
+  const uint32_t off = block_exclusive_scan<kLeanThreads>(cnt, sm.scan_sum[0], &total);
+  const bool over = __syncthreads_or(cnt > (uint32_t)kCandCap);
+  if (over || lo == kNoEstimate || total < kk || total > (uint32_t)kLeanCand) {  // uniform over the workgroup
+    if (tid == 0) {
+      const uint32_t pos = atomicAdd(&wcnt[kCountSlot], 1u);
+      wcnt[(int64_t)pos * kTopkFilterWgMax + kFallbackSlot] = (uint32_t)b;
+      atomicOr(&co.flags[b >> 5], 1u << (b & 31));
+    }
+    return;
+  }
+  sm.reg_off[tid] = off;
+  for (int i = tid; i < kTopkBins; i += kLeanThreads) sm.hist1[i] = sm.hist2[i] = 0;
+  if (tid < 256) sm.hist3[tid] = 0;
+  for (int i = tid; i < words; i += kLeanThreads) sm.sel[i] = sm.tie[i] = 0;
+  __syncthreads();
+  // Candidate c of the concatenated lists lies in the last block whose
+  // first candidate is <= c (blocks before it that hold none share its
+  // offset; those after it start past c).  All of a thread's loads go out
+  // together (clamped to the last candidate).
+  const uint2* cb = co.cand + (int64_t)b * nb * kCandCap;
+  constexpr int kCandPer = kLeanCand / kLeanThreads;
+  uint2 e[kCandPer];
+#pragma unroll
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint32_t c = min(tid + j * kLeanThreads, total - 1u);
+    int r = 0;
+#pragma unroll
+    for (int step = kRowsMax / kCandBlock / 2; step > 0; step >>= 1)
+      if (r + step < nb && sm.reg_off[r + step] <= c) r += step;
+    e[j] = cb[r * kCandCap + (int)(c - sm.reg_off[r])];
+  }
+#pragma unroll
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint32_t c = tid + j * kLeanThreads;
+    if (c < total) {
+      const uint32_t bits = e[j].x;
+      const uint32_t key = order_key(__builtin_bit_cast(float, bits));
+      sm.cand_key[c] = key;
+      sm.cand_slot[c] = e[j].y;
+      atomicAdd(&sm.hist1[key >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t T, ties;
+  select_candidates<kLeanThreads>(sm.cand_key, (int)total, kk, sm.hist1, sm.hist2, sm.hist3, sm.scan_sum, sm.found,
+                                  T, ties);
+  for (int c = tid; c < (int)total; c += kLeanThreads) {
+    const uint32_t key = sm.cand_key[c], i = sm.cand_slot[c];
+    if (key > T) atomicOr(&sm.sel[i >> 5], 1u << (i & 31));
+    else if (key == T) atomicOr(&sm.tie[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  finish_output_lds<kLeanThreads>(sm.sel, sm.tie, words, ties, kk, nullptr, 1, sm.fin_sum, out + (int64_t)b * k);
+}
+
+// The rows topk_cand_select_kernel or topk_region_select_kernel left: a
+// grid of one workgroup per CU claims the listed rows one by one until the
+// list is exhausted.  kCandIn: first the selection among up to 8,192 of the
+// row's filter candidates, else (and without kCandIn) the full passes over
+// the row's scores.
+template <bool kCandIn>
 __global__ __launch_bounds__(kFinalThreads) void topk_rows_flagged_kernel(const float* __restrict__ scores, int64_t n,
                                                                           const int32_t* __restrict__ lens,
                                                                           int32_t len_div, int32_t k,
@@ -1175,7 +1244,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_rows_flagged_kernel(const 
     __syncthreads();
     if (i >= count) break;  // uniform
     const int b = (int)wcnt[(int64_t)i * kTopkFilterWgMax + kFallbackSlot];
-    rows_select<64, true>(sm, b, scores, n, lens, len_div, k, nullptr, 0, 1, out, nullptr, cand_in, wcnt);
+    rows_select<64, kCandIn>(sm, b, scores, n, lens, len_div, k, nullptr, 0, 1, out, nullptr, cand_in, wcnt);
     __syncthreads();  // LDS is reused by the next row
   }
 }
@@ -1427,7 +1496,7 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_kernel<64, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_flagged_kernel),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_flagged_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(topk_cand_select_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(LeanSmem)) != hipSuccess ||
@@ -1451,7 +1520,7 @@ csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int
     if (k <= kLeanK && !pool && !gids) {
       hipLaunchKernelGGL(topk_cand_select_kernel, dim3(n_seq), dim3(kLeanThreads), sizeof(LeanSmem), stream, n, lens,
                          len_div, k, out, ws.cand, ws.wcnt);
-      hipLaunchKernelGGL(topk_rows_flagged_kernel, dim3(std::min(n_seq, kFlaggedGrid)), dim3(kFinalThreads),
+      hipLaunchKernelGGL(topk_rows_flagged_kernel<true>, dim3(std::min(n_seq, kFlaggedGrid)), dim3(kFinalThreads),
                          sizeof(RowsSmem), stream, scores, n, lens, len_div, k, out, ws.cand, ws.wcnt);
     } else {
       hipLaunchKernelGGL((topk_rows_kernel<64, true>), dim3(n_seq), dim3(kFinalThreads), sizeof(RowsSmem), stream,
@@ -1505,6 +1574,46 @@ csa2_status pool_select_launch(const float* scores, int64_t n, int32_t k, const 
   hipLaunchKernelGGL(pool_select_kernel, dim3(n_seq), dim3(kPoolSelThreads), sizeof(PoolSmem), stream, scores,
                      (int32_t)n, k, pool, n_pool, blk, static_cast<const uint32_t*>(ws.bound), out);
   return launch_status("pool selection");
+}
+
+// Whether a prefill chunk's rows (n slots each, n_rows of them, Top-k) are
+// selected from candidates filtered while they are scored: the shapes that
+// the many-row selection takes, with k <= kLeanK.
+bool prefill_filter_applies(int64_t n, int32_t n_rows, int32_t k) {
+  return n > 32 * kFinalThreads && n <= kRowsMax && n_rows >= kManyRows && k <= kLeanK;
+}
+
+// The selection of many rows filtered while they are scored
+// (prefill_filter_applies; lens = the rows' visible counts): stage 0 takes
+// each row's threshold estimate from its sampled scores, stage 1 selects
+// among each row's candidates (co) and lists and flags the rows it cannot
+// take, stage 2 runs the full selection of the listed rows over their
+// rescored rows.
+csa2_status prefill_select_launch(int stage, const float* scores, int64_t n, const int32_t* lens, int32_t k,
+                                  int32_t* out, const TopkWs& ws, const PrefillCandOut& co, int32_t n_rows,
+                                  hipStream_t stream) {
+  if (n_rows == 0) return CSA2_OK;
+  CSA2_REQUIRE(prefill_filter_applies(n, n_rows, k) && co.n_blocks == (n + kCandBlock - 1) / kCandBlock &&
+                   co.n_blocks <= kLeanThreads,
+               CSA2_ESHAPE, "prefill selection: bad shape");
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_region_select_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(LeanSmem)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(topk_rows_flagged_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RowsSmem)) != hipSuccess)
+      return launch_status("prefill selection (shared memory attribute)");
+    attr_set = true;
+  }
+  if (stage == 0)
+    hipLaunchKernelGGL(topk_sample_kernel, dim3(n_rows), dim3(kPassThreads), 0, stream, scores, n, lens, 1, k, ws);
+  else if (stage == 1)
+    hipLaunchKernelGGL(topk_region_select_kernel, dim3(n_rows), dim3(kLeanThreads), sizeof(LeanSmem), stream, n,
+                       lens, k, out, co, ws.wcnt);
+  else
+    hipLaunchKernelGGL(topk_rows_flagged_kernel<false>, dim3(std::min(n_rows, kFlaggedGrid)), dim3(kFinalThreads),
+                       sizeof(RowsSmem), stream, scores, n, lens, 1, k, out, nullptr, ws.wcnt);
+  return launch_status("prefill selection");
 }
 
 }  // namespace csa2

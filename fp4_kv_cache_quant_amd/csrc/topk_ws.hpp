@@ -39,6 +39,37 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// A row's threshold estimate of the many-row selection: an order key kept
+// in entry kThresholdSlot of the row's wcnt row (kNoEstimate: none).
+constexpr uint32_t kNoEstimate = 0xFFFFFFFFu;
+constexpr int kThresholdSlot = kTopkFilterWgMax - 1;
+
+// The smallest score whose order key is >= lo, for a threshold key lo that
+// is 0, a key of a non-NaN score, or kNoEstimate: key(x) >= lo and
+// key(x) != 0 hold exactly when x >= key_threshold(lo) (-0 and +0 share a
+// key and compare equal; lo = 0 admits every score but NaN and -inf; the
+// NaN for kNoEstimate admits none).
+__device__ __forceinline__ float key_threshold(uint32_t lo) {
+  if (lo == 0) return -__FLT_MAX__;
+  return __builtin_bit_cast(float, (lo & 0x80000000u) ? (lo & 0x7FFFFFFFu) : ~lo);
+}
+
+// Candidates of many rows filtered while they are scored (a prefill chunk's
+// selection, rows of at most kTopkRowsMax slots): per row and block of
+// kCandBlock slots, the (score bits, slot) pairs of the block's scores at
+// or above the row's threshold, in no particular order, and how many there
+// were (more than kCandCap: the block's list is incomplete).
+constexpr int kCandBlock = 512;
+constexpr int kCandCap = 256;
+struct PrefillCandOut {
+  const uint32_t* thr = nullptr;  // threshold key of row i at thr[i * thr_stride]
+  int64_t thr_stride = 0;
+  uint2* cand = nullptr;          // [n_rows][n_blocks][kCandCap]
+  uint32_t* cnt = nullptr;        // [n_rows][n_blocks]
+  uint32_t* flags = nullptr;      // [ceil(n_rows / 32)]: bit i of word b = row 32b + i left to the full selection
+  int32_t n_blocks = 0;           // ceil(n / kCandBlock)
+};
+
 // Inputs of at most this many slots per sequence are selected by one
 // workgroup per sequence with the scores held in registers, unless a
 // histogram was produced upstream.
@@ -53,6 +84,12 @@ TopkWs topk_ws_carve(void* ws, int64_t n, int32_t n_seq);
 csa2_status topk_launch(const float* scores, int64_t n, const int32_t* lens, int32_t len_div, int32_t k,
                         const int32_t* pool, int32_t n_pool, int32_t blk, int32_t* out, const TopkWs& ws,
                         bool hist_ready, int32_t n_seq, hipStream_t stream, const int32_t* gids = nullptr);
+
+// A prefill chunk's selection filtered while it is scored (see topk.hip).
+bool prefill_filter_applies(int64_t n, int32_t n_rows, int32_t k);
+csa2_status prefill_select_launch(int stage, const float* scores, int64_t n, const int32_t* lens, int32_t k,
+                                  int32_t* out, const TopkWs& ws, const PrefillCandOut& co, int32_t n_rows,
+                                  hipStream_t stream);
 
 // Pool slots of a hierarchical layer selected after scoring that left
 // ws.bound (index_score_launch with tile_bound = ws.bound); n <= 16,384.
