@@ -414,8 +414,16 @@ def prefill_bench(args) -> dict:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
 
-    # The chunk's three ops on their own, launched as the chunk launches them.
+    # The chunk's two ops on their own, launched as the chunk launches them
+    # (its selection, filtered while scoring, and the attention of one
+    # layer), and the unfused public calls beside them: every score written
+    # (csa2_prefill_index_score), then selected from memory (csa2_topk).
     q0 = inp.idx_q[0]
+    sws = torch.zeros(csa2.prefill_select_workspace_size(E, nq, cfg.topk), dtype=torch.uint8, device="cuda")
+    sidx = torch.empty(nq, cfg.topk, dtype=torch.int32, device="cuda")
+    n_vis_sel = torch.empty(nq, dtype=torch.int32, device="cuda")
+    csa2.prefill_select(q0, inp.entry_k, cfg.t0, cfg.ratio, sidx, n_vis_sel, sws)
+    select_matches_chunk = bool(np.array_equal(sidx.cpu().numpy(), idx0))
     scores = torch.empty(nq, E, dtype=torch.float32, device="cuda")
     n_vis = torch.empty(nq, dtype=torch.int32, device="cuda")
     idx = torch.empty(nq, cfg.topk, dtype=torch.int32, device="cuda")
@@ -425,6 +433,8 @@ def prefill_bench(args) -> dict:
     csa2.prefill_index_score(q0, inp.entry_k, cfg.t0, cfg.ratio, scores, n_vis)
     csa2.topk(scores, cfg.topk, idx, lens=n_vis, ws=tws)
     ops = [
+        ("prefill_select", lambda: csa2.prefill_select(q0, inp.entry_k, cfg.t0, cfg.ratio, sidx, n_vis_sel, sws),
+         2.0 * nq * 8 * 64 * E, E * 128 + nq * 1024 + nq * cfg.topk * 4),
         ("prefill_score", lambda: csa2.prefill_index_score(q0, inp.entry_k, cfg.t0, cfg.ratio, scores, n_vis),
          2.0 * nq * 8 * 64 * E, nq * E * 4 + E * 128 + nq * 1024),
         ("prefill_topk", lambda: csa2.topk(scores, cfg.topk, idx, lens=n_vis, ws=tws), 0.0, nq * E * 4),
@@ -461,6 +471,7 @@ def prefill_bench(args) -> dict:
         "workload": cfg.name, "n_entries": E, "ratio": cfg.ratio, "n_q": nq, "t0": cfg.t0, "layers": nl,
         "ms_per_chunk": round(ms, 3), "query_layers_per_s": round(nq * nl / (ms * 1e-3), 1),
         "reps": reps, "ops": op_res,
+        "select_matches_chunk": select_matches_chunk,
         "parity_sample": {"queries": sample, "indices_bit_exact": bool(ok_idx), "attn_max_rel_l2": worst_rel,
                           "attn_max_abs": worst_abs,
                           "ok": bool(ok_idx and worst_rel <= 1e-3 and worst_abs <= 5e-3)},

@@ -101,6 +101,8 @@ _sched_check = _sig("csa2_sched_check", _I32, _P, ctypes.POINTER(_I32), _P)
 _sched_destroy = _sig("csa2_sched_destroy", None, _P)
 _prefill_score = _sig("csa2_prefill_index_score", _I32, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P)
 _prefill_ws = _sig("csa2_prefill_workspace_size", _SZ, ctypes.POINTER(_PrefillDesc))
+_prefill_select_ws = _sig("csa2_prefill_select_workspace_size", _SZ, _I64, _I32, _I32)
+_prefill_select = _sig("csa2_prefill_select", _I32, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P)
 _prefill_chunk = _sig("csa2_prefill_chunk", _I32, ctypes.POINTER(_PrefillDesc), ctypes.POINTER(_PrefillIO),
                       _P, _SZ, _P)
 
@@ -378,6 +380,25 @@ def prefill_index_score(q: torch.Tensor, keys: torch.Tensor, t0: int, ratio: int
     assert scores.dtype == torch.float32 and n_vis.dtype == torch.int32 and n_vis.numel() >= n_q
     _check(_prefill_score(_ptr(q), _ptr(w), _ptr(keys), n_entries, t0, ratio, n_q, _ptr(scores), _ptr(n_vis),
                           _stream(stream)))
+
+
+def prefill_select_workspace_size(n_entries: int, n_q: int, k: int) -> int:
+    n = int(_prefill_select_ws(n_entries, n_q, k))
+    if n == 0:
+        raise Csa2Error(-2, _last_error().decode(errors="replace"))
+    return n
+
+
+def prefill_select(q: torch.Tensor, keys: torch.Tensor, t0: int, ratio: int, idx: torch.Tensor, n_vis: torch.Tensor,
+                   ws: torch.Tensor, w: Optional[torch.Tensor] = None, stream=None) -> None:
+    """q [n_q][8][64] bf16, keys [n_entries][64] bf16 -> idx [n_q][k] int32 (each query's Top-k of its visible
+    entries), n_vis [n_q] int32; ws: prefill_select_workspace_size bytes, zero-filled before its first use."""
+    n_q, k = idx.shape
+    n_entries = keys.numel() // IDX_DIM
+    assert q.numel() == n_q * IDX_HEADS * IDX_DIM and idx.dtype == torch.int32
+    assert n_vis.dtype == torch.int32 and n_vis.numel() >= n_q
+    _check(_prefill_select(_ptr(q), _ptr(w), _ptr(keys), n_entries, t0, ratio, n_q, k, _ptr(idx), _ptr(n_vis),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 class Prefill:

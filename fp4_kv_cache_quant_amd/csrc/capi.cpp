@@ -204,7 +204,7 @@ extern "C" {
 
 const char* csa2_last_error(void) { return g_error.c_str(); }
 
-int32_t csa2_abi_version(void) { return 5; }
+int32_t csa2_abi_version(void) { return 6; }
 
 csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                             void* stream) {

@@ -33,53 +33,95 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: scores [n_q][n_entries] f32 | n_vis [n_q] | win_len
-// [n_q] | Top-k workspace | attention workspace | the layer's window rows
-// as f16 [n_q + swa - 1][512] (each row serves up to swa queries, so it is
-// converted once per layer instead of once per query) | when the selection
-// is filtered while scoring (prefill_filter_applies): candidate lists
-// [n_q][blocks][kCandCap] (score bits, entry), their counts [n_q][blocks]
-// u32 and the flags of the query blocks to rescore [ceil(n_q / 32)] u32
-// (blocks = ceil(n_entries / kCandBlock)).
-struct PrefillWs {
+// The selection of a chunk's queries (csa2_prefill_select and the Full /
+// Reindex layers of csa2_prefill_chunk).  Workspace: scores [n_q][n] f32
+// | Top-k workspace | when the selection is filtered while scoring
+// (prefill_filter_applies): candidate lists [n_q][blocks][kCandCap] (score
+// bits, entry), their counts [n_q][blocks] u32 and the flags of the query
+// blocks to rescore [ceil(n_q / 32)] u32 (blocks = ceil(n / kCandBlock)).
+struct SelectWs {
   float* scores;
-  int32_t* n_vis;
-  int32_t* win_len;
   void* topk;
-  void* attn;
-  uint16_t* win16;
   bool filtered;
   PrefillCandOut co;
   size_t bytes;
 };
 
+SelectWs select_ws_layout(int64_t n_entries, int32_t n_q, int32_t k, uintptr_t p) {
+  size_t off = 0;
+  SelectWs w{};
+  w.scores = reinterpret_cast<float*>(p + off);
+  off += align_up((size_t)n_q * (size_t)n_entries * sizeof(float));
+  w.topk = reinterpret_cast<void*>(p + off);
+  off += align_up(topk_workspace_bytes(n_entries, n_q));
+  w.filtered = prefill_filter_applies(n_entries, n_q, k);
+  if (w.filtered) {
+    const int32_t blocks = (int32_t)((n_entries + kCandBlock - 1) / kCandBlock);
+    w.co.n_blocks = blocks;
+    w.co.cand = reinterpret_cast<uint2*>(p + off);
+    off += align_up((size_t)n_q * blocks * kCandCap * sizeof(uint2));
+    w.co.cnt = reinterpret_cast<uint32_t*>(p + off);
+    off += align_up((size_t)n_q * blocks * sizeof(uint32_t));
+    w.co.flags = reinterpret_cast<uint32_t*>(p + off);
+    off += align_up((size_t)(n_q + 31) / 32 * sizeof(uint32_t));
+  }
+  w.bytes = off;
+  return w;
+}
+
+// Each query's Top-k of its scores over its visible entries into idx, and
+// the visible counts into n_vis (win_len / win: the chunk's window lengths,
+// or null).  Filtered: sampled scores -> thresholds -> candidates ->
+// selection among them; the rows that selection cannot take are scored
+// again in full (their whole query blocks) and selected over all entries.
+csa2_status select_run(const SelectWs& w, const uint16_t* q, const float* wq, const uint16_t* keys,
+                       int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q, int32_t k, int32_t* idx,
+                       int32_t* n_vis, int32_t* win_len, int32_t win, hipStream_t stream) {
+  const TopkWs tw = topk_ws_carve(w.topk, n_entries, n_q);
+  csa2_status st = CSA2_OK;
+  if (w.filtered) {
+    PrefillCandOut co = w.co;
+    co.thr = tw.wcnt + kThresholdSlot;
+    co.thr_stride = kTopkFilterWgMax;
+    for (int stage = 0; stage < 3 && st == CSA2_OK; ++stage) {
+      st = prefill_filter_launch(stage, q, wq, keys, n_entries, t0, ratio, n_q, w.scores, n_vis, win_len, win, co,
+                                 stream);
+      if (st == CSA2_OK)
+        st = prefill_select_launch(stage, w.scores, n_entries, n_vis, k, idx, tw, co, n_q, stream);
+    }
+    return st;
+  }
+  st = prefill_score_launch(q, wq, keys, n_entries, t0, ratio, n_q, w.scores, n_vis, win_len, win, stream);
+  if (st == CSA2_OK) st = topk_launch(w.scores, n_entries, n_vis, 1, k, nullptr, 0, 1, idx, tw, false, n_q, stream);
+  return st;
+}
+
+// Workspace of a chunk: the selection's | n_vis [n_q] | win_len [n_q] |
+// attention workspace | the layer's window rows as f16 [n_q + swa -
+// 1][512] (each row serves up to swa queries, so it is converted once per
+// layer instead of once per query).
+struct PrefillWs {
+  SelectWs sel;
+  int32_t* n_vis;
+  int32_t* win_len;
+  void* attn;
+  uint16_t* win16;
+  size_t bytes;
+};
+
 PrefillWs prefill_ws_layout(const csa2_prefill_desc& d, void* base) {
   const uintptr_t p = reinterpret_cast<uintptr_t>(base);
-  size_t off = 0;
   PrefillWs w{};
-  w.scores = reinterpret_cast<float*>(p + off);
-  off += align_up((size_t)d.n_q * (size_t)d.n_entries * sizeof(float));
+  w.sel = select_ws_layout(d.n_entries, d.n_q, d.topk, p);
+  size_t off = w.sel.bytes;
   w.n_vis = reinterpret_cast<int32_t*>(p + off);
   off += align_up((size_t)d.n_q * sizeof(int32_t));
   w.win_len = reinterpret_cast<int32_t*>(p + off);
   off += align_up((size_t)d.n_q * sizeof(int32_t));
-  w.topk = reinterpret_cast<void*>(p + off);
-  off += align_up(topk_workspace_bytes(d.n_entries, d.n_q));
   w.attn = reinterpret_cast<void*>(p + off);
   off += align_up(attn_workspace_bytes(d.n_q, d.topk, d.swa));
   w.win16 = reinterpret_cast<uint16_t*>(p + off);
   off += align_up(((size_t)d.n_q + d.swa - 1) * CSA2_LATENT * sizeof(uint16_t));
-  w.filtered = prefill_filter_applies(d.n_entries, d.n_q, d.topk);
-  if (w.filtered) {
-    const int32_t blocks = (int32_t)((d.n_entries + kCandBlock - 1) / kCandBlock);
-    w.co.n_blocks = blocks;
-    w.co.cand = reinterpret_cast<uint2*>(p + off);
-    off += align_up((size_t)d.n_q * blocks * kCandCap * sizeof(uint2));
-    w.co.cnt = reinterpret_cast<uint32_t*>(p + off);
-    off += align_up((size_t)d.n_q * blocks * sizeof(uint32_t));
-    w.co.flags = reinterpret_cast<uint32_t*>(p + off);
-    off += align_up((size_t)(d.n_q + 31) / 32 * sizeof(uint32_t));
-  }
   w.bytes = off;
   return w;
 }
@@ -137,6 +179,33 @@ csa2_status csa2_prefill_index_score(const uint16_t* q, const float* w, const ui
   return prefill_score_launch(q, w, keys, n_entries, t0, ratio, n_q, scores, n_vis, nullptr, 0, as_stream(stream));
 }
 
+size_t csa2_prefill_select_workspace_size(int64_t n_entries, int32_t n_q, int32_t k) {
+  clear_error();
+  if (n_q < 1 || n_q > 65535 || n_entries < 1 || n_entries > CSA2_TOPK_NMAX || k < 1 || k > CSA2_TOPK_MAX) {
+    set_error("csa2_prefill_select_workspace_size: need 1 <= n_q <= 65535, 1 <= n_entries <= 1048576, 1 <= k <= 2048");
+    return 0;
+  }
+  return select_ws_layout(n_entries, n_q, k, 0).bytes;
+}
+
+csa2_status csa2_prefill_select(const uint16_t* q, const float* w, const uint16_t* keys, int64_t n_entries, int64_t t0,
+                                int32_t ratio, int32_t n_q, int32_t k, int32_t* idx, int32_t* n_vis, void* ws,
+                                size_t ws_bytes, void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_q >= 1 && n_q <= 65535 && n_entries >= 1 && n_entries <= CSA2_TOPK_NMAX && k >= 1 &&
+                   k <= CSA2_TOPK_MAX,
+               CSA2_ESHAPE, "csa2_prefill_select: need 1 <= n_q <= 65535, 1 <= n_entries <= 1048576, 1 <= k <= 2048");
+  CSA2_REQUIRE(ratio >= 1 && t0 >= 0, CSA2_EINVAL, "csa2_prefill_select: need ratio >= 1 and t0 >= 0");
+  CSA2_REQUIRE(q && keys && idx && n_vis && ws, CSA2_EINVAL, "csa2_prefill_select: null pointer");
+  CSA2_REQUIRE(((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(keys)) & 15) == 0, CSA2_EINVAL,
+               "csa2_prefill_select: q and keys must be 16-byte aligned");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0, CSA2_EINVAL,
+               "csa2_prefill_select: workspace must be 256-byte aligned");
+  const SelectWs sw = select_ws_layout(n_entries, n_q, k, reinterpret_cast<uintptr_t>(ws));
+  CSA2_REQUIRE(ws_bytes >= sw.bytes, CSA2_ECAPACITY, "csa2_prefill_select: workspace too small");
+  return select_run(sw, q, w, keys, n_entries, t0, ratio, n_q, k, idx, n_vis, nullptr, 0, as_stream(stream));
+}
+
 size_t csa2_prefill_workspace_size(const csa2_prefill_desc* desc) {
   clear_error();
   if (check_prefill_desc(desc) != CSA2_OK) return 0;
@@ -183,34 +252,13 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
   }
 
   const hipStream_t stream = as_stream(stream_v);
-  const TopkWs tw = topk_ws_carve(w.topk, d.n_entries, d.n_q);
   const int32_t* cur = nullptr;
   for (int l = 0; l < d.n_layers; ++l) {
     const csa2_layer& L = d.layers[l];
     if (L.mode != CSA2_REUSE) {
       // Full and Reindex both score every visible entry with their own Q.
-      const float* wq = io->idx_w ? io->idx_w[l] : nullptr;
-      if (w.filtered) {
-        // Sampled scores -> thresholds -> candidates -> selection among
-        // them; the rows that selection cannot take are scored again in
-        // full (their whole query blocks) and selected over all entries.
-        PrefillCandOut co = w.co;
-        co.thr = tw.wcnt + kThresholdSlot;
-        co.thr_stride = kTopkFilterWgMax;
-        for (int stage = 0; stage < 3 && st == CSA2_OK; ++stage) {
-          st = prefill_filter_launch(stage, io->idx_q[l], wq, io->entry_k, d.n_entries, d.t0, d.ratio, d.n_q,
-                                     w.scores, w.n_vis, w.win_len, d.swa, co, stream);
-          if (st == CSA2_OK)
-            st = prefill_select_launch(stage, w.scores, d.n_entries, w.n_vis, d.topk, io->idx[l], tw, co, d.n_q,
-                                       stream);
-        }
-      } else {
-        st = prefill_score_launch(io->idx_q[l], wq, io->entry_k, d.n_entries, d.t0, d.ratio, d.n_q, w.scores,
-                                  w.n_vis, w.win_len, d.swa, stream);
-        if (st == CSA2_OK)
-          st = topk_launch(w.scores, d.n_entries, w.n_vis, 1, d.topk, nullptr, 0, 1, io->idx[l], tw, false, d.n_q,
-                           stream);
-      }
+      st = select_run(w.sel, io->idx_q[l], io->idx_w ? io->idx_w[l] : nullptr, io->entry_k, d.n_entries, d.t0,
+                      d.ratio, d.n_q, d.topk, io->idx[l], w.n_vis, w.win_len, d.swa, stream);
       if (st != CSA2_OK) return st;
       cur = io->idx[l];
     }

@@ -402,6 +402,32 @@ csa2_status csa2_prefill_index_score(const uint16_t* q, const float* w, const ui
                                      int64_t n_entries, int64_t t0, int32_t ratio, int32_t n_q,
                                      float* scores, int32_t* n_vis, void* stream);
 
+/* The selection of a chunk's queries, as a Full or Reindex layer of
+ * csa2_prefill_chunk takes it: query i's Top-k of its indexer scores over
+ * its visible entries ([P1 "Compressed Sparse Attention 2 (CSA2)"]: the
+ * indexer picks each query's own top entries), in csa2_topk's order
+ * (score descending, the lower entry first among equal scores, ids
+ * ascending, -1 padded).
+ *   q, w, keys, n_entries, t0, ratio, n_q: as csa2_prefill_index_score
+ *   k      entries kept per query, 1 .. 2048
+ *   idx    [n_q][k] int32 out (device)
+ *   n_vis  [n_q] int32 out (device): vis(t0 + i)
+ *   ws     csa2_prefill_select_workspace_size(n_entries, n_q, k) bytes,
+ *          256-byte aligned, zero-filled before its first use and left
+ *          ready for the next call (calls sharing it must not overlap).
+ * For 32,769 .. 65,536 entries, n_q >= 256 and k <= 512 the selection is
+ * filtered while scoring: only the scores at or above a per-query
+ * threshold estimated from 1,024 sampled entries leave the scoring kernel,
+ * and a query whose candidates cannot give its Top-k exactly is scored
+ * again in full; otherwise all scores are written and selected.  The
+ * result is the same either way.  Requires 1 <= n_q <= 65535,
+ * 1 <= n_entries <= 1,048,576, ratio >= 1, t0 >= 0, q and keys 16-byte
+ * aligned.  Asynchronous on `stream`; allocates nothing. */
+size_t csa2_prefill_select_workspace_size(int64_t n_entries, int32_t n_q, int32_t k);
+csa2_status csa2_prefill_select(const uint16_t* q, const float* w, const uint16_t* keys, int64_t n_entries,
+                                int64_t t0, int32_t ratio, int32_t n_q, int32_t k, int32_t* idx,
+                                int32_t* n_vis, void* ws, size_t ws_bytes, void* stream);
+
 typedef struct {
   int32_t n_layers;
   const csa2_layer* layers; /* host [n_layers]; Full / Reindex (flat) / Reuse */
@@ -428,7 +454,9 @@ typedef struct {
                                      layers (ascending entry ids, -1 padded); Reuse: ignored */
 } csa2_prefill_io;
 
-/* Workspace of csa2_prefill_chunk (scores [n_q][n_entries] f32 dominate). */
+/* Workspace of csa2_prefill_chunk (scores [n_q][n_entries] f32 and, when the
+ * selection is filtered while scoring, candidate lists of 2 KiB per query
+ * and 512 entries dominate). */
 size_t csa2_prefill_workspace_size(const csa2_prefill_desc* desc);
 /* Run the layer table over the chunk: a Full or Reindex layer scores all
  * visible entries with its own indexer Q and keeps a Top-`topk` per query

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(csa2):
 
 
 def test_abi_version(csa2):
-    assert csa2.abi_version() == 5
+    assert csa2.abi_version() == 6
 
 
 def _err(csa2):
@@ -151,6 +151,31 @@ def test_prefill_calls_reject_bad_arguments(csa2):
     assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE, need - 1, None) == -3
     assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE + 16, need, None) == -1
     assert csa2._prefill_chunk(ctypes.byref(d), ctypes.byref(io), FAKE, need, None) == -1    # io pointers null
+
+
+def test_prefill_select_rejects_bad_arguments(csa2):
+    need = csa2.prefill_select_workspace_size(65536, 4096, 512)
+    # filtered shape: candidate lists (2 KiB per query and 512 entries) on top of the scores
+    assert need >= 4096 * 65536 * 4 + 4096 * 128 * 256 * 8
+    # outside the filtered shapes (too few queries, k > 512) no lists are carved
+    assert csa2.prefill_select_workspace_size(65536, 255, 512) < 255 * 65536 * 4 + 255 * 128 * 256 * 8
+    assert csa2.prefill_select_workspace_size(65536, 4096, 1024) < need
+    with pytest.raises(csa2.Csa2Error):
+        csa2.prefill_select_workspace_size(65536, 0, 512)
+    with pytest.raises(csa2.Csa2Error):
+        csa2.prefill_select_workspace_size(65536, 16, 4096)
+
+    def call(q=FAKE, keys=FAKE, n_entries=1000, t0=0, ratio=2, n_q=16, k=512, idx=FAKE, n_vis=FAKE, ws=FAKE * 16,
+             ws_bytes=1 << 30):
+        return csa2._prefill_select(q, None, keys, n_entries, t0, ratio, n_q, k, idx, n_vis, ws, ws_bytes, None)
+
+    assert call(n_q=0) == -2 and call(n_q=65536) == -2
+    assert call(k=0) == -2 and call(k=4096) == -2 and call(n_entries=(1 << 20) + 1) == -2
+    assert call(ratio=0) == -1 and call(t0=-1) == -1
+    assert call(idx=None) == -1 and call(n_vis=None) == -1 and call(ws=None) == -1
+    assert call(q=FAKE + 2) == -1 and "aligned" in _err(csa2)
+    assert call(ws=FAKE * 16 + 16) == -1
+    assert call(ws_bytes=csa2.prefill_select_workspace_size(1000, 16, 512) - 1) == -3
 
 
 def test_key_maintenance_rejects_bad_arguments(csa2):

@@ -196,3 +196,60 @@ def test_prefill_selection_when_the_estimate_fails(wl, planted):
         ref = ow.prefill_reference(cfg, i, entry_keys=keys)
         assert np.array_equal(idx0[i], ref[0].idx), f"query {i} indices"
         assert_attention_close(inp.out[0][i].cpu().numpy(), ref[0].out, f"query {i} layer 0")
+
+
+SELECT_CASES = {
+    # the chunk's shape class that is filtered while scoring (n_q >= 256, k <= 512, 32,769..65,536 entries)
+    "filtered": dict(n_entries=40000, n_q=300, t0=2 * 40000 - 300, weights=False, plant=None),
+    # the same with dyadic head weights (every product and sum exact in binary32)
+    "filtered_weights": dict(n_entries=40000, n_q=300, t0=2 * 40000 - 300, weights=True, plant=None),
+    # sampled entries planted high: the estimate admits fewer than k, the rows are scored again in full
+    "filtered_fallback": dict(n_entries=40000, n_q=300, t0=2 * 40000 - 300, weights=False, plant="high"),
+    # ratio 1 with 4,101..4,400 visible entries: rows without an estimate next to rows with one
+    "filtered_edge": dict(n_entries=40000, n_q=300, t0=4100, ratio=1, weights=False, plant=None),
+    # fewer queries than the filtered path takes: every score is written and selected
+    "unfiltered": dict(n_entries=40000, n_q=100, t0=2 * 40000 - 100, weights=False, plant=None),
+}
+
+
+@pytest.mark.parametrize("name", list(SELECT_CASES))
+def test_prefill_select_matches_oracle(wl, name):
+    """csa2_prefill_select: each query's Top-512 over its visible entries
+    and the visible counts, on sampled queries against the oracle's scores
+    and selection; the call runs twice on one workspace."""
+    import fp4_kv_cache_quant_amd as csa2
+    c = dict(SELECT_CASES[name])
+    weights, plant, ratio = c.pop("weights"), c.pop("plant"), c.pop("ratio", 2)
+    cfg = _small(ratio=ratio, **c)
+    print_case(f"prefill select {name}: n_entries={cfg.n_entries} n_q={cfg.n_q} t0={cfg.t0} ratio={cfg.ratio}")
+    inp = wl.build_prefill_inputs(cfg)
+    keys = ow.prefill_entry_keys(cfg).copy()
+    if plant == "high":
+        keys[_sampled_entries(cfg.n_entries)[:40]] = 0x4280    # bf16 64.0
+    keys_d = torch.from_numpy(keys.view(np.int16)).cuda().view(torch.bfloat16)
+    q = inp.idx_q[0]
+    w_host = w = None
+    if weights:
+        rng = np.random.default_rng(3)
+        w_host = (rng.integers(-2, 5, size=(cfg.n_q, 8)) * 0.25).astype(np.float32)
+        w = torch.from_numpy(w_host).cuda()
+    k = cfg.topk
+    ws = torch.zeros(csa2.prefill_select_workspace_size(cfg.n_entries, cfg.n_q, k), dtype=torch.uint8,
+                     device="cuda")
+    idx = torch.empty(cfg.n_q, k, dtype=torch.int32, device="cuda")
+    n_vis = torch.empty(cfg.n_q, dtype=torch.int32, device="cuda")
+    qh = q.cpu().numpy().view(np.uint16)
+    rng = np.random.default_rng(17)
+    sample = sorted({i for i in (0, 1, 127, 128, cfg.n_q - 1) if i < cfg.n_q} | set(rng.integers(0, cfg.n_q, 5).tolist()))
+    for rep in range(2):
+        idx.fill_(-7)
+        csa2.prefill_select(q, keys_d, cfg.t0, cfg.ratio, idx, n_vis, ws, w=w)
+        torch.cuda.synchronize()
+        got, nv = idx.cpu().numpy(), n_vis.cpu().numpy()
+        for i in sample:
+            v = oracle.prefill_visible_entries(cfg.t0 + i, cfg.ratio, cfg.n_entries)
+            assert nv[i] == v, f"query {i} visible count"
+            ids = np.arange(v)
+            sc = oracle.index_score(qh[i], keys, ids, None if w_host is None else w_host[i])
+            ref = oracle.select(sc, ids, k)
+            assert np.array_equal(got[i], ref), f"call {rep} query {i} indices"
