@@ -44,7 +44,7 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12708979, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12708984, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
                     "938dfffb4d157c3808b5f01f3226865b13aec91416329f85f73c60980805e4ab",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
@@ -52,37 +52,37 @@ MEASURED_TRAFFIC = {
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/block_scan": {
-        "bytes": 210242319, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 210355047, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "decoder20_1m/pool_select": {
-        "bytes": 36499619, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 36532219, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
+                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "bytes": 1092917707, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "bytes": 1092461447, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
+                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
 }
@@ -121,7 +121,7 @@ def measured_traffic(op_key: str):
 # sources are unchanged.
 KERNEL_TRACE = {
     "decoder20_1m/sparse_attn": {
-        "us": 12.71, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 13.13, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
                     "938dfffb4d157c3808b5f01f3226865b13aec91416329f85f73c60980805e4ab",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
@@ -129,27 +129,27 @@ KERNEL_TRACE = {
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
     "decoder20_1m/pool_select": {
-        "us": 20.95, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 21.63, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
+                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "us": 215.37, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "us": 215.3, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "79e210eade170f2855689458a0c318100472fdcb61514fed56b0064316addb5d",
+                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "bc4a460071ae59a970483813592aec776e723a26cb98914fb6c81ef7b57c65e5",
+                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
-                    "4b7d55b0ae6edd0cf9536dc390543840f37476b1e277c61f3daa707c44254ad4",
+                    "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
 }
