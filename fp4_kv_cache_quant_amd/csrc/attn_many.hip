@@ -196,7 +196,7 @@ struct PairWinSrc {
       v[1][k] = p[1][k];
     }
   }
-  __device__ __forceinline__ u32x4 x(int t, int k) const { return kWin == kWinF16 ? v[t][k] : bf16x8_to_f16x8(v[t][k]); }
+  __device__ __forceinline__ u32x4 x(int t, int k) const { return bf16x8_to_f16x8(v[t][k]); }
 };
 
 struct PairNoSrc {
@@ -491,20 +491,16 @@ exceeded:
 
 }  // namespace
 
-// Launch: one 128-thread workgroup (two wavefronts) per query.  win:
-// kWinBf16 or kWinF16.
+// Launch: one 128-thread workgroup (two wavefronts) per query over bf16
+// window rows (win = kWinBf16).
 csa2_status attn_many_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
                              const int32_t* idx, int32_t k_idx, const uint8_t* swa, int win,
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float scale_log2,
                              float* out, hipStream_t stream) {
-  CSA2_REQUIRE(k_idx <= kWaveMaxIdx && (win == kWinF16 || win == kWinBf16), CSA2_EINVAL,
+  CSA2_REQUIRE(k_idx <= kWaveMaxIdx && win == kWinBf16, CSA2_EINVAL,
                "attention (many queries): k_idx above 512 or an unsupported window type");
-  if (win == kWinF16)
-    hipLaunchKernelGGL(attn_pair_kernel<kWinF16>, dim3(n_q), dim3(128), 0, stream, q, kv.codes, kv.scales, kv.cap,
-                       q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, scale_log2, out);
-  else
-    hipLaunchKernelGGL(attn_pair_kernel<kWinBf16>, dim3(n_q), dim3(128), 0, stream, q, kv.codes, kv.scales, kv.cap,
-                       q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, scale_log2, out);
+  hipLaunchKernelGGL(attn_pair_kernel<kWinBf16>, dim3(n_q), dim3(128), 0, stream, q, kv.codes, kv.scales, kv.cap,
+                     q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, scale_log2, out);
   return launch_status("csa2_sparse_attn");
 }
 

@@ -122,6 +122,5 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Element type of the window rows handed to the attention kernels.
 constexpr int kWinBf16 = 0;  // bf16, converted to f16 toward zero in the kernel
 constexpr int kWinE4m3 = 1;  // OCP E4M3FN bytes
-constexpr int kWinF16 = 2;   // f16, already converted as for kWinBf16
 
 }  // namespace csa2

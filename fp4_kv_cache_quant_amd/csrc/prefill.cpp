@@ -25,7 +25,6 @@ size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
                         float*, void*, hipStream_t);
-csa2_status win_f16_launch(const uint16_t*, int64_t, uint16_t*, hipStream_t);
 csa2_status check_kv(const csa2_fp4_kv& kv, const char* who);
 
 namespace {
@@ -97,15 +96,12 @@ csa2_status select_run(const SelectWs& w, const uint16_t* q, const float* wq, co
 }
 
 // Workspace of a chunk: the selection's | n_vis [n_q] | win_len [n_q] |
-// attention workspace | the layer's window rows as f16 [n_q + swa -
-// 1][512] (each row serves up to swa queries, so it is converted once per
-// layer instead of once per query).
+// attention workspace.
 struct PrefillWs {
   SelectWs sel;
   int32_t* n_vis;
   int32_t* win_len;
   void* attn;
-  uint16_t* win16;
   size_t bytes;
 };
 
@@ -120,8 +116,6 @@ PrefillWs prefill_ws_layout(const csa2_prefill_desc& d, void* base) {
   off += align_up((size_t)d.n_q * sizeof(int32_t));
   w.attn = reinterpret_cast<void*>(p + off);
   off += align_up(attn_workspace_bytes(d.n_q, d.topk, d.swa));
-  w.win16 = reinterpret_cast<uint16_t*>(p + off);
-  off += align_up(((size_t)d.n_q + d.swa - 1) * CSA2_LATENT * sizeof(uint16_t));
   w.bytes = off;
   return w;
 }
@@ -262,13 +256,10 @@ csa2_status csa2_prefill_chunk(const csa2_prefill_desc* desc, const csa2_prefill
       if (st != CSA2_OK) return st;
       cur = io->idx[l];
     }
-    // Query i's window rows start at row i of the layer's SWA buffer; the
-    // rows go to f16 once for all the queries that share them (none are
-    // read without a window).
-    st = d.swa > 0 ? win_f16_launch(io->swa[l], (int64_t)d.n_q + d.swa - 1, w.win16, stream) : CSA2_OK;
-    if (st == CSA2_OK)
-      st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, w.win16, kWinF16, 1, w.win_len,
-                       d.swa, nullptr, nullptr, d.sm_scale, io->out[l], w.attn, stream);
+    // Query i's window rows start at row i of the layer's SWA buffer (bf16,
+    // converted to f16 in the attention kernel's registers).
+    st = attn_launch(io->main_q[l], d.n_q, io->kv[L.kv_id], d.n_q, cur, d.topk, io->swa[l], kWinBf16, 1, w.win_len,
+                     d.swa, nullptr, nullptr, d.sm_scale, io->out[l], w.attn, stream);
     if (st != CSA2_OK) return st;
   }
   return CSA2_OK;

@@ -223,8 +223,7 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const u32x4 x = kWin == kWinE4m3 ? fp8x8_to_f16x8(t.raw[k >> 1][2 * (k & 1)], t.raw[k >> 1][2 * (k & 1) + 1])
-                      : kWin == kWinF16 ? t.raw[k]
-                                        : bf16x8_to_f16x8(t.raw[k]);
+                                       : bf16x8_to_f16x8(t.raw[k]);
       *reinterpret_cast<u32x4*>(&sm.xs[row_local * kXPitch + 128 * g + 8 * k]) = x;
       s = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qb_operand(k)), s);
     }
@@ -542,8 +541,7 @@ static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, con
 }
 
 // win: the window rows' element type -- kWinBf16 (bf16 [*][512], converted
-// to f16 toward zero in the kernel), kWinE4m3 (E4M3 bytes [*][512]) or
-// kWinF16 (f16 [*][512], already converted as kWinBf16 would).
+// to f16 toward zero in the kernel) or kWinE4m3 (E4M3 bytes [*][512]).
 // new_win / win_lens: the step's new window row per sequence ([*][512] in
 // the window's element type), or null, and the sequences' positions after
 // the step's append: the new row goes to window slot (lens - 1) % swa_max.
@@ -564,17 +562,14 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const uint8_t* sw = reinterpret_cast<const uint8_t*>(swa);
   const uint8_t* nw = reinterpret_cast<const uint8_t*>(new_win);
-  // Many queries over bf16 / f16 window rows with no step window row (the
+  // Many queries over bf16 window rows with no step window row (the
   // prefill chunk): the two-wavefronts-per-query kernel of attn_many.hip.
-  if (p.waves == 2 && !new_win && k_idx <= kAttnManyMaxIdx && (win == kWinF16 || win == kWinBf16))
+  if (p.waves == 2 && !new_win && k_idx <= kAttnManyMaxIdx && win == kWinBf16)
     return attn_many_launch(q, n_q, kv, q_per_seq, idx, k_idx, sw, win, swa_q_stride_rows, swa_len, swa_max,
                             scale_log2, out, stream);
   if (win == kWinE4m3)
     attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
                             nw, win_lens, scale_log2, part_o, part_ml, out, stream);
-  else if (win == kWinF16)
-    attn_dispatch<kWinF16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                           nw, win_lens, scale_log2, part_o, part_ml, out, stream);
   else
     attn_dispatch<kWinBf16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
                             nw, win_lens, scale_log2, part_o, part_ml, out, stream);
@@ -617,25 +612,6 @@ csa2_status attn_scratch(void** ptr, size_t* bytes) {
   *ptr = g_scratch_ptr[dev];
   *bytes = kAttnScratchBytes;
   return CSA2_OK;
-}
-
-// Window rows bf16 -> f16 toward zero (the conversion the attention kernel
-// applies to bf16 rows), for rows that many queries share: 8 values per
-// thread.
-namespace {
-__global__ __launch_bounds__(256) void win_f16_kernel(const u32x4* __restrict__ src, int64_t n_vec,
-                                                      u32x4* __restrict__ dst) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n_vec) dst[i] = bf16x8_to_f16x8(src[i]);
-}
-}  // namespace
-
-csa2_status win_f16_launch(const uint16_t* src, int64_t n_rows, uint16_t* dst, hipStream_t stream) {
-  const int64_t n_vec = n_rows * (CSA2_LATENT / 8);
-  if (n_vec == 0) return CSA2_OK;
-  hipLaunchKernelGGL(win_f16_kernel, dim3((uint32_t)((n_vec + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4*>(src), n_vec, reinterpret_cast<u32x4*>(dst));
-  return launch_status("window f16 conversion");
 }
 
 }  // namespace csa2
