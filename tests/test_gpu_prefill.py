@@ -209,6 +209,10 @@ SELECT_CASES = {
     "filtered_edge": dict(n_entries=40000, n_q=300, t0=4100, ratio=1, weights=False, plant=None),
     # fewer queries than the filtered path takes: every score is written and selected
     "unfiltered": dict(n_entries=40000, n_q=100, t0=2 * 40000 - 100, weights=False, plant=None),
+    # a small k on the filtered path (thresholds a little over twice 64 entries)
+    "filtered_k64": dict(n_entries=40000, n_q=300, t0=2 * 40000 - 300, weights=False, plant=None, k=64),
+    # k above the filtered path's 512 at the filtered shape: scores written and selected
+    "unfiltered_k1024": dict(n_entries=40000, n_q=300, t0=2 * 40000 - 300, weights=False, plant=None, k=1024),
 }
 
 
@@ -219,7 +223,7 @@ def test_prefill_select_matches_oracle(wl, name):
     and selection; the call runs twice on one workspace."""
     import fp4_kv_cache_quant_amd as csa2
     c = dict(SELECT_CASES[name])
-    weights, plant, ratio = c.pop("weights"), c.pop("plant"), c.pop("ratio", 2)
+    weights, plant, ratio, k = c.pop("weights"), c.pop("plant"), c.pop("ratio", 2), c.pop("k", None)
     cfg = _small(ratio=ratio, **c)
     print_case(f"prefill select {name}: n_entries={cfg.n_entries} n_q={cfg.n_q} t0={cfg.t0} ratio={cfg.ratio}")
     inp = wl.build_prefill_inputs(cfg)
@@ -233,7 +237,7 @@ def test_prefill_select_matches_oracle(wl, name):
         rng = np.random.default_rng(3)
         w_host = (rng.integers(-2, 5, size=(cfg.n_q, 8)) * 0.25).astype(np.float32)
         w = torch.from_numpy(w_host).cuda()
-    k = cfg.topk
+    k = k or cfg.topk
     ws = torch.zeros(csa2.prefill_select_workspace_size(cfg.n_entries, cfg.n_q, k), dtype=torch.uint8,
                      device="cuda")
     idx = torch.empty(cfg.n_q, k, dtype=torch.int32, device="cuda")
