@@ -44,43 +44,43 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12708984, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12721267, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "938dfffb4d157c3808b5f01f3226865b13aec91416329f85f73c60980805e4ab",
+                    "cdb9620b29355fb802f2b19e9479a7c69bc4acff2a4971508a4032d1ed985d5a",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
                     "f661423ba3cb7510492a0ac6c0be9cc00bcf54af70b4fc72973da1614caddf09",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
+                    "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e"}},
     "decoder20_1m/block_scan": {
-        "bytes": 210355047, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 210304718, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
                     "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "decoder20_1m/pool_select": {
-        "bytes": 36532219, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 36533981, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
                     "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
                     "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "bytes": 1092461447, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "bytes": 1092501651, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
                     "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
                     "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
@@ -121,33 +121,33 @@ def measured_traffic(op_key: str):
 # sources are unchanged.
 KERNEL_TRACE = {
     "decoder20_1m/sparse_attn": {
-        "us": 13.13, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 12.66, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "938dfffb4d157c3808b5f01f3226865b13aec91416329f85f73c60980805e4ab",
+                    "cdb9620b29355fb802f2b19e9479a7c69bc4acff2a4971508a4032d1ed985d5a",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
                     "f661423ba3cb7510492a0ac6c0be9cc00bcf54af70b4fc72973da1614caddf09",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb"}},
+                    "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e"}},
     "decoder20_1m/pool_select": {
-        "us": 21.63, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 21.18, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
                     "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
                     "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "us": 215.3, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "us": 214.95, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
                     "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
                     "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
-                    "fb6a185fecd37b44e4ba5201cfe2ced26d08e283b113eceed09602a4c8ee48eb",
+                    "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
                     "851d1bdbabfc69fc98ad3b94960d99fe8e200dd9c6fcf1a619231b9c52f11f07",
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
