@@ -1068,7 +1068,6 @@ struct LeanSmem {
   uint32_t scan_sum[4][kLeanThreads / 64];
   uint32_t fin_sum[2 * kLeanThreads / 64];
   uint32_t found[2];
-  uint32_t reg_off[kLeanThreads];  // first candidate of each region (topk_region_select_kernel)
 };
 static_assert(sizeof(LeanSmem) <= 80 * 1024, "two workgroups per CU");
 
@@ -1163,10 +1162,24 @@ __global__ __launch_bounds__(kLeanThreads, 2) void topk_region_select_kernel(int
   const int words = (nvalid + 31) / 32;
   const uint32_t kk = (uint32_t)k;
   const int nb = co.n_blocks;
+  // Four threads per block list: thread (blk, sub) takes entries sub,
+  // sub + 4, ... of list blk.  Its first kPer entries are loaded at once,
+  // before the count is known (every list has kCandCap places, so the
+  // loads stay in bounds; entries past the count are ignored), so that
+  // they travel with the count load instead of after the scan.
+  constexpr int kTpb = kLeanThreads / (kRowsMax / kCandBlock);
+  constexpr int kPer = 8;
+  static_assert(kTpb * (kRowsMax / kCandBlock) == kLeanThreads && kTpb * kPer <= kCandCap, "list split");
+  const int blk = tid / kTpb, sub = tid % kTpb;
+  const uint2* lb = co.cand + ((int64_t)b * nb + min(blk, nb - 1)) * kCandCap;
+  uint2 e[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) e[j] = lb[sub + kTpb * j];
   const uint32_t lo = wcnt[(int64_t)b * kTopkFilterWgMax + kThresholdSlot];
-  const uint32_t cnt = tid < nb ? co.cnt[(int64_t)b * nb + tid] : 0u;
+  const uint32_t cnt = blk < nb ? co.cnt[(int64_t)b * nb + blk] : 0u;
   uint32_t total;
-  const uint32_t off = block_exclusive_scan<kLeanThreads>(cnt, sm.scan_sum[0], &total);
+  const uint32_t off = block_exclusive_scan<kLeanThreads>(sub == 0 ? cnt : 0u, sm.scan_sum[0], &total);
+  const uint32_t boff = (uint32_t)__shfl((int)off, lane_id() & ~(kTpb - 1));  // the list's first place
   const bool over = __syncthreads_or(cnt > (uint32_t)kCandCap);
   if (over || lo == kNoEstimate || total < kk || total > (uint32_t)kLeanCand) {  // uniform over the workgroup
     if (tid == 0) {
@@ -1176,38 +1189,26 @@ __global__ __launch_bounds__(kLeanThreads, 2) void topk_region_select_kernel(int
     }
     return;
   }
-  sm.reg_off[tid] = off;
-  for (int i = tid; i < kTopkBins; i += kLeanThreads) sm.hist1[i] = sm.hist2[i] = 0;
-  if (tid < 256) sm.hist3[tid] = 0;
-  for (int i = tid; i < words; i += kLeanThreads) sm.sel[i] = sm.tie[i] = 0;
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < kTopkBins / 4; i += kLeanThreads)
+      reinterpret_cast<u32x4*>(sm.hist1)[i] = reinterpret_cast<u32x4*>(sm.hist2)[i] = z;
+    if (tid < 64) reinterpret_cast<u32x4*>(sm.hist3)[tid] = z;
+    for (int i = tid; i < (words + 3) / 4; i += kLeanThreads)
+      reinterpret_cast<u32x4*>(sm.sel)[i] = reinterpret_cast<u32x4*>(sm.tie)[i] = z;
+  }
   __syncthreads();
-  // Candidate c of the concatenated lists lies in the last block whose
-  // first candidate is <= c (blocks before it that hold none share its
-  // offset; those after it start past c).  All of a thread's loads go out
-  // together (clamped to the last candidate).
-  const uint2* cb = co.cand + (int64_t)b * nb * kCandCap;
-  constexpr int kCandPer = kLeanCand / kLeanThreads;
-  uint2 e[kCandPer];
+  auto put = [&](uint32_t c, uint2 v) {
+    const uint32_t bits = v.x;
+    const uint32_t key = order_key(__builtin_bit_cast(float, bits));
+    sm.cand_key[boff + c] = key;
+    sm.cand_slot[boff + c] = v.y;
+    atomicAdd(&sm.hist1[key >> 20], 1u);
+  };
 #pragma unroll
-  for (int j = 0; j < kCandPer; ++j) {
-    const uint32_t c = min(tid + j * kLeanThreads, total - 1u);
-    int r = 0;
-#pragma unroll
-    for (int step = kRowsMax / kCandBlock / 2; step > 0; step >>= 1)
-      if (r + step < nb && sm.reg_off[r + step] <= c) r += step;
-    e[j] = cb[r * kCandCap + (int)(c - sm.reg_off[r])];
-  }
-#pragma unroll
-  for (int j = 0; j < kCandPer; ++j) {
-    const uint32_t c = tid + j * kLeanThreads;
-    if (c < total) {
-      const uint32_t bits = e[j].x;
-      const uint32_t key = order_key(__builtin_bit_cast(float, bits));
-      sm.cand_key[c] = key;
-      sm.cand_slot[c] = e[j].y;
-      atomicAdd(&sm.hist1[key >> 20], 1u);
-    }
-  }
+  for (int j = 0; j < kPer; ++j)
+    if (sub + kTpb * j < (int)cnt) put(sub + kTpb * j, e[j]);
+  for (uint32_t c = sub + kTpb * kPer; c < cnt; c += kTpb) put(c, lb[c]);  // lists longer than kTpb * kPer
   __syncthreads();
   uint32_t T, ties;
   select_candidates<kLeanThreads>(sm.cand_key, (int)total, kk, sm.hist1, sm.hist2, sm.hist3, sm.scan_sum, sm.found,
