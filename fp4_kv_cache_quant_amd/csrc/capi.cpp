@@ -20,7 +20,7 @@ csa2_status append_keys_launch(const uint16_t*, uint16_t*, int64_t, uint16_t*, i
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
                                uint32_t*, hipStream_t, uint32_t* bound_inv = nullptr, int32_t bound_k = 0);
-int64_t index_score_local_groups(int64_t key_cap);
+int64_t flat_local_groups(int64_t key_cap, int32_t k, int32_t n_seq);
 csa2_status index_score_local_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*, int32_t,
                                      float*, int32_t*, int32_t, hipStream_t);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
@@ -78,9 +78,8 @@ csa2_status check_index_score(const uint16_t* q, const uint16_t* keys, int64_t k
 FlatSelectWs flat_select_ws(int64_t key_cap, int32_t k, int32_t n_seq, void* base) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   FlatSelectWs f{};
-  const int64_t groups = index_score_local_groups(key_cap);
-  f.local_groups = (key_cap > kTopkRowsMax && groups * k <= kTopkRowsMax) ? groups : 0;
-  f.n_scores = f.local_groups ? groups * k : key_cap;
+  f.local_groups = flat_local_groups(key_cap, k, n_seq);
+  f.n_scores = f.local_groups ? f.local_groups * k : key_cap;
   char* p = reinterpret_cast<char*>(base);
   size_t off = 0;
   f.scores = reinterpret_cast<float*>(p + off);

@@ -580,6 +580,20 @@ namespace csa2 {
 // Workgroups per sequence of the flat scoring with local selection.
 int64_t index_score_local_groups(int64_t key_cap) { return (key_cap + kLocalSlots - 1) / kLocalSlots; }
 
+// Whether a flat selection of k over key_cap positions for n_seq sequences
+// keeps per-workgroup candidates instead of writing every score (the
+// groups, else 0): the candidates must fit the single-workgroup selection,
+// and up to kTopkRowsMax positions the scoring workgroups must fill the
+// chip (each streams its 8,192 positions at a latency-bound rate: 4 groups
+// x 32 sequences took 75 us against 44 us for scores written and selected,
+// 8 x 32 took 80 against 95 us).
+int64_t flat_local_groups(int64_t key_cap, int32_t k, int32_t n_seq) {
+  const int64_t groups = index_score_local_groups(key_cap);
+  if (groups * k > kTopkRowsMax) return 0;
+  if (key_cap > kTopkRowsMax) return groups;
+  return groups >= 4 && groups * n_seq >= 256 ? groups : 0;
+}
+
 csa2_status index_score_local_launch(const uint16_t* q, const float* w, const uint16_t* keys, int64_t key_cap,
                                      const int32_t* lens, int32_t k, float* cand_score, int32_t* cand_slot,
                                      int32_t n_seq, hipStream_t stream) {

@@ -21,7 +21,7 @@ csa2_status quant_append_launch(const uint16_t*, const csa2_fp4_kv&, int32_t*, i
 csa2_status index_score_launch(const uint16_t*, const float*, const uint16_t*, int64_t, const int32_t*,
                                int32_t, const int32_t*, int32_t, int32_t, float*, int64_t, int32_t,
                                uint32_t*, hipStream_t, uint32_t* bound_inv = nullptr, int32_t bound_k = 0);
-int64_t index_score_local_groups(int64_t key_cap);
+int64_t flat_local_groups(int64_t key_cap, int32_t k, int32_t n_seq);
 size_t attn_workspace_bytes(int32_t, int32_t, int32_t);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
@@ -45,9 +45,9 @@ struct csa2_sched {
   int32_t* pool = nullptr;      // [n_seq][pool_blocks]
   float* scores = nullptr;      // [n_seq][scores_n]
   int64_t scores_n = 0;
-  // Flat selection over more than kTopkRowsMax positions: per-workgroup
-  // Top-k candidates (local_groups * topk per sequence, scores in `scores`,
-  // positions here), then one selection over them.
+  // Flat selection with per-workgroup Top-k candidates (flat_local_groups:
+  // local_groups * topk per sequence, scores in `scores`, positions here),
+  // then one selection over them; 0: every score written and selected.
   int64_t local_groups = 0;
   int32_t* cand_slot = nullptr;  // [n_seq][local_groups * topk]
   void* attn_ws = nullptr;
@@ -167,8 +167,7 @@ csa2_status csa2_sched_create(const csa2_sched_desc* desc, csa2_sched** out) {
       return CSA2_ESHAPE;
     }
     s->scores_n = std::max<int64_t>(s->scores_n, d.key_cap);
-    const int64_t groups = index_score_local_groups(d.key_cap);
-    if (d.key_cap > kTopkRowsMax && groups * d.topk <= kTopkRowsMax) s->local_groups = groups;
+    s->local_groups = flat_local_groups(d.key_cap, d.topk, d.n_seq);
   }
   s->attn_ws_bytes = attn_workspace_bytes(d.n_seq, d.topk, d.swa_max);
   s->topk_ws_bytes = topk_workspace_bytes(s->scores_n, d.n_seq);

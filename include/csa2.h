@@ -162,8 +162,9 @@ csa2_status csa2_topk(const float* scores, int64_t n, const int32_t* lens, int32
  * Attention 2 (CSA2)"]: a fresh Top-k over all positions.  The result equals
  * csa2_index_score (flat, len_div 1, n_out = key_cap) followed by csa2_topk
  * (n = key_cap, lens): out [n_seq][k] int32, ascending positions, -1
- * padded.  For key_cap > 65,536 with ceil(key_cap / 8,192) * k <= 65,536
- * the scores are not written out: every scoring workgroup keeps the Top-k
+ * padded.  With G = ceil(key_cap / 8,192) and G * k <= 65,536, for
+ * key_cap > 65,536, or for G >= 4 and G * n_seq >= 256, the scores are not
+ * written out: every scoring workgroup keeps the Top-k
  * (score descending, position ascending) of its 8,192 positions, and one
  * selection runs over those candidates; otherwise the scores go through
  * csa2_topk's passes.

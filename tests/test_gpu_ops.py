@@ -312,6 +312,28 @@ def test_flat_select_matches_oracle(csa2, key_cap, k, lens, weights):
             assert np.array_equal(got[b], ref), (rep, b)
 
 
+def test_flat_select_many_sequences_per_workgroup_candidates(csa2):
+    """64 sequences over 24,577 positions: four scoring workgroups each
+    (the last holds one position), 256 in all, so the per-workgroup
+    candidates path is taken below 65,536 positions.  Ragged lengths
+    around the 8,192-position workgroup edges, fewer positions than k, and
+    one position; every sequence against the oracle."""
+    n_seq, key_cap, k = 64, 24577, 512
+    rng = np.random.default_rng(23)
+    keys = _bf16_of(rng.integers(-4, 5, size=(n_seq, key_cap, 64)))
+    q = _bf16_of(rng.integers(-4, 5, size=(n_seq, 8, 64)))
+    L = rng.integers(1, key_cap + 1, size=n_seq).astype(np.int32)
+    L[:9] = [key_cap, 1, 511, 512, 513, 8192, 8193, 16384, 24576]
+    print_case(f"flat_select n_seq={n_seq} key_cap={key_cap} k={k}")
+    out = torch.empty(n_seq, k, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(csa2.flat_select_workspace_size(key_cap, k, n_seq), dtype=torch.uint8, device="cuda")
+    csa2.flat_select(dev(q), dev(keys), dev(L), k, out, ws=ws)
+    got = out.cpu().numpy()
+    for b in range(n_seq):
+        ref = oracle.flat_select(q[b], keys[b], int(L[b]), k)
+        assert np.array_equal(got[b], ref), b
+
+
 def test_topk_signed_scores_and_zero_signs(csa2):
     rng = np.random.default_rng(11)
     sc = rng.standard_normal((1, 10000)).astype(np.float32)
