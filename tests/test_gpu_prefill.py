@@ -213,6 +213,10 @@ SELECT_CASES = {
     "filtered_k64": dict(n_entries=40000, n_q=300, t0=2 * 40000 - 300, weights=False, plant=None, k=64),
     # k above the filtered path's 512 at the filtered shape: scores written and selected
     "unfiltered_k1024": dict(n_entries=40000, n_q=300, t0=2 * 40000 - 300, weights=False, plant=None, k=1024),
+    # the filtered path's edges: the fewest queries (256) over the most entries (65,536, 128 lists of 512)
+    "filtered_edge_max": dict(n_entries=65536, n_q=256, t0=2 * 65536 - 256, weights=False, plant=None),
+    # the fewest entries it takes (32,769: a last list of one entry) and a last query block of one query
+    "filtered_edge_min": dict(n_entries=32769, n_q=257, t0=2 * 32769 - 257, weights=False, plant=None),
 }
 
 
