@@ -456,6 +456,43 @@ def test_sparse_attn_workspace_reused_across_calls(csa2):
             assert_attention_close(got[b], ref)
 
 
+def test_sparse_attn_split_shapes_share_a_workspace(csa2):
+    """Few queries split over several workgroups whose partials are merged
+    with log-sum-exp weights: 1, 2, 13, 16 and 64 queries at 5, 17 and 33
+    splits (k_idx 512, 2,000 and 4,000).  All calls share one workspace, in
+    an order that moves between shapes, so that a call whose partials sit
+    where another shape's did still reads only its own; padded selections
+    and ragged window lengths; every output against the oracle."""
+    cap = 4200
+    n_max = 64
+    src = kv_source(4, n_max, cap)
+    kv = _device_cache(csa2, src)
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 4), synth.NORMAL, range(n_max), np.arange(16), 512)
+    swa = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 4), synth.NORMAL, range(n_max), np.arange(128), 512)
+    cases = [(16, 512), (13, 512), (64, 512), (16, 512), (2, 2000), (1, 4000), (1, 512), (16, 512)]
+    need = max(csa2.sparse_attn_workspace_size(n, k, 128) for n, k in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    oracle_rows = {}
+    for i, (n_q, k_idx) in enumerate(cases):
+        rng = np.random.default_rng(100 + i)
+        idx = np.stack([np.sort(rng.choice(cap, k_idx, replace=False)) for _ in range(n_q)]).astype(np.int32)
+        if n_q > 3:
+            idx[3, k_idx // 3:] = -1
+        swa_len = rng.integers(0, 129, n_q).astype(np.int32)
+        swa_len[0] = 128
+        print_case(f"sparse_attn split merge case {i}: n_q={n_q} k_idx={k_idx}")
+        out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+        csa2.sparse_attn(dev(q[:n_q]), kv, dev(idx), dev(swa[:n_q]), dev(swa_len), SM_SCALE, out, ws=ws)
+        got = out.cpu().numpy()
+        assert not np.isnan(got).any(), f"case {i}: NaN output"
+        for b in range(n_q):
+            if b not in oracle_rows:
+                oracle_rows[b] = oracle.quant_rows(src[b])
+            codes, scales = oracle_rows[b]
+            ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa[b], swa_len[b], SM_SCALE)
+            assert_attention_close(got[b], ref, f"case {i} query {b}")
+
+
 @pytest.mark.parametrize("n_q", [300, 1100])
 def test_sparse_attn_many_queries_one_cache(csa2, n_q):
     """Many queries over one cache sequence with per-query window offsets
