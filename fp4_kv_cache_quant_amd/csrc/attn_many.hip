@@ -8,6 +8,13 @@
 // E4M3 scale per 16 channels.  The arithmetic is that of the workgroup
 // kernels in sparse_attn.hip (f16 operands, exact dequantisation, fp32
 // accumulation, P split into f16 hi + lo); what differs is the schedule:
+//   - a chunk of FP4 rows whose E4M3 scales are all <= 1.25 (|x| <= 7.5)
+//     takes P rounded once to f16 (to nearest) instead of hi + lo: the
+//     output then moves by at most 2^-11 * 7.5 < 3.7e-3 per element (each
+//     weight is off by at most 2^-11 of itself, and the weights of the
+//     normaliser are exact), inside the 5e-3 absolute bound, with one P X
+//     product instead of two (per wavefront, from its own channels' scales;
+//     window chunks and chunks with larger scales keep hi + lo);
 //   - a query's two wavefronts split the channels: wavefront w loads,
 //     converts and stores channels 256w..256w+255 of every row, keeps O for
 //     those channels (16 heads x 256, fp32) in registers for the whole
@@ -103,7 +110,8 @@ __device__ __forceinline__ float wave_scores(const f32x4 (&s)[2], const uint64_t
 // path to the next step passes them).
 template <class St>
 __device__ __forceinline__ bool wave_softmax(St& st, const f32x4 (&s)[2], const uint64_t (&ok)[2],
-                                             float scale_log2, int g, bool fixed, u32x4& hi, u32x4& lo) {
+                                             float scale_log2, int g, bool fixed, u32x4& hi, u32x4& lo,
+                                             bool single = false) {
   float z[8];
   const float m = wave_scores(s, ok, scale_log2, g, z);
   // (Uniform selects, no branch: the step stays one block.)  The first
@@ -122,13 +130,24 @@ __device__ __forceinline__ bool wave_softmax(St& st, const f32x4 (&s)[2], const 
     lsum += p[i];
   }
   st.l_run += fold32_add(fold16_add(lsum));
-  // P = hi + lo in f16 (toward zero; p - hi is exact in binary32).
+  if (!single) {
+    // P = hi + lo in f16 (toward zero; p - hi is exact in binary32).
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[2 * i], p[2 * i + 1]));
-    const f16x2 l = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[2 * i] - (float)h[0], p[2 * i + 1] - (float)h[1]));
-    hi[i] = __builtin_bit_cast(uint32_t, h);
-    lo[i] = __builtin_bit_cast(uint32_t, l);
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[2 * i], p[2 * i + 1]));
+      const f16x2 l =
+          __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[2 * i] - (float)h[0], p[2 * i + 1] - (float)h[1]));
+      hi[i] = __builtin_bit_cast(uint32_t, h);
+      lo[i] = __builtin_bit_cast(uint32_t, l);
+    }
+  } else {
+    // P rounded once to f16, to nearest.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 h = {(_Float16)p[2 * i], (_Float16)p[2 * i + 1]};
+      hi[i] = __builtin_bit_cast(uint32_t, h);
+      lo[i] = 0u;
+    }
   }
   return !(above && !unset);
 }
@@ -163,6 +182,21 @@ __device__ __forceinline__ void pair_issue(PairSlot& sl, const WaveArgs& a, int3
     sl.s4[t] = *(gu32p)(a.scales + row * CSA2_SCALE_BYTES + 16 * w + 4 * g);
     sl.ok[t] = __ballot(ok);
   }
+}
+
+// Whether every scale byte of the chunk in sl (this wavefront's channels
+// of both tiles; rows that are not attended count as 0) is an E4M3 value
+// <= 1.25 (code 0x3A), so that every dequantised |x| <= 6 * 1.25: per byte,
+// the low 7 bits + 0x45 reach bit 7 iff they exceed 0x3A (no carry crosses
+// a byte), and a set sign bit counts as large.  Uniform over the wavefront.
+__device__ __forceinline__ bool fp4_chunk_small(const PairSlot& sl, int n) {
+  uint32_t big = 0u;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t s4 = ((sl.ok[t] >> n) & 1) ? sl.s4[t] : 0u;
+    big |= ((s4 & 0x7F7F7F7Fu) + 0x45454545u) | s4;
+  }
+  return __ballot((big & 0x80808080u) != 0u) == 0;
 }
 
 struct PairFp4Src {
@@ -224,10 +258,24 @@ __device__ __forceinline__ PairBGroup pair_read_group(const uint16_t* xs, int kk
   return r;
 }
 
+// O += lo X over this wavefront's half tile (the lo part of P of a chunk
+// whose hi part goes through pair_pv_next<false>).
+__device__ __forceinline__ void pair_pv_lo(PairState& st, const uint16_t* xs, u32x4 lo, int n, int g) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const PairBGroup cur = pair_read_group(xs, kk, n, g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 u0 = __builtin_bit_cast(uint2, cur.t[i][0]), u1 = __builtin_bit_cast(uint2, cur.t[i][1]);
+      st.o[kk + 4 * i] = mfma16x16x32_f16(as_f16x8(lo), as_f16x8(u32x4{u0.x, u0.y, u1.x, u1.y}), st.o[kk + 4 * i]);
+    }
+  }
+}
+
 // O += P X over this wavefront's 256 channels, and the next chunk's half
 // rows: group k (local channels 64g + 8k..) is stored once the blocks
 // k/2 + 4i that read those columns have been read.
-template <class Src>
+template <bool kLo = true, class Src>
 __device__ __forceinline__ void pair_pv_next(PairState& st, uint16_t* xs, u32x4 hi, u32x4 lo, const u32x4 (&qv)[8],
                                              Src&& src, f32x4 (&s_next)[2], int n, int g) {
   f32x4 s_odd[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -244,7 +292,7 @@ __device__ __forceinline__ void pair_pv_next(PairState& st, uint16_t* xs, u32x4 
       const uint2 u0 = __builtin_bit_cast(uint2, cur.t[i][0]), u1 = __builtin_bit_cast(uint2, cur.t[i][1]);
       const f16x8 bx = as_f16x8(u32x4{u0.x, u0.y, u1.x, u1.y});
       st.o[b] = mfma16x16x32_f16(as_f16x8(hi), bx, st.o[b]);
-      st.o[b] = mfma16x16x32_f16(as_f16x8(lo), bx, st.o[b]);
+      if constexpr (kLo) st.o[b] = mfma16x16x32_f16(as_f16x8(lo), bx, st.o[b]);
     }
     if constexpr (std::remove_reference_t<Src>::kHas) {
 #pragma unroll
@@ -263,7 +311,7 @@ __device__ __forceinline__ void pair_pv_next(PairState& st, uint16_t* xs, u32x4 
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < (kLo ? 12 : 8); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
@@ -377,7 +425,9 @@ attend:
           s_cur[t] = mfma16x16x32_f16(as_f16x8(x), as_f16x8(qv[k]), s_cur[t]);
         }
     };
+    bool small_cur = false;  // the FP4 chunk in xs takes a single f16 P
     if (n_fc > 0) {
+      small_cur = fp4_chunk_small(ring, n);
       first(PairFp4Src(ring, n));
       ok_cur[0] = ring.ok[0];
       ok_cur[1] = ring.ok[1];
@@ -391,9 +441,12 @@ attend:
     for (int c = 0; c + 1 < n_fc; ++c) {
       pair_exchange(s_cur, ex, w, lane);
       u32x4 hi, lo;
-      bad |= !wave_softmax(st, s_cur, ok_cur, scale_log2, g, fixed, hi, lo);
       f32x4 s_next[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      pair_pv_next(st, xs, hi, lo, qv, PairFp4Src(ring, n), s_next, n, g);
+      const bool small_next = fp4_chunk_small(ring, n);
+      bad |= !wave_softmax(st, s_cur, ok_cur, scale_log2, g, fixed, hi, lo, small_cur);
+      if (!small_cur) pair_pv_lo(st, xs, lo, n, g);
+      pair_pv_next<false>(st, xs, hi, lo, qv, PairFp4Src(ring, n), s_next, n, g);
+      small_cur = small_next;
       ok_cur[0] = ring.ok[0];
       ok_cur[1] = ring.ok[1];
       pair_issue(ring, a, id_of(c + 2, 0), id_of(c + 2, 1), w, g);
@@ -404,9 +457,10 @@ attend:
     if (n_fc > 0 && n_wc > 0) {
       pair_exchange(s_cur, ex, w, lane);
       u32x4 hi, lo;
-      const bool fits = wave_softmax(st, s_cur, ok_cur, scale_log2, g, fixed, hi, lo);
       f32x4 s_next[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      pair_pv_next(st, xs, hi, lo, qv, win_src(0), s_next, n, g);
+      const bool fits = wave_softmax(st, s_cur, ok_cur, scale_log2, g, fixed, hi, lo, small_cur);
+      if (!small_cur) pair_pv_lo(st, xs, lo, n, g);
+      pair_pv_next<false>(st, xs, hi, lo, qv, win_src(0), s_next, n, g);
       win_ok(0, ok_cur);
       s_cur[0] = s_next[0];
       s_cur[1] = s_next[1];

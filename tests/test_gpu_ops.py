@@ -522,6 +522,46 @@ def test_sparse_attn_many_queries_one_cache(csa2, n_q):
         assert_attention_close(got[b], ref, f"query {b}")
 
 
+def test_sparse_attn_many_queries_scales_around_single_f16_bound(csa2):
+    """Many queries (two wavefronts each): a 32-row chunk of FP4 rows whose
+    E4M3 scales are all <= 1.25 (|x| <= 7.5) takes P rounded once to f16,
+    any other chunk P as f16 hi + lo.  The cache's rows are N(0,1) latents
+    times 1 (scales below the bound), 2.5 (group maxima near 6 * 1.25:
+    scales on both sides of it) or 4 (scales above it); queries select
+    from one kind or from all, so that chunks of either form, and queries
+    that mix them, occur.  Sampled queries vs the oracle at
+    the attention bar (the single-f16 error bound, 2^-11 * 7.5 < 3.7e-3,
+    is inside its 5e-3 absolute limit)."""
+    n_q, cap, k_idx, swa_max = 1024, 4096, 512, 128
+    base = kv_source(5, 1, cap)[0]
+    kinds = np.arange(cap) * 3 // cap
+    factor = np.array([1.0, 2.5, 4.0])[kinds][:, None]
+    src = synth._f32_to_bf16_rne(synth.bf16_to_f32(base) * factor)[None]
+    codes, scales = oracle.quant_rows(src[0])
+    small = np.all(scales <= 0x3A, axis=1)  # E4M3 code 0x3A = 1.25
+    assert small[kinds == 0].all() and not small[kinds == 2].any()
+    assert 0 < small[kinds == 1].sum() < (kinds == 1).sum()
+    kv = _device_cache(csa2, src)
+    rng = np.random.default_rng(55)
+    pools = [np.flatnonzero(kinds == i) for i in range(3)] + [np.arange(cap)]
+    idx = np.empty((n_q, k_idx), np.int32)
+    for b in range(n_q):
+        idx[b] = np.sort(rng.choice(pools[b % 4], k_idx, replace=False))
+    q = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_MAIN_Q, 5), synth.NORMAL, range(n_q), np.arange(16), 512)
+    swa_rows = synth.gen_rows(SEED, synth.tensor_id(synth.KIND_SWA, 5), synth.NORMAL, [0],
+                              np.arange(n_q + swa_max - 1), 512)[0]
+    swa_len = rng.integers(0, swa_max + 1, size=n_q).astype(np.int32)
+    swa_len[:3] = swa_max
+    print_case("sparse_attn many queries, scales around the single-f16 bound")
+    out = torch.full((n_q, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+    csa2.sparse_attn(dev(q), kv, dev(idx), dev(swa_rows), dev(swa_len), SM_SCALE, out, q_per_seq=n_q,
+                     swa_q_stride_rows=1, swa_max=swa_max)
+    got = out.cpu().numpy()
+    for b in sorted({0, 1, 2, 3, 4, 5, 6, 7, n_q - 1, *rng.integers(0, n_q, 9).tolist()}):
+        ref = oracle.sparse_attn(q[b], codes, scales, idx[b], swa_rows[b:b + swa_max], swa_len[b], SM_SCALE)
+        assert_attention_close(got[b], ref, f"query {b}")
+
+
 @pytest.mark.parametrize("where", ["window", "selected"])
 def test_sparse_attn_many_queries_late_maximum(csa2, where):
     """Many queries (one wavefront each) where a row late in a query's order
