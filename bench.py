@@ -44,7 +44,7 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12721267, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12721279, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
                     "cdb9620b29355fb802f2b19e9479a7c69bc4acff2a4971508a4032d1ed985d5a",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
@@ -52,9 +52,9 @@ MEASURED_TRAFFIC = {
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e"}},
     "decoder20_1m/block_scan": {
-        "bytes": 210304718, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 209850117, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
+                    "709a8fb0d0eacbead763334c820a7bdb0967657ff5e4fa7119f473c2273fdcc9",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
@@ -62,11 +62,11 @@ MEASURED_TRAFFIC = {
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "decoder20_1m/pool_select": {
-        "bytes": 36533981, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 36533672, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
+                    "709a8fb0d0eacbead763334c820a7bdb0967657ff5e4fa7119f473c2273fdcc9",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
+                    "5f39e3a7ddddb62d4e1f18f6853b3f8b6a101be74815adc89d5c3061bec1fc70",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
@@ -74,11 +74,11 @@ MEASURED_TRAFFIC = {
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "bytes": 1092501651, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "bytes": 1092364722, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
+                    "709a8fb0d0eacbead763334c820a7bdb0967657ff5e4fa7119f473c2273fdcc9",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
+                    "5f39e3a7ddddb62d4e1f18f6853b3f8b6a101be74815adc89d5c3061bec1fc70",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
@@ -121,7 +121,7 @@ def measured_traffic(op_key: str):
 # sources are unchanged.
 KERNEL_TRACE = {
     "decoder20_1m/sparse_attn": {
-        "us": 12.66, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 12.72, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
                     "cdb9620b29355fb802f2b19e9479a7c69bc4acff2a4971508a4032d1ed985d5a",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
@@ -129,11 +129,11 @@ KERNEL_TRACE = {
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e"}},
     "decoder20_1m/pool_select": {
-        "us": 21.18, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 21.13, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
+                    "709a8fb0d0eacbead763334c820a7bdb0967657ff5e4fa7119f473c2273fdcc9",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
+                    "5f39e3a7ddddb62d4e1f18f6853b3f8b6a101be74815adc89d5c3061bec1fc70",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
@@ -141,11 +141,11 @@ KERNEL_TRACE = {
                     "fp4_kv_cache_quant_amd/csrc/select_dev.hpp":
                     "1a346e416aaaf92b6758b0632876d1ca8b0891d0c26c9feeba822aca9d06e9d9"}},
     "encoder_1m/flat_select": {
-        "us": 214.95, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
+        "us": 215.05, "profile": "profiles/encoder_decode_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/index_score.hip":
-                    "de61a9c7b37d977fa33ab6d4d4a97ece1b5817ada8a9ba88adc04eb014aea3fa",
+                    "709a8fb0d0eacbead763334c820a7bdb0967657ff5e4fa7119f473c2273fdcc9",
                     "fp4_kv_cache_quant_amd/csrc/topk.hip":
-                    "25f60ee539e941b3772bfd816c19ead66153a8ce3e101c7497cd1b8e3f552469",
+                    "5f39e3a7ddddb62d4e1f18f6853b3f8b6a101be74815adc89d5c3061bec1fc70",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
                     "16bbfd324bed22718b51c5dce1bdb40ab694408572eaf2f6e359577fa431688e",
                     "fp4_kv_cache_quant_amd/csrc/topk_ws.hpp":
