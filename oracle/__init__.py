@@ -58,6 +58,10 @@ PINS = {
     "orc_pool_blocks/orc_pool_select": "hierarchical == flat when blocks <= pool; subset/size invariants",
     "orc_sparse_attn": "k >= L equals torch CPU float64 dense softmax attention; 1 key, equal keys, q = 0",
     "decode_step": "Reuse reproduces the latest Full/Reindex indices; Reindex with Full's Q == Full",
+    "orc_sparse_attn_partial": "o / l equals orc_sparse_attn on the same rows; m is the largest base-2 logit "
+                               "(numpy float64); l >= 1; empty share m = -inf, l = 0, o = 0",
+    "orc_attn_merge": "merge of shares over random splits of a query's rows (window on one share, empty "
+                      "shares) equals orc_sparse_attn over all of them; one share gives o / l",
     "orc_fp8_code": "all 65,536 bf16 patterns vs torch's float8_e4m3fn cast in range, saturation and NaN beyond; golden ties",
     "orc_sparse_attn_fp8w": "equals orc_sparse_attn on window rows that FP8 represents exactly (bf16 of E4M3 values)",
     "orc_block_key": "numpy int64 sums of integer keys per block, partial last block; one-hot closed forms",
@@ -110,6 +114,10 @@ def lib() -> ctypes.CDLL:
         L.orc_pool_select.restype = i64
         L.orc_sparse_attn.argtypes = [P, P, P, P, i64, P, i64, ctypes.c_double, P]
         L.orc_sparse_attn.restype = None
+        L.orc_sparse_attn_partial.argtypes = [P, P, P, P, i64, P, i64, ctypes.c_double, P, P]
+        L.orc_sparse_attn_partial.restype = None
+        L.orc_attn_merge.argtypes = [P, P, i64, P]
+        L.orc_attn_merge.restype = None
         L.orc_fp8_code.argtypes = [ctypes.c_uint16]
         L.orc_fp8_code.restype = ctypes.c_uint8
         L.orc_fp8_rows.argtypes = [P, i64, P]
@@ -233,6 +241,33 @@ def sparse_attn_gathered(q, rows_codes, rows_scales, idx, swa, swa_len, sm_scale
     if swa8 is not None:
         return sparse_attn_fp8w(q, rows_codes, rows_scales, local, swa8, swa_len, sm_scale)
     return sparse_attn(q, rows_codes, rows_scales, local, swa, swa_len, sm_scale)
+
+
+def sparse_attn_partial(q, codes, scales, idx, swa, swa_len: int, sm_scale: float):
+    """One rank's share (the rows of :func:`sparse_attn`): o [16][512] and
+    ml [16][2] = (m, l), float64, base-2 units (see orc_sparse_attn_partial)."""
+    q = _u16(q).reshape(HEADS, D)
+    codes = np.ascontiguousarray(codes, np.uint8).reshape(-1, CODE_BYTES)
+    scales = np.ascontiguousarray(scales, np.uint8).reshape(-1, SCALE_BYTES)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    assert idx.max(initial=-1) < codes.shape[0]
+    swa = _u16(swa).reshape(-1, D)
+    assert swa_len <= swa.shape[0]
+    o = np.zeros((HEADS, D), np.float64)
+    ml = np.zeros((HEADS, 2), np.float64)
+    lib().orc_sparse_attn_partial(_p(q), _p(codes), _p(scales), _p(idx), len(idx), _p(swa), swa_len,
+                                  float(sm_scale), _p(o), _p(ml))
+    return o, ml
+
+
+def attn_merge(o_parts, ml_parts) -> np.ndarray:
+    """Softmax over the union of shares: o_parts [S][16][512], ml_parts [S][16][2] -> [16][512] f32."""
+    o_parts = np.ascontiguousarray(o_parts, np.float64).reshape(-1, HEADS, D)
+    ml_parts = np.ascontiguousarray(ml_parts, np.float64).reshape(-1, HEADS, 2)
+    assert o_parts.shape[0] == ml_parts.shape[0]
+    out = np.zeros((HEADS, D), np.float32)
+    lib().orc_attn_merge(_p(o_parts), _p(ml_parts), o_parts.shape[0], _p(out))
+    return out
 
 
 # ------------------------------------------------- block-key maintenance

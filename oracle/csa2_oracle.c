@@ -349,6 +349,77 @@ void orc_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* sca
   free(x);
 }
 
+/* ------------------------------------------------ context-parallel shares */
+
+/* One rank's share of steps (d)+(e) when the attended rows are split over
+ * ranks (one sequence longer than a GPU holds: each rank holds some of the
+ * selected rows, the rank with the tail also the window).  READING (the
+ * pages do not describe a split): the share is the unnormalised softmax
+ * over the rank's rows in base-2 units, per head h:
+ *   z_j = sm_scale * log2(e) * (q_h . x_j),  m_h = max_j z_j,
+ *   l_h = sum_j 2^(z_j - m_h),  o_h = sum_j 2^(z_j - m_h) x_j,
+ * and an empty share is m = -inf, l = 0, o = 0.  o [16][512], ml [16][2]
+ * (m, l), both double.  The rows are those of orc_sparse_attn. */
+void orc_sparse_attn_partial(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                             const int64_t* idx, int64_t n_idx, const uint16_t* swa, int64_t swa_len,
+                             double sm_scale, double* o, double* ml) {
+  const double log2e = 1.0 / log(2.0);
+  const int64_t n = count_selected(idx, n_idx) + (swa_len > 0 ? swa_len : 0);
+  double* x = (double*)malloc((size_t)(n > 0 ? n : 1) * D_LATENT * sizeof(double));
+  double* z = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+  int64_t r = gather_rows(codes, scales, idx, n_idx, x);
+  for (int64_t j = 0; j < swa_len; ++j, ++r)
+    for (int d = 0; d < D_LATENT; ++d) x[r * D_LATENT + d] = orc_bf16_value(swa[j * D_LATENT + d]);
+  for (int h = 0; h < MAIN_HEADS; ++h) {
+    double m = -INFINITY, l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < D_LATENT; ++d) dot += orc_bf16_value(q[h * D_LATENT + d]) * x[j * D_LATENT + d];
+      z[j] = sm_scale * log2e * dot;
+      if (z[j] > m) m = z[j];
+    }
+    for (int64_t j = 0; j < n; ++j) {
+      z[j] = exp2(z[j] - m);
+      l += z[j];
+    }
+    for (int d = 0; d < D_LATENT; ++d) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < n; ++j) acc += z[j] * x[j * D_LATENT + d];
+      o[h * D_LATENT + d] = acc;
+    }
+    ml[2 * h] = m;
+    ml[2 * h + 1] = l;
+  }
+  free(z);
+  free(x);
+}
+
+/* The softmax over the union of n_parts shares (the arithmetic after the
+ * ranks exchange them): per head, M = max_s m_s, then
+ *   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+ * shares with m_s = -inf contributing nothing; no rows at all gives 0.
+ * o [n_parts][16][512], ml [n_parts][16][2]; out [16][512] float. */
+void orc_attn_merge(const double* o, const double* ml, int64_t n_parts, float* out) {
+  for (int h = 0; h < MAIN_HEADS; ++h) {
+    double M = -INFINITY;
+    for (int64_t s = 0; s < n_parts; ++s)
+      if (ml[(s * MAIN_HEADS + h) * 2] > M) M = ml[(s * MAIN_HEADS + h) * 2];
+    double den = 0.0;
+    for (int64_t s = 0; s < n_parts; ++s) {
+      const double ms = ml[(s * MAIN_HEADS + h) * 2];
+      if (ms != -INFINITY) den += exp2(ms - M) * ml[(s * MAIN_HEADS + h) * 2 + 1];
+    }
+    for (int d = 0; d < D_LATENT; ++d) {
+      double acc = 0.0;
+      for (int64_t s = 0; s < n_parts; ++s) {
+        const double ms = ml[(s * MAIN_HEADS + h) * 2];
+        if (ms != -INFINITY) acc += exp2(ms - M) * o[(s * MAIN_HEADS + h) * D_LATENT + d];
+      }
+      out[h * D_LATENT + d] = den > 0.0 ? (float)(acc / den) : 0.0f;
+    }
+  }
+}
+
 /* ------------------------------------------------------------ FP8 window */
 
 /* [P4] summary: the sliding-window KV is kept in FP8.  READING: OCP E4M3FN

@@ -402,6 +402,56 @@ def test_attention_special_cases():
     assert np.allclose(out, ref, rtol=1e-6, atol=1e-6)
 
 
+def test_attention_share_normalises_to_attention_over_its_rows():
+    codes, scales = _random_cache(8, 400)
+    q = synth.gen_rows(8, synth.tensor_id(synth.KIND_MAIN_Q), synth.NORMAL, [0], np.arange(16), 512)[0]
+    swa = synth.gen_rows(8, synth.tensor_id(synth.KIND_SWA), synth.NORMAL, [0], np.arange(128), 512)[0]
+    rng = np.random.default_rng(8)
+    idx = np.sort(rng.choice(400, 150, replace=False)).astype(np.int64)
+    idx[::7] = -1
+    sm = 1 / math.sqrt(512)
+    o, ml = oracle.sparse_attn_partial(q, codes, scales, idx, swa, 60, sm)
+    ref = oracle.sparse_attn(q, codes, scales, idx, swa, 60, sm)
+    assert np.allclose(o / ml[:, 1:2], ref, rtol=1e-6, atol=1e-7)
+    # m is the largest base-2 logit over the rows (numpy float64 matmul), and l >= 1
+    x = np.stack([oracle.dequant_row(codes[i], scales[i]) for i in idx if i >= 0]
+                 + [synth.bf16_to_f32(swa[j]).astype(np.float64) for j in range(60)])
+    logits = sm / math.log(2) * (synth.bf16_to_f32(q).astype(np.float64) @ x.T)
+    assert np.allclose(ml[:, 0], logits.max(axis=1), rtol=1e-12, atol=1e-12)
+    assert np.all(ml[:, 1] >= 1.0) and np.all(ml[:, 1] <= x.shape[0])
+    # an empty share
+    o, ml = oracle.sparse_attn_partial(q, codes, scales, [-1, -1], swa, 0, sm)
+    assert np.all(o == 0) and np.all(ml[:, 0] == -np.inf) and np.all(ml[:, 1] == 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_merge_of_shares_equals_attention_over_all_rows(seed):
+    """The rows of one query split at random over 3 shares (the window on
+    one of them, one share possibly empty): the merge of the shares is the
+    attention over all the rows."""
+    codes, scales = _random_cache(9 + seed, 600)
+    q = synth.gen_rows(9 + seed, synth.tensor_id(synth.KIND_MAIN_Q), synth.NORMAL, [0], np.arange(16), 512)[0]
+    swa = synth.gen_rows(9 + seed, synth.tensor_id(synth.KIND_SWA), synth.NORMAL, [0], np.arange(128), 512)[0]
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(600, 512, replace=False)).astype(np.int64)
+    owner = rng.integers(0, 3 if seed else 2, size=idx.size)  # seed 0: share 2 holds no row
+    tail = int(rng.integers(0, 3))
+    sm = 1 / math.sqrt(512)
+    o_parts, ml_parts = [], []
+    for s in range(3):
+        o, ml = oracle.sparse_attn_partial(q, codes, scales, np.where(owner == s, idx, -1), swa,
+                                           128 if s == tail else 0, sm)
+        o_parts.append(o)
+        ml_parts.append(ml)
+    got = oracle.attn_merge(np.stack(o_parts), np.stack(ml_parts))
+    ref = oracle.sparse_attn(q, codes, scales, idx, swa, 128, sm)
+    assert np.allclose(got, ref, rtol=1e-6, atol=1e-7)
+    # one share merges to its own attention
+    one = oracle.attn_merge(o_parts[tail][None], ml_parts[tail][None])
+    assert np.allclose(one, oracle.sparse_attn(q, codes, scales, np.where(owner == tail, idx, -1), swa, 128, sm),
+                       rtol=1e-6, atol=1e-7)
+
+
 # ---------------------------------------------------------------- layer walk
 def _layer_inputs(seed, n_layers, modes):
     ins = []
