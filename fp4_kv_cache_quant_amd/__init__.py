@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "Csa2Error", "FP4KV", "quant_rows", "quant_append", "index_score", "topk", "topk_workspace_size",
-    "sparse_attn", "sparse_attn_workspace_size", "sparse_attn_noalloc", "pool_select", "pool_select_workspace_size", "flat_select", "flat_select_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
+    "sparse_attn", "sparse_attn_workspace_size", "sparse_attn_noalloc", "sparse_attn_partial", "attn_merge", "pool_select", "pool_select_workspace_size", "flat_select", "flat_select_workspace_size", "Sched", "Layer", "FULL", "REINDEX", "REUSE",
     "prefill_index_score", "Prefill", "quant_fp8_rows", "block_keys", "append_index_keys",
     "LATENT", "CODE_BYTES", "SCALE_BYTES", "HEADS", "IDX_HEADS", "IDX_DIM",
 ]
@@ -91,6 +91,9 @@ _block_keys = _sig("csa2_block_keys", _I32, _P, _I64, _P, _I32, _P, _I64, _I32, 
 _append_keys = _sig("csa2_append_index_keys", _I32, _P, _P, _I64, _P, _I64, _I32, _P, _P, _I32, _P)
 _attn = _sig("csa2_sparse_attn", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64, _P,
              _I32, _F32, _P, _P, _SZ, _P)
+_attn_partial = _sig("csa2_sparse_attn_partial", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64,
+                     _P, _I32, _F32, _P, _P, _P, _SZ, _P)
+_attn_merge = _sig("csa2_attn_merge", _I32, _P, _P, _I32, _I32, _P, _P)
 _attn_noalloc = _sig("csa2_sparse_attn_noalloc", _I32, _P, _I32, ctypes.POINTER(_FP4KV), _I32, _P, _I32, _P, _I64,
                      _P, _I32, _F32, _P, _P)
 _sched_create = _sig("csa2_sched_create", _I32, ctypes.POINTER(_SchedDesc), ctypes.POINTER(_P))
@@ -275,6 +278,33 @@ def sparse_attn_noalloc(q: torch.Tensor, kv: FP4KV, idx: torch.Tensor, swa: torc
     kvc = kv.c()
     _check(_attn_noalloc(_ptr(q), n_q, ctypes.byref(kvc), q_per_seq, _ptr(idx), k_idx, _ptr(swa), swa_q_stride_rows,
                          _ptr(swa_len), swa_max, sm_scale, _ptr(out), _stream(stream)))
+
+
+def sparse_attn_partial(q: torch.Tensor, kv: FP4KV, idx: Optional[torch.Tensor], swa: Optional[torch.Tensor],
+                        swa_len: torch.Tensor, sm_scale: float, out_o: torch.Tensor, out_ml: torch.Tensor,
+                        ws: Optional[torch.Tensor] = None, q_per_seq: int = 1,
+                        swa_q_stride_rows: Optional[int] = None, swa_max: Optional[int] = None, stream=None) -> None:
+    """csa2_sparse_attn_partial: a rank's share of a context-parallel split -- out_o [n_q][16][512] f32
+    (unnormalised), out_ml [n_q][16][2] f32 (base-2 max, sum).  swa None: no window rows (swa_max 0)."""
+    n_q = q.shape[0]
+    k_idx = idx.shape[1] if idx is not None and idx.dim() == 2 else 0
+    if swa_max is None:
+        swa_max = swa.shape[1] if swa is not None and swa.dim() == 3 else 0
+    if swa_q_stride_rows is None:
+        swa_q_stride_rows = swa_max
+    need = sparse_attn_workspace_size(n_q, k_idx, swa_max)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    kvc = kv.c()
+    _check(_attn_partial(_ptr(q), n_q, ctypes.byref(kvc), q_per_seq, _ptr(idx), k_idx, _ptr(swa), swa_q_stride_rows,
+                         _ptr(swa_len), swa_max, sm_scale, _ptr(out_o), _ptr(out_ml), _ptr(ws), ws.numel(),
+                         _stream(stream)))
+
+
+def attn_merge(parts_o: torch.Tensor, parts_ml: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """csa2_attn_merge: parts_o [S][n_q][16][512] f32, parts_ml [S][n_q][16][2] f32 -> out [n_q][16][512]."""
+    n_parts, n_q = parts_o.shape[0], parts_o.shape[1]
+    _check(_attn_merge(_ptr(parts_o), _ptr(parts_ml), n_parts, n_q, _ptr(out), _stream(stream)))
 
 
 def sparse_attn(q: torch.Tensor, kv: FP4KV, idx: torch.Tensor, swa: torch.Tensor, swa_len: torch.Tensor,

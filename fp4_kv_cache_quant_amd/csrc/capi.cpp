@@ -28,6 +28,10 @@ csa2_status attn_scratch(void** ptr, size_t* bytes);
 csa2_status attn_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
                         const void*, int, int64_t, const int32_t*, int32_t, const void*, const int32_t*, float,
                         float*, void*, hipStream_t);
+csa2_status attn_partial_launch(const uint16_t*, int32_t, const csa2_fp4_kv&, int32_t, const int32_t*, int32_t,
+                                const void*, int, int64_t, const int32_t*, int32_t, float, float*, float*, void*,
+                                hipStream_t);
+csa2_status attn_merge_launch(const float*, const float*, int32_t, int32_t, float*, hipStream_t);
 
 namespace {
 thread_local std::string g_error;
@@ -203,7 +207,7 @@ extern "C" {
 
 const char* csa2_last_error(void) { return g_error.c_str(); }
 
-int32_t csa2_abi_version(void) { return 6; }
+int32_t csa2_abi_version(void) { return 7; }
 
 csa2_status csa2_quant_rows(const uint16_t* src, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                             void* stream) {
@@ -319,6 +323,35 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
   if (st != CSA2_OK || n_q == 0) return st;
   return attn_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinBf16, swa_q_stride_rows, swa_len, swa_max,
                      nullptr, nullptr, sm_scale, out, ws, as_stream(stream));
+}
+
+csa2_status csa2_sparse_attn_partial(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                                     const int32_t* idx, int32_t k_idx, const uint16_t* swa,
+                                     int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                                     float sm_scale, float* out_o, float* out_ml, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  clear_error();
+  csa2_status st = check_attn(q, n_q, kv, q_per_seq, idx, k_idx, swa, swa_q_stride_rows, swa_len, swa_max, out_o,
+                              ws, ws_bytes);
+  if (st != CSA2_OK || n_q == 0) return st;
+  CSA2_REQUIRE(out_ml, CSA2_EINVAL, "csa2_sparse_attn_partial: null out_ml");
+  CSA2_REQUIRE((reinterpret_cast<uintptr_t>(out_ml) & 7) == 0, CSA2_EINVAL,
+               "csa2_sparse_attn_partial: out_ml needs 8-byte alignment");
+  return attn_partial_launch(q, n_q, *kv, q_per_seq, idx, k_idx, swa, kWinBf16, swa_q_stride_rows, swa_len,
+                             swa_max, sm_scale, out_o, out_ml, ws, as_stream(stream));
+}
+
+csa2_status csa2_attn_merge(const float* parts_o, const float* parts_ml, int32_t n_parts, int32_t n_q, float* out,
+                            void* stream) {
+  clear_error();
+  CSA2_REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ESHAPE, "csa2_attn_merge: n_q must be in [0, 65535]");
+  CSA2_REQUIRE(n_parts >= 1, CSA2_ESHAPE, "csa2_attn_merge: n_parts must be >= 1");
+  if (n_q == 0) return CSA2_OK;
+  CSA2_REQUIRE(parts_o && parts_ml && out, CSA2_EINVAL, "csa2_attn_merge: null pointer");
+  CSA2_REQUIRE(((reinterpret_cast<uintptr_t>(parts_o) | reinterpret_cast<uintptr_t>(out)) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(parts_ml) & 7) == 0,
+               CSA2_EINVAL, "csa2_attn_merge: parts_o and out need 16-byte, parts_ml 8-byte alignment");
+  return attn_merge_launch(parts_o, parts_ml, n_parts, n_q, out, as_stream(stream));
 }
 
 csa2_status csa2_sparse_attn_noalloc(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,

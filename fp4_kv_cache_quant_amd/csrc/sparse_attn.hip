@@ -37,7 +37,11 @@
 //      next chunk's rows are loaded meanwhile.
 // With one workgroup per query the normalised output is written directly;
 // otherwise each workgroup writes its unnormalised O and (max, sum) per
-// head and a second kernel merges them (log-sum-exp weights).
+// head and a second kernel merges them (log-sum-exp weights).  A rank's
+// share of a context-parallel split (csa2_sparse_attn_partial) is the same
+// computation left unnormalised: O and (max, sum) per head, the max in
+// base-2 units; csa2_attn_merge combines the ranks' shares with the same
+// log-sum-exp merge.
 //
 // Citation keys: [P1] "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M
 // Context, FP4 KV Cache, and Cross-Layer Attention Reuse"; [P3]
@@ -315,9 +319,10 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<W>& sm, AttnState<W>& st, co
 }
 
 // One workgroup = chunks [split * per_split, ...) of query blockIdx.y.  With
-// one split the workgroup covers the whole query and writes the normalised
-// output; otherwise it writes its unnormalised O and (max, sum) per head
-// for the combine kernel.
+// one split and an output the workgroup covers the whole query and writes
+// the normalised output; otherwise (several splits, or out == null for a
+// rank's share) it writes its unnormalised O and (max, sum) per head to
+// part_o / part_ml.
 template <int W, int kWin>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
     if (has_next) cur = nxt;
   }
 
-  if (n_split == 1) {
+  if (n_split == 1 && out) {
     if (tid < 16) sm.l_fin[tid] = st.l_run;
     lds_barrier();
 #pragma unroll
@@ -442,18 +447,23 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_kernel(
   if (tid < 16) part_ml[((int64_t)qb * n_split + split) * 16 + tid] = make_float2(st.m_run, st.l_run);
 }
 
-// Merge the chunks of one (head, query) with log-sum-exp weights:
+// Merge n_parts partials of one (head, query) with log-sum-exp weights:
 //   o_h = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
 // One 128-thread workgroup per (head, query), one float4 of the head's 512
-// channels per thread.  The chunks are taken in batches of 16 whose loads
-// (partial O and (m, l), clamped addresses) are all issued together; a
-// running maximum rescales across batches.
+// channels per thread; partial c of query q is at part_o + q * o_q +
+// c * o_c (floats) and part_ml + q * ml_q + c * ml_c (float2 per head).  The
+// partials are taken in batches of 16 whose loads (partial O and (m, l),
+// clamped addresses) are all issued together; a running maximum rescales
+// across batches.  kNorm: the normalised output; otherwise the merged
+// unnormalised O and (M, sum of 2^(m_c - M) l_c) per head in out_ml.
+template <bool kNorm>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml,
-                                                           int32_t n_split, float* __restrict__ out) {
+                                                           const float2* __restrict__ part_ml, int32_t n_split,
+                                                           int64_t o_q, int64_t o_c, int64_t ml_q, int64_t ml_c,
+                                                           float* __restrict__ out, float2* __restrict__ out_ml) {
   const int h = blockIdx.x, qb = blockIdx.y, tid = threadIdx.x;
-  const float2* ml = part_ml + (int64_t)qb * n_split * 16 + h;
-  const f32x4* pall = reinterpret_cast<const f32x4*>(part_o + (int64_t)qb * n_split * (16 * CSA2_LATENT) + h * CSA2_LATENT) + tid;
+  const float2* ml = part_ml + (int64_t)qb * ml_q + h;
+  const f32x4* pall = reinterpret_cast<const f32x4*>(part_o + (int64_t)qb * o_q + h * CSA2_LATENT) + tid;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f, Mq = kNegInf;
   constexpr int kB = 16;
@@ -463,8 +473,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 #pragma unroll
     for (int cb = 0; cb < kB; ++cb) {
       const int c = min(c0 + cb, n_split - 1);
-      v[cb] = pall[(int64_t)c * (16 * CSA2_LATENT / 4)];
-      m[cb] = ml[c * 16];
+      v[cb] = pall[(int64_t)c * (o_c / 4)];
+      m[cb] = ml[(int64_t)c * ml_c];
     }
     float Mb = Mq;
 #pragma unroll
@@ -480,8 +490,14 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
     }
     Mq = Mb;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  reinterpret_cast<f32x4*>(out + ((int64_t)qb * 16 + h) * CSA2_LATENT)[tid] = acc * inv;
+  f32x4* o4 = reinterpret_cast<f32x4*>(out + ((int64_t)qb * 16 + h) * CSA2_LATENT);
+  if constexpr (kNorm) {
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    o4[tid] = acc * inv;
+  } else {
+    o4[tid] = acc;
+    if (tid == 0) out_ml[(int64_t)qb * 16 + h] = make_float2(Mq, den);
+  }
 }
 
 }  // namespace
@@ -545,10 +561,14 @@ static void attn_dispatch(const AttnPlan& p, int32_t n_q, const uint16_t* q, con
 // new_win / win_lens: the step's new window row per sequence ([*][512] in
 // the window's element type), or null, and the sequences' positions after
 // the step's append: the new row goes to window slot (lens - 1) % swa_max.
-csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
-                        const int32_t* idx, int32_t k_idx, const void* swa, int win,
-                        int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, const void* new_win,
-                        const int32_t* win_lens, float sm_scale, float* out, void* ws, hipStream_t stream) {
+// out_ml == null: the normalised output in out.  Otherwise a rank's share:
+// the unnormalised O in out and (max in base-2 units, sum) per head in
+// out_ml [n_q][16].
+static csa2_status attn_launch_impl(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
+                                    const int32_t* idx, int32_t k_idx, const void* swa, int win,
+                                    int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                                    const void* new_win, const int32_t* win_lens, float sm_scale, float* out,
+                                    float2* out_ml, void* ws, hipStream_t stream) {
   if (n_q == 0) return CSA2_OK;
   const AttnPlan p = attn_plan(n_q, k_idx, swa_max);
   float* part_o = nullptr;
@@ -564,18 +584,60 @@ csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, i
   const uint8_t* nw = reinterpret_cast<const uint8_t*>(new_win);
   // Many queries over bf16 window rows with no step window row (the
   // prefill chunk): the two-wavefronts-per-query kernel of attn_many.hip.
-  if (p.waves == 2 && !new_win && k_idx <= kAttnManyMaxIdx && win == kWinBf16)
+  float* kout = out;
+  if (out_ml && p.splits == 1) {  // a share from one workgroup per query: written in place
+    part_o = out;
+    part_ml = out_ml;
+    kout = nullptr;
+  }
+  if (p.waves == 2 && !new_win && !out_ml && k_idx <= kAttnManyMaxIdx && win == kWinBf16)
     return attn_many_launch(q, n_q, kv, q_per_seq, idx, k_idx, sw, win, swa_q_stride_rows, swa_len, swa_max,
                             scale_log2, out, stream);
   if (win == kWinE4m3)
     attn_dispatch<kWinE4m3>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                            nw, win_lens, scale_log2, part_o, part_ml, out, stream);
+                            nw, win_lens, scale_log2, part_o, part_ml, kout, stream);
   else
     attn_dispatch<kWinBf16>(p, n_q, q, kv, q_per_seq, idx, k_idx, sw, swa_q_stride_rows, swa_len, swa_max,
-                            nw, win_lens, scale_log2, part_o, part_ml, out, stream);
-  if (p.splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml, p.splits, out);
-  return launch_status("csa2_sparse_attn");
+                            nw, win_lens, scale_log2, part_o, part_ml, kout, stream);
+  if (p.splits > 1) {
+    const int64_t o_c = 16 * CSA2_LATENT, o_q = p.splits * o_c, ml_q = p.splits * 16;
+    if (out_ml)
+      hipLaunchKernelGGL(attn_combine_kernel<false>, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml,
+                         p.splits, o_q, o_c, ml_q, (int64_t)16, out, out_ml);
+    else
+      hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(16, n_q), dim3(128), 0, stream, part_o, part_ml,
+                         p.splits, o_q, o_c, ml_q, (int64_t)16, out, nullptr);
+  }
+  return launch_status(out_ml ? "csa2_sparse_attn_partial" : "csa2_sparse_attn");
+}
+
+csa2_status attn_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
+                        const int32_t* idx, int32_t k_idx, const void* swa, int win,
+                        int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, const void* new_win,
+                        const int32_t* win_lens, float sm_scale, float* out, void* ws, hipStream_t stream) {
+  return attn_launch_impl(q, n_q, kv, q_per_seq, idx, k_idx, swa, win, swa_q_stride_rows, swa_len, swa_max,
+                          new_win, win_lens, sm_scale, out, nullptr, ws, stream);
+}
+
+// A rank's share (bf16 or E4M3 window rows, no step window row).
+csa2_status attn_partial_launch(const uint16_t* q, int32_t n_q, const csa2_fp4_kv& kv, int32_t q_per_seq,
+                                const int32_t* idx, int32_t k_idx, const void* swa, int win,
+                                int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max, float sm_scale,
+                                float* out_o, float* out_ml, void* ws, hipStream_t stream) {
+  return attn_launch_impl(q, n_q, kv, q_per_seq, idx, k_idx, swa, win, swa_q_stride_rows, swa_len, swa_max,
+                          nullptr, nullptr, sm_scale, out_o, reinterpret_cast<float2*>(out_ml), ws, stream);
+}
+
+// The softmax over the union of n_parts shares: parts_o [n_parts][n_q][16][512],
+// parts_ml [n_parts][n_q][16][2] -> out [n_q][16][512].
+csa2_status attn_merge_launch(const float* parts_o, const float* parts_ml, int32_t n_parts, int32_t n_q, float* out,
+                              hipStream_t stream) {
+  if (n_q == 0) return CSA2_OK;
+  const int64_t o_q = 16 * CSA2_LATENT, o_c = (int64_t)n_q * o_q;
+  hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(16, n_q), dim3(128), 0, stream, parts_o,
+                     reinterpret_cast<const float2*>(parts_ml), n_parts, o_q, o_c, (int64_t)16, (int64_t)n_q * 16,
+                     out, nullptr);
+  return launch_status("csa2_attn_merge");
 }
 
 // ------------------------------------------------- static scratch

@@ -75,7 +75,8 @@ const char* csa2_last_error(void);
  * the FP8 window, 3 the key maintenance on append, 4 the per-layer indexer
  * K of flat Full layers and csa2_flat_select, 5 the stream argument of
  * csa2_sched_check, the per-step window rows of csa2_step_io and
- * csa2_pool_select). */
+ * csa2_pool_select; 6 csa2_prefill_select; 7 csa2_sparse_attn_partial
+ * and csa2_attn_merge). */
 int32_t csa2_abi_version(void);
 
 /* ------------------------------------------------------------ FP4 cache
@@ -228,6 +229,40 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* 
                              const int32_t* idx, int32_t k_idx, const uint16_t* swa,
                              int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
                              float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The context-parallel split of steps (d)+(e): one sequence longer than a
+ * GPU holds, its positions sharded over ranks.  Each selecting layer: every
+ * rank selects among its own positions with global ids, the ranks exchange
+ * (score, id) pairs and derive the same global Top-512, each rank attends
+ * over the selected rows it holds (the rank with the tail also over the
+ * window), and the ranks' shares are merged.  The pages describe no split:
+ * the share and the merge are the plain log-sum-exp decomposition of the
+ * softmax of csa2_sparse_attn ([P1 "Compressed Sparse Attention 2 (CSA2)"]:
+ * one softmax over the selected rows and the window).  The exchange itself
+ * (RCCL all-gather over xGMI) is the caller's.
+ *
+ * csa2_sparse_attn_partial: a rank's share -- csa2_sparse_attn's arguments
+ * and rows (bf16 window rows; swa_max = 0 or swa_len 0 on ranks without the
+ * window), the softmax left unnormalised:
+ *   out_o  [n_q][16][512] f32: o_h = sum_j 2^(z_j - m_h) x_j
+ *   out_ml [n_q][16][2]  f32: (m_h, l_h), m_h = max_j z_j, l_h = sum_j 2^(z_j - m_h)
+ * with z_j = sm_scale * log2(e) * (q_h . x_j) (base-2 units); a query with no
+ * row gives m = -inf, l = 0, o = 0.  ws: csa2_sparse_attn_workspace_size bytes,
+ * as for csa2_sparse_attn.  out_o 16-byte and out_ml 8-byte aligned.
+ *
+ * csa2_attn_merge: the softmax over the union of n_parts shares, per query
+ * and head: M = max_s m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+ * (0 where no share has a row).  parts_o [n_parts][n_q][16][512],
+ * parts_ml [n_parts][n_q][16][2] (the shares of the ranks, stacked in any
+ * order), out [n_q][16][512] f32.  n_parts >= 1, n_q <= 65535; parts_o and
+ * out 16-byte, parts_ml 8-byte aligned. */
+csa2_status csa2_sparse_attn_partial(const uint16_t* q, int32_t n_q, const csa2_fp4_kv* kv, int32_t q_per_seq,
+                                     const int32_t* idx, int32_t k_idx, const uint16_t* swa,
+                                     int64_t swa_q_stride_rows, const int32_t* swa_len, int32_t swa_max,
+                                     float sm_scale, float* out_o, float* out_ml, void* ws, size_t ws_bytes,
+                                     void* stream);
+csa2_status csa2_attn_merge(const float* parts_o, const float* parts_ml, int32_t n_parts, int32_t n_q, float* out,
+                            void* stream);
 
 /* csa2_sparse_attn for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(csa2):
 
 
 def test_abi_version(csa2):
-    assert csa2.abi_version() == 6
+    assert csa2.abi_version() == 7
 
 
 def _err(csa2):
@@ -86,6 +86,30 @@ def test_attention_rejects_small_workspace_and_bad_sizes(csa2):
     assert call(need, n_q=2) == -2  # two queries, one cache sequence
     assert call(need, q=FAKE + 8) == -1
     assert call(need, st=-1) == -1 and "stride" in _err(csa2)
+
+
+def test_context_parallel_share_and_merge_reject_bad_arguments(csa2):
+    kv = csa2._FP4KV(FAKE, FAKE, 1000, 1)
+    need = csa2.sparse_attn_workspace_size(1, 512, 128)
+
+    def share(out_ml, **kw):
+        a = dict(q=FAKE, n_q=1, k_idx=512, swa_max=128, out_o=FAKE)
+        a.update(kw)
+        return csa2._attn_partial(a["q"], a["n_q"], ctypes.byref(kv), 1, FAKE, a["k_idx"], FAKE, 128, FAKE,
+                                  a["swa_max"], 0.04, a["out_o"], out_ml, FAKE, need, None)
+
+    assert share(None) == -1 and "out_ml" in _err(csa2)
+    assert share(FAKE + 4) == -1 and "align" in _err(csa2)
+    assert share(FAKE, out_o=FAKE + 8) == -1
+    assert share(FAKE, swa_max=5000) == -2
+    assert share(None, n_q=0) == 0  # nothing to do, nothing checked past n_q
+    merge = csa2._attn_merge
+    assert merge(FAKE, FAKE, 0, 4, FAKE, None) == -2 and "n_parts" in _err(csa2)
+    assert merge(FAKE, FAKE, 2, 70000, FAKE, None) == -2
+    assert merge(None, FAKE, 2, 4, FAKE, None) == -1
+    assert merge(FAKE, FAKE + 4, 2, 4, FAKE, None) == -1 and "align" in _err(csa2)
+    assert merge(FAKE + 8, FAKE, 2, 4, FAKE, None) == -1
+    assert merge(None, None, 3, 0, None, None) == 0
 
 
 def test_quant_calls_reject_bad_arguments(csa2):
