@@ -21,7 +21,8 @@ decode workloads (key "configs": one Full layer at 4K positions, the Full +
 and checked the same way; and (keys "fp8_window", "maintained_keys",
 "encoder_decode", "prefill") the step with E4M3 window rows, with block keys
 maintained on append, the encoder's ratio-2 decode and the ratio-2 causal
-prefill chunk.
+prefill chunk; and (key "context_parallel") a rank's attention share and
+the merge of eight shares when a sequence is split over GPUs by positions.
 
 usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-graph] [--no-cpu]
                        [--config NAME] [--no-configs] [--no-prefill] [--prefill-reps 5]
@@ -325,6 +326,59 @@ def op_rooflines(cfg, inp, total_steps, graph: bool = True):
                     "traffic_bytes": measured_traffic(f"{config_key(cfg)}/{key}"),
                     "kernel_trace_us": kernel_trace_us(f"{config_key(cfg)}/{key}")})
     return res
+
+
+def context_parallel_ops(cfg, inp, total_steps, graph: bool = True, ranks: int = 8) -> dict:
+    """The attention of the step when one sequence is split over `ranks`
+    GPUs by positions (context parallelism), at the workload's batch: one
+    rank's share (csa2_sparse_attn_partial) over all 512 selected rows and
+    the window -- the largest share a rank can hold, every selected row on
+    it -- and the merge of `ranks` shares (csa2_attn_merge).  Each rank's
+    selection is the single-GPU selection over its positions, and the
+    exchange between the ranks (RCCL over xGMI) is not on one GPU: neither is
+    timed here.  Bytes per call (n = sequences): the share as the attention
+    plus (m, l) written, n*(512*4 + 512*288 + 128*1024 + 16*1024 + 16*512*4
+    + 16*8); the merge reads every share and writes the output,
+    n*(ranks*(16*512*4 + 16*8) + 16*512*4)."""
+    import torch
+
+    import fp4_kv_cache_quant_amd as csa2
+
+    n = cfg.n_seq
+    L = int(inp.lens[0].item())
+    blk_cap = cfg.blk_cap(total_steps)
+    q0 = inp.idx_q[0][0]
+    bscores = torch.empty(n, blk_cap, dtype=torch.float32, device="cuda")
+    pool = torch.empty(n, cfg.pool_blocks, dtype=torch.int32, device="cuda")
+    idx = torch.empty(n, cfg.topk, dtype=torch.int32, device="cuda")
+    csa2.index_score(q0, inp.blk_k, inp.lens, bscores, len_div=cfg.blk)
+    csa2.topk(bscores, cfg.pool_blocks, pool, lens=inp.lens, len_div=cfg.blk)
+    csa2.pool_select(q0, inp.idx_k, inp.lens, pool, cfg.topk, idx, blk=cfg.blk)
+    aws = torch.empty(max(1, csa2.sparse_attn_workspace_size(n, cfg.topk, cfg.swa)), dtype=torch.uint8,
+                      device="cuda")
+    parts_o = torch.empty(ranks, n, 16, 512, dtype=torch.float32, device="cuda")
+    parts_ml = torch.empty(ranks, n, 16, 2, dtype=torch.float32, device="cuda")
+    out = torch.empty(n, 16, 512, dtype=torch.float32, device="cuda")
+    q, kv, swa = inp.main_q[0][0], inp.kv[0], inp.swa[0]
+
+    def share(r=0):
+        csa2.sparse_attn_partial(q, kv, idx, swa, inp.swa_len, 512 ** -0.5, parts_o[r], parts_ml[r], ws=aws)
+
+    for r in range(ranks):  # valid shares for the merge to read
+        share(r)
+    ops = [("attn_share", "a rank's attention share (sparse_attn_partial: all 512 selected rows + window)",
+            n * (cfg.topk * 4 + cfg.topk * 288 + cfg.swa * 1024 + 16 * 1024 + 16 * 512 * 4 + 16 * 8), share),
+           ("attn_merge", f"merge of {ranks} shares (attn_merge)",
+            n * (ranks * (16 * 512 * 4 + 16 * 8) + 16 * 512 * 4), lambda: csa2.attn_merge(parts_o, parts_ml, out))]
+    res = []
+    for key, name, nbytes, fn in ops:
+        us = _graph_time_us(fn, graph=graph)
+        res.append({"key": key, "op": name, "bytes_per_launch": nbytes, "avg_us": round(us, 2),
+                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
+    return {"ranks": ranks, "positions_per_rank": -(-L // ranks), "ops": res,
+            "not_timed": "the per-rank selection (the single-GPU kernels over L / ranks positions) and the "
+                         "exchange of (score, id) pairs and of the shares between ranks"}
 
 
 def flat_op_rooflines(cfg, inp, graph: bool = True):
@@ -747,6 +801,8 @@ def decode_leg(cfg, K: int, W: int, graph: bool, parity_seqs, cpu: bool, single_
     ops = (op_rooflines(c, inp, total, graph=graph) if c.hierarchical else flat_op_rooflines(c, inp, graph=graph))
     r["roofline"], r["dominant_op"] = roofline_of(ops, config_key(cfg) or c.name)
     r["ops"] = ops
+    if c.hierarchical and config_key(cfg) == "decoder20_1m":
+        r["context_parallel"] = context_parallel_ops(c, inp, total, graph=graph)
     if cpu:
         threads = max(1, len(os.sched_getaffinity(0)))
         seqs = list(parity_seqs)
@@ -856,7 +912,8 @@ def main() -> int:
         "cpu_baseline": head.get("cpu_baseline"), "parity": head.get("parity"),
         "appended_rows_bit_exact": head["appended_rows_bit_exact"],
         "configs": configs, "fp8_window": fp8w, "maintained_keys": keys, "encoder_decode": encoder,
-        "prefill": prefill, "wall_s_timed": head["wall_s_timed"], "build_s": head["build_s"],
+        "prefill": prefill, "context_parallel": head.get("context_parallel"),
+        "wall_s_timed": head["wall_s_timed"], "build_s": head["build_s"],
     }
     print(json.dumps(line), flush=True)
     return 0
