@@ -45,9 +45,9 @@ PEAK_HBM_GBPS = 8000.0
 # those sources are unchanged.
 MEASURED_TRAFFIC = {
     "decoder20_1m/sparse_attn": {
-        "bytes": 12721279, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
+        "bytes": 12728378, "profile": "profiles/decode20_1m_b16_hbm_traffic.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "cdb9620b29355fb802f2b19e9479a7c69bc4acff2a4971508a4032d1ed985d5a",
+                    "28d5635347045cc57ac37e31a076065f6ec85c5949fc68aeb6e2d5b0294b7de4",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
                     "f661423ba3cb7510492a0ac6c0be9cc00bcf54af70b4fc72973da1614caddf09",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
@@ -122,9 +122,9 @@ def measured_traffic(op_key: str):
 # sources are unchanged.
 KERNEL_TRACE = {
     "decoder20_1m/sparse_attn": {
-        "us": 12.72, "profile": "profiles/decode20_1m_b16_kernels.md",
+        "us": 12.74, "profile": "profiles/decode20_1m_b16_kernels.md",
         "sources": {"fp4_kv_cache_quant_amd/csrc/sparse_attn.hip":
-                    "cdb9620b29355fb802f2b19e9479a7c69bc4acff2a4971508a4032d1ed985d5a",
+                    "28d5635347045cc57ac37e31a076065f6ec85c5949fc68aeb6e2d5b0294b7de4",
                     "fp4_kv_cache_quant_amd/csrc/attn_dev.hpp":
                     "f661423ba3cb7510492a0ac6c0be9cc00bcf54af70b4fc72973da1614caddf09",
                     "fp4_kv_cache_quant_amd/csrc/common.hpp":
